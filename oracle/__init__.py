@@ -1,0 +1,131 @@
+"""fp64 CPU oracle for scaled dot-product attention (ctypes binding).
+
+TEST INFRASTRUCTURE.  Only `tests/`, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  The GPU library neither imports
+nor links it, and it shares no code with the GPU path.
+
+The C source (fa_oracle.c) computes the plain definition of attention --
+full score row, two-pass softmax, weighted sum of V -- in fp64 from exactly
+decoded fp16/bf16 inputs.  The definition is the scaled dot-product
+attention formula of "FlashAttention-2 on Ascend NPU: how ops-transformer
+reaches 3x" (2048ai.net, section 1), with the causal reading that key j is
+visible to query i iff j <= i + (Sk - Sq).
+
+Inputs are numpy uint16 arrays holding the 16-bit patterns of the input
+dtype, contiguous, shaped [B, H, S, D].
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+F16, BF16 = 0, 1
+_DTYPES = {"f16": F16, "fp16": F16, "float16": F16, "bf16": BF16, "bfloat16": BF16,
+           F16: F16, BF16: BF16}
+
+_lib = None
+
+
+def load(path: str = None):
+    """Load (building first if absent) the oracle shared library."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_build.LIB) or (
+                os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC)):
+            _build.build()
+        _lib = _bind(ctypes.CDLL(_build.LIB))
+    return _lib
+
+
+def _bind(lib):
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    f64p = ctypes.POINTER(ctypes.c_double)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.ora_f16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.ora_f16_to_f64.restype = ctypes.c_double
+    lib.ora_bf16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.ora_bf16_to_f64.restype = ctypes.c_double
+    lib.ora_decode.argtypes = [u16p, f64p, ctypes.c_int64, ctypes.c_int]
+    lib.ora_decode.restype = None
+    lib.ora_max_threads.argtypes = []
+    lib.ora_max_threads.restype = ctypes.c_int
+    lib.ora_attention_fwd.argtypes = [u16p, u16p, u16p] + [ctypes.c_int] * 5 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_int, f64p, f64p, ctypes.c_int]
+    lib.ora_attention_fwd.restype = ctypes.c_int
+    lib.ora_attention_rows.argtypes = [u16p, u16p, u16p] + [ctypes.c_int] * 5 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_int, i64p, ctypes.c_int64, f64p, f64p,
+        ctypes.c_int]
+    lib.ora_attention_rows.restype = ctypes.c_int
+    return lib
+
+
+def _u16(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("oracle inputs are uint16 bit patterns, got %s" % a.dtype)
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16))
+
+
+def _f64p(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def decode(bits, dtype, lib=None):
+    """Exact fp64 values of an array of fp16/bf16 bit patterns."""
+    lib = lib or load()
+    a, p = _u16(bits)
+    out = np.empty(a.shape, dtype=np.float64)
+    lib.ora_decode(p, _f64p(out), a.size, _DTYPES[dtype])
+    return out
+
+
+def attention_fwd(q, k, v, *, scale, causal, dtype, nthreads=0, lib=None):
+    """Full forward.  q: [B,H,Sq,D], k/v: [B,H,Sk,D] uint16 bit patterns.
+
+    Returns (o [B,H,Sq,D] float64, lse [B,H,Sq] float64)."""
+    lib = lib or load()
+    q, qp = _u16(q)
+    k, kp = _u16(k)
+    v, vp = _u16(v)
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if k.shape != (B, H, Sk, D) or v.shape != k.shape:
+        raise ValueError("shape mismatch q%s k%s v%s" % (q.shape, k.shape, v.shape))
+    o = np.empty((B, H, Sq, D), dtype=np.float64)
+    lse = np.empty((B, H, Sq), dtype=np.float64)
+    rc = lib.ora_attention_fwd(qp, kp, vp, B, H, Sq, Sk, D, ctypes.c_float(scale),
+                               int(bool(causal)), _DTYPES[dtype], _f64p(o), _f64p(lse),
+                               int(nthreads))
+    if rc != 0:
+        raise RuntimeError("ora_attention_fwd failed with code %d" % rc)
+    return o, lse
+
+
+def attention_rows(q, k, v, rows, *, scale, causal, dtype, nthreads=0, lib=None):
+    """Selected rows of the forward.  rows: flat ids (b*H + h)*Sq + i.
+
+    Returns (o [n, D] float64, lse [n] float64)."""
+    lib = lib or load()
+    q, qp = _u16(q)
+    k, kp = _u16(k)
+    v, vp = _u16(v)
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    o = np.empty((rows.size, D), dtype=np.float64)
+    lse = np.empty(rows.size, dtype=np.float64)
+    rc = lib.ora_attention_rows(qp, kp, vp, B, H, Sq, Sk, D, ctypes.c_float(scale),
+                                int(bool(causal)), _DTYPES[dtype],
+                                rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                rows.size, _f64p(o), _f64p(lse), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("ora_attention_rows failed with code %d" % rc)
+    return o, lse
+
+
+def max_threads(lib=None):
+    return (lib or load()).ora_max_threads()

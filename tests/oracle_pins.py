@@ -1,0 +1,231 @@
+"""Pins for the fp64 CPU oracle: facts that the mathematics or the pages fix,
+checked without trusting the oracle's own code.
+
+Each pin takes a loaded oracle library and raises AssertionError when the
+oracle disagrees with the fact.  The pins are run against the real oracle
+(test_oracle.py) and against deliberately broken copies of it
+(test_oracle_mutants.py), which must each fail at least one pin.
+
+Independent routes used here:
+  * input decoding goes through numpy/torch casts, never the oracle's decoder;
+  * closed forms (Q = 0, causal row 0, constant V, key shift);
+  * a 40-digit Python `decimal` evaluation of the definition without the
+    max subtraction, on tiny shapes;
+  * torch's scaled_dot_product_attention in fp64 on the CPU (the pages check
+    their fused operator against exactly this routine: omica.com.cn learning
+    path, "step three");
+  * algebraic invariants (convexity, permutation, chunk merge).
+"""
+from decimal import Decimal, getcontext
+from fractions import Fraction
+import math
+
+import numpy as np
+import torch
+
+import oracle
+from workloads import bits, make_inputs, softmax_scale
+
+
+def _f64(t):
+    """Exact fp64 values of a CPU fp16/bf16 tensor via torch's own cast."""
+    return t.to(torch.float64).numpy()
+
+
+def _run(lib, q, k, v, scale, causal, dtype):
+    return oracle.attention_fwd(bits(q), bits(k), bits(v), scale=scale, causal=causal,
+                                dtype=dtype, lib=lib)
+
+
+def _visible(i, j, Sq, Sk, causal):
+    return (not causal) or j <= i + (Sk - Sq)
+
+
+def pin_decode_f16(lib):
+    allbits = np.arange(65536, dtype=np.uint16)
+    got = oracle.decode(allbits, "f16", lib=lib)
+    ref = allbits.view(np.float16).astype(np.float64)
+    assert np.array_equal(got, ref, equal_nan=True), "fp16 decode differs from numpy"
+    assert np.array_equal(np.signbit(got), np.signbit(ref)), "fp16 decode sign differs"
+
+
+def pin_decode_bf16(lib):
+    allbits = np.arange(65536, dtype=np.uint16)
+    got = oracle.decode(allbits, "bf16", lib=lib)
+    ref = torch.from_numpy(allbits.view(np.int16).copy()).view(torch.bfloat16).to(
+        torch.float64).numpy()
+    assert np.array_equal(got, ref, equal_nan=True), "bf16 decode differs from torch"
+    assert np.array_equal(np.signbit(got), np.signbit(ref)), "bf16 decode sign differs"
+
+
+def pin_q_zero(lib):
+    """Q = 0: every visible score is 0, so O_i is the mean of the visible V rows
+    and lse_i = ln(#visible)."""
+    for dtype, (B, H, S, D) in (("f16", (1, 2, 37, 16)), ("bf16", (2, 1, 70, 8))):
+        _, k, v = make_inputs(B, H, S, D, dtype, seed=11)
+        q = torch.zeros(B, H, S, D, dtype=k.dtype)
+        V = _f64(v)
+        for causal in (False, True):
+            o, lse = _run(lib, q, k, v, softmax_scale(D), causal, dtype)
+            for i in range(S):
+                n = i + 1 if causal else S
+                exp_o = V[:, :, :n, :].mean(axis=2)
+                assert np.allclose(o[:, :, i, :], exp_o, rtol=0, atol=1e-14), (dtype, causal, i)
+                assert np.allclose(lse[:, :, i], math.log(n), rtol=0, atol=1e-14), (dtype, causal, i)
+
+
+def pin_causal_row0(lib):
+    """Causal row 0 sees key 0 only: O_0 = V_0 exactly, lse_0 = scale * q_0 . k_0."""
+    for dtype, q_mult in (("f16", 1.0), ("bf16", 4.0)):
+        B, H, S, D = 2, 3, 19, 64
+        q, k, v = make_inputs(B, H, S, D, dtype, seed=12, q_mult=q_mult)
+        scale = softmax_scale(D)
+        o, lse = _run(lib, q, k, v, scale, True, dtype)
+        assert np.array_equal(o[:, :, 0, :], _f64(v)[:, :, 0, :]), dtype
+        Q, K = _f64(q), _f64(k)
+        for b in range(B):
+            for h in range(H):
+                dot = sum(Fraction(float(a)) * Fraction(float(c)) for a, c in zip(Q[b, h, 0], K[b, h, 0]))
+                want = float(Fraction(scale) * dot)
+                assert abs(lse[b, h, 0] - want) <= 1e-14 * max(1.0, abs(want)), (dtype, b, h)
+
+
+def pin_convexity(lib):
+    """Each output row is a convex combination of the visible V rows."""
+    B, H, S, D = 1, 2, 64, 32
+    q, k, v = make_inputs(B, H, S, D, "f16", seed=13)
+    V = _f64(v)
+    for causal in (False, True):
+        o, _ = _run(lib, q, k, v, softmax_scale(D), causal, "f16")
+        for i in range(S):
+            n = i + 1 if causal else S
+            lo = V[:, :, :n, :].min(axis=2) - 1e-15
+            hi = V[:, :, :n, :].max(axis=2) + 1e-15
+            assert np.all(o[:, :, i, :] >= lo) and np.all(o[:, :, i, :] <= hi), (causal, i)
+
+
+def _decimal_attention(Q, K, V, scale, causal):
+    """The definition at 40 significant digits, without max subtraction."""
+    getcontext().prec = 40
+    Sq, D = Q.shape
+    Sk = K.shape[0]
+    sc = Decimal(scale)
+    o = np.zeros((Sq, D))
+    lse = np.zeros(Sq)
+    for i in range(Sq):
+        ws, num = [], [Decimal(0)] * D
+        for j in range(Sk):
+            if not _visible(i, j, Sq, Sk, causal):
+                continue
+            s = sc * sum(Decimal(float(Q[i, d])) * Decimal(float(K[j, d])) for d in range(D))
+            w = s.exp()
+            ws.append(w)
+            for d in range(D):
+                num[d] += w * Decimal(float(V[j, d]))
+        tot = sum(ws)
+        lse[i] = float(tot.ln())
+        for d in range(D):
+            o[i, d] = float(num[d] / tot)
+    return o, lse
+
+
+def pin_bruteforce_decimal(lib):
+    cases = (("f16", 1, 5, 4, 1.0), ("f16", 2, 16, 8, 1.0), ("bf16", 1, 9, 3, 4.0),
+             ("bf16", 1, 12, 8, 1.0))
+    for dtype, H, S, D, q_mult in cases:
+        q, k, v = make_inputs(1, H, S, D, dtype, seed=14 + S, q_mult=q_mult)
+        scale = softmax_scale(D)
+        Q, K, V = _f64(q), _f64(k), _f64(v)
+        for causal in (False, True):
+            o, lse = _run(lib, q, k, v, scale, causal, dtype)
+            for h in range(H):
+                eo, el = _decimal_attention(Q[0, h], K[0, h], V[0, h], scale, causal)
+                assert np.all(np.abs(o[0, h] - eo) <= 1e-13 * np.maximum(1, np.abs(eo))), (dtype, S, causal)
+                assert np.all(np.abs(lse[0, h] - el) <= 1e-13 * np.maximum(1, np.abs(el))), (dtype, S, causal)
+
+
+def _sdpa(Q, K, V, scale, causal):
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Q), torch.from_numpy(K), torch.from_numpy(V), scale=scale,
+        is_causal=causal).numpy()
+
+
+def pin_sdpa_fp64(lib):
+    for dtype, (B, H, S, D) in (("f16", (1, 2, 128, 64)), ("f16", (2, 3, 300, 32)),
+                                ("bf16", (1, 2, 257, 128))):
+        q, k, v = make_inputs(B, H, S, D, dtype, seed=15 + S)
+        scale = softmax_scale(D)
+        for causal in (False, True):
+            o, _ = _run(lib, q, k, v, scale, causal, dtype)
+            ref = _sdpa(_f64(q), _f64(k), _f64(v), scale, causal)
+            assert np.max(np.abs(o - ref)) <= 1e-12, (dtype, S, causal, np.max(np.abs(o - ref)))
+    # unequal query / key lengths, non-causal
+    q, _, _ = make_inputs(1, 2, 50, 16, "f16", seed=16)
+    _, k, v = make_inputs(1, 2, 77, 16, "f16", seed=17)
+    o, _ = _run(lib, q, k, v, 0.25, False, "f16")
+    ref = _sdpa(_f64(q), _f64(k), _f64(v), 0.25, False)
+    assert np.max(np.abs(o - ref)) <= 1e-12
+
+
+def pin_chunk_merge(lib):
+    """Splitting the keys into chunks and merging the partial results by their
+    log-sum-exp reproduces the one-shot result (the online-softmax identity)."""
+    q, k, v = make_inputs(1, 2, 40, 32, "f16", seed=18, Sk=100)
+    scale = softmax_scale(32)
+    o, lse = _run(lib, q, k, v, scale, False, "f16")
+    parts = []
+    for a, b in ((0, 30), (30, 64), (64, 100)):
+        parts.append(_run(lib, q, k[:, :, a:b].contiguous(), v[:, :, a:b].contiguous(), scale,
+                          False, "f16"))
+    lse_m = np.logaddexp.reduce(np.stack([p[1] for p in parts]), axis=0)
+    o_m = sum(np.exp(p[1] - lse_m)[..., None] * p[0] for p in parts)
+    assert np.max(np.abs(lse_m - lse)) <= 1e-12
+    assert np.max(np.abs(o_m - o)) <= 1e-12
+
+
+def pin_invariances(lib):
+    B, H, S, D = 1, 2, 48, 16
+    scale = softmax_scale(D)
+    # joint permutation of key/value rows (non-causal) leaves O and lse unchanged
+    q, k, v = make_inputs(B, H, S, D, "f16", seed=19)
+    perm = torch.randperm(S, generator=torch.Generator().manual_seed(3))
+    o1, l1 = _run(lib, q, k, v, scale, False, "f16")
+    o2, l2 = _run(lib, q, k[:, :, perm].contiguous(), v[:, :, perm].contiguous(), scale, False, "f16")
+    assert np.max(np.abs(o1 - o2)) <= 1e-13 and np.max(np.abs(l1 - l2)) <= 1e-13
+    # constant V rows give that constant
+    cvec = torch.linspace(-3, 3, D).to(torch.float16)
+    vc = cvec.expand(B, H, S, D).contiguous()
+    for causal in (False, True):
+        o, _ = _run(lib, q, k, vc, scale, causal, "f16")
+        assert np.max(np.abs(o - _f64(cvec))) <= 1e-14, causal
+    # adding u to every key shifts row i's scores by scale*q_i.u: O unchanged, lse shifted.
+    # values on a 1/8 grid so q, k and k+u are exact in fp16
+    g = torch.Generator().manual_seed(4)
+    qg = (torch.randint(-16, 17, (B, H, S, D), generator=g) / 8.0).to(torch.float16)
+    kg = (torch.randint(-16, 17, (B, H, S, D), generator=g) / 8.0).to(torch.float16)
+    u = (torch.randint(-8, 9, (D,), generator=g) / 8.0)
+    ku = (kg.to(torch.float32) + u).to(torch.float16)
+    assert torch.equal(ku.to(torch.float32), kg.to(torch.float32) + u)
+    for causal in (False, True):
+        oa, la = _run(lib, qg, kg, v, scale, causal, "f16")
+        ob, lb = _run(lib, qg, ku, v, scale, causal, "f16")
+        shift = scale * (_f64(qg) @ u.double().numpy())
+        assert np.max(np.abs(oa - ob)) <= 1e-12, causal
+        assert np.max(np.abs(lb - la - shift)) <= 1e-12, causal
+
+
+def pin_rows_match_full(lib):
+    q, k, v = make_inputs(2, 3, 65, 32, "bf16", seed=20)
+    scale = softmax_scale(32)
+    for causal in (False, True):
+        o, lse = _run(lib, q, k, v, scale, causal, "bf16")
+        rows = np.array([0, 1, 64, 65, 130, 194, 2 * 3 * 65 - 1], dtype=np.int64)
+        ro, rl = oracle.attention_rows(bits(q), bits(k), bits(v), rows, scale=scale,
+                                       causal=causal, dtype="bf16", lib=lib)
+        assert np.array_equal(ro, o.reshape(-1, 32)[rows])
+        assert np.array_equal(rl, lse.reshape(-1)[rows])
+
+
+ALL_PINS = [pin_decode_f16, pin_decode_bf16, pin_q_zero, pin_causal_row0, pin_convexity,
+            pin_bruteforce_decimal, pin_sdpa_fp64, pin_chunk_merge, pin_invariances,
+            pin_rows_match_full]

@@ -1,0 +1,68 @@
+"""Pin sensitivity: plausible mistakes planted in a copy of the oracle's C
+source must each be caught by at least one pin.  The mutants are built with
+gcc into a temporary directory; the real oracle is never modified."""
+import os
+import shutil
+import tempfile
+
+import pytest
+
+import oracle
+from oracle import build as obuild
+from oracle_pins import ALL_PINS
+
+# (name, original text, mutated text): each replacement must match exactly once.
+MUTATIONS = [
+    ("f16_exponent_bias", "expo - 25);", "expo - 24);"),
+    ("f16_subnormal_scale", "ldexp((double)frac, -24)", "ldexp((double)frac, -23)"),
+    ("bf16_exponent_bias", "expo - 134);", "expo - 133);"),
+    ("bf16_hidden_bit", "(double)(128 + frac)", "(double)(frac)"),
+    ("diagonal_excluded", "return j <= i + (Sk - Sq);", "return j < i + (Sk - Sq);"),
+    ("mask_polarity", "return j <= i + (Sk - Sq);", "return j >= i + (Sk - Sq);"),
+    ("dropped_feature", "for (int d = 0; d < D; ++d) acc += qrow[d] * kr[d];",
+     "for (int d = 0; d < D - 1; ++d) acc += qrow[d] * kr[d];"),
+    ("wrong_key_row", "const double* kr = K + j * D;", "const double* kr = K + ((j + 1) % Sk) * D;"),
+    ("transposed_scores", "row_attention(Qd + i * D, Kd, Vd,",
+     "row_attention(Sq == Sk ? Kd + i * D : Qd + i * D, Sq == Sk ? Qd : Kd, Vd,"),
+    ("scale_missing", "srow[j] = scale * acc;", "srow[j] = acc;"),
+    ("exp_sign", "double p = exp(srow[j] - m);", "double p = exp(m - srow[j]);"),
+    ("exp_without_max", "double p = exp(srow[j] - m);", "double p = exp(srow[j]);"),
+    ("not_normalised", "double p = srow[j] / l;", "double p = srow[j];"),
+    ("v_rows_reversed", "const double* vr = V + j * D;", "const double* vr = V + (Sk - 1 - j) * D;"),
+    ("lse_drops_max", "*lse_out = m + log(l);", "*lse_out = log(l);"),
+    ("lse_log2", "*lse_out = m + log(l);", "*lse_out = m + log2(l);"),
+    ("rows_wrong_query", "ora_decode(q + rows[r] * D, Qr, D, dtype);",
+     "ora_decode(q + (rows[r] ^ 1) * D, Qr, D, dtype);"),
+]
+
+
+def _mutant_source(orig: str, name: str, old: str, new: str) -> str:
+    assert orig.count(old) == 1, (name, orig.count(old))
+    return orig.replace(old, new)
+
+
+@pytest.fixture(scope="module")
+def workdir():
+    d = tempfile.mkdtemp(prefix="oracle_mutants_")
+    yield d
+    shutil.rmtree(d, ignore_errors=True)
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutant_is_caught(workdir, name, old, new):
+    orig = open(obuild.SRC).read()
+    src = os.path.join(workdir, name + ".c")
+    with open(src, "w") as f:
+        f.write(_mutant_source(orig, name, old, new))
+    lib_path = obuild.build(src, os.path.join(workdir, "lib" + name + ".so"),
+                            extra_flags=("-Wno-unused-parameter", "-Wno-unused-variable"))
+    lib = oracle.load(lib_path)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(lib)
+        except AssertionError:
+            caught.append(pin.__name__)
+        except Exception as e:  # a crash inside a pin also counts as detection
+            caught.append("%s(%s)" % (pin.__name__, type(e).__name__))
+    assert caught, "mutant %s passed every pin" % name
