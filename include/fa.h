@@ -1,0 +1,129 @@
+/*
+ * fa.h -- C ABI of the fused attention forward for AMD MI355X (gfx950).
+ *
+ * The operation is the FlashAttention-2 forward pass: for each batch b and
+ * head h,
+ *
+ *     O[b,h] = softmax(scale * Q[b,h] K[b,h]^T  [+ causal mask]) V[b,h]
+ *     lse[b,h,i] = ln sum_{j visible to i} exp(scale * q_i . k_j)
+ *
+ * computed tile by tile with an online softmax so that the S x S score
+ * matrix never reaches device memory.
+ *
+ * Passages this follows:
+ *   - attention formula, tiling of Q into row blocks with K/V column blocks
+ *     streamed past it, the online running-max / running-sum update, and
+ *     the fusion of the two products and the softmax into one operator:
+ *     "FlashAttention-2 on Ascend NPU: how ops-transformer reaches 3x"
+ *     (2048ai.net), sections 1, 2.1, 2.2 (online softmax equation), 2.3;
+ *   - the [batch, heads, seq_len, head_dim] row-major contiguous layout
+ *     with 128-byte-aligned strides, the causal mode in which a position
+ *     sees only itself and earlier tokens, and skipping of K/V tiles that
+ *     lie wholly beyond a Q tile's last row: "catlass FlashAttention tuning
+ *     for a 13B service" (gsyq.cn), sections "data layout" and "Causal Mask
+ *     implementation" (mode 2);
+ *   - the softmax scale passed explicitly as 1/sqrt(head_dim): "cann-
+ *     learning-hub FlashAttention learning path" (omica.com.cn), steps three
+ *     and five;
+ *   - a launcher that takes a stream and returns a status code:
+ *     "Analysis of the CANN ops-transformer FlashAttention operator"
+ *     (lanjinlin.com.cn), "kernel entry" (unlike that launcher, this one
+ *     never synchronises the stream).
+ *
+ * Threading and ownership: every entry point is stateless and thread-safe.
+ * The caller owns every buffer; the library never allocates, frees or
+ * synchronises.
+ */
+#ifndef TILED_ATTENTION_15_FA_H
+#define TILED_ATTENTION_15_FA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of Q, K, V and O. */
+typedef enum {
+    FA_F16 = 0,  /* IEEE binary16 */
+    FA_BF16 = 1  /* bfloat16 */
+} fa_dtype;
+
+/* Status codes.  Every check runs on the host before anything is launched;
+ * a non-FA_OK return means nothing was enqueued. */
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,         /* q, k, v or o is NULL */
+    FA_ERR_SHAPE = 2,        /* B, H or S < 1, or a size beyond the limits below */
+    FA_ERR_UNSUPPORTED = 3,  /* D not in {64, 128}, or dtype not an fa_dtype */
+    FA_ERR_ALIGN = 4,        /* a pointer is not 16-byte aligned */
+    FA_ERR_SCALE = 5,        /* scale is not finite or not > 0 */
+    FA_ERR_HIP = 6,          /* the HIP runtime reported an error at launch */
+    FA_ERR_ALIAS = 7         /* o or lse overlaps q, k or v, or o overlaps lse */
+} fa_status;
+
+/*
+ * fa_fwd -- fused attention forward.
+ *
+ *   q, k, v  device pointers, each [B, H, S, D] contiguous row-major of
+ *            `dtype` (element (b,h,i,d) at ((b*H + h)*S + i)*D + d).
+ *   o        device pointer, [B, H, S, D] contiguous, same dtype; written.
+ *   lse      device pointer to [B, H, S] contiguous fp32 (natural-log
+ *            log-sum-exp of each row's visible scaled scores), or NULL to
+ *            skip it.
+ *   B, H, S  batch, heads, sequence length (>= 1; any S, not only multiples
+ *            of the tile; B*H*S*D < 2^40 and S*D*2 bytes < 2^31).
+ *   D        head dimension, 64 or 128.
+ *   scale    softmax scale applied to q.k (callers normally pass
+ *            1/sqrt(D)); finite and > 0.
+ *   causal   0: every key visible; nonzero: key j visible to query i iff
+ *            j <= i (the diagonal included).
+ *   dtype    an fa_dtype.
+ *   stream   hipStream_t to enqueue on, or NULL for the default stream.
+ *
+ * Numerics: products on the matrix cores with fp16/bf16 inputs and fp32
+ * accumulation; softmax in fp32 with base-2 exponentials; probabilities
+ * rounded to `dtype` before the second product; O rounded to `dtype` with
+ * round-to-nearest-even.  Results are bitwise reproducible run to run (no
+ * atomics).  Non-finite inputs propagate to the outputs they touch.
+ *
+ * Returns an fa_status.  Asynchronous: a fault inside the kernel surfaces at
+ * the caller's next synchronisation, not here.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int S, int D, float scale, int causal, int dtype,
+           void* stream);
+
+/* Human-readable text of a status code (static storage; never NULL). */
+const char* fa_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int fa_version(void);
+
+/*
+ * fa_fwd_plan -- the launch fa_fwd would make, without launching it.
+ *
+ * Fills (each pointer may be NULL):
+ *   block_q    query rows per workgroup (B_r),
+ *   block_kv   keys per K/V tile (B_c),
+ *   grid       workgroups launched (B * H * ceil(S / B_r)),
+ *   tiles      (query block, K/V tile) pairs the kernel processes: for a
+ *              causal call, only the tiles whose first key does not lie
+ *              beyond the query block's last row, i.e. per query block
+ *              min(ceil(S / B_c), ceil(min(S, (qb+1)*B_r) / B_c)).
+ * Same validation and return codes as fa_fwd (no device pointers are
+ * needed: they are not inspected).  Host only; makes no HIP call.
+ * Follows the tile-count and block-count arithmetic of "FlashAttention-2 on
+ * Ascend NPU: how ops-transformer reaches 3x" (2048ai.net), section 3.2
+ * (ceiling division of the sequence by the block sizes) and the skip rule
+ * of "catlass FlashAttention tuning for a 13B service" (gsyq.cn), section
+ * "Causal Mask implementation".
+ */
+int fa_fwd_plan(int B, int H, int S, int D, int causal, int dtype,
+                int* block_q, int* block_kv, int64_t* grid, int64_t* tiles);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TILED_ATTENTION_15_FA_H */

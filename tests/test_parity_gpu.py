@@ -1,0 +1,213 @@
+"""GPU parity: the HIP kernel through the C ABI against the fp64 oracle.
+
+Small and ragged shapes are compared element by element on every output;
+the five workload shapes are compared on sampled rows that the oracle
+evaluates one by one, in the same launch configuration the benchmark uses.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import parity
+import tiled_attention_15_amd as fa
+from workloads import WORKLOADS, bits, make_inputs, softmax_scale, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def run_gpu(q, k, v, causal, scale=None, return_lse=True):
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale, return_lse=return_lse)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def to64(t):
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def full_check(B, H, S, D, dtype, causal, seed, q_mult=1.0):
+    q, k, v = make_inputs(B, H, S, D, dtype, seed=seed, q_mult=q_mult)
+    scale = softmax_scale(D)
+    say("case", B, H, S, D, dtype, "causal" if causal else "full", "seed", seed)
+    o, lse = run_gpu(q, k, v, causal, scale)
+    o_ref, lse_ref = oracle.attention_fwd(bits(q), bits(k), bits(v), scale=scale, causal=causal,
+                                          dtype=dtype)
+    return parity.assert_parity(to64(o), to64(lse), o_ref, lse_ref, dtype,
+                                "B%d H%d S%d D%d %s causal=%s" % (B, H, S, D, dtype, causal))
+
+
+ODD_S = [1, 2, 17, 63, 64, 65, 127, 255, 256, 257, 1000]
+
+
+@pytest.mark.parametrize("S", ODD_S)
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_odd_shapes_f16(S, D, causal):
+    full_check(1, 2, S, D, "f16", causal, seed=100 + S)
+
+
+@pytest.mark.parametrize("S", ODD_S)
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_odd_shapes_bf16(S, D, causal):
+    full_check(2, 1, S, D, "bf16", causal, seed=200 + S)
+
+
+@pytest.mark.parametrize("S,causal", [(777, True), (1536, False), (1300, True)])
+def test_several_blocks_ragged(S, causal):
+    # several query blocks, several K/V tiles, a ragged tail; Q x4 stresses the range
+    full_check(2, 3, S, 128, "bf16", causal, seed=300 + S, q_mult=4.0)
+    full_check(1, 3, S, 64, "f16", causal, seed=400 + S)
+
+
+def test_tiny_workload_full():
+    w = WORKLOADS["tiny_noncausal_1x2x256x64_f16"]
+    full_check(w.B, w.H, w.S, w.D, w.dtype, w.causal, w.seed, w.q_mult)
+
+
+def sample_rows(B, H, S, n_random=48, seed=0):
+    rng = np.random.default_rng(seed)
+    heads = sorted({0, (B * H) // 2, B * H - 1})
+    fixed = [0, 1, 31, 32, 63, 64, 65, 127, 128, 255, 256, 257, 511, 512, S // 2, S - 257,
+             S - 256, S - 65, S - 64, S - 2, S - 1]
+    rows = []
+    for bh in heads:
+        rs = set(r for r in fixed if 0 <= r < S) | set(rng.integers(0, S, n_random).tolist())
+        rows += [bh * S + r for r in sorted(rs)]
+    return np.array(rows, dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_sampled_rows(name):
+    w = WORKLOADS[name]
+    q, k, v = workload_inputs(w)
+    say("workload", name)
+    o, lse = run_gpu(q, k, v, w.causal, w.scale)
+    assert tuple(o.shape) == (w.B, w.H, w.S, w.D)
+    rows = sample_rows(w.B, w.H, w.S, seed=w.seed)
+    o_ref, lse_ref = oracle.attention_rows(bits(q), bits(k), bits(v), rows, scale=w.scale,
+                                           causal=w.causal, dtype=w.dtype)
+    og = to64(o).reshape(-1, w.D)[rows]
+    lg = to64(lse).reshape(-1)[rows]
+    st = parity.assert_parity(og, lg, o_ref, lse_ref, w.dtype, name)
+    say(name, st)
+    # every output finite at full size
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+
+
+def test_pages_fp16_bound_on_llama_shape():
+    """The pages' own check on this shape: fused vs standard attention max
+    difference below 1e-3 (fp16, 1x32x2048x128, scale 1/sqrt(128))."""
+    import json, os
+    facts = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_facts.json")))
+    bound = facts["fp16_max_abs_diff_vs_sdpa"]["value"]
+    w = WORKLOADS["llama_noncausal_1x32x2048x128_f16"]
+    assert [w.B, w.H, w.S, w.D] == facts["fp16_max_abs_diff_vs_sdpa"]["shape"]
+    q, k, v = workload_inputs(w)
+    o, _ = run_gpu(q, k, v, False, w.scale)
+    rows = sample_rows(w.B, w.H, w.S, n_random=96, seed=7)
+    o_ref, _ = oracle.attention_rows(bits(q), bits(k), bits(v), rows, scale=w.scale, causal=False,
+                                     dtype="f16")
+    assert np.max(np.abs(to64(o).reshape(-1, w.D)[rows] - o_ref)) < bound
+
+
+def test_causal_output_shape_from_pages():
+    import json, os
+    facts = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_facts.json")))
+    f = facts["causal_output_shape"]
+    B, H, S, D = f["input_shape"]
+    q, k, v = make_inputs(B, H, S, D, "f16", seed=9)
+    o, lse = run_gpu(q, k, v, True, softmax_scale(D))
+    assert list(o.shape) == f["value"] and list(lse.shape) == [B, H, S]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_q_zero_gives_mean_of_visible_v(dtype, causal):
+    B, H, S, D = 1, 2, 300, 128
+    _, k, v = make_inputs(B, H, S, D, dtype, seed=21)
+    q = torch.zeros_like(k)
+    o, lse = run_gpu(q, k, v, causal, softmax_scale(D))
+    V = v.to(torch.float64).numpy()
+    n = np.arange(1, S + 1) if causal else np.full(S, S)
+    mean = (np.cumsum(V, axis=2) / n[:, None]) if causal else np.broadcast_to(V.mean(axis=2, keepdims=True), V.shape)
+    parity.assert_parity(to64(o), to64(lse), mean, np.broadcast_to(np.log(n), (B, H, S)), dtype, "q=0")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_causal_row0_is_v0_exactly(dtype):
+    q, k, v = make_inputs(2, 2, 129, 64, dtype, seed=22, q_mult=4.0)
+    o, lse = run_gpu(q, k, v, True, softmax_scale(64))
+    assert torch.equal(o[:, :, 0, :].cpu(), v[:, :, 0, :])
+    want = softmax_scale(64) * (q[:, :, 0, :].double() * k[:, :, 0, :].double()).sum(-1)
+    assert torch.allclose(lse[:, :, 0].cpu().double(), want, rtol=0, atol=1e-4)
+
+
+def test_bitwise_deterministic():
+    q, k, v = make_inputs(1, 8, 2000, 128, "bf16", seed=23)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    outs = []
+    for _ in range(3):
+        o, lse = fa.forward(qd, kd, vd, causal=True)
+        torch.cuda.synchronize()
+        outs.append((o.clone(), lse.clone()))
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+
+
+def test_guard_bands_untouched():
+    B, H, S, D = 1, 2, 333, 64
+    q, k, v = make_inputs(B, H, S, D, "f16", seed=24)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    n, pad = B * H * S * D, 4096
+    obuf = torch.full((n + 2 * pad,), -777.0, dtype=torch.float16, device=DEV)
+    lbuf = torch.full((B * H * S + 2 * pad,), -999.0, dtype=torch.float32, device=DEV)
+    o = obuf[pad:pad + n].view(B, H, S, D)
+    lse = lbuf[pad:pad + B * H * S].view(B, H, S)
+    fa.forward(qd, kd, vd, causal=False, out=o, lse_out=lse)
+    torch.cuda.synchronize()
+    assert (obuf[:pad] == -777.0).all() and (obuf[pad + n:] == -777.0).all()
+    assert (lbuf[:pad] == -999.0).all() and (lbuf[pad + B * H * S:] == -999.0).all()
+    o_ref, l_ref = oracle.attention_fwd(bits(q), bits(k), bits(v), scale=softmax_scale(D),
+                                        causal=False, dtype="f16")
+    parity.assert_parity(to64(o), to64(lse), o_ref, l_ref, "f16", "guard bands")
+
+
+def test_null_lse_and_side_stream():
+    q, k, v = make_inputs(1, 4, 700, 128, "f16", seed=25)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o1, l1 = fa.forward(qd, kd, vd, causal=True)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o2, l2 = fa.forward(qd, kd, vd, causal=True, return_lse=False)
+    s.synchronize()
+    assert l2 is None
+    assert torch.equal(o1, o2)
+    # direct ABI call with an explicit stream handle and a null lse
+    o3 = torch.empty_like(qd)
+    st = fa.fa_fwd(qd, kd, vd, o3, None, 1, 4, 700, 128, softmax_scale(128), 1, fa.F16, s)
+    assert st == 0
+    s.synchronize()
+    assert torch.equal(o1, o3)
+
+
+def test_wrong_scale_is_detected():
+    """Scaling by 1/sqrt(S) instead of 1/sqrt(D) (the misuse the pages warn
+    about) must fail parity against the correctly scaled oracle."""
+    B, H, S, D = 1, 2, 256, 64
+    q, k, v = make_inputs(B, H, S, D, "f16", seed=26)
+    o, lse = run_gpu(q, k, v, False, 1.0 / math.sqrt(S))
+    o_ref, l_ref = oracle.attention_fwd(bits(q), bits(k), bits(v), scale=softmax_scale(D),
+                                        causal=False, dtype="f16")
+    assert not parity.ok(parity.compare(to64(o), to64(lse), o_ref, l_ref, "f16"))

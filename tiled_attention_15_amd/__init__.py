@@ -1,0 +1,144 @@
+"""Fused attention forward for AMD MI355X (gfx950): Python binding.
+
+A thin ctypes layer over the C ABI in include/fa.h (libfa_hip.so, built from
+csrc/ by build.py).  The functions named after the ABI entry points only
+marshal arguments; every step of the computation runs in the HIP kernels.
+PyTorch is used for device memory and streams only.
+
+There is no fallback: if the HIP library is missing or cannot be loaded,
+every call raises.
+"""
+import ctypes
+import math
+import os
+
+__all__ = ["FaError", "fa_fwd", "fa_fwd_plan", "fa_status_string", "fa_version", "forward",
+           "library_path", "F16", "BF16", "STATUS"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libfa_hip.so")
+
+F16, BF16 = 0, 1
+STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED",
+          4: "FA_ERR_ALIGN", 5: "FA_ERR_SCALE", 6: "FA_ERR_HIP", 7: "FA_ERR_ALIAS"}
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status, where="fa_fwd"):
+        self.status = status
+        super().__init__("%s failed: %s (%s)" % (where, STATUS.get(status, status),
+                                                 fa_status_string(status)))
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError("HIP library %s is not built; run tiled_attention_15_amd/build.py "
+                          "(or __graft_entry__.build())" % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = i
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.fa_fwd_plan.argtypes = [i, i, i, i, i, i, ip, ip, i64p, i64p]
+    lib.fa_fwd_plan.restype = i
+    _lib = lib
+    return lib
+
+
+def _ptr(x):
+    """A device address from an int, None or a tensor (its data_ptr)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x or None
+    return x.data_ptr() or None
+
+
+def _stream(s):
+    """A hipStream_t from None, an int handle or a torch stream."""
+    if s is None or isinstance(s, int):
+        return s or None
+    return s.cuda_stream or None
+
+
+def fa_fwd(q, k, v, o, lse, B, H, S, D, scale, causal, dtype, stream):
+    """The ABI call fa_fwd; pointers may be ints or tensors.  Returns the status."""
+    return _load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(S),
+                          int(D), ctypes.c_float(scale), int(bool(causal)), int(dtype),
+                          _stream(stream))
+
+
+def fa_status_string(status):
+    return _load().fa_status_string(int(status)).decode()
+
+
+def fa_version():
+    return _load().fa_version()
+
+
+def fa_fwd_plan(B, H, S, D, causal, dtype):
+    """The ABI call fa_fwd_plan: (block_q, block_kv, grid, tiles); raises on a bad shape."""
+    bq, bkv = ctypes.c_int(), ctypes.c_int()
+    grid, tiles = ctypes.c_int64(), ctypes.c_int64()
+    st = _load().fa_fwd_plan(int(B), int(H), int(S), int(D), int(bool(causal)), int(dtype),
+                             ctypes.byref(bq), ctypes.byref(bkv), ctypes.byref(grid),
+                             ctypes.byref(tiles))
+    if st != 0:
+        raise FaError(st, "fa_fwd_plan")
+    return bq.value, bkv.value, grid.value, tiles.value
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float16:
+        return F16
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("fa: unsupported dtype %s (float16 or bfloat16)" % t.dtype)
+
+
+def forward(q, k, v, causal=False, scale=None, return_lse=True, out=None, lse_out=None):
+    """Attention forward on contiguous [B, H, S, D] GPU tensors.
+
+    Returns (o, lse) with o like q and lse float32 [B, H, S] (None when
+    return_lse is False).  scale defaults to 1/sqrt(D).  Enqueued on the
+    current torch stream; no synchronisation."""
+    import torch
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("fa: q, k, v must share one [B, H, S, D] shape")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("fa: tensors must be on the GPU")
+    if not (q.device == k.device == v.device):
+        raise ValueError("fa: tensors must be on one device")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("fa: q, k, v must share one dtype")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("fa: tensors must be contiguous [B, H, S, D]")
+    B, H, S, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = out if out is not None else torch.empty_like(q)
+    lse = None
+    if return_lse:
+        lse = lse_out if lse_out is not None else torch.empty(
+            (B, H, S), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream().cuda_stream
+    st = fa_fwd(q, k, v, o, lse, B, H, S, D, scale, causal, _dtype_code(q), stream)
+    if st != 0:
+        raise FaError(st)
+    return o, lse

@@ -1,0 +1,51 @@
+"""Compile the HIP kernels and the C ABI into tiled_attention_15_amd/libfa_hip.so.
+
+hipcc cross-compiles for gfx950 without a GPU present.  Packed-fp32 VALU
+instructions are disabled for all device code.
+"""
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libfa_hip.so")
+SOURCES = [os.path.join(CSRC, "fa_api.cpp"), os.path.join(CSRC, "fa_fwd_kernel.hip")]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+
+def hipcc_flags(extra=()):
+    return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
+            "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wall", *extra]
+
+
+def build(out=LIB, extra=(), verbose=False):
+    """Build the shared library (always recompiles) and return its path."""
+    objs = []
+    tmpdir = os.path.join(PKG, "_build")
+    os.makedirs(tmpdir, exist_ok=True)
+    for src in SOURCES:
+        obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
+        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        cmd = [HIPCC, *hipcc_flags(extra), *lang, "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd))
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("hipcc failed for %s:\n%s" % (src, r.stderr))
+        objs.append(obj)
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n%s" % r.stderr)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))
