@@ -39,7 +39,8 @@ def build(out=LIB, extra=(), verbose=False):
             raise RuntimeError("hipcc failed for %s:\n%s" % (src, r.stderr))
         objs.append(obj)
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
+    # --no-undefined: a kernel whose host stub failed to instantiate must fail the build
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Wl,--no-undefined", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s" % r.stderr)

@@ -1,8 +1,8 @@
 // fa_fwd_kernel.hip -- fused attention forward for gfx950 (MI355X).
 //
-// One workgroup owns a block of B_r = 32 * NW query rows of one (batch, head);
-// each of its NW wavefronts owns 32 rows.  K/V tiles of B_c = 64 keys stream
-// through double-buffered LDS.  Per tile and wave:
+// One workgroup owns a block of B_r = 256 query rows of one (batch, head);
+// each of its 8 wavefronts owns 32 rows.  K/V tiles of B_c = 64 keys stream
+// through LDS.  Per tile and wave:
 //   S^T = K_tile . Q_w^T    on the matrix cores (v_mfma_f32_32x32x16_{f16,bf16}),
 //   online softmax on S     (fp32, base-2 exponentials, scale*log2(e) folded in),
 //   O^T += V_tile^T . P^T   on the matrix cores, P taken straight from registers.
@@ -151,200 +151,332 @@ __device__ __forceinline__ void schedule(int wg, int nqb, int BH, bool causal, i
     qb = causal ? (nqb - 1 - slot) : slot;
 }
 
-template <int D, int DT, bool CAUSAL, int NW>
-__global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(FwdParams p) {
-    constexpr int NT = NW * 64;           // threads
-    constexpr int BR = NW * 32;           // query rows per workgroup
-    constexpr int DC = D / 16;            // 16-wide d chunks (k steps of S^T)
-    constexpr int DB = D / 32;            // 32-wide d blocks (output tiles)
+// ---------------------------------------------------------------------------
+// Ping-pong schedule.  The eight wavefronts form two groups of four (waves w
+// and w + 4 share a SIMD) that alternate between a matrix phase (P_{t-1} V_{t-1}
+// and K_t Q^T on the matrix cores, operands from LDS) and a softmax phase
+// (mask, max, exp2, sum, packing of P_t, all VALU).  While one wave of a SIMD
+// runs its matrix phase the other runs its softmax phase, so the matrix core
+// and the vector ALU work at the same time instead of in turn.  A workgroup
+// barrier separates the phases; the matrix phase raises the wave's issue
+// priority.
+//
+// K/V tiles stream into a ring of four LDS slots with direct global->LDS
+// buffer loads issued two steps ahead: the loads of tile t+2 are issued at
+// the start of step t into the slot that held tile t-2 (whose last reads
+// ended with step t-1), and each wave waits for its loads of tile t+1 at the
+// end of step t.  The loads are written as inline assembly so that the
+// compiler, which cannot tell the slots apart, does not make every
+// transposing LDS read wait for all of them.
+// ---------------------------------------------------------------------------
+
+// One 16-byte-per-lane direct load into LDS: lane l's 16 bytes at voffset go
+// to LDS address lds_addr + 16*l.  lds_addr must be wave-uniform.
+__device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t voffset, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voffset), "s"(rsrc), "s"(lds_addr) : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(n) alone (gfx9 encoding: vmcnt split over bits 3:0 and
+// 15:14; expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Buffer descriptor as four dwords (for inline assembly).
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffff));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = (int)BUF_FLAGS;
+    return r;
+}
+
+template <int D, int DT, bool CAUSAL>
+__global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
+    constexpr int NW = 8;
+    constexpr int NT = 512;
+    constexpr int BR = 256;
+    constexpr int DC = D / 16;
+    constexpr int DB = D / 32;
     constexpr int TILE_BYTES = BC * D * 2;
-    constexpr int CHUNKS = TILE_BYTES / 16;          // 16-byte chunks per tile
-    constexpr int CPT = CHUNKS / NT;                 // chunks per thread per tensor
+    constexpr int SLOT_BYTES = 2 * TILE_BYTES;      // K tile then V tile
+    constexpr int NSLOT = 4;
+    constexpr int CHUNKS = TILE_BYTES / 16;
+    constexpr int LPT = CHUNKS / NT;                // 16-byte loads per thread per tensor
     static_assert(CHUNKS % NT == 0, "tile must split evenly over threads");
 
-    __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE_BYTES];  // [buf][K,V]
+    __shared__ __attribute__((aligned(16))) char smem[NSLOT * SLOT_BYTES];
 
     const int tid = threadIdx.x;
-    const int wid = tid >> 6;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    const int lq = lane & 31;             // query column within the wave
-    const int g = lane >> 5;              // lane half
+    const int lq = lane & 31;
+    const int g = lane >> 5;
+    const int grp = wid >> 2;
 
     int bh, qb;
     schedule(blockIdx.x, p.nqb, p.BH, CAUSAL, bh, qb);
     const int S = p.S;
     const int q0 = qb * BR;
-    const int qw0 = q0 + wid * 32;        // first query row of this wave
+    const int qw0 = q0 + wid * 32;
     const int64_t head = (int64_t)bh * S * D;
     const uint32_t head_bytes = (uint32_t)S * D * 2;
 
     const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)p.q + head * 2, head_bytes);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)p.k + head * 2, head_bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char*)p.v + head * 2, head_bytes);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc((char*)p.o + head * 2, head_bytes);
+    const i32x4 rk = rsrc_words((const char*)p.k + head * 2, head_bytes);
+    const i32x4 rv = rsrc_words((const char*)p.v + head * 2, head_bytes);
 
-    // Number of K/V tiles this workgroup visits.  Causal: tiles whose first
-    // key lies beyond the block's last row are skipped.
+    // Every wave visits all nt tiles of its workgroup: a wave whose rows end
+    // before a diagonal tile finds it fully masked (probabilities exactly 0),
+    // and the phase barriers would make it wait for that tile anyway.
     const int nkv = (S + BC - 1) / BC;
     int nt = nkv;
-    if (CAUSAL) {
-        const int last = min(S, q0 + BR);
-        nt = min(nkv, (last + BC - 1) / BC);
-    }
-    // Tiles this wave needs (causal: up to its own last row).
-    int nt_w = (qw0 < S) ? nt : 0;
-    if (CAUSAL && qw0 < S) nt_w = min(nt, (min(S, qw0 + 32) + BC - 1) / BC);
+    if (CAUSAL) nt = min(nkv, (min(S, q0 + BR) + BC - 1) / BC);
 
-    // ---- Q fragments: B operand of S^T, lane (lq, g): d = 16c + 8g + [0,8)
+    // Direct-to-LDS loads: instruction i of wave w fills LDS chunks
+    // (i*NW + w)*64 + lane of a tile; each lane fetches the global chunk that
+    // the swizzled layout puts there.
+    const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
+    uint32_t ksrc[LPT], vsrc[LPT];
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+        const int c = (i * NW + wid) * 64 + lane;
+        const int row = c / (D / 8), cl = c % (D / 8);
+        ksrc[i] = (uint32_t)(row * D + ((cl ^ kswz<D>(row)) << 3)) * 2;
+        const int gc = (((cl >> 2) ^ vseg_swz<D>(row)) << 2) | (cl & 3);
+        vsrc[i] = (uint32_t)(row * D + (gc << 3)) * 2;
+    }
+    auto issue_tile = [&](int t) {
+        const uint32_t tb = (uint32_t)t * TILE_BYTES;
+        const uint32_t sb = lds0 + (uint32_t)(t & (NSLOT - 1)) * SLOT_BYTES;
+#pragma unroll
+        for (int i = 0; i < LPT; ++i) {
+            const uint32_t dst = sb + (uint32_t)(i * NW + wid) * 1024;
+            lds_dma16(rk, ksrc[i] + tb, dst);
+            lds_dma16(rv, vsrc[i] + tb, dst + TILE_BYTES);
+        }
+    };
+
     i32x4 qf[DC];
 #pragma unroll
     for (int c = 0; c < DC; ++c)
         qf[c] = __builtin_amdgcn_raw_buffer_load_b128(rq, ((qw0 + lq) * D + 16 * c + 8 * g) * 2, 0, 0);
 
-    // ---- per-thread K/V staging registers and their LDS destinations
-    i32x4 kst[CPT], vst[CPT];
-    auto gload = [&](int t) {
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int x = tid + i * NT;          // chunk id within tile
-            const int row = x / (D / 8), ch = x % (D / 8);
-            const uint32_t off = ((uint32_t)(t * BC + row) * D + ch * 8) * 2;
-            kst[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
-            vst[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
-        }
-    };
-    auto lstore = [&](int buf) {
-        char* kb = smem + buf * 2 * TILE_BYTES;
-        char* vb = kb + TILE_BYTES;
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int x = tid + i * NT;
-            const int row = x / (D / 8), ch = x % (D / 8);
-            *(i32x4*)(kb + k_lds_off<D>(row, ch)) = kst[i];
-            // a 16-byte V chunk is two 8-byte pieces (d4 = 2ch, 2ch+1), same segment
-            *(i32x4*)(vb + v_lds_off<D>(row, 2 * ch)) = vst[i];
-        }
-    };
-
-    // ---- accumulators and running statistics
     f32x16 oacc[DB];
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[b][i] = 0.0f;
-    float m_run = -INFINITY;   // running max of scale*log2e*s (base-2 units)
-    float l_run = 0.0f;        // this lane's partial row sum (keys of its half)
+    f32x16 s[2];
+    i32x4 pf[4];
+    float m_run = -INFINITY;
+    float l_run = 0.0f;
     const float c2 = p.scale_log2e;
-
-    // K operand row for this lane: pi(lq)
     const int krow = 16 * ((lq >> 2) & 1) + 4 * (lq >> 3) + (lq & 3);
-    // V transposed-read addressing for this lane (see header comment)
-    const int vkey = 16 * g + ((lane & 15) >> 2);                           // + 32kb + 8c + 4rr
-    const int vphi = 4 * (lane & 1) + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // + 8db
+    const int vkey = 16 * g + ((lane & 15) >> 2);
+    const int vphi = 4 * (lane & 1) + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
 
-    if (nt > 0) {
-        gload(0);
-        lstore(0);
-    }
-    __syncthreads();
+    // LDS read addresses.  With the swizzles above, every address this lane
+    // reads is (lane base + slot base) XOR (a small per-read constant in bits
+    // that neither base touches) plus a per-read immediate, so a step costs a
+    // handful of XORs instead of dozens of precomputed address registers.
+    const int ks = kswz<D>(krow);
+    const int kbase_l = krow * (2 * D) + ((g ^ (ks & 1)) << 4) + ((ks >> 1) << 5);
+    const int vbase_l = vkey * (2 * D) + (vseg_swz<D>(vkey) << 6) + (vphi << 3);
 
-    for (int t = 0; t < nt; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < nt) gload(t + 1);
-        if (t < nt_w) {
-            const char* kb = smem + buf * 2 * TILE_BYTES;
-            const char* vb = kb + TILE_BYTES;
-            // ---- S^T = K Q^T for the 64 keys of this tile (two 32-key blocks)
-            f32x16 s[2];
+    // Matrix phase pieces: O += P V (V tile of tile t), S = K Q^T (K tile of t).
+    auto pv = [&](int t) {
+        const int vb = (t & (NSLOT - 1)) * SLOT_BYTES + TILE_BYTES + vbase_l;
+        // kc outer, b inner: consecutive MFMAs accumulate into different O
+        // blocks, so none waits for the previous one's result.
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) s[kb2][i] = 0.0f;
-#pragma unroll
-                for (int c = 0; c < DC; ++c) {
-                    const i32x4 a = *(const i32x4*)(kb + k_lds_off<D>(32 * kb2 + krow, 2 * c + g));
-                    s[kb2] = mfma32<DT>(a, qf[c], s[kb2]);
-                }
-            }
-            // ---- mask: causal keys beyond the row, and keys past the end
-            const int key0 = t * BC + 16 * g;  // key of s[kb2][i] is key0 + 32*kb2 + i
-            const int qrow = qw0 + lq;
-            const bool need_mask = (t * BC + BC > S) || (CAUSAL && t * BC + BC - 1 > qw0);
-            if (need_mask) {
-                const int lim = CAUSAL ? min(qrow, S - 1) : S - 1;  // last visible key
-#pragma unroll
-                for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        if (key0 + 32 * kb2 + i > lim) s[kb2][i] = -INFINITY;
-            }
-            // ---- online softmax (base 2)
-            float mx = s[0][0];
-#pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb2][i]);
-            mx = xmax32(mx) * c2;  // c2 > 0, so max commutes with the scaling
-            const bool grow = mx > m_run + RESCALE_THRESHOLD;
-            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-                const float m_new = fmaxf(m_run, mx);
-                const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
-                m_run = m_new;
-                l_run *= alpha;
-#pragma unroll
-                for (int b = 0; b < DB; ++b)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[b][i] *= alpha;
-            }
-            const float mb = (m_run == -INFINITY) ? 0.0f : m_run;
-            float lsum = 0.0f;
-#pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float e = fast_exp2(__builtin_fmaf(s[kb2][i], c2, -mb));
-                    s[kb2][i] = e;
-                    lsum += e;
-                }
-            l_run += lsum;
-            // ---- P as B operand: chunk (kb2, c) holds keys 32kb2 + 16g + 8c + [0,8)
-            i32x4 pf[4];
-#pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    i32x4 w;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        w[e] = pack2<DT>(s[kb2][8 * c + 2 * e], s[kb2][8 * c + 2 * e + 1]);
-                    pf[2 * kb2 + c] = w;
-                }
-            // ---- O^T += V^T P^T
+        for (int kc = 0; kc < 4; ++kc) {
 #pragma unroll
             for (int b = 0; b < DB; ++b) {
-#pragma unroll
-                for (int kc = 0; kc < 4; ++kc) {
-                    const int kb2 = kc >> 1, c = kc & 1;
-                    const int key = 32 * kb2 + 8 * c + vkey;
-                    const int d4 = 8 * b + vphi;
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) i16x4*)(vb + v_lds_off<D>(key, d4)));
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) i16x4*)(vb + v_lds_off<D>(key + 4, d4)));
-                    i32x4 a;
-                    a[0] = __builtin_bit_cast(int, (short __attribute__((ext_vector_type(2)))){lo[0], lo[1]});
-                    a[1] = __builtin_bit_cast(int, (short __attribute__((ext_vector_type(2)))){lo[2], lo[3]});
-                    a[2] = __builtin_bit_cast(int, (short __attribute__((ext_vector_type(2)))){hi[0], hi[1]});
-                    a[3] = __builtin_bit_cast(int, (short __attribute__((ext_vector_type(2)))){hi[2], hi[3]});
-                    oacc[b] = mfma32<DT>(a, pf[kc], oacc[b]);
-                }
+                const int kb2 = kc >> 1, c = kc & 1;
+                const int off = (vb ^ (b << 6)) + (32 * kb2 + 8 * c) * (2 * D);
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4*)(smem + off));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4*)(smem + off + 4 * (2 * D)));
+                i32x4 a;
+                a[0] = __builtin_bit_cast(int, (short __attribute__((ext_vector_type(2)))){lo[0], lo[1]});
+                a[1] = __builtin_bit_cast(int, (short __attribute__((ext_vector_type(2)))){lo[2], lo[3]});
+                a[2] = __builtin_bit_cast(int, (short __attribute__((ext_vector_type(2)))){hi[0], hi[1]});
+                a[3] = __builtin_bit_cast(int, (short __attribute__((ext_vector_type(2)))){hi[2], hi[3]});
+                oacc[b] = mfma32<DT>(a, pf[kc], oacc[b]);
             }
         }
-        if (t + 1 < nt) lstore(buf ^ 1);
-        __syncthreads();
+    };
+    auto qk = [&](int t) {
+        const int kb = (t & (NSLOT - 1)) * SLOT_BYTES + kbase_l;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[kb2][i] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+            const int kc_off = kb ^ (c << 5);
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
+                const i32x4 a = *(const i32x4*)(smem + kc_off + kb2 * 32 * (2 * D));
+                s[kb2] = mfma32<DT>(a, qf[c], s[kb2]);
+            }
+        }
+    };
+
+    // Softmax phase of step t: mask, running max, exponentials, P_t packed.
+    auto swork = [&](int t) {
+        const int key0 = t * BC + 16 * g;
+        const int qrow = qw0 + lq;
+        const bool need_mask = (t * BC + BC > S) || (CAUSAL && t * BC + BC - 1 > qw0);
+        if (need_mask) {
+            const int lim = CAUSAL ? min(qrow, S - 1) : S - 1;
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (key0 + 32 * kb2 + i > lim) s[kb2][i] = -INFINITY;
+        }
+        float mx = s[0][0];
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb2][i]);
+        mx = xmax32(mx) * c2;
+        const bool grow = mx > m_run + RESCALE_THRESHOLD;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int b = 0; b < DB; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[b][i] *= alpha;
+        }
+        const float mb = (m_run == -INFINITY) ? 0.0f : m_run;
+        float lsum = 0.0f;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float e = fast_exp2(__builtin_fmaf(s[kb2][i], c2, -mb));
+                s[kb2][i] = e;
+                lsum += e;
+            }
+        l_run += lsum;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                i32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    w[e] = pack2<DT>(s[kb2][8 * c + 2 * e], s[kb2][8 * c + 2 * e + 1]);
+                pf[2 * kb2 + c] = w;
+            }
+    };
+
+    // Instruction order of a matrix phase (P V then K Q^T: 32 MFMAs, 2*16
+    // transposing V reads then 16 K reads): LDS reads run a few MFMAs ahead
+    // of their use, so the matrix core does not wait on LDS latency.
+    auto mphase_schedule = [&]() {
+        constexpr int MFMA = 0x008, DSR = 0x100;
+        constexpr int PV_N = 4 * DB, QK_N = 2 * DC;         // MFMAs of each product
+        constexpr int AHEAD = 4;                            // MFMAs of lookahead
+        __builtin_amdgcn_sched_group_barrier(DSR, 2 * AHEAD, 0);
+#pragma unroll
+        for (int m = 0; m < PV_N - AHEAD; ++m) {
+            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(DSR, 2, 0);
+        }
+#pragma unroll
+        for (int m = 0; m < AHEAD; ++m) {
+            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(DSR, 1, 0);
+        }
+#pragma unroll
+        for (int m = 0; m < QK_N - AHEAD; ++m) {
+            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(DSR, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(MFMA, AHEAD, 0);
+    };
+    auto mphase = [&](int t) {
+        __builtin_amdgcn_s_setprio(1);
+        pv(t - 1);
+        qk(t);
+        mphase_schedule();
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    // Phase boundaries.  The one in the middle of a step only keeps the two
+    // groups in alternation (no data passes through LDS across it).  The one
+    // ending step t first waits for this wave's loads of tile t+1 (loads
+    // complete in issue order, so at most those of tile t+2 stay in flight),
+    // which together with the barrier publishes tile t+1 to every wave.
+    auto mid_barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto end_barrier = [&](int t) {
+        if (t + 2 < nt) wait_vmcnt<2 * LPT>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
+
+    // Prologue: Q, tile 0 and tile 1 requested; tile 0 (and Q) waited for.
+    issue_tile(0);
+    if (nt > 1) issue_tile(1);
+    end_barrier(-1);
+
+    // The two groups run the same sequence of barriers (two per step for
+    // steps 0 .. nt-1, one for the final step) with their phases swapped.
+    // Step 0: S_0 = K_0 Q^T.  Steps 1 .. nt-1: O += P_{t-1} V_{t-1} and
+    // S_t = K_t Q^T in the matrix phase, softmax of S_t in the other.
+    // Step nt: the last O += P V.
+    if (grp == 0) {
+        if (nt > 2) issue_tile(2);
+        qk(0);
+        mid_barrier();
+        swork(0);
+        end_barrier(0);
+        for (int t = 1; t < nt; ++t) {
+            if (t + 2 < nt) issue_tile(t + 2);
+            mphase(t);
+            mid_barrier();
+            swork(t);
+            end_barrier(t);
+        }
+        pv(nt - 1);
+        mid_barrier();
+    } else {
+        if (nt > 2) issue_tile(2);
+        mid_barrier();
+        qk(0);
+        end_barrier(0);
+        for (int t = 1; t < nt; ++t) {
+            if (t + 2 < nt) issue_tile(t + 2);
+            swork(t - 1);
+            mid_barrier();
+            mphase(t);
+            end_barrier(t);
+        }
+        swork(nt - 1);
+        mid_barrier();
+        pv(nt - 1);
     }
 
-    // ---- epilogue: O /= l, round to dtype, store; lse = (m + log2 l) ln 2
     const float l_tot = xsum32(l_run);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     const int qrow = qw0 + lq;
@@ -366,17 +498,15 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(FwdParams p) {
     }
 }
 
-template <int D, int DT, bool CAUSAL, int NW>
-static hipError_t launch_instance(const FwdParams& p, int64_t grid, hipStream_t stream) {
-    hipLaunchKernelGGL((fa_fwd_kernel<D, DT, CAUSAL, NW>), dim3((unsigned)grid), dim3(NW * 64), 0,
-                       stream, p);
+template <int D, int DT, bool CAUSAL>
+static hipError_t launch_kernel(const FwdParams& p, int64_t grid, hipStream_t stream) {
+    hipLaunchKernelGGL((fa_fwd_kernel<D, DT, CAUSAL>), dim3((unsigned)grid), dim3(512), 0, stream, p);
     return hipGetLastError();
 }
 
 template <int D, int DT>
 static hipError_t launch_c(const FwdParams& p, bool causal, int64_t grid, hipStream_t s) {
-    return causal ? launch_instance<D, DT, true, FA_WAVES>(p, grid, s)
-                  : launch_instance<D, DT, false, FA_WAVES>(p, grid, s);
+    return causal ? launch_kernel<D, DT, true>(p, grid, s) : launch_kernel<D, DT, false>(p, grid, s);
 }
 
 hipError_t launch_fwd(const FwdParams& p, int D, int dtype, bool causal, int64_t grid,

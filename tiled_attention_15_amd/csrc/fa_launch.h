@@ -3,13 +3,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#ifndef FA_WAVES
-#define FA_WAVES 8  // wavefronts per workgroup; each owns 32 query rows
-#endif
-
 namespace fa {
 
-constexpr int kBlockQ = FA_WAVES * 32;  // query rows per workgroup (B_r)
+constexpr int kBlockQ = 256;           // query rows per workgroup (B_r): 8 waves x 32
 constexpr int kBlockKV = 64;            // keys per K/V tile (B_c)
 
 struct FwdParams {
