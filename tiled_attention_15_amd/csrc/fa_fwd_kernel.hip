@@ -162,12 +162,15 @@ __device__ __forceinline__ void schedule(int wg, int nqb, int BH, bool causal, i
 // priority.
 //
 // K/V tiles stream into a ring of four LDS slots with direct global->LDS
-// buffer loads issued two steps ahead: the loads of tile t+2 are issued at
-// the start of step t into the slot that held tile t-2 (whose last reads
-// ended with step t-1), and each wave waits for its loads of tile t+1 at the
-// end of step t.  The loads are written as inline assembly so that the
+// buffer loads issued two steps ahead: the loads of tile t+2 are issued
+// during step t into the slot that held tile t-2 (whose last reads ended with
+// step t-1), and each wave waits for its own loads of tile t+1 at the end of
+// step t.  Group 1 loads the K tiles and group 0 the V tiles, each at the
+// start of its softmax phase, so no matrix phase queues behind load
+// instructions.  The loads are written as inline assembly so that the
 // compiler, which cannot tell the slots apart, does not make every
-// transposing LDS read wait for all of them.
+// transposing LDS read wait for all of them; M0, which they set, is used by
+// nothing else in this kernel.
 // ---------------------------------------------------------------------------
 
 // One 16-byte-per-lane direct load into LDS: lane l's 16 bytes at voffset go
@@ -239,28 +242,32 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
     int nt = nkv;
     if (CAUSAL) nt = min(nkv, (min(S, q0 + BR) + BC - 1) / BC);
 
-    // Direct-to-LDS loads: instruction i of wave w fills LDS chunks
-    // (i*NW + w)*64 + lane of a tile; each lane fetches the global chunk that
-    // the swizzled layout puts there.
+    // Direct-to-LDS loads.  Group 1 loads every K tile and group 0 every V
+    // tile, each at the start of its softmax phase, so no wave's matrix phase
+    // queues behind load instructions.  Instruction i of wave w (w within its
+    // group) fills LDS chunks (i*4 + w)*64 + lane of the tile; each lane
+    // fetches the global chunk that the swizzled layout puts there.
     const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
-    uint32_t ksrc[LPT], vsrc[LPT];
+    uint32_t src[2 * LPT];
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-        const int c = (i * NW + wid) * 64 + lane;
+    for (int i = 0; i < 2 * LPT; ++i) {
+        const int c = (i * 4 + (wid & 3)) * 64 + lane;
         const int row = c / (D / 8), cl = c % (D / 8);
-        ksrc[i] = (uint32_t)(row * D + ((cl ^ kswz<D>(row)) << 3)) * 2;
-        const int gc = (((cl >> 2) ^ vseg_swz<D>(row)) << 2) | (cl & 3);
-        vsrc[i] = (uint32_t)(row * D + (gc << 3)) * 2;
+        if (grp != 0) {
+            src[i] = (uint32_t)(row * D + ((cl ^ kswz<D>(row)) << 3)) * 2;
+        } else {
+            const int gc = (((cl >> 2) ^ vseg_swz<D>(row)) << 2) | (cl & 3);
+            src[i] = (uint32_t)(row * D + (gc << 3)) * 2;
+        }
     }
+    const i32x4 rkv = grp != 0 ? rk : rv;
+    const uint32_t part = grp != 0 ? 0u : (uint32_t)TILE_BYTES;
     auto issue_tile = [&](int t) {
         const uint32_t tb = (uint32_t)t * TILE_BYTES;
-        const uint32_t sb = lds0 + (uint32_t)(t & (NSLOT - 1)) * SLOT_BYTES;
+        const uint32_t sb = lds0 + (uint32_t)(t & (NSLOT - 1)) * SLOT_BYTES + part;
 #pragma unroll
-        for (int i = 0; i < LPT; ++i) {
-            const uint32_t dst = sb + (uint32_t)(i * NW + wid) * 1024;
-            lds_dma16(rk, ksrc[i] + tb, dst);
-            lds_dma16(rv, vsrc[i] + tb, dst + TILE_BYTES);
-        }
+        for (int i = 0; i < 2 * LPT; ++i)
+            lds_dma16(rkv, src[i] + tb, sb + (uint32_t)(i * 4 + (wid & 3)) * 1024);
     };
 
     i32x4 qf[DC];
@@ -446,15 +453,15 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
     // S_t = K_t Q^T in the matrix phase, softmax of S_t in the other.
     // Step nt: the last O += P V.
     if (grp == 0) {
-        if (nt > 2) issue_tile(2);
         qk(0);
         mid_barrier();
+        if (nt > 2) issue_tile(2);
         swork(0);
         end_barrier(0);
         for (int t = 1; t < nt; ++t) {
-            if (t + 2 < nt) issue_tile(t + 2);
             mphase(t);
             mid_barrier();
+            if (t + 2 < nt) issue_tile(t + 2);
             swork(t);
             end_barrier(t);
         }
