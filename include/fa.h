@@ -59,7 +59,9 @@ typedef enum {
     FA_ERR_ALIGN = 4,        /* a pointer is not 16-byte aligned */
     FA_ERR_SCALE = 5,        /* scale is not finite or not > 0 */
     FA_ERR_HIP = 6,          /* the HIP runtime reported an error at launch */
-    FA_ERR_ALIAS = 7         /* o or lse overlaps q, k or v, or o overlaps lse */
+    FA_ERR_ALIAS = 7,        /* o or lse overlaps q, k or v, or o overlaps lse */
+    FA_ERR_STRIDE = 8        /* a stride is negative, not a multiple of 8
+                                elements, or makes o overlap itself */
 } fa_status;
 
 /*
@@ -93,6 +95,47 @@ typedef enum {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int S, int D, float scale, int causal, int dtype,
            void* stream);
+
+/*
+ * fa_fwd_strided -- the same forward for strided tensors and for query and
+ * key sequences of different lengths (cross attention, a query block
+ * attending to a longer key sequence).
+ *
+ *   q        [B, H, Sq, D]: element (b,h,i,d) at
+ *            q_strides[0]*b + q_strides[1]*h + q_strides[2]*i + d
+ *            (element strides; the head dimension is contiguous).
+ *   k, v     [B, H, Sk, D] with k_strides / v_strides likewise.  A head
+ *            stride of 0 shares one K (or V) between all heads of a batch.
+ *   o        [B, H, Sq, D] with o_strides; written.  Its strides must not
+ *            make two elements share an address.
+ *   lse      [B, H, Sq] contiguous fp32, or NULL.
+ *   Sq, Sk   query and key/value rows per head (>= 1).
+ *   causal   0: every key visible; nonzero: key j visible to query i iff
+ *            j <= i + (Sk - Sq), i.e. the last query row sees every key (for
+ *            Sq == Sk this is fa_fwd's causal mask).  A row that sees no key
+ *            (Sq > Sk) gets O = 0 and lse = -inf.
+ *   other arguments as for fa_fwd.
+ *
+ * Strides (in elements) must be >= 0 and multiples of 8 (16-byte rows); a
+ * row stride must be >= D.  Per tensor and head, the rows a query block or
+ * key tile can address must span fewer than 2^31 bytes:
+ * (round_up(S, 256) + 64) * row_stride * 2 < 2^31.
+ *
+ * The causal reading for Sq != Sk (bottom-right alignment) extends the
+ * pages' rule that a position sees only itself and earlier tokens ("catlass
+ * FlashAttention tuning for a 13B service" (gsyq.cn), "Causal Mask
+ * implementation") to a query block that ends at the end of the keys; the
+ * need for unequal lengths is named by the cross-attention use case of
+ * "Analysis of the CANN ops-transformer FlashAttention operator"
+ * (lanjinlin.com.cn), "application scenarios".
+ *
+ * Returns an fa_status (FA_ERR_STRIDE for the stride rules above).
+ */
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Sq, int Sk, int D,
+                   const int64_t* q_strides, const int64_t* k_strides,
+                   const int64_t* v_strides, const int64_t* o_strides,
+                   float scale, int causal, int dtype, void* stream);
 
 /* Human-readable text of a status code (static storage; never NULL). */
 const char* fa_status_string(int status);

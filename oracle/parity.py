@@ -8,6 +8,9 @@ output dtype, which no kernel that returns O in that dtype can avoid (at
 |O| >= 4 the bf16 spacing is 2^-5, whose half alone exceeds 1e-2).  The raw
 max |dO| is reported beside it.
 LSE: |lse_gpu - lse_ref| <= 1e-4 * max(1, |lse_ref|).
+Infinite values (lse = -inf for a row that sees no key) must match exactly;
+such mismatches are counted separately because the differences they give
+are not finite.
 """
 import numpy as np
 
@@ -27,6 +30,11 @@ def ulp(x, dtype):
 
 def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype):
     """Return a dict of error statistics (no assertion)."""
+    with np.errstate(invalid="ignore"):      # inf - inf where both sides are -inf
+        return _compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype)
+
+
+def _compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype):
     o_gpu = np.asarray(o_gpu, dtype=np.float64)
     o_ref = np.asarray(o_ref, dtype=np.float64)
     d = np.abs(o_gpu - o_ref)
@@ -44,13 +52,16 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype):
         st["lse_max_abs"] = float(np.nanmax(dl)) if dl.size else 0.0
         st["lse_max_scaled"] = float(np.nanmax(dl / np.maximum(1.0, np.abs(lr)))) if dl.size else 0.0
         st["lse_nan"] = int(np.isnan(lg).sum())
+        st["lse_inf_mismatch"] = int(((np.isinf(lg) | np.isinf(lr)) & (lg != lr)).sum())
+    st["inf_mismatch"] = int(((np.isinf(o_gpu) | np.isinf(o_ref)) & (o_gpu != o_ref)).sum())
     return st
 
 
 def ok(st):
-    good = st["nan"] == 0 and st["max_ulp_net"] <= st["o_tol"]
+    good = st["nan"] == 0 and st["inf_mismatch"] == 0 and st["max_ulp_net"] <= st["o_tol"]
     if "lse_max_scaled" in st:
-        good = good and st["lse_nan"] == 0 and st["lse_max_scaled"] <= LSE_RTOL
+        good = good and st["lse_nan"] == 0 and st["lse_inf_mismatch"] == 0 and \
+            st["lse_max_scaled"] <= LSE_RTOL
     return good
 
 

@@ -226,6 +226,34 @@ def pin_rows_match_full(lib):
         assert np.array_equal(rl, lse.reshape(-1)[rows])
 
 
+def pin_unequal_causal_suffix(lib):
+    """Causal attention of a query block against a longer key sequence is the
+    tail of the square causal problem: with Sq < Sk, query row i plays the
+    role of row i + (Sk - Sq) of the Sk x Sk problem (whose causal mask the
+    pages fix: each position sees itself and earlier ones).  With Sq > Sk the
+    first Sq - Sk rows see no key (O = 0, lse = -inf) and the rest are the
+    square problem's rows."""
+    D = 16
+    scale = softmax_scale(D)
+    for dtype, Sq, Sk in (("f16", 23, 57), ("bf16", 5, 64), ("f16", 57, 23)):
+        qf, k, v = make_inputs(1, 2, max(Sq, Sk), D, dtype, seed=21 + Sq, Sk=Sk)
+        o_sq, l_sq = _run(lib, qf[:, :, :Sk].contiguous(), k, v, scale, True, dtype)
+        if Sq <= Sk:
+            q = qf[:, :, Sk - Sq:Sk].contiguous()
+            o, lse = _run(lib, q, k, v, scale, True, dtype)
+            assert np.array_equal(o, o_sq[:, :, Sk - Sq:]), (dtype, Sq, Sk)
+            assert np.array_equal(lse, l_sq[:, :, Sk - Sq:]), (dtype, Sq, Sk)
+        else:
+            q = torch.cat([qf[:, :, Sk:Sq], qf[:, :, :Sk]], dim=2).contiguous()
+            o, lse = _run(lib, q, k, v, scale, True, dtype)
+            n = Sq - Sk
+            assert np.all(o[:, :, :n] == 0.0) and np.all(np.isneginf(lse[:, :, :n])), (dtype, Sq, Sk)
+            assert np.array_equal(o[:, :, n:], o_sq) and np.array_equal(lse[:, :, n:], l_sq)
+        # the last query row sees every key: it equals the non-causal result
+        o_nc, l_nc = _run(lib, q, k, v, scale, False, dtype)
+        assert np.array_equal(o[:, :, -1], o_nc[:, :, -1]) and np.array_equal(lse[:, :, -1], l_nc[:, :, -1])
+
+
 ALL_PINS = [pin_decode_f16, pin_decode_bf16, pin_q_zero, pin_causal_row0, pin_convexity,
             pin_bruteforce_decimal, pin_sdpa_fp64, pin_chunk_merge, pin_invariances,
-            pin_rows_match_full]
+            pin_rows_match_full, pin_unequal_causal_suffix]

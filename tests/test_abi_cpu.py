@@ -38,14 +38,28 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert fa.fa_version() >= 10000
-    for code in range(8):
+    for code in range(9):
         s = fa.fa_status_string(code)
         assert s and s != "unknown status", code
     assert fa.fa_status_string(99) == "unknown status"
 
 
-# fake, 16-byte aligned, non-overlapping "device" addresses: validation never dereferences them
+# fake, 16-byte aligned, non-overlapping "device" addresses: validation never dereferences them.
+# Every call below must fail a host check; as a safety net the calls are not made at all where a
+# GPU is visible, so a call that wrongly passed validation could never launch on fake addresses.
 Q, K, V, O, L = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0      # counts devices without initialising them
+    except Exception:
+        return False
+
+
+fake_addresses = pytest.mark.skipif(_gpu_visible(), reason="fake device addresses are only passed "
+                                    "where no GPU is visible")
 GOOD = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, S=256, D=64, scale=0.125, causal=0, dtype=0)
 
 
@@ -66,6 +80,7 @@ def call(**kw):
     (dict(scale=float("inf")), 5),
     (dict(o=Q), 7), (dict(o=K + 64), 7), (dict(lse=V), 7), (dict(lse=O + 16), 7),
 ])
+@fake_addresses
 def test_rejects_bad_arguments(lib, kw, code):
     assert call(**kw) == code
 
@@ -118,3 +133,46 @@ def test_python_forward_rejects_cpu_tensors(lib):
     q = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
     with pytest.raises(ValueError):
         fa.forward(q, q, q)
+
+
+# fa_fwd_strided: a [B, H, S, D] layout given by element strides
+def scall(B=2, H=3, Sq=100, Sk=150, D=64, qs=None, ks=None, vs=None, os_=None, **kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, scale=0.125, causal=1, dtype=0)
+    a.update(kw)
+    qs = qs or (H * Sq * D, Sq * D, D)
+    ks = ks or (H * Sk * D, Sk * D, D)
+    vs = vs or (H * Sk * D, Sk * D, D)
+    os_ = os_ or (H * Sq * D, Sq * D, D)
+    return fa.fa_fwd_strided(a["q"], a["k"], a["v"], a["o"], a["lse"], B, H, Sq, Sk, D, qs, ks, vs,
+                             os_, a["scale"], a["causal"], a["dtype"], None)
+
+
+@fake_addresses
+def test_strided_rejects_bad_arguments(lib):
+    D = 64
+    assert scall(Sk=0) == 2 and scall(Sq=0) == 2
+    assert scall(qs=(3 * 100 * D, 100 * D, D + 4)) == 8            # row stride not a multiple of 8
+    assert scall(ks=(3 * 150 * D, 150 * D, 56)) == 8               # row stride < D
+    assert scall(vs=(-8, 150 * D, D)) == 8                         # negative stride
+    assert scall(os_=(3 * 100 * D, 0, D)) == 8                     # heads of o share memory
+    assert scall(os_=(3 * 100 * D, 64, D)) == 8                    # rows of one head overlap the next head's
+    assert scall(B=1, os_=(0, 100 * D, D), o=K + 64) == 7          # batch stride 0 is fine at B=1; o overlaps k
+    assert scall(o=K) == 7 and scall(lse=Q + 64) == 7              # aliasing
+    assert scall(q=Q + 8) == 4
+    assert scall(qs=(3 * 100 * D, 100 * D, 1 << 26)) == 2          # head span beyond 2^31 bytes
+    assert scall(D=96, qs=(0, 0, 96), ks=(0, 0, 96), vs=(0, 0, 96), os_=(300 * 96, 100 * 96, 96)) == 3
+
+
+@fake_addresses
+def test_strided_accepts_layouts_up_to_the_launch(lib):
+    """Valid layouts pass every host check; with null stream and fake
+    addresses a launch would be made, so only the checks that come before it
+    are exercised here, through layouts that must be rejected one step later
+    (an unaligned lse)."""
+    D = 128
+    B, H, Sq, Sk = 2, 4, 100, 300
+    bshd_q = (Sq * H * D, D, H * D)
+    bshd_kv = (Sk * H * D, D, H * D)
+    shared = (Sk * D, 0, D)
+    for qs, ks, vs in ((bshd_q, bshd_kv, bshd_kv), (None, shared, shared)):
+        assert scall(B=B, H=H, Sq=Sq, Sk=Sk, D=D, qs=qs, ks=ks, vs=vs, os_=bshd_q, lse=L + 4) == 4

@@ -19,6 +19,8 @@ MUTATIONS = [
     ("bf16_hidden_bit", "(double)(128 + frac)", "(double)(frac)"),
     ("diagonal_excluded", "return j <= i + (Sk - Sq);", "return j < i + (Sk - Sq);"),
     ("mask_polarity", "return j <= i + (Sk - Sq);", "return j >= i + (Sk - Sq);"),
+    ("causal_top_left", "return j <= i + (Sk - Sq);", "return j <= i;"),
+    ("causal_offset_sign", "return j <= i + (Sk - Sq);", "return j <= i + (Sq - Sk);"),
     ("dropped_feature", "for (int d = 0; d < D; ++d) acc += qrow[d] * kr[d];",
      "for (int d = 0; d < D - 1; ++d) acc += qrow[d] * kr[d];"),
     ("wrong_key_row", "const double* kr = K + j * D;", "const double* kr = K + ((j + 1) % Sk) * D;"),

@@ -12,15 +12,16 @@ import ctypes
 import math
 import os
 
-__all__ = ["FaError", "fa_fwd", "fa_fwd_plan", "fa_status_string", "fa_version", "forward",
-           "library_path", "F16", "BF16", "STATUS"]
+__all__ = ["FaError", "fa_fwd", "fa_fwd_strided", "fa_fwd_plan", "fa_status_string",
+           "fa_version", "forward", "library_path", "F16", "BF16", "STATUS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libfa_hip.so")
 
 F16, BF16 = 0, 1
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED",
-          4: "FA_ERR_ALIGN", 5: "FA_ERR_SCALE", 6: "FA_ERR_HIP", 7: "FA_ERR_ALIAS"}
+          4: "FA_ERR_ALIGN", 5: "FA_ERR_SCALE", 6: "FA_ERR_HIP", 7: "FA_ERR_ALIAS",
+          8: "FA_ERR_STRIDE"}
 
 _lib = None
 
@@ -55,6 +56,9 @@ def _load():
     ip = ctypes.POINTER(ctypes.c_int)
     lib.fa_fwd_plan.argtypes = [i, i, i, i, i, i, ip, ip, i64p, i64p]
     lib.fa_fwd_plan.restype = i
+    lib.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i64p, i64p, i64p, i64p,
+                                   f, i, i, vp]
+    lib.fa_fwd_strided.restype = i
     _lib = lib
     return lib
 
@@ -80,6 +84,22 @@ def fa_fwd(q, k, v, o, lse, B, H, S, D, scale, causal, dtype, stream):
     return _load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(S),
                           int(D), ctypes.c_float(scale), int(bool(causal)), int(dtype),
                           _stream(stream))
+
+
+def _strides3(st):
+    a = (ctypes.c_int64 * 3)(*[int(x) for x in st])
+    return a
+
+
+def fa_fwd_strided(q, k, v, o, lse, B, H, Sq, Sk, D, q_strides, k_strides, v_strides, o_strides,
+                   scale, causal, dtype, stream):
+    """The ABI call fa_fwd_strided; strides are 3-sequences of element strides
+    (batch, head, row).  Returns the status."""
+    return _load().fa_fwd_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+                                  int(Sq), int(Sk), int(D), _strides3(q_strides),
+                                  _strides3(k_strides), _strides3(v_strides),
+                                  _strides3(o_strides), ctypes.c_float(scale),
+                                  int(bool(causal)), int(dtype), _stream(stream))
 
 
 def fa_status_string(status):
@@ -112,33 +132,45 @@ def _dtype_code(t):
 
 
 def forward(q, k, v, causal=False, scale=None, return_lse=True, out=None, lse_out=None):
-    """Attention forward on contiguous [B, H, S, D] GPU tensors.
+    """Attention forward on GPU tensors q [B, H, Sq, D], k and v [B, H, Sk, D].
 
-    Returns (o, lse) with o like q and lse float32 [B, H, S] (None when
-    return_lse is False).  scale defaults to 1/sqrt(D).  Enqueued on the
-    current torch stream; no synchronisation."""
+    Any strides with a contiguous last dimension are accepted (for example a
+    [B, S, H, D] tensor viewed as [B, H, S, D] with transpose(1, 2)).  Returns
+    (o, lse): o [B, H, Sq, D] contiguous of q's dtype (or `out`, which may be
+    strided) and lse float32 [B, H, Sq] (None when return_lse is False).
+    causal: key j visible to query i iff j <= i + (Sk - Sq).  scale defaults
+    to 1/sqrt(D).  Enqueued on the current torch stream; no synchronisation."""
     import torch
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("fa: q, k, v must share one [B, H, S, D] shape")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("fa: q, k, v must be 4-d [B, H, S, D]")
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if tuple(k.shape) != (B, H, Sk, D) or tuple(v.shape) != (B, H, Sk, D):
+        raise ValueError("fa: k and v must be [B, H, Sk, D] matching q [B, H, Sq, D]")
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("fa: tensors must be on the GPU")
     if not (q.device == k.device == v.device):
         raise ValueError("fa: tensors must be on one device")
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("fa: q, k, v must share one dtype")
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("fa: tensors must be contiguous [B, H, S, D]")
-    B, H, S, D = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.stride(3) != 1 and D > 1:
+            raise ValueError("fa: %s must have a contiguous last dimension" % name)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    o = out if out is not None else torch.empty_like(q)
+    o = out if out is not None else torch.empty((B, H, Sq, D), dtype=q.dtype, device=q.device)
+    if tuple(o.shape) != (B, H, Sq, D) or o.dtype != q.dtype or o.stride(3) != 1:
+        raise ValueError("fa: out must be [B, H, Sq, D] of q's dtype with a contiguous last dimension")
     lse = None
     if return_lse:
         lse = lse_out if lse_out is not None else torch.empty(
-            (B, H, S), dtype=torch.float32, device=q.device)
+            (B, H, Sq), dtype=torch.float32, device=q.device)
+        if tuple(lse.shape) != (B, H, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise ValueError("fa: lse_out must be contiguous float32 [B, H, Sq]")
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream().cuda_stream
-    st = fa_fwd(q, k, v, o, lse, B, H, S, D, scale, causal, _dtype_code(q), stream)
+    st = fa_fwd_strided(q, k, v, o, lse, B, H, Sq, Sk, D, q.stride()[:3], k.stride()[:3],
+                        v.stride()[:3], o.stride()[:3], scale, causal, _dtype_code(q), stream)
     if st != 0:
-        raise FaError(st)
+        raise FaError(st, "fa_fwd_strided")
     return o, lse

@@ -14,26 +14,67 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
 
-int validate_shape(int B, int H, int S, int D, int dtype) {
-    if (B < 1 || H < 1 || S < 1) return FA_ERR_SHAPE;
+int validate_shape(int B, int H, int Sq, int Sk, int D, int dtype) {
+    if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return FA_ERR_SHAPE;
     if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
     if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
-    // Per-head byte offsets are 32-bit (buffer descriptors): the head plus the
-    // padding rows of its last query block must stay below 2^31 bytes.
-    const int64_t head_bytes = ((int64_t)S + fa::kBlockQ) * D * 2;
-    if (head_bytes >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
+    const int S = Sq > Sk ? Sq : Sk;
     const int64_t elems = (int64_t)B * H * S * D;
     if (elems >= (int64_t(1) << 40)) return FA_ERR_SHAPE;
-    const int64_t grid = (int64_t)B * H * ((S + fa::kBlockQ - 1) / fa::kBlockQ);
+    const int64_t grid = (int64_t)B * H * ((Sq + fa::kBlockQ - 1) / fa::kBlockQ);
     if (grid >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
     return FA_OK;
 }
 
-bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
-    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
-    return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+// Byte offsets inside one head are 32-bit (buffer descriptors): every row a
+// query block (rows up to a multiple of kBlockQ) or a key tile (up to 64
+// rows past the end) can address must lie below 2^31 bytes.
+bool head_span_ok(int S, int64_t row_stride, int D) {
+    const int64_t rows = ((int64_t)S + fa::kBlockQ - 1) / fa::kBlockQ * fa::kBlockQ + fa::kBlockKV;
+    return (rows * row_stride + D) * 2 < (int64_t(1) << 31);
+}
+
+bool overlap(uintptr_t x, uintptr_t xe, uintptr_t y, uintptr_t ye) { return x < ye && y < xe; }
+
+// Byte range [lo, hi) covered by a [B, H, S, D] tensor with element strides
+// st (strides are >= 0).
+void span(const void* p, int B, int H, int S, int D, const int64_t* st, uintptr_t& lo, uintptr_t& hi) {
+    lo = (uintptr_t)p;
+    hi = lo + (uintptr_t)(((B - 1) * st[0] + (H - 1) * st[1] + (int64_t)(S - 1) * st[2] + D) * 2);
+}
+
+int check_strides(const int64_t* st, int D) {
+    for (int i = 0; i < 3; ++i)
+        if (st[i] < 0 || (st[i] & 7) != 0) return FA_ERR_STRIDE;
+    if (st[2] < D) return FA_ERR_STRIDE;
+    if (st[2] >= (int64_t(1) << 30)) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
+// o's elements must not share addresses: with its three strides sorted
+// (largest first, extents n1 n2 n3), s3 >= D, s2 >= n3*s3, s1 >= n2*s2.
+// A dimension of extent 1 is ignored.
+bool no_self_overlap(const int64_t* st, int B, int H, int S, int D) {
+    int64_t s[3] = {st[0], st[1], st[2]};
+    int64_t n[3] = {B, H, S};
+    for (int i = 0; i < 3; ++i)
+        if (n[i] == 1) s[i] = 0;
+    for (int i = 0; i < 3; ++i)
+        for (int j = i + 1; j < 3; ++j)
+            if (s[j] > s[i]) {
+                std::swap(s[i], s[j]);
+                std::swap(n[i], n[j]);
+            }
+    // s[0] >= s[1] >= s[2]; zero strides only for extent-1 dimensions
+    int64_t need = D;
+    for (int i = 2; i >= 0; --i) {
+        if (n[i] == 1) continue;
+        if (s[i] < need) return false;
+        need = s[i] * n[i];
+    }
+    return true;
 }
 
 }  // namespace
@@ -52,13 +93,15 @@ const char* fa_status_string(int status) {
         case FA_ERR_SCALE: return "scale not finite and positive";
         case FA_ERR_HIP: return "HIP runtime error at launch";
         case FA_ERR_ALIAS: return "output buffer overlaps an input or the other output";
+        case FA_ERR_STRIDE: return "invalid strides (negative, not a multiple of 8, row stride < D, or overlapping output)";
         default: return "unknown status";
     }
 }
 
 int fa_fwd_plan(int B, int H, int S, int D, int causal, int dtype, int* block_q, int* block_kv,
                 int64_t* grid, int64_t* tiles) {
-    const int st = validate_shape(B, H, S, D, dtype);
+    int st = validate_shape(B, H, S, S, D, dtype);
+    if (st == FA_OK && !head_span_ok(S, D, D)) st = FA_ERR_SHAPE;
     if (st != FA_OK) return st;
     const int br = fa::kBlockQ, bc = fa::kBlockKV;
     const int64_t nqb = (S + br - 1) / br;
@@ -78,21 +121,40 @@ int fa_fwd_plan(int B, int H, int S, int D, int causal, int dtype, int* block_q,
     return FA_OK;
 }
 
-int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int S,
-           int D, float scale, int causal, int dtype, void* stream) {
-    if (!q || !k || !v || !o) return FA_ERR_NULL;
-    const int st = validate_shape(B, H, S, D, dtype);
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Sq, int Sk, int D,
+                   const int64_t* q_strides, const int64_t* k_strides,
+                   const int64_t* v_strides, const int64_t* o_strides,
+                   float scale, int causal, int dtype, void* stream) {
+    if (!q || !k || !v || !o || !q_strides || !k_strides || !v_strides || !o_strides)
+        return FA_ERR_NULL;
+    int st = validate_shape(B, H, Sq, Sk, D, dtype);
     if (st != FA_OK) return st;
+    const int64_t* strides[4] = {q_strides, k_strides, v_strides, o_strides};
+    for (const int64_t* s4 : strides)
+        if ((st = check_strides(s4, D)) != FA_OK) return st;
+    if (!head_span_ok(Sq, q_strides[2], D) || !head_span_ok(Sk, k_strides[2], D) ||
+        !head_span_ok(Sk, v_strides[2], D) || !head_span_ok(Sq, o_strides[2], D))
+        return FA_ERR_SHAPE;
+    if (o_strides[0] == 0 && B > 1) return FA_ERR_STRIDE;
+    if (o_strides[1] == 0 && H > 1) return FA_ERR_STRIDE;
+    if (!no_self_overlap(o_strides, B, H, Sq, D)) return FA_ERR_STRIDE;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse) & 15)
         return FA_ERR_ALIGN;
     if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_SCALE;
-    const int64_t tbytes = (int64_t)B * H * S * D * 2;
-    const int64_t lbytes = (int64_t)B * H * S * 4;
-    if (overlap(o, tbytes, q, tbytes) || overlap(o, tbytes, k, tbytes) || overlap(o, tbytes, v, tbytes))
+    uintptr_t ql, qh, kl, kh, vl, vh, ol, oh;
+    span(q, B, H, Sq, D, q_strides, ql, qh);
+    span(k, B, H, Sk, D, k_strides, kl, kh);
+    span(v, B, H, Sk, D, v_strides, vl, vh);
+    span(o, B, H, Sq, D, o_strides, ol, oh);
+    if (overlap(ol, oh, ql, qh) || overlap(ol, oh, kl, kh) || overlap(ol, oh, vl, vh))
         return FA_ERR_ALIAS;
-    if (lse && (overlap(lse, lbytes, q, tbytes) || overlap(lse, lbytes, k, tbytes) ||
-                overlap(lse, lbytes, v, tbytes) || overlap(lse, lbytes, o, tbytes)))
-        return FA_ERR_ALIAS;
+    if (lse) {
+        const uintptr_t ll = (uintptr_t)lse, lh = ll + (uintptr_t)((int64_t)B * H * Sq * 4);
+        if (overlap(ll, lh, ql, qh) || overlap(ll, lh, kl, kh) || overlap(ll, lh, vl, vh) ||
+            overlap(ll, lh, ol, oh))
+            return FA_ERR_ALIAS;
+    }
 
     fa::FwdParams p;
     p.q = q;
@@ -100,13 +162,27 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     p.v = v;
     p.o = o;
     p.lse = lse;
-    p.S = S;
+    p.Sq = Sq;
+    p.Sk = Sk;
+    p.H = H;
     p.BH = B * H;
-    p.nqb = (S + fa::kBlockQ - 1) / fa::kBlockQ;
+    p.nqb = (Sq + fa::kBlockQ - 1) / fa::kBlockQ;
     p.scale_log2e = (float)((double)scale * 1.4426950408889634074);
+    p.q_sb = q_strides[0], p.q_sh = q_strides[1], p.q_ss = (int)q_strides[2];
+    p.k_sb = k_strides[0], p.k_sh = k_strides[1], p.k_ss = (int)k_strides[2];
+    p.v_sb = v_strides[0], p.v_sh = v_strides[1], p.v_ss = (int)v_strides[2];
+    p.o_sb = o_strides[0], p.o_sh = o_strides[1], p.o_ss = (int)o_strides[2];
     const int64_t grid = (int64_t)p.BH * p.nqb;
     const hipError_t err = fa::launch_fwd(p, D, dtype, causal != 0, grid, (hipStream_t)stream);
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int S,
+           int D, float scale, int causal, int dtype, void* stream) {
+    // contiguous [B, H, S, D]
+    const int64_t st[3] = {(int64_t)H * S * D, (int64_t)S * D, D};
+    return fa_fwd_strided(q, k, v, o, lse, B, H, S, S, D, st, st, st, st, scale, causal, dtype,
+                          stream);
 }
 
 }  // extern "C"

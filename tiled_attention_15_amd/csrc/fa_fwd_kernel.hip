@@ -224,23 +224,35 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
 
     int bh, qb;
     schedule(blockIdx.x, p.nqb, p.BH, CAUSAL, bh, qb);
-    const int S = p.S;
+    const int Sq = p.Sq, Sk = p.Sk;
+    // Causal diagonal: key j is visible to query i iff j <= i + diag (the
+    // last query row sees the last key).
+    const int diag = Sk - Sq;
     const int q0 = qb * BR;
     const int qw0 = q0 + wid * 32;
-    const int64_t head = (int64_t)bh * S * D;
-    const uint32_t head_bytes = (uint32_t)S * D * 2;
+    const int b_ = bh / p.H, h_ = bh - b_ * p.H;
 
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)p.q + head * 2, head_bytes);
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc((char*)p.o + head * 2, head_bytes);
-    const i32x4 rk = rsrc_words((const char*)p.k + head * 2, head_bytes);
-    const i32x4 rv = rsrc_words((const char*)p.v + head * 2, head_bytes);
+    // One buffer descriptor per tensor and head; its record count is the
+    // head's extent (last row's end), so rows past the sequence read as zero
+    // and stores to them are dropped.
+    auto head_rsrc = [&](const void* base, int64_t sb, int64_t sh, int ss, int rows) {
+        const char* hb = (const char*)base + ((int64_t)b_ * sb + (int64_t)h_ * sh) * 2;
+        return make_rsrc(hb, (uint32_t)(((int64_t)(rows - 1) * ss + D) * 2));
+    };
+    const __amdgpu_buffer_rsrc_t rq = head_rsrc(p.q, p.q_sb, p.q_sh, p.q_ss, Sq);
+    const __amdgpu_buffer_rsrc_t ro = head_rsrc(p.o, p.o_sb, p.o_sh, p.o_ss, Sq);
+    const i32x4 rk = rsrc_words((const char*)p.k + ((int64_t)b_ * p.k_sb + (int64_t)h_ * p.k_sh) * 2,
+                                (uint32_t)(((int64_t)(Sk - 1) * p.k_ss + D) * 2));
+    const i32x4 rv = rsrc_words((const char*)p.v + ((int64_t)b_ * p.v_sb + (int64_t)h_ * p.v_sh) * 2,
+                                (uint32_t)(((int64_t)(Sk - 1) * p.v_ss + D) * 2));
 
     // Every wave visits all nt tiles of its workgroup: a wave whose rows end
     // before a diagonal tile finds it fully masked (probabilities exactly 0),
-    // and the phase barriers would make it wait for that tile anyway.
-    const int nkv = (S + BC - 1) / BC;
+    // and the phase barriers would make it wait for that tile anyway.  A
+    // block none of whose rows sees a key still runs one (fully masked) tile.
+    const int nkv = (Sk + BC - 1) / BC;
     int nt = nkv;
-    if (CAUSAL) nt = min(nkv, (min(S, q0 + BR) + BC - 1) / BC);
+    if (CAUSAL) nt = max(1, min(nkv, (min(Sq, q0 + BR) + diag + BC - 1) / BC));
 
     // Direct-to-LDS loads.  Group 1 loads every K tile and group 0 every V
     // tile, each at the start of its softmax phase, so no wave's matrix phase
@@ -248,22 +260,24 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
     // group) fills LDS chunks (i*4 + w)*64 + lane of the tile; each lane
     // fetches the global chunk that the swizzled layout puts there.
     const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
+    const int kv_ss = grp != 0 ? p.k_ss : p.v_ss;     // row stride of the tensor this wave loads
     uint32_t src[2 * LPT];
 #pragma unroll
     for (int i = 0; i < 2 * LPT; ++i) {
         const int c = (i * 4 + (wid & 3)) * 64 + lane;
         const int row = c / (D / 8), cl = c % (D / 8);
         if (grp != 0) {
-            src[i] = (uint32_t)(row * D + ((cl ^ kswz<D>(row)) << 3)) * 2;
+            src[i] = (uint32_t)(row * kv_ss + ((cl ^ kswz<D>(row)) << 3)) * 2;
         } else {
             const int gc = (((cl >> 2) ^ vseg_swz<D>(row)) << 2) | (cl & 3);
-            src[i] = (uint32_t)(row * D + (gc << 3)) * 2;
+            src[i] = (uint32_t)(row * kv_ss + (gc << 3)) * 2;
         }
     }
     const i32x4 rkv = grp != 0 ? rk : rv;
     const uint32_t part = grp != 0 ? 0u : (uint32_t)TILE_BYTES;
+    const uint32_t tile_stride = (uint32_t)BC * kv_ss * 2;     // bytes between K/V tiles
     auto issue_tile = [&](int t) {
-        const uint32_t tb = (uint32_t)t * TILE_BYTES;
+        const uint32_t tb = (uint32_t)t * tile_stride;
         const uint32_t sb = lds0 + (uint32_t)(t & (NSLOT - 1)) * SLOT_BYTES + part;
 #pragma unroll
         for (int i = 0; i < 2 * LPT; ++i)
@@ -273,7 +287,7 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
     i32x4 qf[DC];
 #pragma unroll
     for (int c = 0; c < DC; ++c)
-        qf[c] = __builtin_amdgcn_raw_buffer_load_b128(rq, ((qw0 + lq) * D + 16 * c + 8 * g) * 2, 0, 0);
+        qf[c] = __builtin_amdgcn_raw_buffer_load_b128(rq, ((qw0 + lq) * p.q_ss + 16 * c + 8 * g) * 2, 0, 0);
 
     f32x16 oacc[DB];
 #pragma unroll
@@ -342,9 +356,9 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
     auto swork = [&](int t) {
         const int key0 = t * BC + 16 * g;
         const int qrow = qw0 + lq;
-        const bool need_mask = (t * BC + BC > S) || (CAUSAL && t * BC + BC - 1 > qw0);
+        const bool need_mask = (t * BC + BC > Sk) || (CAUSAL && t * BC + BC - 1 > qw0 + diag);
         if (need_mask) {
-            const int lim = CAUSAL ? min(qrow, S - 1) : S - 1;
+            const int lim = CAUSAL ? min(qrow + diag, Sk - 1) : Sk - 1;
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -495,13 +509,13 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
             w0[e] = pack2<DT>(oacc[b][2 * e] * inv, oacc[b][2 * e + 1] * inv);
             w1[e] = pack2<DT>(oacc[b][8 + 2 * e] * inv, oacc[b][8 + 2 * e + 1] * inv);
         }
-        const uint32_t off = ((uint32_t)qrow * D + 32 * b + 16 * g) * 2;
+        const uint32_t off = ((uint32_t)qrow * p.o_ss + 32 * b + 16 * g) * 2;
         __builtin_amdgcn_raw_buffer_store_b128(w0, ro, off, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b128(w1, ro, off + 16, 0, 0);
     }
-    if (p.lse != nullptr && g == 0 && qrow < S) {
+    if (p.lse != nullptr && g == 0 && qrow < Sq) {
         const float lse2 = (l_tot > 0.0f) ? (m_run == -INFINITY ? 0.0f : m_run) + log2f(l_tot) : -INFINITY;
-        p.lse[(int64_t)bh * S + qrow] = lse2 * 0.69314718055994530942f;
+        p.lse[(int64_t)bh * Sq + qrow] = lse2 * 0.69314718055994530942f;
     }
 }
 

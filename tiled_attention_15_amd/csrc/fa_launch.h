@@ -13,11 +13,16 @@ struct FwdParams {
     const void* k;
     const void* v;
     void* o;
-    float* lse;        // may be null
-    int S;             // sequence length
+    float* lse;        // [B, H, Sq] fp32, contiguous; may be null
+    int Sq;            // query rows per head
+    int Sk;            // key / value rows per head
+    int H;             // heads (bh = b * H + h)
     int BH;            // batch * heads
-    int nqb;           // query blocks per head: ceil(S / kBlockQ)
+    int nqb;           // query blocks per head: ceil(Sq / kBlockQ)
     float scale_log2e; // scale * log2(e), fp32
+    // Element strides of batch, head and row (the head dimension is contiguous).
+    int64_t q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;
+    int q_ss, k_ss, v_ss, o_ss;
 };
 
 // Enqueue the forward kernel; returns hipGetLastError() after the launch.
