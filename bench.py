@@ -15,8 +15,12 @@ Prints ONE JSON line:
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of rows of
              the same workload on this host's cores (rank 0, one GPU only).
 
+  naive_unfused  the same attention computed the unfused way (scores and
+             probabilities written to device memory, four kernels of this
+             library), timed the same way, with the fused kernel's speedup.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--cpu-seconds T] [--no-cpu-baseline]
+                       [--cpu-seconds T] [--no-cpu-baseline] [--no-naive]
 """
 import argparse
 import hashlib
@@ -36,9 +40,10 @@ from workloads import HEADLINE, WORKLOADS, bits, workload_inputs  # noqa: E402
 # MI355X published dense matrix-core peak for fp16/bf16 (2.4 GHz, 256 CUs).
 MFMA_PEAK_TFLOPS = 2516.6
 HBM_PEAK_GBS = 8000.0
+# The fused kernel and its parameter block: the HBM counters in profiles/ stay
+# valid while these are unchanged.
 KERNEL_SOURCES = ["tiled_attention_15_amd/csrc/fa_fwd_kernel.hip",
-                  "tiled_attention_15_amd/csrc/fa_launch.h",
-                  "tiled_attention_15_amd/csrc/fa_api.cpp"]
+                  "tiled_attention_15_amd/csrc/fa_launch.h"]
 
 
 def kernel_source_hash():
@@ -99,6 +104,48 @@ def gpu_leg(w, steps, warmup):
     if not torch.isfinite(o).all().item():
         raise RuntimeError("non-finite output in the benchmark run")
     return ev_ms / steps, wall / steps * 1e3
+
+
+def naive_leg(w, steps, warmup):
+    """The unfused comparison path (scores and probabilities materialised in
+    device memory) on the same inputs, timed like the fused kernel."""
+    import torch
+    import tiled_attention_15_amd as fa
+
+    dev = torch.device("cuda:0")
+    need = fa.fa_naive_workspace_bytes(w.B, w.H, w.S, w.D)
+    if need <= 0:
+        return None
+    q, k, v = workload_inputs(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    code = fa.BF16 if w.dtype == "bf16" else fa.F16
+
+    def step():
+        st = fa.fa_naive_fwd(qd, kd, vd, o, lse, w.B, w.H, w.S, w.D, w.scale, w.causal, code, ws,
+                             need, stream)
+        if st != 0:
+            raise fa.FaError(st, "fa_naive_fwd")
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    del ws
+    return {"ms_per_step": round(ms, 4), "value": round(w.flops() / (ms * 1e-3) / 1e12, 3),
+            "unit": "TFLOP/s", "workspace_bytes": int(need), "steps": steps,
+            "path": "scores (fp32) and probabilities materialised in device memory: four kernels "
+                    "(Q K^T, row softmax, V transpose, P V)"}
 
 
 def copy_leg(mib, steps, warmup):
@@ -172,6 +219,8 @@ def main():
     ap.add_argument("--workload", default=HEADLINE, choices=list(WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-naive", action="store_true",
+                    help="skip the unfused comparison path")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of attention, time a plain device-to-device copy of this many "
                          "MiB (the reference kernel for scaling HBM byte counters)")
@@ -212,6 +261,11 @@ def main():
                      "traffic": traffic},
         "cpu_baseline": None,
     }
+    if not a.no_naive:
+        nv = naive_leg(w, max(2, min(20, a.steps // 10)), 2)
+        if nv is not None:
+            nv["fused_speedup"] = round(nv["ms_per_step"] / ms, 2)
+        out["naive_unfused"] = nv
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_leg(w, a.cpu_seconds)
     print(json.dumps(out), flush=True)

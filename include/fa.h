@@ -165,6 +165,36 @@ int fa_version(void);
 int fa_fwd_plan(int B, int H, int S, int D, int causal, int dtype,
                 int* block_q, int* block_kv, int64_t* grid, int64_t* tiles);
 
+/*
+ * fa_naive_fwd -- the same forward computed the unfused way, for comparison:
+ * scores S = scale * Q K^T (causal mask applied) written to `workspace` in
+ * fp32, a row softmax writing P (in `dtype`) and lse, then O = P V.  This is
+ * the three-step flow that "FlashAttention-2 on Ascend NPU: how
+ * ops-transformer reaches 3x" (2048ai.net), section 1, and "ops-transformer
+ * FlashAttention operator in practice" (ai6s.net), sections 1 and 4, describe
+ * as the baseline the fused operator replaces; its S x S matrices cost
+ * O(S^2) device memory and traffic.  Arguments as for fa_fwd (contiguous
+ * [B, H, S, D], same outputs and numerics up to rounding order), plus:
+ *
+ *   workspace        device memory of at least fa_naive_workspace_bytes()
+ *                    bytes, 16-byte aligned, not overlapping any other
+ *                    argument; owned by the caller, contents overwritten.
+ *   workspace_bytes  its size.
+ *
+ * Limits: S <= 16384 (one workgroup's registers hold a whole softmax row) and
+ * B * H <= 65535; otherwise FA_ERR_SHAPE.  A workspace that is NULL or too
+ * small gives FA_ERR_NULL / FA_ERR_SHAPE; one that overlaps q, k, v, o or lse
+ * gives FA_ERR_ALIAS.  Launches four kernels on `stream`.
+ */
+int fa_naive_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int S, int D, float scale, int causal, int dtype,
+                 void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace fa_naive_fwd needs for this shape (0 for an invalid
+ * shape): per (batch, head), S x Sp fp32 scores, S x Sp probabilities and
+ * D x Sp transposed values (16-bit), Sp = S rounded up to a multiple of 16. */
+int64_t fa_naive_workspace_bytes(int B, int H, int S, int D);
+
 #ifdef __cplusplus
 }
 #endif

@@ -176,3 +176,30 @@ def test_strided_accepts_layouts_up_to_the_launch(lib):
     shared = (Sk * D, 0, D)
     for qs, ks, vs in ((bshd_q, bshd_kv, bshd_kv), (None, shared, shared)):
         assert scall(B=B, H=H, Sq=Sq, Sk=Sk, D=D, qs=qs, ks=ks, vs=vs, os_=bshd_q, lse=L + 4) == 4
+
+
+@fake_addresses
+def test_naive_rejects_bad_arguments(lib):
+    W = 0x10000000
+    B, H, S, D = 1, 2, 256, 64
+    need = fa.fa_naive_workspace_bytes(B, H, S, D)
+    Sp = 256
+    assert need >= B * H * (S * Sp * 6 + D * Sp * 2)
+    assert fa.fa_naive_workspace_bytes(1, 1, 16385, 64) == 0     # beyond the 16384-key limit
+    assert fa.fa_naive_workspace_bytes(1, 1, 0, 64) == 0
+
+    def ncall(**kw):
+        a = dict(q=Q, k=K, v=V, o=O, lse=L, B=B, H=H, S=S, D=D, scale=0.125, causal=1, dtype=0,
+                 ws=W, wsb=need)
+        a.update(kw)
+        return fa.fa_naive_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["S"],
+                               a["D"], a["scale"], a["causal"], a["dtype"], a["ws"], a["wsb"], None)
+
+    assert ncall(ws=0) == 1
+    assert ncall(wsb=need - 1) == 2
+    assert ncall(S=20000, wsb=1 << 40) == 2
+    assert ncall(ws=W + 8) == 4
+    assert ncall(ws=Q) == 7                  # workspace overlaps q
+    assert ncall(o=K) == 7
+    assert ncall(scale=0.0) == 5
+    assert ncall(D=96) == 3

@@ -12,8 +12,9 @@ import ctypes
 import math
 import os
 
-__all__ = ["FaError", "fa_fwd", "fa_fwd_strided", "fa_fwd_plan", "fa_status_string",
-           "fa_version", "forward", "library_path", "F16", "BF16", "STATUS"]
+__all__ = ["FaError", "fa_fwd", "fa_fwd_strided", "fa_fwd_plan", "fa_naive_fwd",
+           "fa_naive_workspace_bytes", "fa_status_string", "fa_version", "forward",
+           "naive_forward", "library_path", "F16", "BF16", "STATUS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libfa_hip.so")
@@ -59,6 +60,10 @@ def _load():
     lib.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i64p, i64p, i64p, i64p,
                                    f, i, i, vp]
     lib.fa_fwd_strided.restype = i
+    lib.fa_naive_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, ctypes.c_int64, vp]
+    lib.fa_naive_fwd.restype = i
+    lib.fa_naive_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_naive_workspace_bytes.restype = ctypes.c_int64
     _lib = lib
     return lib
 
@@ -100,6 +105,19 @@ def fa_fwd_strided(q, k, v, o, lse, B, H, Sq, Sk, D, q_strides, k_strides, v_str
                                   _strides3(k_strides), _strides3(v_strides),
                                   _strides3(o_strides), ctypes.c_float(scale),
                                   int(bool(causal)), int(dtype), _stream(stream))
+
+
+def fa_naive_fwd(q, k, v, o, lse, B, H, S, D, scale, causal, dtype, workspace, workspace_bytes,
+                 stream):
+    """The ABI call fa_naive_fwd (the unfused comparison path).  Returns the status."""
+    return _load().fa_naive_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+                                int(S), int(D), ctypes.c_float(scale), int(bool(causal)),
+                                int(dtype), _ptr(workspace), int(workspace_bytes),
+                                _stream(stream))
+
+
+def fa_naive_workspace_bytes(B, H, S, D):
+    return _load().fa_naive_workspace_bytes(int(B), int(H), int(S), int(D))
 
 
 def fa_status_string(status):
@@ -173,4 +191,35 @@ def forward(q, k, v, causal=False, scale=None, return_lse=True, out=None, lse_ou
                         v.stride()[:3], o.stride()[:3], scale, causal, _dtype_code(q), stream)
     if st != 0:
         raise FaError(st, "fa_fwd_strided")
+    return o, lse
+
+
+def naive_forward(q, k, v, causal=False, scale=None, workspace=None):
+    """The unfused comparison path on contiguous [B, H, S, D] GPU tensors:
+    scores and probabilities materialised in a workspace (allocated here with
+    torch unless given as a uint8 tensor of at least fa_naive_workspace_bytes).
+    Returns (o, lse)."""
+    import torch
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("fa: q, k, v must share one [B, H, S, D] shape")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("fa: the unfused path takes contiguous tensors")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("fa: q, k, v must share one dtype")
+    B, H, S, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = fa_naive_workspace_bytes(B, H, S, D)
+    if need <= 0:
+        raise FaError(2, "fa_naive_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream().cuda_stream
+    st = fa_naive_fwd(q, k, v, o, lse, B, H, S, D, scale, causal, _dtype_code(q), workspace,
+                      workspace.numel() * workspace.element_size(), stream)
+    if st != 0:
+        raise FaError(st, "fa_naive_fwd")
     return o, lse

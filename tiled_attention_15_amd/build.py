@@ -11,7 +11,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa_hip.so")
-SOURCES = [os.path.join(CSRC, "fa_api.cpp"), os.path.join(CSRC, "fa_fwd_kernel.hip")]
+SOURCES = [os.path.join(CSRC, "fa_api.cpp"), os.path.join(CSRC, "fa_fwd_kernel.hip"),
+           os.path.join(CSRC, "fa_naive.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -11,6 +11,7 @@
 
 #include "fa.h"
 #include "fa_launch.h"
+#include "fa_naive.h"
 
 namespace {
 
@@ -183,6 +184,77 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     const int64_t st[3] = {(int64_t)H * S * D, (int64_t)S * D, D};
     return fa_fwd_strided(q, k, v, o, lse, B, H, S, S, D, st, st, st, st, scale, causal, dtype,
                           stream);
+}
+
+namespace {
+
+// Workspace regions of the unfused path, each rounded up to 256 bytes.
+struct NaiveLayout {
+    int64_t s_bytes, p_bytes, vt_bytes, total;
+};
+
+bool naive_layout(int B, int H, int S, int D, NaiveLayout& L) {
+    if (validate_shape(B, H, S, S, D, FA_F16) != FA_OK) return false;
+    const int64_t Sp = (S + 15) / 16 * 16;
+    if (Sp > 16384 || (int64_t)B * H > 65535) return false;
+    if (S * Sp * 4 >= (int64_t(1) << 31)) return false;
+    auto r256 = [](int64_t x) { return (x + 255) / 256 * 256; };
+    const int64_t bh = (int64_t)B * H;
+    L.s_bytes = r256(bh * S * Sp * 4);
+    L.p_bytes = r256(bh * S * Sp * 2);
+    L.vt_bytes = r256(bh * D * Sp * 2);
+    L.total = L.s_bytes + L.p_bytes + L.vt_bytes;
+    return true;
+}
+
+}  // namespace
+
+int64_t fa_naive_workspace_bytes(int B, int H, int S, int D) {
+    NaiveLayout L;
+    return naive_layout(B, H, S, D, L) ? L.total : 0;
+}
+
+int fa_naive_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int S, int D, float scale, int causal, int dtype, void* workspace,
+                 int64_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !o || !workspace) return FA_ERR_NULL;
+    int st = validate_shape(B, H, S, S, D, dtype);
+    if (st != FA_OK) return st;
+    NaiveLayout L;
+    if (!naive_layout(B, H, S, D, L) || workspace_bytes < L.total) return FA_ERR_SHAPE;
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse |
+         (uintptr_t)workspace) & 15)
+        return FA_ERR_ALIGN;
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_SCALE;
+    const uintptr_t tb = (uintptr_t)((int64_t)B * H * S * D * 2);
+    const uintptr_t lb = (uintptr_t)((int64_t)B * H * S * 4);
+    const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + (uintptr_t)L.total;
+    const uintptr_t io[5][2] = {{(uintptr_t)q, (uintptr_t)q + tb}, {(uintptr_t)k, (uintptr_t)k + tb},
+                                {(uintptr_t)v, (uintptr_t)v + tb}, {(uintptr_t)o, (uintptr_t)o + tb},
+                                {(uintptr_t)lse, (uintptr_t)lse + (lse ? lb : 0)}};
+    for (int i = 0; i < 5; ++i)
+        if (io[i][1] > io[i][0] && overlap(w0, w1, io[i][0], io[i][1])) return FA_ERR_ALIAS;
+    for (int i = 0; i < 3; ++i)
+        for (int j = 3; j < 5; ++j)
+            if (io[j][1] > io[j][0] && overlap(io[i][0], io[i][1], io[j][0], io[j][1])) return FA_ERR_ALIAS;
+    if (lse && overlap(io[3][0], io[3][1], io[4][0], io[4][1])) return FA_ERR_ALIAS;
+
+    fa::naive::NaiveParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.s = (float*)workspace;
+    p.p = (uint16_t*)((char*)workspace + L.s_bytes);
+    p.vt = (uint16_t*)((char*)workspace + L.s_bytes + L.p_bytes);
+    p.Sq = S;
+    p.Sk = S;
+    p.Skp = (S + 15) / 16 * 16;
+    p.causal = causal != 0;
+    p.scale = scale;
+    const hipError_t err = fa::naive::launch_naive(p, B * H, D, dtype, (hipStream_t)stream);
+    return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 }  // extern "C"
