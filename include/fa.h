@@ -192,7 +192,7 @@ int fa_naive_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 
 /* Bytes of workspace fa_naive_fwd needs for this shape (0 for an invalid
  * shape): per (batch, head), S x Sp fp32 scores, S x Sp probabilities and
- * D x Sp transposed values (16-bit), Sp = S rounded up to a multiple of 16. */
+ * D x Sp transposed values (16-bit), Sp = S rounded up to a multiple of 64. */
 int64_t fa_naive_workspace_bytes(int B, int H, int S, int D);
 
 #ifdef __cplusplus

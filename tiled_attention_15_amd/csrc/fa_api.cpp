@@ -195,7 +195,7 @@ struct NaiveLayout {
 
 bool naive_layout(int B, int H, int S, int D, NaiveLayout& L) {
     if (validate_shape(B, H, S, S, D, FA_F16) != FA_OK) return false;
-    const int64_t Sp = (S + 15) / 16 * 16;
+    const int64_t Sp = (S + 63) / 64 * 64;
     if (Sp > 16384 || (int64_t)B * H > 65535) return false;
     if (S * Sp * 4 >= (int64_t(1) << 31)) return false;
     auto r256 = [](int64_t x) { return (x + 255) / 256 * 256; };
@@ -250,7 +250,7 @@ int fa_naive_fwd(const void* q, const void* k, const void* v, void* o, float* ls
     p.vt = (uint16_t*)((char*)workspace + L.s_bytes + L.p_bytes);
     p.Sq = S;
     p.Sk = S;
-    p.Skp = (S + 15) / 16 * 16;
+    p.Skp = (S + 63) / 64 * 64;
     p.causal = causal != 0;
     p.scale = scale;
     const hipError_t err = fa::naive::launch_naive(p, B * H, D, dtype, (hipStream_t)stream);

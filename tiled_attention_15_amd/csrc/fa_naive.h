@@ -15,7 +15,7 @@ struct NaiveParams {
     float* s;          // workspace: scores, [BH, Sq, Skp] fp32
     uint16_t* p;       // workspace: probabilities, [BH, Sq, Skp] of the input dtype
     uint16_t* vt;      // workspace: V^T, [BH, D, Skp]
-    int Sq, Sk, Skp;   // Skp = Sk rounded up to a multiple of 16
+    int Sq, Sk, Skp;   // Skp = Sk rounded up to a multiple of 64
     int causal;
     float scale;
 };

@@ -18,7 +18,7 @@
 //
 // Workspace layout (caller-allocated, see fa_naive_workspace_bytes): per head
 // S as Sq x Skp fp32, then P as Sq x Skp of the input dtype, then V^T as
-// D x Skp, with Skp = Sk rounded up to a multiple of 16 and the padding
+// D x Skp, with Skp = Sk rounded up to a multiple of 64 and the padding
 // columns zero in P and V^T.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -199,14 +199,22 @@ __global__ __launch_bounds__(256) void naive_pv(NaiveParams p) {
         for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
     const int kq = 8 * (lane >> 5);
     const uint32_t arow = (uint32_t)(r0 + (lane & 31)) * p.Skp;
-    for (int k0 = 0; k0 < p.Skp; k0 += 16) {
-        const i32x4 af = __builtin_amdgcn_raw_buffer_load_b128(rp, (arow + k0 + kq) * 2, 0, 0);
+    // four 16-key steps per iteration (Skp is a multiple of 64): all their
+    // loads are issued before the first of their MFMAs
+    for (int k0 = 0; k0 < p.Skp; k0 += 64) {
+        i32x4 af[4], bf[4][D / 32];
 #pragma unroll
-        for (int b = 0; b < D / 32; ++b) {
-            const i32x4 bf = __builtin_amdgcn_raw_buffer_load_b128(
-                rv, ((uint32_t)(32 * b + (lane & 31)) * p.Skp + k0 + kq) * 2, 0, 0);
-            acc[b] = mma<DT>(af, bf, acc[b]);
+        for (int u = 0; u < 4; ++u) {
+            af[u] = __builtin_amdgcn_raw_buffer_load_b128(rp, (arow + k0 + 16 * u + kq) * 2, 0, 0);
+#pragma unroll
+            for (int b = 0; b < D / 32; ++b)
+                bf[u][b] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rv, ((uint32_t)(32 * b + (lane & 31)) * p.Skp + k0 + 16 * u + kq) * 2, 0, 0);
         }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int b = 0; b < D / 32; ++b) acc[b] = mma<DT>(af[u], bf[u][b], acc[b]);
     }
     uint16_t* O = (uint16_t*)p.o + (int64_t)bh * p.Sq * D;
 #pragma unroll
