@@ -11,6 +11,11 @@ attention formula of "FlashAttention-2 on Ascend NPU: how ops-transformer
 reaches 3x" (2048ai.net, section 1), with the causal reading that key j is
 visible to query i iff j <= i + (Sk - Sq).
 
+The backward (attention_bwd, attention_bwd_rows) is the chain-rule
+derivative of the same definition with the probability matrix materialised:
+dV = P^T dO, dS = P * (dO V^T - rowsum(P * dO V^T)), dQ = scale dS K,
+dK = scale dS^T Q.
+
 Inputs are numpy uint16 arrays holding the 16-bit patterns of the input
 dtype, contiguous, shaped [B, H, S, D].
 """
@@ -60,6 +65,13 @@ def _bind(lib):
         ctypes.c_float, ctypes.c_int, ctypes.c_int, i64p, ctypes.c_int64, f64p, f64p,
         ctypes.c_int]
     lib.ora_attention_rows.restype = ctypes.c_int
+    lib.ora_attention_bwd.argtypes = [u16p, u16p, u16p, u16p] + [ctypes.c_int] * 5 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_int, f64p, f64p, f64p, ctypes.c_int]
+    lib.ora_attention_bwd.restype = ctypes.c_int
+    lib.ora_attention_bwd_rows.argtypes = [u16p, u16p, u16p, u16p] + [ctypes.c_int] * 5 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_int, i64p, ctypes.c_int64, i64p, ctypes.c_int64,
+        f64p, f64p, f64p, ctypes.c_int]
+    lib.ora_attention_bwd_rows.restype = ctypes.c_int
     return lib
 
 
@@ -125,6 +137,59 @@ def attention_rows(q, k, v, rows, *, scale, causal, dtype, nthreads=0, lib=None)
     if rc != 0:
         raise RuntimeError("ora_attention_rows failed with code %d" % rc)
     return o, lse
+
+
+def attention_bwd(q, k, v, dout, *, scale, causal, dtype, nthreads=0, lib=None):
+    """Full backward.  q, dout: [B,H,Sq,D], k/v: [B,H,Sk,D] uint16 bit patterns.
+
+    Returns (dq [B,H,Sq,D], dk [B,H,Sk,D], dv [B,H,Sk,D]) float64: the
+    gradients of sum(O * dout) with respect to q, k and v."""
+    lib = lib or load()
+    q, qp = _u16(q)
+    k, kp = _u16(k)
+    v, vp = _u16(v)
+    dout, gp = _u16(dout)
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if k.shape != (B, H, Sk, D) or v.shape != k.shape or dout.shape != q.shape:
+        raise ValueError("shape mismatch q%s k%s v%s dout%s" % (q.shape, k.shape, v.shape, dout.shape))
+    dq = np.empty((B, H, Sq, D), dtype=np.float64)
+    dk = np.empty((B, H, Sk, D), dtype=np.float64)
+    dv = np.empty((B, H, Sk, D), dtype=np.float64)
+    rc = lib.ora_attention_bwd(qp, kp, vp, gp, B, H, Sq, Sk, D, ctypes.c_float(scale),
+                               int(bool(causal)), _DTYPES[dtype], _f64p(dq), _f64p(dk), _f64p(dv),
+                               int(nthreads))
+    if rc != 0:
+        raise RuntimeError("ora_attention_bwd failed with code %d" % rc)
+    return dq, dk, dv
+
+
+def attention_bwd_rows(q, k, v, dout, qrows, krows, *, scale, causal, dtype, nthreads=0, lib=None):
+    """Selected rows of the backward.  qrows: flat query ids (b*H + h)*Sq + i
+    (dQ rows); krows: flat key ids (b*H + h)*Sk + j (dK and dV rows).
+
+    Returns (dq [nq, D], dk [nk, D], dv [nk, D]) float64."""
+    lib = lib or load()
+    q, qp = _u16(q)
+    k, kp = _u16(k)
+    v, vp = _u16(v)
+    dout, gp = _u16(dout)
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    qrows = np.ascontiguousarray(qrows, dtype=np.int64)
+    krows = np.ascontiguousarray(krows, dtype=np.int64)
+    dq = np.empty((qrows.size, D), dtype=np.float64)
+    dk = np.empty((krows.size, D), dtype=np.float64)
+    dv = np.empty((krows.size, D), dtype=np.float64)
+    i64 = ctypes.POINTER(ctypes.c_int64)
+    rc = lib.ora_attention_bwd_rows(qp, kp, vp, gp, B, H, Sq, Sk, D, ctypes.c_float(scale),
+                                    int(bool(causal)), _DTYPES[dtype],
+                                    qrows.ctypes.data_as(i64), qrows.size,
+                                    krows.ctypes.data_as(i64), krows.size,
+                                    _f64p(dq), _f64p(dk), _f64p(dv), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("ora_attention_bwd_rows failed with code %d" % rc)
+    return dq, dk, dv
 
 
 def max_threads(lib=None):

@@ -98,12 +98,12 @@ static int visible(int64_t i, int64_t j, int64_t Sq, int64_t Sk, int causal) {
     return j <= i + (Sk - Sq);
 }
 
-/* One query row against all keys of its head: materialise the score row,
- * two-pass softmax, then the weighted sum of V.  qrow: D values; K, V:
- * Sk x D row-major; srow: Sk scratch.  Writes D outputs and the lse. */
-static void row_attention(const double* qrow, const double* K, const double* V, int64_t i,
-                          int64_t Sq, int64_t Sk, int D, double scale, int causal,
-                          double* srow, double* orow, double* lse_out) {
+/* Probabilities of one query row against all keys of its head: materialise
+ * the score row, then the two-pass softmax.  qrow: D values; K: Sk x D
+ * row-major; srow: Sk outputs, P_ij (0 where key j is hidden, all 0 when no
+ * key is visible).  Returns lse_i (-inf when no key is visible). */
+static double row_probs(const double* qrow, const double* K, int64_t i, int64_t Sq, int64_t Sk,
+                        int D, double scale, int causal, double* srow) {
     /* scores */
     for (int64_t j = 0; j < Sk; ++j) {
         if (!visible(i, j, Sq, Sk, causal)) { srow[j] = -INFINITY; continue; }
@@ -115,23 +115,34 @@ static void row_attention(const double* qrow, const double* K, const double* V, 
     /* pass 1: row maximum */
     double m = -INFINITY;
     for (int64_t j = 0; j < Sk; ++j) if (srow[j] > m) m = srow[j];
-    for (int d = 0; d < D; ++d) orow[d] = 0.0;
-    if (m == -INFINITY) { *lse_out = -INFINITY; return; }
-    /* pass 2: exponentials and their sum */
+    if (m == -INFINITY) {
+        for (int64_t j = 0; j < Sk; ++j) srow[j] = 0.0;
+        return -INFINITY;
+    }
+    /* pass 2: exponentials and their sum, then normalisation */
     double l = 0.0;
     for (int64_t j = 0; j < Sk; ++j) {
         double p = exp(srow[j] - m);
         srow[j] = p;
         l += p;
     }
-    /* normalised probabilities times V */
+    for (int64_t j = 0; j < Sk; ++j) srow[j] = srow[j] / l;
+    return m + log(l);
+}
+
+/* One query row of the forward: probabilities, then the weighted sum of V.
+ * V: Sk x D row-major; srow: Sk scratch.  Writes D outputs and the lse. */
+static void row_attention(const double* qrow, const double* K, const double* V, int64_t i,
+                          int64_t Sq, int64_t Sk, int D, double scale, int causal,
+                          double* srow, double* orow, double* lse_out) {
+    *lse_out = row_probs(qrow, K, i, Sq, Sk, D, scale, causal, srow);
+    for (int d = 0; d < D; ++d) orow[d] = 0.0;
     for (int64_t j = 0; j < Sk; ++j) {
-        double p = srow[j] / l;
+        double p = srow[j];
         if (p == 0.0) continue;
         const double* vr = V + j * D;
         for (int d = 0; d < D; ++d) orow[d] += p * vr[d];
     }
-    *lse_out = m + log(l);
 }
 
 static void set_threads(int nthreads) {
@@ -139,6 +150,14 @@ static void set_threads(int nthreads) {
     if (nthreads > 0) omp_set_num_threads(nthreads);
 #else
     (void)nthreads;
+#endif
+}
+
+static int thread_id(void) {
+#ifdef _OPENMP
+    return omp_get_thread_num();
+#else
+    return 0;
 #endif
 }
 
@@ -228,4 +247,238 @@ int ora_attention_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
         free(Qr); free(Kd); free(Vd); free(Sr);
     }
     return err;
+}
+
+/*
+ * Backward of the same definition: the gradients of L = sum_{i,d} O_id dO_id
+ * with respect to q, k and v, evaluated as the chain rule reads, one head at
+ * a time with the probability matrix materialised (nothing is tiled or
+ * recomputed here):
+ *
+ *   P_ij  = the forward's probabilities (row_probs)
+ *   dV_j  = sum_i P_ij dO_i
+ *   dP_ij = dO_i . v_j
+ *   dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik)     (Jacobian of the row softmax)
+ *   dQ_i  = scale sum_j dS_ij k_j
+ *   dK_j  = scale sum_i dS_ij q_i
+ *
+ * The pages say only that the backward pass recomputes the scores instead of
+ * storing them ("ops-transformer FlashAttention operator in practice",
+ * ai6s.net, section 2, table of core optimisations; "FlashAttention-2 on
+ * Ascend NPU" (2048ai.net), section 6.2 on checkpointing) and that it comes in
+ * a deterministic and a faster atomic-accumulation mode ("catlass
+ * FlashAttention tuning for a 13B service" (gsyq.cn), section on the
+ * backward pass).  The formulas above are the derivative of the forward's
+ * definition; both modes must reach them.
+ *
+ * q, k, v, dout: contiguous 16-bit patterns ([B,H,Sq,D] for q and dout,
+ * [B,H,Sk,D] for k and v).  dq: [B,H,Sq,D] fp64, dk, dv: [B,H,Sk,D] fp64.
+ */
+static void head_backward(const double* Qd, const double* Kd, const double* Vd, const double* dOd,
+                          int64_t Sq, int64_t Sk, int D, double sc, int causal,
+                          double* P, double* dS, double* dq, double* dk, double* dv) {
+    #pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t i = 0; i < Sq; ++i) {
+        double* prow = P + i * Sk;
+        double* srow = dS + i * Sk;
+        row_probs(Qd + i * D, Kd, i, Sq, Sk, D, sc, causal, prow);
+        const double* gi = dOd + i * D;
+        double rowdot = 0.0;
+        for (int64_t j = 0; j < Sk; ++j) {
+            const double* vr = Vd + j * D;
+            double dp = 0.0;
+            for (int d = 0; d < D; ++d) dp += gi[d] * vr[d];
+            srow[j] = dp;
+            rowdot += prow[j] * dp;
+        }
+        for (int64_t j = 0; j < Sk; ++j) srow[j] = prow[j] * (srow[j] - rowdot);
+        double* gq = dq + i * D;
+        for (int d = 0; d < D; ++d) gq[d] = 0.0;
+        for (int64_t j = 0; j < Sk; ++j) {
+            const double* kr = Kd + j * D;
+            for (int d = 0; d < D; ++d) gq[d] += srow[j] * kr[d];
+        }
+        for (int d = 0; d < D; ++d) gq[d] *= sc;
+    }
+    #pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t j = 0; j < Sk; ++j) {
+        double* gk = dk + j * D;
+        double* gv = dv + j * D;
+        for (int d = 0; d < D; ++d) { gk[d] = 0.0; gv[d] = 0.0; }
+        for (int64_t i = 0; i < Sq; ++i) {
+            const double pij = P[i * Sk + j], sij = dS[i * Sk + j];
+            const double* qr = Qd + i * D;
+            const double* gi = dOd + i * D;
+            for (int d = 0; d < D; ++d) {
+                gv[d] += pij * gi[d];
+                gk[d] += sij * qr[d];
+            }
+        }
+        for (int d = 0; d < D; ++d) gk[d] *= sc;
+    }
+}
+
+int ora_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
+                      int B, int H, int Sq, int Sk, int D, float scale, int causal, int dtype,
+                      double* dq, double* dk, double* dv, int nthreads) {
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || B < 0 || H < 0 || Sq < 0 || Sk < 0 || D <= 0)
+        return 1;
+    if (dtype != ORA_F16 && dtype != ORA_BF16) return 2;
+    set_threads(nthreads);
+    const double sc = (double)scale;
+    const int64_t qh = (int64_t)Sq * D, kh = (int64_t)Sk * D, ph = (int64_t)Sq * Sk;
+    double* Qd = (double*)malloc(sizeof(double) * (size_t)(qh > 0 ? qh : 1));
+    double* dOd = (double*)malloc(sizeof(double) * (size_t)(qh > 0 ? qh : 1));
+    double* Kd = (double*)malloc(sizeof(double) * (size_t)(kh > 0 ? kh : 1));
+    double* Vd = (double*)malloc(sizeof(double) * (size_t)(kh > 0 ? kh : 1));
+    double* P = (double*)malloc(sizeof(double) * (size_t)(ph > 0 ? ph : 1));
+    double* dS = (double*)malloc(sizeof(double) * (size_t)(ph > 0 ? ph : 1));
+    int rc = 0;
+    if (!Qd || !dOd || !Kd || !Vd || !P || !dS) {
+        rc = 3;
+    } else {
+        for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+            ora_decode(q + bh * qh, Qd, qh, dtype);
+            ora_decode(dout + bh * qh, dOd, qh, dtype);
+            ora_decode(k + bh * kh, Kd, kh, dtype);
+            ora_decode(v + bh * kh, Vd, kh, dtype);
+            head_backward(Qd, Kd, Vd, dOd, Sq, Sk, D, sc, causal, P, dS,
+                          dq + bh * qh, dk + bh * kh, dv + bh * kh);
+        }
+    }
+    free(Qd); free(dOd); free(Kd); free(Vd); free(P); free(dS);
+    return rc;
+}
+
+/*
+ * The same gradients on selected rows only, for checks at sizes where the
+ * full backward is too slow.  qrows[r] = (b*H + h)*Sq + i selects a dQ row;
+ * krows[r] = (b*H + h)*Sk + j selects a dK and a dV row.  A selected key
+ * needs every query row of its head (its column of P and dS), so each head
+ * named in krows costs one pass over all its rows; the rows are visited in
+ * parallel and each thread accumulates its own partial sums, added up in
+ * thread order afterwards.  dq: nq x D, dk and dv: nk x D (fp64).
+ */
+int ora_attention_bwd_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           const uint16_t* dout, int B, int H, int Sq, int Sk, int D, float scale,
+                           int causal, int dtype, const int64_t* qrows, int64_t nq,
+                           const int64_t* krows, int64_t nk, double* dq, double* dk, double* dv,
+                           int nthreads) {
+    if (!q || !k || !v || !dout || B < 0 || H < 0 || Sq < 0 || Sk < 0 || D <= 0) return 1;
+    if ((nq > 0 && (!qrows || !dq)) || (nk > 0 && (!krows || !dk || !dv))) return 1;
+    if (dtype != ORA_F16 && dtype != ORA_BF16) return 2;
+    const int64_t BH = (int64_t)B * H;
+    for (int64_t r = 0; r < nq; ++r) if (qrows[r] < 0 || qrows[r] >= BH * Sq) return 4;
+    for (int64_t r = 0; r < nk; ++r) if (krows[r] < 0 || krows[r] >= BH * Sk) return 4;
+    set_threads(nthreads);
+    const double sc = (double)scale;
+    const int64_t kh = (int64_t)Sk * D;
+    const int nthr = ora_max_threads();
+    const int64_t accn = 2 * (nk > 0 ? nk : 1) * (int64_t)D;
+    const size_t skn = (size_t)(Sk > 0 ? Sk : 1);
+    double* Kd = (double*)malloc(sizeof(double) * (size_t)(kh > 0 ? kh : 1));
+    double* Vd = (double*)malloc(sizeof(double) * (size_t)(kh > 0 ? kh : 1));
+    double* Qb = (double*)malloc(sizeof(double) * (size_t)nthr * D);
+    double* Gb = (double*)malloc(sizeof(double) * (size_t)nthr * D);
+    double* Pb = (double*)malloc(sizeof(double) * (size_t)nthr * skn);
+    double* Sb = (double*)malloc(sizeof(double) * (size_t)nthr * skn);
+    double* acc = (double*)malloc(sizeof(double) * (size_t)nthr * (size_t)accn);
+    if (!Kd || !Vd || !Qb || !Gb || !Pb || !Sb || !acc) {
+        free(Kd); free(Vd); free(Qb); free(Gb); free(Pb); free(Sb); free(acc);
+        return 3;
+    }
+    for (int64_t r = 0; r < nk; ++r)
+        for (int d = 0; d < D; ++d) { dk[r * D + d] = 0.0; dv[r * D + d] = 0.0; }
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        int64_t nq_h = 0, nk_h = 0;
+        for (int64_t r = 0; r < nq; ++r) nq_h += qrows[r] / Sq == bh;
+        for (int64_t r = 0; r < nk; ++r) nk_h += krows[r] / Sk == bh;
+        if (nq_h == 0 && nk_h == 0) continue;
+        ora_decode(k + bh * kh, Kd, kh, dtype);
+        ora_decode(v + bh * kh, Vd, kh, dtype);
+        /* query rows to visit: every row of the head when a key is selected */
+        const int64_t nvisit = nk_h > 0 ? Sq : 0;
+        for (int t = 0; t < nthr; ++t)
+            memset(acc + (size_t)t * accn, 0, sizeof(double) * (size_t)accn);
+        #pragma omp parallel num_threads(nthr)
+        {
+            const int t = thread_id();
+            double* Qr = Qb + (size_t)t * D;
+            double* Gr = Gb + (size_t)t * D;
+            double* Pr = Pb + (size_t)t * Sk;
+            double* Sr = Sb + (size_t)t * Sk;
+            double* ac = acc + (size_t)t * accn;
+            /* selected dQ rows of this head */
+            #pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < nq; ++r) {
+                if (qrows[r] / Sq != bh) continue;
+                const int64_t i = qrows[r] % Sq;
+                ora_decode(q + qrows[r] * D, Qr, D, dtype);
+                ora_decode(dout + qrows[r] * D, Gr, D, dtype);
+                row_probs(Qr, Kd, i, Sq, Sk, D, sc, causal, Pr);
+                double rowdot = 0.0;
+                for (int64_t j = 0; j < Sk; ++j) {
+                    const double* vr = Vd + j * D;
+                    double dp = 0.0;
+                    for (int d = 0; d < D; ++d) dp += Gr[d] * vr[d];
+                    Sr[j] = dp;
+                    rowdot += Pr[j] * dp;
+                }
+                double* gq = dq + r * D;
+                for (int d = 0; d < D; ++d) gq[d] = 0.0;
+                for (int64_t j = 0; j < Sk; ++j) {
+                    const double ds = Pr[j] * (Sr[j] - rowdot);
+                    const double* kr = Kd + j * D;
+                    for (int d = 0; d < D; ++d) gq[d] += ds * kr[d];
+                }
+                for (int d = 0; d < D; ++d) gq[d] *= sc;
+            }
+            /* every query row of the head, for the selected keys */
+            #pragma omp for schedule(static)
+            for (int64_t i = 0; i < nvisit; ++i) {
+                ora_decode(q + (bh * Sq + i) * D, Qr, D, dtype);
+                ora_decode(dout + (bh * Sq + i) * D, Gr, D, dtype);
+                row_probs(Qr, Kd, i, Sq, Sk, D, sc, causal, Pr);
+                double rowdot = 0.0;
+                for (int64_t j = 0; j < Sk; ++j) {
+                    if (Pr[j] == 0.0) continue;
+                    const double* vr = Vd + j * D;
+                    double dp = 0.0;
+                    for (int d = 0; d < D; ++d) dp += Gr[d] * vr[d];
+                    rowdot += Pr[j] * dp;
+                }
+                for (int64_t r = 0; r < nk; ++r) {
+                    if (krows[r] / Sk != bh) continue;
+                    const int64_t j = krows[r] % Sk;
+                    const double pij = Pr[j];
+                    if (pij == 0.0) continue;
+                    const double* vr = Vd + j * D;
+                    double dp = 0.0;
+                    for (int d = 0; d < D; ++d) dp += Gr[d] * vr[d];
+                    const double sij = pij * (dp - rowdot);
+                    double* av = ac + (r * 2) * D;
+                    double* ak = ac + (r * 2 + 1) * D;
+                    for (int d = 0; d < D; ++d) {
+                        av[d] += pij * Gr[d];
+                        ak[d] += sij * Qr[d];
+                    }
+                }
+            }
+        }
+        /* partial sums added up in thread order */
+        for (int t = 0; t < nthr; ++t) {
+            const double* ac = acc + (size_t)t * accn;
+            for (int64_t r = 0; r < nk; ++r) {
+                if (krows[r] / Sk != bh) continue;
+                for (int d = 0; d < D; ++d) {
+                    dv[r * D + d] += ac[(r * 2) * D + d];
+                    dk[r * D + d] += ac[(r * 2 + 1) * D + d];
+                }
+            }
+        }
+    }
+    for (int64_t r = 0; r < nk; ++r)
+        for (int d = 0; d < D; ++d) dk[r * D + d] *= sc;
+    free(Kd); free(Vd); free(Qb); free(Gb); free(Pb); free(Sb); free(acc);
+    return 0;
 }

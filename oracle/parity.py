@@ -11,6 +11,17 @@ LSE: |lse_gpu - lse_ref| <= 1e-4 * max(1, |lse_ref|).
 Infinite values (lse = -inf for a row that sees no key) must match exactly;
 such mismatches are counted separately because the differences they give
 are not finite.
+
+Gradients (dQ, dK, dV of the backward), per (batch, head) slice G of each:
+  max_e (|G_gpu - G_ref| - ulp(|G_ref|)/2) <= 3 u max|G_ref|   and
+  rms(G_gpu - G_ref) <= 2 u rms(G_ref),
+with u the unit roundoff of the input dtype (2^-8 for bf16, 2^-11 for fp16).
+Each gradient is a sum of products in which one factor (the recomputed
+probability P or the score gradient dS) is rounded to the input dtype before
+the fp32-accumulated product, a relative perturbation of at most u per term;
+an fp32 emulation of that rounding on N(0,1) inputs gives a largest error of
+about 1.25 u max|G| and an rms error of about 0.6 u rms(G).  A slice whose
+reference is all zero must be all zero.
 """
 import numpy as np
 
@@ -68,4 +79,45 @@ def ok(st):
 def assert_parity(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what=""):
     st = compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype)
     assert ok(st), "parity failed %s: %s" % (what, st)
+    return st
+
+
+GRAD_U = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+GRAD_MAX_C = 3.0
+GRAD_RMS_C = 2.0
+
+
+def compare_grad(g_gpu, g_ref, dtype):
+    """Error statistics of one gradient tensor [..., rows, D], per leading slice."""
+    g_gpu = np.asarray(g_gpu, dtype=np.float64)
+    g_ref = np.asarray(g_ref, dtype=np.float64)
+    lead = g_ref.shape[:-2] if g_ref.ndim > 2 else ()
+    gg = g_gpu.reshape((-1,) + g_gpu.shape[-2:]) if lead else g_gpu[None]
+    gr = g_ref.reshape((-1,) + g_ref.shape[-2:]) if lead else g_ref[None]
+    u = GRAD_U[dtype]
+    worst_max, worst_rms = 0.0, 0.0
+    nan = int(np.isnan(gg).sum()) + int(np.isinf(gg).sum())
+    zero_bad = 0
+    for a, r in zip(gg, gr):
+        d = np.abs(a - r)
+        m = float(np.max(np.abs(r))) if r.size else 0.0
+        rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+        if m == 0.0:
+            zero_bad += int(np.count_nonzero(a))
+            continue
+        net = float(np.max(d - 0.5 * ulp(r, dtype)))
+        worst_max = max(worst_max, net / (u * m))
+        worst_rms = max(worst_rms, float(np.sqrt(np.mean(d * d))) / (u * rms))
+    return {"max_in_u": worst_max, "rms_in_u": worst_rms, "nan_or_inf": nan,
+            "nonzero_where_zero": zero_bad}
+
+
+def grad_ok(st):
+    return (st["nan_or_inf"] == 0 and st["nonzero_where_zero"] == 0
+            and st["max_in_u"] <= GRAD_MAX_C and st["rms_in_u"] <= GRAD_RMS_C)
+
+
+def assert_grad_parity(g_gpu, g_ref, dtype, what=""):
+    st = compare_grad(g_gpu, g_ref, dtype)
+    assert grad_ok(st), "gradient parity failed %s: %s" % (what, st)
     return st

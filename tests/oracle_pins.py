@@ -15,6 +15,13 @@ Independent routes used here:
     their fused operator against exactly this routine: omica.com.cn learning
     path, "step three");
   * algebraic invariants (convexity, permutation, chunk merge).
+
+The backward (gradients of sum(O * dO)) is pinned by torch autograd through
+torch's fp64 scaled_dot_product_attention, by central differences of the
+40-digit forward on tiny shapes, by closed forms (one key; Q = 0) and by
+invariants (the key-shift symmetry gives sum_j dK_j = 0; rows of P sum to
+one give sum_j dV_j = sum_i dO_i; the scores' bilinearity gives
+sum_i q_i.dQ_i = sum_j k_j.dK_j).
 """
 from decimal import Decimal, getcontext
 from fractions import Fraction
@@ -254,6 +261,163 @@ def pin_unequal_causal_suffix(lib):
         assert np.array_equal(o[:, :, -1], o_nc[:, :, -1]) and np.array_equal(lse[:, :, -1], l_nc[:, :, -1])
 
 
+def _run_bwd(lib, q, k, v, g, scale, causal, dtype):
+    return oracle.attention_bwd(bits(q), bits(k), bits(v), bits(g), scale=scale, causal=causal,
+                                dtype=dtype, lib=lib)
+
+
+def _grad_inputs(B, H, Sq, Sk, D, dtype, seed, q_mult=1.0):
+    q, k, v = make_inputs(B, H, max(Sq, Sk), D, dtype, seed=seed, q_mult=q_mult, Sk=Sk)
+    q = q[:, :, :Sq].contiguous()
+    g, _, _ = make_inputs(B, H, Sq, D, dtype, seed=seed + 1000)
+    return q, k, v, g
+
+
+def pin_bwd_autograd(lib):
+    """torch autograd through torch's fp64 scaled_dot_product_attention (with a
+    bottom-right boolean mask when causal) gives the same three gradients."""
+    cases = (("f16", (1, 2, 64, 64, 32), False, 1.0), ("bf16", (2, 1, 45, 45, 16), True, 4.0),
+             ("f16", (1, 2, 30, 71, 16), True, 1.0), ("bf16", (1, 1, 33, 20, 64), False, 1.0))
+    for dtype, (B, H, Sq, Sk, D), causal, q_mult in cases:
+        q, k, v, g = _grad_inputs(B, H, Sq, Sk, D, dtype, seed=30 + Sq, q_mult=q_mult)
+        scale = softmax_scale(D)
+        dq, dk, dv = _run_bwd(lib, q, k, v, g, scale, causal, dtype)
+        Q, K, V = (torch.from_numpy(_f64(t)).requires_grad_() for t in (q, k, v))
+        mask = None
+        if causal:
+            i = torch.arange(Sq)[:, None]
+            j = torch.arange(Sk)[None, :]
+            mask = j <= i + (Sk - Sq)
+        o = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask, scale=scale)
+        (o * torch.from_numpy(_f64(g))).sum().backward()
+        for name, got, ref in (("dq", dq, Q.grad), ("dk", dk, K.grad), ("dv", dv, V.grad)):
+            ref = ref.numpy()
+            err = np.max(np.abs(got - ref))
+            assert err <= 1e-12 * max(1.0, np.max(np.abs(ref))), (name, dtype, Sq, Sk, causal, err)
+
+
+def _decimal_loss(Q, K, V, G, scale, causal):
+    """sum(O * G) of the definition at 40 digits (one head)."""
+    o, _ = _decimal_attention(Q, K, V, scale, causal)
+    return o, float(np.sum(o * G))
+
+
+def pin_bwd_finite_difference(lib):
+    """Central differences of the 40-digit forward: d/dx sum(O * dO) for single
+    entries of q, k and v against the oracle's gradients."""
+    getcontext().prec = 40
+    for dtype, Sq, Sk, D, causal in (("f16", 3, 4, 3, False), ("bf16", 4, 4, 2, True),
+                                     ("f16", 2, 5, 2, True)):
+        q, k, v, g = _grad_inputs(1, 1, Sq, Sk, D, dtype, seed=40 + Sq + Sk)
+        scale = softmax_scale(D)
+        dq, dk, dv = _run_bwd(lib, q, k, v, g, scale, causal, dtype)
+        Q, K, V, G = (_f64(t)[0, 0] for t in (q, k, v, g))
+        sc = Decimal(scale)
+
+        def loss(Qx, Kx, Vx):
+            tot = Decimal(0)
+            for i in range(Sq):
+                ws, num = [], [Decimal(0)] * D
+                for j in range(Sk):
+                    if not _visible(i, j, Sq, Sk, causal):
+                        continue
+                    s = sc * sum(Qx[i][d] * Kx[j][d] for d in range(D))
+                    w = s.exp()
+                    ws.append(w)
+                    for d in range(D):
+                        num[d] += w * Vx[j][d]
+                den = sum(ws)
+                for d in range(D):
+                    tot += num[d] / den * Decimal(float(G[i, d]))
+            return tot
+
+        dec = lambda A: [[Decimal(float(x)) for x in row] for row in A]
+        h = Decimal("1e-12")
+        for which, grad, rows in (("q", dq, Sq), ("k", dk, Sk), ("v", dv, Sk)):
+            for r in range(rows):
+                for d in range(D):
+                    X = {"q": dec(Q), "k": dec(K), "v": dec(V)}
+                    X[which][r][d] += h
+                    up = loss(X["q"], X["k"], X["v"])
+                    X[which][r][d] -= 2 * h
+                    dn = loss(X["q"], X["k"], X["v"])
+                    fd = float((up - dn) / (2 * h))
+                    assert abs(grad[0, 0, r, d] - fd) <= 1e-12 * max(1.0, abs(fd)), \
+                        (which, r, d, dtype, causal, grad[0, 0, r, d], fd)
+
+
+def pin_bwd_closed_forms(lib):
+    """One key: O_i = v_0 for every row that sees it (every row when
+    non-causal; with the bottom-right causal mask only the last one), so dV_0
+    is the sum of dO over those rows and dQ = dK = 0.
+    Q = 0 (non-causal): P = 1/Sk, so dV_j = (1/Sk) sum_i dO_i and
+    dQ_i = (scale/Sk) sum_j (dO_i . (v_j - mean v)) k_j."""
+    for dtype in ("f16", "bf16"):
+        q, k, v, g = _grad_inputs(2, 2, 13, 1, 16, dtype, seed=50)
+        for causal in (False, True):
+            dq, dk, dv = _run_bwd(lib, q, k, v, g, 0.25, causal, dtype)
+            G = _f64(g)
+            assert np.all(dq == 0.0) and np.all(dk == 0.0), (dtype, causal)
+            want = G[:, :, -1] if causal else G.sum(axis=2)
+            assert np.max(np.abs(dv[:, :, 0] - want)) <= 1e-13, (dtype, causal)
+        q, k, v, g = _grad_inputs(1, 2, 20, 31, 8, dtype, seed=51)
+        q = torch.zeros_like(q)
+        scale = softmax_scale(8)
+        dq, dk, dv = _run_bwd(lib, q, k, v, g, scale, False, dtype)
+        K, V, G = _f64(k), _f64(v), _f64(g)
+        Sk = K.shape[2]
+        assert np.max(np.abs(dv - G.sum(axis=2, keepdims=True) / Sk)) <= 1e-13, dtype
+        vc = V - V.mean(axis=2, keepdims=True)
+        w = np.einsum("bhid,bhjd->bhij", G, vc)
+        want = scale / Sk * np.einsum("bhij,bhjd->bhid", w, K)
+        assert np.max(np.abs(dq - want)) <= 1e-13, dtype
+        assert np.max(np.abs(dk)) == 0.0, dtype
+
+
+def pin_bwd_invariants(lib):
+    """sum_j dK_j = 0 (adding a vector to every key leaves O unchanged); rows of
+    P sum to one, so sum_j dV_j = sum of dO over rows that see a key; the
+    scores are bilinear in q and k, so sum_i q_i.dQ_i = sum_j k_j.dK_j; a row
+    that sees no key has dQ = 0 and its dO reaches no gradient."""
+    for dtype, (Sq, Sk), causal, q_mult in (("f16", (48, 48), False, 1.0), ("bf16", (48, 48), True, 4.0),
+                                            ("f16", (29, 64), True, 1.0), ("bf16", (64, 29), True, 1.0)):
+        q, k, v, g = _grad_inputs(1, 2, Sq, Sk, 16, dtype, seed=60 + Sq, q_mult=q_mult)
+        scale = softmax_scale(16)
+        dq, dk, dv = _run_bwd(lib, q, k, v, g, scale, causal, dtype)
+        Q, K, G = _f64(q), _f64(k), _f64(g)
+        big = max(1.0, np.max(np.abs(dk)))
+        assert np.max(np.abs(dk.sum(axis=2))) <= 1e-12 * big * Sk, (dtype, Sq, Sk, causal)
+        seen = np.array([Sk > 0 and (not causal or i + (Sk - Sq) >= 0) for i in range(Sq)])
+        assert np.max(np.abs(dv.sum(axis=2) - G[:, :, seen].sum(axis=2))) <= 1e-12 * Sq
+        lhs = np.sum(Q * dq)
+        rhs = np.sum(K * dk)
+        assert abs(lhs - rhs) <= 1e-12 * max(1.0, np.sum(np.abs(Q * dq))), (dtype, lhs, rhs)
+        if not seen.all():
+            assert np.all(dq[:, :, ~seen] == 0.0)
+            g2 = g.clone()
+            g2[:, :, torch.from_numpy(~seen)] = 0
+            dq2, dk2, dv2 = _run_bwd(lib, q, k, v, g2, scale, causal, dtype)
+            assert np.array_equal(dk2, dk) and np.array_equal(dv2, dv)
+
+
+def pin_bwd_rows_match_full(lib):
+    for dtype, (B, H, Sq, Sk), causal in (("bf16", (2, 3, 65, 65), True), ("f16", (1, 2, 40, 77), False),
+                                          ("f16", (1, 2, 50, 30), True)):
+        q, k, v, g = _grad_inputs(B, H, Sq, Sk, 32, dtype, seed=70 + Sq)
+        scale = softmax_scale(32)
+        dq, dk, dv = _run_bwd(lib, q, k, v, g, scale, causal, dtype)
+        qr = np.array([0, 1, Sq - 1, Sq, (B * H * Sq) // 2 + 3, B * H * Sq - 1], dtype=np.int64)
+        kr = np.array([0, Sk - 1, Sk + 2, B * H * Sk - 1, 5], dtype=np.int64)
+        a, b, c = oracle.attention_bwd_rows(bits(q), bits(k), bits(v), bits(g), qr, kr, scale=scale,
+                                            causal=causal, dtype=dtype, lib=lib)
+        scl = max(1.0, np.max(np.abs(dk)), np.max(np.abs(dv)))
+        assert np.max(np.abs(a - dq.reshape(-1, 32)[qr])) <= 1e-13 * scl, dtype
+        assert np.max(np.abs(b - dk.reshape(-1, 32)[kr])) <= 1e-13 * scl, dtype
+        assert np.max(np.abs(c - dv.reshape(-1, 32)[kr])) <= 1e-13 * scl, dtype
+
+
 ALL_PINS = [pin_decode_f16, pin_decode_bf16, pin_q_zero, pin_causal_row0, pin_convexity,
             pin_bruteforce_decimal, pin_sdpa_fp64, pin_chunk_merge, pin_invariances,
-            pin_rows_match_full, pin_unequal_causal_suffix]
+            pin_rows_match_full, pin_unequal_causal_suffix, pin_bwd_autograd,
+            pin_bwd_finite_difference, pin_bwd_closed_forms, pin_bwd_invariants,
+            pin_bwd_rows_match_full]

@@ -22,3 +22,30 @@ def test_oracle_rejects_bad_arguments(lib):
         oracle.attention_fwd(z.astype(np.float32), z, z, scale=1.0, causal=False, dtype="f16", lib=lib)
     with pytest.raises(RuntimeError):
         oracle.attention_rows(z, z, z, np.array([4]), scale=1.0, causal=False, dtype="f16", lib=lib)
+    with pytest.raises(RuntimeError):
+        oracle.attention_bwd_rows(z, z, z, z, np.array([0]), np.array([4]), scale=1.0,
+                                  causal=False, dtype="f16", lib=lib)
+    with pytest.raises(ValueError):
+        oracle.attention_bwd(z, z, z, z[:, :, :3], scale=1.0, causal=False, dtype="f16", lib=lib)
+
+
+def test_gradient_rule():
+    """The gradient parity rule accepts rounding-sized errors and rejects a
+    dropped term, a sign error and a value where the reference is zero."""
+    import numpy as np
+    from oracle import parity
+    rng = np.random.default_rng(0)
+    ref = rng.standard_normal((2, 3, 50, 16))
+    u = parity.GRAD_U["bf16"]
+    assert parity.grad_ok(parity.compare_grad(ref * (1 + u / 2), ref, "bf16"))
+    assert parity.grad_ok(parity.compare_grad(ref + u * rng.standard_normal(ref.shape) * 0.5, ref, "bf16"))
+    assert not parity.grad_ok(parity.compare_grad(ref * 0.98, ref, "bf16"))
+    bad = ref.copy()
+    bad[1, 2, 7, 3] = -bad[1, 2, 7, 3]
+    assert not parity.grad_ok(parity.compare_grad(bad, ref, "bf16"))
+    z = np.zeros((1, 1, 4, 4))
+    assert parity.grad_ok(parity.compare_grad(z, z, "f16"))
+    assert not parity.grad_ok(parity.compare_grad(z + 1e-30, z, "f16"))
+    nanv = ref.copy()
+    nanv[0, 0, 0, 0] = np.nan
+    assert not parity.grad_ok(parity.compare_grad(nanv, ref, "f16"))

@@ -29,12 +29,40 @@ MUTATIONS = [
     ("scale_missing", "srow[j] = scale * acc;", "srow[j] = acc;"),
     ("exp_sign", "double p = exp(srow[j] - m);", "double p = exp(m - srow[j]);"),
     ("exp_without_max", "double p = exp(srow[j] - m);", "double p = exp(srow[j]);"),
-    ("not_normalised", "double p = srow[j] / l;", "double p = srow[j];"),
+    ("not_normalised", "for (int64_t j = 0; j < Sk; ++j) srow[j] = srow[j] / l;", ""),
     ("v_rows_reversed", "const double* vr = V + j * D;", "const double* vr = V + (Sk - 1 - j) * D;"),
-    ("lse_drops_max", "*lse_out = m + log(l);", "*lse_out = log(l);"),
-    ("lse_log2", "*lse_out = m + log(l);", "*lse_out = m + log2(l);"),
+    ("lse_drops_max", "return m + log(l);", "return log(l);"),
+    ("lse_log2", "return m + log(l);", "return m + log2(l);"),
     ("rows_wrong_query", "ora_decode(q + rows[r] * D, Qr, D, dtype);",
      "ora_decode(q + (rows[r] ^ 1) * D, Qr, D, dtype);"),
+    # backward
+    ("bwd_rowdot_dropped", "for (int64_t j = 0; j < Sk; ++j) srow[j] = prow[j] * (srow[j] - rowdot);",
+     "for (int64_t j = 0; j < Sk; ++j) srow[j] = prow[j] * srow[j];"),
+    ("bwd_ds_sign", "for (int64_t j = 0; j < Sk; ++j) srow[j] = prow[j] * (srow[j] - rowdot);",
+     "for (int64_t j = 0; j < Sk; ++j) srow[j] = prow[j] * (rowdot - srow[j]);"),
+    ("bwd_rowdot_unweighted", "            rowdot += prow[j] * dp;\n", "            rowdot += dp;\n"),
+    ("bwd_dp_uses_keys", "            const double* vr = Vd + j * D;\n            double dp = 0.0;\n"
+     "            for (int d = 0; d < D; ++d) dp += gi[d] * vr[d];\n            srow[j] = dp;",
+     "            const double* vr = Kd + j * D;\n            double dp = 0.0;\n"
+     "            for (int d = 0; d < D; ++d) dp += gi[d] * vr[d];\n            srow[j] = dp;"),
+    ("bwd_dq_scale_missing", "            for (int d = 0; d < D; ++d) gq[d] += srow[j] * kr[d];\n        }\n"
+     "        for (int d = 0; d < D; ++d) gq[d] *= sc;",
+     "            for (int d = 0; d < D; ++d) gq[d] += srow[j] * kr[d];\n        }\n"),
+    ("bwd_dq_uses_values", "            const double* kr = Kd + j * D;\n            for (int d = 0; d < D; ++d) gq[d] += srow[j] * kr[d];",
+     "            const double* kr = Vd + j * D;\n            for (int d = 0; d < D; ++d) gq[d] += srow[j] * kr[d];"),
+    ("bwd_dq_uses_probs", "for (int d = 0; d < D; ++d) gq[d] += srow[j] * kr[d];",
+     "for (int d = 0; d < D; ++d) gq[d] += prow[j] * kr[d];"),
+    ("bwd_dk_scale_missing", "        for (int d = 0; d < D; ++d) gk[d] *= sc;\n", ""),
+    ("bwd_dv_uses_ds", "gv[d] += pij * gi[d];", "gv[d] += sij * gi[d];"),
+    ("bwd_dk_uses_dout", "gk[d] += sij * qr[d];", "gk[d] += sij * gi[d];"),
+    ("bwd_dk_uses_probs", "gk[d] += sij * qr[d];", "gk[d] += pij * qr[d];"),
+    ("bwd_dk_transposed", "const double pij = P[i * Sk + j], sij = dS[i * Sk + j];",
+     "const double pij = P[i * Sk + j], sij = dS[(Sq == Sk ? j * Sk + i : i * Sk + j)];"),
+    ("bwd_rows_rowdot_dropped", "const double sij = pij * (dp - rowdot);", "const double sij = pij * dp;"),
+    ("bwd_rows_dq_rowdot_dropped", "const double ds = Pr[j] * (Sr[j] - rowdot);", "const double ds = Pr[j] * Sr[j];"),
+    ("bwd_rows_dk_scale_missing", "for (int d = 0; d < D; ++d) dk[r * D + d] *= sc;",
+     "for (int d = 0; d < D; ++d) dk[r * D + d] *= 1.0;"),
+    ("bwd_rows_wrong_key", "const int64_t j = krows[r] % Sk;", "const int64_t j = (krows[r] + 1) % Sk;"),
 ]
 
 
