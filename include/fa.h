@@ -195,6 +195,52 @@ int fa_naive_fwd(const void* q, const void* k, const void* v, void* o, float* ls
  * D x Sp transposed values (16-bit), Sp = S rounded up to a multiple of 64. */
 int64_t fa_naive_workspace_bytes(int B, int H, int S, int D);
 
+/*
+ * fa_bwd -- gradients of the attention forward above: given dout = dL/dO,
+ * writes dq = dL/dq, dk = dL/dk and dv = dL/dv.  The scores and
+ * probabilities are recomputed from q, k and the forward's lse rather than
+ * stored ("ops-transformer FlashAttention operator in practice" (ai6s.net),
+ * section 2, table of core optimisations: recomputation in the backward;
+ * "FlashAttention-2 on Ascend NPU" (2048ai.net), section 6.2).  With
+ * P_ij = exp(scale q_i.k_j - lse_i) (0 where masked) and D_i = dout_i . o_i:
+ *   dv_j = sum_i P_ij dout_i,  dS_ij = P_ij (dout_i . v_j - D_i),
+ *   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i.
+ * The two accumulation modes of dq follow "catlass FlashAttention tuning for
+ * a 13B service" (gsyq.cn), backward-pass section:
+ *   deterministic != 0  dq by a separate pass in a fixed order: bitwise
+ *                       reproducible, the scores recomputed once more;
+ *   deterministic == 0  dq accumulated with fp32 atomic adds in the
+ *                       workspace while dk/dv are computed, then rounded;
+ *                       the last bits may differ from run to run.
+ *
+ *   q, o, dout, dq   device, contiguous [B,H,Sq,D] of `dtype`
+ *   k, v, dk, dv     device, contiguous [B,H,Sk,D] of `dtype`
+ *   lse              device, [B,H,Sq] fp32, as written by fa_fwd for the same
+ *                    q, k, v, scale and causal flag (natural log; -inf for a
+ *                    row that sees no key)
+ *   causal           key j visible to query i iff j <= i + (Sk - Sq)
+ *   workspace        device memory of at least
+ *                    fa_bwd_workspace_bytes(B,H,Sq,D,deterministic) bytes,
+ *                    16-byte aligned, owned by the caller, contents
+ *                    overwritten; it must not overlap any other argument
+ *   stream           HIP stream (NULL = default); asynchronous, no allocation
+ *                    and no synchronisation inside.
+ * All pointers 16-byte aligned.  Inputs may overlap each other; dq, dk, dv
+ * and the workspace must not overlap each other or any input (FA_ERR_ALIAS).
+ * Limits: D in {64, 128}; (max(Sq, Sk) rounded up to 128, plus 128) * D * 2
+ * bytes below 2^31.  Returns FA_OK or a status as for fa_fwd; nothing is
+ * enqueued on error.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk, int D,
+           float scale, int causal, int dtype, int deterministic, void* workspace,
+           int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace fa_bwd needs (0 for an invalid shape): the row dot
+ * products D_i, B*H*Sq fp32, plus in atomic mode (deterministic == 0) the
+ * fp32 dq accumulator, B*H*Sq*D fp32; each part rounded up to 256 bytes. */
+int64_t fa_bwd_workspace_bytes(int B, int H, int Sq, int D, int deterministic);
+
 #ifdef __cplusplus
 }
 #endif

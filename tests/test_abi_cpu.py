@@ -203,3 +203,37 @@ def test_naive_rejects_bad_arguments(lib):
     assert ncall(o=K) == 7
     assert ncall(scale=0.0) == 5
     assert ncall(D=96) == 3
+
+
+@fake_addresses
+def test_bwd_rejects_bad_arguments(lib):
+    B, H, Sq, Sk, D = 1, 2, 300, 200, 64
+    DO, DQ, DK, DV, W = 0x600000, 0x700000, 0x800000, 0x900000, 0x10000000
+    for det in (0, 1):
+        need = fa.fa_bwd_workspace_bytes(B, H, Sq, D, det)
+        rows = B * H * Sq
+        assert need == ((rows * 4 + 255) // 256 * 256) + (0 if det else (rows * D * 4 + 255) // 256 * 256)
+    assert fa.fa_bwd_workspace_bytes(1, 1, 0, 64, 1) == 0
+    assert fa.fa_bwd_workspace_bytes(1, 1, 16, 96, 1) == 0
+    need = fa.fa_bwd_workspace_bytes(B, H, Sq, D, 0)
+
+    def bcall(**kw):
+        a = dict(q=Q, k=K, v=V, o=O, do=DO, lse=L, dq=DQ, dk=DK, dv=DV, B=B, H=H, Sq=Sq, Sk=Sk, D=D,
+                 scale=0.125, causal=1, dtype=1, det=0, ws=W, wsb=need)
+        a.update(kw)
+        return fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                         a["B"], a["H"], a["Sq"], a["Sk"], a["D"], a["scale"], a["causal"], a["dtype"],
+                         a["det"], a["ws"], a["wsb"], None)
+
+    for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "ws"):
+        assert bcall(**{name: 0}) == 1, name
+    assert bcall(Sq=0) == 2 and bcall(B=0) == 2
+    assert bcall(wsb=need - 1) == 2
+    assert bcall(D=96) == 3 and bcall(dtype=2) == 3
+    assert bcall(Sk=1 << 24, wsb=1 << 40) == 2          # head span beyond 32-bit offsets
+    assert bcall(dk=DK + 8) == 4 and bcall(ws=W + 4) == 4
+    assert bcall(scale=float("nan")) == 5 and bcall(scale=-1.0) == 5
+    assert bcall(dq=Q) == 7                  # output over an input
+    assert bcall(dv=DK + 64) == 7            # two outputs overlap
+    assert bcall(ws=DO) == 7                 # workspace over an input
+    assert bcall(dk=W + 256) == 7            # output inside the workspace

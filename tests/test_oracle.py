@@ -46,6 +46,9 @@ def test_gradient_rule():
     z = np.zeros((1, 1, 4, 4))
     assert parity.grad_ok(parity.compare_grad(z, z, "f16"))
     assert not parity.grad_ok(parity.compare_grad(z + 1e-30, z, "f16"))
+    u16 = parity.GRAD_U["f16"]
+    assert parity.grad_ok(parity.compare_grad(z + 2 * u16, z, "f16", zero_scale=1.0))
+    assert not parity.grad_ok(parity.compare_grad(z + 4 * u16, z, "f16", zero_scale=1.0))
     nanv = ref.copy()
     nanv[0, 0, 0, 0] = np.nan
     assert not parity.grad_ok(parity.compare_grad(nanv, ref, "f16"))

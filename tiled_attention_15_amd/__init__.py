@@ -64,6 +64,11 @@ def _load():
     lib.fa_naive_fwd.restype = i
     lib.fa_naive_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_naive_workspace_bytes.restype = ctypes.c_int64
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp,
+                           ctypes.c_int64, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_bwd_workspace_bytes.restype = ctypes.c_int64
     _lib = lib
     return lib
 
@@ -118,6 +123,19 @@ def fa_naive_fwd(q, k, v, o, lse, B, H, S, D, scale, causal, dtype, workspace, w
 
 def fa_naive_workspace_bytes(B, H, S, D):
     return _load().fa_naive_workspace_bytes(int(B), int(H), int(S), int(D))
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, scale, causal, dtype, deterministic,
+           workspace, workspace_bytes, stream):
+    """C ABI fa_bwd: gradients dq, dk, dv of the forward given dout."""
+    return _load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                          _ptr(dk), _ptr(dv), B, H, Sq, Sk, D, float(scale), int(bool(causal)),
+                          int(dtype), int(bool(deterministic)), _ptr(workspace),
+                          int(workspace_bytes), _stream(stream))
+
+
+def fa_bwd_workspace_bytes(B, H, Sq, D, deterministic):
+    return _load().fa_bwd_workspace_bytes(B, H, Sq, D, int(bool(deterministic)))
 
 
 def fa_status_string(status):
@@ -223,3 +241,40 @@ def naive_forward(q, k, v, causal=False, scale=None, workspace=None):
     if st != 0:
         raise FaError(st, "fa_naive_fwd")
     return o, lse
+
+
+def backward(q, k, v, o, lse, dout, causal=False, scale=None, deterministic=True, workspace=None):
+    """Gradients (dq, dk, dv) of the forward on contiguous [B, H, Sq, D] q, o,
+    dout and [B, H, Sk, D] k, v GPU tensors, with o and lse from forward() on
+    the same inputs.  The workspace (allocated here with torch unless given as
+    a uint8 tensor of at least fa_bwd_workspace_bytes) holds the row dot
+    products and, when deterministic is False, the fp32 dq accumulator."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("fa: q/o/dout [B, H, Sq, D] and k/v [B, H, Sk, D] expected")
+    if q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+        raise ValueError("fa: q and k must share batch, heads and head dimension")
+    ts = (q, k, v, o, dout)
+    if not all(t.is_contiguous() for t in ts) or not lse.is_contiguous():
+        raise ValueError("fa: the backward takes contiguous tensors")
+    if not all(t.dtype == q.dtype for t in ts) or lse.dtype != torch.float32:
+        raise ValueError("fa: q, k, v, o, dout share one dtype; lse is float32")
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = fa_bwd_workspace_bytes(B, H, Sq, D, deterministic)
+    if need <= 0:
+        raise FaError(2, "fa_bwd_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream().cuda_stream
+    st = fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, scale, causal, _dtype_code(q),
+                deterministic, workspace, workspace.numel() * workspace.element_size(), stream)
+    if st != 0:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv

@@ -11,11 +11,12 @@
 
 #include "fa.h"
 #include "fa_launch.h"
+#include "fa_bwd.h"
 #include "fa_naive.h"
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 2 * 100 + 0;
 
 int validate_shape(int B, int H, int Sq, int Sk, int D, int dtype) {
     if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return FA_ERR_SHAPE;
@@ -254,6 +255,92 @@ int fa_naive_fwd(const void* q, const void* k, const void* v, void* o, float* ls
     p.causal = causal != 0;
     p.scale = scale;
     const hipError_t err = fa::naive::launch_naive(p, B * H, D, dtype, (hipStream_t)stream);
+    return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+namespace {
+
+struct BwdLayout {
+    int64_t dvec_bytes = 0, acc_bytes = 0, total = 0;
+};
+
+int64_t r256b(int64_t x) { return (x + 255) / 256 * 256; }
+
+bool bwd_layout(int B, int H, int Sq, int D, int deterministic, BwdLayout& L) {
+    if (B < 1 || H < 1 || Sq < 1 || (D != 64 && D != 128)) return false;
+    const int64_t rows = (int64_t)B * H * Sq;
+    L.dvec_bytes = r256b(rows * 4);
+    L.acc_bytes = deterministic ? 0 : r256b(rows * D * 4);
+    L.total = L.dvec_bytes + L.acc_bytes;
+    return true;
+}
+
+// Offsets inside one head are 32-bit: tiles reach up to 128 rows past the
+// sequence end.
+bool bwd_span_ok(int S, int D) {
+    const int64_t rows = ((int64_t)S + fa::bwd::kKeyBlock - 1) / fa::bwd::kKeyBlock * fa::bwd::kKeyBlock +
+                         fa::bwd::kKeyBlock;
+    return rows * D * 2 < (int64_t(1) << 31);
+}
+
+}  // namespace
+
+int64_t fa_bwd_workspace_bytes(int B, int H, int Sq, int D, int deterministic) {
+    BwdLayout L;
+    return bwd_layout(B, H, Sq, D, deterministic, L) ? L.total : 0;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk, int D,
+           float scale, int causal, int dtype, int deterministic, void* workspace,
+           int64_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
+    int st = validate_shape(B, H, Sq, Sk, D, dtype);
+    if (st != FA_OK) return st;
+    if (!bwd_span_ok(std::max(Sq, Sk), D)) return FA_ERR_SHAPE;
+    BwdLayout L;
+    if (!bwd_layout(B, H, Sq, D, deterministic, L) || workspace_bytes < L.total) return FA_ERR_SHAPE;
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)lse |
+         (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)workspace) & 15)
+        return FA_ERR_ALIGN;
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_SCALE;
+    const uintptr_t qb = (uintptr_t)((int64_t)B * H * Sq * D * 2);
+    const uintptr_t kb = (uintptr_t)((int64_t)B * H * Sk * D * 2);
+    const uintptr_t lb = (uintptr_t)((int64_t)B * H * Sq * 4);
+    const uintptr_t in[6][2] = {{(uintptr_t)q, (uintptr_t)q + qb},       {(uintptr_t)k, (uintptr_t)k + kb},
+                                {(uintptr_t)v, (uintptr_t)v + kb},       {(uintptr_t)o, (uintptr_t)o + qb},
+                                {(uintptr_t)dout, (uintptr_t)dout + qb}, {(uintptr_t)lse, (uintptr_t)lse + lb}};
+    const uintptr_t out[4][2] = {{(uintptr_t)dq, (uintptr_t)dq + qb},
+                                 {(uintptr_t)dk, (uintptr_t)dk + kb},
+                                 {(uintptr_t)dv, (uintptr_t)dv + kb},
+                                 {(uintptr_t)workspace, (uintptr_t)workspace + (uintptr_t)L.total}};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlap(out[i][0], out[i][1], in[j][0], in[j][1])) return FA_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(out[i][0], out[i][1], out[j][0], out[j][1])) return FA_ERR_ALIAS;
+    }
+
+    fa::bwd::BwdParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.dout = dout;
+    p.lse = lse;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.dvec = (float*)workspace;
+    p.dqacc = deterministic ? nullptr : (float*)((char*)workspace + L.dvec_bytes);
+    p.Sq = Sq;
+    p.Sk = Sk;
+    p.BH = B * H;
+    p.nkb = (Sk + fa::bwd::kKeyBlock - 1) / fa::bwd::kKeyBlock;
+    p.nqb = (Sq + fa::bwd::kQueryBlock - 1) / fa::bwd::kQueryBlock;
+    p.scale = scale;
+    p.scale_log2e = scale * 1.4426950408889634f;
+    const hipError_t err = fa::bwd::launch_bwd(p, D, dtype, causal != 0, deterministic != 0, (hipStream_t)stream);
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

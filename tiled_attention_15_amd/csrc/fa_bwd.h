@@ -1,0 +1,40 @@
+// fa_bwd.h -- internal interface of the attention backward kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+namespace bwd {
+
+struct BwdParams {
+    const void* q;      // [BH, Sq, D] contiguous, input dtype
+    const void* k;      // [BH, Sk, D]
+    const void* v;      // [BH, Sk, D]
+    const void* o;      // [BH, Sq, D]  forward output
+    const void* dout;   // [BH, Sq, D]  gradient of the output
+    const float* lse;   // [BH, Sq]     forward row log-sum-exp (natural log)
+    void* dq;           // [BH, Sq, D]
+    void* dk;           // [BH, Sk, D]
+    void* dv;           // [BH, Sk, D]
+    float* dvec;        // workspace [BH, Sq]: rowsum(dout * o)
+    float* dqacc;       // workspace [BH, Sq, D] fp32 (atomic mode), else null
+    int Sq, Sk, BH;
+    int nkb;            // key blocks of the dK/dV kernel per head
+    int nqb;            // query blocks of the dQ kernel per head
+    float scale;        // softmax scale
+    float scale_log2e;  // scale * log2(e)
+};
+
+constexpr int kKeyBlock = 128;   // keys per dK/dV workgroup (32 per wave)
+constexpr int kQueryTile = 64;   // queries per step of the dK/dV kernel
+constexpr int kQueryBlock = 128; // queries per dQ workgroup (32 per wave)
+constexpr int kKeyTile = 64;     // keys per step of the dQ kernel
+
+// Enqueue the backward on `stream`: row dot products (and, in atomic mode,
+// the zeroing of the fp32 dQ accumulator), the dK/dV kernel, then either the
+// dQ kernel (deterministic) or the conversion of the accumulator (atomic).
+hipError_t launch_bwd(const BwdParams& p, int D, int dtype, int causal, int deterministic,
+                      hipStream_t stream);
+
+}  // namespace bwd
+}  // namespace fa

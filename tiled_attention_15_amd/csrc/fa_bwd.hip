@@ -1,0 +1,635 @@
+// fa_bwd.hip -- attention backward for gfx950 (MI355X).
+//
+// Gradients of the loss sum(O * dO) with respect to Q, K and V.  The score
+// and probability tiles are recomputed from Q, K and the forward's row
+// log-sum-exp instead of being stored ("ops-transformer FlashAttention
+// operator in practice" (ai6s.net), section 2, table of core optimisations:
+// recomputation in the backward pass; "FlashAttention-2 on Ascend NPU"
+// (2048ai.net), section 6.2: the forward keeps no attention matrix, so the
+// backward recomputes it).  Two accumulation modes for dQ, after "catlass
+// FlashAttention tuning for a 13B service" (gsyq.cn), backward-pass section:
+//   deterministic  a second kernel owns each dQ row and sums its key tiles in
+//                  a fixed order (scores recomputed once more);
+//   atomic         the dK/dV kernel adds each key block's dQ contribution to
+//                  an fp32 accumulator with hardware float atomics; the order
+//                  of the additions, hence the last bits, varies run to run.
+//
+// Per (batch, head), with P_ij = exp(scale q_i.k_j - lse_i) (0 where hidden)
+// and D_i = dO_i . O_i (= sum_j P_ij dP_ij):
+//   dV_j = sum_i P_ij dO_i,   dP_ij = dO_i . v_j,   dS_ij = P_ij (dP_ij - D_i),
+//   dQ_i = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i.
+//
+// Kernels:
+//   bwd_pre   D_i for every row (and zeroes the dQ accumulator in atomic mode);
+//   bwd_dkdv  one workgroup per 128-key block (32 keys per wave, K and V of
+//             those keys resident in registers); 64-query tiles of Q and dO
+//             stream through LDS (double-buffered, staged through registers);
+//             per tile S = Q K^T and dP = dO V^T on the matrix cores (queries
+//             on MFMA rows, keys on columns), P and dS in fp32 registers, then
+//             dV^T += dO^T P and dK^T += Q^T dS with P and dS taken straight
+//             from the accumulators as B operands and dO^T, Q^T read from LDS
+//             by transposing reads (ds_read_b64_tr_b16);
+//   bwd_dq    (deterministic) one workgroup per 128-query block (32 queries
+//             per wave, Q and dO resident); 64-key tiles of K and V stream
+//             through LDS; S^T = K Q^T, dP^T = V dO^T, then dQ^T += K^T dS^T;
+//   bwd_dq_convert  (atomic) dQ = scale * accumulator, rounded to the dtype.
+//
+// Operand layout of v_mfma_f32_32x32x16: lane l supplies row (A) or column
+// (B) l%32 and the 8 k-values in slots 8*(l/32)..+7; accumulator register r
+// of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.  Taking the
+// accumulator of one product as an operand of the next makes k-slot e of
+// lane half g in k-step s stand for row 16*s + 8*(e/4) + 4*g + e%4; the LDS
+// operand of that product is read with the same mapping: two transposing
+// reads, each of four consecutive rows.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_bwd.h"
+
+namespace fa {
+namespace bwd {
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) char lds_t;
+
+constexpr float LOG2E = 1.4426950408889634f;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                             (int)(bytes < 0x80000000ull ? bytes : 0x7fffffffull),
+                                             (int)0x00020000);
+}
+
+template <int DT>
+__device__ __forceinline__ f32x16 mma(i32x4 a, i32x4 b, f32x16 c) {
+    if constexpr (DT == 0)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Two fp32 -> one dword of two 16-bit values (round to nearest even).
+template <int DT>
+__device__ __forceinline__ int pack2(float x, float y) {
+    if constexpr (DT == 0)
+        return __builtin_bit_cast(int, __builtin_convertvector((f32x2){x, y}, f16x2));
+    else
+        return __builtin_bit_cast(int, __builtin_convertvector((f32x2){x, y}, bf16x2));
+}
+
+// The 16-bit value in the low (hi = 0) or high half of a dword, as fp32.
+template <int DT>
+__device__ __forceinline__ float half_f32(int w, int hi) {
+    const uint32_t h = ((uint32_t)w >> (16 * hi)) & 0xffffu;
+    if constexpr (DT == 0)
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+    else
+        return __uint_as_float(h << 16);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+    f32x16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+    return z;
+}
+
+// LDS tiles are [rows][W] 16-bit values (W = 64 or 128), stored in 16-byte
+// chunks whose index within the row is XOR-ed with swz(row).  A fragment
+// read (16 lanes on 16 consecutive rows, one chunk each) and a transposing
+// read (16 lanes on four consecutive rows, two adjacent chunks each) both
+// fall on distinct chunk positions.
+template <int W>
+__device__ __forceinline__ int swz(int r) {
+    const int f = ((r & 3) << 1) | ((r >> 2) & 1);
+    if constexpr (W == 128)
+        return f | (((r >> 3) & 1) << 3);
+    else
+        return f;
+}
+template <int W>
+__device__ __forceinline__ int toff(int r, int ch) {
+    return r * (2 * W) + ((ch ^ swz<W>(r)) << 4);
+}
+
+// Operand fragment by rows: 8 consecutive values (chunk ch) of row r.
+template <int W>
+__device__ __forceinline__ i32x4 row_frag(const lds_t* tile, int r, int ch) {
+    return *(const __attribute__((address_space(3))) i32x4*)(tile + toff<W>(r, ch));
+}
+
+// Per-lane constants of the transposing reads: source lane 4j + t of each
+// 16-lane group G addresses row 4*(G/2) + j (+16 s, +8 for the second read)
+// and columns 16*(G%2) + 4t .. +3 of a 32-column block.
+struct TrLane {
+    int row, ch, byte;
+};
+__device__ __forceinline__ TrLane tr_lane(int lane) {
+    const int G = lane >> 4, m = lane & 15;
+    return {4 * (G >> 1) + (m >> 2), 2 * (G & 1) + ((m & 3) >> 1), (m & 1) * 8};
+}
+
+// Operand fragment of column block b (columns 32b + lane%32) over rows
+// 16s .. 16s+15 in the k-slot order above.
+template <int W>
+__device__ __forceinline__ i32x4 tr_frag(const lds_t* tile, int s, int b, const TrLane& tl) {
+    const int r0 = 16 * s + tl.row, r1 = r0 + 8, ch = 4 * b + tl.ch;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(tile + r0 * (2 * W) + ((ch ^ swz<W>(r0)) << 4) + tl.byte));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(tile + r1 * (2 * W) + ((ch ^ swz<W>(r1)) << 4) + tl.byte));
+    i32x4 a;
+    a[0] = (int)(uint16_t)lo[0] | ((int)(uint16_t)lo[1] << 16);
+    a[1] = (int)(uint16_t)lo[2] | ((int)(uint16_t)lo[3] << 16);
+    a[2] = (int)(uint16_t)hi[0] | ((int)(uint16_t)hi[1] << 16);
+    a[3] = (int)(uint16_t)hi[2] | ((int)(uint16_t)hi[3] << 16);
+    return a;
+}
+
+// B operand of k-step s from a 32-row-block pair of accumulators (rows
+// 32*(s/2) .. of the product), packed to 16 bits.
+template <int DT>
+__device__ __forceinline__ i32x4 acc_frag(const f32x16& x, int h) {
+    i32x4 a;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = pack2<DT>(x[8 * h + 2 * i], x[8 * h + 2 * i + 1]);
+    return a;
+}
+
+// Workgroup -> (batch*head, block).  When the head count is a multiple of 8,
+// each XCD (workgroup ids are dealt round-robin over the 8 XCDs) takes a
+// contiguous range of heads, so the blocks of a head share one L2.  Blocks
+// of a head come in slot order; `reverse` hands out the last block first.
+__device__ __forceinline__ void block_order(int wg, int nblk, int BH, bool reverse, int& bh, int& blk) {
+    int slot;
+    if ((BH & 7) == 0) {
+        const int xcd = wg & 7, k = wg >> 3, hpx = BH >> 3;
+        bh = xcd * hpx + k % hpx;
+        slot = k / hpx;
+    } else {
+        bh = wg % BH;
+        slot = wg / BH;
+    }
+    blk = reverse ? (nblk - 1 - slot) : slot;
+}
+
+// ---------------------------------------------------------------------------
+// D_i = sum_d dO_id O_id in fp32; in atomic mode also zero the dQ accumulator.
+template <int D, int DT>
+__global__ __launch_bounds__(256) void bwd_pre(BwdParams p) {
+    constexpr int TPR = D / 8;            // threads per row (8 values each)
+    constexpr int RPB = 256 / TPR;        // rows per workgroup
+    const int64_t rows = (int64_t)p.BH * p.Sq;
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+    const int c = threadIdx.x % TPR;
+    float acc = 0.0f;
+    if (row < rows) {
+        const int64_t off = row * D + 8 * c;
+        const i32x4 a = *(const i32x4*)((const uint16_t*)p.o + off);
+        const i32x4 b = *(const i32x4*)((const uint16_t*)p.dout + off);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc += half_f32<DT>(a[i], 0) * half_f32<DT>(b[i], 0) + half_f32<DT>(a[i], 1) * half_f32<DT>(b[i], 1);
+        if (p.dqacc) {
+            const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+            *(f32x4*)(p.dqacc + off) = z;
+            *(f32x4*)(p.dqacc + off + 4) = z;
+        }
+    }
+#pragma unroll
+    for (int o = TPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    if (row < rows && c == 0) p.dvec[row] = acc;
+}
+
+// dQ = scale * accumulator, rounded to the dtype (atomic mode).
+template <int DT>
+__global__ __launch_bounds__(256) void bwd_dq_convert(BwdParams p, int64_t n8) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n8) return;
+    const f32x4 a = *(const f32x4*)(p.dqacc + 8 * i);
+    const f32x4 b = *(const f32x4*)(p.dqacc + 8 * i + 4);
+    const float s = p.scale;
+    i32x4 w;
+    w[0] = pack2<DT>(a[0] * s, a[1] * s);
+    w[1] = pack2<DT>(a[2] * s, a[3] * s);
+    w[2] = pack2<DT>(b[0] * s, b[1] * s);
+    w[3] = pack2<DT>(b[2] * s, b[3] * s);
+    *(i32x4*)((uint16_t*)p.dq + 8 * i) = w;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV (and in atomic mode the dQ contributions) of one 128-key block.
+template <int D, int DT, bool CAUSAL, bool ATOMIC>
+__global__ __launch_bounds__(256) void bwd_dkdv(BwdParams p) {
+    constexpr int DC = D / 16;                         // k-steps over the head dimension
+    constexpr int DB = D / 32;                         // 32-column blocks of the head dimension
+    constexpr int QT = kQueryTile;
+    constexpr int TILE = QT * D * 2;                   // bytes of one Q or dO tile
+    constexpr int CPT = QT * D / 8 / 256;              // 16-byte chunks per thread per tile
+    constexpr int KBLK = ATOMIC ? kKeyBlock * D * 2 : 0;
+    constexpr int DSB = ATOMIC ? kKeyBlock * QT * 2 : 0;
+    constexpr int KCPT = kKeyBlock * D / 8 / 256;
+    static_assert(CPT >= 1 && KCPT >= 1, "tile must split over the threads");
+
+    __shared__ __attribute__((aligned(16))) char smem[4 * TILE + KBLK + DSB];
+    __shared__ __attribute__((aligned(16))) float lse_s[2][QT];
+    __shared__ __attribute__((aligned(16))) float dv_s[2][QT];
+    lds_t* const sm = (lds_t*)smem;
+
+    const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, g = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int bh, kb;
+    block_order(blockIdx.x, p.nkb, p.BH, false, bh, kb);
+    const int Sq = p.Sq, Sk = p.Sk, diag = Sk - Sq;
+    const int k0 = kb * kKeyBlock, kw0 = k0 + 32 * w;
+
+    const char* qh = (const char*)p.q + (int64_t)bh * Sq * D * 2;
+    const char* doh = (const char*)p.dout + (int64_t)bh * Sq * D * 2;
+    const __amdgpu_buffer_rsrc_t rq = rsrc(qh, (uint64_t)Sq * D * 2);
+    const __amdgpu_buffer_rsrc_t rdo = rsrc(doh, (uint64_t)Sq * D * 2);
+    const __amdgpu_buffer_rsrc_t rk = rsrc((const char*)p.k + (int64_t)bh * Sk * D * 2, (uint64_t)Sk * D * 2);
+    const __amdgpu_buffer_rsrc_t rv = rsrc((const char*)p.v + (int64_t)bh * Sk * D * 2, (uint64_t)Sk * D * 2);
+    const __amdgpu_buffer_rsrc_t rl = rsrc(p.lse + (int64_t)bh * Sq, (uint64_t)Sq * 4);
+    const __amdgpu_buffer_rsrc_t rdv = rsrc(p.dvec + (int64_t)bh * Sq, (uint64_t)Sq * 4);
+
+    // K and V of this wave's 32 keys as B operands (key = column lq, 8 values
+    // of the head dimension per k-step); keys past Sk read as zero.  In
+    // atomic mode the K block is in LDS anyway and its fragments are read
+    // from there at each use, which leaves registers for the dQ product.
+    i32x4 kf[ATOMIC ? 1 : DC], vf[DC];
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+        if constexpr (!ATOMIC)
+            kf[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((kw0 + lq) * D + 16 * c + 8 * g) * 2, 0, 0);
+        vf[c] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((kw0 + lq) * D + 16 * c + 8 * g) * 2, 0, 0);
+    }
+    if constexpr (ATOMIC) {
+        // the whole key block in LDS, for the dQ product
+#pragma unroll
+        for (int i = 0; i < KCPT; ++i) {
+            const int ci = tid + 256 * i, r = ci / (D / 8), ch = ci % (D / 8);
+            const i32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rk, ((k0 + r) * D + 8 * ch) * 2, 0, 0);
+            *(__attribute__((address_space(3))) i32x4*)(sm + 4 * TILE + toff<D>(r, ch)) = x;
+        }
+    }
+
+    const lds_t* kblk = sm + 4 * TILE;
+    const int nqt = (Sq + QT - 1) / QT;
+    int t0 = 0;
+    if (CAUSAL) t0 = max(0, k0 - diag) / QT;
+
+    // Staging of the next query tile in registers.
+    i32x4 sq[CPT], sd[CPT];
+    float sl = 0.0f;
+    auto fetch = [&](int t) {
+        const int q0 = t * QT;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int ci = tid + 256 * i, r = ci / (D / 8), ch = ci % (D / 8);
+            sq[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, ((q0 + r) * D + 8 * ch) * 2, 0, 0);
+            sd[i] = __builtin_amdgcn_raw_buffer_load_b128(rdo, ((q0 + r) * D + 8 * ch) * 2, 0, 0);
+        }
+        if (tid < QT)
+            sl = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, (q0 + tid) * 4, 0, 0));
+        else if (tid < 2 * QT)
+            sl = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdv, (q0 + tid - QT) * 4, 0, 0));
+    };
+    auto commit = [&](int buf) {
+        lds_t* tq = sm + buf * 2 * TILE;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int ci = tid + 256 * i, r = ci / (D / 8), ch = ci % (D / 8);
+            *(__attribute__((address_space(3))) i32x4*)(tq + toff<D>(r, ch)) = sq[i];
+            *(__attribute__((address_space(3))) i32x4*)(tq + TILE + toff<D>(r, ch)) = sd[i];
+        }
+        if (tid < QT)
+            lse_s[buf][tid] = sl * LOG2E;
+        else if (tid < 2 * QT)
+            dv_s[buf][tid - QT] = sl;
+    };
+
+    const TrLane tl = tr_lane(lane);
+    const float c2 = p.scale_log2e;
+    const int key = kw0 + lq;
+    f32x16 dva[DB], dka[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+        dva[b] = zero16();
+        dka[b] = zero16();
+    }
+
+    if (t0 < nqt) {
+        fetch(t0);
+        commit(0);
+    }
+    __syncthreads();
+
+    for (int t = t0; t < nqt; ++t) {
+        const int buf = (t - t0) & 1;
+        if (t + 1 < nqt) fetch(t + 1);
+        const lds_t* tq = sm + buf * 2 * TILE;
+        const lds_t* tdo = tq + TILE;
+        const int q0 = t * QT;
+
+        // S = Q K^T and dP = dO V^T for 64 queries x this wave's 32 keys
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            s[rb] = zero16();
+            dp[rb] = zero16();
+        }
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                i32x4 kc;
+                if constexpr (ATOMIC)
+                    kc = row_frag<D>(kblk, 32 * w + lq, 2 * c + g);
+                else
+                    kc = kf[c];
+                s[rb] = mma<DT>(row_frag<D>(tq, 32 * rb + lq, 2 * c + g), kc, s[rb]);
+                dp[rb] = mma<DT>(row_frag<D>(tdo, 32 * rb + lq, 2 * c + g), vf[c], dp[rb]);
+            }
+        }
+
+        // P = exp2(s * scale*log2e - lse*log2e), dS = P (dP - D_i)
+        const bool need_mask = (q0 + QT > Sq) || (kw0 + 32 > Sk) || (CAUSAL && kw0 + 31 > q0 + diag);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const int qr = 32 * rb + 8 * a + 4 * g;
+                const f32x4 l4 = *(const f32x4*)&lse_s[buf][qr];
+                const f32x4 d4 = *(const f32x4*)&dv_s[buf][qr];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * a + e;
+                    float pv = __builtin_amdgcn_exp2f(s[rb][r] * c2 - l4[e]);
+                    if (need_mask) {
+                        const int qi = q0 + qr + e;
+                        const bool vis = qi < Sq && key < Sk && (!CAUSAL || key <= qi + diag);
+                        pv = vis ? pv : 0.0f;
+                    }
+                    s[rb][r] = pv;
+                    dp[rb][r] = pv * (dp[rb][r] - d4[e]);
+                }
+            }
+        }
+
+        // dV^T += dO^T P, dK^T += Q^T dS  (rows: head dimension, columns: keys)
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const i32x4 pa = acc_frag<DT>(s[st >> 1], st & 1);
+            const i32x4 da = acc_frag<DT>(dp[st >> 1], st & 1);
+#pragma unroll
+            for (int b = 0; b < DB; ++b) {
+                dva[b] = mma<DT>(tr_frag<D>(tdo, st, b, tl), pa, dva[b]);
+                dka[b] = mma<DT>(tr_frag<D>(tq, st, b, tl), da, dka[b]);
+            }
+        }
+
+        if constexpr (ATOMIC) {
+            // dS^T of this wave's keys into LDS as [key][query], then
+            // dQ[q][d] += sum over the block's 128 keys of dS[q][key] K[key][d].
+            lds_t* dst = sm + 4 * TILE + KBLK;
+            const int kr = 32 * w + lq;
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    i32x2 v2;
+                    v2[0] = pack2<DT>(dp[rb][4 * a], dp[rb][4 * a + 1]);
+                    v2[1] = pack2<DT>(dp[rb][4 * a + 2], dp[rb][4 * a + 3]);
+                    *(__attribute__((address_space(3))) i32x2*)(dst + toff<QT>(kr, 4 * rb + a) + 8 * g) = v2;
+                }
+            }
+            __syncthreads();
+            constexpr int NBLK = 2 * DB / 4;           // 32x32 output blocks per wave
+#pragma unroll
+            for (int ob = 0; ob < NBLK; ++ob) {
+                const int id = w * NBLK + ob;
+                const int rbq = id & 1, db = id >> 1;
+                f32x16 acc = zero16();
+#pragma unroll
+                for (int st = 0; st < kKeyBlock / 16; ++st)
+                    acc = mma<DT>(tr_frag<QT>(dst, st, rbq, tl), tr_frag<D>(kblk, st, db, tl), acc);
+                float* base = p.dqacc + ((int64_t)bh * Sq) * D + 32 * db + lq;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int qi = q0 + 32 * rbq + 8 * (r >> 2) + 4 * g + (r & 3);
+                    if (qi < Sq) unsafeAtomicAdd(base + (int64_t)qi * D, acc[r]);
+                }
+            }
+        }
+
+        if (t + 1 < nqt) commit(buf ^ 1);
+        __syncthreads();
+    }
+
+    // dK^T (times scale) and dV^T: register r of block b holds head-dimension
+    // index 32b + 8(r/4) + 4g + r%4 of key `key`: four consecutive values per
+    // 8-byte store; stores past Sk are dropped by the buffer range.
+    const __amdgpu_buffer_rsrc_t wk = rsrc((char*)p.dk + (int64_t)bh * Sk * D * 2, (uint64_t)Sk * D * 2);
+    const __amdgpu_buffer_rsrc_t wv = rsrc((char*)p.dv + (int64_t)bh * Sk * D * 2, (uint64_t)Sk * D * 2);
+    const float sc = p.scale;
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const uint32_t off = (uint32_t)((key * D + 32 * b + 8 * a + 4 * g) * 2);
+            i32x2 kv, vv;
+            kv[0] = pack2<DT>(dka[b][4 * a] * sc, dka[b][4 * a + 1] * sc);
+            kv[1] = pack2<DT>(dka[b][4 * a + 2] * sc, dka[b][4 * a + 3] * sc);
+            vv[0] = pack2<DT>(dva[b][4 * a], dva[b][4 * a + 1]);
+            vv[1] = pack2<DT>(dva[b][4 * a + 2], dva[b][4 * a + 3]);
+            __builtin_amdgcn_raw_buffer_store_b64(kv, wk, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(vv, wv, off, 0, 0);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ of one 128-query block (deterministic mode).
+template <int D, int DT, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_dq(BwdParams p) {
+    constexpr int DC = D / 16, DB = D / 32;
+    constexpr int KT = kKeyTile;
+    constexpr int TILE = KT * D * 2;
+    constexpr int CPT = KT * D / 8 / 256;
+    static_assert(CPT >= 1, "tile must split over the threads");
+
+    __shared__ __attribute__((aligned(16))) char smem[4 * TILE];
+    lds_t* const sm = (lds_t*)smem;
+
+    const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, g = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int bh, qb;
+    block_order(blockIdx.x, p.nqb, p.BH, CAUSAL, bh, qb);
+    const int Sq = p.Sq, Sk = p.Sk, diag = Sk - Sq;
+    const int q0 = qb * kQueryBlock, qw0 = q0 + 32 * w;
+    const int qi = qw0 + lq;
+
+    const __amdgpu_buffer_rsrc_t rq = rsrc((const char*)p.q + (int64_t)bh * Sq * D * 2, (uint64_t)Sq * D * 2);
+    const __amdgpu_buffer_rsrc_t rdo = rsrc((const char*)p.dout + (int64_t)bh * Sq * D * 2, (uint64_t)Sq * D * 2);
+    const __amdgpu_buffer_rsrc_t rk = rsrc((const char*)p.k + (int64_t)bh * Sk * D * 2, (uint64_t)Sk * D * 2);
+    const __amdgpu_buffer_rsrc_t rv = rsrc((const char*)p.v + (int64_t)bh * Sk * D * 2, (uint64_t)Sk * D * 2);
+    const __amdgpu_buffer_rsrc_t rl = rsrc(p.lse + (int64_t)bh * Sq, (uint64_t)Sq * 4);
+    const __amdgpu_buffer_rsrc_t rdv = rsrc(p.dvec + (int64_t)bh * Sq, (uint64_t)Sq * 4);
+
+    // Q and dO of this wave's 32 queries as B operands (query = column lq).
+    i32x4 qf[DC], df[DC];
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+        qf[c] = __builtin_amdgcn_raw_buffer_load_b128(rq, (qi * D + 16 * c + 8 * g) * 2, 0, 0);
+        df[c] = __builtin_amdgcn_raw_buffer_load_b128(rdo, (qi * D + 16 * c + 8 * g) * 2, 0, 0);
+    }
+    const float lse2 = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, qi * 4, 0, 0)) * LOG2E;
+    const float dvl = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdv, qi * 4, 0, 0));
+
+    int nkt = (Sk + KT - 1) / KT;
+    if (CAUSAL) nkt = min(nkt, max(0, (min(Sq, q0 + kQueryBlock) + diag + KT - 1) / KT));
+
+    i32x4 sk[CPT], sv[CPT];
+    auto fetch = [&](int t) {
+        const int k0 = t * KT;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int ci = tid + 256 * i, r = ci / (D / 8), ch = ci % (D / 8);
+            sk[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((k0 + r) * D + 8 * ch) * 2, 0, 0);
+            sv[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((k0 + r) * D + 8 * ch) * 2, 0, 0);
+        }
+    };
+    auto commit = [&](int buf) {
+        lds_t* tk = sm + buf * 2 * TILE;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int ci = tid + 256 * i, r = ci / (D / 8), ch = ci % (D / 8);
+            *(__attribute__((address_space(3))) i32x4*)(tk + toff<D>(r, ch)) = sk[i];
+            *(__attribute__((address_space(3))) i32x4*)(tk + TILE + toff<D>(r, ch)) = sv[i];
+        }
+    };
+
+    const TrLane tl = tr_lane(lane);
+    const float c2 = p.scale_log2e;
+    f32x16 dqa[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) dqa[b] = zero16();
+
+    if (nkt > 0) {
+        fetch(0);
+        commit(0);
+    }
+    __syncthreads();
+
+    for (int t = 0; t < nkt; ++t) {
+        const int buf = t & 1;
+        if (t + 1 < nkt) fetch(t + 1);
+        const lds_t* tk = sm + buf * 2 * TILE;
+        const lds_t* tv = tk + TILE;
+        const int kt0 = t * KT;
+
+        // S^T = K Q^T and dP^T = V dO^T: 64 keys (rows) x this wave's 32 queries
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            s[rb] = zero16();
+            dp[rb] = zero16();
+        }
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                s[rb] = mma<DT>(row_frag<D>(tk, 32 * rb + lq, 2 * c + g), qf[c], s[rb]);
+                dp[rb] = mma<DT>(row_frag<D>(tv, 32 * rb + lq, 2 * c + g), df[c], dp[rb]);
+            }
+        }
+
+        const bool need_mask = (kt0 + KT > Sk) || (qw0 + 32 > Sq) || (CAUSAL && kt0 + KT - 1 > qw0 + diag);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float pv = __builtin_amdgcn_exp2f(s[rb][r] * c2 - lse2);
+                if (need_mask) {
+                    const int kj = kt0 + 32 * rb + 8 * (r >> 2) + 4 * g + (r & 3);
+                    const bool vis = qi < Sq && kj < Sk && (!CAUSAL || kj <= qi + diag);
+                    pv = vis ? pv : 0.0f;
+                }
+                dp[rb][r] = pv * (dp[rb][r] - dvl);
+            }
+        }
+
+        // dQ^T += K^T dS^T  (rows: head dimension, columns: queries)
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const i32x4 da = acc_frag<DT>(dp[st >> 1], st & 1);
+#pragma unroll
+            for (int b = 0; b < DB; ++b) dqa[b] = mma<DT>(tr_frag<D>(tk, st, b, tl), da, dqa[b]);
+        }
+
+        if (t + 1 < nkt) commit(buf ^ 1);
+        __syncthreads();
+    }
+
+    const __amdgpu_buffer_rsrc_t wq = rsrc((char*)p.dq + (int64_t)bh * Sq * D * 2, (uint64_t)Sq * D * 2);
+    const float sc = p.scale;
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            i32x2 v2;
+            v2[0] = pack2<DT>(dqa[b][4 * a] * sc, dqa[b][4 * a + 1] * sc);
+            v2[1] = pack2<DT>(dqa[b][4 * a + 2] * sc, dqa[b][4 * a + 3] * sc);
+            __builtin_amdgcn_raw_buffer_store_b64(v2, wq, (uint32_t)((qi * D + 32 * b + 8 * a + 4 * g) * 2), 0, 0);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+template <int D, int DT, bool CAUSAL>
+static hipError_t run(const BwdParams& p, int deterministic, hipStream_t st) {
+    const int64_t rows = (int64_t)p.BH * p.Sq;
+    constexpr int RPB = 256 / (D / 8);
+    if (rows > 0)
+        hipLaunchKernelGGL((bwd_pre<D, DT>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st, p);
+    if (p.Sk > 0) {
+        const dim3 grid((unsigned)(p.BH * p.nkb));
+        if (deterministic)
+            hipLaunchKernelGGL((bwd_dkdv<D, DT, CAUSAL, false>), grid, dim3(256), 0, st, p);
+        else
+            hipLaunchKernelGGL((bwd_dkdv<D, DT, CAUSAL, true>), grid, dim3(256), 0, st, p);
+    }
+    if (rows > 0) {
+        if (deterministic) {
+            hipLaunchKernelGGL((bwd_dq<D, DT, CAUSAL>), dim3((unsigned)(p.BH * p.nqb)), dim3(256), 0, st, p);
+        } else {
+            const int64_t n8 = rows * D / 8;
+            hipLaunchKernelGGL((bwd_dq_convert<DT>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, p, n8);
+        }
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdParams& p, int D, int dtype, int causal, int deterministic,
+                      hipStream_t stream) {
+    if (D == 64) {
+        if (dtype == 0) return causal ? run<64, 0, true>(p, deterministic, stream) : run<64, 0, false>(p, deterministic, stream);
+        return causal ? run<64, 1, true>(p, deterministic, stream) : run<64, 1, false>(p, deterministic, stream);
+    }
+    if (dtype == 0) return causal ? run<128, 0, true>(p, deterministic, stream) : run<128, 0, false>(p, deterministic, stream);
+    return causal ? run<128, 1, true>(p, deterministic, stream) : run<128, 1, false>(p, deterministic, stream);
+}
+
+}  // namespace bwd
+}  // namespace fa
