@@ -18,9 +18,12 @@ Prints ONE JSON line:
   naive_unfused  the same attention computed the unfused way (scores and
              probabilities written to device memory, four kernels of this
              library), timed the same way, with the fused kernel's speedup.
+  backward   the gradients (fa_bwd) on the same inputs, atomic and
+             deterministic dq modes, in TFLOP/s at 2.5x the forward's flops.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--cpu-seconds T] [--no-cpu-baseline] [--no-naive]
+                       [--no-backward]
 """
 import argparse
 import hashlib
@@ -148,6 +151,55 @@ def naive_leg(w, steps, warmup):
                     "(Q K^T, row softmax, V transpose, P V)"}
 
 
+def backward_leg(w, steps, warmup):
+    """The backward (fa_bwd) on the same inputs, both dq modes, timed like the
+    forward.  Algorithmic flops: FlashAttention-2 convention, 2.5 x the
+    forward's (five S x S x D products), whatever a mode recomputes."""
+    import torch
+    import tiled_attention_15_amd as fa
+    from workloads import make_inputs
+
+    dev = torch.device("cuda:0")
+    q, k, v = workload_inputs(w)
+    g, _, _ = make_inputs(w.B, w.H, w.S, w.D, w.dtype, seed=w.seed + 1000)
+    qd, kd, vd, gd = q.to(dev), k.to(dev), v.to(dev), g.to(dev)
+    o, lse = fa.forward(qd, kd, vd, causal=w.causal, scale=w.scale)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    stream = torch.cuda.current_stream(dev)
+    code = fa.BF16 if w.dtype == "bf16" else fa.F16
+    flops = 2.5 * w.flops()
+    out = {"unit": "TFLOP/s", "flops_per_step": flops, "steps": steps}
+    for det in (False, True):
+        need = fa.fa_bwd_workspace_bytes(w.B, w.H, w.S, w.D, det)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+        def step():
+            st = fa.fa_bwd(qd, kd, vd, o, gd, lse, dq, dk, dv, w.B, w.H, w.S, w.S, w.D, w.scale,
+                           w.causal, code, det, ws, need, stream)
+            if st != 0:
+                raise fa.FaError(st, "fa_bwd")
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / steps
+        if not (torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()):
+            raise RuntimeError("non-finite gradient in the benchmark run")
+        tf = flops / (ms * 1e-3) / 1e12
+        out["deterministic" if det else "atomic"] = {
+            "ms_per_step": round(ms, 4), "value": round(tf, 3),
+            "frac_of_mfma_peak": round(tf / MFMA_PEAK_TFLOPS, 4), "workspace_bytes": int(need)}
+        del ws
+    return out
+
+
 def copy_leg(mib, steps, warmup):
     """A plain device copy of known size: its HBM byte counters per dispatch
     calibrate the counters read on the attention kernel."""
@@ -221,6 +273,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-naive", action="store_true",
                     help="skip the unfused comparison path")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward (gradient) timing")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of attention, time a plain device-to-device copy of this many "
                          "MiB (the reference kernel for scaling HBM byte counters)")
@@ -266,6 +320,8 @@ def main():
         if nv is not None:
             nv["fused_speedup"] = round(nv["ms_per_step"] / ms, 2)
         out["naive_unfused"] = nv
+    if not a.no_backward:
+        out["backward"] = backward_leg(w, max(2, min(20, a.steps // 10)), 2)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_leg(w, a.cpu_seconds)
     print(json.dumps(out), flush=True)
