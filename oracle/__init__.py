@@ -16,6 +16,9 @@ derivative of the same definition with the probability matrix materialised:
 dV = P^T dO, dS = P * (dO V^T - rowsum(P * dO V^T)), dQ = scale dS K,
 dK = scale dS^T Q.
 
+attention_fwd_ext adds an explicit boolean mask and keep-and-rescale
+dropout whose keep decisions come from Philox4x32-10 (philox4x32_10).
+
 Inputs are numpy uint16 arrays holding the 16-bit patterns of the input
 dtype, contiguous, shaped [B, H, S, D].
 """
@@ -72,6 +75,15 @@ def _bind(lib):
         ctypes.c_float, ctypes.c_int, ctypes.c_int, i64p, ctypes.c_int64, i64p, ctypes.c_int64,
         f64p, f64p, f64p, ctypes.c_int]
     lib.ora_attention_bwd_rows.restype = ctypes.c_int
+    u32p = ctypes.POINTER(ctypes.c_uint32)
+    lib.ora_philox4x32_10.argtypes = [u32p, u32p, u32p]
+    lib.ora_philox4x32_10.restype = None
+    lib.ora_dropout_threshold.argtypes = [ctypes.c_float]
+    lib.ora_dropout_threshold.restype = ctypes.c_int
+    lib.ora_attention_fwd_ext.argtypes = [u16p, u16p, u16p] + [ctypes.c_int] * 5 + [
+        ctypes.POINTER(ctypes.c_uint8), i64p, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint32,
+        ctypes.c_float, ctypes.c_int, ctypes.c_int, i64p, ctypes.c_int64, f64p, f64p, ctypes.c_int]
+    lib.ora_attention_fwd_ext.restype = ctypes.c_int
     return lib
 
 
@@ -190,6 +202,61 @@ def attention_bwd_rows(q, k, v, dout, qrows, krows, *, scale, causal, dtype, nth
     if rc != 0:
         raise RuntimeError("ora_attention_bwd_rows failed with code %d" % rc)
     return dq, dk, dv
+
+
+def philox4x32_10(counter, key, lib=None):
+    """One Philox4x32-10 block: four 32-bit counter words, two key words ->
+    four 32-bit outputs."""
+    lib = lib or load()
+    c = (ctypes.c_uint32 * 4)(*[int(x) & 0xffffffff for x in counter])
+    k = (ctypes.c_uint32 * 2)(*[int(x) & 0xffffffff for x in key])
+    out = (ctypes.c_uint32 * 4)()
+    lib.ora_philox4x32_10(c, k, out)
+    return [int(x) for x in out]
+
+
+def dropout_threshold(p, lib=None):
+    """t = round(p * 65536): a score is kept iff its 16-bit draw is >= t."""
+    return (lib or load()).ora_dropout_threshold(ctypes.c_float(p))
+
+
+def attention_fwd_ext(q, k, v, *, scale, causal, dtype, mask=None, mask_strides=None,
+                      dropout_p=0.0, seed=0, offset=0, rows=None, nthreads=0, lib=None):
+    """Forward with an explicit boolean mask (uint8, nonzero = keep, element
+    strides (batch, head, row) in mask_strides, columns contiguous) and
+    keep-and-rescale dropout.  rows: optional flat row ids.
+
+    Returns (o [B,H,Sq,D] or [n, D], lse [B,H,Sq] or [n]) float64."""
+    lib = lib or load()
+    q, qp = _u16(q)
+    k, kp = _u16(k)
+    v, vp = _u16(v)
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    mp, sp = None, None
+    if mask is not None:
+        mask = np.asarray(mask)
+        if mask.dtype != np.uint8:
+            raise TypeError("mask must be uint8")
+        mask_strides = np.ascontiguousarray(mask_strides, dtype=np.int64)
+        mp = mask.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+        sp = mask_strides.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        o = np.empty((rows.size, D), dtype=np.float64)
+        lse = np.empty(rows.size, dtype=np.float64)
+        rp, nr = rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), rows.size
+    else:
+        o = np.empty((B, H, Sq, D), dtype=np.float64)
+        lse = np.empty((B, H, Sq), dtype=np.float64)
+        rp, nr = None, 0
+    rc = lib.ora_attention_fwd_ext(qp, kp, vp, B, H, Sq, Sk, D, mp, sp, ctypes.c_float(dropout_p),
+                                   ctypes.c_uint64(seed), ctypes.c_uint32(offset),
+                                   ctypes.c_float(scale), int(bool(causal)), _DTYPES[dtype], rp, nr,
+                                   _f64p(o), _f64p(lse), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("ora_attention_fwd_ext failed with code %d" % rc)
+    return o, lse
 
 
 def max_threads(lib=None):

@@ -482,3 +482,148 @@ int ora_attention_bwd_rows(const uint16_t* q, const uint16_t* k, const uint16_t*
     free(Kd); free(Vd); free(Qb); free(Gb); free(Pb); free(Sb); free(acc);
     return 0;
 }
+
+/*
+ * Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and
+ * Shaw, "Parallel random numbers: as easy as 1, 2, 3" (SC 2011): ten rounds
+ * of two 32x32->64-bit multiplications (multipliers 0xD2511F53 and
+ * 0xCD9E8D57) whose high halves are XOR-ed with the other counter words and
+ * the key, and a Weyl bump of the key (0x9E3779B9, 0xBB67AE85) between
+ * rounds.  Written from that definition; pinned against its published
+ * known-answer vectors.
+ */
+void ora_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4]) {
+    uint32_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+    uint32_t k0 = key_in[0], k1 = key_in[1];
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n1 = (uint32_t)p1;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        const uint32_t n3 = (uint32_t)p0;
+        c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/*
+ * Dropout threshold: keep probability 1 - t/65536 with t = round(p * 65536)
+ * (ties to even, p < 1), so that the keep decision is an integer comparison.
+ */
+int ora_dropout_threshold(float p) {
+    if (!(p >= 0.0f) || !(p < 1.0f)) return -1;
+    const long t = lrintf(p * 65536.0f);
+    return t > 65535 ? -1 : (int)t;
+}
+
+/* Keep decision of score (bh, i, j): the 16-bit value of key j among the
+ * eight that one Philox4x32-10 call gives for counter (j/8, i, bh, offset)
+ * under key (seed low word, seed high word): word (j%8)/2, low half for even
+ * j, high half for odd j; kept iff that value >= t. */
+static int keep_element(uint64_t seed, uint32_t offset, int64_t bh, int64_t i, int64_t j, int t) {
+    const uint32_t ctr[4] = {(uint32_t)(j >> 3), (uint32_t)i, (uint32_t)bh, offset};
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t out[4];
+    ora_philox4x32_10(ctr, key, out);
+    const uint32_t r16 = (out[(j & 7) >> 1] >> (16 * (j & 1))) & 0xffffu;
+    return (int)r16 >= t;
+}
+
+/*
+ * The forward with an explicit boolean mask and dropout
+ * ("FlashAttention-2 on Ascend NPU" (2048ai.net), section 3.4, fused mask
+ * and dropout, and section 6.3):
+ *   visible(i,j) = causal rule and mask[b,h,i,j] != 0 (nonzero = keep, as the
+ *                  page's kernel treats a true entry);
+ *   P_ij         = softmax over the visible keys, lse_i as in the forward;
+ *   O_i          = sum_j P_ij * keep_ij / (1 - t/65536) * v_j,
+ * i.e. standard keep-and-rescale dropout applied to the probabilities (the
+ * page's listing writes -inf into the scores instead, which renormalises and
+ * is not dropout; that reading is not followed).  The lse is that of the
+ * undropped softmax.  mask: uint8 with element strides (batch, head, row) in
+ * mstride, columns contiguous; NULL = no mask.  dropout_p = 0 keeps all.
+ */
+static void row_attention_ext(const double* qrow, const double* K, const double* V, int64_t bh,
+                              int64_t i, int64_t Sq, int64_t Sk, int D, double scale, int causal,
+                              const uint8_t* mrow, int t, uint64_t seed, uint32_t offset,
+                              double* srow, double* orow, double* lse_out) {
+    for (int64_t j = 0; j < Sk; ++j) {
+        const int vis = visible(i, j, Sq, Sk, causal) && (!mrow || mrow[j] != 0);
+        if (!vis) { srow[j] = -INFINITY; continue; }
+        double acc = 0.0;
+        for (int d = 0; d < D; ++d) acc += qrow[d] * K[j * D + d];
+        srow[j] = scale * acc;
+    }
+    double m = -INFINITY;
+    for (int64_t j = 0; j < Sk; ++j) if (srow[j] > m) m = srow[j];
+    for (int d = 0; d < D; ++d) orow[d] = 0.0;
+    if (m == -INFINITY) { *lse_out = -INFINITY; return; }
+    double l = 0.0;
+    for (int64_t j = 0; j < Sk; ++j) {
+        const double e = exp(srow[j] - m);
+        srow[j] = e;
+        l += e;
+    }
+    const double keep_scale = 65536.0 / (65536.0 - (double)t);
+    for (int64_t j = 0; j < Sk; ++j) {
+        if (srow[j] == 0.0) continue;
+        if (t > 0 && !keep_element(seed, offset, bh, i, j, t)) continue;
+        const double w = srow[j] / l * keep_scale;
+        for (int d = 0; d < D; ++d) orow[d] += w * V[j * D + d];
+    }
+    *lse_out = m + log(l);
+}
+
+int ora_attention_fwd_ext(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int H,
+                          int Sq, int Sk, int D, const uint8_t* mask, const int64_t* mstride,
+                          float dropout_p, uint64_t seed, uint32_t offset, float scale, int causal,
+                          int dtype, const int64_t* rows, int64_t nrows, double* o, double* lse,
+                          int nthreads) {
+    if (!q || !k || !v || !o || !lse || B < 0 || H < 0 || Sq < 0 || Sk < 0 || D <= 0) return 1;
+    if (dtype != ORA_F16 && dtype != ORA_BF16) return 2;
+    if (mask && !mstride) return 1;
+    const int t = ora_dropout_threshold(dropout_p);
+    if (t < 0) return 5;
+    const int64_t total = (int64_t)B * H * Sq;
+    const int64_t n = rows ? nrows : total;
+    if (rows) for (int64_t r = 0; r < nrows; ++r) if (rows[r] < 0 || rows[r] >= total) return 4;
+    set_threads(nthreads);
+    const double sc = (double)scale;
+    const int64_t kh = (int64_t)Sk * D;
+    int err = 0;
+    #pragma omp parallel
+    {
+        double* Qr = (double*)malloc(sizeof(double) * (size_t)D);
+        double* Kd = (double*)malloc(sizeof(double) * (size_t)(kh > 0 ? kh : 1));
+        double* Vd = (double*)malloc(sizeof(double) * (size_t)(kh > 0 ? kh : 1));
+        double* Sr = (double*)malloc(sizeof(double) * (size_t)(Sk > 0 ? Sk : 1));
+        int64_t cur_bh = -1;
+        if (!Qr || !Kd || !Vd || !Sr) {
+            #pragma omp atomic write
+            err = 3;
+        } else {
+            #pragma omp for schedule(dynamic, 4)
+            for (int64_t r = 0; r < n; ++r) {
+                const int64_t row = rows ? rows[r] : r;
+                const int64_t bh = row / Sq, i = row % Sq;
+                if (bh != cur_bh) {
+                    ora_decode(k + bh * kh, Kd, kh, dtype);
+                    ora_decode(v + bh * kh, Vd, kh, dtype);
+                    cur_bh = bh;
+                }
+                ora_decode(q + row * D, Qr, D, dtype);
+                const uint8_t* mrow = NULL;
+                if (mask) {
+                    const int64_t b = bh / H, h = bh % H;
+                    mrow = mask + b * mstride[0] + h * mstride[1] + i * mstride[2];
+                }
+                row_attention_ext(Qr, Kd, Vd, bh, i, Sq, Sk, D, sc, causal, mrow, t, seed, offset,
+                                  Sr, o + r * D, lse + r);
+            }
+        }
+        free(Qr); free(Kd); free(Vd); free(Sr);
+    }
+    return err;
+}

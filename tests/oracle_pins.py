@@ -22,10 +22,19 @@ torch's fp64 scaled_dot_product_attention, by central differences of the
 invariants (the key-shift symmetry gives sum_j dK_j = 0; rows of P sum to
 one give sum_j dV_j = sum_i dO_i; the scores' bilinearity gives
 sum_i q_i.dQ_i = sum_j k_j.dK_j).
+
+The forward with an explicit mask and dropout is pinned by Philox4x32-10's
+published known-answer vectors, by torch's fp64 scaled_dot_product_attention
+with the same boolean mask, by the identity-V case (O = P) against a second
+Philox written from its definition in this file, by the kept fraction, and
+by reducing to the plain forward (no mask, p = 0; all-true mask; triangular
+mask = causal flag) bit for bit.
 """
 from decimal import Decimal, getcontext
 from fractions import Fraction
+import json
 import math
+import os
 
 import numpy as np
 import torch
@@ -416,8 +425,174 @@ def pin_bwd_rows_match_full(lib):
         assert np.max(np.abs(c - dv.reshape(-1, 32)[kr])) <= 1e-13 * scl, dtype
 
 
+# --- explicit mask and dropout -------------------------------------------------
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def pin_philox_kat(lib):
+    """Philox4x32-10 against the known-answer vectors published with it."""
+    kat = json.load(open(os.path.join(GOLDEN, "philox4x32_10_kat.json")))
+    for vec in kat["vectors"]:
+        ctr = [int(x, 16) for x in vec["counter"]]
+        key = [int(x, 16) for x in vec["key"]]
+        want = [int(x, 16) for x in vec["out"]]
+        assert oracle.philox4x32_10(ctr, key, lib=lib) == want, vec
+
+
+def pin_dropout_threshold(lib):
+    for p in (0.0, 0.1, 0.25, 0.5, 1.0 / 3.0, 0.9999):
+        want = int(np.rint(np.float32(p) * np.float32(65536.0)))
+        assert oracle.dropout_threshold(p, lib=lib) == want, p
+    for p in (1.0, 1.5, -0.1, float("nan"), 0.99999999):
+        assert oracle.dropout_threshold(p, lib=lib) == -1, p
+
+
+def _philox_py(ctr, key):
+    """Philox4x32-10 written again from its definition (Salmon et al. 2011),
+    for the keep pattern check."""
+    c0, c1, c2, c3 = ctr
+    k0, k1 = key
+    for r in range(10):
+        if r:
+            k0, k1 = (k0 + 0x9E3779B9) & 0xFFFFFFFF, (k1 + 0xBB67AE85) & 0xFFFFFFFF
+        p0, p1 = 0xD2511F53 * c0, 0xCD9E8D57 * c2
+        c0, c1, c2, c3 = ((p1 >> 32) ^ c1 ^ k0) & 0xFFFFFFFF, p1 & 0xFFFFFFFF, \
+            ((p0 >> 32) ^ c3 ^ k1) & 0xFFFFFFFF, p0 & 0xFFFFFFFF
+    return c0, c1, c2, c3
+
+
+def keep_pattern(Sq, Sk, bh, seed, offset, t):
+    """keep[i, j] for one head: the 16-bit draw for key j is half j%2 of word
+    (j%8)/2 of Philox4x32-10 at counter (j/8, i, bh, offset), key (seed low,
+    seed high)."""
+    keep = np.zeros((Sq, Sk), dtype=bool)
+    for i in range(Sq):
+        for jb in range((Sk + 7) // 8):
+            out = _philox_py((jb, i, bh, offset), (seed & 0xFFFFFFFF, seed >> 32))
+            for j in range(8 * jb, min(Sk, 8 * jb + 8)):
+                r16 = (out[(j & 7) >> 1] >> (16 * (j & 1))) & 0xFFFF
+                keep[i, j] = r16 >= t
+    return keep
+
+
+def _ext(lib, q, k, v, scale, causal, dtype, **kw):
+    return oracle.attention_fwd_ext(bits(q), bits(k), bits(v), scale=scale, causal=causal,
+                                    dtype=dtype, lib=lib, **kw)
+
+
+def pin_ext_plain_equals_forward(lib):
+    """No mask and p = 0 is the forward itself, bit for bit; an all-true mask
+    too; a bottom-right lower-triangular mask is the causal flag."""
+    for dtype, (Sq, Sk) in (("f16", (40, 40)), ("bf16", (23, 57)), ("f16", (57, 23))):
+        q, k, v = make_inputs(2, 2, max(Sq, Sk), 16, dtype, seed=80 + Sq, Sk=Sk)
+        q = q[:, :, :Sq].contiguous()
+        scale = softmax_scale(16)
+        for causal in (False, True):
+            o, lse = _run(lib, q, k, v, scale, causal, dtype)
+            oe, le = _ext(lib, q, k, v, scale, causal, dtype)
+            assert np.array_equal(o, oe) and np.array_equal(lse, le), (dtype, Sq, Sk, causal)
+            ones = np.ones((Sq, Sk), np.uint8)
+            om, lm = _ext(lib, q, k, v, scale, causal, dtype, mask=ones, mask_strides=(0, 0, Sk))
+            assert np.array_equal(o, om) and np.array_equal(lse, lm)
+        tri = np.array([[1 if j <= i + (Sk - Sq) else 0 for j in range(Sk)] for i in range(Sq)], np.uint8)
+        oc, lc = _run(lib, q, k, v, scale, True, dtype)
+        ot, lt = _ext(lib, q, k, v, scale, False, dtype, mask=tri, mask_strides=(0, 0, Sk))
+        assert np.array_equal(oc, ot) and np.array_equal(lc, lt), (dtype, Sq, Sk)
+
+
+def pin_ext_mask_sdpa(lib):
+    """A random per-(batch, head) mask against torch's fp64 scaled dot-product
+    attention with that boolean mask (True = attend); rows the mask hides
+    completely give O = 0, lse = -inf."""
+    B, H, Sq, Sk, D = 2, 3, 37, 45, 16
+    q, k, v = make_inputs(B, H, max(Sq, Sk), D, "bf16", seed=90, Sk=Sk)
+    q = q[:, :, :Sq].contiguous()
+    rng = np.random.default_rng(91)
+    m = (rng.random((B, H, Sq, Sk)) < 0.6).astype(np.uint8)
+    m[0, 1, 5, :] = 0
+    m[1, 2, 0, :] = 0
+    scale = softmax_scale(D)
+    for causal in (False, True):
+        o, lse = _ext(lib, q, k, v, scale, causal, "bf16", mask=m,
+                      mask_strides=(H * Sq * Sk, Sq * Sk, Sk))
+        allow = torch.from_numpy(m.astype(bool))
+        if causal:
+            i = torch.arange(Sq)[:, None]
+            j = torch.arange(Sk)[None, :]
+            allow = allow & (j <= i + (Sk - Sq))
+        seen = allow.any(-1).numpy()
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(_f64(q)), torch.from_numpy(_f64(k)), torch.from_numpy(_f64(v)),
+            attn_mask=allow, scale=scale).numpy()
+        assert np.max(np.abs(o[seen] - ref[seen])) <= 1e-12, causal
+        assert np.all(o[~seen] == 0.0) and np.all(np.isneginf(lse[~seen])), causal
+        # a padded mask row (row stride > Sk) reads the same entries
+        wide = np.zeros((B, H, Sq, Sk + 19), np.uint8)
+        wide[..., :Sk] = m
+        ow, lw = _ext(lib, q, k, v, scale, causal, "bf16", mask=wide,
+                      mask_strides=(H * Sq * (Sk + 19), Sq * (Sk + 19), Sk + 19))
+        assert np.array_equal(o, ow) and np.array_equal(lse, lw)
+
+
+def pin_ext_dropout_pattern(lib):
+    """With V = the identity (Sk = D), O_i is the probability row P_i itself;
+    dropout must give P_ij * keep_ij * 65536 / (65536 - t) with keep from
+    Philox4x32-10 at the documented counter, and lse unchanged."""
+    Sq, Sk = 20, 32
+    q, k, _ = make_inputs(1, 2, Sk, Sk, "f16", seed=95, Sk=Sk)
+    q = q[:, :, :Sq].contiguous()
+    v = torch.eye(Sk, dtype=torch.float16).expand(1, 2, Sk, Sk).contiguous()
+    scale = softmax_scale(Sk)
+    # a threshold equal to one draw: that score is kept (the comparison is >=)
+    first = _philox_py((0, 0, 0, 11), (17, 0))[0] & 0xFFFF
+    assert first > 0
+    cases = ((0.25, 0x1234_5678_9ABC_DEF0, 7, False), (0.5, 3, 0, True), (first / 65536.0, 17, 11, False))
+    for p, seed, offset, causal in cases:
+        t = oracle.dropout_threshold(p, lib=lib)
+        o0, l0 = _ext(lib, q, k, v, scale, causal, "f16")
+        od, ld = _ext(lib, q, k, v, scale, causal, "f16", dropout_p=p, seed=seed, offset=offset)
+        assert np.array_equal(l0, ld)
+        for h in range(2):
+            keep = keep_pattern(Sq, Sk, h, seed, offset, t)
+            want = o0[0, h] * keep * (65536.0 / (65536.0 - t))
+            assert np.max(np.abs(od[0, h] - want)) <= 1e-15, (p, h)
+
+
+def pin_ext_dropout_rate(lib):
+    """Over 64k scores the kept fraction is 1 - t/65536 within 5 sigma, and
+    another offset gives another pattern."""
+    S = 256
+    q, k, _ = make_inputs(1, 1, S, S, "f16", seed=96)
+    q = torch.zeros_like(q)                      # P = 1/S everywhere
+    v = torch.eye(S, dtype=torch.float16)[None, None].contiguous()
+    t = oracle.dropout_threshold(0.1, lib=lib)
+    o1, _ = _ext(lib, q, k, v, 1.0, False, "f16", dropout_p=0.1, seed=42, offset=0)
+    o2, _ = _ext(lib, q, k, v, 1.0, False, "f16", dropout_p=0.1, seed=42, offset=1)
+    kept = o1 != 0
+    pk = 1 - t / 65536.0
+    sigma = math.sqrt(pk * (1 - pk) / kept.size)
+    assert abs(kept.mean() - pk) <= 5 * sigma, kept.mean()
+    assert np.allclose(o1[kept], 1.0 / S * 65536.0 / (65536.0 - t), rtol=1e-15, atol=0)
+    assert (kept != (o2 != 0)).mean() > 0.1
+
+
+def pin_ext_rows_match_full(lib):
+    B, H, Sq, Sk, D = 2, 2, 50, 70, 32
+    q, k, v = make_inputs(B, H, Sk, D, "bf16", seed=97, Sk=Sk)
+    q = q[:, :, :Sq].contiguous()
+    m = (np.random.default_rng(98).random((Sq, Sk)) < 0.8).astype(np.uint8)
+    kw = dict(mask=m, mask_strides=(0, 0, Sk), dropout_p=0.2, seed=5, offset=9)
+    o, lse = _ext(lib, q, k, v, softmax_scale(D), True, "bf16", **kw)
+    rows = np.array([0, 3, Sq - 1, Sq, 2 * Sq + 7, B * H * Sq - 1], np.int64)
+    ro, rl = _ext(lib, q, k, v, softmax_scale(D), True, "bf16", rows=rows, **kw)
+    assert np.array_equal(ro, o.reshape(-1, D)[rows]) and np.array_equal(rl, lse.reshape(-1)[rows])
+
+
 ALL_PINS = [pin_decode_f16, pin_decode_bf16, pin_q_zero, pin_causal_row0, pin_convexity,
             pin_bruteforce_decimal, pin_sdpa_fp64, pin_chunk_merge, pin_invariances,
             pin_rows_match_full, pin_unequal_causal_suffix, pin_bwd_autograd,
             pin_bwd_finite_difference, pin_bwd_closed_forms, pin_bwd_invariants,
-            pin_bwd_rows_match_full]
+            pin_bwd_rows_match_full, pin_philox_kat, pin_dropout_threshold,
+            pin_ext_plain_equals_forward, pin_ext_mask_sdpa, pin_ext_dropout_pattern,
+            pin_ext_dropout_rate, pin_ext_rows_match_full]

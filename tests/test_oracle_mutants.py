@@ -26,7 +26,10 @@ MUTATIONS = [
     ("wrong_key_row", "const double* kr = K + j * D;", "const double* kr = K + ((j + 1) % Sk) * D;"),
     ("transposed_scores", "row_attention(Qd + i * D, Kd, Vd,",
      "row_attention(Sq == Sk ? Kd + i * D : Qd + i * D, Sq == Sk ? Qd : Kd, Vd,"),
-    ("scale_missing", "srow[j] = scale * acc;", "srow[j] = acc;"),
+    ("scale_missing", "        srow[j] = scale * acc;\n    }\n    /* pass 1: row maximum */",
+     "        srow[j] = acc;\n    }\n    /* pass 1: row maximum */"),
+    ("ext_scale_missing", "        srow[j] = scale * acc;\n    }\n    double m = -INFINITY;",
+     "        srow[j] = acc;\n    }\n    double m = -INFINITY;"),
     ("exp_sign", "double p = exp(srow[j] - m);", "double p = exp(m - srow[j]);"),
     ("exp_without_max", "double p = exp(srow[j] - m);", "double p = exp(srow[j]);"),
     ("not_normalised", "for (int64_t j = 0; j < Sk; ++j) srow[j] = srow[j] / l;", ""),
@@ -63,6 +66,33 @@ MUTATIONS = [
     ("bwd_rows_dk_scale_missing", "for (int d = 0; d < D; ++d) dk[r * D + d] *= sc;",
      "for (int d = 0; d < D; ++d) dk[r * D + d] *= 1.0;"),
     ("bwd_rows_wrong_key", "const int64_t j = krows[r] % Sk;", "const int64_t j = (krows[r] + 1) % Sk;"),
+    # explicit mask and dropout
+    ("philox_nine_rounds", "for (int r = 0; r < 10; ++r) {\n        if (r > 0) { k0 += 0x9E3779B9u;",
+     "for (int r = 0; r < 9; ++r) {\n        if (r > 0) { k0 += 0x9E3779B9u;"),
+    ("philox_multiplier", "(uint64_t)0xD2511F53u * c0", "(uint64_t)0xD2511F57u * c0"),
+    ("philox_key_bump", "k1 += 0xBB67AE85u;", "k1 += 0x9E3779B9u;"),
+    ("philox_output_order", "out[0] = c0; out[1] = c1;", "out[0] = c1; out[1] = c0;"),
+    ("threshold_truncated", "const long t = lrintf(p * 65536.0f);", "const long t = (long)(p * 65536.0f);"),
+    ("keep_compare", "return (int)r16 >= t;", "return (int)r16 > t;"),
+    ("keep_word", "out[(j & 7) >> 1]", "out[j & 3]"),
+    ("keep_half", ">> (16 * (j & 1))) & 0xffffu", ">> (16 * ((j >> 1) & 1))) & 0xffffu"),
+    ("keep_counter_swapped", "{(uint32_t)(j >> 3), (uint32_t)i, (uint32_t)bh, offset}",
+     "{(uint32_t)i, (uint32_t)(j >> 3), (uint32_t)bh, offset}"),
+    ("keep_offset_ignored", "(uint32_t)bh, offset};", "(uint32_t)bh, 0u};"),
+    ("keep_head_ignored", "(uint32_t)i, (uint32_t)bh, offset}", "(uint32_t)i, 0u, offset}"),
+    ("keep_seed_words_swapped", "{(uint32_t)seed, (uint32_t)(seed >> 32)}",
+     "{(uint32_t)(seed >> 32), (uint32_t)seed}"),
+    ("ext_mask_polarity", "(!mrow || mrow[j] != 0)", "(!mrow || mrow[j] == 0)"),
+    ("ext_mask_head_stride", "mrow = mask + b * mstride[0] + h * mstride[1] + i * mstride[2];",
+     "mrow = mask + b * mstride[0] + i * mstride[2];"),
+    ("ext_mask_row_stride", "mrow = mask + b * mstride[0] + h * mstride[1] + i * mstride[2];",
+     "mrow = mask + b * mstride[0] + h * mstride[1] + i * Sk;"),
+    ("dropout_scale_missing", "const double keep_scale = 65536.0 / (65536.0 - (double)t);",
+     "const double keep_scale = 1.0;"),
+    ("dropout_renormalised", "        srow[j] = e;\n        l += e;",
+     "        srow[j] = e;\n        l += (t > 0 && !keep_element(seed, offset, bh, i, j, t)) ? 0.0 : e;"),
+    ("ext_causal_ignored", "const int vis = visible(i, j, Sq, Sk, causal) && (!mrow || mrow[j] != 0);",
+     "const int vis = (!mrow || mrow[j] != 0);"),
 ]
 
 
