@@ -60,8 +60,10 @@ typedef enum {
     FA_ERR_SCALE = 5,        /* scale is not finite or not > 0 */
     FA_ERR_HIP = 6,          /* the HIP runtime reported an error at launch */
     FA_ERR_ALIAS = 7,        /* o or lse overlaps q, k or v, or o overlaps lse */
-    FA_ERR_STRIDE = 8        /* a stride is negative, not a multiple of 8
+    FA_ERR_STRIDE = 8,       /* a stride is negative, not a multiple of 8
                                 elements, or makes o overlap itself */
+    FA_ERR_MASK_DROPOUT = 9  /* fa_fwd_ext: bad mask layout or dropout
+                                probability outside [0, 1) */
 } fa_status;
 
 /*
@@ -194,6 +196,44 @@ int fa_naive_fwd(const void* q, const void* k, const void* v, void* o, float* ls
  * shape): per (batch, head), S x Sp fp32 scores, S x Sp probabilities and
  * D x Sp transposed values (16-bit), Sp = S rounded up to a multiple of 64. */
 int64_t fa_naive_workspace_bytes(int B, int H, int S, int D);
+
+/*
+ * fa_fwd_ext -- the forward with an explicit boolean mask and/or dropout,
+ * fused into one kernel ("FlashAttention-2 on Ascend NPU: how
+ * ops-transformer reaches 3x" (2048ai.net), section 3.4 and section 6.3):
+ * the mask and the dropout act on the score tile on chip, so no S x S
+ * pass touches device memory.
+ *
+ *   q, o        device, contiguous [B,H,Sq,D] of `dtype`; k, v [B,H,Sk,D]
+ *   lse         device [B,H,Sq] fp32 or NULL: log-sum-exp of the masked,
+ *               undropped scores (-inf for a row with no visible key)
+ *   mask        device uint8 or NULL; element (b,h,i,j) at
+ *               mask[b*mask_strides[0] + h*mask_strides[1] + i*mask_strides[2] + j];
+ *               nonzero keeps score (i, j), zero hides it (on top of the
+ *               causal rule).  Strides in bytes, >= 0 (0 broadcasts over
+ *               batch or heads), multiples of 4, row stride >= Sk; the
+ *               pointer 4-byte aligned; one head's rows must span less than
+ *               2^31 bytes.  A row with no visible key gives O = 0.
+ *   dropout_p   in [0, 1): each probability is kept with probability
+ *               1 - t/65536, t = round(dropout_p * 65536) (ties to even),
+ *               and the kept ones are scaled by 65536/(65536 - t).  The keep
+ *               decision of score (b*H+h, i, j) compares with t the 16-bit
+ *               half j%2 (low half for even j) of word (j%8)/2 of
+ *               Philox4x32-10 (Salmon et al., SC 2011) at counter
+ *               (j/8, i, b*H+h, offset) and key (seed & 0xffffffff, seed >> 32).
+ *               dropout_p = 0 keeps everything.
+ *   causal, scale, dtype, stream  as for fa_fwd (bottom-right causal rule
+ *               when Sq != Sk).
+ * The same result as fa_fwd when mask is NULL and dropout_p is 0 (computed
+ * by a different kernel, so equal within rounding, not bit for bit).
+ * Returns FA_OK or an fa_status; FA_ERR_MASK_DROPOUT for a bad mask layout
+ * or dropout probability.
+ */
+int fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int Sq, int Sk, int D,
+               const uint8_t* mask, const int64_t* mask_strides,
+               float dropout_p, uint64_t seed, uint32_t offset,
+               float scale, int causal, int dtype, void* stream);
 
 /*
  * fa_bwd -- gradients of the attention forward above: given dout = dL/dO,

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert fa.fa_version() >= 10000
-    for code in range(9):
+    for code in range(10):
         s = fa.fa_status_string(code)
         assert s and s != "unknown status", code
     assert fa.fa_status_string(99) == "unknown status"
@@ -237,3 +237,34 @@ def test_bwd_rejects_bad_arguments(lib):
     assert bcall(dv=DK + 64) == 7            # two outputs overlap
     assert bcall(ws=DO) == 7                 # workspace over an input
     assert bcall(dk=W + 256) == 7            # output inside the workspace
+
+
+@fake_addresses
+def test_ext_rejects_bad_arguments(lib):
+    B, H, Sq, Sk, D = 2, 2, 100, 120, 64
+    M = 0x20000000
+
+    def ecall(**kw):
+        a = dict(q=Q, k=K, v=V, o=O, lse=L, B=B, H=H, Sq=Sq, Sk=Sk, D=D, mask=M,
+                 ms=(H * Sq * 128, Sq * 128, 128), p=0.1, seed=1, off=0, scale=0.125, causal=1,
+                 dtype=0)
+        a.update(kw)
+        return fa.fa_fwd_ext(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Sq"],
+                             a["Sk"], a["D"], a["mask"], a["ms"], a["p"], a["seed"], a["off"],
+                             a["scale"], a["causal"], a["dtype"], None)
+
+    assert ecall(q=0) == 1 and ecall(o=0) == 1
+    assert ecall(Sq=0) == 2 and ecall(D=80) == 3 and ecall(dtype=3) == 3
+    assert ecall(o=O + 8) == 4 and ecall(lse=L + 4) == 4
+    assert ecall(scale=0.0) == 5
+    for bad in (1.0, -0.01, float("nan"), 0.9999999):
+        assert ecall(p=bad) == 9, bad
+    assert ecall(mask=M + 2) == 9                       # mask not 4-byte aligned
+    assert ecall(ms=None) == 9                          # strides missing
+    assert ecall(ms=(0, 0, 118)) == 9                   # row stride < Sk
+    assert ecall(ms=(0, 0, 130)) == 9                   # row stride not a multiple of 4
+    assert ecall(ms=(-128, 0, 128)) == 9                # negative stride
+    assert ecall(ms=(0, 0, 1 << 26)) == 9               # one head's rows beyond 2^31 bytes
+    assert ecall(o=M + 64) == 7                         # output over the mask
+    assert ecall(lse=K) == 7
+    assert ecall(Sq=1 << 24, Sk=1 << 24, ms=(0, 0, 1 << 24)) == 2    # head span beyond 32-bit offsets

@@ -1,0 +1,145 @@
+"""GPU parity of the forward with an explicit boolean mask and dropout
+(fa_fwd_ext) against the fp64 oracle: full outputs on small and ragged
+shapes, the exact keep pattern of the dropout, and sampled rows at the long
+causal workload's size."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import parity
+import tiled_attention_15_amd as fa
+from workloads import WORKLOADS, bits, make_inputs, softmax_scale, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def to64(t):
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def inputs(B, H, Sq, Sk, D, dtype, seed, q_mult=1.0):
+    q, k, v = make_inputs(B, H, max(Sq, Sk), D, dtype, seed=seed, q_mult=q_mult, Sk=Sk)
+    return q[:, :, :Sq].contiguous(), k, v
+
+
+def make_mask(kind, B, H, Sq, Sk, seed):
+    """(mask uint8 numpy array laid out as stored, strides in bytes) or (None, None)."""
+    rng = np.random.default_rng(seed)
+    if kind is None:
+        return None, None
+    if kind == "per_head":                      # [B, H, Sq, Sk_pad], rows padded to a multiple of 4
+        ld = (Sk + 3) // 4 * 4
+        m = np.zeros((B, H, Sq, ld), np.uint8)
+        m[..., :Sk] = rng.random((B, H, Sq, Sk)) < 0.7
+        m[0, 0, min(3, Sq - 1), :] = 0           # one row with no visible key
+        return m, (H * Sq * ld, Sq * ld, ld)
+    if kind == "shared":                        # one [Sq, Sk_pad + 8] mask for every head
+        ld = (Sk + 3) // 4 * 4 + 8
+        m = np.zeros((Sq, ld), np.uint8)
+        m[:, :Sk] = rng.random((Sq, Sk)) < 0.85
+        return m, (0, 0, ld)
+    raise ValueError(kind)
+
+
+def run_ext(q, k, v, causal, dtype, mask, ms, p, seed, offset):
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    md = None if mask is None else torch.from_numpy(mask).to(DEV)
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=DEV)
+    st = fa.fa_fwd_ext(qd, kd, vd, o, lse, B, H, Sq, Sk, D, md, ms, p, seed, offset,
+                       softmax_scale(D), causal, fa.BF16 if dtype == "bf16" else fa.F16, None)
+    assert st == 0, fa.fa_status_string(st)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+CASES = [
+    # (B, H, Sq, Sk, D, causal, dtype, mask kind, dropout p)
+    (1, 2, 64, 64, 64, False, "f16", "per_head", 0.0),
+    (1, 2, 128, 128, 128, True, "bf16", None, 0.1),
+    (2, 1, 200, 200, 64, True, "f16", "shared", 0.25),
+    (1, 2, 257, 257, 128, True, "bf16", "per_head", 0.5),
+    (1, 1, 100, 300, 128, True, "f16", "shared", 0.0),
+    (1, 1, 300, 100, 64, True, "bf16", "per_head", 0.1),
+    (2, 2, 130, 67, 128, False, "f16", None, 0.3),
+    (1, 3, 1, 1, 64, False, "bf16", "per_head", 0.0),
+    (1, 2, 77, 45, 64, False, "f16", None, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=["%dx%dx%dx%dx%d%s%s_%s_p%g" % (c[0], c[1], c[2], c[3], c[4],
+                                                                          "c" if c[5] else "n", c[6], c[7], c[8])
+                                             for c in CASES])
+def test_ext_matches_oracle(case):
+    B, H, Sq, Sk, D, causal, dtype, kind, p = case
+    say("case ext", case)
+    q, k, v = inputs(B, H, Sq, Sk, D, dtype, seed=2000 + Sq + 3 * Sk + D)
+    mask, ms = make_mask(kind, B, H, Sq, Sk, seed=2100 + Sq)
+    seed, offset = 0xC0FFEE_0000_1234 + Sq, 5
+    o, lse = run_ext(q, k, v, causal, dtype, mask, ms, p, seed, offset)
+    o_ref, l_ref = oracle.attention_fwd_ext(bits(q), bits(k), bits(v), scale=softmax_scale(D),
+                                            causal=causal, dtype=dtype, mask=mask, mask_strides=ms,
+                                            dropout_p=p, seed=seed, offset=offset)
+    st = parity.assert_parity(to64(o), to64(lse), o_ref, l_ref, dtype, "ext %s" % (case,))
+    say("  ", st)
+
+
+@pytest.mark.parametrize("D,p,causal", [(64, 0.1, False), (128, 0.5, True), (64, 0.3, True)])
+def test_ext_keep_pattern_is_exact(D, p, causal):
+    """With V = the identity (Sk = D) the output row is the probability row
+    times keep/(1-p): the GPU's zero pattern must equal the oracle's, element
+    for element (the keep decisions are integer comparisons on both sides)."""
+    Sq, Sk = 96, D
+    q, k, _ = inputs(2, 2, Sq, Sk, D, "f16", seed=2200 + D, q_mult=0.25)
+    v = torch.eye(Sk, dtype=torch.float16).expand(2, 2, Sk, D).contiguous()
+    seed, offset = 123456789, 3
+    o, _ = run_ext(q, k, v, causal, "f16", None, None, p, seed, offset)
+    o_ref, _ = oracle.attention_fwd_ext(bits(q), bits(k), bits(v), scale=softmax_scale(D), causal=causal,
+                                        dtype="f16", dropout_p=p, seed=seed, offset=offset)
+    got = to64(o) != 0
+    want = o_ref != 0
+    assert np.array_equal(got, want), int((got != want).sum())
+    kept = want.sum() / max(1, (o_ref != 0).size)
+    say("   kept fraction", kept)
+
+
+def test_ext_plain_agrees_with_fused_forward():
+    """No mask and p = 0: the same attention as the tuned forward (both within
+    the oracle bound, so within twice of it of each other)."""
+    q, k, v = inputs(1, 4, 700, 700, 128, "bf16", seed=2300)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    for causal in (False, True):
+        o1, l1 = fa.forward_ext(qd, kd, vd, causal=causal)
+        o2, l2 = fa.forward(qd, kd, vd, causal=causal)
+        torch.cuda.synchronize()
+        assert (o1.float() - o2.float()).abs().max().item() <= 2 * parity.O_TOL["bf16"] + 2 ** -5
+        assert (l1 - l2).abs().max().item() <= 2e-4 * max(1.0, l2.abs().max().item())
+
+
+def test_ext_workload_sampled_rows():
+    """The long causal workload (1x32x8192x128 bf16, Q x4) with a shared random
+    mask (90% kept) and dropout 0.1: sampled rows against the oracle."""
+    w = WORKLOADS["long_causal_1x32x8192x128_bf16_q4"]
+    q, k, v = workload_inputs(w)
+    S = w.S
+    rng = np.random.default_rng(2400)
+    mask = (rng.random((S, S)) < 0.9).astype(np.uint8)
+    ms = (0, 0, S)
+    say("case ext workload", w.name)
+    o, lse = run_ext(q, k, v, w.causal, w.dtype, mask, ms, 0.1, 77, 0)
+    rows = np.sort(rng.choice(w.B * w.H * S, size=192, replace=False)).astype(np.int64)
+    o_ref, l_ref = oracle.attention_fwd_ext(bits(q), bits(k), bits(v), scale=w.scale, causal=w.causal,
+                                            dtype=w.dtype, mask=mask, mask_strides=ms, dropout_p=0.1,
+                                            seed=77, offset=0, rows=rows)
+    st = parity.assert_parity(to64(o).reshape(-1, w.D)[rows], to64(lse).reshape(-1)[rows], o_ref, l_ref,
+                              w.dtype, "ext workload rows")
+    say("  ", st)

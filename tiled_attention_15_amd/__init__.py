@@ -14,7 +14,8 @@ import os
 
 __all__ = ["FaError", "fa_fwd", "fa_fwd_strided", "fa_fwd_plan", "fa_naive_fwd",
            "fa_naive_workspace_bytes", "fa_status_string", "fa_version", "forward",
-           "naive_forward", "library_path", "F16", "BF16", "STATUS"]
+           "naive_forward", "library_path", "F16", "BF16", "STATUS", "fa_bwd",
+           "fa_bwd_workspace_bytes", "backward", "fa_fwd_ext", "forward_ext"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libfa_hip.so")
@@ -22,7 +23,7 @@ _LIB_PATH = os.path.join(_PKG, "libfa_hip.so")
 F16, BF16 = 0, 1
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED",
           4: "FA_ERR_ALIGN", 5: "FA_ERR_SCALE", 6: "FA_ERR_HIP", 7: "FA_ERR_ALIAS",
-          8: "FA_ERR_STRIDE"}
+          8: "FA_ERR_STRIDE", 9: "FA_ERR_MASK_DROPOUT"}
 
 _lib = None
 
@@ -69,6 +70,9 @@ def _load():
     lib.fa_bwd.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_int64
+    lib.fa_fwd_ext.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, i64p, f, ctypes.c_uint64,
+                               ctypes.c_uint32, f, i, i, vp]
+    lib.fa_fwd_ext.restype = i
     _lib = lib
     return lib
 
@@ -132,6 +136,17 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, scale, causal, dt
                           _ptr(dk), _ptr(dv), B, H, Sq, Sk, D, float(scale), int(bool(causal)),
                           int(dtype), int(bool(deterministic)), _ptr(workspace),
                           int(workspace_bytes), _stream(stream))
+
+
+def fa_fwd_ext(q, k, v, o, lse, B, H, Sq, Sk, D, mask, mask_strides, dropout_p, seed, offset,
+               scale, causal, dtype, stream):
+    """C ABI fa_fwd_ext: the forward with an explicit boolean mask and/or dropout."""
+    ms = None if mask_strides is None else _strides3(mask_strides)
+    return _load().fa_fwd_ext(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(Sq),
+                              int(Sk), int(D), _ptr(mask), ms, ctypes.c_float(dropout_p),
+                              ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF),
+                              ctypes.c_uint32(int(offset) & 0xFFFFFFFF), ctypes.c_float(scale),
+                              int(bool(causal)), int(dtype), _stream(stream))
 
 
 def fa_bwd_workspace_bytes(B, H, Sq, D, deterministic):
@@ -278,3 +293,43 @@ def backward(q, k, v, o, lse, dout, causal=False, scale=None, deterministic=True
     if st != 0:
         raise FaError(st, "fa_bwd")
     return dq, dk, dv
+
+
+def forward_ext(q, k, v, causal=False, scale=None, mask=None, dropout_p=0.0, seed=0, offset=0):
+    """Forward with an explicit boolean mask and/or dropout on contiguous
+    [B, H, Sq, D] q and [B, H, Sk, D] k, v GPU tensors.  mask: a uint8 or bool
+    GPU tensor broadcastable to [B, H, Sq, Sk] (nonzero keeps), with a
+    contiguous last dimension and the other strides multiples of 4 bytes.
+    Returns (o, lse)."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("fa: q [B, H, Sq, D] and k, v [B, H, Sk, D] expected")
+    if q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+        raise ValueError("fa: q and k must share batch, heads and head dimension")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("fa: the masked/dropout forward takes contiguous q, k, v")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("fa: q, k, v must share one dtype")
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    strides = None
+    if mask is not None:
+        if mask.dtype == torch.bool:
+            mask = mask.view(torch.uint8)
+        if mask.dtype != torch.uint8 or mask.device != q.device:
+            raise ValueError("fa: mask must be a uint8/bool tensor on q's device")
+        mask = mask.expand(B, H, Sq, Sk)
+        if mask.stride(3) != 1:
+            raise ValueError("fa: the mask's last dimension must be contiguous")
+        strides = (mask.stride(0), mask.stride(1), mask.stride(2))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream().cuda_stream
+    st = fa_fwd_ext(q, k, v, o, lse, B, H, Sq, Sk, D, mask, strides, dropout_p, seed, offset,
+                    scale, causal, _dtype_code(q), stream)
+    if st != 0:
+        raise FaError(st, "fa_fwd_ext")
+    return o, lse

@@ -12,7 +12,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa_hip.so")
 SOURCES = [os.path.join(CSRC, "fa_api.cpp"), os.path.join(CSRC, "fa_fwd_kernel.hip"),
-           os.path.join(CSRC, "fa_naive.hip"), os.path.join(CSRC, "fa_bwd.hip")]
+           os.path.join(CSRC, "fa_naive.hip"), os.path.join(CSRC, "fa_bwd.hip"),
+           os.path.join(CSRC, "fa_fwd_ext.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

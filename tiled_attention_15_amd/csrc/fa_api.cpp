@@ -12,6 +12,7 @@
 #include "fa.h"
 #include "fa_launch.h"
 #include "fa_bwd.h"
+#include "fa_ext.h"
 #include "fa_naive.h"
 
 namespace {
@@ -96,6 +97,7 @@ const char* fa_status_string(int status) {
         case FA_ERR_HIP: return "HIP runtime error at launch";
         case FA_ERR_ALIAS: return "output buffer overlaps an input or the other output";
         case FA_ERR_STRIDE: return "invalid strides (negative, not a multiple of 8, row stride < D, or overlapping output)";
+        case FA_ERR_MASK_DROPOUT: return "invalid mask layout or dropout probability";
         default: return "unknown status";
     }
 }
@@ -284,6 +286,67 @@ bool bwd_span_ok(int S, int D) {
 }
 
 }  // namespace
+
+int fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Sq,
+               int Sk, int D, const uint8_t* mask, const int64_t* mask_strides, float dropout_p,
+               uint64_t seed, uint32_t offset, float scale, int causal, int dtype, void* stream) {
+    if (!q || !k || !v || !o) return FA_ERR_NULL;
+    int st = validate_shape(B, H, Sq, Sk, D, dtype);
+    if (st != FA_OK) return st;
+    if (!bwd_span_ok(std::max(Sq, Sk), D)) return FA_ERR_SHAPE;
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse) & 15) return FA_ERR_ALIGN;
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_SCALE;
+    if (!(dropout_p >= 0.0f) || !(dropout_p < 1.0f)) return FA_ERR_MASK_DROPOUT;
+    const long t = lrintf(dropout_p * 65536.0f);
+    if (t > 65535) return FA_ERR_MASK_DROPOUT;
+    uintptr_t m0 = 0, m1 = 0;
+    if (mask) {
+        if (!mask_strides || ((uintptr_t)mask & 3)) return FA_ERR_MASK_DROPOUT;
+        for (int i = 0; i < 3; ++i)
+            if (mask_strides[i] < 0 || (mask_strides[i] & 3) != 0) return FA_ERR_MASK_DROPOUT;
+        if (mask_strides[2] < Sk || mask_strides[2] >= (int64_t(1) << 31)) return FA_ERR_MASK_DROPOUT;
+        if ((int64_t)(Sq - 1) * mask_strides[2] + Sk + 3 >= (int64_t(1) << 31)) return FA_ERR_MASK_DROPOUT;
+        m0 = (uintptr_t)mask;
+        m1 = m0 + (uintptr_t)((int64_t)(B - 1) * mask_strides[0] + (int64_t)(H - 1) * mask_strides[1] +
+                              (int64_t)(Sq - 1) * mask_strides[2] + Sk);
+    }
+    const uintptr_t qb = (uintptr_t)((int64_t)B * H * Sq * D * 2);
+    const uintptr_t kb = (uintptr_t)((int64_t)B * H * Sk * D * 2);
+    const uintptr_t lb = (uintptr_t)((int64_t)B * H * Sq * 4);
+    const uintptr_t in[4][2] = {{(uintptr_t)q, (uintptr_t)q + qb}, {(uintptr_t)k, (uintptr_t)k + kb},
+                                {(uintptr_t)v, (uintptr_t)v + kb}, {m0, m1}};
+    const uintptr_t out[2][2] = {{(uintptr_t)o, (uintptr_t)o + qb}, {(uintptr_t)lse, (uintptr_t)lse + (lse ? lb : 0)}};
+    for (int i = 0; i < 2; ++i) {
+        if (out[i][1] == out[i][0]) continue;
+        for (int j = 0; j < 4; ++j)
+            if (in[j][1] > in[j][0] && overlap(out[i][0], out[i][1], in[j][0], in[j][1])) return FA_ERR_ALIAS;
+    }
+    if (lse && overlap(out[0][0], out[0][1], out[1][0], out[1][1])) return FA_ERR_ALIAS;
+
+    fa::ext::ExtParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.mask = mask;
+    p.m_sb = mask ? mask_strides[0] : 0;
+    p.m_sh = mask ? mask_strides[1] : 0;
+    p.m_ss = mask ? mask_strides[2] : 0;
+    p.Sq = Sq;
+    p.Sk = Sk;
+    p.H = H;
+    p.BH = B * H;
+    p.nqb = (Sq + fa::ext::kQueryBlock - 1) / fa::ext::kQueryBlock;
+    p.scale_log2e = (float)((double)scale * 1.4426950408889634074);
+    p.drop_t = (uint32_t)t;
+    p.keep_scale = (float)(65536.0 / (65536.0 - (double)t));
+    p.seed_lo = (uint32_t)seed;
+    p.seed_hi = (uint32_t)(seed >> 32);
+    p.offset = offset;
+    const hipError_t err = fa::ext::launch_ext(p, D, dtype, causal != 0, (hipStream_t)stream);
+    return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
 
 int64_t fa_bwd_workspace_bytes(int B, int H, int Sq, int D, int deterministic) {
     BwdLayout L;

@@ -34,155 +34,17 @@
 //             through LDS; S^T = K Q^T, dP^T = V dO^T, then dQ^T += K^T dS^T;
 //   bwd_dq_convert  (atomic) dQ = scale * accumulator, rounded to the dtype.
 //
-// Operand layout of v_mfma_f32_32x32x16: lane l supplies row (A) or column
-// (B) l%32 and the 8 k-values in slots 8*(l/32)..+7; accumulator register r
-// of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.  Taking the
-// accumulator of one product as an operand of the next makes k-slot e of
-// lane half g in k-step s stand for row 16*s + 8*(e/4) + 4*g + e%4; the LDS
-// operand of that product is read with the same mapping: two transposing
-// reads, each of four consecutive rows.
+// The operand layouts and LDS helpers are in fa_tile.h.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "fa_bwd.h"
+#include "fa_tile.h"
 
 namespace fa {
 namespace bwd {
 
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) char lds_t;
-
-constexpr float LOG2E = 1.4426950408889634f;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
-                                             (int)(bytes < 0x80000000ull ? bytes : 0x7fffffffull),
-                                             (int)0x00020000);
-}
-
-template <int DT>
-__device__ __forceinline__ f32x16 mma(i32x4 a, i32x4 b, f32x16 c) {
-    if constexpr (DT == 0)
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-    else
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-// Two fp32 -> one dword of two 16-bit values (round to nearest even).
-template <int DT>
-__device__ __forceinline__ int pack2(float x, float y) {
-    if constexpr (DT == 0)
-        return __builtin_bit_cast(int, __builtin_convertvector((f32x2){x, y}, f16x2));
-    else
-        return __builtin_bit_cast(int, __builtin_convertvector((f32x2){x, y}, bf16x2));
-}
-
-// The 16-bit value in the low (hi = 0) or high half of a dword, as fp32.
-template <int DT>
-__device__ __forceinline__ float half_f32(int w, int hi) {
-    const uint32_t h = ((uint32_t)w >> (16 * hi)) & 0xffffu;
-    if constexpr (DT == 0)
-        return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-    else
-        return __uint_as_float(h << 16);
-}
-
-__device__ __forceinline__ f32x16 zero16() {
-    f32x16 z;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) z[i] = 0.0f;
-    return z;
-}
-
-// LDS tiles are [rows][W] 16-bit values (W = 64 or 128), stored in 16-byte
-// chunks whose index within the row is XOR-ed with swz(row).  A fragment
-// read (16 lanes on 16 consecutive rows, one chunk each) and a transposing
-// read (16 lanes on four consecutive rows, two adjacent chunks each) both
-// fall on distinct chunk positions.
-template <int W>
-__device__ __forceinline__ int swz(int r) {
-    const int f = ((r & 3) << 1) | ((r >> 2) & 1);
-    if constexpr (W == 128)
-        return f | (((r >> 3) & 1) << 3);
-    else
-        return f;
-}
-template <int W>
-__device__ __forceinline__ int toff(int r, int ch) {
-    return r * (2 * W) + ((ch ^ swz<W>(r)) << 4);
-}
-
-// Operand fragment by rows: 8 consecutive values (chunk ch) of row r.
-template <int W>
-__device__ __forceinline__ i32x4 row_frag(const lds_t* tile, int r, int ch) {
-    return *(const __attribute__((address_space(3))) i32x4*)(tile + toff<W>(r, ch));
-}
-
-// Per-lane constants of the transposing reads: source lane 4j + t of each
-// 16-lane group G addresses row 4*(G/2) + j (+16 s, +8 for the second read)
-// and columns 16*(G%2) + 4t .. +3 of a 32-column block.
-struct TrLane {
-    int row, ch, byte;
-};
-__device__ __forceinline__ TrLane tr_lane(int lane) {
-    const int G = lane >> 4, m = lane & 15;
-    return {4 * (G >> 1) + (m >> 2), 2 * (G & 1) + ((m & 3) >> 1), (m & 1) * 8};
-}
-
-// Operand fragment of column block b (columns 32b + lane%32) over rows
-// 16s .. 16s+15 in the k-slot order above.
-template <int W>
-__device__ __forceinline__ i32x4 tr_frag(const lds_t* tile, int s, int b, const TrLane& tl) {
-    const int r0 = 16 * s + tl.row, r1 = r0 + 8, ch = 4 * b + tl.ch;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(tile + r0 * (2 * W) + ((ch ^ swz<W>(r0)) << 4) + tl.byte));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(tile + r1 * (2 * W) + ((ch ^ swz<W>(r1)) << 4) + tl.byte));
-    i32x4 a;
-    a[0] = (int)(uint16_t)lo[0] | ((int)(uint16_t)lo[1] << 16);
-    a[1] = (int)(uint16_t)lo[2] | ((int)(uint16_t)lo[3] << 16);
-    a[2] = (int)(uint16_t)hi[0] | ((int)(uint16_t)hi[1] << 16);
-    a[3] = (int)(uint16_t)hi[2] | ((int)(uint16_t)hi[3] << 16);
-    return a;
-}
-
-// B operand of k-step s from a 32-row-block pair of accumulators (rows
-// 32*(s/2) .. of the product), packed to 16 bits.
-template <int DT>
-__device__ __forceinline__ i32x4 acc_frag(const f32x16& x, int h) {
-    i32x4 a;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = pack2<DT>(x[8 * h + 2 * i], x[8 * h + 2 * i + 1]);
-    return a;
-}
-
-// Workgroup -> (batch*head, block).  When the head count is a multiple of 8,
-// each XCD (workgroup ids are dealt round-robin over the 8 XCDs) takes a
-// contiguous range of heads, so the blocks of a head share one L2.  Blocks
-// of a head come in slot order; `reverse` hands out the last block first.
-__device__ __forceinline__ void block_order(int wg, int nblk, int BH, bool reverse, int& bh, int& blk) {
-    int slot;
-    if ((BH & 7) == 0) {
-        const int xcd = wg & 7, k = wg >> 3, hpx = BH >> 3;
-        bh = xcd * hpx + k % hpx;
-        slot = k / hpx;
-    } else {
-        bh = wg % BH;
-        slot = wg / BH;
-    }
-    blk = reverse ? (nblk - 1 - slot) : slot;
-}
+using namespace tile;
 
 // ---------------------------------------------------------------------------
 // D_i = sum_d dO_id O_id in fp32; in atomic mode also zero the dQ accumulator.

@@ -1,0 +1,278 @@
+// fa_fwd_ext.hip -- fused attention forward with an explicit boolean mask and
+// keep-and-rescale dropout, for gfx950 (MI355X).
+//
+// Mask and dropout are applied inside the attention kernel, on the score tile
+// in registers, so neither a mask pass nor a dropout pass over an S x S
+// matrix touches device memory ("FlashAttention-2 on Ascend NPU: how
+// ops-transformer reaches 3x" (2048ai.net), section 3.4, and section 6.3).
+// Semantics:
+//   * a nonzero mask byte keeps the score, a zero byte hides it (as the
+//     page's kernel treats a true entry); combined with the causal rule;
+//   * dropout keeps each probability with probability 1 - t/65536 and scales
+//     the kept ones by 65536 / (65536 - t); the row normaliser (and the lse)
+//     is that of the undropped softmax.  The keep decision of score (bh, i, j)
+//     compares half j%2 of word (j%8)/2 of Philox4x32-10 (Salmon et al.,
+//     "Parallel random numbers: as easy as 1, 2, 3", SC 2011) at counter
+//     (j/8, i, bh, offset) and key (seed low, seed high) with t, so any
+//     implementation of the generator reproduces the pattern.
+//
+// Layout (the helpers and operand conventions are in fa_tile.h): a workgroup
+// of 4 waves owns 128 query rows, 32 per wave, with Q resident in registers
+// as the B operand of S^T = K Q^T (keys on MFMA rows, queries on columns, so
+// a lane holds one query and 32 keys of a tile).  64-key tiles of K and V
+// stream through LDS, double-buffered and staged through registers.  Per
+// tile: mask bytes (one dword per four keys) are loaded before the MFMAs, the
+// online softmax runs in fp32 on the accumulators, the dropout decisions are
+// drawn, and O^T += V^T P^T takes P straight from the accumulators with V^T
+// read by transposing LDS reads.  This kernel is the general path for masks
+// and dropout; the plain forward (fa_fwd_kernel.hip) is the tuned one.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_ext.h"
+#include "fa_tile.h"
+
+namespace fa {
+namespace ext {
+
+using namespace tile;
+
+// Philox4x32-10 block function: ten rounds of two 32x32->64 multiplications
+// (0xD2511F53, 0xCD9E8D57) whose high halves are XOR-ed with the other two
+// counter words and the key; the key is bumped by (0x9E3779B9, 0xBB67AE85)
+// between rounds.
+__device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint32_t hi0 = __umulhi(0xD2511F53u, c[0]), lo0 = 0xD2511F53u * c[0];
+        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c[2]), lo1 = 0xCD9E8D57u * c[2];
+        const uint32_t n0 = hi1 ^ c[1] ^ k0;
+        const uint32_t n2 = hi0 ^ c[3] ^ k1;
+        c[0] = n0;
+        c[1] = lo1;
+        c[2] = n2;
+        c[3] = lo0;
+    }
+}
+
+template <int D, int DT, bool CAUSAL, bool MASK, bool DROP>
+__global__ __launch_bounds__(256) void fwd_ext(ExtParams p) {
+    constexpr int DC = D / 16, DB = D / 32;
+    constexpr int KT = kKeyTile;
+    constexpr int TILE = KT * D * 2;
+    constexpr int CPT = KT * D / 8 / 256;
+    static_assert(CPT >= 1, "tile must split over the threads");
+
+    __shared__ __attribute__((aligned(16))) char smem[4 * TILE];
+    lds_t* const sm = (lds_t*)smem;
+
+    const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, g = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int bh, qb;
+    block_order(blockIdx.x, p.nqb, p.BH, CAUSAL, bh, qb);
+    const int Sq = p.Sq, Sk = p.Sk, diag = Sk - Sq;
+    const int q0 = qb * kQueryBlock, qw0 = q0 + 32 * w;
+    const int qi = qw0 + lq;
+
+    const __amdgpu_buffer_rsrc_t rq = rsrc((const char*)p.q + (int64_t)bh * Sq * D * 2, (uint64_t)Sq * D * 2);
+    const __amdgpu_buffer_rsrc_t rk = rsrc((const char*)p.k + (int64_t)bh * Sk * D * 2, (uint64_t)Sk * D * 2);
+    const __amdgpu_buffer_rsrc_t rv = rsrc((const char*)p.v + (int64_t)bh * Sk * D * 2, (uint64_t)Sk * D * 2);
+
+    // Mask rows of this head: a buffer over [first row, last row + Sk)
+    // rounded up to whole dwords; offsets beyond it read as zero (hidden).
+    __amdgpu_buffer_rsrc_t rm = rq;
+    if constexpr (MASK) {
+        const int b_ = bh / p.H, h_ = bh - b_ * p.H;
+        const uint8_t* mb = p.mask + (int64_t)b_ * p.m_sb + (int64_t)h_ * p.m_sh;
+        rm = rsrc(mb, (uint64_t)(((int64_t)(Sq - 1) * p.m_ss + Sk + 3) & ~(int64_t)3));
+    }
+
+    i32x4 qf[DC];
+#pragma unroll
+    for (int c = 0; c < DC; ++c)
+        qf[c] = __builtin_amdgcn_raw_buffer_load_b128(rq, (qi * D + 16 * c + 8 * g) * 2, 0, 0);
+
+    int nkt = (Sk + KT - 1) / KT;
+    if (CAUSAL) nkt = min(nkt, max(0, (min(Sq, q0 + kQueryBlock) + diag + KT - 1) / KT));
+
+    i32x4 sk[CPT], sv[CPT];
+    auto fetch = [&](int t) {
+        const int k0 = t * KT;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int ci = tid + 256 * i, r = ci / (D / 8), ch = ci % (D / 8);
+            sk[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((k0 + r) * D + 8 * ch) * 2, 0, 0);
+            sv[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((k0 + r) * D + 8 * ch) * 2, 0, 0);
+        }
+    };
+    auto commit = [&](int buf) {
+        lds_t* tk = sm + buf * 2 * TILE;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int ci = tid + 256 * i, r = ci / (D / 8), ch = ci % (D / 8);
+            *(__attribute__((address_space(3))) i32x4*)(tk + toff<D>(r, ch)) = sk[i];
+            *(__attribute__((address_space(3))) i32x4*)(tk + TILE + toff<D>(r, ch)) = sv[i];
+        }
+    };
+
+    const TrLane tl = tr_lane(lane);
+    const float c2 = p.scale_log2e;
+    f32x16 oa[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) oa[b] = zero16();
+    float m_run = -INFINITY;   // running max, base-2 units
+    float l_run = 0.0f;        // this lane's share of the running sum
+
+    if (nkt > 0) {
+        fetch(0);
+        commit(0);
+    }
+    __syncthreads();
+
+    for (int t = 0; t < nkt; ++t) {
+        const int buf = t & 1;
+        if (t + 1 < nkt) fetch(t + 1);
+        const lds_t* tk = sm + buf * 2 * TILE;
+        const lds_t* tv = tk + TILE;
+        const int kt0 = t * KT;
+
+        // mask bytes of keys kt0 + 32rb + 8a + 4g .. +3 for this lane's query
+        uint32_t mk[2][4];
+        if constexpr (MASK) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+                    mk[rb][a] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+                        rm, (uint32_t)((int64_t)qi * p.m_ss + kt0 + 32 * rb + 8 * a + 4 * g), 0, 0);
+        }
+
+        // S^T = K Q^T: 64 keys x this wave's 32 queries
+        f32x16 s[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) s[rb] = zero16();
+#pragma unroll
+        for (int c = 0; c < DC; ++c)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+                s[rb] = mma<DT>(row_frag<D>(tk, 32 * rb + lq, 2 * c + g), qf[c], s[rb]);
+
+        const bool need_mask = MASK || (kt0 + KT > Sk) || (CAUSAL && kt0 + KT - 1 > qw0 + diag);
+        if (need_mask) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kj = kt0 + 32 * rb + 8 * (r >> 2) + 4 * g + (r & 3);
+                    bool vis = kj < Sk && (!CAUSAL || kj <= qi + diag);
+                    if constexpr (MASK) vis = vis && ((mk[rb][r >> 2] >> (8 * (r & 3))) & 0xffu) != 0;
+                    if (!vis) s[rb][r] = -INFINITY;
+                }
+        }
+
+        // online softmax (base 2, scale*log2(e) folded into one FMA)
+        float mx = s[0][0];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[rb][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        const float mb = (m_new == -INFINITY) ? 0.0f : m_new;
+        m_run = m_new;
+        float lsum = 0.0f;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][r], c2, -mb));
+                s[rb][r] = e;
+                lsum += e;
+            }
+        l_run = l_run * alpha + lsum;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+            for (int b = 0; b < DB; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oa[b][i] *= alpha;
+        }
+
+        if constexpr (DROP) {
+            // keys kt0 + 32rb + 8a + 0..7 share one Philox call; this lane
+            // uses words 2g and 2g+1 (keys 8a + 4g + 0..3)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    uint32_t c[4] = {(uint32_t)((kt0 + 32 * rb + 8 * a) >> 3), (uint32_t)qi, (uint32_t)bh,
+                                     p.offset};
+                    philox4x32_10(c, p.seed_lo, p.seed_hi);
+                    const uint32_t w0 = g ? c[2] : c[0];
+                    const uint32_t w1 = g ? c[3] : c[1];
+                    const uint32_t r16[4] = {w0 & 0xffffu, w0 >> 16, w1 & 0xffffu, w1 >> 16};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (r16[e] < p.drop_t) s[rb][4 * a + e] = 0.0f;
+                }
+        }
+
+        // O^T += V^T P^T
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const i32x4 pa = acc_frag<DT>(s[st >> 1], st & 1);
+#pragma unroll
+            for (int b = 0; b < DB; ++b) oa[b] = mma<DT>(tr_frag<D>(tv, st, b, tl), pa, oa[b]);
+        }
+
+        if (t + 1 < nkt) commit(buf ^ 1);
+        __syncthreads();
+    }
+
+    // O = O^T / l (times the dropout rescale): register r of block b holds
+    // head-dimension index 32b + 8(r/4) + 4g + r%4 of query qi.
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = l_tot > 0.0f ? p.keep_scale / l_tot : 0.0f;
+    const __amdgpu_buffer_rsrc_t wo = rsrc((char*)p.o + (int64_t)bh * Sq * D * 2, (uint64_t)Sq * D * 2);
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            i32x2 v2;
+            v2[0] = pack2<DT>(oa[b][4 * a] * inv, oa[b][4 * a + 1] * inv);
+            v2[1] = pack2<DT>(oa[b][4 * a + 2] * inv, oa[b][4 * a + 3] * inv);
+            __builtin_amdgcn_raw_buffer_store_b64(v2, wo, (uint32_t)((qi * D + 32 * b + 8 * a + 4 * g) * 2), 0, 0);
+        }
+    }
+    if (p.lse != nullptr && g == 0 && qi < Sq) {
+        const float lse2 = l_tot > 0.0f ? m_run + log2f(l_tot) : -INFINITY;
+        p.lse[(int64_t)bh * Sq + qi] = lse2 * 0.69314718055994530942f;
+    }
+}
+
+template <int D, int DT, bool CAUSAL>
+static hipError_t run(const ExtParams& p, hipStream_t st) {
+    const dim3 grid((unsigned)(p.BH * p.nqb)), block(256);
+    const bool mask = p.mask != nullptr, drop = p.drop_t != 0;
+    if (mask && drop) hipLaunchKernelGGL((fwd_ext<D, DT, CAUSAL, true, true>), grid, block, 0, st, p);
+    else if (mask) hipLaunchKernelGGL((fwd_ext<D, DT, CAUSAL, true, false>), grid, block, 0, st, p);
+    else if (drop) hipLaunchKernelGGL((fwd_ext<D, DT, CAUSAL, false, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((fwd_ext<D, DT, CAUSAL, false, false>), grid, block, 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_ext(const ExtParams& p, int D, int dtype, int causal, hipStream_t stream) {
+    if (D == 64) {
+        if (dtype == 0) return causal ? run<64, 0, true>(p, stream) : run<64, 0, false>(p, stream);
+        return causal ? run<64, 1, true>(p, stream) : run<64, 1, false>(p, stream);
+    }
+    if (dtype == 0) return causal ? run<128, 0, true>(p, stream) : run<128, 0, false>(p, stream);
+    return causal ? run<128, 1, true>(p, stream) : run<128, 1, false>(p, stream);
+}
+
+}  // namespace ext
+}  // namespace fa
