@@ -20,10 +20,11 @@ Prints ONE JSON line:
              library), timed the same way, with the fused kernel's speedup.
   backward   the gradients (fa_bwd) on the same inputs, atomic and
              deterministic dq modes, in TFLOP/s at 2.5x the forward's flops.
+  mask_dropout  the forward with an explicit mask and/or dropout (fa_fwd_ext).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--cpu-seconds T] [--no-cpu-baseline] [--no-naive]
-                       [--no-backward]
+                       [--no-backward] [--no-ext]
 """
 import argparse
 import hashlib
@@ -200,6 +201,56 @@ def backward_leg(w, steps, warmup):
     return out
 
 
+def ext_leg(w, steps, warmup):
+    """The masked/dropout forward (fa_fwd_ext) on the same inputs: without
+    mask or dropout, with a shared random boolean mask (90% of scores kept),
+    with dropout 0.1, and with both.  TFLOP/s at the forward's algorithmic
+    flops (a mask hides scores but the convention counts the full causal
+    product)."""
+    import numpy as np
+    import torch
+    import tiled_attention_15_amd as fa
+
+    dev = torch.device("cuda:0")
+    q, k, v = workload_inputs(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+    ld = (w.S + 3) // 4 * 4
+    rng = np.random.default_rng(2400)
+    mask = torch.zeros((w.S, ld), dtype=torch.uint8)
+    mask[:, :w.S] = torch.from_numpy((rng.random((w.S, w.S)) < 0.9).astype(np.uint8))
+    md = mask.to(dev)
+    stream = torch.cuda.current_stream(dev)
+    code = fa.BF16 if w.dtype == "bf16" else fa.F16
+    out = {"unit": "TFLOP/s", "steps": steps, "mask": "one [S, S] uint8 mask shared by all heads, 90% kept",
+           "dropout_p": 0.1}
+    for name, m, p in (("plain", None, 0.0), ("mask", md, 0.0), ("dropout", None, 0.1), ("mask_dropout", md, 0.1)):
+        ms = None if m is None else (0, 0, ld)
+
+        def step():
+            st = fa.fa_fwd_ext(qd, kd, vd, o, lse, w.B, w.H, w.S, w.S, w.D, m, ms, p, 1234, 0,
+                               w.scale, w.causal, code, stream)
+            if st != 0:
+                raise fa.FaError(st, "fa_fwd_ext")
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms_step = ev0.elapsed_time(ev1) / steps
+        tf = w.flops() / (ms_step * 1e-3) / 1e12
+        out[name] = {"ms_per_step": round(ms_step, 4), "value": round(tf, 3),
+                     "frac_of_mfma_peak": round(tf / MFMA_PEAK_TFLOPS, 4)}
+    return out
+
+
 def copy_leg(mib, steps, warmup):
     """A plain device copy of known size: its HBM byte counters per dispatch
     calibrate the counters read on the attention kernel."""
@@ -275,6 +326,8 @@ def main():
                     help="skip the unfused comparison path")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward (gradient) timing")
+    ap.add_argument("--no-ext", action="store_true",
+                    help="skip the masked / dropout forward timing")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of attention, time a plain device-to-device copy of this many "
                          "MiB (the reference kernel for scaling HBM byte counters)")
@@ -322,6 +375,8 @@ def main():
         out["naive_unfused"] = nv
     if not a.no_backward:
         out["backward"] = backward_leg(w, max(2, min(20, a.steps // 10)), 2)
+    if not a.no_ext:
+        out["mask_dropout"] = ext_leg(w, max(2, min(20, a.steps // 10)), 2)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_leg(w, a.cpu_seconds)
     print(json.dumps(out), flush=True)
