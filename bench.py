@@ -170,6 +170,9 @@ def backward_leg(w, steps, warmup):
     code = fa.BF16 if w.dtype == "bf16" else fa.F16
     flops = 2.5 * w.flops()
     out = {"unit": "TFLOP/s", "flops_per_step": flops, "steps": steps}
+    if fa.fa_bwd_workspace_bytes(w.B, w.H, w.S, w.D, True) <= 0:
+        out["skipped"] = "the backward takes D in {64, 128}"
+        return out
     for det in (False, True):
         need = fa.fa_bwd_workspace_bytes(w.B, w.H, w.S, w.D, det)
         ws = torch.empty(need, dtype=torch.uint8, device=dev)

@@ -55,7 +55,8 @@ typedef enum {
     FA_OK = 0,
     FA_ERR_NULL = 1,         /* q, k, v or o is NULL */
     FA_ERR_SHAPE = 2,        /* B, H or S < 1, or a size beyond the limits below */
-    FA_ERR_UNSUPPORTED = 3,  /* D not in {64, 128}, or dtype not an fa_dtype */
+    FA_ERR_UNSUPPORTED = 3,  /* D not in {64, 128, 256} ({64, 128} for fa_bwd and
+                                fa_naive_fwd), or dtype not an fa_dtype */
     FA_ERR_ALIGN = 4,        /* a pointer is not 16-byte aligned */
     FA_ERR_SCALE = 5,        /* scale is not finite or not > 0 */
     FA_ERR_HIP = 6,          /* the HIP runtime reported an error at launch */
@@ -77,7 +78,10 @@ typedef enum {
  *            skip it.
  *   B, H, S  batch, heads, sequence length (>= 1; any S, not only multiples
  *            of the tile; B*H*S*D < 2^40 and S*D*2 bytes < 2^31).
- *   D        head dimension, 64 or 128.
+ *   D        head dimension, 64, 128 or 256.  D = 256 (named among the
+ *            head dimensions of "FlashAttention-2 on Ascend NPU" (2048ai.net),
+ *            tiling parameters) runs on the general kernel of fa_fwd_ext
+ *            (128-row blocks, 32-key tiles), the others on the tuned one.
  *   scale    softmax scale applied to q.k (callers normally pass
  *            1/sqrt(D)); finite and > 0.
  *   causal   0: every key visible; nonzero: key j visible to query i iff
@@ -267,7 +271,7 @@ int fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
  *                    and no synchronisation inside.
  * All pointers 16-byte aligned.  Inputs may overlap each other; dq, dk, dv
  * and the workspace must not overlap each other or any input (FA_ERR_ALIAS).
- * Limits: D in {64, 128}; (max(Sq, Sk) rounded up to 128, plus 128) * D * 2
+ * Limits: D in {64, 128} (256: FA_ERR_UNSUPPORTED); (max(Sq, Sk) rounded up to 128, plus 128) * D * 2
  * bytes below 2^31.  Returns FA_OK or a status as for fa_fwd; nothing is
  * enqueued on error.
  */

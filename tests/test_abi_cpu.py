@@ -74,7 +74,7 @@ def call(**kw):
     (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(o=0), 1),
     (dict(B=0), 2), (dict(H=0), 2), (dict(S=0), 2), (dict(S=-5), 2), (dict(B=-1), 2),
     (dict(S=1 << 23, D=128), 2),
-    (dict(D=96), 3), (dict(D=256), 3), (dict(D=0), 3), (dict(dtype=2), 3), (dict(dtype=-1), 3),
+    (dict(D=96), 3), (dict(D=512), 3), (dict(D=0), 3), (dict(dtype=2), 3), (dict(dtype=-1), 3),
     (dict(q=Q + 8), 4), (dict(o=O + 2), 4), (dict(lse=L + 4), 4),
     (dict(scale=0.0), 5), (dict(scale=-1.0), 5), (dict(scale=float("nan")), 5),
     (dict(scale=float("inf")), 5),
@@ -203,6 +203,8 @@ def test_naive_rejects_bad_arguments(lib):
     assert ncall(o=K) == 7
     assert ncall(scale=0.0) == 5
     assert ncall(D=96) == 3
+    assert ncall(D=256) == 3                 # the unfused path stops at D = 128
+    assert fa.fa_naive_workspace_bytes(1, 1, 256, 256) == 0
 
 
 @fake_addresses
@@ -230,6 +232,7 @@ def test_bwd_rejects_bad_arguments(lib):
     assert bcall(Sq=0) == 2 and bcall(B=0) == 2
     assert bcall(wsb=need - 1) == 2
     assert bcall(D=96) == 3 and bcall(dtype=2) == 3
+    assert bcall(D=256) == 3                 # the backward stops at D = 128
     assert bcall(Sk=1 << 24, wsb=1 << 40) == 2          # head span beyond 32-bit offsets
     assert bcall(dk=DK + 8) == 4 and bcall(ws=W + 4) == 4
     assert bcall(scale=float("nan")) == 5 and bcall(scale=-1.0) == 5
@@ -268,3 +271,14 @@ def test_ext_rejects_bad_arguments(lib):
     assert ecall(o=M + 64) == 7                         # output over the mask
     assert ecall(lse=K) == 7
     assert ecall(Sq=1 << 24, Sk=1 << 24, ms=(0, 0, 1 << 24)) == 2    # head span beyond 32-bit offsets
+
+
+def test_plan_d256_uses_the_general_kernel(lib):
+    for causal in (0, 1):
+        br, bc, grid, tiles = fa.fa_fwd_plan(2, 3, 1000, 256, causal, 1)
+        assert (br, bc) == (128, 32)
+        nqb = (1000 + 127) // 128
+        assert grid == 2 * 3 * nqb
+        nkv = (1000 + 31) // 32
+        want = sum(min(nkv, (min(1000, (qb + 1) * 128) + 31) // 32) if causal else nkv for qb in range(nqb))
+        assert tiles == want * 6

@@ -21,7 +21,7 @@ constexpr int kVersion = 1 * 10000 + 2 * 100 + 0;
 
 int validate_shape(int B, int H, int Sq, int Sk, int D, int dtype) {
     if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return FA_ERR_SHAPE;
-    if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
     if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
     const int S = Sq > Sk ? Sq : Sk;
     const int64_t elems = (int64_t)B * H * S * D;
@@ -107,7 +107,9 @@ int fa_fwd_plan(int B, int H, int S, int D, int causal, int dtype, int* block_q,
     int st = validate_shape(B, H, S, S, D, dtype);
     if (st == FA_OK && !head_span_ok(S, D, D)) st = FA_ERR_SHAPE;
     if (st != FA_OK) return st;
-    const int br = fa::kBlockQ, bc = fa::kBlockKV;
+    // D = 256 runs on the general kernel (128-row blocks, 32-key tiles)
+    const int br = D == 256 ? fa::ext::kQueryBlock : fa::kBlockQ;
+    const int bc = D == 256 ? fa::ext::key_tile(256) : fa::kBlockKV;
     const int64_t nqb = (S + br - 1) / br;
     const int64_t nkv = (S + bc - 1) / bc;
     if (block_q) *block_q = br;
@@ -160,6 +162,32 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
             return FA_ERR_ALIAS;
     }
 
+    if (D == 256) {
+        // the tuned kernel holds O and Q in registers for D <= 128; D = 256
+        // runs on the general kernel with neither mask nor dropout
+        fa::ext::ExtParams e = {};
+        e.q = q;
+        e.k = k;
+        e.v = v;
+        e.o = o;
+        e.lse = lse;
+        e.q_sb = q_strides[0], e.q_sh = q_strides[1], e.q_ss = (int)q_strides[2];
+        e.k_sb = k_strides[0], e.k_sh = k_strides[1], e.k_ss = (int)k_strides[2];
+        e.v_sb = v_strides[0], e.v_sh = v_strides[1], e.v_ss = (int)v_strides[2];
+        e.o_sb = o_strides[0], e.o_sh = o_strides[1], e.o_ss = (int)o_strides[2];
+        e.mask = nullptr;
+        e.Sq = Sq;
+        e.Sk = Sk;
+        e.H = H;
+        e.BH = B * H;
+        e.nqb = (Sq + fa::ext::kQueryBlock - 1) / fa::ext::kQueryBlock;
+        e.scale_log2e = (float)((double)scale * 1.4426950408889634074);
+        e.drop_t = 0;
+        e.keep_scale = 1.0f;
+        const hipError_t err = fa::ext::launch_ext(e, D, dtype, causal != 0, (hipStream_t)stream);
+        return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+    }
+
     fa::FwdParams p;
     p.q = q;
     p.k = k;
@@ -197,7 +225,7 @@ struct NaiveLayout {
 };
 
 bool naive_layout(int B, int H, int S, int D, NaiveLayout& L) {
-    if (validate_shape(B, H, S, S, D, FA_F16) != FA_OK) return false;
+    if (validate_shape(B, H, S, S, D, FA_F16) != FA_OK || D == 256) return false;
     const int64_t Sp = (S + 63) / 64 * 64;
     if (Sp > 16384 || (int64_t)B * H > 65535) return false;
     if (S * Sp * 4 >= (int64_t(1) << 31)) return false;
@@ -223,6 +251,7 @@ int fa_naive_fwd(const void* q, const void* k, const void* v, void* o, float* ls
     if (!q || !k || !v || !o || !workspace) return FA_ERR_NULL;
     int st = validate_shape(B, H, S, S, D, dtype);
     if (st != FA_OK) return st;
+    if (D == 256) return FA_ERR_UNSUPPORTED;
     NaiveLayout L;
     if (!naive_layout(B, H, S, D, L) || workspace_bytes < L.total) return FA_ERR_SHAPE;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse |
@@ -323,12 +352,17 @@ int fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
     }
     if (lse && overlap(out[0][0], out[0][1], out[1][0], out[1][1])) return FA_ERR_ALIAS;
 
-    fa::ext::ExtParams p;
+    fa::ext::ExtParams p = {};
     p.q = q;
     p.k = k;
     p.v = v;
     p.o = o;
     p.lse = lse;
+    p.q_sb = p.o_sb = (int64_t)H * Sq * D;
+    p.q_sh = p.o_sh = (int64_t)Sq * D;
+    p.k_sb = p.v_sb = (int64_t)H * Sk * D;
+    p.k_sh = p.v_sh = (int64_t)Sk * D;
+    p.q_ss = p.k_ss = p.v_ss = p.o_ss = D;
     p.mask = mask;
     p.m_sb = mask ? mask_strides[0] : 0;
     p.m_sh = mask ? mask_strides[1] : 0;
@@ -360,6 +394,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
     int st = validate_shape(B, H, Sq, Sk, D, dtype);
     if (st != FA_OK) return st;
+    if (D == 256) return FA_ERR_UNSUPPORTED;
     if (!bwd_span_ok(std::max(Sq, Sk), D)) return FA_ERR_SHAPE;
     BwdLayout L;
     if (!bwd_layout(B, H, Sq, D, deterministic, L) || workspace_bytes < L.total) return FA_ERR_SHAPE;

@@ -8,11 +8,13 @@ namespace fa {
 namespace ext {
 
 struct ExtParams {
-    const void* q;          // [BH, Sq, D] contiguous
-    const void* k;          // [BH, Sk, D]
-    const void* v;          // [BH, Sk, D]
-    void* o;                // [BH, Sq, D]
-    float* lse;             // [BH, Sq] or null
+    const void* q;          // [B, H, Sq, D] with the element strides below (head dimension contiguous)
+    const void* k;          // [B, H, Sk, D]
+    const void* v;          // [B, H, Sk, D]
+    void* o;                // [B, H, Sq, D]
+    float* lse;             // [B*H, Sq] contiguous, or null
+    int64_t q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;   // batch and head strides
+    int q_ss, k_ss, v_ss, o_ss;                                 // row strides
     const uint8_t* mask;    // nonzero = keep; null = no mask
     int64_t m_sb, m_sh, m_ss;  // mask strides in bytes (batch, head, row); multiples of 4
     int Sq, Sk, H, BH, nqb;
@@ -23,7 +25,9 @@ struct ExtParams {
 };
 
 constexpr int kQueryBlock = 128;   // queries per workgroup (32 per wave)
-constexpr int kKeyTile = 64;       // keys per K/V tile
+// keys per K/V tile: 64, or 32 at D = 256 (the staged tile and its LDS
+// double buffer stay at 32 KiB and 64 KiB)
+constexpr int key_tile(int D) { return D == 256 ? 32 : 64; }
 
 hipError_t launch_ext(const ExtParams& p, int D, int dtype, int causal, hipStream_t stream);
 

@@ -19,8 +19,10 @@
 // Layout (the helpers and operand conventions are in fa_tile.h): a workgroup
 // of 4 waves owns 128 query rows, 32 per wave, with Q resident in registers
 // as the B operand of S^T = K Q^T (keys on MFMA rows, queries on columns, so
-// a lane holds one query and 32 keys of a tile).  64-key tiles of K and V
-// stream through LDS, double-buffered and staged through registers.  Per
+// a lane holds one query and 32 keys of a 64-key tile).  Tiles of K and V (64
+// keys, 32 at D = 256) stream through LDS, double-buffered and staged through
+// registers.  Q, K, V and O take batch, head and row strides (head dimension
+// contiguous); this kernel also serves the plain forward at D = 256.  Per
 // tile: mask bytes (one dword per four keys) are loaded before the MFMAs, the
 // online softmax runs in fp32 on the accumulators, the dropout decisions are
 // drawn, and O^T += V^T P^T takes P straight from the accumulators with V^T
@@ -62,7 +64,9 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32
 template <int D, int DT, bool CAUSAL, bool MASK, bool DROP>
 __global__ __launch_bounds__(256) void fwd_ext(ExtParams p) {
     constexpr int DC = D / 16, DB = D / 32;
-    constexpr int KT = kKeyTile;
+    constexpr int KT = key_tile(D);
+    constexpr int RB = KT / 32;                        // 32-key row blocks of S^T per tile
+    constexpr int ST = KT / 16;                        // 16-key k-steps of P V per tile
     constexpr int TILE = KT * D * 2;
     constexpr int CPT = KT * D / 8 / 256;
     static_assert(CPT >= 1, "tile must split over the threads");
@@ -78,15 +82,21 @@ __global__ __launch_bounds__(256) void fwd_ext(ExtParams p) {
     const int q0 = qb * kQueryBlock, qw0 = q0 + 32 * w;
     const int qi = qw0 + lq;
 
-    const __amdgpu_buffer_rsrc_t rq = rsrc((const char*)p.q + (int64_t)bh * Sq * D * 2, (uint64_t)Sq * D * 2);
-    const __amdgpu_buffer_rsrc_t rk = rsrc((const char*)p.k + (int64_t)bh * Sk * D * 2, (uint64_t)Sk * D * 2);
-    const __amdgpu_buffer_rsrc_t rv = rsrc((const char*)p.v + (int64_t)bh * Sk * D * 2, (uint64_t)Sk * D * 2);
+    // One buffer per tensor and head, its record count the head's extent:
+    // rows past the sequence read as zero and stores to them are dropped.
+    const int b_ = bh / p.H, h_ = bh - b_ * p.H;
+    auto head = [&](const void* base, int64_t sb, int64_t sh, int ss, int rows) {
+        return rsrc((const char*)base + ((int64_t)b_ * sb + (int64_t)h_ * sh) * 2,
+                    (uint64_t)(((int64_t)(rows - 1) * ss + D) * 2));
+    };
+    const __amdgpu_buffer_rsrc_t rq = head(p.q, p.q_sb, p.q_sh, p.q_ss, Sq);
+    const __amdgpu_buffer_rsrc_t rk = head(p.k, p.k_sb, p.k_sh, p.k_ss, Sk);
+    const __amdgpu_buffer_rsrc_t rv = head(p.v, p.v_sb, p.v_sh, p.v_ss, Sk);
 
     // Mask rows of this head: a buffer over [first row, last row + Sk)
     // rounded up to whole dwords; offsets beyond it read as zero (hidden).
     __amdgpu_buffer_rsrc_t rm = rq;
     if constexpr (MASK) {
-        const int b_ = bh / p.H, h_ = bh - b_ * p.H;
         const uint8_t* mb = p.mask + (int64_t)b_ * p.m_sb + (int64_t)h_ * p.m_sh;
         rm = rsrc(mb, (uint64_t)(((int64_t)(Sq - 1) * p.m_ss + Sk + 3) & ~(int64_t)3));
     }
@@ -94,7 +104,7 @@ __global__ __launch_bounds__(256) void fwd_ext(ExtParams p) {
     i32x4 qf[DC];
 #pragma unroll
     for (int c = 0; c < DC; ++c)
-        qf[c] = __builtin_amdgcn_raw_buffer_load_b128(rq, (qi * D + 16 * c + 8 * g) * 2, 0, 0);
+        qf[c] = __builtin_amdgcn_raw_buffer_load_b128(rq, (qi * p.q_ss + 16 * c + 8 * g) * 2, 0, 0);
 
     int nkt = (Sk + KT - 1) / KT;
     if (CAUSAL) nkt = min(nkt, max(0, (min(Sq, q0 + kQueryBlock) + diag + KT - 1) / KT));
@@ -105,8 +115,8 @@ __global__ __launch_bounds__(256) void fwd_ext(ExtParams p) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int ci = tid + 256 * i, r = ci / (D / 8), ch = ci % (D / 8);
-            sk[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((k0 + r) * D + 8 * ch) * 2, 0, 0);
-            sv[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((k0 + r) * D + 8 * ch) * 2, 0, 0);
+            sk[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((k0 + r) * p.k_ss + 8 * ch) * 2, 0, 0);
+            sv[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((k0 + r) * p.v_ss + 8 * ch) * 2, 0, 0);
         }
     };
     auto commit = [&](int buf) {
@@ -141,30 +151,30 @@ __global__ __launch_bounds__(256) void fwd_ext(ExtParams p) {
         const int kt0 = t * KT;
 
         // mask bytes of keys kt0 + 32rb + 8a + 4g .. +3 for this lane's query
-        uint32_t mk[2][4];
+        uint32_t mk[RB][4];
         if constexpr (MASK) {
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
+            for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                 for (int a = 0; a < 4; ++a)
                     mk[rb][a] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
                         rm, (uint32_t)((int64_t)qi * p.m_ss + kt0 + 32 * rb + 8 * a + 4 * g), 0, 0);
         }
 
-        // S^T = K Q^T: 64 keys x this wave's 32 queries
-        f32x16 s[2];
+        // S^T = K Q^T: KT keys x this wave's 32 queries
+        f32x16 s[RB];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) s[rb] = zero16();
+        for (int rb = 0; rb < RB; ++rb) s[rb] = zero16();
 #pragma unroll
         for (int c = 0; c < DC; ++c)
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
+            for (int rb = 0; rb < RB; ++rb)
                 s[rb] = mma<DT>(row_frag<D>(tk, 32 * rb + lq, 2 * c + g), qf[c], s[rb]);
 
         const bool need_mask = MASK || (kt0 + KT > Sk) || (CAUSAL && kt0 + KT - 1 > qw0 + diag);
         if (need_mask) {
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
+            for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int kj = kt0 + 32 * rb + 8 * (r >> 2) + 4 * g + (r & 3);
@@ -177,7 +187,7 @@ __global__ __launch_bounds__(256) void fwd_ext(ExtParams p) {
         // online softmax (base 2, scale*log2(e) folded into one FMA)
         float mx = s[0][0];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[rb][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
@@ -187,7 +197,7 @@ __global__ __launch_bounds__(256) void fwd_ext(ExtParams p) {
         m_run = m_new;
         float lsum = 0.0f;
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][r], c2, -mb));
@@ -206,7 +216,7 @@ __global__ __launch_bounds__(256) void fwd_ext(ExtParams p) {
             // keys kt0 + 32rb + 8a + 0..7 share one Philox call; this lane
             // uses words 2g and 2g+1 (keys 8a + 4g + 0..3)
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
+            for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
                     uint32_t c[4] = {(uint32_t)((kt0 + 32 * rb + 8 * a) >> 3), (uint32_t)qi, (uint32_t)bh,
@@ -223,7 +233,7 @@ __global__ __launch_bounds__(256) void fwd_ext(ExtParams p) {
 
         // O^T += V^T P^T
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
+        for (int st = 0; st < ST; ++st) {
             const i32x4 pa = acc_frag<DT>(s[st >> 1], st & 1);
 #pragma unroll
             for (int b = 0; b < DB; ++b) oa[b] = mma<DT>(tr_frag<D>(tv, st, b, tl), pa, oa[b]);
@@ -237,7 +247,7 @@ __global__ __launch_bounds__(256) void fwd_ext(ExtParams p) {
     // head-dimension index 32b + 8(r/4) + 4g + r%4 of query qi.
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = l_tot > 0.0f ? p.keep_scale / l_tot : 0.0f;
-    const __amdgpu_buffer_rsrc_t wo = rsrc((char*)p.o + (int64_t)bh * Sq * D * 2, (uint64_t)Sq * D * 2);
+    const __amdgpu_buffer_rsrc_t wo = head(p.o, p.o_sb, p.o_sh, p.o_ss, Sq);
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
 #pragma unroll
@@ -245,7 +255,7 @@ __global__ __launch_bounds__(256) void fwd_ext(ExtParams p) {
             i32x2 v2;
             v2[0] = pack2<DT>(oa[b][4 * a] * inv, oa[b][4 * a + 1] * inv);
             v2[1] = pack2<DT>(oa[b][4 * a + 2] * inv, oa[b][4 * a + 3] * inv);
-            __builtin_amdgcn_raw_buffer_store_b64(v2, wo, (uint32_t)((qi * D + 32 * b + 8 * a + 4 * g) * 2), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(v2, wo, (uint32_t)((qi * p.o_ss + 32 * b + 8 * a + 4 * g) * 2), 0, 0);
         }
     }
     if (p.lse != nullptr && g == 0 && qi < Sq) {
@@ -266,6 +276,10 @@ static hipError_t run(const ExtParams& p, hipStream_t st) {
 }
 
 hipError_t launch_ext(const ExtParams& p, int D, int dtype, int causal, hipStream_t stream) {
+    if (D == 256) {
+        if (dtype == 0) return causal ? run<256, 0, true>(p, stream) : run<256, 0, false>(p, stream);
+        return causal ? run<256, 1, true>(p, stream) : run<256, 1, false>(p, stream);
+    }
     if (D == 64) {
         if (dtype == 0) return causal ? run<64, 0, true>(p, stream) : run<64, 0, false>(p, stream);
         return causal ? run<64, 1, true>(p, stream) : run<64, 1, false>(p, stream);

@@ -72,7 +72,7 @@ __device__ __forceinline__ f32x16 zero16() {
     return z;
 }
 
-// LDS tiles are [rows][W] 16-bit values (W = 64 or 128), stored in 16-byte
+// LDS tiles are [rows][W] 16-bit values (W = 64, 128 or 256), stored in 16-byte
 // chunks whose index within the row is XOR-ed with swz(row).  A fragment
 // read (16 lanes on 16 consecutive rows, one chunk each) and a transposing
 // read (16 lanes on four consecutive rows, two adjacent chunks each) both
@@ -80,7 +80,7 @@ __device__ __forceinline__ f32x16 zero16() {
 template <int W>
 __device__ __forceinline__ int swz(int r) {
     const int f = ((r & 3) << 1) | ((r >> 2) & 1);
-    if constexpr (W == 128)
+    if constexpr (W >= 128)
         return f | (((r >> 3) & 1) << 3);
     else
         return f;

@@ -63,6 +63,11 @@ WORKLOADS = {
         Workload("long_causal_1x32x8192x128_bf16_q4", 1, 32, 8192, 128, "bf16", True, 4.0, 4),
     "13b_causal_1x40x16384x128_bf16":
         Workload("13b_causal_1x40x16384x128_bf16", 1, 40, 16384, 128, "bf16", True, 1.0, 5),
+    # Not one of the five: head dimension 256, which the 2048ai.net page names
+    # among the common head dimensions its block size suits (section 3.2);
+    # same flops as the long causal case.
+    "d256_causal_1x16x8192x256_bf16":
+        Workload("d256_causal_1x16x8192x256_bf16", 1, 16, 8192, 256, "bf16", True, 1.0, 6),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 HEADLINE = "long_causal_1x32x8192x128_bf16_q4"
