@@ -15,6 +15,14 @@ SOURCES = [os.path.join(CSRC, "fa_api.cpp"), os.path.join(CSRC, "fa_fwd_kernel.h
            os.path.join(CSRC, "fa_naive.hip"), os.path.join(CSRC, "fa_bwd.hip"),
            os.path.join(CSRC, "fa_fwd_ext.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# Kernels whose MFMA accumulators are also worked on by vector instructions:
+# the VGPR form of the MFMA instructions keeps those accumulators in VGPRs
+# instead of AGPRs, which removes the AGPR<->VGPR copies the compiler
+# otherwise inserts around every softmax step (and lowers register use).
+PER_SOURCE_FLAGS = {
+    "fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "fa_fwd_ext.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 ARCH = "gfx950"
 
 
@@ -33,7 +41,8 @@ def build(out=LIB, extra=(), verbose=False):
     for src in SOURCES:
         obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [HIPCC, *hipcc_flags(extra), *lang, "-c", src, "-o", obj]
+        per = PER_SOURCE_FLAGS.get(os.path.basename(src), [])
+        cmd = [HIPCC, *hipcc_flags(extra), *per, *lang, "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd))
         r = subprocess.run(cmd, capture_output=True, text=True)
