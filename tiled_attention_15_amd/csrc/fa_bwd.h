@@ -26,7 +26,7 @@ struct BwdParams {
 };
 
 constexpr int kKeyBlock = 128;   // keys per dK/dV workgroup (32 per wave)
-constexpr int kQueryTile = 64;   // queries per step of the dK/dV kernel
+constexpr int kQueryTile = 32;   // queries per step of the dK/dV kernel
 constexpr int kQueryBlock = 128; // queries per dQ workgroup (32 per wave)
 constexpr int kKeyTile = 64;     // keys per step of the dQ kernel
 

@@ -92,19 +92,23 @@ __global__ __launch_bounds__(256) void bwd_dq_convert(BwdParams p, int64_t n8) {
 
 // ---------------------------------------------------------------------------
 // dK, dV (and in atomic mode the dQ contributions) of one 128-key block.
+// Sized for two workgroups per CU (two waves per SIMD, <= 256 registers per
+// lane): the key block sits in LDS (K fragments are read from there at each
+// use) while V's fragments and the dK^T, dV^T accumulators stay in registers;
+// 32-query tiles of Q and dO go straight from global memory into LDS.
 template <int D, int DT, bool CAUSAL, bool ATOMIC>
-__global__ __launch_bounds__(256) void bwd_dkdv(BwdParams p) {
+__global__ __launch_bounds__(256, ATOMIC ? 1 : 2) void bwd_dkdv(BwdParams p) {
     constexpr int DC = D / 16;                         // k-steps over the head dimension
     constexpr int DB = D / 32;                         // 32-column blocks of the head dimension
     constexpr int QT = kQueryTile;
     constexpr int TILE = QT * D * 2;                   // bytes of one Q or dO tile
-    constexpr int CPT = QT * D / 8 / 256;              // 16-byte chunks per thread per tile
-    constexpr int KBLK = ATOMIC ? kKeyBlock * D * 2 : 0;
+    constexpr int TN = QT * D / 8 / 256;               // direct loads per thread per tile
+    constexpr int KBLK = kKeyBlock * D * 2;            // bytes of the key block
+    constexpr int KN = kKeyBlock * D / 8 / 256;        // direct loads per thread for it
     constexpr int DSB = ATOMIC ? kKeyBlock * QT * 2 : 0;
-    constexpr int KCPT = kKeyBlock * D / 8 / 256;
-    static_assert(CPT >= 1 && KCPT >= 1, "tile must split over the threads");
+    static_assert(TN >= 1 && KN >= 1, "tile must split over the threads");
 
-    __shared__ __attribute__((aligned(16))) char smem[4 * TILE + KBLK + DSB];
+    __shared__ __attribute__((aligned(16))) char smem[KBLK + 4 * TILE + DSB];
     __shared__ __attribute__((aligned(16))) float lse_s[2][QT];
     __shared__ __attribute__((aligned(16))) float dv_s[2][QT];
     lds_t* const sm = (lds_t*)smem;
@@ -118,63 +122,43 @@ __global__ __launch_bounds__(256) void bwd_dkdv(BwdParams p) {
 
     const char* qh = (const char*)p.q + (int64_t)bh * Sq * D * 2;
     const char* doh = (const char*)p.dout + (int64_t)bh * Sq * D * 2;
-    const __amdgpu_buffer_rsrc_t rq = rsrc(qh, (uint64_t)Sq * D * 2);
-    const __amdgpu_buffer_rsrc_t rdo = rsrc(doh, (uint64_t)Sq * D * 2);
-    const __amdgpu_buffer_rsrc_t rk = rsrc((const char*)p.k + (int64_t)bh * Sk * D * 2, (uint64_t)Sk * D * 2);
+    const char* kh = (const char*)p.k + (int64_t)bh * Sk * D * 2;
+    const i32x4 rq = rsrc_words(qh, (uint64_t)Sq * D * 2);
+    const i32x4 rdo = rsrc_words(doh, (uint64_t)Sq * D * 2);
+    const i32x4 rk = rsrc_words(kh, (uint64_t)Sk * D * 2);
     const __amdgpu_buffer_rsrc_t rv = rsrc((const char*)p.v + (int64_t)bh * Sk * D * 2, (uint64_t)Sk * D * 2);
     const __amdgpu_buffer_rsrc_t rl = rsrc(p.lse + (int64_t)bh * Sq, (uint64_t)Sq * 4);
     const __amdgpu_buffer_rsrc_t rdv = rsrc(p.dvec + (int64_t)bh * Sq, (uint64_t)Sq * 4);
 
-    // K and V of this wave's 32 keys as B operands (key = column lq, 8 values
-    // of the head dimension per k-step); keys past Sk read as zero.  In
-    // atomic mode the K block is in LDS anyway and its fragments are read
-    // from there at each use, which leaves registers for the dQ product.
-    i32x4 kf[ATOMIC ? 1 : DC], vf[DC];
+    const uint32_t lds0 = (uint32_t)(uintptr_t)sm;
+    const lds_t* kblk = sm;
+    // the key block (keys past Sk read as zero)
+    tile_dma<D, KN>(rk, k0, D, lds0, w, lane);
+    // V of this wave's 32 keys as B operands (key = column lq, 8 values of
+    // the head dimension per k-step)
+    i32x4 vf[DC];
 #pragma unroll
-    for (int c = 0; c < DC; ++c) {
-        if constexpr (!ATOMIC)
-            kf[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((kw0 + lq) * D + 16 * c + 8 * g) * 2, 0, 0);
+    for (int c = 0; c < DC; ++c)
         vf[c] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((kw0 + lq) * D + 16 * c + 8 * g) * 2, 0, 0);
-    }
-    if constexpr (ATOMIC) {
-        // the whole key block in LDS, for the dQ product
-#pragma unroll
-        for (int i = 0; i < KCPT; ++i) {
-            const int ci = tid + 256 * i, r = ci / (D / 8), ch = ci % (D / 8);
-            const i32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rk, ((k0 + r) * D + 8 * ch) * 2, 0, 0);
-            *(__attribute__((address_space(3))) i32x4*)(sm + 4 * TILE + toff<D>(r, ch)) = x;
-        }
-    }
 
-    const lds_t* kblk = sm + 4 * TILE;
     const int nqt = (Sq + QT - 1) / QT;
     int t0 = 0;
     if (CAUSAL) t0 = max(0, k0 - diag) / QT;
 
-    // Staging of the next query tile in registers.
-    i32x4 sq[CPT], sd[CPT];
-    float sl = 0.0f;
-    auto fetch = [&](int t) {
-        const int q0 = t * QT;
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int ci = tid + 256 * i, r = ci / (D / 8), ch = ci % (D / 8);
-            sq[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, ((q0 + r) * D + 8 * ch) * 2, 0, 0);
-            sd[i] = __builtin_amdgcn_raw_buffer_load_b128(rdo, ((q0 + r) * D + 8 * ch) * 2, 0, 0);
-        }
-        if (tid < QT)
-            sl = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, (q0 + tid) * 4, 0, 0));
-        else if (tid < 2 * QT)
-            sl = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdv, (q0 + tid - QT) * 4, 0, 0));
+    auto issue = [&](int t, int buf) {
+        const uint32_t base = lds0 + (uint32_t)(KBLK + buf * 2 * TILE);
+        tile_dma<D, TN>(rq, t * QT, D, base, w, lane);
+        tile_dma<D, TN>(rdo, t * QT, D, base + TILE, w, lane);
     };
-    auto commit = [&](int buf) {
-        lds_t* tq = sm + buf * 2 * TILE;
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int ci = tid + 256 * i, r = ci / (D / 8), ch = ci % (D / 8);
-            *(__attribute__((address_space(3))) i32x4*)(tq + toff<D>(r, ch)) = sq[i];
-            *(__attribute__((address_space(3))) i32x4*)(tq + TILE + toff<D>(r, ch)) = sd[i];
-        }
+    // lse (times log2 e) and D_i of a tile: threads 0..QT-1 and QT..2QT-1
+    float sl = 0.0f;
+    auto fetch_stats = [&](int t) {
+        if (tid < QT)
+            sl = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, (t * QT + tid) * 4, 0, 0));
+        else if (tid < 2 * QT)
+            sl = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdv, (t * QT + tid - QT) * 4, 0, 0));
+    };
+    auto store_stats = [&](int buf) {
         if (tid < QT)
             lse_s[buf][tid] = sl * LOG2E;
         else if (tid < 2 * QT)
@@ -192,68 +176,58 @@ __global__ __launch_bounds__(256) void bwd_dkdv(BwdParams p) {
     }
 
     if (t0 < nqt) {
-        fetch(t0);
-        commit(0);
+        issue(t0, 0);
+        fetch_stats(t0);
     }
+    wait_vmcnt<0>();
+    if (t0 < nqt) store_stats(0);
     __syncthreads();
 
     for (int t = t0; t < nqt; ++t) {
         const int buf = (t - t0) & 1;
-        if (t + 1 < nqt) fetch(t + 1);
-        const lds_t* tq = sm + buf * 2 * TILE;
+        if (t + 1 < nqt) {
+            issue(t + 1, buf ^ 1);
+            fetch_stats(t + 1);
+        }
+        const lds_t* tq = sm + KBLK + buf * 2 * TILE;
         const lds_t* tdo = tq + TILE;
         const int q0 = t * QT;
 
-        // S = Q K^T and dP = dO V^T for 64 queries x this wave's 32 keys
-        f32x16 s[2], dp[2];
+        // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
+        f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            s[rb] = zero16();
-            dp[rb] = zero16();
-        }
+        for (int c = 0; c < DC; ++c)
+            s = mma<DT>(row_frag<D>(tq, lq, 2 * c + g), row_frag<D>(kblk, 32 * w + lq, 2 * c + g), s);
 #pragma unroll
-        for (int c = 0; c < DC; ++c) {
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                i32x4 kc;
-                if constexpr (ATOMIC)
-                    kc = row_frag<D>(kblk, 32 * w + lq, 2 * c + g);
-                else
-                    kc = kf[c];
-                s[rb] = mma<DT>(row_frag<D>(tq, 32 * rb + lq, 2 * c + g), kc, s[rb]);
-                dp[rb] = mma<DT>(row_frag<D>(tdo, 32 * rb + lq, 2 * c + g), vf[c], dp[rb]);
-            }
-        }
+        for (int c = 0; c < DC; ++c)
+            dp = mma<DT>(row_frag<D>(tdo, lq, 2 * c + g), vf[c], dp);
 
         // P = exp2(s * scale*log2e - lse*log2e), dS = P (dP - D_i)
         const bool need_mask = (q0 + QT > Sq) || (kw0 + 32 > Sk) || (CAUSAL && kw0 + 31 > q0 + diag);
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        for (int a = 0; a < 4; ++a) {
+            const int qr = 8 * a + 4 * g;
+            const f32x4 l4 = *(const f32x4*)&lse_s[buf][qr];
+            const f32x4 d4 = *(const f32x4*)&dv_s[buf][qr];
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const int qr = 32 * rb + 8 * a + 4 * g;
-                const f32x4 l4 = *(const f32x4*)&lse_s[buf][qr];
-                const f32x4 d4 = *(const f32x4*)&dv_s[buf][qr];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * a + e;
-                    float pv = __builtin_amdgcn_exp2f(s[rb][r] * c2 - l4[e]);
-                    if (need_mask) {
-                        const int qi = q0 + qr + e;
-                        const bool vis = qi < Sq && key < Sk && (!CAUSAL || key <= qi + diag);
-                        pv = vis ? pv : 0.0f;
-                    }
-                    s[rb][r] = pv;
-                    dp[rb][r] = pv * (dp[rb][r] - d4[e]);
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * a + e;
+                float pv = __builtin_amdgcn_exp2f(s[r] * c2 - l4[e]);
+                if (need_mask) {
+                    const int qi = q0 + qr + e;
+                    const bool vis = qi < Sq && key < Sk && (!CAUSAL || key <= qi + diag);
+                    pv = vis ? pv : 0.0f;
                 }
+                s[r] = pv;
+                dp[r] = pv * (dp[r] - d4[e]);
             }
         }
 
         // dV^T += dO^T P, dK^T += Q^T dS  (rows: head dimension, columns: keys)
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const i32x4 pa = acc_frag<DT>(s[st >> 1], st & 1);
-            const i32x4 da = acc_frag<DT>(dp[st >> 1], st & 1);
+        for (int st = 0; st < QT / 16; ++st) {
+            const i32x4 pa = acc_frag<DT>(s, st);
+            const i32x4 da = acc_frag<DT>(dp, st);
 #pragma unroll
             for (int b = 0; b < DB; ++b) {
                 dva[b] = mma<DT>(tr_frag<D>(tdo, st, b, tl), pa, dva[b]);
@@ -263,39 +237,33 @@ __global__ __launch_bounds__(256) void bwd_dkdv(BwdParams p) {
 
         if constexpr (ATOMIC) {
             // dS^T of this wave's keys into LDS as [key][query], then
-            // dQ[q][d] += sum over the block's 128 keys of dS[q][key] K[key][d].
-            lds_t* dst = sm + 4 * TILE + KBLK;
+            // dQ[q][d] += sum over the block's 128 keys of dS[q][key] K[key][d]
+            lds_t* dst = sm + KBLK + 4 * TILE;
             const int kr = 32 * w + lq;
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    i32x2 v2;
-                    v2[0] = pack2<DT>(dp[rb][4 * a], dp[rb][4 * a + 1]);
-                    v2[1] = pack2<DT>(dp[rb][4 * a + 2], dp[rb][4 * a + 3]);
-                    *(__attribute__((address_space(3))) i32x2*)(dst + toff<QT>(kr, 4 * rb + a) + 8 * g) = v2;
-                }
+            for (int a = 0; a < 4; ++a) {
+                i32x2 v2;
+                v2[0] = pack2<DT>(dp[4 * a], dp[4 * a + 1]);
+                v2[1] = pack2<DT>(dp[4 * a + 2], dp[4 * a + 3]);
+                *(__attribute__((address_space(3))) i32x2*)(dst + toff<QT>(kr, a) + 8 * g) = v2;
             }
             __syncthreads();
-            constexpr int NBLK = 2 * DB / 4;           // 32x32 output blocks per wave
-#pragma unroll
-            for (int ob = 0; ob < NBLK; ++ob) {
-                const int id = w * NBLK + ob;
-                const int rbq = id & 1, db = id >> 1;
+            for (int db = w; db < DB; db += 4) {
                 f32x16 acc = zero16();
 #pragma unroll
                 for (int st = 0; st < kKeyBlock / 16; ++st)
-                    acc = mma<DT>(tr_frag<QT>(dst, st, rbq, tl), tr_frag<D>(kblk, st, db, tl), acc);
+                    acc = mma<DT>(tr_frag<QT>(dst, st, 0, tl), tr_frag<D>(kblk, st, db, tl), acc);
                 float* base = p.dqacc + ((int64_t)bh * Sq) * D + 32 * db + lq;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int qi = q0 + 32 * rbq + 8 * (r >> 2) + 4 * g + (r & 3);
+                    const int qi = q0 + 8 * (r >> 2) + 4 * g + (r & 3);
                     if (qi < Sq) unsafeAtomicAdd(base + (int64_t)qi * D, acc[r]);
                 }
             }
         }
 
-        if (t + 1 < nqt) commit(buf ^ 1);
+        wait_vmcnt<0>();
+        if (t + 1 < nqt) store_stats(buf ^ 1);
         __syncthreads();
     }
 
@@ -324,7 +292,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dQ of one 128-query block (deterministic mode).
 template <int D, int DT, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dq(BwdParams p) {
+__global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
     constexpr int DC = D / 16, DB = D / 32;
     constexpr int KT = kKeyTile;
     constexpr int TILE = KT * D * 2;
@@ -344,8 +312,8 @@ __global__ __launch_bounds__(256) void bwd_dq(BwdParams p) {
 
     const __amdgpu_buffer_rsrc_t rq = rsrc((const char*)p.q + (int64_t)bh * Sq * D * 2, (uint64_t)Sq * D * 2);
     const __amdgpu_buffer_rsrc_t rdo = rsrc((const char*)p.dout + (int64_t)bh * Sq * D * 2, (uint64_t)Sq * D * 2);
-    const __amdgpu_buffer_rsrc_t rk = rsrc((const char*)p.k + (int64_t)bh * Sk * D * 2, (uint64_t)Sk * D * 2);
-    const __amdgpu_buffer_rsrc_t rv = rsrc((const char*)p.v + (int64_t)bh * Sk * D * 2, (uint64_t)Sk * D * 2);
+    const i32x4 rk = rsrc_words((const char*)p.k + (int64_t)bh * Sk * D * 2, (uint64_t)Sk * D * 2);
+    const i32x4 rv = rsrc_words((const char*)p.v + (int64_t)bh * Sk * D * 2, (uint64_t)Sk * D * 2);
     const __amdgpu_buffer_rsrc_t rl = rsrc(p.lse + (int64_t)bh * Sq, (uint64_t)Sq * 4);
     const __amdgpu_buffer_rsrc_t rdv = rsrc(p.dvec + (int64_t)bh * Sq, (uint64_t)Sq * 4);
 
@@ -362,24 +330,14 @@ __global__ __launch_bounds__(256) void bwd_dq(BwdParams p) {
     int nkt = (Sk + KT - 1) / KT;
     if (CAUSAL) nkt = min(nkt, max(0, (min(Sq, q0 + kQueryBlock) + diag + KT - 1) / KT));
 
-    i32x4 sk[CPT], sv[CPT];
-    auto fetch = [&](int t) {
-        const int k0 = t * KT;
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int ci = tid + 256 * i, r = ci / (D / 8), ch = ci % (D / 8);
-            sk[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((k0 + r) * D + 8 * ch) * 2, 0, 0);
-            sv[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((k0 + r) * D + 8 * ch) * 2, 0, 0);
-        }
-    };
-    auto commit = [&](int buf) {
-        lds_t* tk = sm + buf * 2 * TILE;
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int ci = tid + 256 * i, r = ci / (D / 8), ch = ci % (D / 8);
-            *(__attribute__((address_space(3))) i32x4*)(tk + toff<D>(r, ch)) = sk[i];
-            *(__attribute__((address_space(3))) i32x4*)(tk + TILE + toff<D>(r, ch)) = sv[i];
-        }
+    // K and V tiles go straight from global memory into the LDS buffers
+    // (no staging registers); a step waits for its successor's loads just
+    // before the closing barrier.
+    const uint32_t lds0 = (uint32_t)(uintptr_t)sm;
+    auto issue = [&](int t, int buf) {
+        const uint32_t base = lds0 + (uint32_t)(buf * 2 * TILE);
+        tile_dma<D, CPT>(rk, t * KT, D, base, w, lane);
+        tile_dma<D, CPT>(rv, t * KT, D, base + TILE, w, lane);
     };
 
     const TrLane tl = tr_lane(lane);
@@ -388,15 +346,13 @@ __global__ __launch_bounds__(256) void bwd_dq(BwdParams p) {
 #pragma unroll
     for (int b = 0; b < DB; ++b) dqa[b] = zero16();
 
-    if (nkt > 0) {
-        fetch(0);
-        commit(0);
-    }
+    if (nkt > 0) issue(0, 0);
+    wait_vmcnt<0>();
     __syncthreads();
 
     for (int t = 0; t < nkt; ++t) {
         const int buf = t & 1;
-        if (t + 1 < nkt) fetch(t + 1);
+        if (t + 1 < nkt) issue(t + 1, buf ^ 1);
         const lds_t* tk = sm + buf * 2 * TILE;
         const lds_t* tv = tk + TILE;
         const int kt0 = t * KT;
@@ -440,7 +396,7 @@ __global__ __launch_bounds__(256) void bwd_dq(BwdParams p) {
             for (int b = 0; b < DB; ++b) dqa[b] = mma<DT>(tr_frag<D>(tk, st, b, tl), da, dqa[b]);
         }
 
-        if (t + 1 < nkt) commit(buf ^ 1);
+        wait_vmcnt<0>();
         __syncthreads();
     }
 

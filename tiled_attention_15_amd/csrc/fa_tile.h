@@ -72,13 +72,16 @@ __device__ __forceinline__ f32x16 zero16() {
     return z;
 }
 
-// LDS tiles are [rows][W] 16-bit values (W = 64, 128 or 256), stored in 16-byte
+// LDS tiles are [rows][W] 16-bit values (W = 32, 64, 128 or 256), stored in 16-byte
 // chunks whose index within the row is XOR-ed with swz(row).  A fragment
 // read (16 lanes on 16 consecutive rows, one chunk each) and a transposing
 // read (16 lanes on four consecutive rows, two adjacent chunks each) both
 // fall on distinct chunk positions.
 template <int W>
 __device__ __forceinline__ int swz(int r) {
+    // 64-byte rows (W = 32): four consecutive rows of a transposing read
+    // already fall on distinct banks, and there are only four chunks
+    if constexpr (W == 32) return 0;
     const int f = ((r & 3) << 1) | ((r >> 2) & 1);
     if constexpr (W >= 128)
         return f | (((r >> 3) & 1) << 3);
@@ -149,6 +152,53 @@ __device__ __forceinline__ void block_order(int wg, int nblk, int BH, bool rever
         slot = wg / BH;
     }
     blk = reverse ? (nblk - 1 - slot) : slot;
+}
+
+// Direct global->LDS load of 16 bytes per lane: lane l's 16 bytes at byte
+// offset `voffset` of the buffer go to LDS address lds_addr + 16*l
+// (lds_addr wave-uniform).  Written as inline assembly (it sets M0, which
+// nothing else in these kernels uses); the compiler does not see it, so the
+// caller waits for it with wait_vmcnt before the barrier that publishes the
+// tile.
+__device__ __forceinline__ void lds_dma16(i32x4 rsrc_words, uint32_t voffset, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voffset), "s"(rsrc_words), "s"(lds_addr) : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Buffer descriptor as four wave-uniform dwords (for the inline assembly):
+// base, stride 0, `bytes` records, raw 32-bit format.
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint64_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffff));
+    r[2] = __builtin_amdgcn_readfirstlane((int)(bytes < 0x80000000ull ? bytes : 0x7fffffffull));
+    r[3] = 0x00020000;
+    return r;
+}
+
+// Direct loads of one [rows][W] 16-bit tile (rows = 256 * N / (W / 8), i.e.
+// N instructions per thread of a 256-thread workgroup) into the swizzled LDS
+// layout of toff(): instruction i of wave w fills LDS chunks
+// (4i + w)*64 + lane, and each lane fetches the global chunk that the swizzle
+// puts there.  row0: first global row; ss: global row stride in elements.
+template <int W, int N>
+__device__ __forceinline__ void tile_dma(i32x4 rw, int row0, int ss, uint32_t lds_tile, int w, int lane) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int c = (4 * i + w) * 64 + lane;
+        const int r = c / (W / 8), pos = c % (W / 8);
+        const int ch = pos ^ swz<W>(r);
+        lds_dma16(rw, (uint32_t)(((row0 + r) * ss + 8 * ch) * 2), lds_tile + (uint32_t)((4 * i + w) * 1024));
+    }
 }
 
 }  // namespace tile
