@@ -90,8 +90,12 @@ __global__ __launch_bounds__(256) void fwd_ext(ExtParams p) {
                     (uint64_t)(((int64_t)(rows - 1) * ss + D) * 2));
     };
     const __amdgpu_buffer_rsrc_t rq = head(p.q, p.q_sb, p.q_sh, p.q_ss, Sq);
-    const __amdgpu_buffer_rsrc_t rk = head(p.k, p.k_sb, p.k_sh, p.k_ss, Sk);
-    const __amdgpu_buffer_rsrc_t rv = head(p.v, p.v_sb, p.v_sh, p.v_ss, Sk);
+    auto head_words = [&](const void* base, int64_t sb, int64_t sh, int ss, int rows) {
+        return rsrc_words((const char*)base + ((int64_t)b_ * sb + (int64_t)h_ * sh) * 2,
+                          (uint64_t)(((int64_t)(rows - 1) * ss + D) * 2));
+    };
+    const i32x4 rk = head_words(p.k, p.k_sb, p.k_sh, p.k_ss, Sk);
+    const i32x4 rv = head_words(p.v, p.v_sb, p.v_sh, p.v_ss, Sk);
 
     // Mask rows of this head: a buffer over [first row, last row + Sk)
     // rounded up to whole dwords; offsets beyond it read as zero (hidden).
@@ -109,24 +113,26 @@ __global__ __launch_bounds__(256) void fwd_ext(ExtParams p) {
     int nkt = (Sk + KT - 1) / KT;
     if (CAUSAL) nkt = min(nkt, max(0, (min(Sq, q0 + kQueryBlock) + diag + KT - 1) / KT));
 
-    i32x4 sk[CPT], sv[CPT];
-    auto fetch = [&](int t) {
-        const int k0 = t * KT;
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int ci = tid + 256 * i, r = ci / (D / 8), ch = ci % (D / 8);
-            sk[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((k0 + r) * p.k_ss + 8 * ch) * 2, 0, 0);
-            sv[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((k0 + r) * p.v_ss + 8 * ch) * 2, 0, 0);
-        }
+    // K and V tiles go straight from global memory into the LDS buffers; a
+    // step waits for its successor's loads just before the closing barrier.
+    // The compiler does not see these loads, so with a mask they are issued
+    // after the tile's mask bytes (compiler-visible loads) have been used:
+    // its wait for those would otherwise also wait for the tile loads.
+    const uint32_t lds0 = (uint32_t)(uintptr_t)sm;
+    auto issue = [&](int t, int buf) {
+        const uint32_t base = lds0 + (uint32_t)(buf * 2 * TILE);
+        tile_dma<D, CPT>(rk, t * KT, p.k_ss, base, w, lane);
+        tile_dma<D, CPT>(rv, t * KT, p.v_ss, base + TILE, w, lane);
     };
-    auto commit = [&](int buf) {
-        lds_t* tk = sm + buf * 2 * TILE;
+    // mask bytes of keys t*KT + 32rb + 8a + 4g .. +3 for this lane's query
+    uint32_t mk[RB][4];
+    auto load_mask = [&](int t) {
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int ci = tid + 256 * i, r = ci / (D / 8), ch = ci % (D / 8);
-            *(__attribute__((address_space(3))) i32x4*)(tk + toff<D>(r, ch)) = sk[i];
-            *(__attribute__((address_space(3))) i32x4*)(tk + TILE + toff<D>(r, ch)) = sv[i];
-        }
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+                mk[rb][a] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+                    rm, (uint32_t)((int64_t)qi * p.m_ss + t * KT + 32 * rb + 8 * a + 4 * g), 0, 0);
     };
 
     const TrLane tl = tr_lane(lane);
@@ -138,28 +144,19 @@ __global__ __launch_bounds__(256) void fwd_ext(ExtParams p) {
     float l_run = 0.0f;        // this lane's share of the running sum
 
     if (nkt > 0) {
-        fetch(0);
-        commit(0);
+        issue(0, 0);
+        if constexpr (MASK) load_mask(0);
     }
+    wait_vmcnt<0>();
     __syncthreads();
 
     for (int t = 0; t < nkt; ++t) {
         const int buf = t & 1;
-        if (t + 1 < nkt) fetch(t + 1);
+        if constexpr (!MASK)
+            if (t + 1 < nkt) issue(t + 1, buf ^ 1);
         const lds_t* tk = sm + buf * 2 * TILE;
         const lds_t* tv = tk + TILE;
         const int kt0 = t * KT;
-
-        // mask bytes of keys kt0 + 32rb + 8a + 4g .. +3 for this lane's query
-        uint32_t mk[RB][4];
-        if constexpr (MASK) {
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                for (int a = 0; a < 4; ++a)
-                    mk[rb][a] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
-                        rm, (uint32_t)((int64_t)qi * p.m_ss + kt0 + 32 * rb + 8 * a + 4 * g), 0, 0);
-        }
 
         // S^T = K Q^T: KT keys x this wave's 32 queries
         f32x16 s[RB];
@@ -182,6 +179,12 @@ __global__ __launch_bounds__(256) void fwd_ext(ExtParams p) {
                     if constexpr (MASK) vis = vis && ((mk[rb][r >> 2] >> (8 * (r & 3))) & 0xffu) != 0;
                     if (!vis) s[rb][r] = -INFINITY;
                 }
+        }
+        if constexpr (MASK) {
+            if (t + 1 < nkt) {
+                issue(t + 1, buf ^ 1);
+                load_mask(t + 1);
+            }
         }
 
         // online softmax (base 2, scale*log2(e) folded into one FMA)
@@ -239,7 +242,7 @@ __global__ __launch_bounds__(256) void fwd_ext(ExtParams p) {
             for (int b = 0; b < DB; ++b) oa[b] = mma<DT>(tr_frag<D>(tv, st, b, tl), pa, oa[b]);
         }
 
-        if (t + 1 < nkt) commit(buf ^ 1);
+        wait_vmcnt<0>();
         __syncthreads();
     }
 
