@@ -72,21 +72,23 @@ __device__ __forceinline__ f32x16 zero16() {
     return z;
 }
 
-// LDS tiles are [rows][W] 16-bit values (W = 32, 64, 128 or 256), stored in 16-byte
-// chunks whose index within the row is XOR-ed with swz(row).  A fragment
-// read (16 lanes on 16 consecutive rows, one chunk each) and a transposing
-// read (16 lanes on four consecutive rows, two adjacent chunks each) both
-// fall on distinct chunk positions.
+// LDS tiles are [rows][W] 16-bit values (W = 32, 64, 128 or 256), stored in
+// 16-byte chunks whose index within the row is XOR-ed with swz(row).  With
+// 64 banks of 4 bytes, a fragment read (ds_read_b128: 16 lanes on 16
+// consecutive rows, one chunk each) and a transposing read
+// (ds_read_b64_tr_b16: 32 lanes on four consecutive rows, four adjacent
+// chunks each) both fall on distinct banks:
+//   W >= 128 (rows of 256 or 512 bytes): the two low bits of the row pick the
+//     4-chunk group, the next two the chunk within it;
+//   W = 64 (128-byte rows, two rows per bank period): the row's parity picks
+//     the bank half, bit 1 the 4-chunk group, bits 2-3 the chunk in it;
+//   W = 32 (64-byte rows, only read transposed): four consecutive rows
+//     already cover all banks.
 template <int W>
 __device__ __forceinline__ int swz(int r) {
-    // 64-byte rows (W = 32): four consecutive rows of a transposing read
-    // already fall on distinct banks, and there are only four chunks
     if constexpr (W == 32) return 0;
-    const int f = ((r & 3) << 1) | ((r >> 2) & 1);
-    if constexpr (W >= 128)
-        return f | (((r >> 3) & 1) << 3);
-    else
-        return f;
+    if constexpr (W >= 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 template <int W>
 __device__ __forceinline__ int toff(int r, int ch) {
