@@ -84,6 +84,11 @@ def _bind(lib):
         ctypes.POINTER(ctypes.c_uint8), i64p, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint32,
         ctypes.c_float, ctypes.c_int, ctypes.c_int, i64p, ctypes.c_int64, f64p, f64p, ctypes.c_int]
     lib.ora_attention_fwd_ext.restype = ctypes.c_int
+    lib.ora_attention_bwd_ext.argtypes = [u16p, u16p, u16p, u16p] + [ctypes.c_int] * 5 + [
+        ctypes.POINTER(ctypes.c_uint8), i64p, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint32,
+        ctypes.c_float, ctypes.c_int, ctypes.c_int, i64p, ctypes.c_int64, i64p, ctypes.c_int64,
+        f64p, f64p, f64p, ctypes.c_int]
+    lib.ora_attention_bwd_ext.restype = ctypes.c_int
     return lib
 
 
@@ -257,6 +262,47 @@ def attention_fwd_ext(q, k, v, *, scale, causal, dtype, mask=None, mask_strides=
     if rc != 0:
         raise RuntimeError("ora_attention_fwd_ext failed with code %d" % rc)
     return o, lse
+
+
+def attention_bwd_ext(q, k, v, dout, *, scale, causal, dtype, mask=None, mask_strides=None,
+                      dropout_p=0.0, seed=0, offset=0, qrows=None, krows=None, nthreads=0, lib=None):
+    """Backward of attention_fwd_ext (gradients of sum(O * dout)).  qrows /
+    krows: flat query / key row ids to return (all rows when None).
+
+    Returns (dq, dk, dv): [B,H,Sq,D], [B,H,Sk,D], [B,H,Sk,D] float64 when
+    the rows are not given, else [nq, D], [nk, D], [nk, D]."""
+    lib = lib or load()
+    q, qp = _u16(q)
+    k, kp = _u16(k)
+    v, vp = _u16(v)
+    dout, gp = _u16(dout)
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    full = qrows is None and krows is None
+    qrows = np.arange(B * H * Sq, dtype=np.int64) if qrows is None else np.ascontiguousarray(qrows, np.int64)
+    krows = np.arange(B * H * Sk, dtype=np.int64) if krows is None else np.ascontiguousarray(krows, np.int64)
+    mp, sp = None, None
+    if mask is not None:
+        mask = np.asarray(mask)
+        if mask.dtype != np.uint8:
+            raise TypeError("mask must be uint8")
+        mask_strides = np.ascontiguousarray(mask_strides, dtype=np.int64)
+        mp = mask.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+        sp = mask_strides.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    dq = np.empty((qrows.size, D), dtype=np.float64)
+    dk = np.empty((krows.size, D), dtype=np.float64)
+    dv = np.empty((krows.size, D), dtype=np.float64)
+    i64 = ctypes.POINTER(ctypes.c_int64)
+    rc = lib.ora_attention_bwd_ext(qp, kp, vp, gp, B, H, Sq, Sk, D, mp, sp, ctypes.c_float(dropout_p),
+                                   ctypes.c_uint64(seed), ctypes.c_uint32(offset), ctypes.c_float(scale),
+                                   int(bool(causal)), _DTYPES[dtype], qrows.ctypes.data_as(i64), qrows.size,
+                                   krows.ctypes.data_as(i64), krows.size, _f64p(dq), _f64p(dk), _f64p(dv),
+                                   int(nthreads))
+    if rc != 0:
+        raise RuntimeError("ora_attention_bwd_ext failed with code %d" % rc)
+    if full:
+        return dq.reshape(B, H, Sq, D), dk.reshape(B, H, Sk, D), dv.reshape(B, H, Sk, D)
+    return dq, dk, dv
 
 
 def max_threads(lib=None):

@@ -627,3 +627,144 @@ int ora_attention_fwd_ext(const uint16_t* q, const uint16_t* k, const uint16_t* 
     }
     return err;
 }
+
+/*
+ * Backward of the forward with an explicit mask and dropout
+ * (ora_attention_fwd_ext): with P the masked, undropped probabilities, Z the
+ * keep indicators and c = 65536 / (65536 - t) the rescale,
+ *   O_i   = sum_j P_ij Z_ij c v_j
+ *   dV_j  = sum_i P_ij Z_ij c dO_i
+ *   dP_ij = Z_ij c (dO_i . v_j)                  (gradient with respect to P_ij)
+ *   dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik)      (Jacobian of the row softmax)
+ *   dQ_i  = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i.
+ * The chain rule through the forward's definition; nothing here is tiled.
+ * Evaluated row by row: for each head with a selected row or key, every
+ * query row's P, Z and dS are formed once; dQ is written for the selected
+ * query rows (qrows, flat (b*H+h)*Sq+i) and dK, dV are accumulated for the
+ * selected keys (krows, flat (b*H+h)*Sk+j), with per-thread partial sums
+ * added in thread order.  dq: nq x D, dk and dv: nk x D (fp64).
+ */
+int ora_attention_bwd_ext(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                          const uint16_t* dout, int B, int H, int Sq, int Sk, int D,
+                          const uint8_t* mask, const int64_t* mstride, float dropout_p,
+                          uint64_t seed, uint32_t offset, float scale, int causal, int dtype,
+                          const int64_t* qrows, int64_t nq, const int64_t* krows, int64_t nk,
+                          double* dq, double* dk, double* dv, int nthreads) {
+    if (!q || !k || !v || !dout || B < 0 || H < 0 || Sq < 0 || Sk < 0 || D <= 0) return 1;
+    if ((nq > 0 && (!qrows || !dq)) || (nk > 0 && (!krows || !dk || !dv))) return 1;
+    if (mask && !mstride) return 1;
+    if (dtype != ORA_F16 && dtype != ORA_BF16) return 2;
+    const int t = ora_dropout_threshold(dropout_p);
+    if (t < 0) return 5;
+    const int64_t BH = (int64_t)B * H;
+    for (int64_t r = 0; r < nq; ++r) if (qrows[r] < 0 || qrows[r] >= BH * Sq) return 4;
+    for (int64_t r = 0; r < nk; ++r) if (krows[r] < 0 || krows[r] >= BH * Sk) return 4;
+    set_threads(nthreads);
+    const double sc = (double)scale;
+    const double keep_scale = 65536.0 / (double)(65536 - t);
+    const int64_t kh = (int64_t)Sk * D;
+    const int nthr = ora_max_threads();
+    const int64_t accn = 2 * (nk > 0 ? nk : 1) * (int64_t)D;
+    const size_t skn = (size_t)(Sk > 0 ? Sk : 1);
+    double* Kd = (double*)malloc(sizeof(double) * (size_t)(kh > 0 ? kh : 1));
+    double* Vd = (double*)malloc(sizeof(double) * (size_t)(kh > 0 ? kh : 1));
+    double* Qb = (double*)malloc(sizeof(double) * (size_t)nthr * D);
+    double* Gb = (double*)malloc(sizeof(double) * (size_t)nthr * D);
+    double* Pb = (double*)malloc(sizeof(double) * (size_t)nthr * skn);
+    double* Zb = (double*)malloc(sizeof(double) * (size_t)nthr * skn);
+    double* Db = (double*)malloc(sizeof(double) * (size_t)nthr * skn);
+    double* acc = (double*)malloc(sizeof(double) * (size_t)nthr * (size_t)accn);
+    if (!Kd || !Vd || !Qb || !Gb || !Pb || !Zb || !Db || !acc) {
+        free(Kd); free(Vd); free(Qb); free(Gb); free(Pb); free(Zb); free(Db); free(acc);
+        return 3;
+    }
+    for (int64_t r = 0; r < nk; ++r)
+        for (int d = 0; d < D; ++d) { dk[r * D + d] = 0.0; dv[r * D + d] = 0.0; }
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        int64_t sel = 0;
+        for (int64_t r = 0; r < nq; ++r) sel += qrows[r] / Sq == bh;
+        for (int64_t r = 0; r < nk; ++r) sel += krows[r] / Sk == bh;
+        if (sel == 0) continue;
+        ora_decode(k + bh * kh, Kd, kh, dtype);
+        ora_decode(v + bh * kh, Vd, kh, dtype);
+        const int64_t b = bh / H, h = bh % H;
+        for (int th = 0; th < nthr; ++th)
+            memset(acc + (size_t)th * accn, 0, sizeof(double) * (size_t)accn);
+        #pragma omp parallel for schedule(static) num_threads(nthr)
+        for (int64_t i = 0; i < Sq; ++i) {
+            const int th = thread_id();
+            double* Qr = Qb + (size_t)th * D;
+            double* Gr = Gb + (size_t)th * D;
+            double* Pr = Pb + (size_t)th * skn;
+            double* Zr = Zb + (size_t)th * skn;
+            double* dPr = Db + (size_t)th * skn;
+            double* ac = acc + (size_t)th * accn;
+            ora_decode(q + (bh * Sq + i) * D, Qr, D, dtype);
+            ora_decode(dout + (bh * Sq + i) * D, Gr, D, dtype);
+            const uint8_t* mrow = mask ? mask + b * mstride[0] + h * mstride[1] + i * mstride[2] : NULL;
+            /* masked, undropped probabilities */
+            double m = -INFINITY;
+            for (int64_t j = 0; j < Sk; ++j) {
+                if (!visible(i, j, Sq, Sk, causal) || (mrow && mrow[j] == 0)) { Pr[j] = -INFINITY; continue; }
+                double a = 0.0;
+                for (int d = 0; d < D; ++d) a += Qr[d] * Kd[j * D + d];
+                Pr[j] = sc * a;
+                if (Pr[j] > m) m = Pr[j];
+            }
+            double l = 0.0;
+            for (int64_t j = 0; j < Sk; ++j) {
+                Pr[j] = m == -INFINITY ? 0.0 : exp(Pr[j] - m);
+                l += Pr[j];
+            }
+            for (int64_t j = 0; j < Sk; ++j) Pr[j] = l > 0.0 ? Pr[j] / l : 0.0;
+            /* keep factors, dP and the row term */
+            double rowdot = 0.0;
+            for (int64_t j = 0; j < Sk; ++j) {
+                Zr[j] = (t == 0 || keep_element(seed, offset, bh, i, j, t)) ? keep_scale : 0.0;
+                double a = 0.0;
+                for (int d = 0; d < D; ++d) a += Gr[d] * Vd[j * D + d];
+                dPr[j] = Zr[j] * a;
+                rowdot += Pr[j] * dPr[j];
+            }
+            /* dQ of a selected row */
+            for (int64_t r = 0; r < nq; ++r) {
+                if (qrows[r] != bh * Sq + i) continue;
+                double* gq = dq + r * D;
+                for (int d = 0; d < D; ++d) gq[d] = 0.0;
+                for (int64_t j = 0; j < Sk; ++j) {
+                    const double ds = Pr[j] * (dPr[j] - rowdot);
+                    for (int d = 0; d < D; ++d) gq[d] += ds * Kd[j * D + d];
+                }
+                for (int d = 0; d < D; ++d) gq[d] *= sc;
+            }
+            /* dK, dV of the selected keys */
+            for (int64_t r = 0; r < nk; ++r) {
+                if (krows[r] / Sk != bh) continue;
+                const int64_t j = krows[r] - bh * Sk;
+                if (Pr[j] == 0.0) continue;
+                const double pz = Pr[j] * Zr[j];
+                const double ds = Pr[j] * (dPr[j] - rowdot);
+                double* av = ac + (r * 2) * D;
+                double* ak = ac + (r * 2 + 1) * D;
+                for (int d = 0; d < D; ++d) {
+                    av[d] += pz * Gr[d];
+                    ak[d] += ds * Qr[d];
+                }
+            }
+        }
+        for (int th = 0; th < nthr; ++th) {
+            const double* ac = acc + (size_t)th * accn;
+            for (int64_t r = 0; r < nk; ++r) {
+                if (krows[r] / Sk != bh) continue;
+                for (int d = 0; d < D; ++d) {
+                    dv[r * D + d] += ac[(r * 2) * D + d];
+                    dk[r * D + d] += ac[(r * 2 + 1) * D + d];
+                }
+            }
+        }
+    }
+    for (int64_t r = 0; r < nk; ++r)
+        for (int d = 0; d < D; ++d) dk[r * D + d] = sc * dk[r * D + d];
+    free(Kd); free(Vd); free(Qb); free(Gb); free(Pb); free(Zb); free(Db); free(acc);
+    return 0;
+}

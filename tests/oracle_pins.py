@@ -589,10 +589,125 @@ def pin_ext_rows_match_full(lib):
     assert np.array_equal(ro, o.reshape(-1, D)[rows]) and np.array_equal(rl, lse.reshape(-1)[rows])
 
 
+def _bwd_ext(lib, q, k, v, g, scale, causal, dtype, **kw):
+    return oracle.attention_bwd_ext(bits(q), bits(k), bits(v), bits(g), scale=scale, causal=causal,
+                                    dtype=dtype, lib=lib, **kw)
+
+
+def pin_bwd_ext_plain_equals_bwd(lib):
+    """No mask and p = 0: the backward of the plain forward."""
+    for dtype, (Sq, Sk), causal in (("f16", (40, 40), True), ("bf16", (23, 57), False), ("f16", (57, 23), True)):
+        q, k, v, g = _grad_inputs(1, 2, Sq, Sk, 16, dtype, seed=100 + Sq)
+        a = _run_bwd(lib, q, k, v, g, softmax_scale(16), causal, dtype)
+        b = _bwd_ext(lib, q, k, v, g, softmax_scale(16), causal, dtype)
+        for x, y in zip(a, b):
+            assert np.max(np.abs(x - y)) <= 1e-13 * max(1.0, np.max(np.abs(x))), (dtype, Sq, Sk)
+
+
+def _keep_matrix(B, H, Sq, Sk, seed, offset, p):
+    t = int(np.rint(np.float32(p) * np.float32(65536.0)))
+    z = np.zeros((B, H, Sq, Sk))
+    for bh in range(B * H):
+        z[bh // H, bh % H] = keep_pattern(Sq, Sk, bh, seed, offset, t) * (65536.0 / (65536.0 - t))
+    return z
+
+
+def pin_bwd_ext_autograd(lib):
+    """torch autograd in fp64 through softmax(masked scores) * Z * c @ V, with
+    the keep matrix from the Philox written in this file: the oracle's
+    gradients with a per-head mask and dropout."""
+    for dtype, (B, H, Sq, Sk, D), causal, p in (("f16", (1, 2, 30, 41, 16), True, 0.25),
+                                                ("bf16", (2, 1, 33, 33, 8), False, 0.5)):
+        q, k, v, g = _grad_inputs(B, H, Sq, Sk, D, dtype, seed=110 + Sq)
+        rng = np.random.default_rng(111 + Sq)
+        m = (rng.random((B, H, Sq, Sk)) < 0.7).astype(np.uint8)
+        m[0, 0, 2, :] = 0
+        ms = (H * Sq * Sk, Sq * Sk, Sk)
+        seed, offset = 0xABCDEF012345, 3
+        scale = softmax_scale(D)
+        dq, dk, dv = _bwd_ext(lib, q, k, v, g, scale, causal, dtype, mask=m, mask_strides=ms,
+                              dropout_p=p, seed=seed, offset=offset)
+        allow = torch.from_numpy(m.astype(bool))
+        if causal:
+            i = torch.arange(Sq)[:, None]
+            j = torch.arange(Sk)[None, :]
+            allow = allow & (j <= i + (Sk - Sq))
+        Z = torch.from_numpy(_keep_matrix(B, H, Sq, Sk, seed, offset, p))
+        Q, K, V = (torch.from_numpy(_f64(t)).requires_grad_() for t in (q, k, v))
+        s = (scale * Q @ K.transpose(-1, -2)).masked_fill(~allow, float("-inf"))
+        P = torch.softmax(s, dim=-1).nan_to_num(0.0)
+        o = (P * Z) @ V
+        (o * torch.from_numpy(_f64(g))).sum().backward()
+        for name, got, ref in (("dq", dq, Q.grad), ("dk", dk, K.grad), ("dv", dv, V.grad)):
+            ref = ref.numpy()
+            err = np.max(np.abs(got - ref))
+            assert err <= 1e-12 * max(1.0, np.max(np.abs(ref))), (name, dtype, err)
+        assert np.max(np.abs(dk.sum(axis=2))) <= 1e-12 * max(1.0, np.max(np.abs(dk))) * Sk
+
+
+def pin_bwd_ext_finite_difference(lib):
+    """Central differences of the 40-digit forward with a mask and dropout."""
+    getcontext().prec = 40
+    Sq, Sk, D, p = 3, 8, 2, 0.5
+    q, k, v, g = _grad_inputs(1, 1, Sq, Sk, D, "f16", seed=120)
+    m = np.array([[1, 1, 0, 1, 1, 1, 0, 1], [0, 1, 1, 1, 1, 0, 1, 1], [1, 0, 1, 1, 0, 1, 1, 1]], np.uint8)
+    seed, offset = 77, 1
+    scale = softmax_scale(D)
+    dq, dk, dv = _bwd_ext(lib, q, k, v, g, scale, False, "f16", mask=m, mask_strides=(0, 0, Sk),
+                          dropout_p=p, seed=seed, offset=offset)
+    Z = _keep_matrix(1, 1, Sq, Sk, seed, offset, p)[0, 0]
+    Q, K, V, G = (_f64(t)[0, 0] for t in (q, k, v, g))
+    sc = Decimal(scale)
+
+    def loss(Qx, Kx, Vx):
+        tot = Decimal(0)
+        for i in range(Sq):
+            ws, num, den = [], [Decimal(0)] * D, Decimal(0)
+            for j in range(Sk):
+                if not m[i, j]:
+                    continue
+                w = (sc * sum(Qx[i][d] * Kx[j][d] for d in range(D))).exp()
+                den += w
+                for d in range(D):
+                    num[d] += w * Decimal(float(Z[i, j])) * Vx[j][d]
+            for d in range(D):
+                tot += num[d] / den * Decimal(float(G[i, d]))
+        return tot
+
+    dec = lambda A: [[Decimal(float(x)) for x in row] for row in A]
+    h = Decimal("1e-12")
+    for which, grad, rows in (("q", dq, Sq), ("k", dk, Sk), ("v", dv, Sk)):
+        for r in range(rows):
+            for d in range(D):
+                X = {"q": dec(Q), "k": dec(K), "v": dec(V)}
+                X[which][r][d] += h
+                up = loss(X["q"], X["k"], X["v"])
+                X[which][r][d] -= 2 * h
+                dn = loss(X["q"], X["k"], X["v"])
+                fd = float((up - dn) / (2 * h))
+                assert abs(grad[0, 0, r, d] - fd) <= 1e-12 * max(1.0, abs(fd)), (which, r, d, grad[0, 0, r, d], fd)
+
+
+def pin_bwd_ext_rows_match_full(lib):
+    B, H, Sq, Sk, D = 2, 2, 45, 60, 16
+    q, k, v, g = _grad_inputs(B, H, Sq, Sk, D, "bf16", seed=130)
+    m = (np.random.default_rng(131).random((Sq, Sk)) < 0.8).astype(np.uint8)
+    kw = dict(mask=m, mask_strides=(0, 0, Sk), dropout_p=0.2, seed=9, offset=2)
+    dq, dk, dv = _bwd_ext(lib, q, k, v, g, softmax_scale(D), True, "bf16", **kw)
+    qr = np.array([0, 5, Sq - 1, 2 * Sq + 1, B * H * Sq - 1], np.int64)
+    kr = np.array([0, Sk + 3, 3 * Sk - 1, B * H * Sk - 1], np.int64)
+    a, b, c = _bwd_ext(lib, q, k, v, g, softmax_scale(D), True, "bf16", qrows=qr, krows=kr, **kw)
+    scl = max(1.0, np.max(np.abs(dk)), np.max(np.abs(dv)), np.max(np.abs(dq)))
+    assert np.max(np.abs(a - dq.reshape(-1, D)[qr])) <= 1e-13 * scl
+    assert np.max(np.abs(b - dk.reshape(-1, D)[kr])) <= 1e-13 * scl
+    assert np.max(np.abs(c - dv.reshape(-1, D)[kr])) <= 1e-13 * scl
+
+
 ALL_PINS = [pin_decode_f16, pin_decode_bf16, pin_q_zero, pin_causal_row0, pin_convexity,
             pin_bruteforce_decimal, pin_sdpa_fp64, pin_chunk_merge, pin_invariances,
             pin_rows_match_full, pin_unequal_causal_suffix, pin_bwd_autograd,
             pin_bwd_finite_difference, pin_bwd_closed_forms, pin_bwd_invariants,
             pin_bwd_rows_match_full, pin_philox_kat, pin_dropout_threshold,
             pin_ext_plain_equals_forward, pin_ext_mask_sdpa, pin_ext_dropout_pattern,
-            pin_ext_dropout_rate, pin_ext_rows_match_full]
+            pin_ext_dropout_rate, pin_ext_rows_match_full, pin_bwd_ext_plain_equals_bwd,
+            pin_bwd_ext_autograd, pin_bwd_ext_finite_difference, pin_bwd_ext_rows_match_full]

@@ -91,6 +91,18 @@ MUTATIONS = [
      "const double keep_scale = 1.0;"),
     ("dropout_renormalised", "        srow[j] = e;\n        l += e;",
      "        srow[j] = e;\n        l += (t > 0 && !keep_element(seed, offset, bh, i, j, t)) ? 0.0 : e;"),
+    ("bwdx_dv_keep_missing", "const double pz = Pr[j] * Zr[j];", "const double pz = Pr[j];"),
+    ("bwdx_dp_keep_missing", "                dPr[j] = Zr[j] * a;", "                dPr[j] = a;"),
+    ("bwdx_keep_scale_missing", "const double keep_scale = 65536.0 / (double)(65536 - t);",
+     "const double keep_scale = 1.0;"),
+    ("bwdx_mask_ignored", "if (!visible(i, j, Sq, Sk, causal) || (mrow && mrow[j] == 0)) { Pr[j] = -INFINITY; continue; }",
+     "if (!visible(i, j, Sq, Sk, causal)) { Pr[j] = -INFINITY; continue; }"),
+    ("bwdx_rowdot_undropped", "                rowdot += Pr[j] * dPr[j];", "                rowdot += Pr[j] * a;"),
+    ("bwdx_ds_sign", "const double ds = Pr[j] * (dPr[j] - rowdot);\n                    for (int d = 0; d < D; ++d) gq[d] += ds * Kd[j * D + d];",
+     "const double ds = Pr[j] * (rowdot - dPr[j]);\n                    for (int d = 0; d < D; ++d) gq[d] += ds * Kd[j * D + d];"),
+    ("bwdx_dk_uses_dout", "                    ak[d] += ds * Qr[d];", "                    ak[d] += ds * Gr[d];"),
+    ("bwdx_dk_scale_missing", "dk[r * D + d] = sc * dk[r * D + d];", "dk[r * D + d] = dk[r * D + d];"),
+    ("bwdx_wrong_key", "const int64_t j = krows[r] - bh * Sk;", "const int64_t j = (krows[r] - bh * Sk + 1) % Sk;"),
     ("ext_causal_ignored", "const int vis = visible(i, j, Sq, Sk, causal) && (!mrow || mrow[j] != 0);",
      "const int vis = (!mrow || mrow[j] != 0);"),
 ]
