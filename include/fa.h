@@ -280,6 +280,25 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            float scale, int causal, int dtype, int deterministic, void* workspace,
            int64_t workspace_bytes, void* stream);
 
+/*
+ * fa_bwd_ext -- gradients of fa_fwd_ext: the backward with the same explicit
+ * mask and dropout as the forward that produced o and lse (same mask, strides,
+ * dropout_p, seed and offset).  With Z c the forward's keep factor
+ * (0 or 65536/(65536 - t)):
+ *   dv_j = sum_i P_ij Z_ij c dout_i,  dS_ij = P_ij (Z_ij c dout_i . v_j - D_i),
+ *   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,
+ * D_i = dout_i . o_i.  Always the deterministic mode: the workspace is
+ * fa_bwd_workspace_bytes(B, H, Sq, D, 1).  Arguments as for fa_bwd and
+ * fa_fwd_ext (mask rows are read up to 31 rows past the last query, so
+ * (Sq + 31) * mask row stride + Sk must stay below 2^31 bytes); the mask
+ * must not overlap an output.  D in {64, 128}.
+ */
+int fa_bwd_ext(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk, int D,
+               const uint8_t* mask, const int64_t* mask_strides, float dropout_p, uint64_t seed,
+               uint32_t offset, float scale, int causal, int dtype, void* workspace,
+               int64_t workspace_bytes, void* stream);
+
 /* Bytes of workspace fa_bwd needs (0 for an invalid shape): the row dot
  * products D_i, B*H*Sq fp32, plus in atomic mode (deterministic == 0) the
  * fp32 dq accumulator, B*H*Sq*D fp32; each part rounded up to 256 bytes. */

@@ -282,3 +282,26 @@ def test_plan_d256_uses_the_general_kernel(lib):
         nkv = (1000 + 31) // 32
         want = sum(min(nkv, (min(1000, (qb + 1) * 128) + 31) // 32) if causal else nkv for qb in range(nqb))
         assert tiles == want * 6
+
+
+@fake_addresses
+def test_bwd_ext_rejects_bad_arguments(lib):
+    B, H, Sq, Sk, D = 1, 2, 100, 120, 64
+    DO, DQ, DK, DV, W, M = 0x600000, 0x700000, 0x800000, 0x900000, 0x10000000, 0x20000000
+    need = fa.fa_bwd_workspace_bytes(B, H, Sq, D, 1)
+
+    def call(**kw):
+        a = dict(q=Q, k=K, v=V, o=O, do=DO, lse=L, dq=DQ, dk=DK, dv=DV, Sq=Sq, Sk=Sk, D=D, mask=M,
+                 ms=(0, 0, 128), p=0.1, ws=W, wsb=need)
+        a.update(kw)
+        return fa.fa_bwd_ext(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                             B, H, a["Sq"], a["Sk"], a["D"], a["mask"], a["ms"], a["p"], 1, 0, 0.125, 1, 0,
+                             a["ws"], a["wsb"], None)
+
+    assert call(ws=0) == 1 and call(dq=0) == 1
+    assert call(D=256) == 3
+    assert call(p=1.0) == 9 and call(p=-0.5) == 9
+    assert call(mask=M + 1) == 9 and call(ms=(0, 0, 100)) == 9 and call(ms=(0, 0, 126)) == 9
+    assert call(ms=(0, 0, 1 << 25)) == 9                 # mask rows beyond 2^31 bytes
+    assert call(dk=M) == 7                                # an output over the mask
+    assert call(wsb=need - 1) == 2

@@ -1,0 +1,125 @@
+"""GPU parity of the backward with an explicit mask and dropout (fa_bwd_ext)
+against the fp64 oracle's backward of the masked / dropout forward."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import parity
+import tiled_attention_15_amd as fa
+from workloads import bits, make_inputs, softmax_scale
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def to64(t):
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def grad_inputs(B, H, Sq, Sk, D, dtype, seed, q_mult=1.0):
+    q, k, v = make_inputs(B, H, max(Sq, Sk), D, dtype, seed=seed, q_mult=q_mult, Sk=Sk)
+    q = q[:, :, :Sq].contiguous()
+    g, _, _ = make_inputs(B, H, Sq, D, dtype, seed=seed + 1000)
+    return q, k, v, g
+
+
+def make_mask(kind, B, H, Sq, Sk, seed):
+    rng = np.random.default_rng(seed)
+    if kind is None:
+        return None, None
+    ld = (Sk + 3) // 4 * 4
+    if kind == "per_head":
+        m = np.zeros((B, H, Sq, ld), np.uint8)
+        m[..., :Sk] = rng.random((B, H, Sq, Sk)) < 0.7
+        m[0, 0, min(2, Sq - 1), :] = 0                  # a row with no visible key
+        return m, (H * Sq * ld, Sq * ld, ld)
+    m = np.zeros((Sq, ld + 4), np.uint8)
+    m[:, :Sk] = rng.random((Sq, Sk)) < 0.85
+    return m, (0, 0, ld + 4)
+
+
+def run(q, k, v, g, causal, dtype, mask, ms, p, seed, offset):
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
+    md = None if mask is None else torch.from_numpy(mask).to(DEV)
+    code = fa.BF16 if dtype == "bf16" else fa.F16
+    sc = softmax_scale(D)
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=DEV)
+    assert fa.fa_fwd_ext(qd, kd, vd, o, lse, B, H, Sq, Sk, D, md, ms, p, seed, offset, sc, causal, code, None) == 0
+    need = fa.fa_bwd_workspace_bytes(B, H, Sq, D, 1)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    st = fa.fa_bwd_ext(qd, kd, vd, o, gd, lse, dq, dk, dv, B, H, Sq, Sk, D, md, ms, p, seed, offset, sc, causal,
+                       code, ws, need, None)
+    assert st == 0, fa.fa_status_string(st)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+CASES = [
+    # (B, H, Sq, Sk, D, causal, dtype, mask kind, p)
+    (1, 2, 64, 64, 64, False, "f16", "per_head", 0.0),
+    (1, 2, 128, 128, 128, True, "bf16", None, 0.1),
+    (2, 1, 200, 200, 64, True, "f16", "shared", 0.25),
+    (1, 2, 257, 257, 128, True, "bf16", "per_head", 0.5),
+    (1, 1, 100, 300, 128, True, "f16", "shared", 0.2),
+    (1, 1, 300, 100, 64, True, "bf16", "per_head", 0.1),
+    (2, 2, 130, 67, 128, False, "f16", None, 0.3),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=["%dx%dx%dx%dx%d%s%s_%s_p%g" % (c[0], c[1], c[2], c[3], c[4],
+                                                                          "c" if c[5] else "n", c[6], c[7], c[8])
+                                             for c in CASES])
+def test_bwd_ext_matches_oracle(case):
+    B, H, Sq, Sk, D, causal, dtype, kind, p = case
+    say("case bwd ext", case)
+    q, k, v, g = grad_inputs(B, H, Sq, Sk, D, dtype, seed=3000 + Sq + 3 * Sk + D)
+    mask, ms = make_mask(kind, B, H, Sq, Sk, seed=3100 + Sq)
+    seed, offset = 0x5EED_0000_0001 + Sq, 11
+    dq, dk, dv = run(q, k, v, g, causal, dtype, mask, ms, p, seed, offset)
+    refs = oracle.attention_bwd_ext(bits(q), bits(k), bits(v), bits(g), scale=softmax_scale(D), causal=causal,
+                                    dtype=dtype, mask=mask, mask_strides=ms, dropout_p=p, seed=seed, offset=offset)
+    mx = {n: float(t.abs().max()) for n, t in (("q", q), ("k", k), ("v", v), ("g", g))}
+    sc = softmax_scale(D) * 65536.0 / (65536.0 - round(p * 65536))
+    zs = {"dq": sc * mx["g"] * mx["v"] * mx["k"], "dk": sc * mx["g"] * mx["v"] * mx["q"], "dv": mx["g"] * sc}
+    for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
+        st = parity.assert_grad_parity(to64(got), ref, dtype, "%s %s" % (name, case), zero_scale=zs[name])
+        say("  ", name, st)
+
+
+def test_bwd_ext_without_mask_or_dropout_is_fa_bwd():
+    q, k, v, g = grad_inputs(1, 3, 300, 300, 128, "bf16", seed=3200)
+    a = run(q, k, v, g, True, "bf16", None, None, 0.0, 0, 0)
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
+    o, lse = fa.forward_ext(qd, kd, vd, causal=True)
+    b = fa.backward(qd, kd, vd, o, lse, gd, causal=True, deterministic=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_bwd_ext_medium_sampled_rows():
+    """1x4x2048x128 bf16 causal with a shared mask and dropout 0.1: sampled dq
+    rows and dk/dv rows of two heads against the oracle."""
+    B, H, S, D = 1, 4, 2048, 128
+    q, k, v, g = grad_inputs(B, H, S, S, D, "bf16", seed=3300)
+    mask, ms = make_mask("shared", B, H, S, S, seed=3301)
+    dq, dk, dv = run(q, k, v, g, True, "bf16", mask, ms, 0.1, 4242, 5)
+    rng = np.random.default_rng(3302)
+    qrows = np.sort(rng.choice(B * H * S, size=64, replace=False)).astype(np.int64)
+    krows = np.sort(np.concatenate([h * S + rng.choice(S, size=24, replace=False) for h in (1, 3)])).astype(np.int64)
+    rq, rk, rv = oracle.attention_bwd_ext(bits(q), bits(k), bits(v), bits(g), scale=softmax_scale(D), causal=True,
+                                          dtype="bf16", mask=mask, mask_strides=ms, dropout_p=0.1, seed=4242,
+                                          offset=5, qrows=qrows, krows=krows)
+    for nm, got, ref, rows in (("dq", dq, rq, qrows), ("dk", dk, rk, krows), ("dv", dv, rv, krows)):
+        sel = to64(got).reshape(-1, D)[rows]
+        say("  ", nm, parity.assert_grad_parity(sel[None, None], ref[None, None], "bf16", "medium " + nm))

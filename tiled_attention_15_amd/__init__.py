@@ -15,7 +15,8 @@ import os
 __all__ = ["FaError", "fa_fwd", "fa_fwd_strided", "fa_fwd_plan", "fa_naive_fwd",
            "fa_naive_workspace_bytes", "fa_status_string", "fa_version", "forward",
            "naive_forward", "library_path", "F16", "BF16", "STATUS", "fa_bwd",
-           "fa_bwd_workspace_bytes", "backward", "fa_fwd_ext", "forward_ext"]
+           "fa_bwd_workspace_bytes", "backward", "fa_fwd_ext", "forward_ext", "fa_bwd_ext",
+           "backward_ext"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libfa_hip.so")
@@ -73,6 +74,9 @@ def _load():
     lib.fa_fwd_ext.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, i64p, f, ctypes.c_uint64,
                                ctypes.c_uint32, f, i, i, vp]
     lib.fa_fwd_ext.restype = i
+    lib.fa_bwd_ext.argtypes = [vp] * 9 + [i] * 5 + [vp, i64p, f, ctypes.c_uint64, ctypes.c_uint32, f, i, i,
+                                                     vp, ctypes.c_int64, vp]
+    lib.fa_bwd_ext.restype = i
     _lib = lib
     return lib
 
@@ -147,6 +151,18 @@ def fa_fwd_ext(q, k, v, o, lse, B, H, Sq, Sk, D, mask, mask_strides, dropout_p, 
                               ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF),
                               ctypes.c_uint32(int(offset) & 0xFFFFFFFF), ctypes.c_float(scale),
                               int(bool(causal)), int(dtype), _stream(stream))
+
+
+def fa_bwd_ext(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, mask, mask_strides, dropout_p, seed,
+               offset, scale, causal, dtype, workspace, workspace_bytes, stream):
+    """C ABI fa_bwd_ext: gradients of the masked / dropout forward."""
+    ms = None if mask_strides is None else _strides3(mask_strides)
+    return _load().fa_bwd_ext(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                              _ptr(dk), _ptr(dv), int(B), int(H), int(Sq), int(Sk), int(D), _ptr(mask), ms,
+                              ctypes.c_float(dropout_p), ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF),
+                              ctypes.c_uint32(int(offset) & 0xFFFFFFFF), ctypes.c_float(scale),
+                              int(bool(causal)), int(dtype), _ptr(workspace), int(workspace_bytes),
+                              _stream(stream))
 
 
 def fa_bwd_workspace_bytes(B, H, Sq, D, deterministic):
@@ -333,3 +349,42 @@ def forward_ext(q, k, v, causal=False, scale=None, mask=None, dropout_p=0.0, see
     if st != 0:
         raise FaError(st, "fa_fwd_ext")
     return o, lse
+
+
+def backward_ext(q, k, v, o, lse, dout, causal=False, scale=None, mask=None, dropout_p=0.0, seed=0, offset=0,
+                 workspace=None):
+    """Gradients (dq, dk, dv) of forward_ext with the same mask, dropout_p,
+    seed and offset (o and lse from that call); contiguous tensors."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("fa: q/o/dout [B, H, Sq, D] and k/v [B, H, Sk, D] expected")
+    if not all(t.is_contiguous() for t in (q, k, v, o, dout)) or not lse.is_contiguous():
+        raise ValueError("fa: the backward takes contiguous tensors")
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    strides = None
+    if mask is not None:
+        if mask.dtype == torch.bool:
+            mask = mask.view(torch.uint8)
+        if mask.dtype != torch.uint8 or mask.device != q.device:
+            raise ValueError("fa: mask must be a uint8/bool tensor on q's device")
+        mask = mask.expand(B, H, Sq, Sk)
+        if mask.stride(3) != 1:
+            raise ValueError("fa: the mask's last dimension must be contiguous")
+        strides = (mask.stride(0), mask.stride(1), mask.stride(2))
+    need = fa_bwd_workspace_bytes(B, H, Sq, D, True)
+    if need <= 0:
+        raise FaError(2, "fa_bwd_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream().cuda_stream
+    st = fa_bwd_ext(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, mask, strides, dropout_p, seed, offset,
+                    scale, causal, _dtype_code(q), workspace, workspace.numel() * workspace.element_size(),
+                    stream)
+    if st != 0:
+        raise FaError(st, "fa_bwd_ext")
+    return dq, dk, dv

@@ -387,10 +387,11 @@ int64_t fa_bwd_workspace_bytes(int B, int H, int Sq, int D, int deterministic) {
     return bwd_layout(B, H, Sq, D, deterministic, L) ? L.total : 0;
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-           const float* lse, void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk, int D,
-           float scale, int causal, int dtype, int deterministic, void* workspace,
-           int64_t workspace_bytes, void* stream) {
+static int bwd_common(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk, int D,
+                      const uint8_t* mask, const int64_t* mask_strides, float dropout_p, uint64_t seed,
+                      uint32_t offset, float scale, int causal, int dtype, int deterministic,
+                      void* workspace, int64_t workspace_bytes, void* stream) {
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
     int st = validate_shape(B, H, Sq, Sk, D, dtype);
     if (st != FA_OK) return st;
@@ -402,24 +403,41 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
          (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)workspace) & 15)
         return FA_ERR_ALIGN;
     if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_SCALE;
+    if (!(dropout_p >= 0.0f) || !(dropout_p < 1.0f)) return FA_ERR_MASK_DROPOUT;
+    const long drop_t = lrintf(dropout_p * 65536.0f);
+    if (drop_t > 65535) return FA_ERR_MASK_DROPOUT;
+    uintptr_t m0 = 0, m1 = 0;
+    if (mask) {
+        if (!mask_strides || ((uintptr_t)mask & 3)) return FA_ERR_MASK_DROPOUT;
+        for (int i = 0; i < 3; ++i)
+            if (mask_strides[i] < 0 || (mask_strides[i] & 3) != 0) return FA_ERR_MASK_DROPOUT;
+        if (mask_strides[2] < Sk || mask_strides[2] >= (int64_t(1) << 31)) return FA_ERR_MASK_DROPOUT;
+        // mask rows are read up to 31 past the last query (the last tile)
+        if ((int64_t)(Sq + 31) * mask_strides[2] + Sk + 3 >= (int64_t(1) << 31)) return FA_ERR_MASK_DROPOUT;
+        m0 = (uintptr_t)mask;
+        m1 = m0 + (uintptr_t)((int64_t)(B - 1) * mask_strides[0] + (int64_t)(H - 1) * mask_strides[1] +
+                              (int64_t)(Sq - 1) * mask_strides[2] + Sk);
+    }
     const uintptr_t qb = (uintptr_t)((int64_t)B * H * Sq * D * 2);
     const uintptr_t kb = (uintptr_t)((int64_t)B * H * Sk * D * 2);
     const uintptr_t lb = (uintptr_t)((int64_t)B * H * Sq * 4);
-    const uintptr_t in[6][2] = {{(uintptr_t)q, (uintptr_t)q + qb},       {(uintptr_t)k, (uintptr_t)k + kb},
+    const uintptr_t in[7][2] = {{(uintptr_t)q, (uintptr_t)q + qb},       {(uintptr_t)k, (uintptr_t)k + kb},
                                 {(uintptr_t)v, (uintptr_t)v + kb},       {(uintptr_t)o, (uintptr_t)o + qb},
-                                {(uintptr_t)dout, (uintptr_t)dout + qb}, {(uintptr_t)lse, (uintptr_t)lse + lb}};
+                                {(uintptr_t)dout, (uintptr_t)dout + qb}, {(uintptr_t)lse, (uintptr_t)lse + lb},
+                                {m0, m1}};
     const uintptr_t out[4][2] = {{(uintptr_t)dq, (uintptr_t)dq + qb},
                                  {(uintptr_t)dk, (uintptr_t)dk + kb},
                                  {(uintptr_t)dv, (uintptr_t)dv + kb},
                                  {(uintptr_t)workspace, (uintptr_t)workspace + (uintptr_t)L.total}};
     for (int i = 0; i < 4; ++i) {
-        for (int j = 0; j < 6; ++j)
-            if (overlap(out[i][0], out[i][1], in[j][0], in[j][1])) return FA_ERR_ALIAS;
+        for (int j = 0; j < 7; ++j)
+            if (in[j][1] > in[j][0] && overlap(out[i][0], out[i][1], in[j][0], in[j][1])) return FA_ERR_ALIAS;
         for (int j = i + 1; j < 4; ++j)
             if (overlap(out[i][0], out[i][1], out[j][0], out[j][1])) return FA_ERR_ALIAS;
     }
 
-    fa::bwd::BwdParams p;
+    fa::bwd::BwdParams p = {};
+    p.H = H;
     p.q = q;
     p.k = k;
     p.v = v;
@@ -438,8 +456,34 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     p.nqb = (Sq + fa::bwd::kQueryBlock - 1) / fa::bwd::kQueryBlock;
     p.scale = scale;
     p.scale_log2e = scale * 1.4426950408889634f;
+    p.mask = mask;
+    p.m_sb = mask ? mask_strides[0] : 0;
+    p.m_sh = mask ? mask_strides[1] : 0;
+    p.m_ss = mask ? mask_strides[2] : 0;
+    p.drop_t = (uint32_t)drop_t;
+    p.keep_scale = (float)(65536.0 / (65536.0 - (double)drop_t));
+    p.seed_lo = (uint32_t)seed;
+    p.seed_hi = (uint32_t)(seed >> 32);
+    p.offset = offset;
     const hipError_t err = fa::bwd::launch_bwd(p, D, dtype, causal != 0, deterministic != 0, (hipStream_t)stream);
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk, int D,
+           float scale, int causal, int dtype, int deterministic, void* workspace,
+           int64_t workspace_bytes, void* stream) {
+    return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, nullptr, nullptr, 0.0f, 0, 0,
+                      scale, causal, dtype, deterministic, workspace, workspace_bytes, stream);
+}
+
+int fa_bwd_ext(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk, int D,
+               const uint8_t* mask, const int64_t* mask_strides, float dropout_p, uint64_t seed,
+               uint32_t offset, float scale, int causal, int dtype, void* workspace,
+               int64_t workspace_bytes, void* stream) {
+    return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, mask, mask_strides, dropout_p, seed,
+                      offset, scale, causal, dtype, 1, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

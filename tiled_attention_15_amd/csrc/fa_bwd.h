@@ -18,6 +18,12 @@ struct BwdParams {
     void* dv;           // [BH, Sk, D]
     float* dvec;        // workspace [BH, Sq]: rowsum(dout * o)
     float* dqacc;       // workspace [BH, Sq, D] fp32 (atomic mode), else null
+    const uint8_t* mask;    // nonzero = keep, null = no mask (deterministic mode only)
+    int64_t m_sb, m_sh, m_ss;  // mask strides in bytes (batch, head, row)
+    uint32_t drop_t;        // dropout: keep iff the 16-bit Philox draw >= drop_t (0 = none)
+    float keep_scale;       // 65536 / (65536 - drop_t)
+    uint32_t seed_lo, seed_hi, offset;
+    int H;
     int Sq, Sk, BH;
     int nkb;            // key blocks of the dK/dV kernel per head
     int nqb;            // query blocks of the dQ kernel per head

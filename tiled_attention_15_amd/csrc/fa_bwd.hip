@@ -96,8 +96,8 @@ __global__ __launch_bounds__(256) void bwd_dq_convert(BwdParams p, int64_t n8) {
 // lane): the key block sits in LDS (K fragments are read from there at each
 // use) while V's fragments and the dK^T, dV^T accumulators stay in registers;
 // 32-query tiles of Q and dO go straight from global memory into LDS.
-template <int D, int DT, bool CAUSAL, bool ATOMIC>
-__global__ __launch_bounds__(256, ATOMIC ? 1 : 2) void bwd_dkdv(BwdParams p) {
+template <int D, int DT, bool CAUSAL, bool ATOMIC, bool MASK = false, bool DROP = false>
+__global__ __launch_bounds__(256, (ATOMIC || MASK || DROP) ? 1 : 2) void bwd_dkdv(BwdParams p) {
     constexpr int DC = D / 16;                         // k-steps over the head dimension
     constexpr int DB = D / 32;                         // 32-column blocks of the head dimension
     constexpr int QT = kQueryTile;
@@ -111,6 +111,10 @@ __global__ __launch_bounds__(256, ATOMIC ? 1 : 2) void bwd_dkdv(BwdParams p) {
     __shared__ __attribute__((aligned(16))) char smem[KBLK + 4 * TILE + DSB];
     __shared__ __attribute__((aligned(16))) float lse_s[2][QT];
     __shared__ __attribute__((aligned(16))) float dv_s[2][QT];
+    // mask bytes of a tile, [query][key of the block] (with a mask), and the
+    // keep bits of a tile, [query][8-key group] one bit per key (with dropout)
+    __shared__ __attribute__((aligned(16))) uint8_t msk_s[2][MASK ? QT * kKeyBlock : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t keep_s[2][DROP ? QT * kKeyBlock / 8 : 16];
     lds_t* const sm = (lds_t*)smem;
 
     const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, g = lane >> 5;
@@ -145,10 +149,45 @@ __global__ __launch_bounds__(256, ATOMIC ? 1 : 2) void bwd_dkdv(BwdParams p) {
     int t0 = 0;
     if (CAUSAL) t0 = max(0, k0 - diag) / QT;
 
+    // Mask rows of this head: a buffer over [first row, last row + Sk)
+    // rounded up to whole dwords; offsets beyond it read as zero (hidden).
+    i32x4 rm = rq;
+    if constexpr (MASK) {
+        const int b_ = bh / p.H, h_ = bh - b_ * p.H;
+        rm = rsrc_words(p.mask + (int64_t)b_ * p.m_sb + (int64_t)h_ * p.m_sh,
+                        (uint64_t)(((int64_t)(Sq - 1) * p.m_ss + Sk + 3) & ~(int64_t)3));
+    }
+    const uint32_t msk0 = (uint32_t)(uintptr_t)(lds_t*)&msk_s[0][0];
     auto issue = [&](int t, int buf) {
         const uint32_t base = lds0 + (uint32_t)(KBLK + buf * 2 * TILE);
         tile_dma<D, TN>(rq, t * QT, D, base, w, lane);
         tile_dma<D, TN>(rdo, t * QT, D, base + TILE, w, lane);
+        if constexpr (MASK) {
+            // QT rows x 128 bytes, one dword per lane and instruction
+#pragma unroll
+            for (int i = 0; i < QT * kKeyBlock / 4 / 256; ++i) {
+                const int c = (4 * i + w) * 64 + lane, r = c / (kKeyBlock / 4), dw = c % (kKeyBlock / 4);
+                lds_dma4(rm, (uint32_t)((int64_t)(t * QT + r) * p.m_ss + k0 + 4 * dw),
+                         msk0 + (uint32_t)(buf * QT * kKeyBlock + (4 * i + w) * 256));
+            }
+        }
+    };
+    // keep bits of a tile: each thread draws two Philox4x32-10 blocks, one
+    // per (query, 8-key group), and stores their 8 keep bits as one byte
+    auto make_keep = [&](int t, int buf) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int id = 2 * tid + u, ql = id >> 4, grp = id & 15;
+            uint32_t c[4] = {(uint32_t)((k0 >> 3) + grp), (uint32_t)(t * QT + ql), (uint32_t)bh, p.offset};
+            philox4x32_10(c, p.seed_lo, p.seed_hi);
+            uint32_t bits = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t r16 = (c[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                bits |= (r16 >= p.drop_t ? 1u : 0u) << e;
+            }
+            keep_s[buf][id] = (uint8_t)bits;
+        }
     };
     // lse (times log2 e) and D_i of a tile: threads 0..QT-1 and QT..2QT-1
     float sl = 0.0f;
@@ -178,6 +217,7 @@ __global__ __launch_bounds__(256, ATOMIC ? 1 : 2) void bwd_dkdv(BwdParams p) {
     if (t0 < nqt) {
         issue(t0, 0);
         fetch_stats(t0);
+        if constexpr (DROP) make_keep(t0, 0);
     }
     wait_vmcnt<0>();
     if (t0 < nqt) store_stats(0);
@@ -188,6 +228,7 @@ __global__ __launch_bounds__(256, ATOMIC ? 1 : 2) void bwd_dkdv(BwdParams p) {
         if (t + 1 < nqt) {
             issue(t + 1, buf ^ 1);
             fetch_stats(t + 1);
+            if constexpr (DROP) make_keep(t + 1, buf ^ 1);
         }
         const lds_t* tq = sm + KBLK + buf * 2 * TILE;
         const lds_t* tdo = tq + TILE;
@@ -202,8 +243,10 @@ __global__ __launch_bounds__(256, ATOMIC ? 1 : 2) void bwd_dkdv(BwdParams p) {
         for (int c = 0; c < DC; ++c)
             dp = mma<DT>(row_frag<D>(tdo, lq, 2 * c + g), vf[c], dp);
 
-        // P = exp2(s * scale*log2e - lse*log2e), dS = P (dP - D_i)
-        const bool need_mask = (q0 + QT > Sq) || (kw0 + 32 > Sk) || (CAUSAL && kw0 + 31 > q0 + diag);
+        // P = exp2(s * scale*log2e - lse*log2e), dS = P (Z c dP - D_i) and
+        // P Z c for dV, with Z c the dropout keep factor
+        const bool need_mask = MASK || (q0 + QT > Sq) || (kw0 + 32 > Sk) || (CAUSAL && kw0 + 31 > q0 + diag);
+        const int kl = 32 * w + lq;                    // key within the block
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             const int qr = 8 * a + 4 * g;
@@ -215,11 +258,19 @@ __global__ __launch_bounds__(256, ATOMIC ? 1 : 2) void bwd_dkdv(BwdParams p) {
                 float pv = __builtin_amdgcn_exp2f(s[r] * c2 - l4[e]);
                 if (need_mask) {
                     const int qi = q0 + qr + e;
-                    const bool vis = qi < Sq && key < Sk && (!CAUSAL || key <= qi + diag);
+                    bool vis = qi < Sq && key < Sk && (!CAUSAL || key <= qi + diag);
+                    if constexpr (MASK) vis = vis && msk_s[buf][(qr + e) * kKeyBlock + kl] != 0;
                     pv = vis ? pv : 0.0f;
                 }
-                s[r] = pv;
-                dp[r] = pv * (dp[r] - d4[e]);
+                if constexpr (DROP) {
+                    const float z = ((keep_s[buf][(qr + e) * (kKeyBlock / 8) + (kl >> 3)] >> (kl & 7)) & 1)
+                                        ? p.keep_scale : 0.0f;
+                    s[r] = pv * z;
+                    dp[r] = pv * (z * dp[r] - d4[e]);
+                } else {
+                    s[r] = pv;
+                    dp[r] = pv * (dp[r] - d4[e]);
+                }
             }
         }
 
@@ -291,7 +342,7 @@ __global__ __launch_bounds__(256, ATOMIC ? 1 : 2) void bwd_dkdv(BwdParams p) {
 
 // ---------------------------------------------------------------------------
 // dQ of one 128-query block (deterministic mode).
-template <int D, int DT, bool CAUSAL>
+template <int D, int DT, bool CAUSAL, bool MASK = false, bool DROP = false>
 __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
     constexpr int DC = D / 16, DB = D / 32;
     constexpr int KT = kKeyTile;
@@ -327,6 +378,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
     const float lse2 = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, qi * 4, 0, 0)) * LOG2E;
     const float dvl = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdv, qi * 4, 0, 0));
 
+    // Mask rows of this head (offsets beyond the buffer read as zero: hidden).
+    __amdgpu_buffer_rsrc_t rm = rl;
+    if constexpr (MASK) {
+        const int b_ = bh / p.H, h_ = bh - b_ * p.H;
+        rm = rsrc(p.mask + (int64_t)b_ * p.m_sb + (int64_t)h_ * p.m_sh,
+                  (uint64_t)(((int64_t)(Sq - 1) * p.m_ss + Sk + 3) & ~(int64_t)3));
+    }
+    // mask bytes of keys t*KT + 32rb + 8a + 4g .. +3 for this lane's query
+    uint32_t mk[2][4];
+    auto load_mask = [&](int t) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+                mk[rb][a] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+                    rm, (uint32_t)((int64_t)qi * p.m_ss + t * KT + 32 * rb + 8 * a + 4 * g), 0, 0);
+    };
+
     int nkt = (Sk + KT - 1) / KT;
     if (CAUSAL) nkt = min(nkt, max(0, (min(Sq, q0 + kQueryBlock) + diag + KT - 1) / KT));
 
@@ -346,13 +415,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
 #pragma unroll
     for (int b = 0; b < DB; ++b) dqa[b] = zero16();
 
-    if (nkt > 0) issue(0, 0);
+    if (nkt > 0) {
+        issue(0, 0);
+        if constexpr (MASK) load_mask(0);
+    }
     wait_vmcnt<0>();
     __syncthreads();
 
     for (int t = 0; t < nkt; ++t) {
         const int buf = t & 1;
-        if (t + 1 < nkt) issue(t + 1, buf ^ 1);
+        // with a mask the next tile's loads wait until this tile's mask bytes
+        // (loads the compiler waits for) have been used
+        if constexpr (!MASK)
+            if (t + 1 < nkt) issue(t + 1, buf ^ 1);
         const lds_t* tk = sm + buf * 2 * TILE;
         const lds_t* tv = tk + TILE;
         const int kt0 = t * KT;
@@ -373,7 +448,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
             }
         }
 
-        const bool need_mask = (kt0 + KT > Sk) || (qw0 + 32 > Sq) || (CAUSAL && kt0 + KT - 1 > qw0 + diag);
+        const bool need_mask = MASK || (kt0 + KT > Sk) || (qw0 + 32 > Sq) || (CAUSAL && kt0 + KT - 1 > qw0 + diag);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
@@ -381,10 +456,40 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
                 float pv = __builtin_amdgcn_exp2f(s[rb][r] * c2 - lse2);
                 if (need_mask) {
                     const int kj = kt0 + 32 * rb + 8 * (r >> 2) + 4 * g + (r & 3);
-                    const bool vis = qi < Sq && kj < Sk && (!CAUSAL || kj <= qi + diag);
+                    bool vis = qi < Sq && kj < Sk && (!CAUSAL || kj <= qi + diag);
+                    if constexpr (MASK) vis = vis && ((mk[rb][r >> 2] >> (8 * (r & 3))) & 0xffu) != 0;
                     pv = vis ? pv : 0.0f;
                 }
-                dp[rb][r] = pv * (dp[rb][r] - dvl);
+                s[rb][r] = pv;
+            }
+        }
+        if constexpr (MASK) {
+            if (t + 1 < nkt) {
+                issue(t + 1, buf ^ 1);
+                load_mask(t + 1);
+            }
+        }
+        // dS^T = P (Z c dP - D_i): keys kt0 + 32rb + 8a + 0..7 share one
+        // Philox block; this lane uses words 2g and 2g+1 (keys 8a + 4g + 0..3)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                float z[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+                if constexpr (DROP) {
+                    uint32_t c[4] = {(uint32_t)((kt0 + 32 * rb + 8 * a) >> 3), (uint32_t)qi, (uint32_t)bh, p.offset};
+                    philox4x32_10(c, p.seed_lo, p.seed_hi);
+                    const uint32_t w0 = g ? c[2] : c[0];
+                    const uint32_t w1 = g ? c[3] : c[1];
+                    const uint32_t r16[4] = {w0 & 0xffffu, w0 >> 16, w1 & 0xffffu, w1 >> 16};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) z[e] = r16[e] >= p.drop_t ? p.keep_scale : 0.0f;
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * a + e;
+                    dp[rb][r] = s[rb][r] * (z[e] * dp[rb][r] - dvl);
+                }
             }
         }
 
@@ -415,12 +520,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+template <int D, int DT, bool CAUSAL, bool MASK, bool DROP>
+static void run_masked(const BwdParams& p, hipStream_t st) {
+    hipLaunchKernelGGL((bwd_dkdv<D, DT, CAUSAL, false, MASK, DROP>), dim3((unsigned)(p.BH * p.nkb)), dim3(256), 0,
+                       st, p);
+    hipLaunchKernelGGL((bwd_dq<D, DT, CAUSAL, MASK, DROP>), dim3((unsigned)(p.BH * p.nqb)), dim3(256), 0, st, p);
+}
+
 template <int D, int DT, bool CAUSAL>
 static hipError_t run(const BwdParams& p, int deterministic, hipStream_t st) {
     const int64_t rows = (int64_t)p.BH * p.Sq;
     constexpr int RPB = 256 / (D / 8);
     if (rows > 0)
         hipLaunchKernelGGL((bwd_pre<D, DT>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st, p);
+    if (p.mask != nullptr || p.drop_t != 0) {
+        // masks and dropout run in the deterministic mode
+        if (p.mask != nullptr && p.drop_t != 0) run_masked<D, DT, CAUSAL, true, true>(p, st);
+        else if (p.mask != nullptr) run_masked<D, DT, CAUSAL, true, false>(p, st);
+        else run_masked<D, DT, CAUSAL, false, true>(p, st);
+        return hipGetLastError();
+    }
     if (p.Sk > 0) {
         const dim3 grid((unsigned)(p.BH * p.nkb));
         if (deterministic)

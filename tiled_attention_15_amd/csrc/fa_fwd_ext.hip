@@ -39,28 +39,6 @@ namespace ext {
 
 using namespace tile;
 
-// Philox4x32-10 block function: ten rounds of two 32x32->64 multiplications
-// (0xD2511F53, 0xCD9E8D57) whose high halves are XOR-ed with the other two
-// counter words and the key; the key is bumped by (0x9E3779B9, 0xBB67AE85)
-// between rounds.
-__device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
-#pragma unroll
-    for (int r = 0; r < 10; ++r) {
-        if (r > 0) {
-            k0 += 0x9E3779B9u;
-            k1 += 0xBB67AE85u;
-        }
-        const uint32_t hi0 = __umulhi(0xD2511F53u, c[0]), lo0 = 0xD2511F53u * c[0];
-        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c[2]), lo1 = 0xCD9E8D57u * c[2];
-        const uint32_t n0 = hi1 ^ c[1] ^ k0;
-        const uint32_t n2 = hi0 ^ c[3] ^ k1;
-        c[0] = n0;
-        c[1] = lo1;
-        c[2] = n2;
-        c[3] = lo0;
-    }
-}
-
 template <int D, int DT, bool CAUSAL, bool MASK, bool DROP>
 __global__ __launch_bounds__(256) void fwd_ext(ExtParams p) {
     constexpr int DC = D / 16, DB = D / 32;

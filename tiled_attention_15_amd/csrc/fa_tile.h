@@ -167,6 +167,35 @@ __device__ __forceinline__ void lds_dma16(i32x4 rsrc_words, uint32_t voffset, ui
                  :: "v"(voffset), "s"(rsrc_words), "s"(lds_addr) : "memory", "m0");
 }
 
+// As lds_dma16 with 4 bytes per lane (LDS address lds_addr + 4*l).
+__device__ __forceinline__ void lds_dma4(i32x4 rsrc_words, uint32_t voffset, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :: "v"(voffset), "s"(rsrc_words), "s"(lds_addr) : "memory", "m0");
+}
+
+// Philox4x32-10 block function (Salmon et al., "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011): ten rounds of two 32x32->64 multiplications
+// (0xD2511F53, 0xCD9E8D57) whose high halves are XOR-ed with the other two
+// counter words and the key; the key is bumped by (0x9E3779B9, 0xBB67AE85)
+// between rounds.
+__device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint32_t hi0 = __umulhi(0xD2511F53u, c[0]), lo0 = 0xD2511F53u * c[0];
+        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c[2]), lo1 = 0xCD9E8D57u * c[2];
+        const uint32_t n0 = hi1 ^ c[1] ^ k0;
+        const uint32_t n2 = hi0 ^ c[3] ^ k1;
+        c[0] = n0;
+        c[1] = lo1;
+        c[2] = n2;
+        c[3] = lo0;
+    }
+}
+
 // s_waitcnt vmcnt(N) alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
 // expcnt and lgkmcnt left at their maxima).
 template <int N>
