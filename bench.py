@@ -201,6 +201,45 @@ def backward_leg(w, steps, warmup):
             "ms_per_step": round(ms, 4), "value": round(tf, 3),
             "frac_of_mfma_peak": round(tf / MFMA_PEAK_TFLOPS, 4), "workspace_bytes": int(need)}
         del ws
+    # the backward of the masked / dropout forward: one [S, S] mask shared by
+    # all heads (90% kept) and dropout 0.1, deterministic mode
+    import numpy as np
+    ld = (w.S + 3) // 4 * 4
+    rng = np.random.default_rng(2400)
+    mask = torch.zeros((w.S, ld), dtype=torch.uint8)
+    mask[:, :w.S] = torch.from_numpy((rng.random((w.S, w.S)) < 0.9).astype(np.uint8))
+    md = mask.to(dev)
+    ms = (0, 0, ld)
+    lse_x = torch.empty_like(lse)
+    o_x = torch.empty_like(o)
+    st = fa.fa_fwd_ext(qd, kd, vd, o_x, lse_x, w.B, w.H, w.S, w.S, w.D, md, ms, 0.1, 1234, 0, w.scale, w.causal,
+                       code, stream)
+    if st != 0:
+        raise fa.FaError(st, "fa_fwd_ext")
+    need = fa.fa_bwd_workspace_bytes(w.B, w.H, w.S, w.D, True)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+    def step_x():
+        st = fa.fa_bwd_ext(qd, kd, vd, o_x, gd, lse_x, dq, dk, dv, w.B, w.H, w.S, w.S, w.D, md, ms, 0.1, 1234, 0,
+                           w.scale, w.causal, code, ws, need, stream)
+        if st != 0:
+            raise fa.FaError(st, "fa_bwd_ext")
+
+    for _ in range(warmup):
+        step_x()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        step_x()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_x = ev0.elapsed_time(ev1) / steps
+    tf = flops / (ms_x * 1e-3) / 1e12
+    out["mask_dropout"] = {"ms_per_step": round(ms_x, 4), "value": round(tf, 3),
+                           "frac_of_mfma_peak": round(tf / MFMA_PEAK_TFLOPS, 4),
+                           "mask": "one [S, S] uint8 mask shared by all heads, 90% kept", "dropout_p": 0.1}
     return out
 
 
