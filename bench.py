@@ -24,7 +24,7 @@ Prints ONE JSON line:
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--cpu-seconds T] [--no-cpu-baseline] [--no-naive]
-                       [--no-backward] [--no-ext]
+                       [--no-backward] [--no-ext] [--cold N]
 """
 import argparse
 import hashlib
@@ -72,7 +72,11 @@ def measured_traffic(workload_name):
     return float(m_val.group(1))
 
 
-def gpu_leg(w, steps, warmup):
+def gpu_leg(w, steps, warmup, cold=0):
+    """Times `steps` back-to-back launches (the headline figure); then 50
+    launches timed one by one (median and minimum); with cold > 0, that many
+    launches each preceded by a 512 MiB device write that evicts the caches."""
+    import statistics
     import torch
     import tiled_attention_15_amd as fa
 
@@ -107,7 +111,28 @@ def gpu_leg(w, steps, warmup):
     ev_ms = ev0.elapsed_time(ev1)
     if not torch.isfinite(o).all().item():
         raise RuntimeError("non-finite output in the benchmark run")
-    return ev_ms / steps, wall / steps * 1e3
+
+    def one_by_one(n, before=None):
+        times = []
+        for _ in range(n):
+            if before is not None:
+                before()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return {"median_ms": round(statistics.median(times), 6), "min_ms": round(min(times), 6), "launches": n}
+
+    stats = {"warm": one_by_one(50)}
+    if cold > 0:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        stats["cold"] = one_by_one(cold, lambda: scratch.fill_(1))
+        stats["cold"]["between_launches"] = "512 MiB device write"
+        del scratch
+    return ev_ms / steps, wall / steps * 1e3, stats
 
 
 def naive_leg(w, steps, warmup):
@@ -345,10 +370,21 @@ def cpu_leg(w, seconds):
         if t >= 0.6 * seconds or n >= total:
             break
         n = int(min(total, n * max(2.0, 0.9 * seconds / max(t, 1e-3))))
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": flops / t / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.max_threads(),
+        "cpu_model": cpu_model,
+        "wall_s": round(t, 3),
         "kind": "oracle",
         "sample": "%d of %d query rows (random, seed 12345) of %s, fp64 oracle row by row; "
                   "%.1f s wall; flops counted per row as 4*D*visible_keys" % (
@@ -370,6 +406,9 @@ def main():
                     help="skip the backward (gradient) timing")
     ap.add_argument("--no-ext", action="store_true",
                     help="skip the masked / dropout forward timing")
+    ap.add_argument("--cold", type=int, default=0,
+                    help="also time this many launches one by one with a 512 MiB cache-evicting write "
+                         "before each (cold caches)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of attention, time a plain device-to-device copy of this many "
                          "MiB (the reference kernel for scaling HBM byte counters)")
@@ -383,7 +422,7 @@ def main():
         print(json.dumps(copy_leg(a.copy_mib, a.steps, a.warmup)), flush=True)
         return
     w = WORKLOADS[a.workload]
-    ms, wall_ms = gpu_leg(w, a.steps, a.warmup)
+    ms, wall_ms, launch_stats = gpu_leg(w, a.steps, a.warmup, a.cold)
     tflops = w.flops() / (ms * 1e-3) / 1e12
     traffic = measured_traffic(w.name)
     out = {
@@ -405,6 +444,7 @@ def main():
         "pct_of_mfma_peak": round(100.0 * tflops / MFMA_PEAK_TFLOPS, 2),
         "hbm_gbs_algorithmic": round(w.bytes() / (ms * 1e-3) / 1e9, 2),
         "wall_ms_per_step": round(wall_ms, 6),
+        "launch_stats": launch_stats,
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
                      "traffic": traffic},
