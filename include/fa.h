@@ -299,6 +299,38 @@ int fa_bwd_ext(const void* q, const void* k, const void* v, const void* o, const
                uint32_t offset, float scale, int causal, int dtype, void* workspace,
                int64_t workspace_bytes, void* stream);
 
+/*
+ * fa_bwd_strided -- fa_bwd and fa_bwd_ext for strided tensors, e.g. the
+ * [B, S, H, D] layout of a fused projection, where the backward's inputs and
+ * gradients are views of larger buffers.  Same mathematics as fa_bwd (and, with
+ * a mask or dropout, as fa_bwd_ext).
+ *   strides  host array of 24 element strides: batch, head and row stride of
+ *            q, k, v, o, dout, dq, dk, dv, in that order (element (b, h, i, d)
+ *            of a tensor at b*s[0] + h*s[1] + i*s[2] + d; the head dimension
+ *            is contiguous).  Every stride is >= 0 and a multiple of 8; row
+ *            strides >= D and below 2^30.  Input strides may be 0 (one K
+ *            shared by all heads, say); dq, dk and dv must not map two
+ *            elements to one address (FA_ERR_STRIDE).
+ *   lse      contiguous [B, H, Sq] fp32, as for fa_bwd.
+ *   mask, mask_strides, dropout_p, seed, offset  as for fa_bwd_ext (mask
+ *            NULL and dropout_p 0 for the plain backward).  With a mask or
+ *            dropout the deterministic mode runs whatever `deterministic`
+ *            says.
+ *   workspace  at least fa_bwd_workspace_bytes(B, H, Sq, D, deterministic)
+ *            bytes; contiguous scratch as for fa_bwd.
+ * Aliasing: the byte range each tensor spans (from its first to past its
+ * last element) of dq, dk, dv and the workspace must not overlap one another
+ * or any input's (FA_ERR_ALIAS).  Per tensor and head, rows up to
+ * round_up(S, 128) + 128 are addressed with 32-bit offsets:
+ * ((round_up(S, 128) + 128) * row_stride + D) * 2 < 2^31.  D in {64, 128}.
+ * Returns an fa_status; nothing is enqueued on error.
+ */
+int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk, int D,
+                   const int64_t* strides, const uint8_t* mask, const int64_t* mask_strides,
+                   float dropout_p, uint64_t seed, uint32_t offset, float scale, int causal, int dtype,
+                   int deterministic, void* workspace, int64_t workspace_bytes, void* stream);
+
 /* Bytes of workspace fa_bwd needs (0 for an invalid shape): the row dot
  * products D_i, B*H*Sq fp32, plus in atomic mode (deterministic == 0) the
  * fp32 dq accumulator, B*H*Sq*D fp32; each part rounded up to 256 bytes. */

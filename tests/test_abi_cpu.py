@@ -305,3 +305,61 @@ def test_bwd_ext_rejects_bad_arguments(lib):
     assert call(ms=(0, 0, 1 << 25)) == 9                 # mask rows beyond 2^31 bytes
     assert call(dk=M) == 7                                # an output over the mask
     assert call(wsb=need - 1) == 2
+
+
+@fake_addresses
+def test_bwd_strided_validation(lib):
+    """fa_bwd_strided: layout rules per tensor (q, k, v, o, dout inputs; dq, dk,
+    dv outputs), the aliasing rule on byte spans, and valid [B, S, H, D]
+    layouts passing every check before the launch (shown by an unaligned
+    workspace being the first thing rejected)."""
+    B, H, Sq, Sk, D = 2, 4, 100, 300, 64
+    sz_q, sz_k = B * H * Sq * D * 2, B * H * Sk * D * 2
+    base = 0x40000000
+    addr = {}
+    for i, name in enumerate(("q", "k", "v", "o", "do", "dq", "dk", "dv")):
+        addr[name] = base + i * 0x1000000
+    W, M = base + 9 * 0x1000000, base + 10 * 0x1000000
+    assert sz_k < 0x1000000
+    bhsd_q, bhsd_k = (H * Sq * D, Sq * D, D), (H * Sk * D, Sk * D, D)
+    bshd_q, bshd_k = (Sq * H * D, D, H * D), (Sk * H * D, D, H * D)
+    need = fa.fa_bwd_workspace_bytes(B, H, Sq, D, 0)
+
+    def call(strides=None, det=0, mask=None, ms=None, p=0.0, **kw):
+        a = dict(addr, ws=W, wsb=need, D=D)
+        a.update(kw)
+        if strides is None:
+            strides = [s for t in (bhsd_q, bhsd_k, bhsd_k, bhsd_q, bhsd_q, bhsd_q, bhsd_k, bhsd_k) for s in t]
+        return fa.fa_bwd_strided(a["q"], a["k"], a["v"], a["o"], a["do"], L, a["dq"], a["dk"], a["dv"], B, H,
+                                 Sq, Sk, a["D"], strides, mask, ms, p, 1, 0, 0.125, 1, 1, det, a["ws"], a["wsb"],
+                                 None)
+
+    def with_tensor(t, st):
+        s = [x for u in (bhsd_q, bhsd_k, bhsd_k, bhsd_q, bhsd_q, bhsd_q, bhsd_k, bhsd_k) for x in u]
+        s[3 * t:3 * t + 3] = st
+        return s
+
+    assert call(ws=W + 4) == 4                                   # contiguous: every layout check passes
+    bshd = [x for t in (bshd_q, bshd_k, bshd_k, bshd_q, bshd_q, bshd_q, bshd_k, bshd_k) for x in t]
+    assert call(bshd, ws=W + 4) == 4                             # [B, S, H, D] views of every tensor
+    shared_kv = with_tensor(1, (Sk * D, 0, D))
+    assert call(shared_kv, ws=W + 4) == 4                        # one K shared by the heads of a batch
+    assert call(with_tensor(6, (Sk * D, 0, D))) == 8             # dk heads sharing memory
+    assert call(with_tensor(5, (H * Sq * D, Sq * D, D + 4))) == 8    # row stride not a multiple of 8
+    assert call(with_tensor(2, (H * Sk * D, Sk * D, 56))) == 8       # row stride < D
+    assert call(with_tensor(4, (-8, Sq * D, D))) == 8                # negative stride
+    assert call(with_tensor(7, (H * Sk * D, 64, D))) == 8            # dv rows run into the next head
+    assert call(with_tensor(0, (0, 0, 1 << 22))) == 2                # a head beyond 32-bit offsets
+    with pytest.raises(ValueError):
+        call(strides=[D] * 23)
+    # aliasing on the spans of strided tensors
+    wide = with_tensor(5, (H * Sq * D * 4, Sq * D * 4, D * 4))       # dq spread over 4x its size
+    assert call(wide, dk=addr["dq"] + sz_q + 64) == 7                 # dk inside dq's span
+    assert call(dq=addr["o"] + 128) == 7 and call(ws=addr["dv"]) == 7
+    assert call(mask=M, ms=(0, 0, 300), dq=M + 64) == 7               # output over the mask
+    # a mask or dropout takes the deterministic path, so its smaller workspace is enough
+    need_det = fa.fa_bwd_workspace_bytes(B, H, Sq, D, 1)
+    assert call(mask=M, ms=(0, 0, 300), wsb=need_det, ws=W + 4) == 4
+    assert call(p=0.2, wsb=need_det, ws=W + 4) == 4
+    assert call(wsb=need_det) == 2                                    # atomic mode needs the accumulator
+    assert call(p=1.0) == 9 and call(mask=M + 1, ms=(0, 0, 300)) == 9

@@ -143,3 +143,19 @@ def test_ext_workload_sampled_rows():
     st = parity.assert_parity(to64(o).reshape(-1, w.D)[rows], to64(lse).reshape(-1)[rows], o_ref, l_ref,
                               w.dtype, "ext workload rows")
     say("  ", st)
+
+
+def test_forward_ext_pads_unaligned_mask_rows():
+    """A bool mask with rows of Sk = 45 bytes (not 4-byte aligned) goes through
+    the binding (which copies it to aligned rows) and matches the oracle."""
+    B, H, Sq, Sk, D = 1, 2, 50, 45, 64
+    q, k, v = inputs(B, H, Sq, Sk, D, "f16", seed=2500)
+    m = torch.rand(Sq, Sk, generator=torch.Generator().manual_seed(2501)) < 0.7
+    o, lse = fa.forward_ext(q.to(DEV), k.to(DEV), v.to(DEV), causal=False, mask=m.to(DEV), dropout_p=0.2,
+                            seed=3, offset=1)
+    torch.cuda.synchronize()
+    mu = m.numpy().astype(np.uint8)
+    o_ref, l_ref = oracle.attention_fwd_ext(bits(q), bits(k), bits(v), scale=softmax_scale(D), causal=False,
+                                            dtype="f16", mask=mu, mask_strides=(0, 0, Sk), dropout_p=0.2, seed=3,
+                                            offset=1)
+    parity.assert_parity(to64(o), to64(lse), o_ref, l_ref, "f16", "unaligned mask rows")

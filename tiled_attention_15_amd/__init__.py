@@ -16,7 +16,7 @@ __all__ = ["FaError", "fa_fwd", "fa_fwd_strided", "fa_fwd_plan", "fa_naive_fwd",
            "fa_naive_workspace_bytes", "fa_status_string", "fa_version", "forward",
            "naive_forward", "library_path", "F16", "BF16", "STATUS", "fa_bwd",
            "fa_bwd_workspace_bytes", "backward", "fa_fwd_ext", "forward_ext", "fa_bwd_ext",
-           "backward_ext"]
+           "backward_ext", "fa_bwd_strided"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libfa_hip.so")
@@ -77,6 +77,9 @@ def _load():
     lib.fa_bwd_ext.argtypes = [vp] * 9 + [i] * 5 + [vp, i64p, f, ctypes.c_uint64, ctypes.c_uint32, f, i, i,
                                                      vp, ctypes.c_int64, vp]
     lib.fa_bwd_ext.restype = i
+    lib.fa_bwd_strided.argtypes = [vp] * 9 + [i] * 5 + [i64p, vp, i64p, f, ctypes.c_uint64, ctypes.c_uint32, f,
+                                                         i, i, i, vp, ctypes.c_int64, vp]
+    lib.fa_bwd_strided.restype = i
     _lib = lib
     return lib
 
@@ -163,6 +166,24 @@ def fa_bwd_ext(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, mask, mask_st
                               ctypes.c_uint32(int(offset) & 0xFFFFFFFF), ctypes.c_float(scale),
                               int(bool(causal)), int(dtype), _ptr(workspace), int(workspace_bytes),
                               _stream(stream))
+
+
+def fa_bwd_strided(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, strides, mask, mask_strides,
+                   dropout_p, seed, offset, scale, causal, dtype, deterministic, workspace, workspace_bytes,
+                   stream):
+    """C ABI fa_bwd_strided: strides is a sequence of 24 element strides
+    (batch, head, row of q, k, v, o, dout, dq, dk, dv)."""
+    st = [int(x) for x in strides]
+    if len(st) != 24:
+        raise ValueError("fa: fa_bwd_strided takes 24 strides")
+    ms = None if mask_strides is None else _strides3(mask_strides)
+    return _load().fa_bwd_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                                  _ptr(dk), _ptr(dv), int(B), int(H), int(Sq), int(Sk), int(D),
+                                  (ctypes.c_int64 * 24)(*st), _ptr(mask), ms, ctypes.c_float(dropout_p),
+                                  ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF),
+                                  ctypes.c_uint32(int(offset) & 0xFFFFFFFF), ctypes.c_float(scale),
+                                  int(bool(causal)), int(dtype), int(bool(deterministic)), _ptr(workspace),
+                                  int(workspace_bytes), _stream(stream))
 
 
 def fa_bwd_workspace_bytes(B, H, Sq, D, deterministic):
@@ -274,41 +295,89 @@ def naive_forward(q, k, v, causal=False, scale=None, workspace=None):
     return o, lse
 
 
-def backward(q, k, v, o, lse, dout, causal=False, scale=None, deterministic=True, workspace=None):
-    """Gradients (dq, dk, dv) of the forward on contiguous [B, H, Sq, D] q, o,
-    dout and [B, H, Sk, D] k, v GPU tensors, with o and lse from forward() on
-    the same inputs.  The workspace (allocated here with torch unless given as
-    a uint8 tensor of at least fa_bwd_workspace_bytes) holds the row dot
-    products and, when deterministic is False, the fp32 dq accumulator."""
+def _bwd_call(q, k, v, o, lse, dout, causal, scale, mask, dropout_p, seed, offset, deterministic, workspace,
+              grads):
     import torch
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
         raise ValueError("fa: q/o/dout [B, H, Sq, D] and k/v [B, H, Sk, D] expected")
     if q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
         raise ValueError("fa: q and k must share batch, heads and head dimension")
     ts = (q, k, v, o, dout)
-    if not all(t.is_contiguous() for t in ts) or not lse.is_contiguous():
-        raise ValueError("fa: the backward takes contiguous tensors")
+    if not all(t.is_cuda and t.device == q.device for t in ts + (lse,)):
+        raise ValueError("fa: tensors must be on one GPU")
     if not all(t.dtype == q.dtype for t in ts) or lse.dtype != torch.float32:
         raise ValueError("fa: q, k, v, o, dout share one dtype; lse is float32")
     B, H, Sq, D = q.shape
     Sk = k.shape[2]
+    if tuple(lse.shape) != (B, H, Sq) or not lse.is_contiguous():
+        raise ValueError("fa: lse must be contiguous float32 [B, H, Sq]")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    mask, mstrides = _mask_arg(mask, q, B, H, Sq, Sk)
+    if mask is not None or dropout_p != 0.0:
+        deterministic = True
+    if grads is None:
+        grads = tuple(t if t.stride(3) == 1 else torch.empty(t.shape, dtype=t.dtype, device=t.device)
+                      for t in (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)))
+    dq, dk, dv = grads
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if tuple(t.shape) != tuple(ref.shape) or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("fa: %s must match the shape and dtype of its input" % name)
+    for t in ts + (dq, dk, dv):
+        if t.stride(3) != 1 and D > 1:
+            raise ValueError("fa: every tensor must have a contiguous last dimension")
     need = fa_bwd_workspace_bytes(B, H, Sq, D, deterministic)
     if need <= 0:
         raise FaError(2, "fa_bwd_workspace_bytes")
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    dq = torch.empty_like(q)
-    dk = torch.empty_like(k)
-    dv = torch.empty_like(v)
+    strides = [s for t in ts + (dq, dk, dv) for s in t.stride()[:3]]
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream().cuda_stream
-    st = fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, scale, causal, _dtype_code(q),
-                deterministic, workspace, workspace.numel() * workspace.element_size(), stream)
+    st = fa_bwd_strided(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, strides, mask, mstrides, dropout_p,
+                        seed, offset, scale, causal, _dtype_code(q), deterministic, workspace,
+                        workspace.numel() * workspace.element_size(), stream)
     if st != 0:
-        raise FaError(st, "fa_bwd")
+        raise FaError(st, "fa_bwd_strided")
     return dq, dk, dv
+
+
+def backward(q, k, v, o, lse, dout, causal=False, scale=None, deterministic=True, workspace=None, grads=None):
+    """Gradients (dq, dk, dv) of the forward on GPU tensors q, o, dout
+    [B, H, Sq, D] and k, v [B, H, Sk, D], with o and lse from forward() on the
+    same inputs.  Any strides with a contiguous last dimension are accepted
+    (a [B, S, H, D] buffer viewed with transpose(1, 2), say).  The gradients
+    are new tensors laid out like their inputs (torch.empty_like), or the
+    given `grads` triple (any such strides).  The workspace (allocated here
+    with torch unless given as a uint8 tensor of at least
+    fa_bwd_workspace_bytes) holds the row dot products and, when
+    deterministic is False, the fp32 dq accumulator."""
+    return _bwd_call(q, k, v, o, lse, dout, causal, scale, None, 0.0, 0, 0, deterministic, workspace, grads)
+
+
+def _mask_arg(mask, q, B, H, Sq, Sk):
+    """(mask view, byte strides) for the C ABI from a uint8/bool GPU tensor
+    broadcastable to [B, H, Sq, Sk]: batch and head strides may be 0
+    (broadcast); when the rows do not start on 4-byte boundaries the mask is
+    copied once into a [.., Sq, Sk rounded up to 4] buffer."""
+    import torch
+    if mask is None:
+        return None, None
+    if mask.dtype == torch.bool:
+        mask = mask.view(torch.uint8)
+    if mask.dtype != torch.uint8 or mask.device != q.device:
+        raise ValueError("fa: mask must be a uint8/bool tensor on q's device")
+    while mask.dim() < 4:
+        mask = mask.unsqueeze(0)
+    m = mask.expand(B, H, Sq, Sk)
+    aligned = m.stride(3) == 1 and m.data_ptr() % 4 == 0 and all(st % 4 == 0 for st in m.stride()[:3])
+    if not aligned:
+        lead = [B if mask.shape[0] != 1 else 1, H if mask.shape[1] != 1 else 1]
+        ld = (Sk + 3) // 4 * 4
+        padded = torch.zeros(lead + [Sq, ld], dtype=torch.uint8, device=q.device)
+        padded[..., :Sk] = mask.expand(lead + [Sq, Sk])
+        m = padded[..., :Sk].expand(B, H, Sq, Sk)
+    return m, (m.stride(0), m.stride(1), m.stride(2))
 
 
 def forward_ext(q, k, v, causal=False, scale=None, mask=None, dropout_p=0.0, seed=0, offset=0):
@@ -330,16 +399,7 @@ def forward_ext(q, k, v, causal=False, scale=None, mask=None, dropout_p=0.0, see
     Sk = k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    strides = None
-    if mask is not None:
-        if mask.dtype == torch.bool:
-            mask = mask.view(torch.uint8)
-        if mask.dtype != torch.uint8 or mask.device != q.device:
-            raise ValueError("fa: mask must be a uint8/bool tensor on q's device")
-        mask = mask.expand(B, H, Sq, Sk)
-        if mask.stride(3) != 1:
-            raise ValueError("fa: the mask's last dimension must be contiguous")
-        strides = (mask.stride(0), mask.stride(1), mask.stride(2))
+    mask, strides = _mask_arg(mask, q, B, H, Sq, Sk)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     with torch.cuda.device(q.device):
@@ -352,39 +412,8 @@ def forward_ext(q, k, v, causal=False, scale=None, mask=None, dropout_p=0.0, see
 
 
 def backward_ext(q, k, v, o, lse, dout, causal=False, scale=None, mask=None, dropout_p=0.0, seed=0, offset=0,
-                 workspace=None):
+                 workspace=None, grads=None):
     """Gradients (dq, dk, dv) of forward_ext with the same mask, dropout_p,
-    seed and offset (o and lse from that call); contiguous tensors."""
-    import torch
-    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
-        raise ValueError("fa: q/o/dout [B, H, Sq, D] and k/v [B, H, Sk, D] expected")
-    if not all(t.is_contiguous() for t in (q, k, v, o, dout)) or not lse.is_contiguous():
-        raise ValueError("fa: the backward takes contiguous tensors")
-    B, H, Sq, D = q.shape
-    Sk = k.shape[2]
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    strides = None
-    if mask is not None:
-        if mask.dtype == torch.bool:
-            mask = mask.view(torch.uint8)
-        if mask.dtype != torch.uint8 or mask.device != q.device:
-            raise ValueError("fa: mask must be a uint8/bool tensor on q's device")
-        mask = mask.expand(B, H, Sq, Sk)
-        if mask.stride(3) != 1:
-            raise ValueError("fa: the mask's last dimension must be contiguous")
-        strides = (mask.stride(0), mask.stride(1), mask.stride(2))
-    need = fa_bwd_workspace_bytes(B, H, Sq, D, True)
-    if need <= 0:
-        raise FaError(2, "fa_bwd_workspace_bytes")
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    with torch.cuda.device(q.device):
-        stream = torch.cuda.current_stream().cuda_stream
-    st = fa_bwd_ext(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, mask, strides, dropout_p, seed, offset,
-                    scale, causal, _dtype_code(q), workspace, workspace.numel() * workspace.element_size(),
-                    stream)
-    if st != 0:
-        raise FaError(st, "fa_bwd_ext")
-    return dq, dk, dv
+    seed and offset (o and lse from that call); strides as for backward().
+    Always the deterministic kernels."""
+    return _bwd_call(q, k, v, o, lse, dout, causal, scale, mask, dropout_p, seed, offset, True, workspace, grads)

@@ -17,7 +17,7 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 2 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 3 * 100 + 0;
 
 int validate_shape(int B, int H, int Sq, int Sk, int D, int dtype) {
     if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return FA_ERR_SHAPE;
@@ -308,10 +308,10 @@ bool bwd_layout(int B, int H, int Sq, int D, int deterministic, BwdLayout& L) {
 
 // Offsets inside one head are 32-bit: tiles reach up to 128 rows past the
 // sequence end.
-bool bwd_span_ok(int S, int D) {
+bool bwd_span_ok(int S, int64_t row_stride, int D) {
     const int64_t rows = ((int64_t)S + fa::bwd::kKeyBlock - 1) / fa::bwd::kKeyBlock * fa::bwd::kKeyBlock +
                          fa::bwd::kKeyBlock;
-    return rows * D * 2 < (int64_t(1) << 31);
+    return (rows * row_stride + D) * 2 < (int64_t(1) << 31);
 }
 
 }  // namespace
@@ -322,7 +322,7 @@ int fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
     if (!q || !k || !v || !o) return FA_ERR_NULL;
     int st = validate_shape(B, H, Sq, Sk, D, dtype);
     if (st != FA_OK) return st;
-    if (!bwd_span_ok(std::max(Sq, Sk), D)) return FA_ERR_SHAPE;
+    if (!bwd_span_ok(std::max(Sq, Sk), D, D)) return FA_ERR_SHAPE;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse) & 15) return FA_ERR_ALIGN;
     if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_SCALE;
     if (!(dropout_p >= 0.0f) || !(dropout_p < 1.0f)) return FA_ERR_MASK_DROPOUT;
@@ -387,16 +387,25 @@ int64_t fa_bwd_workspace_bytes(int B, int H, int Sq, int D, int deterministic) {
     return bwd_layout(B, H, Sq, D, deterministic, L) ? L.total : 0;
 }
 
+// Shared body of the backward entry points.  `strides` holds batch, head
+// and row element strides of q, k, v, o, dout, dq, dk, dv in that order.
 static int bwd_common(const void* q, const void* k, const void* v, const void* o, const void* dout,
                       const float* lse, void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk, int D,
-                      const uint8_t* mask, const int64_t* mask_strides, float dropout_p, uint64_t seed,
-                      uint32_t offset, float scale, int causal, int dtype, int deterministic,
-                      void* workspace, int64_t workspace_bytes, void* stream) {
-    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
+                      const int64_t* strides, const uint8_t* mask, const int64_t* mask_strides,
+                      float dropout_p, uint64_t seed, uint32_t offset, float scale, int causal, int dtype,
+                      int deterministic, void* workspace, int64_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace || !strides) return FA_ERR_NULL;
     int st = validate_shape(B, H, Sq, Sk, D, dtype);
     if (st != FA_OK) return st;
     if (D == 256) return FA_ERR_UNSUPPORTED;
-    if (!bwd_span_ok(std::max(Sq, Sk), D)) return FA_ERR_SHAPE;
+    // tensor t has sequence length len[t] (Sq for q, o, dout, dq; Sk for k, v, dk, dv)
+    const int len[8] = {Sq, Sk, Sk, Sq, Sq, Sq, Sk, Sk};
+    for (int t = 0; t < 8; ++t) {
+        if ((st = check_strides(strides + 3 * t, D)) != FA_OK) return st;
+        if (!bwd_span_ok(len[t], strides[3 * t + 2], D)) return FA_ERR_SHAPE;
+    }
+    for (int t = 5; t < 8; ++t)
+        if (!no_self_overlap(strides + 3 * t, B, H, len[t], D)) return FA_ERR_STRIDE;
     BwdLayout L;
     if (!bwd_layout(B, H, Sq, D, deterministic, L) || workspace_bytes < L.total) return FA_ERR_SHAPE;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)lse |
@@ -418,16 +427,14 @@ static int bwd_common(const void* q, const void* k, const void* v, const void* o
         m1 = m0 + (uintptr_t)((int64_t)(B - 1) * mask_strides[0] + (int64_t)(H - 1) * mask_strides[1] +
                               (int64_t)(Sq - 1) * mask_strides[2] + Sk);
     }
-    const uintptr_t qb = (uintptr_t)((int64_t)B * H * Sq * D * 2);
-    const uintptr_t kb = (uintptr_t)((int64_t)B * H * Sk * D * 2);
+    const void* ptr[8] = {q, k, v, o, dout, dq, dk, dv};
+    uintptr_t sp[8][2];
+    for (int t = 0; t < 8; ++t) span(ptr[t], B, H, len[t], D, strides + 3 * t, sp[t][0], sp[t][1]);
     const uintptr_t lb = (uintptr_t)((int64_t)B * H * Sq * 4);
-    const uintptr_t in[7][2] = {{(uintptr_t)q, (uintptr_t)q + qb},       {(uintptr_t)k, (uintptr_t)k + kb},
-                                {(uintptr_t)v, (uintptr_t)v + kb},       {(uintptr_t)o, (uintptr_t)o + qb},
-                                {(uintptr_t)dout, (uintptr_t)dout + qb}, {(uintptr_t)lse, (uintptr_t)lse + lb},
+    const uintptr_t in[7][2] = {{sp[0][0], sp[0][1]}, {sp[1][0], sp[1][1]}, {sp[2][0], sp[2][1]},
+                                {sp[3][0], sp[3][1]}, {sp[4][0], sp[4][1]}, {(uintptr_t)lse, (uintptr_t)lse + lb},
                                 {m0, m1}};
-    const uintptr_t out[4][2] = {{(uintptr_t)dq, (uintptr_t)dq + qb},
-                                 {(uintptr_t)dk, (uintptr_t)dk + kb},
-                                 {(uintptr_t)dv, (uintptr_t)dv + kb},
+    const uintptr_t out[4][2] = {{sp[5][0], sp[5][1]}, {sp[6][0], sp[6][1]}, {sp[7][0], sp[7][1]},
                                  {(uintptr_t)workspace, (uintptr_t)workspace + (uintptr_t)L.total}};
     for (int i = 0; i < 4; ++i) {
         for (int j = 0; j < 7; ++j)
@@ -447,6 +454,8 @@ static int bwd_common(const void* q, const void* k, const void* v, const void* o
     p.dq = dq;
     p.dk = dk;
     p.dv = dv;
+    fa::bwd::Lay* lay[8] = {&p.Lq, &p.Lk, &p.Lv, &p.Lo, &p.Ldo, &p.Ldq, &p.Ldk, &p.Ldv};
+    for (int t = 0; t < 8; ++t) *lay[t] = {strides[3 * t], strides[3 * t + 1], (int)strides[3 * t + 2]};
     p.dvec = (float*)workspace;
     p.dqacc = deterministic ? nullptr : (float*)((char*)workspace + L.dvec_bytes);
     p.Sq = Sq;
@@ -469,11 +478,25 @@ static int bwd_common(const void* q, const void* k, const void* v, const void* o
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+namespace {
+// contiguous [B, H, S, D] strides for q, k, v, o, dout, dq, dk, dv
+void contiguous_bwd_strides(int H, int Sq, int Sk, int D, int64_t* st) {
+    const int len[8] = {Sq, Sk, Sk, Sq, Sq, Sq, Sk, Sk};
+    for (int t = 0; t < 8; ++t) {
+        st[3 * t] = (int64_t)H * len[t] * D;
+        st[3 * t + 1] = (int64_t)len[t] * D;
+        st[3 * t + 2] = D;
+    }
+}
+}  // namespace
+
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk, int D,
            float scale, int causal, int dtype, int deterministic, void* workspace,
            int64_t workspace_bytes, void* stream) {
-    return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, nullptr, nullptr, 0.0f, 0, 0,
+    int64_t st[24];
+    contiguous_bwd_strides(H, Sq, Sk, D, st);
+    return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, st, nullptr, nullptr, 0.0f, 0, 0,
                       scale, causal, dtype, deterministic, workspace, workspace_bytes, stream);
 }
 
@@ -482,8 +505,22 @@ int fa_bwd_ext(const void* q, const void* k, const void* v, const void* o, const
                const uint8_t* mask, const int64_t* mask_strides, float dropout_p, uint64_t seed,
                uint32_t offset, float scale, int causal, int dtype, void* workspace,
                int64_t workspace_bytes, void* stream) {
-    return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, mask, mask_strides, dropout_p, seed,
-                      offset, scale, causal, dtype, 1, workspace, workspace_bytes, stream);
+    int64_t st[24];
+    contiguous_bwd_strides(H, Sq, Sk, D, st);
+    return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, st, mask, mask_strides, dropout_p,
+                      seed, offset, scale, causal, dtype, 1, workspace, workspace_bytes, stream);
+}
+
+int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk, int D,
+                   const int64_t* strides, const uint8_t* mask, const int64_t* mask_strides,
+                   float dropout_p, uint64_t seed, uint32_t offset, float scale, int causal, int dtype,
+                   int deterministic, void* workspace, int64_t workspace_bytes, void* stream) {
+    // a mask or dropout always takes the deterministic kernels
+    if (mask || dropout_p != 0.0f) deterministic = 1;
+    return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, strides, mask, mask_strides,
+                      dropout_p, seed, offset, scale, causal, dtype, deterministic, workspace, workspace_bytes,
+                      stream);
 }
 
 }  // extern "C"

@@ -6,16 +6,24 @@
 namespace fa {
 namespace bwd {
 
+// Layout of one [B, H, S, D] tensor: element strides of batch, head and row
+// (the head dimension contiguous).
+struct Lay {
+    int64_t sb, sh;
+    int ss;
+};
+
 struct BwdParams {
-    const void* q;      // [BH, Sq, D] contiguous, input dtype
-    const void* k;      // [BH, Sk, D]
-    const void* v;      // [BH, Sk, D]
-    const void* o;      // [BH, Sq, D]  forward output
-    const void* dout;   // [BH, Sq, D]  gradient of the output
+    const void* q;      // [B, H, Sq, D] (layout Lq), input dtype
+    const void* k;      // [B, H, Sk, D]
+    const void* v;      // [B, H, Sk, D]
+    const void* o;      // [B, H, Sq, D]  forward output
+    const void* dout;   // [B, H, Sq, D]  gradient of the output
     const float* lse;   // [BH, Sq]     forward row log-sum-exp (natural log)
-    void* dq;           // [BH, Sq, D]
-    void* dk;           // [BH, Sk, D]
-    void* dv;           // [BH, Sk, D]
+    void* dq;           // [B, H, Sq, D]
+    void* dk;           // [B, H, Sk, D]
+    void* dv;           // [B, H, Sk, D]
+    Lay Lq, Lk, Lv, Lo, Ldo, Ldq, Ldk, Ldv;   // layouts of q, k, v, o, dout, dq, dk, dv
     float* dvec;        // workspace [BH, Sq]: rowsum(dout * o)
     float* dqacc;       // workspace [BH, Sq, D] fp32 (atomic mode), else null
     const uint8_t* mask;    // nonzero = keep, null = no mask (deterministic mode only)

@@ -46,6 +46,17 @@ namespace bwd {
 
 using namespace tile;
 
+// Start of head bh of a tensor with layout L (byte pointer), and the bytes one
+// head spans over `rows` rows (the last row's end).
+__device__ __forceinline__ const char* head_of(const void* base, const Lay& L, int bh, int H) {
+    const int b = bh / H, h = bh - b * H;
+    return (const char*)base + ((int64_t)b * L.sb + (int64_t)h * L.sh) * 2;
+}
+template <int D>
+__device__ __forceinline__ uint64_t head_bytes(const Lay& L, int rows) {
+    return (uint64_t)(((int64_t)(rows - 1) * L.ss + D) * 2);
+}
+
 // ---------------------------------------------------------------------------
 // D_i = sum_d dO_id O_id in fp32; in atomic mode also zero the dQ accumulator.
 template <int D, int DT>
@@ -57,9 +68,10 @@ __global__ __launch_bounds__(256) void bwd_pre(BwdParams p) {
     const int c = threadIdx.x % TPR;
     float acc = 0.0f;
     if (row < rows) {
-        const int64_t off = row * D + 8 * c;
-        const i32x4 a = *(const i32x4*)((const uint16_t*)p.o + off);
-        const i32x4 b = *(const i32x4*)((const uint16_t*)p.dout + off);
+        const int bh = (int)(row / p.Sq), qi = (int)(row - (int64_t)bh * p.Sq);
+        const int64_t off = row * D + 8 * c;   // the accumulator is contiguous
+        const i32x4 a = *(const i32x4*)(head_of(p.o, p.Lo, bh, p.H) + ((int64_t)qi * p.Lo.ss + 8 * c) * 2);
+        const i32x4 b = *(const i32x4*)(head_of(p.dout, p.Ldo, bh, p.H) + ((int64_t)qi * p.Ldo.ss + 8 * c) * 2);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             acc += half_f32<DT>(a[i], 0) * half_f32<DT>(b[i], 0) + half_f32<DT>(a[i], 1) * half_f32<DT>(b[i], 1);
@@ -75,10 +87,13 @@ __global__ __launch_bounds__(256) void bwd_pre(BwdParams p) {
 }
 
 // dQ = scale * accumulator, rounded to the dtype (atomic mode).
-template <int DT>
+template <int D, int DT>
 __global__ __launch_bounds__(256) void bwd_dq_convert(BwdParams p, int64_t n8) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n8) return;
+    const int64_t row = i / (D / 8);
+    const int c = (int)(i - row * (D / 8));
+    const int bh = (int)(row / p.Sq), qi = (int)(row - (int64_t)bh * p.Sq);
     const f32x4 a = *(const f32x4*)(p.dqacc + 8 * i);
     const f32x4 b = *(const f32x4*)(p.dqacc + 8 * i + 4);
     const float s = p.scale;
@@ -87,7 +102,7 @@ __global__ __launch_bounds__(256) void bwd_dq_convert(BwdParams p, int64_t n8) {
     w[1] = pack2<DT>(a[2] * s, a[3] * s);
     w[2] = pack2<DT>(b[0] * s, b[1] * s);
     w[3] = pack2<DT>(b[2] * s, b[3] * s);
-    *(i32x4*)((uint16_t*)p.dq + 8 * i) = w;
+    *(i32x4*)(const_cast<char*>(head_of(p.dq, p.Ldq, bh, p.H)) + ((int64_t)qi * p.Ldq.ss + 8 * c) * 2) = w;
 }
 
 // ---------------------------------------------------------------------------
@@ -124,26 +139,23 @@ __global__ __launch_bounds__(256, (ATOMIC || MASK || DROP) ? 1 : 2) void bwd_dkd
     const int Sq = p.Sq, Sk = p.Sk, diag = Sk - Sq;
     const int k0 = kb * kKeyBlock, kw0 = k0 + 32 * w;
 
-    const char* qh = (const char*)p.q + (int64_t)bh * Sq * D * 2;
-    const char* doh = (const char*)p.dout + (int64_t)bh * Sq * D * 2;
-    const char* kh = (const char*)p.k + (int64_t)bh * Sk * D * 2;
-    const i32x4 rq = rsrc_words(qh, (uint64_t)Sq * D * 2);
-    const i32x4 rdo = rsrc_words(doh, (uint64_t)Sq * D * 2);
-    const i32x4 rk = rsrc_words(kh, (uint64_t)Sk * D * 2);
-    const __amdgpu_buffer_rsrc_t rv = rsrc((const char*)p.v + (int64_t)bh * Sk * D * 2, (uint64_t)Sk * D * 2);
+    const i32x4 rq = rsrc_words(head_of(p.q, p.Lq, bh, p.H), head_bytes<D>(p.Lq, Sq));
+    const i32x4 rdo = rsrc_words(head_of(p.dout, p.Ldo, bh, p.H), head_bytes<D>(p.Ldo, Sq));
+    const i32x4 rk = rsrc_words(head_of(p.k, p.Lk, bh, p.H), head_bytes<D>(p.Lk, Sk));
+    const __amdgpu_buffer_rsrc_t rv = rsrc(head_of(p.v, p.Lv, bh, p.H), head_bytes<D>(p.Lv, Sk));
     const __amdgpu_buffer_rsrc_t rl = rsrc(p.lse + (int64_t)bh * Sq, (uint64_t)Sq * 4);
     const __amdgpu_buffer_rsrc_t rdv = rsrc(p.dvec + (int64_t)bh * Sq, (uint64_t)Sq * 4);
 
     const uint32_t lds0 = (uint32_t)(uintptr_t)sm;
     const lds_t* kblk = sm;
     // the key block (keys past Sk read as zero)
-    tile_dma<D, KN>(rk, k0, D, lds0, w, lane);
+    tile_dma<D, KN>(rk, k0, p.Lk.ss, lds0, w, lane);
     // V of this wave's 32 keys as B operands (key = column lq, 8 values of
     // the head dimension per k-step)
     i32x4 vf[DC];
 #pragma unroll
     for (int c = 0; c < DC; ++c)
-        vf[c] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((kw0 + lq) * D + 16 * c + 8 * g) * 2, 0, 0);
+        vf[c] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((kw0 + lq) * p.Lv.ss + 16 * c + 8 * g) * 2, 0, 0);
 
     const int nqt = (Sq + QT - 1) / QT;
     int t0 = 0;
@@ -160,8 +172,8 @@ __global__ __launch_bounds__(256, (ATOMIC || MASK || DROP) ? 1 : 2) void bwd_dkd
     const uint32_t msk0 = (uint32_t)(uintptr_t)(lds_t*)&msk_s[0][0];
     auto issue = [&](int t, int buf) {
         const uint32_t base = lds0 + (uint32_t)(KBLK + buf * 2 * TILE);
-        tile_dma<D, TN>(rq, t * QT, D, base, w, lane);
-        tile_dma<D, TN>(rdo, t * QT, D, base + TILE, w, lane);
+        tile_dma<D, TN>(rq, t * QT, p.Lq.ss, base, w, lane);
+        tile_dma<D, TN>(rdo, t * QT, p.Ldo.ss, base + TILE, w, lane);
         if constexpr (MASK) {
             // QT rows x 128 bytes, one dword per lane and instruction
 #pragma unroll
@@ -321,21 +333,22 @@ __global__ __launch_bounds__(256, (ATOMIC || MASK || DROP) ? 1 : 2) void bwd_dkd
     // dK^T (times scale) and dV^T: register r of block b holds head-dimension
     // index 32b + 8(r/4) + 4g + r%4 of key `key`: four consecutive values per
     // 8-byte store; stores past Sk are dropped by the buffer range.
-    const __amdgpu_buffer_rsrc_t wk = rsrc((char*)p.dk + (int64_t)bh * Sk * D * 2, (uint64_t)Sk * D * 2);
-    const __amdgpu_buffer_rsrc_t wv = rsrc((char*)p.dv + (int64_t)bh * Sk * D * 2, (uint64_t)Sk * D * 2);
+    const __amdgpu_buffer_rsrc_t wk = rsrc(head_of(p.dk, p.Ldk, bh, p.H), head_bytes<D>(p.Ldk, Sk));
+    const __amdgpu_buffer_rsrc_t wv = rsrc(head_of(p.dv, p.Ldv, bh, p.H), head_bytes<D>(p.Ldv, Sk));
     const float sc = p.scale;
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            const uint32_t off = (uint32_t)((key * D + 32 * b + 8 * a + 4 * g) * 2);
+            const uint32_t offk = (uint32_t)((key * p.Ldk.ss + 32 * b + 8 * a + 4 * g) * 2);
+            const uint32_t offv = (uint32_t)((key * p.Ldv.ss + 32 * b + 8 * a + 4 * g) * 2);
             i32x2 kv, vv;
             kv[0] = pack2<DT>(dka[b][4 * a] * sc, dka[b][4 * a + 1] * sc);
             kv[1] = pack2<DT>(dka[b][4 * a + 2] * sc, dka[b][4 * a + 3] * sc);
             vv[0] = pack2<DT>(dva[b][4 * a], dva[b][4 * a + 1]);
             vv[1] = pack2<DT>(dva[b][4 * a + 2], dva[b][4 * a + 3]);
-            __builtin_amdgcn_raw_buffer_store_b64(kv, wk, off, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b64(vv, wv, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(kv, wk, offk, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(vv, wv, offv, 0, 0);
         }
     }
 }
@@ -361,10 +374,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
     const int q0 = qb * kQueryBlock, qw0 = q0 + 32 * w;
     const int qi = qw0 + lq;
 
-    const __amdgpu_buffer_rsrc_t rq = rsrc((const char*)p.q + (int64_t)bh * Sq * D * 2, (uint64_t)Sq * D * 2);
-    const __amdgpu_buffer_rsrc_t rdo = rsrc((const char*)p.dout + (int64_t)bh * Sq * D * 2, (uint64_t)Sq * D * 2);
-    const i32x4 rk = rsrc_words((const char*)p.k + (int64_t)bh * Sk * D * 2, (uint64_t)Sk * D * 2);
-    const i32x4 rv = rsrc_words((const char*)p.v + (int64_t)bh * Sk * D * 2, (uint64_t)Sk * D * 2);
+    const __amdgpu_buffer_rsrc_t rq = rsrc(head_of(p.q, p.Lq, bh, p.H), head_bytes<D>(p.Lq, Sq));
+    const __amdgpu_buffer_rsrc_t rdo = rsrc(head_of(p.dout, p.Ldo, bh, p.H), head_bytes<D>(p.Ldo, Sq));
+    const i32x4 rk = rsrc_words(head_of(p.k, p.Lk, bh, p.H), head_bytes<D>(p.Lk, Sk));
+    const i32x4 rv = rsrc_words(head_of(p.v, p.Lv, bh, p.H), head_bytes<D>(p.Lv, Sk));
     const __amdgpu_buffer_rsrc_t rl = rsrc(p.lse + (int64_t)bh * Sq, (uint64_t)Sq * 4);
     const __amdgpu_buffer_rsrc_t rdv = rsrc(p.dvec + (int64_t)bh * Sq, (uint64_t)Sq * 4);
 
@@ -372,8 +385,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
     i32x4 qf[DC], df[DC];
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
-        qf[c] = __builtin_amdgcn_raw_buffer_load_b128(rq, (qi * D + 16 * c + 8 * g) * 2, 0, 0);
-        df[c] = __builtin_amdgcn_raw_buffer_load_b128(rdo, (qi * D + 16 * c + 8 * g) * 2, 0, 0);
+        qf[c] = __builtin_amdgcn_raw_buffer_load_b128(rq, (qi * p.Lq.ss + 16 * c + 8 * g) * 2, 0, 0);
+        df[c] = __builtin_amdgcn_raw_buffer_load_b128(rdo, (qi * p.Ldo.ss + 16 * c + 8 * g) * 2, 0, 0);
     }
     const float lse2 = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, qi * 4, 0, 0)) * LOG2E;
     const float dvl = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdv, qi * 4, 0, 0));
@@ -405,8 +418,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
     const uint32_t lds0 = (uint32_t)(uintptr_t)sm;
     auto issue = [&](int t, int buf) {
         const uint32_t base = lds0 + (uint32_t)(buf * 2 * TILE);
-        tile_dma<D, CPT>(rk, t * KT, D, base, w, lane);
-        tile_dma<D, CPT>(rv, t * KT, D, base + TILE, w, lane);
+        tile_dma<D, CPT>(rk, t * KT, p.Lk.ss, base, w, lane);
+        tile_dma<D, CPT>(rv, t * KT, p.Lv.ss, base + TILE, w, lane);
     };
 
     const TrLane tl = tr_lane(lane);
@@ -505,7 +518,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
         __syncthreads();
     }
 
-    const __amdgpu_buffer_rsrc_t wq = rsrc((char*)p.dq + (int64_t)bh * Sq * D * 2, (uint64_t)Sq * D * 2);
+    const __amdgpu_buffer_rsrc_t wq = rsrc(head_of(p.dq, p.Ldq, bh, p.H), head_bytes<D>(p.Ldq, Sq));
     const float sc = p.scale;
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
@@ -514,7 +527,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
             i32x2 v2;
             v2[0] = pack2<DT>(dqa[b][4 * a] * sc, dqa[b][4 * a + 1] * sc);
             v2[1] = pack2<DT>(dqa[b][4 * a + 2] * sc, dqa[b][4 * a + 3] * sc);
-            __builtin_amdgcn_raw_buffer_store_b64(v2, wq, (uint32_t)((qi * D + 32 * b + 8 * a + 4 * g) * 2), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(v2, wq, (uint32_t)((qi * p.Ldq.ss + 32 * b + 8 * a + 4 * g) * 2), 0, 0);
         }
     }
 }
@@ -552,7 +565,7 @@ static hipError_t run(const BwdParams& p, int deterministic, hipStream_t st) {
             hipLaunchKernelGGL((bwd_dq<D, DT, CAUSAL>), dim3((unsigned)(p.BH * p.nqb)), dim3(256), 0, st, p);
         } else {
             const int64_t n8 = rows * D / 8;
-            hipLaunchKernelGGL((bwd_dq_convert<DT>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, p, n8);
+            hipLaunchKernelGGL((bwd_dq_convert<D, DT>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, p, n8);
         }
     }
     return hipGetLastError();
