@@ -240,6 +240,27 @@ int fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
                float scale, int causal, int dtype, void* stream);
 
 /*
+ * fa_fwd_ext_strided -- fa_fwd_ext for strided q, k, v, o (a [B, S, H, D]
+ * buffer viewed as [B, H, S, D], a packed q/k/v projection, K and V shared by
+ * the heads of a batch).
+ *   strides  host array of 12 element strides: batch, head and row stride of
+ *            q, k, v, o in that order (element (b, h, i, d) of a tensor at
+ *            b*s[0] + h*s[1] + i*s[2] + d; the head dimension contiguous).
+ *            Every stride >= 0 and a multiple of 8; row strides >= D and below
+ *            2^30; o's strides must not map two elements to one address
+ *            (FA_ERR_STRIDE).  Per tensor and head,
+ *            ((round_up(S, 128) + 128) * row_stride + D) * 2 < 2^31 bytes.
+ * Aliasing: o's and lse's byte spans (first to past the last element) must
+ * not overlap any input's span or each other (FA_ERR_ALIAS).  Everything
+ * else as for fa_fwd_ext; fa_fwd_ext is this call with contiguous strides.
+ */
+int fa_fwd_ext_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int Sq, int Sk, int D, const int64_t* strides,
+                       const uint8_t* mask, const int64_t* mask_strides,
+                       float dropout_p, uint64_t seed, uint32_t offset,
+                       float scale, int causal, int dtype, void* stream);
+
+/*
  * fa_bwd -- gradients of the attention forward above: given dout = dL/dO,
  * writes dq = dL/dq, dk = dL/dk and dv = dL/dv.  The scores and
  * probabilities are recomputed from q, k and the forward's lse rather than

@@ -363,3 +363,37 @@ def test_bwd_strided_validation(lib):
     assert call(p=0.2, wsb=need_det, ws=W + 4) == 4
     assert call(wsb=need_det) == 2                                    # atomic mode needs the accumulator
     assert call(p=1.0) == 9 and call(mask=M + 1, ms=(0, 0, 300)) == 9
+
+
+@fake_addresses
+def test_fwd_ext_strided_validation(lib):
+    """fa_fwd_ext_strided: per-tensor layout rules, span aliasing, and valid
+    [B, S, H, D] / head-shared layouts passing every check (an unaligned lse
+    is then the first thing rejected)."""
+    B, H, Sq, Sk, D = 2, 4, 100, 300, 128
+    base = 0x40000000
+    Qa, Ka, Va, Oa, La, M = (base + i * 0x1000000 for i in range(6))
+    bhsd_q, bhsd_k = (H * Sq * D, Sq * D, D), (H * Sk * D, Sk * D, D)
+    bshd_q, bshd_k = (Sq * H * D, D, H * D), (Sk * H * D, D, H * D)
+
+    def call(st=(bhsd_q, bhsd_k, bhsd_k, bhsd_q), **kw):
+        a = dict(q=Qa, k=Ka, v=Va, o=Oa, lse=La, mask=None, ms=None, p=0.0, D=D)
+        a.update(kw)
+        flat = [x for t in st for x in t]
+        return fa.fa_fwd_ext_strided(a["q"], a["k"], a["v"], a["o"], a["lse"], B, H, Sq, Sk, a["D"], flat,
+                                     a["mask"], a["ms"], a["p"], 1, 0, 0.125, 1, 1, None)
+
+    assert call(lse=La + 4) == 4
+    assert call((bshd_q, bshd_k, bshd_k, bshd_q), lse=La + 4) == 4
+    assert call((bhsd_q, (Sk * D, 0, D), (Sk * D, 0, D), bhsd_q), lse=La + 4) == 4   # shared K, V
+    assert call((bhsd_q, bhsd_k, bhsd_k, (H * Sq * D, 0, D))) == 8                    # o heads collide
+    assert call((bhsd_q, (H * Sk * D, Sk * D, D + 8 - 4), bhsd_k, bhsd_q)) == 8        # row stride % 8
+    assert call((bhsd_q, bhsd_k, (0, 0, 120), bhsd_q)) == 8                           # row stride < D
+    assert call(((0, 0, 1 << 22), bhsd_k, bhsd_k, bhsd_q)) == 2                       # head span > 2^31 B
+    assert call(o=Qa + 256) == 7 and call(lse=Oa + 64) == 7
+    assert call(mask=M, ms=(0, 0, 300), o=M + 64) == 7
+    assert call(mask=M, ms=(0, 0, 298)) == 9 and call(p=1.0) == 9
+    assert call(D=96) == 3 and call(q=0) == 1
+    with pytest.raises(ValueError):
+        fa.fa_fwd_ext_strided(Qa, Ka, Va, Oa, La, B, H, Sq, Sk, D, [D] * 11, None, None, 0.0, 0, 0, 0.1, 0, 0,
+                              None)

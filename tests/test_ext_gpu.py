@@ -159,3 +159,47 @@ def test_forward_ext_pads_unaligned_mask_rows():
                                             dtype="f16", mask=mu, mask_strides=(0, 0, Sk), dropout_p=0.2, seed=3,
                                             offset=1)
     parity.assert_parity(to64(o), to64(lse), o_ref, l_ref, "f16", "unaligned mask rows")
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_forward_ext_strided_views(D):
+    """[B, S, H, D] views of q, k, v and of the output, with a mask and
+    dropout: bit for bit the contiguous call's result (same kernel, other
+    addresses), and within the oracle's bound."""
+    B, H, Sq, Sk, dtype = 2, 3, 140, 196, "bf16"
+    say("case ext strided", B, H, Sq, Sk, D)
+    q, k, v = inputs(B, H, Sq, Sk, D, dtype, seed=2600 + D)
+    mask, ms = make_mask("per_head", B, H, Sq, Sk, seed=2650 + D)
+    md = torch.from_numpy(mask).to(DEV)[..., :Sk]
+    kw = dict(causal=True, mask=md, dropout_p=0.2, seed=11, offset=2)
+    views = [t.to(DEV).transpose(1, 2).contiguous().transpose(1, 2) for t in (q, k, v)]
+    out = torch.empty((B, Sq, H, D), dtype=q.dtype, device=DEV).transpose(1, 2)
+    o, lse = fa.forward_ext(*views, out=out, **kw)
+    assert o.data_ptr() == out.data_ptr()
+    o_c, lse_c = fa.forward_ext(*(t.to(DEV) for t in (q, k, v)), **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_c) and torch.equal(lse, lse_c)
+    o_ref, l_ref = oracle.attention_fwd_ext(bits(q), bits(k), bits(v), scale=softmax_scale(D), causal=True,
+                                            dtype=dtype, mask=mask, mask_strides=ms, dropout_p=0.2, seed=11,
+                                            offset=2)
+    parity.assert_parity(to64(o), to64(lse), o_ref, l_ref, dtype, "ext strided D=%d" % D)
+
+
+def test_forward_ext_packed_qkv_shared_mask():
+    """q, k, v slices of one packed [B, S, 3, H, D] buffer, one [S, S] mask for
+    every batch and head, dropout: against the oracle."""
+    B, H, S, D, dtype = 1, 4, 230, 128, "f16"
+    say("case ext packed qkv", B, H, S, D)
+    q, k, v = inputs(B, H, S, S, D, dtype, seed=2700)
+    packed = torch.stack([t.transpose(1, 2) for t in (q, k, v)], dim=2).to(DEV)
+    qv, kv, vv = (packed[:, :, i].transpose(1, 2) for i in range(3))
+    m = (torch.rand(S, S, generator=torch.Generator().manual_seed(2701)) < 0.75)
+    o, lse = fa.forward_ext(qv, kv, vv, causal=False, mask=m.to(DEV), dropout_p=0.1, seed=5, offset=0)
+    torch.cuda.synchronize()
+    ld = (S + 3) // 4 * 4
+    mu = np.zeros((S, ld), np.uint8)
+    mu[:, :S] = m.numpy()
+    o_ref, l_ref = oracle.attention_fwd_ext(bits(q), bits(k), bits(v), scale=softmax_scale(D), causal=False,
+                                            dtype=dtype, mask=mu, mask_strides=(0, 0, ld), dropout_p=0.1, seed=5,
+                                            offset=0)
+    parity.assert_parity(to64(o), to64(lse), o_ref, l_ref, dtype, "ext packed qkv")

@@ -16,7 +16,7 @@ __all__ = ["FaError", "fa_fwd", "fa_fwd_strided", "fa_fwd_plan", "fa_naive_fwd",
            "fa_naive_workspace_bytes", "fa_status_string", "fa_version", "forward",
            "naive_forward", "library_path", "F16", "BF16", "STATUS", "fa_bwd",
            "fa_bwd_workspace_bytes", "backward", "fa_fwd_ext", "forward_ext", "fa_bwd_ext",
-           "backward_ext", "fa_bwd_strided"]
+           "backward_ext", "fa_bwd_strided", "fa_fwd_ext_strided"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libfa_hip.so")
@@ -80,6 +80,9 @@ def _load():
     lib.fa_bwd_strided.argtypes = [vp] * 9 + [i] * 5 + [i64p, vp, i64p, f, ctypes.c_uint64, ctypes.c_uint32, f,
                                                          i, i, i, vp, ctypes.c_int64, vp]
     lib.fa_bwd_strided.restype = i
+    lib.fa_fwd_ext_strided.argtypes = [vp] * 5 + [i] * 5 + [i64p, vp, i64p, f, ctypes.c_uint64, ctypes.c_uint32, f,
+                                                             i, i, vp]
+    lib.fa_fwd_ext_strided.restype = i
     _lib = lib
     return lib
 
@@ -154,6 +157,21 @@ def fa_fwd_ext(q, k, v, o, lse, B, H, Sq, Sk, D, mask, mask_strides, dropout_p, 
                               ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF),
                               ctypes.c_uint32(int(offset) & 0xFFFFFFFF), ctypes.c_float(scale),
                               int(bool(causal)), int(dtype), _stream(stream))
+
+
+def fa_fwd_ext_strided(q, k, v, o, lse, B, H, Sq, Sk, D, strides, mask, mask_strides, dropout_p, seed, offset,
+                       scale, causal, dtype, stream):
+    """C ABI fa_fwd_ext_strided: strides is a sequence of 12 element strides
+    (batch, head, row of q, k, v, o)."""
+    st = [int(x) for x in strides]
+    if len(st) != 12:
+        raise ValueError("fa: fa_fwd_ext_strided takes 12 strides")
+    ms = None if mask_strides is None else _strides3(mask_strides)
+    return _load().fa_fwd_ext_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(Sq),
+                                      int(Sk), int(D), (ctypes.c_int64 * 12)(*st), _ptr(mask), ms,
+                                      ctypes.c_float(dropout_p), ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF),
+                                      ctypes.c_uint32(int(offset) & 0xFFFFFFFF), ctypes.c_float(scale),
+                                      int(bool(causal)), int(dtype), _stream(stream))
 
 
 def fa_bwd_ext(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, mask, mask_strides, dropout_p, seed,
@@ -380,34 +398,41 @@ def _mask_arg(mask, q, B, H, Sq, Sk):
     return m, (m.stride(0), m.stride(1), m.stride(2))
 
 
-def forward_ext(q, k, v, causal=False, scale=None, mask=None, dropout_p=0.0, seed=0, offset=0):
-    """Forward with an explicit boolean mask and/or dropout on contiguous
-    [B, H, Sq, D] q and [B, H, Sk, D] k, v GPU tensors.  mask: a uint8 or bool
-    GPU tensor broadcastable to [B, H, Sq, Sk] (nonzero keeps), with a
-    contiguous last dimension and the other strides multiples of 4 bytes.
-    Returns (o, lse)."""
+def forward_ext(q, k, v, causal=False, scale=None, mask=None, dropout_p=0.0, seed=0, offset=0, out=None):
+    """Forward with an explicit boolean mask and/or dropout on GPU tensors
+    q [B, H, Sq, D] and k, v [B, H, Sk, D] with any strides whose last
+    dimension is contiguous.  mask: a uint8 or bool GPU tensor broadcastable
+    to [B, H, Sq, Sk] (nonzero keeps); rows that do not start on 4-byte
+    boundaries are copied to an aligned buffer.  Returns (o, lse): o
+    contiguous (or `out`, which may be strided) and lse float32 [B, H, Sq]."""
     import torch
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
         raise ValueError("fa: q [B, H, Sq, D] and k, v [B, H, Sk, D] expected")
     if q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
         raise ValueError("fa: q and k must share batch, heads and head dimension")
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("fa: the masked/dropout forward takes contiguous q, k, v")
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("fa: tensors must be on one GPU")
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("fa: q, k, v must share one dtype")
     B, H, Sq, D = q.shape
     Sk = k.shape[2]
+    o = out if out is not None else torch.empty((B, H, Sq, D), dtype=q.dtype, device=q.device)
+    if tuple(o.shape) != (B, H, Sq, D) or o.dtype != q.dtype or o.device != q.device:
+        raise ValueError("fa: out must be [B, H, Sq, D] of q's dtype")
+    for t in (q, k, v, o):
+        if t.stride(3) != 1 and D > 1:
+            raise ValueError("fa: every tensor must have a contiguous last dimension")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    mask, strides = _mask_arg(mask, q, B, H, Sq, Sk)
-    o = torch.empty_like(q)
+    mask, mstrides = _mask_arg(mask, q, B, H, Sq, Sk)
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    strides = [s for t in (q, k, v, o) for s in t.stride()[:3]]
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream().cuda_stream
-    st = fa_fwd_ext(q, k, v, o, lse, B, H, Sq, Sk, D, mask, strides, dropout_p, seed, offset,
-                    scale, causal, _dtype_code(q), stream)
+    st = fa_fwd_ext_strided(q, k, v, o, lse, B, H, Sq, Sk, D, strides, mask, mstrides, dropout_p, seed, offset,
+                            scale, causal, _dtype_code(q), stream)
     if st != 0:
-        raise FaError(st, "fa_fwd_ext")
+        raise FaError(st, "fa_fwd_ext_strided")
     return o, lse
 
 

@@ -316,13 +316,21 @@ bool bwd_span_ok(int S, int64_t row_stride, int D) {
 
 }  // namespace
 
-int fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Sq,
-               int Sk, int D, const uint8_t* mask, const int64_t* mask_strides, float dropout_p,
-               uint64_t seed, uint32_t offset, float scale, int causal, int dtype, void* stream) {
-    if (!q || !k || !v || !o) return FA_ERR_NULL;
+// Shared body of the masked / dropout forward entry points.  `strides`
+// holds batch, head and row element strides of q, k, v, o in that order.
+static int ext_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Sq,
+                      int Sk, int D, const int64_t* strides, const uint8_t* mask, const int64_t* mask_strides,
+                      float dropout_p, uint64_t seed, uint32_t offset, float scale, int causal, int dtype,
+                      void* stream) {
+    if (!q || !k || !v || !o || !strides) return FA_ERR_NULL;
     int st = validate_shape(B, H, Sq, Sk, D, dtype);
     if (st != FA_OK) return st;
-    if (!bwd_span_ok(std::max(Sq, Sk), D, D)) return FA_ERR_SHAPE;
+    const int len[4] = {Sq, Sk, Sk, Sq};
+    for (int t = 0; t < 4; ++t) {
+        if ((st = check_strides(strides + 3 * t, D)) != FA_OK) return st;
+        if (!bwd_span_ok(len[t], strides[3 * t + 2], D)) return FA_ERR_SHAPE;
+    }
+    if (!no_self_overlap(strides + 9, B, H, Sq, D)) return FA_ERR_STRIDE;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse) & 15) return FA_ERR_ALIGN;
     if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_SCALE;
     if (!(dropout_p >= 0.0f) || !(dropout_p < 1.0f)) return FA_ERR_MASK_DROPOUT;
@@ -339,12 +347,12 @@ int fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
         m1 = m0 + (uintptr_t)((int64_t)(B - 1) * mask_strides[0] + (int64_t)(H - 1) * mask_strides[1] +
                               (int64_t)(Sq - 1) * mask_strides[2] + Sk);
     }
-    const uintptr_t qb = (uintptr_t)((int64_t)B * H * Sq * D * 2);
-    const uintptr_t kb = (uintptr_t)((int64_t)B * H * Sk * D * 2);
+    const void* ptr[4] = {q, k, v, o};
+    uintptr_t sp[4][2];
+    for (int i = 0; i < 4; ++i) span(ptr[i], B, H, len[i], D, strides + 3 * i, sp[i][0], sp[i][1]);
     const uintptr_t lb = (uintptr_t)((int64_t)B * H * Sq * 4);
-    const uintptr_t in[4][2] = {{(uintptr_t)q, (uintptr_t)q + qb}, {(uintptr_t)k, (uintptr_t)k + kb},
-                                {(uintptr_t)v, (uintptr_t)v + kb}, {m0, m1}};
-    const uintptr_t out[2][2] = {{(uintptr_t)o, (uintptr_t)o + qb}, {(uintptr_t)lse, (uintptr_t)lse + (lse ? lb : 0)}};
+    const uintptr_t in[4][2] = {{sp[0][0], sp[0][1]}, {sp[1][0], sp[1][1]}, {sp[2][0], sp[2][1]}, {m0, m1}};
+    const uintptr_t out[2][2] = {{sp[3][0], sp[3][1]}, {(uintptr_t)lse, (uintptr_t)lse + (lse ? lb : 0)}};
     for (int i = 0; i < 2; ++i) {
         if (out[i][1] == out[i][0]) continue;
         for (int j = 0; j < 4; ++j)
@@ -358,11 +366,10 @@ int fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
     p.v = v;
     p.o = o;
     p.lse = lse;
-    p.q_sb = p.o_sb = (int64_t)H * Sq * D;
-    p.q_sh = p.o_sh = (int64_t)Sq * D;
-    p.k_sb = p.v_sb = (int64_t)H * Sk * D;
-    p.k_sh = p.v_sh = (int64_t)Sk * D;
-    p.q_ss = p.k_ss = p.v_ss = p.o_ss = D;
+    p.q_sb = strides[0], p.q_sh = strides[1], p.q_ss = (int)strides[2];
+    p.k_sb = strides[3], p.k_sh = strides[4], p.k_ss = (int)strides[5];
+    p.v_sb = strides[6], p.v_sh = strides[7], p.v_ss = (int)strides[8];
+    p.o_sb = strides[9], p.o_sh = strides[10], p.o_ss = (int)strides[11];
     p.mask = mask;
     p.m_sb = mask ? mask_strides[0] : 0;
     p.m_sh = mask ? mask_strides[1] : 0;
@@ -380,6 +387,24 @@ int fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
     p.offset = offset;
     const hipError_t err = fa::ext::launch_ext(p, D, dtype, causal != 0, (hipStream_t)stream);
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Sq,
+               int Sk, int D, const uint8_t* mask, const int64_t* mask_strides, float dropout_p,
+               uint64_t seed, uint32_t offset, float scale, int causal, int dtype, void* stream) {
+    // contiguous [B, H, S, D]
+    const int64_t st[12] = {(int64_t)H * Sq * D, (int64_t)Sq * D, D, (int64_t)H * Sk * D, (int64_t)Sk * D, D,
+                            (int64_t)H * Sk * D, (int64_t)Sk * D, D, (int64_t)H * Sq * D, (int64_t)Sq * D, D};
+    return ext_common(q, k, v, o, lse, B, H, Sq, Sk, D, st, mask, mask_strides, dropout_p, seed, offset, scale,
+                      causal, dtype, stream);
+}
+
+int fa_fwd_ext_strided(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                       int Sq, int Sk, int D, const int64_t* strides, const uint8_t* mask,
+                       const int64_t* mask_strides, float dropout_p, uint64_t seed, uint32_t offset,
+                       float scale, int causal, int dtype, void* stream) {
+    return ext_common(q, k, v, o, lse, B, H, Sq, Sk, D, strides, mask, mask_strides, dropout_p, seed, offset,
+                      scale, causal, dtype, stream);
 }
 
 int64_t fa_bwd_workspace_bytes(int B, int H, int Sq, int D, int deterministic) {
