@@ -55,7 +55,7 @@ typedef enum {
     FA_OK = 0,
     FA_ERR_NULL = 1,         /* q, k, v or o is NULL */
     FA_ERR_SHAPE = 2,        /* B, H or S < 1, or a size beyond the limits below */
-    FA_ERR_UNSUPPORTED = 3,  /* D not in {64, 128, 256} ({64, 128} for fa_bwd and
+    FA_ERR_UNSUPPORTED = 3,  /* D not in {64, 128, 256} ({64, 128} for
                                 fa_naive_fwd), or dtype not an fa_dtype */
     FA_ERR_ALIGN = 4,        /* a pointer is not 16-byte aligned */
     FA_ERR_SCALE = 5,        /* scale is not finite or not > 0 */
@@ -292,7 +292,8 @@ int fa_fwd_ext_strided(const void* q, const void* k, const void* v, void* o, flo
  *                    and no synchronisation inside.
  * All pointers 16-byte aligned.  Inputs may overlap each other; dq, dk, dv
  * and the workspace must not overlap each other or any input (FA_ERR_ALIAS).
- * Limits: D in {64, 128} (256: FA_ERR_UNSUPPORTED); (max(Sq, Sk) rounded up to 128, plus 128) * D * 2
+ * Limits: D in {64, 128, 256} (D = 256 runs with one workgroup per compute
+ * unit, the accumulators in the matrix-core registers); (max(Sq, Sk) rounded up to 128, plus 128) * D * 2
  * bytes below 2^31.  Returns FA_OK or a status as for fa_fwd; nothing is
  * enqueued on error.
  */
@@ -312,7 +313,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
  * fa_bwd_workspace_bytes(B, H, Sq, D, 1).  Arguments as for fa_bwd and
  * fa_fwd_ext (mask rows are read up to 31 rows past the last query, so
  * (Sq + 31) * mask row stride + Sk must stay below 2^31 bytes); the mask
- * must not overlap an output.  D in {64, 128}.
+ * must not overlap an output.  D in {64, 128, 256}.
  */
 int fa_bwd_ext(const void* q, const void* k, const void* v, const void* o, const void* dout,
                const float* lse, void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk, int D,
@@ -343,7 +344,7 @@ int fa_bwd_ext(const void* q, const void* k, const void* v, const void* o, const
  * last element) of dq, dk, dv and the workspace must not overlap one another
  * or any input's (FA_ERR_ALIAS).  Per tensor and head, rows up to
  * round_up(S, 128) + 128 are addressed with 32-bit offsets:
- * ((round_up(S, 128) + 128) * row_stride + D) * 2 < 2^31.  D in {64, 128}.
+ * ((round_up(S, 128) + 128) * row_stride + D) * 2 < 2^31.  D in {64, 128, 256}.
  * Returns an fa_status; nothing is enqueued on error.
  */
 int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -232,7 +232,10 @@ def test_bwd_rejects_bad_arguments(lib):
     assert bcall(Sq=0) == 2 and bcall(B=0) == 2
     assert bcall(wsb=need - 1) == 2
     assert bcall(D=96) == 3 and bcall(dtype=2) == 3
-    assert bcall(D=256) == 3                 # the backward stops at D = 128
+    assert bcall(D=512) == 3
+    need256 = fa.fa_bwd_workspace_bytes(B, H, Sq, 256, 0)
+    assert need256 == ((B * H * Sq * 4 + 255) // 256 * 256) + (B * H * Sq * 256 * 4 + 255) // 256 * 256
+    assert bcall(D=256, wsb=need256, ws=W + 4) == 4      # D = 256 passes the shape checks
     assert bcall(Sk=1 << 24, wsb=1 << 40) == 2          # head span beyond 32-bit offsets
     assert bcall(dk=DK + 8) == 4 and bcall(ws=W + 4) == 4
     assert bcall(scale=float("nan")) == 5 and bcall(scale=-1.0) == 5
@@ -299,7 +302,7 @@ def test_bwd_ext_rejects_bad_arguments(lib):
                              a["ws"], a["wsb"], None)
 
     assert call(ws=0) == 1 and call(dq=0) == 1
-    assert call(D=256) == 3
+    assert call(D=512) == 3
     assert call(p=1.0) == 9 and call(p=-0.5) == 9
     assert call(mask=M + 1) == 9 and call(ms=(0, 0, 100)) == 9 and call(ms=(0, 0, 126)) == 9
     assert call(ms=(0, 0, 1 << 25)) == 9                 # mask rows beyond 2^31 bytes

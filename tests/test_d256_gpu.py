@@ -1,5 +1,7 @@
-"""GPU parity of head dimension 256 (the general kernel behind fa_fwd,
-fa_fwd_strided and fa_fwd_ext at D = 256) against the fp64 oracle."""
+"""GPU parity of head dimension 256 against the fp64 oracle: the forward
+(the general kernel behind fa_fwd, fa_fwd_strided and fa_fwd_ext at
+D = 256) and the backward (fa_bwd / fa_bwd_strided kernels at D = 256, both
+dQ modes, with a mask and dropout, on strided views)."""
 import numpy as np
 import pytest
 import torch
@@ -74,8 +76,69 @@ def test_d256_mask_and_dropout():
     say("  ", parity.assert_parity(to64(o), to64(lse), o_ref, l_ref, "f16", "d256 mask dropout"))
 
 
-def test_d256_backward_is_rejected():
-    q = torch.zeros(1, 1, 16, D, dtype=torch.float16, device=DEV)
-    lse = torch.zeros(1, 1, 16, dtype=torch.float32, device=DEV)
-    with pytest.raises(fa.FaError):
-        fa.backward(q, q.clone(), q.clone(), q.clone(), lse, q.clone())
+def _grad_inputs(B, H, Sq, Sk, dtype, seed):
+    q, k, v = make_inputs(B, H, max(Sq, Sk), D, dtype, seed=seed, Sk=Sk)
+    q = q[:, :, :Sq].contiguous()
+    g, _, _ = make_inputs(B, H, Sq, D, dtype, seed=seed + 1000)
+    return q, k, v, g
+
+
+def _zero_scales(q, k, v, g):
+    mx = {n: float(t.abs().max()) for n, t in (("q", q), ("k", k), ("v", v), ("g", g))}
+    sc = softmax_scale(D)
+    return {"dq": sc * mx["g"] * mx["v"] * mx["k"], "dk": sc * mx["g"] * mx["v"] * mx["q"], "dv": mx["g"]}
+
+
+BWD_CASES = [
+    # (B, H, Sq, Sk, causal, dtype)
+    (1, 2, 64, 64, False, "f16"),
+    (1, 2, 257, 257, True, "bf16"),
+    (2, 1, 1, 1, True, "f16"),
+    (1, 1, 100, 300, True, "bf16"),
+    (1, 2, 300, 100, True, "f16"),
+    (2, 2, 130, 67, False, "bf16"),
+]
+
+
+@pytest.mark.parametrize("deterministic", [True, False], ids=["det", "atomic"])
+@pytest.mark.parametrize("case", BWD_CASES, ids=["%dx%dx%dx%d%s%s" % (c[0], c[1], c[2], c[3], "c" if c[4] else "n",
+                                                                      c[5]) for c in BWD_CASES])
+def test_d256_backward_matches_oracle(case, deterministic):
+    B, H, Sq, Sk, causal, dtype = case
+    say("case d256 bwd", case, "det" if deterministic else "atomic")
+    q, k, v, g = _grad_inputs(B, H, Sq, Sk, dtype, seed=2800 + Sq + 3 * Sk)
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
+    o, lse = fa.forward(qd, kd, vd, causal=causal)
+    grads = fa.backward(qd, kd, vd, o, lse, gd, causal=causal, deterministic=deterministic)
+    torch.cuda.synchronize()
+    refs = oracle.attention_bwd(bits(q), bits(k), bits(v), bits(g), scale=softmax_scale(D), causal=causal,
+                                dtype=dtype)
+    zs = _zero_scales(q, k, v, g)
+    for name, got, ref in zip(("dq", "dk", "dv"), grads, refs):
+        say("  ", name, parity.assert_grad_parity(to64(got), ref, dtype, "d256 %s %s" % (name, case),
+                                                  zero_scale=zs[name]))
+
+
+def test_d256_backward_mask_dropout_strided():
+    """Masked and dropout backward at D = 256 on [B, S, H, D] views: equal to
+    the contiguous call bit for bit, and within the oracle's bound."""
+    B, H, Sq, Sk, dtype = 1, 2, 150, 172, "bf16"
+    say("case d256 bwd mask dropout", B, H, Sq, Sk, dtype)
+    q, k, v, g = _grad_inputs(B, H, Sq, Sk, dtype, seed=2900)
+    rng = np.random.default_rng(2901)
+    mask = (rng.random((Sq, Sk)) < 0.8).astype(np.uint8)
+    kw = dict(causal=True, mask=torch.from_numpy(mask).to(DEV), dropout_p=0.1, seed=21, offset=3)
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
+    o, lse = fa.forward_ext(qd, kd, vd, **kw)
+    ref = fa.backward_ext(qd, kd, vd, o, lse, gd, **kw)
+    views = [t.transpose(1, 2).contiguous().transpose(1, 2) for t in (qd, kd, vd, o, gd)]
+    got = fa.backward_ext(views[0], views[1], views[2], views[3], lse, views[4], **kw)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        assert torch.equal(a, b), name
+    refs = oracle.attention_bwd_ext(bits(q), bits(k), bits(v), bits(g), scale=softmax_scale(D), causal=True,
+                                    dtype=dtype, mask=mask, mask_strides=(0, 0, Sk), dropout_p=0.1, seed=21,
+                                    offset=3)
+    zs = _zero_scales(q, k, v, g)
+    for name, a, r in zip(("dq", "dk", "dv"), got, refs):
+        say("  ", name, parity.assert_grad_parity(to64(a), r, dtype, "d256 ext %s" % name, zero_scale=zs[name]))

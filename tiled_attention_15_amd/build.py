@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa_hip.so")
 SOURCES = [os.path.join(CSRC, "fa_api.cpp"), os.path.join(CSRC, "fa_fwd_kernel.hip"),
            os.path.join(CSRC, "fa_naive.hip"), os.path.join(CSRC, "fa_bwd.hip"),
-           os.path.join(CSRC, "fa_fwd_ext.hip")]
+           os.path.join(CSRC, "fa_fwd_ext.hip"), os.path.join(CSRC, "fa_bwd256.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Kernels whose MFMA accumulators are also worked on by vector instructions:
 # the VGPR form of the MFMA instructions keeps those accumulators in VGPRs

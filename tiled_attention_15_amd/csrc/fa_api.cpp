@@ -298,7 +298,7 @@ struct BwdLayout {
 int64_t r256b(int64_t x) { return (x + 255) / 256 * 256; }
 
 bool bwd_layout(int B, int H, int Sq, int D, int deterministic, BwdLayout& L) {
-    if (B < 1 || H < 1 || Sq < 1 || (D != 64 && D != 128)) return false;
+    if (B < 1 || H < 1 || Sq < 1 || (D != 64 && D != 128 && D != 256)) return false;
     const int64_t rows = (int64_t)B * H * Sq;
     L.dvec_bytes = r256b(rows * 4);
     L.acc_bytes = deterministic ? 0 : r256b(rows * D * 4);
@@ -422,7 +422,6 @@ static int bwd_common(const void* q, const void* k, const void* v, const void* o
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace || !strides) return FA_ERR_NULL;
     int st = validate_shape(B, H, Sq, Sk, D, dtype);
     if (st != FA_OK) return st;
-    if (D == 256) return FA_ERR_UNSUPPORTED;
     // tensor t has sequence length len[t] (Sq for q, o, dout, dq; Sk for k, v, dk, dv)
     const int len[8] = {Sq, Sk, Sk, Sq, Sq, Sq, Sk, Sk};
     for (int t = 0; t < 8; ++t) {

@@ -49,6 +49,8 @@ constexpr int kKeyTile = 64;     // keys per step of the dQ kernel
 // dQ kernel (deterministic) or the conversion of the accumulator (atomic).
 hipError_t launch_bwd(const BwdParams& p, int D, int dtype, int causal, int deterministic,
                       hipStream_t stream);
+// The same at D = 256 (fa_bwd256.hip).
+hipError_t launch_bwd256(const BwdParams& p, int dtype, int causal, int deterministic, hipStream_t stream);
 
 }  // namespace bwd
 }  // namespace fa

@@ -1,0 +1,545 @@
+// fa_bwd_kernels.h -- the attention backward kernels (templates), shared by
+// fa_bwd.hip (head dimensions 64 and 128, built with the VGPR form of the
+// MFMA instructions) and fa_bwd256.hip (head dimension 256: one wave per
+// SIMD, the dK/dV or dQ accumulators in AGPRs).  The mathematics and the
+// kernel structure are described at the top of fa_bwd.hip.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_bwd.h"
+#include "fa_tile.h"
+
+namespace fa {
+namespace bwd {
+
+using namespace tile;
+
+// Start of head bh of a tensor with layout L (byte pointer), and the bytes one
+// head spans over `rows` rows (the last row's end).
+__device__ __forceinline__ const char* head_of(const void* base, const Lay& L, int bh, int H) {
+    const int b = bh / H, h = bh - b * H;
+    return (const char*)base + ((int64_t)b * L.sb + (int64_t)h * L.sh) * 2;
+}
+template <int D>
+__device__ __forceinline__ uint64_t head_bytes(const Lay& L, int rows) {
+    return (uint64_t)(((int64_t)(rows - 1) * L.ss + D) * 2);
+}
+
+// ---------------------------------------------------------------------------
+// D_i = sum_d dO_id O_id in fp32; in atomic mode also zero the dQ accumulator.
+template <int D, int DT>
+__global__ __launch_bounds__(256) void bwd_pre(BwdParams p) {
+    constexpr int TPR = D / 8;            // threads per row (8 values each)
+    constexpr int RPB = 256 / TPR;        // rows per workgroup
+    const int64_t rows = (int64_t)p.BH * p.Sq;
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+    const int c = threadIdx.x % TPR;
+    float acc = 0.0f;
+    if (row < rows) {
+        const int bh = (int)(row / p.Sq), qi = (int)(row - (int64_t)bh * p.Sq);
+        const int64_t off = row * D + 8 * c;   // the accumulator is contiguous
+        const i32x4 a = *(const i32x4*)(head_of(p.o, p.Lo, bh, p.H) + ((int64_t)qi * p.Lo.ss + 8 * c) * 2);
+        const i32x4 b = *(const i32x4*)(head_of(p.dout, p.Ldo, bh, p.H) + ((int64_t)qi * p.Ldo.ss + 8 * c) * 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc += half_f32<DT>(a[i], 0) * half_f32<DT>(b[i], 0) + half_f32<DT>(a[i], 1) * half_f32<DT>(b[i], 1);
+        if (p.dqacc) {
+            const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+            *(f32x4*)(p.dqacc + off) = z;
+            *(f32x4*)(p.dqacc + off + 4) = z;
+        }
+    }
+#pragma unroll
+    for (int o = TPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    if (row < rows && c == 0) p.dvec[row] = acc;
+}
+
+// dQ = scale * accumulator, rounded to the dtype (atomic mode).
+template <int D, int DT>
+__global__ __launch_bounds__(256) void bwd_dq_convert(BwdParams p, int64_t n8) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n8) return;
+    const int64_t row = i / (D / 8);
+    const int c = (int)(i - row * (D / 8));
+    const int bh = (int)(row / p.Sq), qi = (int)(row - (int64_t)bh * p.Sq);
+    const f32x4 a = *(const f32x4*)(p.dqacc + 8 * i);
+    const f32x4 b = *(const f32x4*)(p.dqacc + 8 * i + 4);
+    const float s = p.scale;
+    i32x4 w;
+    w[0] = pack2<DT>(a[0] * s, a[1] * s);
+    w[1] = pack2<DT>(a[2] * s, a[3] * s);
+    w[2] = pack2<DT>(b[0] * s, b[1] * s);
+    w[3] = pack2<DT>(b[2] * s, b[3] * s);
+    *(i32x4*)(const_cast<char*>(head_of(p.dq, p.Ldq, bh, p.H)) + ((int64_t)qi * p.Ldq.ss + 8 * c) * 2) = w;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV (and in atomic mode the dQ contributions) of one 128-key block.
+// Sized for two workgroups per CU at D <= 128 (two waves per SIMD, <= 256
+// registers per lane; one with a mask, dropout or the atomic dQ, and at
+// D = 256, where the accumulators fill the 256 AGPRs): the key block sits in LDS (K fragments are read from there at each
+// use) while V's fragments and the dK^T, dV^T accumulators stay in registers;
+// 32-query tiles of Q and dO go straight from global memory into LDS.
+template <int D, int DT, bool CAUSAL, bool ATOMIC, bool MASK = false, bool DROP = false>
+__global__ __launch_bounds__(256, (ATOMIC || MASK || DROP || D > 128) ? 1 : 2) void bwd_dkdv(BwdParams p) {
+    constexpr int DC = D / 16;                         // k-steps over the head dimension
+    constexpr int DB = D / 32;                         // 32-column blocks of the head dimension
+    constexpr int QT = kQueryTile;
+    constexpr int TILE = QT * D * 2;                   // bytes of one Q or dO tile
+    constexpr int TN = QT * D / 8 / 256;               // direct loads per thread per tile
+    constexpr int KBLK = kKeyBlock * D * 2;            // bytes of the key block
+    constexpr int KN = kKeyBlock * D / 8 / 256;        // direct loads per thread for it
+    constexpr int DSB = ATOMIC ? kKeyBlock * QT * 2 : 0;
+    static_assert(TN >= 1 && KN >= 1, "tile must split over the threads");
+
+    __shared__ __attribute__((aligned(16))) char smem[KBLK + 4 * TILE + DSB];
+    __shared__ __attribute__((aligned(16))) float lse_s[2][QT];
+    __shared__ __attribute__((aligned(16))) float dv_s[2][QT];
+    // mask bytes of a tile, [query][key of the block] (with a mask), and the
+    // keep bits of a tile, [query][8-key group] one bit per key (with dropout)
+    __shared__ __attribute__((aligned(16))) uint8_t msk_s[2][MASK ? QT * kKeyBlock : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t keep_s[2][DROP ? QT * kKeyBlock / 8 : 16];
+    lds_t* const sm = (lds_t*)smem;
+
+    const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, g = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int bh, kb;
+    block_order(blockIdx.x, p.nkb, p.BH, false, bh, kb);
+    const int Sq = p.Sq, Sk = p.Sk, diag = Sk - Sq;
+    const int k0 = kb * kKeyBlock, kw0 = k0 + 32 * w;
+
+    const i32x4 rq = rsrc_words(head_of(p.q, p.Lq, bh, p.H), head_bytes<D>(p.Lq, Sq));
+    const i32x4 rdo = rsrc_words(head_of(p.dout, p.Ldo, bh, p.H), head_bytes<D>(p.Ldo, Sq));
+    const i32x4 rk = rsrc_words(head_of(p.k, p.Lk, bh, p.H), head_bytes<D>(p.Lk, Sk));
+    const __amdgpu_buffer_rsrc_t rv = rsrc(head_of(p.v, p.Lv, bh, p.H), head_bytes<D>(p.Lv, Sk));
+    const __amdgpu_buffer_rsrc_t rl = rsrc(p.lse + (int64_t)bh * Sq, (uint64_t)Sq * 4);
+    const __amdgpu_buffer_rsrc_t rdv = rsrc(p.dvec + (int64_t)bh * Sq, (uint64_t)Sq * 4);
+
+    const uint32_t lds0 = (uint32_t)(uintptr_t)sm;
+    const lds_t* kblk = sm;
+    // the key block (keys past Sk read as zero)
+    tile_dma<D, KN>(rk, k0, p.Lk.ss, lds0, w, lane);
+    // V of this wave's 32 keys as B operands (key = column lq, 8 values of
+    // the head dimension per k-step)
+    i32x4 vf[DC];
+#pragma unroll
+    for (int c = 0; c < DC; ++c)
+        vf[c] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((kw0 + lq) * p.Lv.ss + 16 * c + 8 * g) * 2, 0, 0);
+
+    const int nqt = (Sq + QT - 1) / QT;
+    int t0 = 0;
+    if (CAUSAL) t0 = max(0, k0 - diag) / QT;
+
+    // Mask rows of this head: a buffer over [first row, last row + Sk)
+    // rounded up to whole dwords; offsets beyond it read as zero (hidden).
+    i32x4 rm = rq;
+    if constexpr (MASK) {
+        const int b_ = bh / p.H, h_ = bh - b_ * p.H;
+        rm = rsrc_words(p.mask + (int64_t)b_ * p.m_sb + (int64_t)h_ * p.m_sh,
+                        (uint64_t)(((int64_t)(Sq - 1) * p.m_ss + Sk + 3) & ~(int64_t)3));
+    }
+    const uint32_t msk0 = (uint32_t)(uintptr_t)(lds_t*)&msk_s[0][0];
+    auto issue = [&](int t, int buf) {
+        const uint32_t base = lds0 + (uint32_t)(KBLK + buf * 2 * TILE);
+        tile_dma<D, TN>(rq, t * QT, p.Lq.ss, base, w, lane);
+        tile_dma<D, TN>(rdo, t * QT, p.Ldo.ss, base + TILE, w, lane);
+        if constexpr (MASK) {
+            // QT rows x 128 bytes, one dword per lane and instruction
+#pragma unroll
+            for (int i = 0; i < QT * kKeyBlock / 4 / 256; ++i) {
+                const int c = (4 * i + w) * 64 + lane, r = c / (kKeyBlock / 4), dw = c % (kKeyBlock / 4);
+                lds_dma4(rm, (uint32_t)((int64_t)(t * QT + r) * p.m_ss + k0 + 4 * dw),
+                         msk0 + (uint32_t)(buf * QT * kKeyBlock + (4 * i + w) * 256));
+            }
+        }
+    };
+    // keep bits of a tile: each thread draws two Philox4x32-10 blocks, one
+    // per (query, 8-key group), and stores their 8 keep bits as one byte
+    auto make_keep = [&](int t, int buf) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int id = 2 * tid + u, ql = id >> 4, grp = id & 15;
+            uint32_t c[4] = {(uint32_t)((k0 >> 3) + grp), (uint32_t)(t * QT + ql), (uint32_t)bh, p.offset};
+            philox4x32_10(c, p.seed_lo, p.seed_hi);
+            uint32_t bits = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t r16 = (c[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                bits |= (r16 >= p.drop_t ? 1u : 0u) << e;
+            }
+            keep_s[buf][id] = (uint8_t)bits;
+        }
+    };
+    // lse (times log2 e) and D_i of a tile: threads 0..QT-1 and QT..2QT-1
+    float sl = 0.0f;
+    auto fetch_stats = [&](int t) {
+        if (tid < QT)
+            sl = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, (t * QT + tid) * 4, 0, 0));
+        else if (tid < 2 * QT)
+            sl = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdv, (t * QT + tid - QT) * 4, 0, 0));
+    };
+    auto store_stats = [&](int buf) {
+        if (tid < QT)
+            lse_s[buf][tid] = sl * LOG2E;
+        else if (tid < 2 * QT)
+            dv_s[buf][tid - QT] = sl;
+    };
+
+    const TrLane tl = tr_lane(lane);
+    const float c2 = p.scale_log2e;
+    const int key = kw0 + lq;
+    f32x16 dva[DB], dka[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+        dva[b] = zero16();
+        dka[b] = zero16();
+    }
+
+    if (t0 < nqt) {
+        issue(t0, 0);
+        fetch_stats(t0);
+        if constexpr (DROP) make_keep(t0, 0);
+    }
+    wait_vmcnt<0>();
+    if (t0 < nqt) store_stats(0);
+    __syncthreads();
+
+    for (int t = t0; t < nqt; ++t) {
+        const int buf = (t - t0) & 1;
+        if (t + 1 < nqt) {
+            issue(t + 1, buf ^ 1);
+            fetch_stats(t + 1);
+            if constexpr (DROP) make_keep(t + 1, buf ^ 1);
+        }
+        const lds_t* tq = sm + KBLK + buf * 2 * TILE;
+        const lds_t* tdo = tq + TILE;
+        const int q0 = t * QT;
+
+        // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
+        f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+        for (int c = 0; c < DC; ++c)
+            s = mma<DT>(row_frag<D>(tq, lq, 2 * c + g), row_frag<D>(kblk, 32 * w + lq, 2 * c + g), s);
+#pragma unroll
+        for (int c = 0; c < DC; ++c)
+            dp = mma<DT>(row_frag<D>(tdo, lq, 2 * c + g), vf[c], dp);
+
+        // P = exp2(s * scale*log2e - lse*log2e), dS = P (Z c dP - D_i) and
+        // P Z c for dV, with Z c the dropout keep factor
+        const bool need_mask = MASK || (q0 + QT > Sq) || (kw0 + 32 > Sk) || (CAUSAL && kw0 + 31 > q0 + diag);
+        const int kl = 32 * w + lq;                    // key within the block
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const int qr = 8 * a + 4 * g;
+            const f32x4 l4 = *(const f32x4*)&lse_s[buf][qr];
+            const f32x4 d4 = *(const f32x4*)&dv_s[buf][qr];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * a + e;
+                float pv = __builtin_amdgcn_exp2f(s[r] * c2 - l4[e]);
+                if (need_mask) {
+                    const int qi = q0 + qr + e;
+                    bool vis = qi < Sq && key < Sk && (!CAUSAL || key <= qi + diag);
+                    if constexpr (MASK) vis = vis && msk_s[buf][(qr + e) * kKeyBlock + kl] != 0;
+                    pv = vis ? pv : 0.0f;
+                }
+                if constexpr (DROP) {
+                    const float z = ((keep_s[buf][(qr + e) * (kKeyBlock / 8) + (kl >> 3)] >> (kl & 7)) & 1)
+                                        ? p.keep_scale : 0.0f;
+                    s[r] = pv * z;
+                    dp[r] = pv * (z * dp[r] - d4[e]);
+                } else {
+                    s[r] = pv;
+                    dp[r] = pv * (dp[r] - d4[e]);
+                }
+            }
+        }
+
+        // dV^T += dO^T P, dK^T += Q^T dS  (rows: head dimension, columns: keys)
+#pragma unroll
+        for (int st = 0; st < QT / 16; ++st) {
+            const i32x4 pa = acc_frag<DT>(s, st);
+            const i32x4 da = acc_frag<DT>(dp, st);
+#pragma unroll
+            for (int b = 0; b < DB; ++b) {
+                dva[b] = mma<DT>(tr_frag<D>(tdo, st, b, tl), pa, dva[b]);
+                dka[b] = mma<DT>(tr_frag<D>(tq, st, b, tl), da, dka[b]);
+            }
+        }
+
+        if constexpr (ATOMIC) {
+            // dS^T of this wave's keys into LDS as [key][query], then
+            // dQ[q][d] += sum over the block's 128 keys of dS[q][key] K[key][d]
+            lds_t* dst = sm + KBLK + 4 * TILE;
+            const int kr = 32 * w + lq;
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                i32x2 v2;
+                v2[0] = pack2<DT>(dp[4 * a], dp[4 * a + 1]);
+                v2[1] = pack2<DT>(dp[4 * a + 2], dp[4 * a + 3]);
+                *(__attribute__((address_space(3))) i32x2*)(dst + toff<QT>(kr, a) + 8 * g) = v2;
+            }
+            __syncthreads();
+            for (int db = w; db < DB; db += 4) {
+                f32x16 acc = zero16();
+#pragma unroll
+                for (int st = 0; st < kKeyBlock / 16; ++st)
+                    acc = mma<DT>(tr_frag<QT>(dst, st, 0, tl), tr_frag<D>(kblk, st, db, tl), acc);
+                float* base = p.dqacc + ((int64_t)bh * Sq) * D + 32 * db + lq;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int qi = q0 + 8 * (r >> 2) + 4 * g + (r & 3);
+                    if (qi < Sq) unsafeAtomicAdd(base + (int64_t)qi * D, acc[r]);
+                }
+            }
+        }
+
+        wait_vmcnt<0>();
+        if (t + 1 < nqt) store_stats(buf ^ 1);
+        __syncthreads();
+    }
+
+    // dK^T (times scale) and dV^T: register r of block b holds head-dimension
+    // index 32b + 8(r/4) + 4g + r%4 of key `key`: four consecutive values per
+    // 8-byte store; stores past Sk are dropped by the buffer range.
+    const __amdgpu_buffer_rsrc_t wk = rsrc(head_of(p.dk, p.Ldk, bh, p.H), head_bytes<D>(p.Ldk, Sk));
+    const __amdgpu_buffer_rsrc_t wv = rsrc(head_of(p.dv, p.Ldv, bh, p.H), head_bytes<D>(p.Ldv, Sk));
+    const float sc = p.scale;
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const uint32_t offk = (uint32_t)((key * p.Ldk.ss + 32 * b + 8 * a + 4 * g) * 2);
+            const uint32_t offv = (uint32_t)((key * p.Ldv.ss + 32 * b + 8 * a + 4 * g) * 2);
+            i32x2 kv, vv;
+            kv[0] = pack2<DT>(dka[b][4 * a] * sc, dka[b][4 * a + 1] * sc);
+            kv[1] = pack2<DT>(dka[b][4 * a + 2] * sc, dka[b][4 * a + 3] * sc);
+            vv[0] = pack2<DT>(dva[b][4 * a], dva[b][4 * a + 1]);
+            vv[1] = pack2<DT>(dva[b][4 * a + 2], dva[b][4 * a + 3]);
+            __builtin_amdgcn_raw_buffer_store_b64(kv, wk, offk, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(vv, wv, offv, 0, 0);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ of one 128-query block (deterministic mode).
+template <int D, int DT, bool CAUSAL, bool MASK = false, bool DROP = false>
+__global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_dq(BwdParams p) {
+    constexpr int DC = D / 16, DB = D / 32;
+    constexpr int KT = kKeyTile;
+    constexpr int TILE = KT * D * 2;
+    constexpr int CPT = KT * D / 8 / 256;
+    static_assert(CPT >= 1, "tile must split over the threads");
+
+    __shared__ __attribute__((aligned(16))) char smem[4 * TILE];
+    lds_t* const sm = (lds_t*)smem;
+
+    const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, g = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int bh, qb;
+    block_order(blockIdx.x, p.nqb, p.BH, CAUSAL, bh, qb);
+    const int Sq = p.Sq, Sk = p.Sk, diag = Sk - Sq;
+    const int q0 = qb * kQueryBlock, qw0 = q0 + 32 * w;
+    const int qi = qw0 + lq;
+
+    const __amdgpu_buffer_rsrc_t rq = rsrc(head_of(p.q, p.Lq, bh, p.H), head_bytes<D>(p.Lq, Sq));
+    const __amdgpu_buffer_rsrc_t rdo = rsrc(head_of(p.dout, p.Ldo, bh, p.H), head_bytes<D>(p.Ldo, Sq));
+    const i32x4 rk = rsrc_words(head_of(p.k, p.Lk, bh, p.H), head_bytes<D>(p.Lk, Sk));
+    const i32x4 rv = rsrc_words(head_of(p.v, p.Lv, bh, p.H), head_bytes<D>(p.Lv, Sk));
+    const __amdgpu_buffer_rsrc_t rl = rsrc(p.lse + (int64_t)bh * Sq, (uint64_t)Sq * 4);
+    const __amdgpu_buffer_rsrc_t rdv = rsrc(p.dvec + (int64_t)bh * Sq, (uint64_t)Sq * 4);
+
+    // Q and dO of this wave's 32 queries as B operands (query = column lq).
+    i32x4 qf[DC], df[DC];
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+        qf[c] = __builtin_amdgcn_raw_buffer_load_b128(rq, (qi * p.Lq.ss + 16 * c + 8 * g) * 2, 0, 0);
+        df[c] = __builtin_amdgcn_raw_buffer_load_b128(rdo, (qi * p.Ldo.ss + 16 * c + 8 * g) * 2, 0, 0);
+    }
+    const float lse2 = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, qi * 4, 0, 0)) * LOG2E;
+    const float dvl = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdv, qi * 4, 0, 0));
+
+    // Mask rows of this head (offsets beyond the buffer read as zero: hidden).
+    __amdgpu_buffer_rsrc_t rm = rl;
+    if constexpr (MASK) {
+        const int b_ = bh / p.H, h_ = bh - b_ * p.H;
+        rm = rsrc(p.mask + (int64_t)b_ * p.m_sb + (int64_t)h_ * p.m_sh,
+                  (uint64_t)(((int64_t)(Sq - 1) * p.m_ss + Sk + 3) & ~(int64_t)3));
+    }
+    // mask bytes of keys t*KT + 32rb + 8a + 4g .. +3 for this lane's query
+    uint32_t mk[2][4];
+    auto load_mask = [&](int t) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+                mk[rb][a] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+                    rm, (uint32_t)((int64_t)qi * p.m_ss + t * KT + 32 * rb + 8 * a + 4 * g), 0, 0);
+    };
+
+    int nkt = (Sk + KT - 1) / KT;
+    if (CAUSAL) nkt = min(nkt, max(0, (min(Sq, q0 + kQueryBlock) + diag + KT - 1) / KT));
+
+    // K and V tiles go straight from global memory into the LDS buffers
+    // (no staging registers); a step waits for its successor's loads just
+    // before the closing barrier.
+    const uint32_t lds0 = (uint32_t)(uintptr_t)sm;
+    auto issue = [&](int t, int buf) {
+        const uint32_t base = lds0 + (uint32_t)(buf * 2 * TILE);
+        tile_dma<D, CPT>(rk, t * KT, p.Lk.ss, base, w, lane);
+        tile_dma<D, CPT>(rv, t * KT, p.Lv.ss, base + TILE, w, lane);
+    };
+
+    const TrLane tl = tr_lane(lane);
+    const float c2 = p.scale_log2e;
+    f32x16 dqa[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) dqa[b] = zero16();
+
+    if (nkt > 0) {
+        issue(0, 0);
+        if constexpr (MASK) load_mask(0);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+
+    for (int t = 0; t < nkt; ++t) {
+        const int buf = t & 1;
+        // with a mask the next tile's loads wait until this tile's mask bytes
+        // (loads the compiler waits for) have been used
+        if constexpr (!MASK)
+            if (t + 1 < nkt) issue(t + 1, buf ^ 1);
+        const lds_t* tk = sm + buf * 2 * TILE;
+        const lds_t* tv = tk + TILE;
+        const int kt0 = t * KT;
+
+        // S^T = K Q^T and dP^T = V dO^T: 64 keys (rows) x this wave's 32 queries
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            s[rb] = zero16();
+            dp[rb] = zero16();
+        }
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                s[rb] = mma<DT>(row_frag<D>(tk, 32 * rb + lq, 2 * c + g), qf[c], s[rb]);
+                dp[rb] = mma<DT>(row_frag<D>(tv, 32 * rb + lq, 2 * c + g), df[c], dp[rb]);
+            }
+        }
+
+        const bool need_mask = MASK || (kt0 + KT > Sk) || (qw0 + 32 > Sq) || (CAUSAL && kt0 + KT - 1 > qw0 + diag);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float pv = __builtin_amdgcn_exp2f(s[rb][r] * c2 - lse2);
+                if (need_mask) {
+                    const int kj = kt0 + 32 * rb + 8 * (r >> 2) + 4 * g + (r & 3);
+                    bool vis = qi < Sq && kj < Sk && (!CAUSAL || kj <= qi + diag);
+                    if constexpr (MASK) vis = vis && ((mk[rb][r >> 2] >> (8 * (r & 3))) & 0xffu) != 0;
+                    pv = vis ? pv : 0.0f;
+                }
+                s[rb][r] = pv;
+            }
+        }
+        if constexpr (MASK) {
+            if (t + 1 < nkt) {
+                issue(t + 1, buf ^ 1);
+                load_mask(t + 1);
+            }
+        }
+        // dS^T = P (Z c dP - D_i): keys kt0 + 32rb + 8a + 0..7 share one
+        // Philox block; this lane uses words 2g and 2g+1 (keys 8a + 4g + 0..3)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                float z[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+                if constexpr (DROP) {
+                    uint32_t c[4] = {(uint32_t)((kt0 + 32 * rb + 8 * a) >> 3), (uint32_t)qi, (uint32_t)bh, p.offset};
+                    philox4x32_10(c, p.seed_lo, p.seed_hi);
+                    const uint32_t w0 = g ? c[2] : c[0];
+                    const uint32_t w1 = g ? c[3] : c[1];
+                    const uint32_t r16[4] = {w0 & 0xffffu, w0 >> 16, w1 & 0xffffu, w1 >> 16};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) z[e] = r16[e] >= p.drop_t ? p.keep_scale : 0.0f;
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * a + e;
+                    dp[rb][r] = s[rb][r] * (z[e] * dp[rb][r] - dvl);
+                }
+            }
+        }
+
+        // dQ^T += K^T dS^T  (rows: head dimension, columns: queries)
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const i32x4 da = acc_frag<DT>(dp[st >> 1], st & 1);
+#pragma unroll
+            for (int b = 0; b < DB; ++b) dqa[b] = mma<DT>(tr_frag<D>(tk, st, b, tl), da, dqa[b]);
+        }
+
+        wait_vmcnt<0>();
+        __syncthreads();
+    }
+
+    const __amdgpu_buffer_rsrc_t wq = rsrc(head_of(p.dq, p.Ldq, bh, p.H), head_bytes<D>(p.Ldq, Sq));
+    const float sc = p.scale;
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            i32x2 v2;
+            v2[0] = pack2<DT>(dqa[b][4 * a] * sc, dqa[b][4 * a + 1] * sc);
+            v2[1] = pack2<DT>(dqa[b][4 * a + 2] * sc, dqa[b][4 * a + 3] * sc);
+            __builtin_amdgcn_raw_buffer_store_b64(v2, wq, (uint32_t)((qi * p.Ldq.ss + 32 * b + 8 * a + 4 * g) * 2), 0, 0);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+template <int D, int DT, bool CAUSAL, bool MASK, bool DROP>
+static void run_masked(const BwdParams& p, hipStream_t st) {
+    hipLaunchKernelGGL((bwd_dkdv<D, DT, CAUSAL, false, MASK, DROP>), dim3((unsigned)(p.BH * p.nkb)), dim3(256), 0,
+                       st, p);
+    hipLaunchKernelGGL((bwd_dq<D, DT, CAUSAL, MASK, DROP>), dim3((unsigned)(p.BH * p.nqb)), dim3(256), 0, st, p);
+}
+
+template <int D, int DT, bool CAUSAL>
+static hipError_t run(const BwdParams& p, int deterministic, hipStream_t st) {
+    const int64_t rows = (int64_t)p.BH * p.Sq;
+    constexpr int RPB = 256 / (D / 8);
+    if (rows > 0)
+        hipLaunchKernelGGL((bwd_pre<D, DT>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st, p);
+    if (p.mask != nullptr || p.drop_t != 0) {
+        // masks and dropout run in the deterministic mode
+        if (p.mask != nullptr && p.drop_t != 0) run_masked<D, DT, CAUSAL, true, true>(p, st);
+        else if (p.mask != nullptr) run_masked<D, DT, CAUSAL, true, false>(p, st);
+        else run_masked<D, DT, CAUSAL, false, true>(p, st);
+        return hipGetLastError();
+    }
+    if (p.Sk > 0) {
+        const dim3 grid((unsigned)(p.BH * p.nkb));
+        if (deterministic)
+            hipLaunchKernelGGL((bwd_dkdv<D, DT, CAUSAL, false>), grid, dim3(256), 0, st, p);
+        else
+            hipLaunchKernelGGL((bwd_dkdv<D, DT, CAUSAL, true>), grid, dim3(256), 0, st, p);
+    }
+    if (rows > 0) {
+        if (deterministic) {
+            hipLaunchKernelGGL((bwd_dq<D, DT, CAUSAL>), dim3((unsigned)(p.BH * p.nqb)), dim3(256), 0, st, p);
+        } else {
+            const int64_t n8 = rows * D / 8;
+            hipLaunchKernelGGL((bwd_dq_convert<D, DT>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, p, n8);
+        }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace bwd
+}  // namespace fa
