@@ -21,6 +21,8 @@ Prints ONE JSON line:
   backward   the gradients (fa_bwd) on the same inputs, atomic and
              deterministic dq modes, in TFLOP/s at 2.5x the forward's flops.
   mask_dropout  the forward with an explicit mask and/or dropout (fa_fwd_ext).
+             The backward and mask_dropout objects carry their own
+             cpu_baseline: the fp64 oracle on the first heads of the workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--cpu-seconds T] [--no-cpu-baseline] [--no-naive]
@@ -290,7 +292,7 @@ def ext_leg(w, steps, warmup):
     md = mask.to(dev)
     stream = torch.cuda.current_stream(dev)
     code = fa.BF16 if w.dtype == "bf16" else fa.F16
-    out = {"unit": "TFLOP/s", "steps": steps, "mask": "one [S, S] uint8 mask shared by all heads, 90% kept",
+    out = {"unit": "TFLOP/s", "steps": steps, "mask_layout": "one [S, S] uint8 mask shared by all heads, 90% kept",
            "dropout_p": 0.1}
     for name, m, p in (("plain", None, 0.0), ("mask", md, 0.0), ("dropout", None, 0.1), ("mask_dropout", md, 0.1)):
         ms = None if m is None else (0, 0, ld)
@@ -392,6 +394,52 @@ def cpu_leg(w, seconds):
     }
 
 
+def oracle_heads_leg(w, seconds, what):
+    """The fp64 oracle on the first h heads of the workload (heads are
+    independent, so these are exact gradients / outputs of those heads),
+    h grown until the run takes most of `seconds`.  what: "backward" (the
+    plain backward, flops 2.5x the forward's per head) or "mask_dropout"
+    (the forward with the shared 90% mask and dropout 0.1)."""
+    import numpy as np
+    import oracle
+    from workloads import make_inputs
+
+    q, k, v = workload_inputs(w)
+    g, _, _ = make_inputs(w.B, w.H, w.S, w.D, w.dtype, seed=w.seed + 1000)
+    qb, kb, vb, gb = bits(q), bits(k), bits(v), bits(g)
+    per_head = w.flops() / (w.B * w.H) * (2.5 if what == "backward" else 1.0)
+    mask = None
+    if what == "mask_dropout":
+        ld = (w.S + 3) // 4 * 4
+        rng = np.random.default_rng(2400)
+        mask = np.zeros((w.S, ld), np.uint8)
+        mask[:, :w.S] = (rng.random((w.S, w.S)) < 0.9).astype(np.uint8)
+
+    def run(h):
+        sl = (slice(0, 1), slice(0, h))
+        qs, ks, vs, gs = (np.ascontiguousarray(x[sl]) for x in (qb, kb, vb, gb))
+        t0 = time.perf_counter()
+        if what == "backward":
+            oracle.attention_bwd(qs, ks, vs, gs, scale=w.scale, causal=w.causal, dtype=w.dtype)
+        else:
+            oracle.attention_fwd_ext(qs, ks, vs, scale=w.scale, causal=w.causal, dtype=w.dtype, mask=mask,
+                                     mask_strides=(0, 0, mask.shape[1]), dropout_p=0.1, seed=1234, offset=0)
+        return time.perf_counter() - t0
+
+    h = 1
+    while True:
+        t = run(h)
+        if t >= 0.6 * seconds or h >= w.H:
+            break
+        h = int(min(w.H, max(h + 1, math.ceil(h * 0.9 * seconds / max(t, 1e-3)))))
+    return {"value": per_head * h / t / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "wall_s": round(t, 3), "kind": "oracle",
+            "sample": "heads 0..%d of batch 0 (of %d heads) of %s, the fp64 oracle's full %s of those "
+                      "heads; %.1f s wall; flops counted as for the GPU figure" % (
+                          h - 1, w.B * w.H, w.name,
+                          "backward" if what == "backward" else "masked/dropout forward", t)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -461,6 +509,11 @@ def main():
         out["mask_dropout"] = ext_leg(w, max(2, min(20, a.steps // 10)), 2)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_leg(w, a.cpu_seconds)
+        # the oracle timed beside the backward and the masked/dropout forward too
+        if not a.no_backward and "skipped" not in out["backward"]:
+            out["backward"]["cpu_baseline"] = oracle_heads_leg(w, a.cpu_seconds / 2, "backward")
+        if not a.no_ext:
+            out["mask_dropout"]["cpu_baseline"] = oracle_heads_leg(w, a.cpu_seconds / 2, "mask_dropout")
     print(json.dumps(out), flush=True)
 
 
