@@ -82,11 +82,12 @@ bool no_self_overlap(const int64_t* st, int B, int H, int S, int D) {
 
 }  // namespace
 
-// The tuned kernel (D = 64 or 128) on validated arguments.
+// The tuned kernel (D = 64 or 128) on validated arguments; mask (with its
+// byte strides) may be null.
 static int launch_tuned(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Sq,
                         int Sk, int D, const int64_t* q_strides, const int64_t* k_strides,
-                        const int64_t* v_strides, const int64_t* o_strides, float scale, int causal, int dtype,
-                        void* stream) {
+                        const int64_t* v_strides, const int64_t* o_strides, const uint8_t* mask,
+                        const int64_t* mask_strides, float scale, int causal, int dtype, void* stream) {
     fa::FwdParams p;
     p.q = q;
     p.k = k;
@@ -103,6 +104,10 @@ static int launch_tuned(const void* q, const void* k, const void* v, void* o, fl
     p.k_sb = k_strides[0], p.k_sh = k_strides[1], p.k_ss = (int)k_strides[2];
     p.v_sb = v_strides[0], p.v_sh = v_strides[1], p.v_ss = (int)v_strides[2];
     p.o_sb = o_strides[0], p.o_sh = o_strides[1], p.o_ss = (int)o_strides[2];
+    p.mask = mask;
+    p.m_sb = mask ? mask_strides[0] : 0;
+    p.m_sh = mask ? mask_strides[1] : 0;
+    p.m_ss = mask ? (int)mask_strides[2] : 0;
     const int64_t grid = (int64_t)p.BH * p.nqb;
     const hipError_t err = fa::launch_fwd(p, D, dtype, causal != 0, grid, (hipStream_t)stream);
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
@@ -214,8 +219,8 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
         return err == hipSuccess ? FA_OK : FA_ERR_HIP;
     }
 
-    return launch_tuned(q, k, v, o, lse, B, H, Sq, Sk, D, q_strides, k_strides, v_strides, o_strides, scale,
-                        causal, dtype, stream);
+    return launch_tuned(q, k, v, o, lse, B, H, Sq, Sk, D, q_strides, k_strides, v_strides, o_strides, nullptr,
+                        nullptr, scale, causal, dtype, stream);
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int S,
@@ -369,12 +374,13 @@ static int ext_common(const void* q, const void* k, const void* v, void* o, floa
     }
     if (lse && overlap(out[0][0], out[0][1], out[1][0], out[1][1])) return FA_ERR_ALIAS;
 
-    // Neither mask nor dropout: the plain forward, on the tuned kernel where
-    // fa_fwd_strided would run it (so the two calls agree bit for bit).
-    if (!mask && t == 0 && D != 256 && head_span_ok(Sq, strides[2], D) && head_span_ok(Sk, strides[5], D) &&
+    // No dropout at D <= 128: the tuned kernel, with the mask if there is
+    // one.  Without a mask this is the plain forward exactly as
+    // fa_fwd_strided runs it (the two calls agree bit for bit).
+    if (t == 0 && D != 256 && head_span_ok(Sq, strides[2], D) && head_span_ok(Sk, strides[5], D) &&
         head_span_ok(Sk, strides[8], D) && head_span_ok(Sq, strides[11], D))
-        return launch_tuned(q, k, v, o, lse, B, H, Sq, Sk, D, strides, strides + 3, strides + 6, strides + 9, scale,
-                            causal, dtype, stream);
+        return launch_tuned(q, k, v, o, lse, B, H, Sq, Sk, D, strides, strides + 3, strides + 6, strides + 9, mask,
+                            mask_strides, scale, causal, dtype, stream);
 
     fa::ext::ExtParams p = {};
     p.q = q;

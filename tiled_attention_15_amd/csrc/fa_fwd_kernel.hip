@@ -43,6 +43,12 @@
 // * Edges.  All global traffic uses buffer instructions with the head's
 //   extent as the record count: reads past the sequence end return zero and
 //   writes past it are dropped, so ragged S needs no branches on loads.
+// * Optional boolean mask (the MASK instances): each lane reads the mask
+//   bytes of its query row and its 32 keys of a tile one step ahead and sets
+//   the hidden scores to -inf before the online softmax, as the causal rule
+//   does on diagonal tiles ("FlashAttention-2 on Ascend NPU: how
+//   ops-transformer reaches 3x" (2048ai.net), section 3.4: the mask acts on
+//   the score tile on chip).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -199,7 +205,7 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
     return r;
 }
 
-template <int D, int DT, bool CAUSAL>
+template <int D, int DT, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
     constexpr int NW = 8;
     constexpr int NT = 512;
@@ -245,6 +251,37 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
                                 (uint32_t)(((int64_t)(Sk - 1) * p.k_ss + D) * 2));
     const i32x4 rv = rsrc_words((const char*)p.v + ((int64_t)b_ * p.v_sb + (int64_t)h_ * p.v_sh) * 2,
                                 (uint32_t)(((int64_t)(Sk - 1) * p.v_ss + D) * 2));
+
+    // Mask rows of this head: one buffer over [first row, last row + Sk)
+    // rounded up to whole dwords, so reads past it (rows beyond the sequence,
+    // keys beyond the last dword) return zero, i.e. hidden.  A lane reads the
+    // bytes of its query row and its 32 keys of a tile: mk[4*kb2 + j] holds
+    // keys 32*kb2 + 16*g + 4*j .. +3, byte e of it key 32*kb2 + 16*g + 4*j + e,
+    // the keys of accumulator registers 4*j + e of s[kb2].
+    __amdgpu_buffer_rsrc_t rm = rq;
+    uint32_t mk[8];
+    if constexpr (MASK) {
+        const uint8_t* mbase = p.mask + (int64_t)b_ * p.m_sb + (int64_t)h_ * p.m_sh;
+        rm = make_rsrc(mbase, (uint32_t)(((int64_t)(Sq - 1) * p.m_ss + Sk + 3) & ~(int64_t)3));
+    }
+    // Separate dword loads (an empty asm statement between them keeps the
+    // compiler from fusing a lane's four adjacent dwords into one 16-byte
+    // load): each dword is range-checked on its own, so a row's last keys
+    // read correctly up to the buffer's end.
+    auto load_mask = [&](int t) {
+        // rows past the sequence read from beyond the buffer (2^31 exceeds
+        // its record count): zero, without 32-bit wraparound of the offset
+        const int qrow = qw0 + lq;
+        const uint32_t row = qrow < Sq ? (uint32_t)qrow * (uint32_t)p.m_ss + (uint32_t)(t * BC + 16 * g)
+                                       : 0x80000000u;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                mk[4 * kb2 + j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rm, row + 32 * kb2 + 4 * j, 0, 0);
+                asm volatile("" ::: "memory");
+            }
+    };
 
     // Every wave visits all nt tiles of its workgroup: a wave whose rows end
     // before a diagonal tile finds it fully masked (probabilities exactly 0),
@@ -352,6 +389,23 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
         }
     };
 
+    // Explicit mask of the scores of tile t (the words load_mask(t) read).
+    // It runs before the phase issues its tile loads, and an asm statement
+    // holding the results keeps it there: the compiler, which does not see those loads,
+    // waits for every outstanding load before it reads the mask words, and
+    // the loads in flight at that point are ones this step needs anyway.
+    // The next tile's mask words are requested right after the tile loads.
+    auto mask_scores = [&]() {
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (((mk[4 * kb2 + (i >> 2)] >> (8 * (i & 3))) & 0xffu) == 0) s[kb2][i] = -INFINITY;
+        // the masked scores as operands of a volatile asm statement: they are
+        // complete before the (volatile asm) tile loads that follow
+        asm volatile("" : "+v"(s[0]), "+v"(s[1]));
+    };
+
     // Softmax phase of step t: mask, running max, exponentials, P_t packed.
     auto swork = [&](int t) {
         const int key0 = t * BC + 16 * g;
@@ -448,18 +502,25 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
     };
-    auto end_barrier = [&](int t) {
-        if (t + 2 < nt) wait_vmcnt<2 * LPT>();
-        else wait_vmcnt<0>();
+    // mask_after: this wave issued the mask words of its next softmax phase
+    // after its loads of tile t + 2, so those 8 loads may stay in flight too.
+    auto end_barrier = [&](int t, bool mask_after) {
+        if (t + 2 < nt) {
+            if (MASK && mask_after) wait_vmcnt<2 * LPT + 8>();
+            else wait_vmcnt<2 * LPT>();
+        } else {
+            wait_vmcnt<0>();
+        }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     };
 
     // Prologue: Q, tile 0 and tile 1 requested; tile 0 (and Q) waited for.
+    if constexpr (MASK) load_mask(0);
     issue_tile(0);
     if (nt > 1) issue_tile(1);
-    end_barrier(-1);
+    end_barrier(-1, false);
 
     // The two groups run the same sequence of barriers (two per step for
     // steps 0 .. nt-1, one for the final step) with their phases swapped.
@@ -469,15 +530,19 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
     if (grp == 0) {
         qk(0);
         mid_barrier();
+        if constexpr (MASK) mask_scores();
         if (nt > 2) issue_tile(2);
+        if constexpr (MASK) if (nt > 1) load_mask(1);
         swork(0);
-        end_barrier(0);
+        end_barrier(0, true);
         for (int t = 1; t < nt; ++t) {
             mphase(t);
             mid_barrier();
+            if constexpr (MASK) mask_scores();
             if (t + 2 < nt) issue_tile(t + 2);
+            if constexpr (MASK) if (t + 1 < nt) load_mask(t + 1);
             swork(t);
-            end_barrier(t);
+            end_barrier(t, true);
         }
         pv(nt - 1);
         mid_barrier();
@@ -485,14 +550,17 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
         if (nt > 2) issue_tile(2);
         mid_barrier();
         qk(0);
-        end_barrier(0);
+        end_barrier(0, false);
         for (int t = 1; t < nt; ++t) {
+            if constexpr (MASK) mask_scores();
             if (t + 2 < nt) issue_tile(t + 2);
+            if constexpr (MASK) load_mask(t);
             swork(t - 1);
             mid_barrier();
             mphase(t);
-            end_barrier(t);
+            end_barrier(t, true);
         }
+        if constexpr (MASK) mask_scores();
         swork(nt - 1);
         mid_barrier();
         pv(nt - 1);
@@ -521,7 +589,10 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
 
 template <int D, int DT, bool CAUSAL>
 static hipError_t launch_kernel(const FwdParams& p, int64_t grid, hipStream_t stream) {
-    hipLaunchKernelGGL((fa_fwd_kernel<D, DT, CAUSAL>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    if (p.mask != nullptr)
+        hipLaunchKernelGGL((fa_fwd_kernel<D, DT, CAUSAL, true>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    else
+        hipLaunchKernelGGL((fa_fwd_kernel<D, DT, CAUSAL, false>), dim3((unsigned)grid), dim3(512), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -23,9 +23,16 @@ struct FwdParams {
     // Element strides of batch, head and row (the head dimension is contiguous).
     int64_t q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;
     int q_ss, k_ss, v_ss, o_ss;
+    // Optional boolean mask: element (b, h, i, j) at byte
+    // b*m_sb + h*m_sh + i*m_ss + j, nonzero keeps the score.  Strides are
+    // multiples of 4 and one head's rows span less than 2^31 bytes.
+    const uint8_t* mask;   // null = no mask
+    int64_t m_sb, m_sh;
+    int m_ss;
 };
 
-// Enqueue the forward kernel; returns hipGetLastError() after the launch.
+// Enqueue the forward kernel (the masked instance when p.mask is set);
+// returns hipGetLastError() after the launch.
 hipError_t launch_fwd(const FwdParams& p, int D, int dtype, bool causal, int64_t grid,
                       hipStream_t stream);
 
