@@ -153,7 +153,12 @@ int fa_version(void);
  * fa_fwd_plan -- the launch fa_fwd would make, without launching it.
  *
  * Fills (each pointer may be NULL):
- *   block_q    query rows per workgroup (B_r),
+ *   block_q    query rows per workgroup (B_r): 256; 128 at D = 256, and at
+ *              D = 64 when B * H * ceil(S / 256) < 256 (the key-split
+ *              instance: both wave groups on the same 128 rows, the K/V
+ *              tiles shared out even/odd between them and the two partial
+ *              results merged; with an odd count one extra, fully masked
+ *              tile is visited, not counted below),
  *   block_kv   keys per K/V tile (B_c),
  *   grid       workgroups launched (B * H * ceil(S / B_r)),
  *   tiles      (query block, K/V tile) pairs the kernel processes: for a

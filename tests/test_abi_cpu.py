@@ -87,7 +87,8 @@ def test_rejects_bad_arguments(lib, kw, code):
 
 def test_null_lse_is_not_an_error_in_validation(lib):
     # lse=NULL passes validation; check through the planner (no launch)
-    assert fa.fa_fwd_plan(1, 2, 256, 64, False, 0)[2] == 2
+    br, _, grid, _ = fa.fa_fwd_plan(1, 2, 256, 64, False, 0)
+    assert grid == 2 * -(-256 // br)
 
 
 def _expected_tiles(B, H, S, br, bc, causal):

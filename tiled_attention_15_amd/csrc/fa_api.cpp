@@ -31,6 +31,15 @@ int validate_shape(int B, int H, int Sq, int Sk, int D, int dtype) {
     return FA_OK;
 }
 
+// The key-split instance of the tuned kernel (D = 64, no mask): when the
+// 256-row blocks would not give every compute unit a workgroup, 128-row
+// blocks with the key range split between the two wave groups double the
+// workgroups and halve each one's chain of K/V steps.
+bool use_split(int B, int H, int Sq, int D, bool has_mask) {
+    const int64_t blocks = (int64_t)B * H * ((Sq + fa::kBlockQ - 1) / fa::kBlockQ);
+    return D == 64 && !has_mask && blocks < fa::kComputeUnits;
+}
+
 // Byte offsets inside one head are 32-bit (buffer descriptors): every row a
 // query block (rows up to a multiple of kBlockQ) or a key tile (up to 64
 // rows past the end) can address must lie below 2^31 bytes.
@@ -98,7 +107,9 @@ static int launch_tuned(const void* q, const void* k, const void* v, void* o, fl
     p.Sk = Sk;
     p.H = H;
     p.BH = B * H;
-    p.nqb = (Sq + fa::kBlockQ - 1) / fa::kBlockQ;
+    const bool split = use_split(B, H, Sq, D, mask != nullptr);
+    const int br = split ? fa::kBlockQSplit : fa::kBlockQ;
+    p.nqb = (Sq + br - 1) / br;
     p.scale_log2e = (float)((double)scale * 1.4426950408889634074);
     p.q_sb = q_strides[0], p.q_sh = q_strides[1], p.q_ss = (int)q_strides[2];
     p.k_sb = k_strides[0], p.k_sh = k_strides[1], p.k_ss = (int)k_strides[2];
@@ -109,7 +120,7 @@ static int launch_tuned(const void* q, const void* k, const void* v, void* o, fl
     p.m_sh = mask ? mask_strides[1] : 0;
     p.m_ss = mask ? (int)mask_strides[2] : 0;
     const int64_t grid = (int64_t)p.BH * p.nqb;
-    const hipError_t err = fa::launch_fwd(p, D, dtype, causal != 0, grid, (hipStream_t)stream);
+    const hipError_t err = fa::launch_fwd(p, D, dtype, causal != 0, grid, split, (hipStream_t)stream);
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -138,8 +149,10 @@ int fa_fwd_plan(int B, int H, int S, int D, int causal, int dtype, int* block_q,
     int st = validate_shape(B, H, S, S, D, dtype);
     if (st == FA_OK && !head_span_ok(S, D, D)) st = FA_ERR_SHAPE;
     if (st != FA_OK) return st;
-    // D = 256 runs on the general kernel (128-row blocks, 32-key tiles)
-    const int br = D == 256 ? fa::ext::kQueryBlock : fa::kBlockQ;
+    // D = 256 runs on the general kernel (128-row blocks, 32-key tiles); a
+    // small D = 64 grid on the key-split instance (128-row blocks)
+    const int br = D == 256 ? fa::ext::kQueryBlock
+                 : use_split(B, H, S, D, false) ? fa::kBlockQSplit : fa::kBlockQ;
     const int bc = D == 256 ? fa::ext::key_tile(256) : fa::kBlockKV;
     const int64_t nqb = (S + br - 1) / br;
     const int64_t nkv = (S + bc - 1) / bc;

@@ -43,6 +43,11 @@
 // * Edges.  All global traffic uses buffer instructions with the head's
 //   extent as the record count: reads past the sequence end return zero and
 //   writes past it are dropped, so ragged S needs no branches on loads.
+// * Key split (the SPLIT instances, D = 64): for grids too small to fill
+//   the chip, both wave groups own the same 128 query rows and take the even
+//   and odd K/V tiles respectively; the two partial (O, running max, running
+//   sum) are merged through LDS at the end, the same rescale-and-add as the
+//   online softmax's own update.
 // * Optional boolean mask (the MASK instances): each lane reads the mask
 //   bytes of its query row and its 32 keys of a tile one step ahead and sets
 //   the hidden scores to -inf before the online softmax, as the causal rule
@@ -205,16 +210,17 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
     return r;
 }
 
-template <int D, int DT, bool CAUSAL, bool MASK>
+template <int D, int DT, bool CAUSAL, bool MASK, bool SPLIT>
 __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
+    static_assert(!SPLIT || (D == 64 && !MASK), "the split instance is for D = 64 without a mask");
     constexpr int NW = 8;
     constexpr int NT = 512;
-    constexpr int BR = 256;
+    constexpr int BR = SPLIT ? 128 : 256;
     constexpr int DC = D / 16;
     constexpr int DB = D / 32;
     constexpr int TILE_BYTES = BC * D * 2;
     constexpr int SLOT_BYTES = 2 * TILE_BYTES;      // K tile then V tile
-    constexpr int NSLOT = 4;
+    constexpr int NSLOT = SPLIT ? 8 : 4;
     constexpr int CHUNKS = TILE_BYTES / 16;
     constexpr int LPT = CHUNKS / NT;                // 16-byte loads per thread per tensor
     static_assert(CHUNKS % NT == 0, "tile must split evenly over threads");
@@ -235,7 +241,7 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
     // last query row sees the last key).
     const int diag = Sk - Sq;
     const int q0 = qb * BR;
-    const int qw0 = q0 + wid * 32;
+    const int qw0 = q0 + (SPLIT ? (wid & 3) : wid) * 32;   // split: both groups share the rows
     const int b_ = bh / p.H, h_ = bh - b_ * p.H;
 
     // One buffer descriptor per tensor and head; its record count is the
@@ -484,13 +490,15 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
         }
         __builtin_amdgcn_sched_group_barrier(MFMA, AHEAD, 0);
     };
-    auto mphase = [&](int t) {
+    // matrix phase: O += P_tp V_tp, then S = K_t Q^T
+    auto mphase2 = [&](int tp, int t) {
         __builtin_amdgcn_s_setprio(1);
-        pv(t - 1);
+        pv(tp);
         qk(t);
         mphase_schedule();
         __builtin_amdgcn_s_setprio(0);
     };
+    auto mphase = [&](int t) { mphase2(t - 1, t); };
 
     // Phase boundaries.  The one in the middle of a step only keeps the two
     // groups in alternation (no data passes through LDS across it).  The one
@@ -516,6 +524,95 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     };
 
+    if constexpr (SPLIT) {
+    // Key range split inside the workgroup (for grids smaller than the chip):
+    // both groups own the same 128 query rows; group 0 takes the even K/V
+    // tiles and group 1 the odd ones, with the same ping-pong, and their
+    // partial (O, m, l) are merged through LDS at the end.  Step s handles
+    // tiles 2s (group 0) and 2s + 1 (group 1); with an odd tile count group 1's
+    // last tile lies past the block's keys and is fully masked (it is loaded,
+    // so its values are finite and its probabilities exactly 0).  The ring has
+    // eight slots; the loads of step s + 2 are issued during step s.
+    const int ns = (nt + 1) >> 1;
+    auto issue_pair = [&](int st) { issue_tile(2 * st); issue_tile(2 * st + 1); };
+    auto end_split = [&](int st) {
+        if (st + 2 < ns) wait_vmcnt<4 * LPT>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
+    issue_pair(0);
+    if (ns > 1) issue_pair(1);
+    end_split(-1);
+    if (grp == 0) {
+        qk(0);
+        mid_barrier();
+        if (ns > 2) issue_pair(2);
+        swork(0);
+        end_split(0);
+        for (int st = 1; st < ns; ++st) {
+            mphase2(2 * st - 2, 2 * st);
+            mid_barrier();
+            if (st + 2 < ns) issue_pair(st + 2);
+            swork(2 * st);
+            end_split(st);
+        }
+        pv(2 * ns - 2);
+        mid_barrier();
+    } else {
+        if (ns > 2) issue_pair(2);
+        mid_barrier();
+        qk(1);
+        end_split(0);
+        for (int st = 1; st < ns; ++st) {
+            if (st + 2 < ns) issue_pair(st + 2);
+            swork(2 * st - 1);
+            mid_barrier();
+            mphase2(2 * st - 1, 2 * st + 1);
+            end_split(st);
+        }
+        swork(2 * ns - 1);
+        mid_barrier();
+        pv(2 * ns - 1);
+    }
+    // Merge: group 1 hands its O accumulators, running max and sum to the
+    // wave of group 0 that owns the same rows (same lane layout), which
+    // rescales both to the larger max and adds them.
+    float* const xbuf = (float*)smem;
+    const int xb = (wid & 3) * (DB * 16 + 2) * 64 + lane;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    if (grp != 0) {
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) xbuf[xb + (16 * b + i) * 64] = oacc[b][i];
+        xbuf[xb + 16 * DB * 64] = m_run;
+        xbuf[xb + (16 * DB + 1) * 64] = l_run;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    if (grp != 0) return;
+    {
+        const float m1 = xbuf[xb + 16 * DB * 64];
+        const float l1 = xbuf[xb + (16 * DB + 1) * 64];
+        const float m = fmaxf(m_run, m1);
+        float a0 = 0.0f, a1 = 0.0f;
+        if (m != -INFINITY) {
+            a0 = fast_exp2(m_run - m);
+            a1 = fast_exp2(m1 - m);
+        }
+        l_run = a0 * l_run + a1 * l1;
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[b][i] = a0 * oacc[b][i] + a1 * xbuf[xb + (16 * b + i) * 64];
+        m_run = m;
+    }
+    } else {
     // Prologue: Q, tile 0 and tile 1 requested; tile 0 (and Q) waited for.
     if constexpr (MASK) load_mask(0);
     issue_tile(0);
@@ -565,6 +662,7 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
         mid_barrier();
         pv(nt - 1);
     }
+    }
 
     const float l_tot = xsum32(l_run);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
@@ -588,25 +686,33 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
 }
 
 template <int D, int DT, bool CAUSAL>
-static hipError_t launch_kernel(const FwdParams& p, int64_t grid, hipStream_t stream) {
+static hipError_t launch_kernel(const FwdParams& p, int64_t grid, bool split, hipStream_t stream) {
     if (p.mask != nullptr)
-        hipLaunchKernelGGL((fa_fwd_kernel<D, DT, CAUSAL, true>), dim3((unsigned)grid), dim3(512), 0, stream, p);
-    else
-        hipLaunchKernelGGL((fa_fwd_kernel<D, DT, CAUSAL, false>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+        hipLaunchKernelGGL((fa_fwd_kernel<D, DT, CAUSAL, true, false>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    else if constexpr (D == 64) {
+        if (split)
+            hipLaunchKernelGGL((fa_fwd_kernel<D, DT, CAUSAL, false, true>), dim3((unsigned)grid), dim3(512), 0,
+                               stream, p);
+        else
+            hipLaunchKernelGGL((fa_fwd_kernel<D, DT, CAUSAL, false, false>), dim3((unsigned)grid), dim3(512), 0,
+                               stream, p);
+    } else {
+        hipLaunchKernelGGL((fa_fwd_kernel<D, DT, CAUSAL, false, false>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    }
     return hipGetLastError();
 }
 
 template <int D, int DT>
-static hipError_t launch_c(const FwdParams& p, bool causal, int64_t grid, hipStream_t s) {
-    return causal ? launch_kernel<D, DT, true>(p, grid, s) : launch_kernel<D, DT, false>(p, grid, s);
+static hipError_t launch_c(const FwdParams& p, bool causal, int64_t grid, bool split, hipStream_t s) {
+    return causal ? launch_kernel<D, DT, true>(p, grid, split, s) : launch_kernel<D, DT, false>(p, grid, split, s);
 }
 
-hipError_t launch_fwd(const FwdParams& p, int D, int dtype, bool causal, int64_t grid,
+hipError_t launch_fwd(const FwdParams& p, int D, int dtype, bool causal, int64_t grid, bool split,
                       hipStream_t stream) {
-    if (D == 64) return dtype == 0 ? launch_c<64, 0>(p, causal, grid, stream)
-                                   : launch_c<64, 1>(p, causal, grid, stream);
-    return dtype == 0 ? launch_c<128, 0>(p, causal, grid, stream)
-                      : launch_c<128, 1>(p, causal, grid, stream);
+    if (D == 64) return dtype == 0 ? launch_c<64, 0>(p, causal, grid, split, stream)
+                                   : launch_c<64, 1>(p, causal, grid, split, stream);
+    return dtype == 0 ? launch_c<128, 0>(p, causal, grid, false, stream)
+                      : launch_c<128, 1>(p, causal, grid, false, stream);
 }
 
 }  // namespace fa

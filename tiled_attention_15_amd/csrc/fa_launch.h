@@ -6,6 +6,8 @@
 namespace fa {
 
 constexpr int kBlockQ = 256;           // query rows per workgroup (B_r): 8 waves x 32
+constexpr int kBlockQSplit = 128;      // B_r of the key-split instance (both wave groups on 128 rows)
+constexpr int kComputeUnits = 256;     // MI355X
 constexpr int kBlockKV = 64;            // keys per K/V tile (B_c)
 
 struct FwdParams {
@@ -31,9 +33,10 @@ struct FwdParams {
     int m_ss;
 };
 
-// Enqueue the forward kernel (the masked instance when p.mask is set);
-// returns hipGetLastError() after the launch.
-hipError_t launch_fwd(const FwdParams& p, int D, int dtype, bool causal, int64_t grid,
+// Enqueue the forward kernel (the masked instance when p.mask is set; the
+// key-split instance when split, D = 64 only, p.nqb counted in
+// kBlockQSplit-row blocks); returns hipGetLastError() after the launch.
+hipError_t launch_fwd(const FwdParams& p, int D, int dtype, bool causal, int64_t grid, bool split,
                       hipStream_t stream);
 
 }  // namespace fa
