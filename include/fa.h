@@ -154,7 +154,8 @@ int fa_version(void);
  *
  * Fills (each pointer may be NULL):
  *   block_q    query rows per workgroup (B_r): 256; 128 at D = 256, and at
- *              D = 64 when B * H * ceil(S / 256) < 256 (the key-split
+ *              D = 64 or 128 when n = B * H * ceil(S / 256) satisfies
+ *              2n <= 256, or n < 256 for a causal call (the key-split
  *              instance: both wave groups on the same 128 rows, the K/V
  *              tiles shared out even/odd between them and the two partial
  *              results merged; with an odd count one extra, fully masked

@@ -112,9 +112,10 @@ def test_all_ones_mask_is_the_plain_forward(D, dtype, causal):
 def test_causal_rule_as_a_mask(Sq, Sk):
     """The causal rule written out as a mask (key j visible to query i iff
     j <= i + Sk - Sq) on a non-causal call: the tiles the causal call skips
-    contribute exact zeros, so the two agree bit for bit."""
+    contribute exact zeros, so the two agree bit for bit.  (130 heads: enough
+    256-row blocks that the causal call runs the unsplit block layout too.)"""
     D, dtype = 128, "bf16"
-    q, k, v = inputs(1, 3, Sq, Sk, D, dtype, seed=4300 + Sq)
+    q, k, v = inputs(1, 130, Sq, Sk, D, dtype, seed=4300 + Sq)
     i = np.arange(Sq)[:, None]
     j = np.arange(Sk)[None, :]
     ld = (Sk + 3) // 4 * 4

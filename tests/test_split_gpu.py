@@ -1,9 +1,9 @@
 """GPU parity of the key-split instance of the tuned forward kernel.
 
-At D = 64, when 256-row query blocks would leave compute units without a
-workgroup, the forward runs 128-row blocks whose two wave groups share the
-rows and split the K/V tiles (even / odd), merging their partial (O, m, l)
-through LDS at the end.  Checked against the fp64 oracle on shapes with even
+At D = 64 and 128, for grids of 256-row blocks too small for the chip, the
+forward runs 128-row blocks whose two wave groups share the rows and split
+the K/V tiles (even / odd), merging their partial (O, m, l) through LDS at
+the end.  Checked against the fp64 oracle on shapes with even
 and odd tile counts (an odd count gives group 1 a fully masked padding tile),
 unequal lengths, ragged rows and strided views.
 """
@@ -33,32 +33,40 @@ def inputs(B, H, Sq, Sk, D, dtype, seed):
     return q[:, :, :Sq].contiguous(), k, v
 
 
-def test_split_is_chosen_for_small_d64_grids():
-    br, bc, grid, _ = fa.fa_fwd_plan(2, 12, 2048, 64, True, 0)     # the GPT-shaped workload
+def test_split_is_chosen_for_small_grids():
+    br, bc, grid, _ = fa.fa_fwd_plan(2, 12, 2048, 64, True, 0)     # the GPT-shaped workload: 192 blocks
     assert (br, bc, grid) == (128, 64, 2 * 12 * 16)
     br, _, grid, _ = fa.fa_fwd_plan(4, 64, 2048, 64, True, 0)      # 2048 blocks of 256 rows
     assert (br, grid) == (256, 4 * 64 * 8)
-    br, _, _, _ = fa.fa_fwd_plan(1, 2, 2048, 128, True, 1)         # D = 128 never splits
-    assert br == 256
+    assert fa.fa_fwd_plan(1, 32, 1024, 128, False, 1)[0] == 128    # 128 blocks: the doubled grid fits
+    assert fa.fa_fwd_plan(1, 33, 1024, 128, False, 1)[0] == 256    # 132 blocks, non-causal: no split
+    assert fa.fa_fwd_plan(1, 33, 1024, 128, True, 1)[0] == 128     # causal, fewer blocks than CUs
+    assert fa.fa_fwd_plan(1, 64, 1024, 128, True, 1)[0] == 256     # 256 blocks
+    assert fa.fa_fwd_plan(1, 2, 2048, 256, True, 1)[0] == 128      # D = 256: the general kernel's blocks
 
 
 CASES = [
-    # (B, H, Sq, Sk, causal, dtype)
-    (1, 2, 256, 256, False, "f16"),      # the tiny workload's shape
-    (1, 3, 192, 192, True, "bf16"),      # block 1: three tiles (odd)
-    (2, 2, 129, 130, False, "f16"),      # three key tiles (odd), ragged rows
-    (1, 1, 700, 190, True, "bf16"),      # Sq > Sk: leading rows see no key
-    (1, 2, 300, 777, True, "f16"),       # Sq < Sk, bottom-right causal
-    (1, 1, 1, 1, False, "f16"),
-    (1, 4, 1000, 1000, True, "f16"),
+    # (B, H, Sq, Sk, causal, dtype, D)
+    (1, 2, 256, 256, False, "f16", 64),      # the tiny workload's shape
+    (1, 3, 192, 192, True, "bf16", 128),     # block 1: three tiles (odd)
+    (2, 2, 129, 130, False, "f16", 128),     # three key tiles (odd), ragged rows
+    (1, 1, 700, 190, True, "bf16", 128),
+    (1, 2, 300, 777, True, "f16", 128),
+    (1, 1, 1, 1, False, "bf16", 128),
+    (1, 4, 1000, 1000, True, "bf16", 128),
+    (1, 3, 192, 192, True, "bf16", 64),      # block 1: three tiles (odd)
+    (2, 2, 129, 130, False, "f16", 64),      # three key tiles (odd), ragged rows
+    (1, 1, 700, 190, True, "bf16", 64),      # Sq > Sk: leading rows see no key
+    (1, 2, 300, 777, True, "f16", 64),       # Sq < Sk, bottom-right causal
+    (1, 1, 1, 1, False, "f16", 64),
+    (1, 4, 1000, 1000, True, "f16", 64),
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=["%dx%dx%dx%d%s%s" % (c[0], c[1], c[2], c[3], "c" if c[4] else "n",
-                                                                    c[5]) for c in CASES])
+@pytest.mark.parametrize("case", CASES, ids=["%dx%dx%dx%dx%d%s%s" % (c[0], c[1], c[2], c[3], c[6],
+                                                                       "c" if c[4] else "n", c[5]) for c in CASES])
 def test_split_matches_oracle(case):
-    B, H, Sq, Sk, causal, dtype = case
-    D = 64
+    B, H, Sq, Sk, causal, dtype, D = case
     say("case split", case)
     assert fa.fa_fwd_plan(B, H, Sq, D, causal, fa.BF16 if dtype == "bf16" else fa.F16)[0] == 128
     q, k, v = inputs(B, H, Sq, Sk, D, dtype, seed=5000 + Sq + 3 * Sk)
@@ -72,10 +80,11 @@ def test_split_matches_oracle(case):
     say("  ", st)
 
 
-def test_split_strided_views():
+@pytest.mark.parametrize("D", [64, 128])
+def test_split_strided_views(D):
     """[B, S, H, D] views in and out: bit for bit the contiguous call."""
-    B, H, Sq, Sk, D = 2, 3, 333, 400, 64
-    q, k, v = inputs(B, H, Sq, Sk, D, "bf16", seed=5100)
+    B, H, Sq, Sk = 2, 3, 333, 400
+    q, k, v = inputs(B, H, Sq, Sk, D, "bf16", seed=5100 + D)
     views = [t.to(DEV).transpose(1, 2).contiguous().transpose(1, 2) for t in (q, k, v)]
     out = torch.empty((B, Sq, H, D), dtype=q.dtype, device=DEV).transpose(1, 2)
     o, lse = fa.forward(*views, causal=True, out=out)

@@ -43,10 +43,10 @@
 // * Edges.  All global traffic uses buffer instructions with the head's
 //   extent as the record count: reads past the sequence end return zero and
 //   writes past it are dropped, so ragged S needs no branches on loads.
-// * Key split (the SPLIT instances, D = 64): for grids too small to fill
-//   the chip, both wave groups own the same 128 query rows and take the even
-//   and odd K/V tiles respectively; the two partial (O, running max, running
-//   sum) are merged through LDS at the end, the same rescale-and-add as the
+// * Key split (the SPLIT instances): for grids too small to fill the chip,
+//   both wave groups own the same 128 query rows and take the even and odd
+//   K/V tiles respectively; the two partial (O, running max, running sum)
+//   are merged through LDS at the end, the same rescale-and-add as the
 //   online softmax's own update.
 // * Optional boolean mask (the MASK instances): each lane reads the mask
 //   bytes of its query row and its 32 keys of a tile one step ahead and sets
@@ -212,7 +212,7 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
 
 template <int D, int DT, bool CAUSAL, bool MASK, bool SPLIT>
 __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
-    static_assert(!SPLIT || (D == 64 && !MASK), "the split instance is for D = 64 without a mask");
+    static_assert(!(SPLIT && MASK), "the split instance takes no mask");
     constexpr int NW = 8;
     constexpr int NT = 512;
     constexpr int BR = SPLIT ? 128 : 256;
@@ -220,7 +220,7 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
     constexpr int DB = D / 32;
     constexpr int TILE_BYTES = BC * D * 2;
     constexpr int SLOT_BYTES = 2 * TILE_BYTES;      // K tile then V tile
-    constexpr int NSLOT = SPLIT ? 8 : 4;
+    constexpr int NSLOT = (SPLIT && D == 64) ? 8 : 4;
     constexpr int CHUNKS = TILE_BYTES / 16;
     constexpr int LPT = CHUNKS / NT;                // 16-byte loads per thread per tensor
     static_assert(CHUNKS % NT == 0, "tile must split evenly over threads");
@@ -534,6 +534,64 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
     // so its values are finite and its probabilities exactly 0).  The ring has
     // eight slots; the loads of step s + 2 are issued during step s.
     const int ns = (nt + 1) >> 1;
+    if constexpr (D == 128) {
+    // At D = 128 the four-slot ring holds the split with loads one step
+    // ahead: in step s group 1 loads K of tiles 2s + 2 and 2s + 3 (into the K
+    // halves last read in step s - 1) and group 0, before its matrix phase,
+    // V of tiles 2s and 2s + 1 (into the V halves last read in step s - 1).
+    // Every load of step s is consumed in step s + 1, so each step ends with
+    // all of them complete.
+    auto end_split = [&]() {
+        wait_vmcnt<0>();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
+    if (grp != 0) {
+        issue_tile(0);
+        issue_tile(1);
+    }
+    end_split();
+    if (grp == 0) {
+        issue_tile(0);
+        issue_tile(1);
+        qk(0);
+        mid_barrier();
+        swork(0);
+        end_split();
+        for (int st = 1; st < ns; ++st) {
+            issue_tile(2 * st);
+            issue_tile(2 * st + 1);
+            mphase2(2 * st - 2, 2 * st);
+            mid_barrier();
+            swork(2 * st);
+            end_split();
+        }
+        pv(2 * ns - 2);
+        mid_barrier();
+    } else {
+        if (ns > 1) {
+            issue_tile(2);
+            issue_tile(3);
+        }
+        mid_barrier();
+        qk(1);
+        end_split();
+        for (int st = 1; st < ns; ++st) {
+            if (st + 1 < ns) {
+                issue_tile(2 * st + 2);
+                issue_tile(2 * st + 3);
+            }
+            swork(2 * st - 1);
+            mid_barrier();
+            mphase2(2 * st - 1, 2 * st + 1);
+            end_split();
+        }
+        swork(2 * ns - 1);
+        mid_barrier();
+        pv(2 * ns - 1);
+    }
+    } else {
     auto issue_pair = [&](int st) { issue_tile(2 * st); issue_tile(2 * st + 1); };
     auto end_split = [&](int st) {
         if (st + 2 < ns) wait_vmcnt<4 * LPT>();
@@ -575,6 +633,7 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
         swork(2 * ns - 1);
         mid_barrier();
         pv(2 * ns - 1);
+    }
     }
     // Merge: group 1 hands its O accumulators, running max and sum to the
     // wave of group 0 that owns the same rows (same lane layout), which
@@ -689,16 +748,10 @@ template <int D, int DT, bool CAUSAL>
 static hipError_t launch_kernel(const FwdParams& p, int64_t grid, bool split, hipStream_t stream) {
     if (p.mask != nullptr)
         hipLaunchKernelGGL((fa_fwd_kernel<D, DT, CAUSAL, true, false>), dim3((unsigned)grid), dim3(512), 0, stream, p);
-    else if constexpr (D == 64) {
-        if (split)
-            hipLaunchKernelGGL((fa_fwd_kernel<D, DT, CAUSAL, false, true>), dim3((unsigned)grid), dim3(512), 0,
-                               stream, p);
-        else
-            hipLaunchKernelGGL((fa_fwd_kernel<D, DT, CAUSAL, false, false>), dim3((unsigned)grid), dim3(512), 0,
-                               stream, p);
-    } else {
+    else if (split)
+        hipLaunchKernelGGL((fa_fwd_kernel<D, DT, CAUSAL, false, true>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    else
         hipLaunchKernelGGL((fa_fwd_kernel<D, DT, CAUSAL, false, false>), dim3((unsigned)grid), dim3(512), 0, stream, p);
-    }
     return hipGetLastError();
 }
 
@@ -711,8 +764,8 @@ hipError_t launch_fwd(const FwdParams& p, int D, int dtype, bool causal, int64_t
                       hipStream_t stream) {
     if (D == 64) return dtype == 0 ? launch_c<64, 0>(p, causal, grid, split, stream)
                                    : launch_c<64, 1>(p, causal, grid, split, stream);
-    return dtype == 0 ? launch_c<128, 0>(p, causal, grid, false, stream)
-                      : launch_c<128, 1>(p, causal, grid, false, stream);
+    return dtype == 0 ? launch_c<128, 0>(p, causal, grid, split, stream)
+                      : launch_c<128, 1>(p, causal, grid, split, stream);
 }
 
 }  // namespace fa

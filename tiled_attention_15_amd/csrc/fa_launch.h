@@ -34,7 +34,7 @@ struct FwdParams {
 };
 
 // Enqueue the forward kernel (the masked instance when p.mask is set; the
-// key-split instance when split, D = 64 only, p.nqb counted in
+// key-split instance when split, p.nqb counted in
 // kBlockQSplit-row blocks); returns hipGetLastError() after the launch.
 hipError_t launch_fwd(const FwdParams& p, int D, int dtype, bool causal, int64_t grid, bool split,
                       hipStream_t stream);
