@@ -33,18 +33,6 @@ def inputs(B, H, Sq, Sk, D, dtype, seed):
     return q[:, :, :Sq].contiguous(), k, v
 
 
-def test_split_is_chosen_for_small_grids():
-    br, bc, grid, _ = fa.fa_fwd_plan(2, 12, 2048, 64, True, 0)     # the GPT-shaped workload: 192 blocks
-    assert (br, bc, grid) == (128, 64, 2 * 12 * 16)
-    br, _, grid, _ = fa.fa_fwd_plan(4, 64, 2048, 64, True, 0)      # 2048 blocks of 256 rows
-    assert (br, grid) == (256, 4 * 64 * 8)
-    assert fa.fa_fwd_plan(1, 32, 1024, 128, False, 1)[0] == 128    # 128 blocks: the doubled grid fits
-    assert fa.fa_fwd_plan(1, 33, 1024, 128, False, 1)[0] == 256    # 132 blocks, non-causal: no split
-    assert fa.fa_fwd_plan(1, 33, 1024, 128, True, 1)[0] == 128     # causal, fewer blocks than CUs
-    assert fa.fa_fwd_plan(1, 64, 1024, 128, True, 1)[0] == 256     # 256 blocks
-    assert fa.fa_fwd_plan(1, 2, 2048, 256, True, 1)[0] == 128      # D = 256: the general kernel's blocks
-
-
 CASES = [
     # (B, H, Sq, Sk, causal, dtype, D)
     (1, 2, 256, 256, False, "f16", 64),      # the tiny workload's shape
