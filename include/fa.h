@@ -159,7 +159,8 @@ int fa_version(void);
  *              instance: both wave groups on the same 128 rows, the K/V
  *              tiles shared out even/odd between them and the two partial
  *              results merged; with an odd count one extra, fully masked
- *              tile is visited, not counted below),
+ *              tile is visited, not counted below; fa_fwd_ext makes the same
+ *              choice for a mask without dropout),
  *   block_kv   keys per K/V tile (B_c),
  *   grid       workgroups launched (B * H * ceil(S / B_r)),
  *   tiles      (query block, K/V tile) pairs the kernel processes: for a

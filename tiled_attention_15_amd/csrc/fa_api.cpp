@@ -31,16 +31,17 @@ int validate_shape(int B, int H, int Sq, int Sk, int D, int dtype) {
     return FA_OK;
 }
 
-// The key-split instance of the tuned kernel (D = 64 or 128, no mask):
+// The key-split instances of the tuned kernel (D = 64 or 128, with or
+// without a mask):
 // 128-row blocks with the key range split between the two wave groups
 // double the workgroups and halve each one's chain of K/V steps.  Used when
 // the doubled grid still runs in one round (at most half as many 256-row
 // blocks as compute units), or, under the causal rule, whenever the 256-row
 // blocks leave compute units idle (their chains differ in length, so the
 // longest one sets the time).
-bool use_split(int B, int H, int Sq, int D, bool has_mask, bool causal) {
+bool use_split(int B, int H, int Sq, int D, bool causal) {
     const int64_t blocks = (int64_t)B * H * ((Sq + fa::kBlockQ - 1) / fa::kBlockQ);
-    if (D == 256 || has_mask) return false;
+    if (D == 256) return false;
     return 2 * blocks <= fa::kComputeUnits || (causal && blocks < fa::kComputeUnits);
 }
 
@@ -111,7 +112,7 @@ static int launch_tuned(const void* q, const void* k, const void* v, void* o, fl
     p.Sk = Sk;
     p.H = H;
     p.BH = B * H;
-    const bool split = use_split(B, H, Sq, D, mask != nullptr, causal != 0);
+    const bool split = use_split(B, H, Sq, D, causal != 0);
     const int br = split ? fa::kBlockQSplit : fa::kBlockQ;
     p.nqb = (Sq + br - 1) / br;
     p.scale_log2e = (float)((double)scale * 1.4426950408889634074);
@@ -156,7 +157,7 @@ int fa_fwd_plan(int B, int H, int S, int D, int causal, int dtype, int* block_q,
     // D = 256 runs on the general kernel (128-row blocks, 32-key tiles); a
     // small grid on the key-split instance (128-row blocks)
     const int br = D == 256 ? fa::ext::kQueryBlock
-                 : use_split(B, H, S, D, false, causal != 0) ? fa::kBlockQSplit : fa::kBlockQ;
+                 : use_split(B, H, S, D, causal != 0) ? fa::kBlockQSplit : fa::kBlockQ;
     const int bc = D == 256 ? fa::ext::key_tile(256) : fa::kBlockKV;
     const int64_t nqb = (S + br - 1) / br;
     const int64_t nkv = (S + bc - 1) / bc;

@@ -212,7 +212,6 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
 
 template <int D, int DT, bool CAUSAL, bool MASK, bool SPLIT>
 __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
-    static_assert(!(SPLIT && MASK), "the split instance takes no mask");
     constexpr int NW = 8;
     constexpr int NT = 512;
     constexpr int BR = SPLIT ? 128 : 256;
@@ -547,6 +546,10 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     };
+    // With a mask each group reads the mask words of its own next tile
+    // right after its tile loads and applies them at the start of its
+    // softmax phase (every step ends with all loads complete).
+    if constexpr (MASK) load_mask(grp);
     if (grp != 0) {
         issue_tile(0);
         issue_tile(1);
@@ -557,6 +560,10 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
         issue_tile(1);
         qk(0);
         mid_barrier();
+        if constexpr (MASK) {
+            mask_scores();
+            if (ns > 1) load_mask(2);
+        }
         swork(0);
         end_split();
         for (int st = 1; st < ns; ++st) {
@@ -564,6 +571,10 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
             issue_tile(2 * st + 1);
             mphase2(2 * st - 2, 2 * st);
             mid_barrier();
+            if constexpr (MASK) {
+                mask_scores();
+                if (st + 1 < ns) load_mask(2 * st + 2);
+            }
             swork(2 * st);
             end_split();
         }
@@ -578,43 +589,56 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
         qk(1);
         end_split();
         for (int st = 1; st < ns; ++st) {
+            if constexpr (MASK) mask_scores();
             if (st + 1 < ns) {
                 issue_tile(2 * st + 2);
                 issue_tile(2 * st + 3);
             }
+            if constexpr (MASK) load_mask(2 * st + 1);
             swork(2 * st - 1);
             mid_barrier();
             mphase2(2 * st - 1, 2 * st + 1);
             end_split();
         }
+        if constexpr (MASK) mask_scores();
         swork(2 * ns - 1);
         mid_barrier();
         pv(2 * ns - 1);
     }
     } else {
     auto issue_pair = [&](int st) { issue_tile(2 * st); issue_tile(2 * st + 1); };
-    auto end_split = [&](int st) {
-        if (st + 2 < ns) wait_vmcnt<4 * LPT>();
-        else wait_vmcnt<0>();
+    // mask_after: this wave requested mask words after this step's tile loads
+    auto end_split = [&](int st, bool mask_after) {
+        if (st + 2 < ns) {
+            if (MASK && mask_after) wait_vmcnt<4 * LPT + 8>();
+            else wait_vmcnt<4 * LPT>();
+        } else {
+            wait_vmcnt<0>();
+        }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     };
+    if constexpr (MASK) load_mask(grp);
     issue_pair(0);
     if (ns > 1) issue_pair(1);
-    end_split(-1);
+    end_split(-1, false);
     if (grp == 0) {
         qk(0);
         mid_barrier();
+        if constexpr (MASK) mask_scores();
         if (ns > 2) issue_pair(2);
+        if constexpr (MASK) if (ns > 1) load_mask(2);
         swork(0);
-        end_split(0);
+        end_split(0, true);
         for (int st = 1; st < ns; ++st) {
             mphase2(2 * st - 2, 2 * st);
             mid_barrier();
+            if constexpr (MASK) mask_scores();
             if (st + 2 < ns) issue_pair(st + 2);
+            if constexpr (MASK) if (st + 1 < ns) load_mask(2 * st + 2);
             swork(2 * st);
-            end_split(st);
+            end_split(st, true);
         }
         pv(2 * ns - 2);
         mid_barrier();
@@ -622,14 +646,17 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
         if (ns > 2) issue_pair(2);
         mid_barrier();
         qk(1);
-        end_split(0);
+        end_split(0, false);
         for (int st = 1; st < ns; ++st) {
+            if constexpr (MASK) mask_scores();
             if (st + 2 < ns) issue_pair(st + 2);
+            if constexpr (MASK) load_mask(2 * st + 1);
             swork(2 * st - 1);
             mid_barrier();
             mphase2(2 * st - 1, 2 * st + 1);
-            end_split(st);
+            end_split(st, true);
         }
+        if constexpr (MASK) mask_scores();
         swork(2 * ns - 1);
         mid_barrier();
         pv(2 * ns - 1);
@@ -746,7 +773,9 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
 
 template <int D, int DT, bool CAUSAL>
 static hipError_t launch_kernel(const FwdParams& p, int64_t grid, bool split, hipStream_t stream) {
-    if (p.mask != nullptr)
+    if (p.mask != nullptr && split)
+        hipLaunchKernelGGL((fa_fwd_kernel<D, DT, CAUSAL, true, true>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    else if (p.mask != nullptr)
         hipLaunchKernelGGL((fa_fwd_kernel<D, DT, CAUSAL, true, false>), dim3((unsigned)grid), dim3(512), 0, stream, p);
     else if (split)
         hipLaunchKernelGGL((fa_fwd_kernel<D, DT, CAUSAL, false, true>), dim3((unsigned)grid), dim3(512), 0, stream, p);
