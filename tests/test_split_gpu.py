@@ -97,3 +97,39 @@ def test_split_gpt_workload_all_rows_of_two_heads():
                                                 bits(v[sl].contiguous()), scale=w.scale, causal=True, dtype="f16")
         st = parity.assert_parity(to64(o[sl]), to64(lse[sl]), o_ref, l_ref, "f16", "gpt head %d,%d" % (b, h))
         say("  ", b, h, st)
+
+
+def test_split_masked_gpt_workload_two_heads():
+    """The GPT-shaped workload with one shared random mask (85% kept) runs the
+    masked key-split instance: every row of two heads against the oracle."""
+    w = WORKLOADS["gpt_causal_2x12x2048x64_f16"]
+    q, k, v = workload_inputs(w)
+    assert fa.fa_fwd_plan(w.B, w.H, w.S, w.D, True, fa.F16)[0] == 128
+    rng = np.random.default_rng(5200)
+    m = (rng.random((w.S, w.S)) < 0.85).astype(np.uint8)
+    o, lse = fa.forward_ext(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, mask=torch.from_numpy(m).to(DEV))
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (1, 7)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        o_ref, l_ref = oracle.attention_fwd_ext(bits(q[sl].contiguous()), bits(k[sl].contiguous()),
+                                                bits(v[sl].contiguous()), scale=w.scale, causal=True, dtype="f16",
+                                                mask=m, mask_strides=(0, 0, w.S))
+        st = parity.assert_parity(to64(o[sl]), to64(lse[sl]), o_ref, l_ref, "f16", "masked gpt head %d,%d" % (b, h))
+        say("  ", b, h, st)
+
+
+def test_split_d128_two_full_heads():
+    """1x16x2048x128 bf16 causal (128 blocks of 256 rows: the D = 128 key
+    split): every row of heads 0 and 15 against the oracle."""
+    B, H, S, D = 1, 16, 2048, 128
+    assert fa.fa_fwd_plan(B, H, S, D, True, fa.BF16)[0] == 128
+    q, k, v = inputs(B, H, S, S, D, "bf16", seed=5300)
+    o, lse = fa.forward(q.to(DEV), k.to(DEV), v.to(DEV), causal=True)
+    torch.cuda.synchronize()
+    for h in (0, 15):
+        sl = (slice(0, 1), slice(h, h + 1))
+        o_ref, l_ref = oracle.attention_fwd_ext(bits(q[sl].contiguous()), bits(k[sl].contiguous()),
+                                                bits(v[sl].contiguous()), scale=softmax_scale(D), causal=True,
+                                                dtype="bf16")
+        st = parity.assert_parity(to64(o[sl]), to64(lse[sl]), o_ref, l_ref, "bf16", "d128 split head %d" % h)
+        say("  ", h, st)
