@@ -78,10 +78,11 @@ typedef enum {
  *            skip it.
  *   B, H, S  batch, heads, sequence length (>= 1; any S, not only multiples
  *            of the tile; B*H*S*D < 2^40 and S*D*2 bytes < 2^31).
- *   D        head dimension, 64, 128 or 256.  D = 256 (named among the
- *            head dimensions of "FlashAttention-2 on Ascend NPU" (2048ai.net),
- *            tiling parameters) runs on the general kernel of fa_fwd_ext
- *            (128-row blocks, 32-key tiles), the others on the tuned one.
+ *   D        head dimension, 64, 128 or 256 (named among the head
+ *            dimensions of "FlashAttention-2 on Ascend NPU" (2048ai.net),
+ *            tiling parameters).  D = 256 runs the tuned kernel with
+ *            128-row blocks whose two wave groups split the head dimension
+ *            (each computes the full scores and accumulates half of O).
  *   scale    softmax scale applied to q.k (callers normally pass
  *            1/sqrt(D)); finite and > 0.
  *   causal   0: every key visible; nonzero: key j visible to query i iff
@@ -153,7 +154,8 @@ int fa_version(void);
  * fa_fwd_plan -- the launch fa_fwd would make, without launching it.
  *
  * Fills (each pointer may be NULL):
- *   block_q    query rows per workgroup (B_r): 256; 128 at D = 256, and at
+ *   block_q    query rows per workgroup (B_r): 256; 128 at D = 256 (the
+ *              head-dimension split), and at
  *              D = 64 or 128 when n = B * H * ceil(S / 256) satisfies
  *              2n <= 256, or n < 256 for a causal call (the key-split
  *              instance: both wave groups on the same 128 rows, the K/V

@@ -277,14 +277,15 @@ def test_ext_rejects_bad_arguments(lib):
     assert ecall(Sq=1 << 24, Sk=1 << 24, ms=(0, 0, 1 << 24)) == 2    # head span beyond 32-bit offsets
 
 
-def test_plan_d256_uses_the_general_kernel(lib):
+def test_plan_d256_uses_128_row_blocks(lib):
+    """D = 256: 128-row blocks (the head-dimension split) of 64-key tiles."""
     for causal in (0, 1):
         br, bc, grid, tiles = fa.fa_fwd_plan(2, 3, 1000, 256, causal, 1)
-        assert (br, bc) == (128, 32)
+        assert (br, bc) == (128, 64)
         nqb = (1000 + 127) // 128
         assert grid == 2 * 3 * nqb
-        nkv = (1000 + 31) // 32
-        want = sum(min(nkv, (min(1000, (qb + 1) * 128) + 31) // 32) if causal else nkv for qb in range(nqb))
+        nkv = (1000 + 63) // 64
+        want = sum(min(nkv, (min(1000, (qb + 1) * 128) + 63) // 64) if causal else nkv for qb in range(nqb))
         assert tiles == want * 6
 
 

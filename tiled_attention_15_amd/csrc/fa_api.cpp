@@ -113,7 +113,9 @@ static int launch_tuned(const void* q, const void* k, const void* v, void* o, fl
     p.H = H;
     p.BH = B * H;
     const bool split = use_split(B, H, Sq, D, causal != 0);
-    const int br = split ? fa::kBlockQSplit : fa::kBlockQ;
+    // 128-row blocks for the key-split instances and at D = 256 (the
+    // head-dimension split: both wave groups on the same rows)
+    const int br = (split || D == 256) ? fa::kBlockQSplit : fa::kBlockQ;
     p.nqb = (Sq + br - 1) / br;
     p.scale_log2e = (float)((double)scale * 1.4426950408889634074);
     p.q_sb = q_strides[0], p.q_sh = q_strides[1], p.q_ss = (int)q_strides[2];
@@ -154,11 +156,10 @@ int fa_fwd_plan(int B, int H, int S, int D, int causal, int dtype, int* block_q,
     int st = validate_shape(B, H, S, S, D, dtype);
     if (st == FA_OK && !head_span_ok(S, D, D)) st = FA_ERR_SHAPE;
     if (st != FA_OK) return st;
-    // D = 256 runs on the general kernel (128-row blocks, 32-key tiles); a
-    // small grid on the key-split instance (128-row blocks)
-    const int br = D == 256 ? fa::ext::kQueryBlock
-                 : use_split(B, H, S, D, causal != 0) ? fa::kBlockQSplit : fa::kBlockQ;
-    const int bc = D == 256 ? fa::ext::key_tile(256) : fa::kBlockKV;
+    // 128-row blocks at D = 256 (head-dimension split) and on small grids
+    // (key split)
+    const int br = (D == 256 || use_split(B, H, S, D, causal != 0)) ? fa::kBlockQSplit : fa::kBlockQ;
+    const int bc = fa::kBlockKV;
     const int64_t nqb = (S + br - 1) / br;
     const int64_t nkv = (S + bc - 1) / bc;
     if (block_q) *block_q = br;
@@ -209,32 +210,6 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
         if (overlap(ll, lh, ql, qh) || overlap(ll, lh, kl, kh) || overlap(ll, lh, vl, vh) ||
             overlap(ll, lh, ol, oh))
             return FA_ERR_ALIAS;
-    }
-
-    if (D == 256) {
-        // the tuned kernel holds O and Q in registers for D <= 128; D = 256
-        // runs on the general kernel with neither mask nor dropout
-        fa::ext::ExtParams e = {};
-        e.q = q;
-        e.k = k;
-        e.v = v;
-        e.o = o;
-        e.lse = lse;
-        e.q_sb = q_strides[0], e.q_sh = q_strides[1], e.q_ss = (int)q_strides[2];
-        e.k_sb = k_strides[0], e.k_sh = k_strides[1], e.k_ss = (int)k_strides[2];
-        e.v_sb = v_strides[0], e.v_sh = v_strides[1], e.v_ss = (int)v_strides[2];
-        e.o_sb = o_strides[0], e.o_sh = o_strides[1], e.o_ss = (int)o_strides[2];
-        e.mask = nullptr;
-        e.Sq = Sq;
-        e.Sk = Sk;
-        e.H = H;
-        e.BH = B * H;
-        e.nqb = (Sq + fa::ext::kQueryBlock - 1) / fa::ext::kQueryBlock;
-        e.scale_log2e = (float)((double)scale * 1.4426950408889634074);
-        e.drop_t = 0;
-        e.keep_scale = 1.0f;
-        const hipError_t err = fa::ext::launch_ext(e, D, dtype, causal != 0, (hipStream_t)stream);
-        return err == hipSuccess ? FA_OK : FA_ERR_HIP;
     }
 
     return launch_tuned(q, k, v, o, lse, B, H, Sq, Sk, D, q_strides, k_strides, v_strides, o_strides, nullptr,
@@ -392,10 +367,10 @@ static int ext_common(const void* q, const void* k, const void* v, void* o, floa
     }
     if (lse && overlap(out[0][0], out[0][1], out[1][0], out[1][1])) return FA_ERR_ALIAS;
 
-    // No dropout at D <= 128: the tuned kernel, with the mask if there is
-    // one.  Without a mask this is the plain forward exactly as
-    // fa_fwd_strided runs it (the two calls agree bit for bit).
-    if (t == 0 && D != 256 && head_span_ok(Sq, strides[2], D) && head_span_ok(Sk, strides[5], D) &&
+    // No dropout: the tuned kernel (at D = 256 only without a mask), with the
+    // mask if there is one.  Without a mask this is the plain forward exactly
+    // as fa_fwd_strided runs it (the two calls agree bit for bit).
+    if (t == 0 && (D != 256 || !mask) && head_span_ok(Sq, strides[2], D) && head_span_ok(Sk, strides[5], D) &&
         head_span_ok(Sk, strides[8], D) && head_span_ok(Sq, strides[11], D))
         return launch_tuned(q, k, v, o, lse, B, H, Sq, Sk, D, strides, strides + 3, strides + 6, strides + 9, mask,
                             mask_strides, scale, causal, dtype, stream);

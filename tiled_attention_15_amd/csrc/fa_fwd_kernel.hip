@@ -123,7 +123,7 @@ __device__ __forceinline__ float xsum32(float x) {
 template <int D>
 __device__ __forceinline__ int kswz(int row) {
     row &= 31;
-    if constexpr (D == 128) {
+    if constexpr (D >= 128) {
         return (row & 3) | (((row >> 4) & 1) << 2) | (((row >> 2) & 1) << 3);
     } else {
         return ((row & 3) | (((row >> 4) & 1) << 2)) ^ ((row >> 2) & 1);
@@ -131,7 +131,7 @@ __device__ __forceinline__ int kswz(int row) {
 }
 template <int D>
 __device__ __forceinline__ int vseg_swz(int row) {
-    return (D == 128) ? (row & 3) : (row & 1);
+    return (D >= 128) ? (row & 3) : (row & 1);
 }
 // byte offset inside a K tile of 16-byte chunk `ch` of row `row`
 template <int D>
@@ -214,12 +214,17 @@ template <int D, int DT, bool CAUSAL, bool MASK, bool SPLIT>
 __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
     constexpr int NW = 8;
     constexpr int NT = 512;
-    constexpr int BR = SPLIT ? 128 : 256;
+    // D = 256: the two wave groups share 128 query rows and split the head
+    // dimension (each wave holds half of O and computes the full scores).
+    constexpr bool DSPLIT = D == 256;
+    static_assert(!DSPLIT || (!MASK && !SPLIT), "D = 256 has one instance");
+    constexpr int BR = (SPLIT || DSPLIT) ? 128 : 256;
     constexpr int DC = D / 16;
     constexpr int DB = D / 32;
+    constexpr int DO = DSPLIT ? DB / 2 : DB;          // 32-column O blocks this wave holds
     constexpr int TILE_BYTES = BC * D * 2;
     constexpr int SLOT_BYTES = 2 * TILE_BYTES;      // K tile then V tile
-    constexpr int NSLOT = (SPLIT && D == 64) ? 8 : 4;
+    constexpr int NSLOT = DSPLIT ? 2 : (SPLIT && D == 64) ? 8 : 4;
     constexpr int CHUNKS = TILE_BYTES / 16;
     constexpr int LPT = CHUNKS / NT;                // 16-byte loads per thread per tensor
     static_assert(CHUNKS % NT == 0, "tile must split evenly over threads");
@@ -240,7 +245,8 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
     // last query row sees the last key).
     const int diag = Sk - Sq;
     const int q0 = qb * BR;
-    const int qw0 = q0 + (SPLIT ? (wid & 3) : wid) * 32;   // split: both groups share the rows
+    const int qw0 = q0 + ((SPLIT || DSPLIT) ? (wid & 3) : wid) * 32;   // split: both groups share the rows
+    const int dob = DSPLIT ? grp * DO : 0;                             // first O block of this wave
     const int b_ = bh / p.H, h_ = bh - b_ * p.H;
 
     // One buffer descriptor per tensor and head; its record count is the
@@ -331,9 +337,9 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
     for (int c = 0; c < DC; ++c)
         qf[c] = __builtin_amdgcn_raw_buffer_load_b128(rq, ((qw0 + lq) * p.q_ss + 16 * c + 8 * g) * 2, 0, 0);
 
-    f32x16 oacc[DB];
+    f32x16 oacc[DO];
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
+    for (int b = 0; b < DO; ++b)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[b][i] = 0.0f;
     f32x16 s[2];
@@ -361,9 +367,9 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
 #pragma unroll
-            for (int b = 0; b < DB; ++b) {
+            for (int b = 0; b < DO; ++b) {
                 const int kb2 = kc >> 1, c = kc & 1;
-                const int off = (vb ^ (b << 6)) + (32 * kb2 + 8 * c) * (2 * D);
+                const int off = (vb ^ ((b + dob) << 6)) + (32 * kb2 + 8 * c) * (2 * D);
                 const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (__attribute__((address_space(3))) i16x4*)(smem + off));
                 const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -437,7 +443,7 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
             m_run = m_new;
             l_run *= alpha;
 #pragma unroll
-            for (int b = 0; b < DB; ++b)
+            for (int b = 0; b < DO; ++b)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) oacc[b][i] *= alpha;
         }
@@ -469,7 +475,7 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
     // of their use, so the matrix core does not wait on LDS latency.
     auto mphase_schedule = [&]() {
         constexpr int MFMA = 0x008, DSR = 0x100;
-        constexpr int PV_N = 4 * DB, QK_N = 2 * DC;         // MFMAs of each product
+        constexpr int PV_N = 4 * DO, QK_N = 2 * DC;         // MFMAs of each product
         constexpr int AHEAD = 4;                            // MFMAs of lookahead
         __builtin_amdgcn_sched_group_barrier(DSR, 2 * AHEAD, 0);
 #pragma unroll
@@ -698,6 +704,54 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
             for (int i = 0; i < 16; ++i) oacc[b][i] = a0 * oacc[b][i] + a1 * xbuf[xb + (16 * b + i) * 64];
         m_run = m;
     }
+    } else if constexpr (DSPLIT) {
+    // Head-dimension split (D = 256): waves w and w + 4 own the same 32 rows
+    // and compute the same scores and probabilities (identical instructions on
+    // identical data); wave w accumulates O's columns 0..127, wave w + 4
+    // columns 128..255.  The K/V ring has two slots of 64 KiB (a 32 KiB K tile
+    // and a 32 KiB V tile): in step t group 1 loads K of tile t + 1 (into the
+    // K half whose tile t - 1 was last read in step t - 1) and group 0, before
+    // its matrix phase, V of tile t (into the V half last read in step t - 1);
+    // every step ends with all its loads complete.
+    auto end_step = [&]() {
+        wait_vmcnt<0>();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
+    if (grp != 0) issue_tile(0);
+    end_step();
+    if (grp == 0) {
+        issue_tile(0);
+        qk(0);
+        mid_barrier();
+        swork(0);
+        end_step();
+        for (int t = 1; t < nt; ++t) {
+            issue_tile(t);
+            mphase(t);
+            mid_barrier();
+            swork(t);
+            end_step();
+        }
+        pv(nt - 1);
+        mid_barrier();
+    } else {
+        if (nt > 1) issue_tile(1);
+        mid_barrier();
+        qk(0);
+        end_step();
+        for (int t = 1; t < nt; ++t) {
+            if (t + 1 < nt) issue_tile(t + 1);
+            swork(t - 1);
+            mid_barrier();
+            mphase(t);
+            end_step();
+        }
+        swork(nt - 1);
+        mid_barrier();
+        pv(nt - 1);
+    }
     } else {
     // Prologue: Q, tile 0 and tile 1 requested; tile 0 (and Q) waited for.
     if constexpr (MASK) load_mask(0);
@@ -754,18 +808,18 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     const int qrow = qw0 + lq;
 #pragma unroll
-    for (int b = 0; b < DB; ++b) {
+    for (int b = 0; b < DO; ++b) {
         i32x4 w0, w1;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             w0[e] = pack2<DT>(oacc[b][2 * e] * inv, oacc[b][2 * e + 1] * inv);
             w1[e] = pack2<DT>(oacc[b][8 + 2 * e] * inv, oacc[b][8 + 2 * e + 1] * inv);
         }
-        const uint32_t off = ((uint32_t)qrow * p.o_ss + 32 * b + 16 * g) * 2;
+        const uint32_t off = ((uint32_t)qrow * p.o_ss + 32 * (b + dob) + 16 * g) * 2;
         __builtin_amdgcn_raw_buffer_store_b128(w0, ro, off, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b128(w1, ro, off + 16, 0, 0);
     }
-    if (p.lse != nullptr && g == 0 && qrow < Sq) {
+    if (p.lse != nullptr && g == 0 && qrow < Sq && (!DSPLIT || grp == 0)) {
         const float lse2 = (l_tot > 0.0f) ? (m_run == -INFINITY ? 0.0f : m_run) + log2f(l_tot) : -INFINITY;
         p.lse[(int64_t)bh * Sq + qrow] = lse2 * 0.69314718055994530942f;
     }
@@ -789,8 +843,18 @@ static hipError_t launch_c(const FwdParams& p, bool causal, int64_t grid, bool s
     return causal ? launch_kernel<D, DT, true>(p, grid, split, s) : launch_kernel<D, DT, false>(p, grid, split, s);
 }
 
+template <int DT>
+static hipError_t launch_d256(const FwdParams& p, bool causal, int64_t grid, hipStream_t stream) {
+    if (causal)
+        hipLaunchKernelGGL((fa_fwd_kernel<256, DT, true, false, false>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    else
+        hipLaunchKernelGGL((fa_fwd_kernel<256, DT, false, false, false>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_fwd(const FwdParams& p, int D, int dtype, bool causal, int64_t grid, bool split,
                       hipStream_t stream) {
+    if (D == 256) return dtype == 0 ? launch_d256<0>(p, causal, grid, stream) : launch_d256<1>(p, causal, grid, stream);
     if (D == 64) return dtype == 0 ? launch_c<64, 0>(p, causal, grid, split, stream)
                                    : launch_c<64, 1>(p, causal, grid, split, stream);
     return dtype == 0 ? launch_c<128, 0>(p, causal, grid, split, stream)
