@@ -1,7 +1,7 @@
 """GPU parity of the masked forward on the tuned kernel.
 
 fa_fwd_ext / fa_fwd_ext_strided with a boolean mask and no dropout run the
-tuned kernel's masked instance at D = 64 and 128 (the mask bytes of each
+tuned kernel's masked instance at D = 64, 128 and 256 (the mask bytes of each
 lane's query row read one step ahead, hidden scores set to -inf before the
 online softmax).  Checked here against the fp64 oracle's masked forward,
 and bit for bit against the unmasked kernel where a mask changes nothing
@@ -72,6 +72,8 @@ CASES = [
     (2, 2, 257, 131, 128, False, "bf16", True, 0),
     (1, 3, 1, 1, 128, False, "f16", False, 0),
     (1, 1, 45, 1029, 64, False, "bf16", False, 12),
+    (1, 2, 300, 400, 256, True, "bf16", False, 4),      # D = 256: the head-dimension split
+    (2, 1, 257, 257, 256, False, "f16", True, 0),
 ]
 
 

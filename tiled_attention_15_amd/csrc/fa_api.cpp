@@ -367,10 +367,10 @@ static int ext_common(const void* q, const void* k, const void* v, void* o, floa
     }
     if (lse && overlap(out[0][0], out[0][1], out[1][0], out[1][1])) return FA_ERR_ALIAS;
 
-    // No dropout: the tuned kernel (at D = 256 only without a mask), with the
-    // mask if there is one.  Without a mask this is the plain forward exactly
-    // as fa_fwd_strided runs it (the two calls agree bit for bit).
-    if (t == 0 && (D != 256 || !mask) && head_span_ok(Sq, strides[2], D) && head_span_ok(Sk, strides[5], D) &&
+    // No dropout: the tuned kernel, with the mask if there is one.  Without
+    // a mask this is the plain forward exactly as fa_fwd_strided runs it (the
+    // two calls agree bit for bit).
+    if (t == 0 && head_span_ok(Sq, strides[2], D) && head_span_ok(Sk, strides[5], D) &&
         head_span_ok(Sk, strides[8], D) && head_span_ok(Sq, strides[11], D))
         return launch_tuned(q, k, v, o, lse, B, H, Sq, Sk, D, strides, strides + 3, strides + 6, strides + 9, mask,
                             mask_strides, scale, causal, dtype, stream);

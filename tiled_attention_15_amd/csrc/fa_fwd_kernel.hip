@@ -217,7 +217,7 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
     // D = 256: the two wave groups share 128 query rows and split the head
     // dimension (each wave holds half of O and computes the full scores).
     constexpr bool DSPLIT = D == 256;
-    static_assert(!DSPLIT || (!MASK && !SPLIT), "D = 256 has one instance");
+    static_assert(!DSPLIT || !SPLIT, "D = 256 is split by head dimension, not by keys");
     constexpr int BR = (SPLIT || DSPLIT) ? 128 : 256;
     constexpr int DC = D / 16;
     constexpr int DB = D / 32;
@@ -719,18 +719,30 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     };
+    // With a mask both groups apply the same words (same rows, same tile) at
+    // the start of their softmax phase, before that phase's tile loads, and
+    // request the next tile's words after them.
+    if constexpr (MASK) load_mask(0);
     if (grp != 0) issue_tile(0);
     end_step();
     if (grp == 0) {
         issue_tile(0);
         qk(0);
         mid_barrier();
+        if constexpr (MASK) {
+            mask_scores();
+            if (nt > 1) load_mask(1);
+        }
         swork(0);
         end_step();
         for (int t = 1; t < nt; ++t) {
             issue_tile(t);
             mphase(t);
             mid_barrier();
+            if constexpr (MASK) {
+                mask_scores();
+                if (t + 1 < nt) load_mask(t + 1);
+            }
             swork(t);
             end_step();
         }
@@ -742,12 +754,15 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
         qk(0);
         end_step();
         for (int t = 1; t < nt; ++t) {
+            if constexpr (MASK) mask_scores();
             if (t + 1 < nt) issue_tile(t + 1);
+            if constexpr (MASK) load_mask(t);
             swork(t - 1);
             mid_barrier();
             mphase(t);
             end_step();
         }
+        if constexpr (MASK) mask_scores();
         swork(nt - 1);
         mid_barrier();
         pv(nt - 1);
@@ -843,13 +858,18 @@ static hipError_t launch_c(const FwdParams& p, bool causal, int64_t grid, bool s
     return causal ? launch_kernel<D, DT, true>(p, grid, split, s) : launch_kernel<D, DT, false>(p, grid, split, s);
 }
 
+template <int DT, bool CAUSAL>
+static hipError_t launch_d256c(const FwdParams& p, int64_t grid, hipStream_t stream) {
+    if (p.mask != nullptr)
+        hipLaunchKernelGGL((fa_fwd_kernel<256, DT, CAUSAL, true, false>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    else
+        hipLaunchKernelGGL((fa_fwd_kernel<256, DT, CAUSAL, false, false>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    return hipGetLastError();
+}
+
 template <int DT>
 static hipError_t launch_d256(const FwdParams& p, bool causal, int64_t grid, hipStream_t stream) {
-    if (causal)
-        hipLaunchKernelGGL((fa_fwd_kernel<256, DT, true, false, false>), dim3((unsigned)grid), dim3(512), 0, stream, p);
-    else
-        hipLaunchKernelGGL((fa_fwd_kernel<256, DT, false, false, false>), dim3((unsigned)grid), dim3(512), 0, stream, p);
-    return hipGetLastError();
+    return causal ? launch_d256c<DT, true>(p, grid, stream) : launch_d256c<DT, false>(p, grid, stream);
 }
 
 hipError_t launch_fwd(const FwdParams& p, int D, int dtype, bool causal, int64_t grid, bool split,
