@@ -237,11 +237,12 @@ int64_t fa_naive_workspace_bytes(int B, int H, int S, int D);
  *               dropout_p = 0 keeps everything.
  *   causal, scale, dtype, stream  as for fa_fwd (bottom-right causal rule
  *               when Sq != Sk).
- * Kernels: with dropout_p 0 and every tensor's head spanning less than ((round_up(S, 256) + 64) * row_stride + D) * 2 <
- * 2^31 bytes, the call runs the tuned forward kernel of fa_fwd_strided (its
- * masked instance when mask is set); otherwise the general kernel (128-row
- * blocks) that also draws the dropout decisions.  With mask NULL and dropout_p 0 the result
- * therefore equals fa_fwd_strided's bit for bit.
+ * Kernels: with dropout_p 0 and every tensor's head spanning less than
+ * ((round_up(S, 256) + 64) * row_stride + D) * 2 < 2^31 bytes, the call runs
+ * the tuned forward kernel of fa_fwd_strided (its masked instance when mask
+ * is set); otherwise the general kernel (128-row blocks) that also draws the
+ * dropout decisions.  With mask NULL and dropout_p 0 the result therefore
+ * equals fa_fwd_strided's bit for bit.
  * Returns FA_OK or an fa_status; FA_ERR_MASK_DROPOUT for a bad mask layout
  * or dropout probability.
  */
