@@ -21,11 +21,15 @@ probability P or the score gradient dS) is rounded to the input dtype before
 the fp32-accumulated product, a relative perturbation of at most u per term;
 an fp32 emulation of that rounding on N(0,1) inputs gives a largest error of
 about 1.25 u max|G| and an rms error of about 0.6 u rms(G).  A slice whose
-reference is all zero has no magnitude to be relative to: when the zero comes
-from cancellation (one visible key: dS = P (dP - D) with dP = D exactly) the
-caller passes `zero_scale`, the size of one term of the gradient's sum (for
-dQ: scale max|dO| max|V| max|K|), and the slice must stay within 3 u of it;
-without it (zeros forced by the mask) the slice must be exactly zero.
+reference is all zero has no magnitude to be relative to.  Its zeros come
+either from visibility (no key seen: exactly zero on both sides) or from
+cancellation (one visible key: dS = P (dP - D_i) with dP = D_i = dO . v in
+exact arithmetic).  For the latter the caller passes `zero_tol`, an absolute
+bound from cancellation_tolerances(): the two fp32 dot products of D exact
+terms (dP on the matrix cores, D_i from dO and the stored O) differ by at
+most 2 D 2^-24 sum_d |dO_d v_d|, and with dropout the stored O is
+keep_scale * v rounded to the input dtype, which adds u keep_scale
+sum_d |dO_d v_d|.  Without `zero_tol` the slice must be exactly zero.
 """
 import numpy as np
 
@@ -91,7 +95,23 @@ GRAD_MAX_C = 3.0
 GRAD_RMS_C = 2.0
 
 
-def compare_grad(g_gpu, g_ref, dtype, zero_scale=None):
+def cancellation_tolerances(q, k, v, dout, scale, dtype, dropout_p=0.0):
+    """Absolute bounds for gradient slices that cancel to zero (see the module
+    text): {"dq", "dk", "dv"} from the inputs (CPU tensors or arrays
+    [B, H, S, D]).  dV has no cancellation (its zero slices are exact)."""
+    as64 = lambda t: np.abs(np.asarray(t.float().numpy() if hasattr(t, "float") else t, dtype=np.float64))
+    qa, ka, va, ga = as64(q), as64(k), as64(v), as64(dout)
+    D = qa.shape[-1]
+    # largest sum_d |dO_id v_jd| over all query/key pairs of a head
+    dot = float(np.max(np.matmul(ga, np.swapaxes(va, -1, -2)))) if ga.size and va.size else 0.0
+    t = round(dropout_p * 65536.0)
+    keep_scale = 65536.0 / (65536.0 - t)
+    rel = 2.0 * D * 2.0 ** -24 + (GRAD_U[dtype] if t else 0.0)
+    ds = rel * keep_scale * dot          # bound on |dS| for a row with one visible key (P <= 1)
+    return {"dq": scale * ds * float(np.max(ka)), "dk": scale * ds * float(np.max(qa)), "dv": 0.0}
+
+
+def compare_grad(g_gpu, g_ref, dtype, zero_tol=None):
     """Error statistics of one gradient tensor [..., rows, D], per leading slice."""
     g_gpu = np.asarray(g_gpu, dtype=np.float64)
     g_ref = np.asarray(g_ref, dtype=np.float64)
@@ -107,10 +127,10 @@ def compare_grad(g_gpu, g_ref, dtype, zero_scale=None):
         m = float(np.max(np.abs(r))) if r.size else 0.0
         rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
         if m == 0.0:
-            if zero_scale is None:
+            if not zero_tol:
                 zero_bad += int(np.count_nonzero(a))
             else:
-                zero_bad += int(np.count_nonzero(np.abs(a) > GRAD_MAX_C * u * zero_scale))
+                zero_bad += int(np.count_nonzero(np.abs(a) > zero_tol))
             continue
         net = float(np.max(d - 0.5 * ulp(r, dtype)))
         worst_max = max(worst_max, net / (u * m))
@@ -124,7 +144,7 @@ def grad_ok(st):
             and st["max_in_u"] <= GRAD_MAX_C and st["rms_in_u"] <= GRAD_RMS_C)
 
 
-def assert_grad_parity(g_gpu, g_ref, dtype, what="", zero_scale=None):
-    st = compare_grad(g_gpu, g_ref, dtype, zero_scale)
+def assert_grad_parity(g_gpu, g_ref, dtype, what="", zero_tol=None):
+    st = compare_grad(g_gpu, g_ref, dtype, zero_tol)
     assert grad_ok(st), "gradient parity failed %s: %s" % (what, st)
     return st

@@ -43,15 +43,13 @@ def bshd_empty(like):
     return torch.empty((B, S, H, D), dtype=like.dtype, device=DEV).transpose(1, 2)
 
 
-def zero_scales(q, k, v, g, D):
-    mx = {n: float(t.abs().max()) for n, t in (("q", q), ("k", k), ("v", v), ("g", g))}
-    sc = softmax_scale(D)
-    return {"dq": sc * mx["g"] * mx["v"] * mx["k"], "dk": sc * mx["g"] * mx["v"] * mx["q"], "dv": mx["g"]}
+def zero_scales(q, k, v, g, D, dtype="bf16", p=0.0):
+    return parity.cancellation_tolerances(q, k, v, g, softmax_scale(D), dtype, dropout_p=p)
 
 
 def check_oracle(grads, refs, dtype, what, zs):
     for name, got, ref in zip(("dq", "dk", "dv"), grads, refs):
-        st = parity.assert_grad_parity(to64(got), ref, dtype, "%s %s" % (name, what), zero_scale=zs[name])
+        st = parity.assert_grad_parity(to64(got), ref, dtype, "%s %s" % (name, what), zero_tol=zs[name])
         say("  ", name, st)
 
 
@@ -80,7 +78,7 @@ def test_bwd_bshd_views_match_oracle(case, deterministic):
     torch.cuda.synchronize()
     refs = oracle.attention_bwd(bits(q), bits(k), bits(v), bits(g), scale=softmax_scale(D), causal=causal,
                                 dtype=dtype)
-    check_oracle(grads, refs, dtype, case, zero_scales(q, k, v, g, D))
+    check_oracle(grads, refs, dtype, case, zero_scales(q, k, v, g, D, dtype))
     if deterministic:
         qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
         oc, lc = fa.forward(qd, kd, vd, causal=causal)
@@ -152,7 +150,7 @@ def test_bwd_ext_bshd_views_equal_contiguous(D):
     refs = oracle.attention_bwd_ext(bits(q), bits(k), bits(v), bits(g), scale=softmax_scale(D), causal=True,
                                     dtype=dtype, mask=mask, mask_strides=(H * Sq * Sk, Sq * Sk, Sk),
                                     dropout_p=0.15, seed=99, offset=4)
-    check_oracle(grads, refs, dtype, "bwd_ext strided", zero_scales(q, k, v, g, D))
+    check_oracle(grads, refs, dtype, "bwd_ext strided", zero_scales(q, k, v, g, D, dtype, 0.15))
 
 
 def test_bwd_packed_gradients_are_rejected():

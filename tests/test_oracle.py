@@ -46,9 +46,16 @@ def test_gradient_rule():
     z = np.zeros((1, 1, 4, 4))
     assert parity.grad_ok(parity.compare_grad(z, z, "f16"))
     assert not parity.grad_ok(parity.compare_grad(z + 1e-30, z, "f16"))
-    u16 = parity.GRAD_U["f16"]
-    assert parity.grad_ok(parity.compare_grad(z + 2 * u16, z, "f16", zero_scale=1.0))
-    assert not parity.grad_ok(parity.compare_grad(z + 4 * u16, z, "f16", zero_scale=1.0))
+    assert parity.grad_ok(parity.compare_grad(z + 1e-6, z, "f16", zero_tol=2e-6))
+    assert not parity.grad_ok(parity.compare_grad(z + 3e-6, z, "f16", zero_tol=2e-6))
+    # the cancellation bound: 2 D 2^-24 sum|dO v| (scaled by scale max|K| for dQ);
+    # with dropout the storage rounding u of O is added
+    D = 4
+    qq, kk, vv, gg = (np.ones((1, 1, 2, D)) for _ in range(4))
+    tol = parity.cancellation_tolerances(qq, 2 * kk, vv, gg, 0.5, "bf16")
+    assert abs(tol["dq"] - 0.5 * (2 * D * 2.0 ** -24) * D * 2.0) < 1e-15 and tol["dv"] == 0.0
+    tol_d = parity.cancellation_tolerances(qq, kk, vv, gg, 0.5, "bf16", dropout_p=0.5)
+    assert abs(tol_d["dk"] - 0.5 * (2 * D * 2.0 ** -24 + 2.0 ** -8) * 2.0 * D * 1.0) < 1e-12
     nanv = ref.copy()
     nanv[0, 0, 0, 0] = np.nan
     assert not parity.grad_ok(parity.compare_grad(nanv, ref, "f16"))
