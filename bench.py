@@ -74,10 +74,32 @@ def measured_traffic(workload_name):
     return float(m_val.group(1))
 
 
-def gpu_leg(w, steps, warmup, cold=0):
-    """Times `steps` back-to-back launches (the headline figure); then 50
-    launches timed one by one (median and minimum); with cold > 0, that many
-    launches each preceded by a 512 MiB device write that evicts the caches."""
+def warm_up(step, launches, seconds):
+    """At least `launches` calls of step(), and more until `seconds` of wall
+    time have passed with the GPU busy: the shader clock ramps up over the
+    first tens of milliseconds of sustained work, so a fixed handful of
+    launches can leave the timed region on a still-rising clock."""
+    import torch
+    for _ in range(launches):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            step()
+        n += 4
+        torch.cuda.synchronize()
+    return launches + n
+
+
+def gpu_leg(w, steps, warmup, cold=0, warmup_s=1.0):
+    """Times `steps` back-to-back launches (the headline figure) after a
+    warm-up of at least `warmup` launches and `warmup_s` seconds, with the
+    shader clock stamped on the same stream just before and after the timed
+    launches; then 50 launches timed one by one (median and minimum); with
+    cold > 0, that many launches each preceded by a 512 MiB device write that
+    evicts the caches."""
     import statistics
     import torch
     import tiled_attention_15_amd as fa
@@ -96,21 +118,22 @@ def gpu_leg(w, steps, warmup, cold=0):
         if st != 0:
             raise fa.FaError(st)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_launches = warm_up(step, warmup, warmup_s)
     # events on the stream the kernel is enqueued on (torch's current stream)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ck0 = fa.clock_stamps(dev, stream)
     ev0.record(stream)
     for _ in range(steps):
         step()
     ev1.record(stream)
+    ck1 = fa.clock_stamps(dev, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ev_ms = ev0.elapsed_time(ev1)
+    per_xcd = fa.clock_mhz(ck0, ck1)
     if not torch.isfinite(o).all().item():
         raise RuntimeError("non-finite output in the benchmark run")
 
@@ -134,7 +157,15 @@ def gpu_leg(w, steps, warmup, cold=0):
         stats["cold"] = one_by_one(cold, lambda: scratch.fill_(1))
         stats["cold"]["between_launches"] = "512 MiB device write"
         del scratch
-    return ev_ms / steps, wall / steps * 1e3, stats
+    clock = {"sclk_mhz_mean": round(sum(per_xcd.values()) / max(1, len(per_xcd)), 1),
+             "sclk_mhz_per_xcd": {str(x): round(m, 1) for x, m in sorted(per_xcd.items())},
+             "warmup_launches": warm_launches, "warmup_s_min": warmup_s,
+             "method": "shader-clock and 100 MHz real-time counters read on every XCD by a stamp kernel "
+                       "launched on the same stream just before and after the timed launches"}
+    hashes = {"q": hashlib.sha256(bits(q).tobytes()).hexdigest(),
+              "k": hashlib.sha256(bits(k).tobytes()).hexdigest(),
+              "v": hashlib.sha256(bits(v).tobytes()).hexdigest()}
+    return ev_ms / steps, wall / steps * 1e3, stats, clock, hashes
 
 
 def naive_leg(w, steps, warmup):
@@ -161,9 +192,7 @@ def naive_leg(w, steps, warmup):
         if st != 0:
             raise fa.FaError(st, "fa_naive_fwd")
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, warmup, 0.2)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
@@ -210,9 +239,7 @@ def backward_leg(w, steps, warmup):
             if st != 0:
                 raise fa.FaError(st, "fa_bwd")
 
-        for _ in range(warmup):
-            step()
-        torch.cuda.synchronize()
+        warm_up(step, warmup, 0.2)
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
@@ -252,9 +279,7 @@ def backward_leg(w, steps, warmup):
         if st != 0:
             raise fa.FaError(st, "fa_bwd_ext")
 
-    for _ in range(warmup):
-        step_x()
-    torch.cuda.synchronize()
+    warm_up(step_x, warmup, 0.2)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
@@ -303,9 +328,7 @@ def ext_leg(w, steps, warmup):
             if st != 0:
                 raise fa.FaError(st, "fa_fwd_ext")
 
-        for _ in range(warmup):
-            step()
-        torch.cuda.synchronize()
+        warm_up(step, warmup, 0.2)
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
@@ -447,6 +470,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=HEADLINE, choices=list(WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--warmup-seconds", type=float, default=1.0,
+                    help="minimum wall time of warm-up launches before the timed region "
+                         "(in addition to --warmup launches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-naive", action="store_true",
                     help="skip the unfused comparison path")
@@ -470,7 +496,7 @@ def main():
         print(json.dumps(copy_leg(a.copy_mib, a.steps, a.warmup)), flush=True)
         return
     w = WORKLOADS[a.workload]
-    ms, wall_ms, launch_stats = gpu_leg(w, a.steps, a.warmup, a.cold)
+    ms, wall_ms, launch_stats, clock, hashes = gpu_leg(w, a.steps, a.warmup, a.cold, a.warmup_seconds)
     tflops = w.flops() / (ms * 1e-3) / 1e12
     traffic = measured_traffic(w.name)
     out = {
@@ -488,6 +514,7 @@ def main():
         "data": "synthetic: seeded i.i.d. N(0,1) Q/K/V (Q x%g), resident in HBM" % w.q_mult,
         "config": {"workload": w.name, "B": w.B, "H": w.H, "S": w.S, "D": w.D,
                    "causal": w.causal, "q_mult": w.q_mult, "seed": w.seed},
+        "inputs_sha256": hashes,
         "tokens_per_s": round(w.B * w.S / (ms * 1e-3), 1),
         "pct_of_mfma_peak": round(100.0 * tflops / MFMA_PEAK_TFLOPS, 2),
         "hbm_gbs_algorithmic": round(w.bytes() / (ms * 1e-3) / 1e9, 2),
@@ -496,6 +523,10 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
                      "traffic": traffic},
+        # the peak is quoted at 2.4 GHz; the same fraction against the clock
+        # the chip delivered over the timed region
+        "clock": dict(clock, frac_at_delivered_clock=round(
+            tflops / (MFMA_PEAK_TFLOPS * clock["sclk_mhz_mean"] / 2400.0), 4) if clock["sclk_mhz_mean"] else None),
         "cpu_baseline": None,
     }
     if not a.no_naive:

@@ -77,7 +77,7 @@ typedef enum {
  *            log-sum-exp of each row's visible scaled scores), or NULL to
  *            skip it.
  *   B, H, S  batch, heads, sequence length (>= 1; any S, not only multiples
- *            of the tile; B*H*S*D < 2^40 and S*D*2 bytes < 2^31).
+ *            of the tile; S <= 2^30, B*H*S*D < 2^40 and S*D*2 bytes < 2^31).
  *   D        head dimension, 64, 128 or 256 (named among the head
  *            dimensions of "FlashAttention-2 on Ascend NPU" (2048ai.net),
  *            tiling parameters).  D = 256 runs the tuned kernel with
@@ -157,7 +157,8 @@ int fa_version(void);
  *   block_q    query rows per workgroup (B_r): 256; 128 at D = 256 (the
  *              head-dimension split), and at
  *              D = 64 or 128 when n = B * H * ceil(S / 256) satisfies
- *              2n <= 256, or n < 256 for a causal call (the key-split
+ *              2n <= C, or n < C for a causal call, C the current device's
+ *              compute-unit count (256 on MI355X) (the key-split
  *              instance: both wave groups on the same 128 rows, the K/V
  *              tiles shared out even/odd between them and the two partial
  *              results merged; with an odd count one extra, fully masked
@@ -170,7 +171,9 @@ int fa_version(void);
  *              beyond the query block's last row, i.e. per query block
  *              min(ceil(S / B_c), ceil(min(S, (qb+1)*B_r) / B_c)).
  * Same validation and return codes as fa_fwd (no device pointers are
- * needed: they are not inspected).  Host only; makes no HIP call.
+ * needed: they are not inspected).  Launches nothing; its only HIP calls
+ * read the current device's compute-unit count, once per device (256 when
+ * no device answers).
  * Follows the tile-count and block-count arithmetic of "FlashAttention-2 on
  * Ascend NPU: how ops-transformer reaches 3x" (2048ai.net), section 3.2
  * (ceiling division of the sequence by the block sizes) and the skip rule
@@ -179,6 +182,56 @@ int fa_version(void);
  */
 int fa_fwd_plan(int B, int H, int S, int D, int causal, int dtype,
                 int* block_q, int* block_kv, int64_t* grid, int64_t* tiles);
+
+/*
+ * fa_fwd_diag -- a diagnostic (test-only) launch of the tuned forward on
+ * contiguous tensors: the same kernel and arithmetic as fa_fwd_strided
+ * (same block shape and route, q and o [B, H, Sq, D], k and v [B, H, Sk, D],
+ * causal as there), with three extra outputs for checking it:
+ *
+ *   o32          NULL, or device fp32 [B, H, Sq, D] contiguous: O before its
+ *                rounding to `dtype`, so the kernel's own error can be
+ *                measured against the fp64 result without the storage
+ *                rounding of O.  o is still written, identically.
+ *   tile_counts  NULL, or device uint32 [fa_fwd_diag_tile_slots(...)]: for
+ *                workgroup block n (n = (b*H + h) * nqb + query block) and
+ *                wave w, slot 8*n + w counts the K/V tiles that wave ran
+ *                its softmax on.  Its sum over the waves of a block checks
+ *                the causal skip rule of "catlass FlashAttention tuning for
+ *                a 13B service" (gsyq.cn), "Causal Mask implementation"
+ *                (mode 2) on the device: every wave of a 256-row block runs
+ *                every tile the block visits; in the key-split route the two
+ *                wave groups share them out, with one extra, fully masked
+ *                tile when their count is odd.
+ *   flags        0, or FA_DIAG_REVERSE_ORDER: workgroup i takes the block
+ *                workgroup grid-1-i would take.  Blocks are independent, so
+ *                every output must be bitwise equal to the default order's.
+ *
+ * D must be 64 or 128 (else FA_ERR_UNSUPPORTED, as for an unknown flag);
+ * other errors as for fa_fwd, with o32 and tile_counts also checked for
+ * 16-byte alignment and overlap.  Not for production use: it exists for
+ * the tests.
+ */
+#define FA_DIAG_REVERSE_ORDER 1
+int fa_fwd_diag(const void* q, const void* k, const void* v, void* o, float* lse, float* o32,
+                uint32_t* tile_counts, int B, int H, int Sq, int Sk, int D, float scale,
+                int causal, int dtype, int flags, void* stream);
+
+/* Number of uint32 slots fa_fwd_diag writes to tile_counts for these
+ * arguments (8 per workgroup), or 0 for a shape it rejects. */
+int64_t fa_fwd_diag_tile_slots(int B, int H, int Sq, int D, int causal);
+
+/*
+ * fa_clock_stamps -- a measurement aid: launches `groups` workgroups (1 ..
+ * 65536) on `stream`; thread 0 of workgroup n writes out[4n .. 4n+3] =
+ * {XCD id, shader-clock counter, 100 MHz real-time counter, 0}.  Two calls
+ * around a timed region give each XCD's average shader clock over it:
+ * delta shader ticks / delta real-time ticks * 100 MHz, the clock against
+ * which an achieved fraction of the matrix-core peak (quoted at 2.4 GHz) can
+ * be read.  out: device, 16-byte aligned, groups*4 uint64.  Returns
+ * FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_ALIGN or FA_ERR_HIP on failure.
+ */
+int fa_clock_stamps(uint64_t* out, int groups, void* stream);
 
 /*
  * fa_naive_fwd -- the same forward computed the unfused way, for comparison:

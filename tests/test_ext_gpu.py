@@ -165,6 +165,35 @@ def test_forward_ext_pads_unaligned_mask_rows():
     parity.assert_parity(to64(o), to64(lse), o_ref, l_ref, "f16", "unaligned mask rows")
 
 
+@pytest.mark.parametrize("p", [0.0, 0.1])
+def test_forward_ext_key_padding_mask(p):
+    """A key-padding mask [B, 1, 1, Sk] (broadcast over heads and query rows,
+    a row stride of 0 after expansion) goes through the binding, forward and
+    backward, and matches the oracle with the mask written out in full."""
+    B, H, Sq, Sk, D, dtype = 2, 3, 150, 200, 128, "bf16"
+    q, k, v = inputs(B, H, Sq, Sk, D, dtype, seed=2550)
+    g, _, _ = make_inputs(B, H, Sq, D, dtype, seed=2551)
+    keep = torch.ones(B, 1, 1, Sk, dtype=torch.bool)
+    keep[0, ..., 170:] = False
+    keep[1, ..., 30:60] = False
+    kw = dict(causal=False, mask=keep.to(DEV), dropout_p=p, seed=5, offset=2)
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
+    o, lse = fa.forward_ext(qd, kd, vd, **kw)
+    grads = fa.backward_ext(qd, kd, vd, o, lse, gd, **kw)
+    torch.cuda.synchronize()
+    full = np.ascontiguousarray(keep.expand(B, H, Sq, Sk).numpy().astype(np.uint8))
+    ms = (H * Sq * Sk, Sq * Sk, Sk)
+    o_ref, l_ref = oracle.attention_fwd_ext(bits(q), bits(k), bits(v), scale=softmax_scale(D), causal=False,
+                                            dtype=dtype, mask=full, mask_strides=ms, dropout_p=p, seed=5, offset=2)
+    say("key padding p=%g" % p, parity.assert_parity(to64(o), to64(lse), o_ref, l_ref, dtype, "key padding"))
+    refs = oracle.attention_bwd_ext(bits(q), bits(k), bits(v), bits(g), scale=softmax_scale(D), causal=False,
+                                    dtype=dtype, mask=full, mask_strides=ms, dropout_p=p, seed=5, offset=2)
+    zs = parity.cancellation_tolerances(q, k, v, g, softmax_scale(D), dtype, dropout_p=p)
+    for name, got, ref in zip(("dq", "dk", "dv"), grads, refs):
+        say("  ", name, parity.assert_grad_parity(to64(got), ref, dtype, "key padding %s" % name,
+                                                  zero_tol=zs[name]))
+
+
 @pytest.mark.parametrize("D", [64, 128, 256])
 def test_forward_ext_strided_views(D):
     """[B, S, H, D] views of q, k, v and of the output, with a mask and

@@ -1,8 +1,11 @@
 """GPU parity: the HIP kernel through the C ABI against the fp64 oracle.
 
-Small and ragged shapes are compared element by element on every output;
-the five workload shapes are compared on sampled rows that the oracle
-evaluates one by one, in the same launch configuration the benchmark uses.
+Small and ragged shapes are compared element by element on every output.
+The workload shapes run in the launch configuration the benchmark uses,
+with NaN-filled outputs so that an unwritten element fails, and are
+compared on every row (on the 16384-long workload: every row of eight heads
+and 512 rows of each other head).  The unsplit 256-row instance is also
+checked on ragged, unequal-length and strided shapes.
 """
 import math
 
@@ -14,6 +17,7 @@ import oracle
 from oracle import parity
 import tiled_attention_15_amd as fa
 from workloads import WORKLOADS, bits, make_inputs, softmax_scale, workload_inputs
+from workload_ref import workload_reference
 
 pytestmark = pytest.mark.gpu
 
@@ -88,21 +92,75 @@ def sample_rows(B, H, S, n_random=48, seed=0):
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
-def test_workload_sampled_rows(name):
+def test_workload_every_output(name):
+    """Each workload at full size, in the benchmark's launch configuration:
+    outputs pre-filled with NaN, every element written and finite, and the
+    oracle's rows (all rows of every head; on the 16384-long workload all
+    rows of eight heads and 512 rows of each other head) within the rule."""
     w = WORKLOADS[name]
     q, k, v = workload_inputs(w)
     say("workload", name)
-    o, lse = run_gpu(q, k, v, w.causal, w.scale)
-    assert tuple(o.shape) == (w.B, w.H, w.S, w.D)
-    rows = sample_rows(w.B, w.H, w.S, seed=w.seed)
-    o_ref, lse_ref = oracle.attention_rows(bits(q), bits(k), bits(v), rows, scale=w.scale,
-                                           causal=w.causal, dtype=w.dtype)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o = torch.full((w.B, w.H, w.S, w.D), float("nan"), dtype=w.torch_dtype, device=DEV)
+    lse = torch.full((w.B, w.H, w.S), float("nan"), dtype=torch.float32, device=DEV)
+    fa.forward(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse_out=lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all().item(), "an output element is unwritten or not finite"
+    assert torch.isfinite(lse).all().item(), "an lse element is unwritten or not finite"
+    rows, o_ref, lse_ref = workload_reference(w, q, k, v)
     og = to64(o).reshape(-1, w.D)[rows]
     lg = to64(lse).reshape(-1)[rows]
     st = parity.assert_parity(og, lg, o_ref, lse_ref, w.dtype, name)
-    say(name, st)
-    # every output finite at full size
-    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+    say(name, "rows compared", rows.size, "of", w.B * w.H * w.S, st)
+
+
+# The unsplit 256-row instance (the one the D = 128 workloads run) on ragged,
+# unequal-length and strided shapes: enough blocks that the planner does not
+# take the key-split route.
+UNSPLIT_CASES = [
+    # (B, H, Sq, Sk, D, dtype, causal, layout)
+    (1, 130, 333, 333, 128, "bf16", False, "bhsd"),
+    (1, 130, 333, 333, 128, "f16", True, "bhsd"),
+    (1, 136, 333, 333, 128, "bf16", True, "bhsd"),
+    (1, 130, 300, 700, 128, "bf16", True, "bhsd"),
+    (1, 86, 700, 300, 128, "f16", True, "bhsd"),
+    (1, 86, 700, 300, 64, "bf16", False, "bshd"),
+    (2, 65, 333, 333, 64, "f16", True, "bshd"),
+    (1, 130, 300, 700, 64, "f16", False, "bhsd"),
+]
+
+
+@pytest.mark.parametrize("case", UNSPLIT_CASES, ids=["%dx%dx%dx%dx%d%s%s%s" % (c[0], c[1], c[2], c[3], c[4], c[5],
+                                                                             "c" if c[6] else "n", c[7])
+                                                     for c in UNSPLIT_CASES])
+def test_unsplit_instance_ragged(case):
+    B, H, Sq, Sk, D, dtype, causal, layout = case
+    assert fa.fa_fwd_plan(B, H, Sq, D, causal, fa.BF16 if dtype == "bf16" else fa.F16)[0] == 256
+    say("case unsplit", case)
+    q, k, v = make_inputs(B, H, max(Sq, Sk), D, dtype, seed=3100 + Sq + Sk + D + H, q_mult=2.0, Sk=Sk)
+    q = q[:, :, :Sq].contiguous()
+    if layout == "bshd":
+        qd, kd, vd = (t.transpose(1, 2).contiguous().to(DEV).transpose(1, 2) for t in (q, k, v))
+        o = torch.full((B, Sq, H, D), float("nan"), dtype=q.dtype, device=DEV).transpose(1, 2)
+    else:
+        qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+        o = torch.full((B, H, Sq, D), float("nan"), dtype=q.dtype, device=DEV)
+    lse = torch.full((B, H, Sq), float("nan"), dtype=torch.float32, device=DEV)
+    fa.forward(qd, kd, vd, causal=causal, out=o, lse_out=lse)
+    torch.cuda.synchronize()
+    og, lg = to64(o.contiguous()), to64(lse)
+    assert not np.isnan(og).any() and not np.isnan(lg).any()
+    # every row of four heads, 64 random rows of every head
+    rng = np.random.default_rng(Sq + Sk)
+    BH = B * H
+    full = sorted({0, 1, BH // 2, BH - 1})
+    rows = [h * Sq + np.arange(Sq) for h in full]
+    rows += [h * Sq + rng.choice(Sq, min(Sq, 64), replace=False) for h in range(BH) if h not in full]
+    rows = np.unique(np.concatenate(rows)).astype(np.int64)
+    o_ref, l_ref = oracle.attention_rows(bits(q), bits(k), bits(v), rows, scale=softmax_scale(D), causal=causal,
+                                         dtype=dtype)
+    st = parity.assert_parity(og.reshape(-1, D)[rows], lg.reshape(-1)[rows], o_ref, l_ref, dtype, str(case))
+    say("  ", rows.size, "rows", st)
 
 
 def test_pages_fp16_bound_on_llama_shape():

@@ -16,12 +16,15 @@ __all__ = ["FaError", "fa_fwd", "fa_fwd_strided", "fa_fwd_plan", "fa_naive_fwd",
            "fa_naive_workspace_bytes", "fa_status_string", "fa_version", "forward",
            "naive_forward", "library_path", "F16", "BF16", "STATUS", "fa_bwd",
            "fa_bwd_workspace_bytes", "backward", "fa_fwd_ext", "forward_ext", "fa_bwd_ext",
-           "backward_ext", "fa_bwd_strided", "fa_fwd_ext_strided"]
+           "backward_ext", "fa_bwd_strided", "fa_fwd_ext_strided", "fa_fwd_diag",
+           "fa_fwd_diag_tile_slots", "DIAG_REVERSE_ORDER", "fa_clock_stamps", "clock_stamps",
+           "clock_mhz"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libfa_hip.so")
 
 F16, BF16 = 0, 1
+DIAG_REVERSE_ORDER = 1
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED",
           4: "FA_ERR_ALIGN", 5: "FA_ERR_SCALE", 6: "FA_ERR_HIP", 7: "FA_ERR_ALIAS",
           8: "FA_ERR_STRIDE", 9: "FA_ERR_MASK_DROPOUT"}
@@ -83,6 +86,12 @@ def _load():
     lib.fa_fwd_ext_strided.argtypes = [vp] * 5 + [i] * 5 + [i64p, vp, i64p, f, ctypes.c_uint64, ctypes.c_uint32, f,
                                                              i, i, vp]
     lib.fa_fwd_ext_strided.restype = i
+    lib.fa_fwd_diag.argtypes = [vp] * 7 + [i] * 5 + [f, i, i, i, vp]
+    lib.fa_fwd_diag.restype = i
+    lib.fa_fwd_diag_tile_slots.argtypes = [i] * 5
+    lib.fa_fwd_diag_tile_slots.restype = ctypes.c_int64
+    lib.fa_clock_stamps.argtypes = [vp, i, vp]
+    lib.fa_clock_stamps.restype = i
     _lib = lib
     return lib
 
@@ -108,6 +117,53 @@ def fa_fwd(q, k, v, o, lse, B, H, S, D, scale, causal, dtype, stream):
     return _load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(S),
                           int(D), ctypes.c_float(scale), int(bool(causal)), int(dtype),
                           _stream(stream))
+
+
+def fa_fwd_diag(q, k, v, o, lse, o32, tile_counts, B, H, Sq, Sk, D, scale, causal, dtype, flags, stream):
+    """The ABI call fa_fwd_diag (test-only diagnostic launch).  Returns the status."""
+    return _load().fa_fwd_diag(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(o32), _ptr(tile_counts),
+                               int(B), int(H), int(Sq), int(Sk), int(D), ctypes.c_float(scale),
+                               int(bool(causal)), int(dtype), int(flags), _stream(stream))
+
+
+def fa_fwd_diag_tile_slots(B, H, Sq, D, causal):
+    return _load().fa_fwd_diag_tile_slots(int(B), int(H), int(Sq), int(D), int(bool(causal)))
+
+
+def fa_clock_stamps(out, groups, stream):
+    """The ABI call fa_clock_stamps.  Returns the status."""
+    return _load().fa_clock_stamps(_ptr(out), int(groups), _stream(stream))
+
+
+def clock_stamps(device=None, stream=None, groups=512):
+    """Enqueue fa_clock_stamps on `stream` (default: torch's current stream)
+    into a new int64 tensor [groups, 4]; read it after synchronising."""
+    import torch
+    dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    out = torch.empty((groups, 4), dtype=torch.int64, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    st = fa_clock_stamps(out, groups, stream)
+    if st != 0:
+        raise FaError(st, "fa_clock_stamps")
+    return out
+
+
+def clock_mhz(before, after):
+    """Average shader clock per XCD between two clock_stamps() results (CPU
+    or device tensors, read after the work between them has finished):
+    {xcd: MHz}.  Uses, per XCD, the mean counters of its workgroups."""
+    import numpy as np
+    a = before.cpu().numpy().astype(np.float64)
+    b = after.cpu().numpy().astype(np.float64)
+    out = {}
+    for x in sorted(set(a[:, 0].astype(int)) & set(b[:, 0].astype(int))):
+        ra, rb = a[a[:, 0] == x], b[b[:, 0] == x]
+        dt = rb[:, 1].mean() - ra[:, 1].mean()
+        dr = rb[:, 2].mean() - ra[:, 2].mean()
+        if dr > 0:
+            out[int(x)] = dt / dr * 100.0
+    return out
 
 
 def _strides3(st):
@@ -376,8 +432,9 @@ def backward(q, k, v, o, lse, dout, causal=False, scale=None, deterministic=True
 def _mask_arg(mask, q, B, H, Sq, Sk):
     """(mask view, byte strides) for the C ABI from a uint8/bool GPU tensor
     broadcastable to [B, H, Sq, Sk]: batch and head strides may be 0
-    (broadcast); when the rows do not start on 4-byte boundaries the mask is
-    copied once into a [.., Sq, Sk rounded up to 4] buffer."""
+    (broadcast); when the rows do not start on 4-byte boundaries, or the mask
+    is broadcast over the query rows, it is copied once into a
+    [.., Sq, Sk rounded up to 4] buffer."""
     import torch
     if mask is None:
         return None, None
@@ -388,7 +445,11 @@ def _mask_arg(mask, q, B, H, Sq, Sk):
     while mask.dim() < 4:
         mask = mask.unsqueeze(0)
     m = mask.expand(B, H, Sq, Sk)
-    aligned = m.stride(3) == 1 and m.data_ptr() % 4 == 0 and all(st % 4 == 0 for st in m.stride()[:3])
+    # the ABI takes rows that start on 4-byte boundaries, one row per query
+    # (row stride >= Sk): a mask broadcast over the queries (a key-padding
+    # mask [B, 1, 1, Sk], row stride 0) is copied too
+    aligned = m.stride(3) == 1 and m.data_ptr() % 4 == 0 and all(st % 4 == 0 for st in m.stride()[:3]) and \
+        m.stride(2) >= Sk
     if not aligned:
         lead = [B if mask.shape[0] != 1 else 1, H if mask.shape[1] != 1 else 1]
         ld = (Sk + 3) // 4 * 4

@@ -6,6 +6,7 @@ instructions are disabled for all device code.
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -13,7 +14,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa_hip.so")
 SOURCES = [os.path.join(CSRC, "fa_api.cpp"), os.path.join(CSRC, "fa_fwd_kernel.hip"),
            os.path.join(CSRC, "fa_naive.hip"), os.path.join(CSRC, "fa_bwd.hip"),
-           os.path.join(CSRC, "fa_fwd_ext.hip"), os.path.join(CSRC, "fa_bwd256.hip")]
+           os.path.join(CSRC, "fa_fwd_ext.hip"), os.path.join(CSRC, "fa_bwd256.hip"),
+           os.path.join(CSRC, "fa_fwd_diag.hip"), os.path.join(CSRC, "fa_clock.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Kernels whose MFMA accumulators are also worked on by vector instructions:
 # the VGPR form of the MFMA instructions keeps those accumulators in VGPRs
@@ -33,22 +35,32 @@ def hipcc_flags(extra=()):
             "-Wall", *extra]
 
 
-def build(out=LIB, extra=(), verbose=False):
-    """Build the shared library (always recompiles) and return its path."""
-    objs = []
+def build(out=LIB, extra=(), verbose=False, jobs=None):
+    """Build the shared library (always recompiles) and return its path.
+    The sources compile in parallel (one hipcc process each)."""
     tmpdir = os.path.join(PKG, "_build")
     os.makedirs(tmpdir, exist_ok=True)
+    cmds = []
+    objs = []
     for src in SOURCES:
         obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
         per = PER_SOURCE_FLAGS.get(os.path.basename(src), [])
-        cmd = [HIPCC, *hipcc_flags(extra), *per, *lang, "-c", src, "-o", obj]
-        if verbose:
-            print(" ".join(cmd))
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            raise RuntimeError("hipcc failed for %s:\n%s" % (src, r.stderr))
+        cmds.append((src, [HIPCC, *hipcc_flags(extra), *per, *lang, "-c", src, "-o", obj]))
         objs.append(obj)
+
+    def compile_one(item):
+        src, cmd = item
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        return src, subprocess.run(cmd, capture_output=True, text=True)
+
+    if jobs is None:
+        jobs = min(len(cmds), max(1, min(8, len(os.sched_getaffinity(0)))))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        for src, r in ex.map(compile_one, cmds):
+            if r.returncode != 0:
+                raise RuntimeError("hipcc failed for %s:\n%s" % (src, r.stderr))
     tmp = out + ".tmp%d" % os.getpid()
     # --no-undefined: a kernel whose host stub failed to instantiate must fail the build
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Wl,--no-undefined", *objs, "-o", tmp]

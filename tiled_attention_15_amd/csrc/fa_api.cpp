@@ -6,6 +6,7 @@
 // call enqueues nothing.  The launch is asynchronous on the caller's stream;
 // the library never allocates, frees or synchronises.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -15,17 +16,49 @@
 #include "fa_ext.h"
 #include "fa_naive.h"
 
+namespace fa {
+
+// Compute units per device, read from the device the first time a call runs
+// on it (0 = not read yet).  Queried, not assumed: a partitioned part or
+// another SKU has a different count, and the key-split choice depends on it.
+constexpr int kMaxDevices = 64;
+constexpr int kDefaultComputeUnits = 256;   // MI355X, when no device answers
+static std::atomic<int> g_compute_units[kMaxDevices];
+
+int compute_units() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();   // clear our own failure only
+        return kDefaultComputeUnits;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return kDefaultComputeUnits;
+    int n = g_compute_units[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        n = kDefaultComputeUnits;
+    }
+    g_compute_units[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+}  // namespace fa
+
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 3 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 4 * 100 + 0;
 
 int validate_shape(int B, int H, int Sq, int Sk, int D, int dtype) {
     if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return FA_ERR_SHAPE;
+    // sequence lengths up to 2^30, so that every ceiling division by a block
+    // size below stays inside int
+    if (Sq > (1 << 30) || Sk > (1 << 30)) return FA_ERR_SHAPE;
     if (D != 64 && D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
     if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
     const int S = Sq > Sk ? Sq : Sk;
-    const int64_t elems = (int64_t)B * H * S * D;
-    if (elems >= (int64_t(1) << 40)) return FA_ERR_SHAPE;
+    // in double: the product of four ints can exceed 2^63 (exact below 2^53)
+    const double elems = (double)B * (double)H * (double)S * (double)D;
+    if (elems >= 1099511627776.0) return FA_ERR_SHAPE;    // 2^40
     const int64_t grid = (int64_t)B * H * ((Sq + fa::kBlockQ - 1) / fa::kBlockQ);
     if (grid >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
     return FA_OK;
@@ -39,10 +72,10 @@ int validate_shape(int B, int H, int Sq, int Sk, int D, int dtype) {
 // blocks as compute units), or, under the causal rule, whenever the 256-row
 // blocks leave compute units idle (their chains differ in length, so the
 // longest one sets the time).
-bool use_split(int B, int H, int Sq, int D, bool causal) {
+bool use_split(int B, int H, int Sq, int D, bool causal, int cus) {
     const int64_t blocks = (int64_t)B * H * ((Sq + fa::kBlockQ - 1) / fa::kBlockQ);
     if (D == 256) return false;
-    return 2 * blocks <= fa::kComputeUnits || (causal && blocks < fa::kComputeUnits);
+    return 2 * blocks <= cus || (causal && blocks < cus);
 }
 
 // Byte offsets inside one head are 32-bit (buffer descriptors): every row a
@@ -96,13 +129,21 @@ bool no_self_overlap(const int64_t* st, int B, int H, int S, int D) {
 
 }  // namespace
 
+// Diagnostic outputs of fa_fwd_diag (null for the product entry points).
+struct DiagArgs {
+    int flags;
+    float* o32;
+    uint32_t* tiles;
+};
+
 // The tuned kernel (D = 64 or 128) on validated arguments; mask (with its
-// byte strides) may be null.
+// byte strides) may be null; diag selects the diagnostic instance.
 static int launch_tuned(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Sq,
                         int Sk, int D, const int64_t* q_strides, const int64_t* k_strides,
                         const int64_t* v_strides, const int64_t* o_strides, const uint8_t* mask,
-                        const int64_t* mask_strides, float scale, int causal, int dtype, void* stream) {
-    fa::FwdParams p;
+                        const int64_t* mask_strides, float scale, int causal, int dtype, void* stream,
+                        const DiagArgs* diag = nullptr) {
+    fa::FwdParams p = {};
     p.q = q;
     p.k = k;
     p.v = v;
@@ -112,7 +153,7 @@ static int launch_tuned(const void* q, const void* k, const void* v, void* o, fl
     p.Sk = Sk;
     p.H = H;
     p.BH = B * H;
-    const bool split = use_split(B, H, Sq, D, causal != 0);
+    const bool split = use_split(B, H, Sq, D, causal != 0, fa::compute_units());
     // 128-row blocks for the key-split instances and at D = 256 (the
     // head-dimension split: both wave groups on the same rows)
     const int br = (split || D == 256) ? fa::kBlockQSplit : fa::kBlockQ;
@@ -127,6 +168,13 @@ static int launch_tuned(const void* q, const void* k, const void* v, void* o, fl
     p.m_sh = mask ? mask_strides[1] : 0;
     p.m_ss = mask ? (int)mask_strides[2] : 0;
     const int64_t grid = (int64_t)p.BH * p.nqb;
+    if (diag != nullptr) {
+        p.diag_flags = diag->flags;
+        p.o32 = diag->o32;
+        p.tiles = diag->tiles;
+        const hipError_t err = fa::launch_fwd_diag(p, D, dtype, causal != 0, grid, split, (hipStream_t)stream);
+        return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+    }
     const hipError_t err = fa::launch_fwd(p, D, dtype, causal != 0, grid, split, (hipStream_t)stream);
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -158,7 +206,8 @@ int fa_fwd_plan(int B, int H, int S, int D, int causal, int dtype, int* block_q,
     if (st != FA_OK) return st;
     // 128-row blocks at D = 256 (head-dimension split) and on small grids
     // (key split)
-    const int br = (D == 256 || use_split(B, H, S, D, causal != 0)) ? fa::kBlockQSplit : fa::kBlockQ;
+    const int br = (D == 256 || use_split(B, H, S, D, causal != 0, fa::compute_units())) ? fa::kBlockQSplit
+                                                                                         : fa::kBlockQ;
     const int bc = fa::kBlockKV;
     const int64_t nqb = (S + br - 1) / br;
     const int64_t nkv = (S + bc - 1) / bc;
@@ -218,10 +267,54 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int S,
            int D, float scale, int causal, int dtype, void* stream) {
+    // the shape first: the contiguous strides below overflow for absurd shapes
+    const int vs = validate_shape(B, H, S, S, D, dtype);
+    if (vs != FA_OK) return (!q || !k || !v || !o) ? FA_ERR_NULL : vs;
     // contiguous [B, H, S, D]
     const int64_t st[3] = {(int64_t)H * S * D, (int64_t)S * D, D};
     return fa_fwd_strided(q, k, v, o, lse, B, H, S, S, D, st, st, st, st, scale, causal, dtype,
                           stream);
+}
+
+int64_t fa_fwd_diag_tile_slots(int B, int H, int Sq, int D, int causal) {
+    if (validate_shape(B, H, Sq, Sq, D, FA_F16) != FA_OK || D == 256) return 0;
+    const int br = use_split(B, H, Sq, D, causal != 0, fa::compute_units()) ? fa::kBlockQSplit : fa::kBlockQ;
+    return (int64_t)B * H * ((Sq + br - 1) / br) * 8;
+}
+
+int fa_fwd_diag(const void* q, const void* k, const void* v, void* o, float* lse, float* o32,
+                uint32_t* tile_counts, int B, int H, int Sq, int Sk, int D, float scale, int causal,
+                int dtype, int flags, void* stream) {
+    if (!q || !k || !v || !o) return FA_ERR_NULL;
+    int st = validate_shape(B, H, Sq, Sk, D, dtype);
+    if (st != FA_OK) return st;
+    if (D == 256 || (flags & ~fa::kDiagReverseOrder) != 0) return FA_ERR_UNSUPPORTED;
+    const int64_t sq[3] = {(int64_t)H * Sq * D, (int64_t)Sq * D, D};
+    const int64_t sk[3] = {(int64_t)H * Sk * D, (int64_t)Sk * D, D};
+    if (!head_span_ok(Sq, D, D) || !head_span_ok(Sk, D, D)) return FA_ERR_SHAPE;
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse | (uintptr_t)o32 |
+         (uintptr_t)tile_counts) & 15)
+        return FA_ERR_ALIGN;
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_SCALE;
+    const uintptr_t qb = (uintptr_t)((int64_t)B * H * Sq * D * 2), kb = (uintptr_t)((int64_t)B * H * Sk * D * 2);
+    const uintptr_t in[3][2] = {{(uintptr_t)q, (uintptr_t)q + qb}, {(uintptr_t)k, (uintptr_t)k + kb},
+                                {(uintptr_t)v, (uintptr_t)v + kb}};
+    const int64_t nslots = fa_fwd_diag_tile_slots(B, H, Sq, D, causal);
+    const uintptr_t out[4][2] = {
+        {(uintptr_t)o, (uintptr_t)o + qb},
+        {(uintptr_t)lse, (uintptr_t)lse + (lse ? (uintptr_t)((int64_t)B * H * Sq * 4) : 0)},
+        {(uintptr_t)o32, (uintptr_t)o32 + (o32 ? (uintptr_t)((int64_t)B * H * Sq * D * 4) : 0)},
+        {(uintptr_t)tile_counts, (uintptr_t)tile_counts + (tile_counts ? (uintptr_t)(nslots * 4) : 0)}};
+    for (int i = 0; i < 4; ++i) {
+        if (out[i][1] == out[i][0]) continue;
+        for (int j = 0; j < 3; ++j)
+            if (overlap(out[i][0], out[i][1], in[j][0], in[j][1])) return FA_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (out[j][1] > out[j][0] && overlap(out[i][0], out[i][1], out[j][0], out[j][1])) return FA_ERR_ALIAS;
+    }
+    const DiagArgs diag = {flags, o32, tile_counts};
+    return launch_tuned(q, k, v, o, lse, B, H, Sq, Sk, D, sq, sk, sk, sq, nullptr, nullptr, scale, causal, dtype,
+                        stream, &diag);
 }
 
 namespace {
@@ -305,7 +398,7 @@ struct BwdLayout {
 int64_t r256b(int64_t x) { return (x + 255) / 256 * 256; }
 
 bool bwd_layout(int B, int H, int Sq, int D, int deterministic, BwdLayout& L) {
-    if (B < 1 || H < 1 || Sq < 1 || (D != 64 && D != 128 && D != 256)) return false;
+    if (validate_shape(B, H, Sq, Sq, D, FA_F16) != FA_OK) return false;
     const int64_t rows = (int64_t)B * H * Sq;
     L.dvec_bytes = r256b(rows * 4);
     L.acc_bytes = deterministic ? 0 : r256b(rows * D * 4);
@@ -407,6 +500,8 @@ static int ext_common(const void* q, const void* k, const void* v, void* o, floa
 int fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Sq,
                int Sk, int D, const uint8_t* mask, const int64_t* mask_strides, float dropout_p,
                uint64_t seed, uint32_t offset, float scale, int causal, int dtype, void* stream) {
+    const int vs = validate_shape(B, H, Sq, Sk, D, dtype);
+    if (vs != FA_OK) return (!q || !k || !v || !o) ? FA_ERR_NULL : vs;
     // contiguous [B, H, S, D]
     const int64_t st[12] = {(int64_t)H * Sq * D, (int64_t)Sq * D, D, (int64_t)H * Sk * D, (int64_t)Sk * D, D,
                             (int64_t)H * Sk * D, (int64_t)Sk * D, D, (int64_t)H * Sq * D, (int64_t)Sq * D, D};
@@ -533,6 +628,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            const float* lse, void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk, int D,
            float scale, int causal, int dtype, int deterministic, void* workspace,
            int64_t workspace_bytes, void* stream) {
+    const int vs = validate_shape(B, H, Sq, Sk, D, dtype);
+    if (vs != FA_OK) return (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) ? FA_ERR_NULL : vs;
     int64_t st[24];
     contiguous_bwd_strides(H, Sq, Sk, D, st);
     return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, st, nullptr, nullptr, 0.0f, 0, 0,
@@ -544,6 +641,8 @@ int fa_bwd_ext(const void* q, const void* k, const void* v, const void* o, const
                const uint8_t* mask, const int64_t* mask_strides, float dropout_p, uint64_t seed,
                uint32_t offset, float scale, int causal, int dtype, void* workspace,
                int64_t workspace_bytes, void* stream) {
+    const int vs = validate_shape(B, H, Sq, Sk, D, dtype);
+    if (vs != FA_OK) return (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) ? FA_ERR_NULL : vs;
     int64_t st[24];
     contiguous_bwd_strides(H, Sq, Sk, D, st);
     return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, st, mask, mask_strides, dropout_p,

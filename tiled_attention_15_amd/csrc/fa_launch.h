@@ -7,7 +7,6 @@ namespace fa {
 
 constexpr int kBlockQ = 256;           // query rows per workgroup (B_r): 8 waves x 32
 constexpr int kBlockQSplit = 128;      // B_r of the key-split instance (both wave groups on 128 rows)
-constexpr int kComputeUnits = 256;     // MI355X
 constexpr int kBlockKV = 64;            // keys per K/V tile (B_c)
 
 struct FwdParams {
@@ -31,12 +30,25 @@ struct FwdParams {
     const uint8_t* mask;   // null = no mask
     int64_t m_sb, m_sh;
     int m_ss;
+    // Diagnostic instances only (ignored by the others).
+    int diag_flags;        // kDiagReverseOrder: workgroups take their blocks in reverse order
+    float* o32;            // null, or fp32 O [B*H, Sq, D] contiguous
+    uint32_t* tiles;       // null, or [grid][8]: tiles each wave ran its softmax on
 };
+
+constexpr int kDiagReverseOrder = 1;
 
 // Enqueue the forward kernel (the masked instance when p.mask is set; the
 // key-split instance when split, p.nqb counted in
 // kBlockQSplit-row blocks); returns hipGetLastError() after the launch.
 hipError_t launch_fwd(const FwdParams& p, int D, int dtype, bool causal, int64_t grid, bool split,
                       hipStream_t stream);
+// The diagnostic instance (D = 64 or 128, no mask) of the same kernel.
+hipError_t launch_fwd_diag(const FwdParams& p, int D, int dtype, bool causal, int64_t grid, bool split,
+                           hipStream_t stream);
+
+// Compute units of the current device, read once per device and cached
+// (falls back to 256, MI355X's count, when no device can be queried).
+int compute_units();
 
 }  // namespace fa
