@@ -108,6 +108,19 @@ __device__ __forceinline__ int pack2(float x, float y) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// acc + x.lo + x.hi for a dword of two 16-bit values (a dot product with
+// (1, 1): the products are exact, the sum accumulates in fp32).
+template <int DT>
+__device__ __forceinline__ float dot2_ones(int x, float acc) {
+    if constexpr (DT == 0) {
+        const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), one, acc, false);
+    } else {
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), one, acc, false);
+    }
+}
+
 // Value of the partner lane (l ^ 32) combined with our own: returns both halves.
 __device__ __forceinline__ float xmax32(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -356,7 +369,8 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
     f32x16 s[2];
     i32x4 pf[4];
     float m_run = -INFINITY;
-    float l_run = 0.0f;
+    float l_run = 0.0f;     // running sum of the probabilities (fp32): the lse
+    float r_run = 0.0f;     // running sum of the probabilities as rounded for P V: O's divisor
     const float c2 = p.scale_log2e;
     const int krow = 16 * ((lq >> 2) & 1) + 4 * (lq >> 3) + (lq & 3);
     const int vkey = 16 * g + ((lane & 15) >> 2);
@@ -461,6 +475,7 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
             const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
             m_run = m_new;
             l_run *= alpha;
+            r_run *= alpha;
 #pragma unroll
             for (int b = 0; b < DO; ++b)
 #pragma unroll
@@ -487,6 +502,19 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
                     w[e] = pack2<DT>(s[kb2][8 * c + 2 * e], s[kb2][8 * c + 2 * e + 1]);
                 pf[2 * kb2 + c] = w;
             }
+        // The same probabilities as the second product sees them (rounded
+        // to 16 bits), summed exactly by dot products with (1, 1).  O is
+        // divided by this sum, so the weights it applies to V are the
+        // rounded probabilities normalised by their own total: a row
+        // dominated by one key returns that key's V row up to fp32 rounding,
+        // where dividing by the unrounded sum would leave the probability's
+        // 16-bit rounding (up to 2^-9 relative in bf16) on the output.
+        float rsum = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rsum = dot2_ones<DT>(pf[c][e], rsum);
+        r_run += rsum;
     };
 
     // Instruction order of a matrix phase (P V then K Q^T: 32 MFMAs, 2*16
@@ -692,7 +720,7 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
     // wave of group 0 that owns the same rows (same lane layout), which
     // rescales both to the larger max and adds them.
     float* const xbuf = (float*)smem;
-    const int xb = (wid & 3) * (DB * 16 + 2) * 64 + lane;
+    const int xb = (wid & 3) * (DB * 16 + 3) * 64 + lane;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -703,6 +731,7 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
             for (int i = 0; i < 16; ++i) xbuf[xb + (16 * b + i) * 64] = oacc[b][i];
         xbuf[xb + 16 * DB * 64] = m_run;
         xbuf[xb + (16 * DB + 1) * 64] = l_run;
+        xbuf[xb + (16 * DB + 2) * 64] = r_run;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
@@ -718,6 +747,7 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
             a1 = fast_exp2(m1 - m);
         }
         l_run = a0 * l_run + a1 * l1;
+        r_run = a0 * r_run + a1 * xbuf[xb + (16 * DB + 2) * 64];
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -841,7 +871,8 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
 
     if constexpr (!SPLIT) store_tiles();
     const float l_tot = xsum32(l_run);
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const float r_tot = xsum32(r_run);
+    const float inv = r_tot > 0.0f ? 1.0f / r_tot : 0.0f;
     const int qrow = qw0 + lq;
     if constexpr (DIAG) {
         if (p.o32 != nullptr) {

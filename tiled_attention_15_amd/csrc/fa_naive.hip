@@ -5,11 +5,13 @@
 // device memory, then O = P V -- built from this library's own kernels:
 //   naive_scores   S (fp32) = scale * Q K^T with the causal mask applied
 //                  (-inf), an MFMA GEMM over the head dimension;
-//   naive_softmax  P (input dtype) = softmax of each row of S, and the row's
-//                  natural-log log-sum-exp;
+//   naive_softmax  P (input dtype) = exp(S - row max) of each row, the
+//                  reciprocal of the sum of those rounded values, and the
+//                  row's natural-log log-sum-exp;
 //   naive_vt       V^T per head, so that the second product reads both
 //                  operands along the key dimension;
-//   naive_pv       O = P V, an MFMA GEMM over the keys.
+//   naive_pv       O = P V, an MFMA GEMM over the keys, times that
+//                  reciprocal.
 // "FlashAttention-2 on Ascend NPU: how ops-transformer reaches 3x"
 // (2048ai.net), section 1 (the N x N matrices S and P materialised), and
 // "ops-transformer FlashAttention operator in practice" (ai6s.net),
@@ -47,6 +49,12 @@ __device__ __forceinline__ f32x16 mma(i32x4 a, i32x4 b, f32x16 c) {
     else
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+template <int DT>
+__device__ __forceinline__ float from16(uint16_t h) {
+    if constexpr (DT == 0) return (float)__builtin_bit_cast(_Float16, h);
+    else return __uint_as_float((uint32_t)h << 16);
 }
 
 template <int DT>
@@ -154,12 +162,22 @@ __global__ __launch_bounds__(256) void naive_softmax(NaiveParams p) {
         l += x[e];
     }
     l = block_reduce(l, false);
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    // P is stored unnormalised (the largest entry exactly 1) and O is divided
+    // by the sum of the stored, rounded values: the weights applied to V are
+    // then the rounded probabilities normalised by their own total, so the
+    // rounding of a dominant probability does not reach the output.
+    float r = 0.0f;
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
         const int j = tid + 256 * e;
-        if (j < p.Skp) P[j] = to16<DT>(j < p.Sk ? x[e] * inv : 0.0f);
+        const uint16_t h = to16<DT>(j < p.Sk ? x[e] : 0.0f);
+        if (j < p.Skp) P[j] = h;
+        r += from16<DT>(h);
     }
+    r = block_reduce(r, false);
+    // the divisor's reciprocal replaces the row's first score (every thread
+    // has read its scores before the reductions' barriers)
+    if (tid == 0) p.s[row * p.Skp] = r > 0.0f ? 1.0f / r : 0.0f;
     if (tid == 0 && p.lse) p.lse[row] = l > 0.0f ? m + __logf(l) : -INFINITY;
 }
 
@@ -217,13 +235,21 @@ __global__ __launch_bounds__(256) void naive_pv(NaiveParams p) {
             for (int b = 0; b < D / 32; ++b) acc[b] = mma<DT>(af[u], bf[u][b], acc[b]);
     }
     uint16_t* O = (uint16_t*)p.o + (int64_t)bh * p.Sq * D;
+    // 1 / (sum of the row's rounded probabilities), left by the softmax in
+    // the row's first score slot
+    float rinv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int row = r0 + acc_row(i, lane);
+        rinv[i] = row < p.Sq ? p.s[((int64_t)bh * p.Sq + row) * p.Skp] : 0.0f;
+    }
 #pragma unroll
     for (int b = 0; b < D / 32; ++b) {
         const int col = 32 * b + (lane & 31);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int row = r0 + acc_row(i, lane);
-            if (row < p.Sq) O[(int64_t)row * D + col] = to16<DT>(acc[b][i]);
+            if (row < p.Sq) O[(int64_t)row * D + col] = to16<DT>(acc[b][i] * rinv[i]);
         }
     }
 }
