@@ -63,8 +63,10 @@ typedef enum {
     FA_ERR_ALIAS = 7,        /* o or lse overlaps q, k or v, or o overlaps lse */
     FA_ERR_STRIDE = 8,       /* a stride is negative, not a multiple of 8
                                 elements, or makes o overlap itself */
-    FA_ERR_MASK_DROPOUT = 9  /* fa_fwd_ext: bad mask layout or dropout
+    FA_ERR_MASK_DROPOUT = 9, /* fa_fwd_ext: bad mask layout or dropout
                                 probability outside [0, 1) */
+    FA_ERR_SCRATCH = 10      /* fa_bwd_noalloc: the call needs more than the
+                                fixed scratch array holds */
 } fa_status;
 
 /*
@@ -367,6 +369,31 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            const float* lse, void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk, int D,
            float scale, int causal, int dtype, int deterministic, void* workspace,
            int64_t workspace_bytes, void* stream);
+
+/*
+ * fa_bwd_noalloc -- fa_bwd in its deterministic mode without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ * The workspace is a fixed device array inside the library, 16 MiB
+ * (fa_bwd_noalloc_scratch_bytes()), held by each GPU the library runs on
+ * until the process ends; its device address is looked up once per device
+ * on the first call there.  The call itself allocates nothing and does not
+ * synchronise.
+ *
+ * Arguments, layouts, numerics and errors as for fa_bwd with
+ * deterministic = 1 (results bitwise equal to that call), plus
+ * FA_ERR_SCRATCH when fa_bwd_workspace_bytes(B, H, Sq, D, 1) exceeds the
+ * array (B * H * Sq above 4,194,304 rows) and FA_ERR_HIP when the array's
+ * address cannot be obtained.  Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (two streams, two threads)
+ * race and must be ordered by the caller.
+ */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk,
+                   int D, float scale, int causal, int dtype, void* stream);
+
+/* Size in bytes of fa_bwd_noalloc's fixed scratch array. */
+int64_t fa_bwd_noalloc_scratch_bytes(void);
 
 /*
  * fa_bwd_ext -- gradients of fa_fwd_ext: the backward with the same explicit

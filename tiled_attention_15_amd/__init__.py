@@ -18,7 +18,7 @@ __all__ = ["FaError", "fa_fwd", "fa_fwd_strided", "fa_fwd_plan", "fa_naive_fwd",
            "fa_bwd_workspace_bytes", "backward", "fa_fwd_ext", "forward_ext", "fa_bwd_ext",
            "backward_ext", "fa_bwd_strided", "fa_fwd_ext_strided", "fa_fwd_diag",
            "fa_fwd_diag_tile_slots", "DIAG_REVERSE_ORDER", "fa_clock_stamps", "clock_stamps",
-           "clock_mhz"]
+           "clock_mhz", "fa_bwd_noalloc", "fa_bwd_noalloc_scratch_bytes"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libfa_hip.so")
@@ -27,7 +27,7 @@ F16, BF16 = 0, 1
 DIAG_REVERSE_ORDER = 1
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED",
           4: "FA_ERR_ALIGN", 5: "FA_ERR_SCALE", 6: "FA_ERR_HIP", 7: "FA_ERR_ALIAS",
-          8: "FA_ERR_STRIDE", 9: "FA_ERR_MASK_DROPOUT"}
+          8: "FA_ERR_STRIDE", 9: "FA_ERR_MASK_DROPOUT", 10: "FA_ERR_SCRATCH"}
 
 _lib = None
 
@@ -92,6 +92,10 @@ def _load():
     lib.fa_fwd_diag_tile_slots.restype = ctypes.c_int64
     lib.fa_clock_stamps.argtypes = [vp, i, vp]
     lib.fa_clock_stamps.restype = i
+    lib.fa_bwd_noalloc.argtypes = [vp] * 9 + [i] * 5 + [f, i, i, vp]
+    lib.fa_bwd_noalloc.restype = i
+    lib.fa_bwd_noalloc_scratch_bytes.argtypes = []
+    lib.fa_bwd_noalloc_scratch_bytes.restype = ctypes.c_int64
     _lib = lib
     return lib
 
@@ -258,6 +262,18 @@ def fa_bwd_strided(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, strides, 
                                   ctypes.c_uint32(int(offset) & 0xFFFFFFFF), ctypes.c_float(scale),
                                   int(bool(causal)), int(dtype), int(bool(deterministic)), _ptr(workspace),
                                   int(workspace_bytes), _stream(stream))
+
+
+def fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, scale, causal, dtype, stream):
+    """C ABI fa_bwd_noalloc: the deterministic backward with the library's fixed
+    scratch array as its workspace (no allocation)."""
+    return _load().fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                                  _ptr(dk), _ptr(dv), int(B), int(H), int(Sq), int(Sk), int(D),
+                                  ctypes.c_float(scale), int(bool(causal)), int(dtype), _stream(stream))
+
+
+def fa_bwd_noalloc_scratch_bytes():
+    return _load().fa_bwd_noalloc_scratch_bytes()
 
 
 def fa_bwd_workspace_bytes(B, H, Sq, D, deterministic):

@@ -195,6 +195,7 @@ const char* fa_status_string(int status) {
         case FA_ERR_ALIAS: return "output buffer overlaps an input or the other output";
         case FA_ERR_STRIDE: return "invalid strides (negative, not a multiple of 8, row stride < D, or overlapping output)";
         case FA_ERR_MASK_DROPOUT: return "invalid mask layout or dropout probability";
+        case FA_ERR_SCRATCH: return "the call needs more scratch than the allocation-free entry point holds";
         default: return "unknown status";
     }
 }
