@@ -134,8 +134,11 @@ __device__ __forceinline__ float xsum32(float x) {
 // LDS swizzles.  K rows are read 16 bytes per lane by 32 rows at once (the
 // rows pi(0..31)); XOR-ing the 16-byte chunk index with kswz(row) spreads a
 // 16-lane (or 8-lane) group over distinct banks.  V rows are read 8 bytes per
-// lane, 64 contiguous bytes per row; XOR-ing the 64-byte segment with the
-// row's low bits spreads four consecutive rows over distinct segments.
+// lane, 64 contiguous bytes from each of four consecutive rows per 32 lanes
+// (256 bytes: all 64 banks once); XOR-ing the 64-byte segment with row bits
+// puts the four rows on four distinct quarters of the banks: the row's two
+// low bits at D >= 128 (rows of 256 bytes or more), bit 1 at D = 64 (rows of
+// 128 bytes, whose bit 0 already selects the upper half of the banks).
 template <int D>
 __device__ __forceinline__ int kswz(int row) {
     row &= 31;
@@ -147,7 +150,7 @@ __device__ __forceinline__ int kswz(int row) {
 }
 template <int D>
 __device__ __forceinline__ int vseg_swz(int row) {
-    return (D >= 128) ? (row & 3) : (row & 1);
+    return (D >= 128) ? (row & 3) : ((row >> 1) & 1);
 }
 // byte offset inside a K tile of 16-byte chunk `ch` of row `row`
 template <int D>
@@ -482,15 +485,23 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
                 for (int i = 0; i < 16; ++i) oacc[b][i] *= alpha;
         }
         const float mb = (m_run == -INFINITY) ? 0.0f : m_run;
+        // all exponent arguments first, in place, then all exponentials:
+        // independent instructions back to back instead of 32 dependent
+        // (argument, exponential) pairs through one temporary register
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[kb2][i] = __builtin_fmaf(s[kb2][i], c2, -mb);
+        asm volatile("" : "+v"(s[0]), "+v"(s[1]));
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[kb2][i] = fast_exp2(s[kb2][i]);
         float lsum = 0.0f;
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float e = fast_exp2(__builtin_fmaf(s[kb2][i], c2, -mb));
-                s[kb2][i] = e;
-                lsum += e;
-            }
+            for (int i = 0; i < 16; ++i) lsum += s[kb2][i];
         l_run += lsum;
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
