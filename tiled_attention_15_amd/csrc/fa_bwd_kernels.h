@@ -454,16 +454,16 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_dq(BwdParams p) {
         }
         // dS^T = P (Z c dP - D_i): keys kt0 + 32rb + 8a + 0..7 share one
         // Philox block; this lane uses words 2g and 2g+1 (keys 8a + 4g + 0..3)
+        uint32_t kw[2][4][2];
+        if constexpr (DROP) keep_words<2>(kw, kt0, qi, bh, p.offset, p.seed_lo, p.seed_hi, g);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 float z[4] = {1.0f, 1.0f, 1.0f, 1.0f};
                 if constexpr (DROP) {
-                    uint32_t c[4] = {(uint32_t)((kt0 + 32 * rb + 8 * a) >> 3), (uint32_t)qi, (uint32_t)bh, p.offset};
-                    philox4x32_10(c, p.seed_lo, p.seed_hi);
-                    const uint32_t w0 = g ? c[2] : c[0];
-                    const uint32_t w1 = g ? c[3] : c[1];
+                    const uint32_t w0 = kw[rb][a][0];
+                    const uint32_t w1 = kw[rb][a][1];
                     const uint32_t r16[4] = {w0 & 0xffffu, w0 >> 16, w1 & 0xffffu, w1 >> 16};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) z[e] = r16[e] >= p.drop_t ? p.keep_scale : 0.0f;

@@ -194,17 +194,15 @@ __global__ __launch_bounds__(256) void fwd_ext(ExtParams p) {
         }
 
         if constexpr (DROP) {
-            // keys kt0 + 32rb + 8a + 0..7 share one Philox call; this lane
+            // keys kt0 + 32rb + 8a + 0..7 share one Philox block; this lane
             // uses words 2g and 2g+1 (keys 8a + 4g + 0..3)
+            uint32_t kw[RB][4][2];
+            keep_words<RB>(kw, kt0, qi, bh, p.offset, p.seed_lo, p.seed_hi, g);
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
-                    uint32_t c[4] = {(uint32_t)((kt0 + 32 * rb + 8 * a) >> 3), (uint32_t)qi, (uint32_t)bh,
-                                     p.offset};
-                    philox4x32_10(c, p.seed_lo, p.seed_hi);
-                    const uint32_t w0 = g ? c[2] : c[0];
-                    const uint32_t w1 = g ? c[3] : c[1];
+                    const uint32_t w0 = kw[rb][a][0], w1 = kw[rb][a][1];
                     const uint32_t r16[4] = {w0 & 0xffffu, w0 >> 16, w1 & 0xffffu, w1 >> 16};
 #pragma unroll
                     for (int e = 0; e < 4; ++e)

@@ -196,6 +196,40 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32
     }
 }
 
+// The dropout words a lane needs for the S^T accumulator layout of a tile of
+// RB 32-key blocks (lane l holds query lq = l % 32 and, in register 4a + e of
+// block rb, key kt0 + 32 rb + 8a + 4g + e, g = l / 32): for each (rb, a) the
+// two words 2g, 2g + 1 of the Philox4x32-10 block at counter
+// ((kt0 + 32 rb + 8a) / 8, qi, bh, offset) -- the block covers the 8 keys
+// 8a .. 8a + 7, a lane uses the four of them it holds.  Lanes l and l ^ 32
+// (the same query) need the two halves of the same blocks, so each computes
+// the blocks of two of the four 8-key groups (lane half g: a = 2g, 2g + 1)
+// and hands the partner the two words it needs (v_permlane32_swap): four
+// Philox blocks per lane and tile instead of eight.
+template <int RB>
+__device__ __forceinline__ void keep_words(uint32_t kw[RB][4][2], int kt0, int qi, int bh, uint32_t offset,
+                                           uint32_t seed_lo, uint32_t seed_hi, int g) {
+    auto partner = [&](uint32_t x) {
+        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return g ? (uint32_t)r[0] : (uint32_t)r[1];
+    };
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            uint32_t c[4] = {(uint32_t)((kt0 + 32 * rb + 8 * (2 * g + u)) >> 3), (uint32_t)qi, (uint32_t)bh, offset};
+            philox4x32_10(c, seed_lo, seed_hi);
+            const uint32_t k0 = g ? c[2] : c[0], k1 = g ? c[3] : c[1];   // this lane's words of group 2g + u
+            const uint32_t r0 = partner(g ? c[0] : c[2]);                // the partner's words of group
+            const uint32_t r1 = partner(g ? c[1] : c[3]);                // 2(1 - g) + u, computed there
+            kw[rb][u][0] = g ? r0 : k0;
+            kw[rb][u][1] = g ? r1 : k1;
+            kw[rb][2 + u][0] = g ? k0 : r0;
+            kw[rb][2 + u][1] = g ? k1 : r1;
+        }
+    }
+}
+
 // s_waitcnt vmcnt(N) alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
 // expcnt and lgkmcnt left at their maxima).
 template <int N>
