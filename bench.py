@@ -18,8 +18,8 @@ Prints ONE JSON line:
   naive_unfused  the same attention computed the unfused way (scores and
              probabilities written to device memory, four kernels of this
              library), timed the same way, with the fused kernel's speedup.
-  backward   the gradients (fa_bwd) on the same inputs, atomic and
-             deterministic dq modes, in TFLOP/s at 2.5x the forward's flops.
+  backward   the gradients (fa_bwd, bitwise reproducible) on the same
+             inputs, in TFLOP/s at 2.5x the forward's flops.
   mask_dropout  the forward with an explicit mask and/or dropout (fa_fwd_ext).
              The backward and mask_dropout objects carry their own
              cpu_baseline: the fp64 oracle on the first heads of the workload.
@@ -229,34 +229,33 @@ def backward_leg(w, steps, warmup):
     if fa.fa_bwd_workspace_bytes(w.B, w.H, w.S, w.D, True) <= 0:
         out["skipped"] = "the backward takes D in {64, 128}"
         return out
-    for det in (False, True):
-        need = fa.fa_bwd_workspace_bytes(w.B, w.H, w.S, w.D, det)
-        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    need = fa.fa_bwd_workspace_bytes(w.B, w.H, w.S, w.D, True)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
-        def step():
-            st = fa.fa_bwd(qd, kd, vd, o, gd, lse, dq, dk, dv, w.B, w.H, w.S, w.S, w.D, w.scale,
-                           w.causal, code, det, ws, need, stream)
-            if st != 0:
-                raise fa.FaError(st, "fa_bwd")
+    def step():
+        st = fa.fa_bwd(qd, kd, vd, o, gd, lse, dq, dk, dv, w.B, w.H, w.S, w.S, w.D, w.scale,
+                       w.causal, code, True, ws, need, stream)
+        if st != 0:
+            raise fa.FaError(st, "fa_bwd")
 
-        warm_up(step, warmup, 0.2)
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
-        for _ in range(steps):
-            step()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        ms = ev0.elapsed_time(ev1) / steps
-        if not (torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()):
-            raise RuntimeError("non-finite gradient in the benchmark run")
-        tf = flops / (ms * 1e-3) / 1e12
-        out["deterministic" if det else "atomic"] = {
-            "ms_per_step": round(ms, 4), "value": round(tf, 3),
-            "frac_of_mfma_peak": round(tf / MFMA_PEAK_TFLOPS, 4), "workspace_bytes": int(need)}
-        del ws
+    warm_up(step, warmup, 0.2)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    if not (torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()):
+        raise RuntimeError("non-finite gradient in the benchmark run")
+    tf = flops / (ms * 1e-3) / 1e12
+    out["deterministic"] = {
+        "ms_per_step": round(ms, 4), "value": round(tf, 3),
+        "frac_of_mfma_peak": round(tf / MFMA_PEAK_TFLOPS, 4), "workspace_bytes": int(need)}
+    del ws
     # the backward of the masked / dropout forward: one [S, S] mask shared by
-    # all heads (90% kept) and dropout 0.1, deterministic mode
+    # all heads (90% kept) and dropout 0.1
     import numpy as np
     ld = (w.S + 3) // 4 * 4
     rng = np.random.default_rng(2400)

@@ -338,13 +338,14 @@ int fa_fwd_ext_strided(const void* q, const void* k, const void* v, void* o, flo
  * P_ij = exp(scale q_i.k_j - lse_i) (0 where masked) and D_i = dout_i . o_i:
  *   dv_j = sum_i P_ij dout_i,  dS_ij = P_ij (dout_i . v_j - D_i),
  *   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i.
- * The two accumulation modes of dq follow "catlass FlashAttention tuning for
- * a 13B service" (gsyq.cn), backward-pass section:
- *   deterministic != 0  dq by a separate pass in a fixed order: bitwise
- *                       reproducible, the scores recomputed once more;
- *   deterministic == 0  dq accumulated with fp32 atomic adds in the
- *                       workspace while dk/dv are computed, then rounded;
- *                       the last bits may differ from run to run.
+ * dq is computed by a separate pass that sums each row's key tiles in a
+ * fixed order (the scores recomputed once more), the deterministic mode of
+ * "catlass FlashAttention tuning for a 13B service" (gsyq.cn), backward-pass
+ * section: results are bitwise reproducible run to run.
+ *   deterministic    accepted for source compatibility and ignored: the
+ *                    page's non-deterministic mode (dq accumulated with fp32
+ *                    atomic adds while dk/dv are computed) is not provided,
+ *                    every call runs the deterministic kernels.
  *
  *   q, o, dout, dq   device, contiguous [B,H,Sq,D] of `dtype`
  *   k, v, dk, dv     device, contiguous [B,H,Sk,D] of `dtype`
@@ -353,7 +354,7 @@ int fa_fwd_ext_strided(const void* q, const void* k, const void* v, void* o, flo
  *                    row that sees no key)
  *   causal           key j visible to query i iff j <= i + (Sk - Sq)
  *   workspace        device memory of at least
- *                    fa_bwd_workspace_bytes(B,H,Sq,D,deterministic) bytes,
+ *                    fa_bwd_workspace_bytes(B,H,Sq,D,1) bytes,
  *                    16-byte aligned, owned by the caller, contents
  *                    overwritten; it must not overlap any other argument
  *   stream           HIP stream (NULL = default); asynchronous, no allocation
@@ -371,7 +372,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            int64_t workspace_bytes, void* stream);
 
 /*
- * fa_bwd_noalloc -- fa_bwd in its deterministic mode without a workspace
+ * fa_bwd_noalloc -- fa_bwd without a workspace
  * argument, for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid allocation).
  * The workspace is a fixed device array inside the library, 16 MiB
@@ -380,8 +381,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
  * on the first call there.  The call itself allocates nothing and does not
  * synchronise.
  *
- * Arguments, layouts, numerics and errors as for fa_bwd with
- * deterministic = 1 (results bitwise equal to that call), plus
+ * Arguments, layouts, numerics and errors as for fa_bwd (results bitwise
+ * equal to that call), plus
  * FA_ERR_SCRATCH when fa_bwd_workspace_bytes(B, H, Sq, D, 1) exceeds the
  * array (B * H * Sq above 4,194,304 rows) and FA_ERR_HIP when the array's
  * address cannot be obtained.  Every call on one GPU shares that GPU's
@@ -402,7 +403,7 @@ int64_t fa_bwd_noalloc_scratch_bytes(void);
  * (0 or 65536/(65536 - t)):
  *   dv_j = sum_i P_ij Z_ij c dout_i,  dS_ij = P_ij (Z_ij c dout_i . v_j - D_i),
  *   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,
- * D_i = dout_i . o_i.  Always the deterministic mode: the workspace is
+ * D_i = dout_i . o_i.  Deterministic like fa_bwd; the workspace is
  * fa_bwd_workspace_bytes(B, H, Sq, D, 1).  Arguments as for fa_bwd and
  * fa_fwd_ext (mask rows are read up to 31 rows past the last query, so
  * (Sq + 31) * mask row stride + Sk must stay below 2^31 bytes); the mask
@@ -428,10 +429,9 @@ int fa_bwd_ext(const void* q, const void* k, const void* v, const void* o, const
  *            elements to one address (FA_ERR_STRIDE).
  *   lse      contiguous [B, H, Sq] fp32, as for fa_bwd.
  *   mask, mask_strides, dropout_p, seed, offset  as for fa_bwd_ext (mask
- *            NULL and dropout_p 0 for the plain backward).  With a mask or
- *            dropout the deterministic mode runs whatever `deterministic`
- *            says.
- *   workspace  at least fa_bwd_workspace_bytes(B, H, Sq, D, deterministic)
+ *            NULL and dropout_p 0 for the plain backward).
+ *   deterministic  ignored, as for fa_bwd.
+ *   workspace  at least fa_bwd_workspace_bytes(B, H, Sq, D, 1)
  *            bytes; contiguous scratch as for fa_bwd.
  * Aliasing: the byte range each tensor spans (from its first to past its
  * last element) of dq, dk, dv and the workspace must not overlap one another
@@ -446,9 +446,9 @@ int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, c
                    float dropout_p, uint64_t seed, uint32_t offset, float scale, int causal, int dtype,
                    int deterministic, void* workspace, int64_t workspace_bytes, void* stream);
 
-/* Bytes of workspace fa_bwd needs (0 for an invalid shape): the row dot
- * products D_i, B*H*Sq fp32, plus in atomic mode (deterministic == 0) the
- * fp32 dq accumulator, B*H*Sq*D fp32; each part rounded up to 256 bytes. */
+/* Bytes of workspace fa_bwd, fa_bwd_ext and fa_bwd_strided need (0 for an
+ * invalid shape): the row dot products D_i, B*H*Sq fp32, rounded up to 256
+ * bytes.  `deterministic` is ignored, as for fa_bwd. */
 int64_t fa_bwd_workspace_bytes(int B, int H, int Sq, int D, int deterministic);
 
 #ifdef __cplusplus

@@ -166,14 +166,12 @@ static void bwd_checks() {
     const int B = 1, H = 3, Sq = 200, Sk = 333, D = 128;
     const int64_t wd = fa_bwd_workspace_bytes(B, H, Sq, D, 1), wa = fa_bwd_workspace_bytes(B, H, Sq, D, 0);
     CHECK_EQ(wd, ((int64_t)B * H * Sq * 4 + 255) / 256 * 256);
-    CHECK_EQ(wa, wd + ((int64_t)B * H * Sq * D * 4 + 255) / 256 * 256);
+    CHECK_EQ(wa, wd);   // the flag is ignored: no atomic dq accumulator
     CHECK_EQ(fa_bwd_workspace_bytes(0, 1, 1, 64, 1), 0);
     CHECK_EQ(fa_bwd_workspace_bytes(INT_MAX, INT_MAX, INT_MAX, 128, 0), 0);
     CHECK_EQ(fa_bwd(q, k, v, o, g, lse, dq, dk, dv, INT_MAX, INT_MAX, INT_MAX, INT_MAX, D, sc, 1, FA_BF16, 1, ws,
                     wd, nullptr), FA_ERR_SHAPE);
     CHECK_EQ(fa_bwd(q, k, v, o, g, lse, dq, dk, dv, B, H, Sq, Sk, D, sc, 1, FA_BF16, 1, ws, wd - 1, nullptr),
-             FA_ERR_SHAPE);
-    CHECK_EQ(fa_bwd(q, k, v, o, g, lse, dq, dk, dv, B, H, Sq, Sk, D, sc, 1, FA_BF16, 0, ws, wd, nullptr),
              FA_ERR_SHAPE);
     CHECK_EQ(fa_bwd(q, k, v, o, g, nullptr, dq, dk, dv, B, H, Sq, Sk, D, sc, 1, FA_BF16, 1, ws, wd, nullptr),
              FA_ERR_NULL);
@@ -183,9 +181,9 @@ static void bwd_checks() {
              FA_ERR_ALIAS);
     CHECK_EQ(fa_bwd(q, k, v, o, g, lse, dq, dk, dv, B, H, Sq, Sk, D, sc, 1, FA_BF16, 1, ws, wd, nullptr), FA_OK);
     CHECK_EQ(g_stub.last, StubState::kBwd);
-    CHECK_EQ(g_stub.deterministic, 1);
-    CHECK_EQ(fa_bwd(q, k, v, o, g, lse, dq, dk, dv, B, H, Sq, Sk, D, sc, 1, FA_BF16, 0, ws, wa, nullptr), FA_OK);
-    CHECK_EQ(g_stub.deterministic, 0);
+    g_stub.last = StubState::kNone;
+    CHECK_EQ(fa_bwd(q, k, v, o, g, lse, dq, dk, dv, B, H, Sq, Sk, D, sc, 1, FA_BF16, 0, ws, wd, nullptr), FA_OK);
+    CHECK_EQ(g_stub.last, StubState::kBwd);
     // mask and dropout arguments
     const uint8_t* mask = (const uint8_t*)dev(10);
     const int64_t ms_ok[3] = {0, 0, 336};

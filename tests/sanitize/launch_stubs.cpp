@@ -51,10 +51,9 @@ hipError_t launch_fwd_diag(const FwdParams& p, int D, int, bool, int64_t grid, b
     return hipSuccess;
 }
 namespace bwd {
-hipError_t launch_bwd(const BwdParams& p, int D, int, int, int deterministic, hipStream_t) {
+hipError_t launch_bwd(const BwdParams& p, int D, int, int, hipStream_t) {
     g_stub.last = StubState::kBwd;
     g_stub.D = D;
-    g_stub.deterministic = deterministic;
     g_stub.nqb = p.nqb;
     return hipSuccess;
 }

@@ -12,7 +12,6 @@ struct StubState {
     int dtype = 0;
     bool causal = false;
     bool masked = false;
-    int deterministic = 0;
     uint32_t drop_t = 0;
     int device_cus = 0;          // 0: no device answers (compute units fall back to 256)
     int device_queries = 0;

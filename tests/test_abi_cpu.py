@@ -212,10 +212,10 @@ def test_naive_rejects_bad_arguments(lib):
 def test_bwd_rejects_bad_arguments(lib):
     B, H, Sq, Sk, D = 1, 2, 300, 200, 64
     DO, DQ, DK, DV, W = 0x600000, 0x700000, 0x800000, 0x900000, 0x10000000
-    for det in (0, 1):
+    for det in (0, 1):          # the flag is ignored: the workspace holds D_i only
         need = fa.fa_bwd_workspace_bytes(B, H, Sq, D, det)
         rows = B * H * Sq
-        assert need == ((rows * 4 + 255) // 256 * 256) + (0 if det else (rows * D * 4 + 255) // 256 * 256)
+        assert need == (rows * 4 + 255) // 256 * 256
     assert fa.fa_bwd_workspace_bytes(1, 1, 0, 64, 1) == 0
     assert fa.fa_bwd_workspace_bytes(1, 1, 16, 96, 1) == 0
     need = fa.fa_bwd_workspace_bytes(B, H, Sq, D, 0)
@@ -235,7 +235,7 @@ def test_bwd_rejects_bad_arguments(lib):
     assert bcall(D=96) == 3 and bcall(dtype=2) == 3
     assert bcall(D=512) == 3
     need256 = fa.fa_bwd_workspace_bytes(B, H, Sq, 256, 0)
-    assert need256 == ((B * H * Sq * 4 + 255) // 256 * 256) + (B * H * Sq * 256 * 4 + 255) // 256 * 256
+    assert need256 == need                              # D_i only: independent of D
     assert bcall(D=256, wsb=need256, ws=W + 4) == 4      # D = 256 passes the shape checks
     assert bcall(Sk=1 << 24, wsb=1 << 40) == 2          # head span beyond 32-bit offsets
     assert bcall(dk=DK + 8) == 4 and bcall(ws=W + 4) == 4
@@ -362,11 +362,11 @@ def test_bwd_strided_validation(lib):
     assert call(wide, dk=addr["dq"] + sz_q + 64) == 7                 # dk inside dq's span
     assert call(dq=addr["o"] + 128) == 7 and call(ws=addr["dv"]) == 7
     assert call(mask=M, ms=(0, 0, 300), dq=M + 64) == 7               # output over the mask
-    # a mask or dropout takes the deterministic path, so its smaller workspace is enough
-    need_det = fa.fa_bwd_workspace_bytes(B, H, Sq, D, 1)
-    assert call(mask=M, ms=(0, 0, 300), wsb=need_det, ws=W + 4) == 4
-    assert call(p=0.2, wsb=need_det, ws=W + 4) == 4
-    assert call(wsb=need_det) == 2                                    # atomic mode needs the accumulator
+    # one workspace size whatever the flag: there is no atomic dq accumulator
+    assert fa.fa_bwd_workspace_bytes(B, H, Sq, D, 1) == need == (B * H * Sq * 4 + 255) // 256 * 256
+    assert call(mask=M, ms=(0, 0, 300), ws=W + 4) == 4
+    assert call(p=0.2, ws=W + 4) == 4 and call(det=1, ws=W + 4) == 4
+    assert call(wsb=need - 1) == 2
     assert call(p=1.0) == 9 and call(mask=M + 1, ms=(0, 0, 300)) == 9
 
 

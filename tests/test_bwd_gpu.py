@@ -31,7 +31,7 @@ def grad_inputs(B, H, Sq, Sk, D, dtype, seed, q_mult=1.0):
     return q, k, v, g
 
 
-def gpu_grads(q, k, v, g, causal, deterministic, scale=None):
+def gpu_grads(q, k, v, g, causal, deterministic=True, scale=None):
     qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
     o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale)
     dq, dk, dv = fa.backward(qd, kd, vd, o, lse, gd, causal=causal, scale=scale,
@@ -56,14 +56,13 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("deterministic", [True, False], ids=["det", "atomic"])
 @pytest.mark.parametrize("case", CASES, ids=["x".join(map(str, c[:5])) + ("c" if c[5] else "n") + c[6]
                                              for c in CASES])
-def test_bwd_matches_oracle(case, deterministic):
+def test_bwd_matches_oracle(case):
     B, H, Sq, Sk, D, causal, dtype, q_mult = case
-    say("case bwd", case, "det" if deterministic else "atomic")
+    say("case bwd", case)
     q, k, v, g = grad_inputs(B, H, Sq, Sk, D, dtype, seed=1500 + Sq + 7 * Sk + D, q_mult=q_mult)
-    dq, dk, dv = gpu_grads(q, k, v, g, causal, deterministic)
+    dq, dk, dv = gpu_grads(q, k, v, g, causal)
     rq, rk, rv = oracle.attention_bwd(bits(q), bits(k), bits(v), bits(g), scale=softmax_scale(D),
                                       causal=causal, dtype=dtype)
     # bounds for slices that cancel to zero (one visible key)
@@ -73,46 +72,45 @@ def test_bwd_matches_oracle(case, deterministic):
         say("  ", name, st)
 
 
-def test_bwd_deterministic_is_bitwise_repeatable_and_modes_agree():
+def test_bwd_is_bitwise_repeatable_whatever_the_flag():
+    """Every backward is deterministic: repeated calls, with the flag set or
+    not, give the same bits (there is no atomic dq mode)."""
     q, k, v, g = grad_inputs(1, 4, 700, 700, 128, "bf16", seed=1600)
     a = gpu_grads(q, k, v, g, True, True)
-    b = gpu_grads(q, k, v, g, True, True)
-    for x, y in zip(a, b):
-        assert torch.equal(x, y)
-    c = gpu_grads(q, k, v, g, True, False)
-    assert torch.equal(a[1], c[1]) and torch.equal(a[2], c[2])       # dk, dv: same kernel code
+    for det in (True, False):
+        b = gpu_grads(q, k, v, g, True, det)
+        for name, x, y in zip(("dq", "dk", "dv"), a, b):
+            assert torch.equal(x, y), (name, det)
     ref = oracle.attention_bwd(bits(q), bits(k), bits(v), bits(g), scale=softmax_scale(128),
                                causal=True, dtype="bf16")
-    parity.assert_grad_parity(to64(c[0]), ref[0], "bf16", "atomic dq")
-    parity.assert_grad_parity(to64(a[0]), ref[0], "bf16", "deterministic dq")
+    parity.assert_grad_parity(to64(a[0]), ref[0], "bf16", "dq")
 
 
 def test_bwd_overwrites_stale_outputs_and_workspace():
     """Outputs and workspace pre-filled with NaN bit patterns are fully
-    overwritten, in both modes."""
+    overwritten."""
     B, H, Sq, Sk, D = 1, 2, 190, 190, 64
     q, k, v, g = grad_inputs(B, H, Sq, Sk, D, "f16", seed=1700)
     qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
     o, lse = fa.forward(qd, kd, vd, causal=True)
     ref = oracle.attention_bwd(bits(q), bits(k), bits(v), bits(g), scale=softmax_scale(D),
                                causal=True, dtype="f16")
-    for det in (True, False):
-        need = fa.fa_bwd_workspace_bytes(B, H, Sq, D, det)
-        ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
-        outs = [torch.full_like(t, float("nan")) for t in (qd, kd, vd)]
-        st = fa.fa_bwd(qd, kd, vd, o, gd, lse, outs[0], outs[1], outs[2], B, H, Sq, Sk, D,
-                       softmax_scale(D), True, 0, det, ws, need, None)
-        assert st == 0
-        torch.cuda.synchronize()
-        for name, got, r in zip(("dq", "dk", "dv"), outs, ref):
-            parity.assert_grad_parity(to64(got), r, "f16", "%s det=%s" % (name, det))
+    need = fa.fa_bwd_workspace_bytes(B, H, Sq, D, True)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
+    outs = [torch.full_like(t, float("nan")) for t in (qd, kd, vd)]
+    st = fa.fa_bwd(qd, kd, vd, o, gd, lse, outs[0], outs[1], outs[2], B, H, Sq, Sk, D,
+                   softmax_scale(D), True, 0, True, ws, need, None)
+    assert st == 0
+    torch.cuda.synchronize()
+    for name, got, r in zip(("dq", "dk", "dv"), outs, ref):
+        parity.assert_grad_parity(to64(got), r, "f16", name)
 
 
 @pytest.mark.parametrize("name", ["gpt_causal_2x12x2048x64_f16", "llama_noncausal_1x32x2048x128_f16",
                                   "long_causal_1x32x8192x128_bf16_q4"])
 def test_bwd_workload_sampled_rows(name):
     """At the workload sizes, sampled dq rows (any head) and dk/dv rows (of two
-    heads: each needs a full pass over its head in the oracle) in both modes."""
+    heads: each needs a full pass over its head in the oracle)."""
     w = WORKLOADS[name]
     q, k, v = workload_inputs(w)
     g, _, _ = make_inputs(w.B, w.H, w.S, w.D, w.dtype, seed=w.seed + 1000)
@@ -127,10 +125,8 @@ def test_bwd_workload_sampled_rows(name):
     rq, rk, rv = oracle.attention_bwd_rows(bits(q), bits(k), bits(v), bits(g), qrows, krows,
                                            scale=w.scale, causal=w.causal, dtype=w.dtype)
     # the tolerance is relative to each gradient's magnitude over the sampled rows
-    for det in (True, False):
-        dq, dk, dv = gpu_grads(q, k, v, g, w.causal, det, scale=w.scale)
-        for nm, got, ref, rows in (("dq", dq, rq, qrows), ("dk", dk, rk, krows), ("dv", dv, rv, krows)):
-            sel = to64(got).reshape(-1, w.D)[rows]
-            st = parity.assert_grad_parity(sel[None, None], ref[None, None], w.dtype,
-                                           "%s %s det=%s" % (nm, name, det))
-            say("  ", nm, det, st)
+    dq, dk, dv = gpu_grads(q, k, v, g, w.causal, scale=w.scale)
+    for nm, got, ref, rows in (("dq", dq, rq, qrows), ("dk", dk, rk, krows), ("dv", dv, rv, krows)):
+        sel = to64(got).reshape(-1, w.D)[rows]
+        st = parity.assert_grad_parity(sel[None, None], ref[None, None], w.dtype, "%s %s" % (nm, name))
+        say("  ", nm, st)

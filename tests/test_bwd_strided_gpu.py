@@ -2,8 +2,8 @@
 backward() / backward_ext()): [B, S, H, D] views of every input and
 gradient, a packed [B, S, 3, H, D] q/k/v buffer, K and V shared by all heads
 (head stride 0).  Each case is checked against the fp64 oracle on contiguous
-copies; in the deterministic mode the strided result must also equal the
-contiguous call's bit for bit (same arithmetic, other addresses)."""
+copies; the [B, S, H, D] result must also equal the contiguous call's bit
+for bit (same arithmetic, other addresses)."""
 import numpy as np
 import pytest
 import torch
@@ -61,32 +61,30 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("deterministic", [True, False], ids=["det", "atomic"])
 @pytest.mark.parametrize("case", CASES, ids=["x".join(map(str, c[:5])) + ("c" if c[5] else "n") + c[6]
                                              for c in CASES])
-def test_bwd_bshd_views_match_oracle(case, deterministic):
+def test_bwd_bshd_views_match_oracle(case):
     """Every tensor (q, k, v, o, dout and the three gradients) a [B, S, H, D]
     view; o written by the forward through `out`."""
     B, H, Sq, Sk, D, causal, dtype = case
-    say("case bwd strided bshd", case, "det" if deterministic else "atomic")
+    say("case bwd strided bshd", case)
     q, k, v, g = grad_inputs(B, H, Sq, Sk, D, dtype, seed=3100 + Sq + Sk + D)
     qv, kv, vv, gv = (bshd(t) for t in (q, k, v, g))
     o = bshd_empty(qv)
     _, lse = fa.forward(qv, kv, vv, causal=causal, out=o)
     grads = (bshd_empty(qv), bshd_empty(kv), bshd_empty(vv))
-    fa.backward(qv, kv, vv, o, lse, gv, causal=causal, deterministic=deterministic, grads=grads)
+    fa.backward(qv, kv, vv, o, lse, gv, causal=causal, grads=grads)
     torch.cuda.synchronize()
     refs = oracle.attention_bwd(bits(q), bits(k), bits(v), bits(g), scale=softmax_scale(D), causal=causal,
                                 dtype=dtype)
     check_oracle(grads, refs, dtype, case, zero_scales(q, k, v, g, D, dtype))
-    if deterministic:
-        qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
-        oc, lc = fa.forward(qd, kd, vd, causal=causal)
-        ref = fa.backward(qd, kd, vd, oc, lc, gd, causal=causal, deterministic=True)
-        torch.cuda.synchronize()
-        assert torch.equal(oc, o) and torch.equal(lc, lse)
-        for name, a, b in zip(("dq", "dk", "dv"), grads, ref):
-            assert torch.equal(a, b), name
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
+    oc, lc = fa.forward(qd, kd, vd, causal=causal)
+    ref = fa.backward(qd, kd, vd, oc, lc, gd, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(oc, o) and torch.equal(lc, lse)
+    for name, a, b in zip(("dq", "dk", "dv"), grads, ref):
+        assert torch.equal(a, b), name
 
 
 def test_bwd_packed_qkv_input():
@@ -106,20 +104,19 @@ def test_bwd_packed_qkv_input():
     check_oracle(grads, refs, dtype, "packed qkv", zero_scales(q, k, v, g, D))
 
 
-@pytest.mark.parametrize("deterministic", [True, False], ids=["det", "atomic"])
-def test_bwd_kv_shared_by_heads(deterministic):
+def test_bwd_kv_shared_by_heads():
     """K and V with head stride 0 (one K, V per batch for all heads): the
     gradients are those of the per-head copies (the caller sums dk, dv over
     heads for the shared tensor)."""
     B, H, Sq, Sk, D, dtype = 2, 4, 190, 250, 64, "f16"
-    say("case bwd shared kv", B, H, Sq, Sk, D, dtype, deterministic)
+    say("case bwd shared kv", B, H, Sq, Sk, D, dtype)
     _, k1, v1, _ = grad_inputs(B, 1, Sq, Sk, D, dtype, seed=3300)
     q, _, _, g = grad_inputs(B, H, Sq, Sk, D, dtype, seed=3301)
     kd, vd = k1.to(DEV).expand(B, H, Sk, D), v1.to(DEV).expand(B, H, Sk, D)
     assert kd.stride(1) == 0
     qd, gd = q.to(DEV), g.to(DEV)
     o, lse = fa.forward(qd, kd, vd, causal=True)
-    grads = fa.backward(qd, kd, vd, o, lse, gd, causal=True, deterministic=deterministic)
+    grads = fa.backward(qd, kd, vd, o, lse, gd, causal=True)
     torch.cuda.synchronize()
     k, v = k1.expand(B, H, Sk, D).contiguous(), v1.expand(B, H, Sk, D).contiguous()
     refs = oracle.attention_bwd(bits(q), bits(k), bits(v), bits(g), scale=softmax_scale(D), causal=True,

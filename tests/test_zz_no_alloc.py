@@ -1,5 +1,5 @@
 """The allocation-free backward (fa_bwd_noalloc) through the C ABI against
-fa_bwd in its deterministic mode with a caller-owned workspace: bitwise
+fa_bwd with a caller-owned workspace: bitwise
 equal gradients on two calls in a row, the second with a smaller input
 (the shared scratch array keeps the first call's contents), and a call
 beyond the array's size refused with FA_ERR_SCRATCH before anything is
@@ -23,7 +23,7 @@ def _case(B, H, Sq, Sk, D, dtype, causal, seed):
     code = fa.BF16 if dtype == "bf16" else fa.F16
     sc = softmax_scale(D)
     stream = torch.cuda.current_stream()
-    # reference: fa_bwd with its own workspace, deterministic mode
+    # reference: fa_bwd with its own workspace
     need = fa.fa_bwd_workspace_bytes(B, H, Sq, D, True)
     ws = torch.empty(need, dtype=torch.uint8, device=DEV)
     ref = [torch.empty_like(t) for t in (qd, kd, vd)]

@@ -201,7 +201,8 @@ def fa_naive_workspace_bytes(B, H, S, D):
 
 def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, scale, causal, dtype, deterministic,
            workspace, workspace_bytes, stream):
-    """C ABI fa_bwd: gradients dq, dk, dv of the forward given dout."""
+    """C ABI fa_bwd: gradients dq, dk, dv of the forward given dout
+    (`deterministic` is passed through; the library ignores it)."""
     return _load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                           _ptr(dk), _ptr(dv), B, H, Sq, Sk, D, float(scale), int(bool(causal)),
                           int(dtype), int(bool(deterministic)), _ptr(workspace),
@@ -265,7 +266,7 @@ def fa_bwd_strided(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, strides, 
 
 
 def fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, scale, causal, dtype, stream):
-    """C ABI fa_bwd_noalloc: the deterministic backward with the library's fixed
+    """C ABI fa_bwd_noalloc: the backward with the library's fixed
     scratch array as its workspace (no allocation)."""
     return _load().fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                                   _ptr(dk), _ptr(dv), int(B), int(H), int(Sq), int(Sk), int(D),
@@ -404,8 +405,6 @@ def _bwd_call(q, k, v, o, lse, dout, causal, scale, mask, dropout_p, seed, offse
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     mask, mstrides = _mask_arg(mask, q, B, H, Sq, Sk)
-    if mask is not None or dropout_p != 0.0:
-        deterministic = True
     if grads is None:
         grads = tuple(t if t.stride(3) == 1 else torch.empty(t.shape, dtype=t.dtype, device=t.device)
                       for t in (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)))
@@ -440,8 +439,9 @@ def backward(q, k, v, o, lse, dout, causal=False, scale=None, deterministic=True
     are new tensors laid out like their inputs (torch.empty_like), or the
     given `grads` triple (any such strides).  The workspace (allocated here
     with torch unless given as a uint8 tensor of at least
-    fa_bwd_workspace_bytes) holds the row dot products and, when
-    deterministic is False, the fp32 dq accumulator."""
+    fa_bwd_workspace_bytes) holds the row dot products.  Results are
+    bitwise reproducible; `deterministic` is kept for source compatibility
+    and has no effect (there is no atomic dq mode)."""
     return _bwd_call(q, k, v, o, lse, dout, causal, scale, None, 0.0, 0, 0, deterministic, workspace, grads)
 
 
@@ -517,5 +517,5 @@ def backward_ext(q, k, v, o, lse, dout, causal=False, scale=None, mask=None, dro
                  workspace=None, grads=None):
     """Gradients (dq, dk, dv) of forward_ext with the same mask, dropout_p,
     seed and offset (o and lse from that call); strides as for backward().
-    Always the deterministic kernels."""
+    Bitwise reproducible like backward()."""
     return _bwd_call(q, k, v, o, lse, dout, causal, scale, mask, dropout_p, seed, offset, True, workspace, grads)

@@ -46,7 +46,7 @@ int compute_units() {
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 4 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 5 * 100 + 0;
 
 int validate_shape(int B, int H, int Sq, int Sk, int D, int dtype) {
     if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return FA_ERR_SHAPE;
@@ -393,17 +393,17 @@ int fa_naive_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 namespace {
 
 struct BwdLayout {
-    int64_t dvec_bytes = 0, acc_bytes = 0, total = 0;
+    int64_t dvec_bytes = 0, total = 0;
 };
 
 int64_t r256b(int64_t x) { return (x + 255) / 256 * 256; }
 
-bool bwd_layout(int B, int H, int Sq, int D, int deterministic, BwdLayout& L) {
+// The workspace holds D_i, one fp32 per query row.
+bool bwd_layout(int B, int H, int Sq, int D, BwdLayout& L) {
     if (validate_shape(B, H, Sq, Sq, D, FA_F16) != FA_OK) return false;
     const int64_t rows = (int64_t)B * H * Sq;
     L.dvec_bytes = r256b(rows * 4);
-    L.acc_bytes = deterministic ? 0 : r256b(rows * D * 4);
-    L.total = L.dvec_bytes + L.acc_bytes;
+    L.total = L.dvec_bytes;
     return true;
 }
 
@@ -519,8 +519,9 @@ int fa_fwd_ext_strided(const void* q, const void* k, const void* v, void* o, flo
 }
 
 int64_t fa_bwd_workspace_bytes(int B, int H, int Sq, int D, int deterministic) {
+    (void)deterministic;   // every backward is deterministic
     BwdLayout L;
-    return bwd_layout(B, H, Sq, D, deterministic, L) ? L.total : 0;
+    return bwd_layout(B, H, Sq, D, L) ? L.total : 0;
 }
 
 // Shared body of the backward entry points.  `strides` holds batch, head
@@ -529,7 +530,7 @@ static int bwd_common(const void* q, const void* k, const void* v, const void* o
                       const float* lse, void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk, int D,
                       const int64_t* strides, const uint8_t* mask, const int64_t* mask_strides,
                       float dropout_p, uint64_t seed, uint32_t offset, float scale, int causal, int dtype,
-                      int deterministic, void* workspace, int64_t workspace_bytes, void* stream) {
+                      void* workspace, int64_t workspace_bytes, void* stream) {
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace || !strides) return FA_ERR_NULL;
     int st = validate_shape(B, H, Sq, Sk, D, dtype);
     if (st != FA_OK) return st;
@@ -542,7 +543,7 @@ static int bwd_common(const void* q, const void* k, const void* v, const void* o
     for (int t = 5; t < 8; ++t)
         if (!no_self_overlap(strides + 3 * t, B, H, len[t], D)) return FA_ERR_STRIDE;
     BwdLayout L;
-    if (!bwd_layout(B, H, Sq, D, deterministic, L) || workspace_bytes < L.total) return FA_ERR_SHAPE;
+    if (!bwd_layout(B, H, Sq, D, L) || workspace_bytes < L.total) return FA_ERR_SHAPE;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)lse |
          (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)workspace) & 15)
         return FA_ERR_ALIGN;
@@ -592,7 +593,6 @@ static int bwd_common(const void* q, const void* k, const void* v, const void* o
     fa::bwd::Lay* lay[8] = {&p.Lq, &p.Lk, &p.Lv, &p.Lo, &p.Ldo, &p.Ldq, &p.Ldk, &p.Ldv};
     for (int t = 0; t < 8; ++t) *lay[t] = {strides[3 * t], strides[3 * t + 1], (int)strides[3 * t + 2]};
     p.dvec = (float*)workspace;
-    p.dqacc = deterministic ? nullptr : (float*)((char*)workspace + L.dvec_bytes);
     p.Sq = Sq;
     p.Sk = Sk;
     p.BH = B * H;
@@ -609,7 +609,7 @@ static int bwd_common(const void* q, const void* k, const void* v, const void* o
     p.seed_lo = (uint32_t)seed;
     p.seed_hi = (uint32_t)(seed >> 32);
     p.offset = offset;
-    const hipError_t err = fa::bwd::launch_bwd(p, D, dtype, causal != 0, deterministic != 0, (hipStream_t)stream);
+    const hipError_t err = fa::bwd::launch_bwd(p, D, dtype, causal != 0, (hipStream_t)stream);
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -631,10 +631,11 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            int64_t workspace_bytes, void* stream) {
     const int vs = validate_shape(B, H, Sq, Sk, D, dtype);
     if (vs != FA_OK) return (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) ? FA_ERR_NULL : vs;
+    (void)deterministic;   // every backward is deterministic
     int64_t st[24];
     contiguous_bwd_strides(H, Sq, Sk, D, st);
     return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, st, nullptr, nullptr, 0.0f, 0, 0,
-                      scale, causal, dtype, deterministic, workspace, workspace_bytes, stream);
+                      scale, causal, dtype, workspace, workspace_bytes, stream);
 }
 
 int fa_bwd_ext(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -647,7 +648,7 @@ int fa_bwd_ext(const void* q, const void* k, const void* v, const void* o, const
     int64_t st[24];
     contiguous_bwd_strides(H, Sq, Sk, D, st);
     return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, st, mask, mask_strides, dropout_p,
-                      seed, offset, scale, causal, dtype, 1, workspace, workspace_bytes, stream);
+                      seed, offset, scale, causal, dtype, workspace, workspace_bytes, stream);
 }
 
 int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -655,11 +656,9 @@ int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, c
                    const int64_t* strides, const uint8_t* mask, const int64_t* mask_strides,
                    float dropout_p, uint64_t seed, uint32_t offset, float scale, int causal, int dtype,
                    int deterministic, void* workspace, int64_t workspace_bytes, void* stream) {
-    // a mask or dropout always takes the deterministic kernels
-    if (mask || dropout_p != 0.0f) deterministic = 1;
+    (void)deterministic;   // every backward is deterministic
     return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, strides, mask, mask_strides,
-                      dropout_p, seed, offset, scale, causal, dtype, deterministic, workspace, workspace_bytes,
-                      stream);
+                      dropout_p, seed, offset, scale, causal, dtype, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -25,8 +25,7 @@ struct BwdParams {
     void* dv;           // [B, H, Sk, D]
     Lay Lq, Lk, Lv, Lo, Ldo, Ldq, Ldk, Ldv;   // layouts of q, k, v, o, dout, dq, dk, dv
     float* dvec;        // workspace [BH, Sq]: rowsum(dout * o)
-    float* dqacc;       // workspace [BH, Sq, D] fp32 (atomic mode), else null
-    const uint8_t* mask;    // nonzero = keep, null = no mask (deterministic mode only)
+    const uint8_t* mask;    // nonzero = keep, null = no mask
     int64_t m_sb, m_sh, m_ss;  // mask strides in bytes (batch, head, row)
     uint32_t drop_t;        // dropout: keep iff the 16-bit Philox draw >= drop_t (0 = none)
     float keep_scale;       // 65536 / (65536 - drop_t)
@@ -44,13 +43,11 @@ constexpr int kQueryTile = 32;   // queries per step of the dK/dV kernel
 constexpr int kQueryBlock = 128; // queries per dQ workgroup (32 per wave)
 constexpr int kKeyTile = 64;     // keys per step of the dQ kernel
 
-// Enqueue the backward on `stream`: row dot products (and, in atomic mode,
-// the zeroing of the fp32 dQ accumulator), the dK/dV kernel, then either the
-// dQ kernel (deterministic) or the conversion of the accumulator (atomic).
-hipError_t launch_bwd(const BwdParams& p, int D, int dtype, int causal, int deterministic,
-                      hipStream_t stream);
+// Enqueue the backward on `stream`: row dot products, the dK/dV kernel, then
+// the dQ kernel.
+hipError_t launch_bwd(const BwdParams& p, int D, int dtype, int causal, hipStream_t stream);
 // The same at D = 256 (fa_bwd256.hip).
-hipError_t launch_bwd256(const BwdParams& p, int dtype, int causal, int deterministic, hipStream_t stream);
+hipError_t launch_bwd256(const BwdParams& p, int dtype, int causal, hipStream_t stream);
 
 }  // namespace bwd
 }  // namespace fa

@@ -6,13 +6,15 @@
 // operator in practice" (ai6s.net), section 2, table of core optimisations:
 // recomputation in the backward pass; "FlashAttention-2 on Ascend NPU"
 // (2048ai.net), section 6.2: the forward keeps no attention matrix, so the
-// backward recomputes it).  Two accumulation modes for dQ, after "catlass
-// FlashAttention tuning for a 13B service" (gsyq.cn), backward-pass section:
-//   deterministic  a second kernel owns each dQ row and sums its key tiles in
-//                  a fixed order (scores recomputed once more);
-//   atomic         the dK/dV kernel adds each key block's dQ contribution to
-//                  an fp32 accumulator with hardware float atomics; the order
-//                  of the additions, hence the last bits, varies run to run.
+// backward recomputes it).  dQ is computed deterministically, the
+// "deterministic" mode of "catlass FlashAttention tuning for a 13B service"
+// (gsyq.cn), backward-pass section: a second kernel owns each dQ row and sums
+// its key tiles in a fixed order (scores recomputed once more), so results
+// are bitwise reproducible.  The page's faster non-deterministic mode (dQ
+// accumulated with float atomics while dK/dV are computed) is not provided:
+// on MI355X it measured 1.8x slower, and with its atomics removed it only
+// tied this mode (the dQ product, its LDS round trip and barrier inside the
+// dK/dV kernel cost what the separate pass costs).
 //
 // Per (batch, head), with P_ij = exp(scale q_i.k_j - lse_i) (0 where hidden)
 // and D_i = dO_i . O_i (= sum_j P_ij dP_ij):
@@ -20,7 +22,7 @@
 //   dQ_i = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i.
 //
 // Kernels:
-//   bwd_pre   D_i for every row (and zeroes the dQ accumulator in atomic mode);
+//   bwd_pre   D_i for every row;
 //   bwd_dkdv  one workgroup per 128-key block (32 keys per wave, K and V of
 //             those keys resident in registers); 64-query tiles of Q and dO
 //             stream through LDS (double-buffered, staged through registers);
@@ -29,10 +31,9 @@
 //             dV^T += dO^T P and dK^T += Q^T dS with P and dS taken straight
 //             from the accumulators as B operands and dO^T, Q^T read from LDS
 //             by transposing reads (ds_read_b64_tr_b16);
-//   bwd_dq    (deterministic) one workgroup per 128-query block (32 queries
-//             per wave, Q and dO resident); 64-key tiles of K and V stream
-//             through LDS; S^T = K Q^T, dP^T = V dO^T, then dQ^T += K^T dS^T;
-//   bwd_dq_convert  (atomic) dQ = scale * accumulator, rounded to the dtype.
+//   bwd_dq    one workgroup per 128-query block (32 queries per wave, Q and
+//             dO resident); 64-key tiles of K and V stream through LDS;
+//             S^T = K Q^T, dP^T = V dO^T, then dQ^T += K^T dS^T.
 //
 // The operand layouts and LDS helpers are in fa_tile.h.
 #include "fa_bwd_kernels.h"
@@ -40,15 +41,15 @@
 namespace fa {
 namespace bwd {
 
-hipError_t launch_bwd(const BwdParams& p, int D, int dtype, int causal, int deterministic,
+hipError_t launch_bwd(const BwdParams& p, int D, int dtype, int causal,
                       hipStream_t stream) {
-    if (D == 256) return launch_bwd256(p, dtype, causal, deterministic, stream);
+    if (D == 256) return launch_bwd256(p, dtype, causal, stream);
     if (D == 64) {
-        if (dtype == 0) return causal ? run<64, 0, true>(p, deterministic, stream) : run<64, 0, false>(p, deterministic, stream);
-        return causal ? run<64, 1, true>(p, deterministic, stream) : run<64, 1, false>(p, deterministic, stream);
+        if (dtype == 0) return causal ? run<64, 0, true>(p, stream) : run<64, 0, false>(p, stream);
+        return causal ? run<64, 1, true>(p, stream) : run<64, 1, false>(p, stream);
     }
-    if (dtype == 0) return causal ? run<128, 0, true>(p, deterministic, stream) : run<128, 0, false>(p, deterministic, stream);
-    return causal ? run<128, 1, true>(p, deterministic, stream) : run<128, 1, false>(p, deterministic, stream);
+    if (dtype == 0) return causal ? run<128, 0, true>(p, stream) : run<128, 0, false>(p, stream);
+    return causal ? run<128, 1, true>(p, stream) : run<128, 1, false>(p, stream);
 }
 
 }  // namespace bwd

@@ -10,9 +10,9 @@
 namespace fa {
 namespace bwd {
 
-hipError_t launch_bwd256(const BwdParams& p, int dtype, int causal, int deterministic, hipStream_t stream) {
-    if (dtype == 0) return causal ? run<256, 0, true>(p, deterministic, stream) : run<256, 0, false>(p, deterministic, stream);
-    return causal ? run<256, 1, true>(p, deterministic, stream) : run<256, 1, false>(p, deterministic, stream);
+hipError_t launch_bwd256(const BwdParams& p, int dtype, int causal, hipStream_t stream) {
+    if (dtype == 0) return causal ? run<256, 0, true>(p, stream) : run<256, 0, false>(p, stream);
+    return causal ? run<256, 1, true>(p, stream) : run<256, 1, false>(p, stream);
 }
 
 }  // namespace bwd

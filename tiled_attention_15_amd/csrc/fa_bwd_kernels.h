@@ -27,7 +27,7 @@ __device__ __forceinline__ uint64_t head_bytes(const Lay& L, int rows) {
 }
 
 // ---------------------------------------------------------------------------
-// D_i = sum_d dO_id O_id in fp32; in atomic mode also zero the dQ accumulator.
+// D_i = sum_d dO_id O_id in fp32.
 template <int D, int DT>
 __global__ __launch_bounds__(256) void bwd_pre(BwdParams p) {
     constexpr int TPR = D / 8;            // threads per row (8 values each)
@@ -38,51 +38,26 @@ __global__ __launch_bounds__(256) void bwd_pre(BwdParams p) {
     float acc = 0.0f;
     if (row < rows) {
         const int bh = (int)(row / p.Sq), qi = (int)(row - (int64_t)bh * p.Sq);
-        const int64_t off = row * D + 8 * c;   // the accumulator is contiguous
         const i32x4 a = *(const i32x4*)(head_of(p.o, p.Lo, bh, p.H) + ((int64_t)qi * p.Lo.ss + 8 * c) * 2);
         const i32x4 b = *(const i32x4*)(head_of(p.dout, p.Ldo, bh, p.H) + ((int64_t)qi * p.Ldo.ss + 8 * c) * 2);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             acc += half_f32<DT>(a[i], 0) * half_f32<DT>(b[i], 0) + half_f32<DT>(a[i], 1) * half_f32<DT>(b[i], 1);
-        if (p.dqacc) {
-            const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-            *(f32x4*)(p.dqacc + off) = z;
-            *(f32x4*)(p.dqacc + off + 4) = z;
-        }
     }
 #pragma unroll
     for (int o = TPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
     if (row < rows && c == 0) p.dvec[row] = acc;
 }
 
-// dQ = scale * accumulator, rounded to the dtype (atomic mode).
-template <int D, int DT>
-__global__ __launch_bounds__(256) void bwd_dq_convert(BwdParams p, int64_t n8) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n8) return;
-    const int64_t row = i / (D / 8);
-    const int c = (int)(i - row * (D / 8));
-    const int bh = (int)(row / p.Sq), qi = (int)(row - (int64_t)bh * p.Sq);
-    const f32x4 a = *(const f32x4*)(p.dqacc + 8 * i);
-    const f32x4 b = *(const f32x4*)(p.dqacc + 8 * i + 4);
-    const float s = p.scale;
-    i32x4 w;
-    w[0] = pack2<DT>(a[0] * s, a[1] * s);
-    w[1] = pack2<DT>(a[2] * s, a[3] * s);
-    w[2] = pack2<DT>(b[0] * s, b[1] * s);
-    w[3] = pack2<DT>(b[2] * s, b[3] * s);
-    *(i32x4*)(const_cast<char*>(head_of(p.dq, p.Ldq, bh, p.H)) + ((int64_t)qi * p.Ldq.ss + 8 * c) * 2) = w;
-}
-
 // ---------------------------------------------------------------------------
-// dK, dV (and in atomic mode the dQ contributions) of one 128-key block.
-// Sized for two workgroups per CU at D <= 128 (two waves per SIMD, <= 256
-// registers per lane; one with a mask, dropout or the atomic dQ, and at
-// D = 256, where the accumulators fill the 256 AGPRs): the key block sits in LDS (K fragments are read from there at each
-// use) while V's fragments and the dK^T, dV^T accumulators stay in registers;
-// 32-query tiles of Q and dO go straight from global memory into LDS.
-template <int D, int DT, bool CAUSAL, bool ATOMIC, bool MASK = false, bool DROP = false>
-__global__ __launch_bounds__(256, (ATOMIC || MASK || DROP || D > 128) ? 1 : 2) void bwd_dkdv(BwdParams p) {
+// dK, dV of one 128-key block.  Sized for two workgroups per CU at D <= 128
+// (two waves per SIMD, <= 256 registers per lane; one with a mask or dropout,
+// and at D = 256, where the accumulators fill the 256 AGPRs): the key block
+// sits in LDS (K fragments are read from there at each use) while V's
+// fragments and the dK^T, dV^T accumulators stay in registers; 32-query tiles
+// of Q and dO go straight from global memory into LDS.
+template <int D, int DT, bool CAUSAL, bool MASK = false, bool DROP = false>
+__global__ __launch_bounds__(256, (MASK || DROP || D > 128) ? 1 : 2) void bwd_dkdv(BwdParams p) {
     constexpr int DC = D / 16;                         // k-steps over the head dimension
     constexpr int DB = D / 32;                         // 32-column blocks of the head dimension
     constexpr int QT = kQueryTile;
@@ -90,10 +65,9 @@ __global__ __launch_bounds__(256, (ATOMIC || MASK || DROP || D > 128) ? 1 : 2) v
     constexpr int TN = QT * D / 8 / 256;               // direct loads per thread per tile
     constexpr int KBLK = kKeyBlock * D * 2;            // bytes of the key block
     constexpr int KN = kKeyBlock * D / 8 / 256;        // direct loads per thread for it
-    constexpr int DSB = ATOMIC ? kKeyBlock * QT * 2 : 0;
     static_assert(TN >= 1 && KN >= 1, "tile must split over the threads");
 
-    __shared__ __attribute__((aligned(16))) char smem[KBLK + 4 * TILE + DSB];
+    __shared__ __attribute__((aligned(16))) char smem[KBLK + 4 * TILE];
     __shared__ __attribute__((aligned(16))) float lse_s[2][QT];
     __shared__ __attribute__((aligned(16))) float dv_s[2][QT];
     // mask bytes of a tile, [query][key of the block] (with a mask), and the
@@ -268,33 +242,6 @@ __global__ __launch_bounds__(256, (ATOMIC || MASK || DROP || D > 128) ? 1 : 2) v
             }
         }
 
-        if constexpr (ATOMIC) {
-            // dS^T of this wave's keys into LDS as [key][query], then
-            // dQ[q][d] += sum over the block's 128 keys of dS[q][key] K[key][d]
-            lds_t* dst = sm + KBLK + 4 * TILE;
-            const int kr = 32 * w + lq;
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                i32x2 v2;
-                v2[0] = pack2<DT>(dp[4 * a], dp[4 * a + 1]);
-                v2[1] = pack2<DT>(dp[4 * a + 2], dp[4 * a + 3]);
-                *(__attribute__((address_space(3))) i32x2*)(dst + toff<QT>(kr, a) + 8 * g) = v2;
-            }
-            __syncthreads();
-            for (int db = w; db < DB; db += 4) {
-                f32x16 acc = zero16();
-#pragma unroll
-                for (int st = 0; st < kKeyBlock / 16; ++st)
-                    acc = mma<DT>(tr_frag<QT>(dst, st, 0, tl), tr_frag<D>(kblk, st, db, tl), acc);
-                float* base = p.dqacc + ((int64_t)bh * Sq) * D + 32 * db + lq;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int qi = q0 + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if (qi < Sq) unsafeAtomicAdd(base + (int64_t)qi * D, acc[r]);
-                }
-            }
-        }
-
         wait_vmcnt<0>();
         if (t + 1 < nqt) store_stats(buf ^ 1);
         __syncthreads();
@@ -324,7 +271,7 @@ __global__ __launch_bounds__(256, (ATOMIC || MASK || DROP || D > 128) ? 1 : 2) v
 }
 
 // ---------------------------------------------------------------------------
-// dQ of one 128-query block (deterministic mode).
+// dQ of one 128-query block.
 template <int D, int DT, bool CAUSAL, bool MASK = false, bool DROP = false>
 __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_dq(BwdParams p) {
     constexpr int DC = D / 16, DB = D / 32;
@@ -505,39 +452,26 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_dq(BwdParams p) {
 // ---------------------------------------------------------------------------
 template <int D, int DT, bool CAUSAL, bool MASK, bool DROP>
 static void run_masked(const BwdParams& p, hipStream_t st) {
-    hipLaunchKernelGGL((bwd_dkdv<D, DT, CAUSAL, false, MASK, DROP>), dim3((unsigned)(p.BH * p.nkb)), dim3(256), 0,
-                       st, p);
+    hipLaunchKernelGGL((bwd_dkdv<D, DT, CAUSAL, MASK, DROP>), dim3((unsigned)(p.BH * p.nkb)), dim3(256), 0, st, p);
     hipLaunchKernelGGL((bwd_dq<D, DT, CAUSAL, MASK, DROP>), dim3((unsigned)(p.BH * p.nqb)), dim3(256), 0, st, p);
 }
 
 template <int D, int DT, bool CAUSAL>
-static hipError_t run(const BwdParams& p, int deterministic, hipStream_t st) {
+static hipError_t run(const BwdParams& p, hipStream_t st) {
     const int64_t rows = (int64_t)p.BH * p.Sq;
     constexpr int RPB = 256 / (D / 8);
     if (rows > 0)
         hipLaunchKernelGGL((bwd_pre<D, DT>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st, p);
     if (p.mask != nullptr || p.drop_t != 0) {
-        // masks and dropout run in the deterministic mode
         if (p.mask != nullptr && p.drop_t != 0) run_masked<D, DT, CAUSAL, true, true>(p, st);
         else if (p.mask != nullptr) run_masked<D, DT, CAUSAL, true, false>(p, st);
         else run_masked<D, DT, CAUSAL, false, true>(p, st);
         return hipGetLastError();
     }
-    if (p.Sk > 0) {
-        const dim3 grid((unsigned)(p.BH * p.nkb));
-        if (deterministic)
-            hipLaunchKernelGGL((bwd_dkdv<D, DT, CAUSAL, false>), grid, dim3(256), 0, st, p);
-        else
-            hipLaunchKernelGGL((bwd_dkdv<D, DT, CAUSAL, true>), grid, dim3(256), 0, st, p);
-    }
-    if (rows > 0) {
-        if (deterministic) {
-            hipLaunchKernelGGL((bwd_dq<D, DT, CAUSAL>), dim3((unsigned)(p.BH * p.nqb)), dim3(256), 0, st, p);
-        } else {
-            const int64_t n8 = rows * D / 8;
-            hipLaunchKernelGGL((bwd_dq_convert<D, DT>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, p, n8);
-        }
-    }
+    if (p.Sk > 0)
+        hipLaunchKernelGGL((bwd_dkdv<D, DT, CAUSAL>), dim3((unsigned)(p.BH * p.nkb)), dim3(256), 0, st, p);
+    if (rows > 0)
+        hipLaunchKernelGGL((bwd_dq<D, DT, CAUSAL>), dim3((unsigned)(p.BH * p.nqb)), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
