@@ -239,11 +239,25 @@ static void ext_checks() {
              FA_OK);
     CHECK_EQ(g_stub.last, StubState::kFwd);
     CHECK_EQ(g_stub.masked, 1);
-    // dropout: the general kernel, threshold round(p * 65536)
+    CHECK_EQ(g_stub.drop_t, 0);
+    // dropout: the dropout instances of the tuned kernel, threshold round(p * 65536)
     CHECK_EQ(fa_fwd_ext(q, k, v, o, lse, 1, 4, 256, 300, 128, mask, ms_ok, 0.1f, 1, 0, sc, 1, FA_F16, nullptr),
              FA_OK);
-    CHECK_EQ(g_stub.last, StubState::kExt);
+    CHECK_EQ(g_stub.last, StubState::kFwdDrop);
+    CHECK_EQ(g_stub.masked, 1);
     CHECK_EQ(g_stub.drop_t, 6554);
+    // a row stride the tuned kernel's 32-bit head offsets do not reach (a head
+    // padded to 320 rows spans 2^31 bytes or more) but the general kernel's do
+    // (256 rows): the general kernel
+    {
+        const int64_t r = 4000000;
+        const int64_t st[12] = {100 * r, 100 * r, r, 100 * r, 100 * r, r, 100 * r, 100 * r, r, 100 * r, 100 * r, r};
+        g_stub.last = StubState::kNone;
+        CHECK_EQ(fa_fwd_ext_strided(q, k, v, o, lse, 1, 1, 100, 100, 128, st, nullptr, nullptr, 0.1f, 1, 0, sc, 1,
+                                    FA_F16, nullptr), FA_OK);
+        CHECK_EQ(g_stub.last, StubState::kExt);
+        CHECK_EQ(g_stub.drop_t, 6554);
+    }
     // a dropout probability that rounds to 65536 is refused
     CHECK_EQ(fa_fwd_ext(q, k, v, o, lse, 1, 4, 256, 300, 128, nullptr, nullptr, 0.99999994f, 1, 0, sc, 1, FA_F16,
                         nullptr), FA_ERR_MASK_DROPOUT);

@@ -40,6 +40,13 @@ hipError_t launch_fwd(const FwdParams& p, int D, int dtype, bool causal, int64_t
     g_stub.dtype = dtype;
     g_stub.causal = causal;
     g_stub.masked = p.mask != nullptr;
+    g_stub.drop_t = p.drop_t;
+    return hipSuccess;
+}
+hipError_t launch_fwd_drop(const FwdParams& p, int D, int dtype, bool causal, int64_t grid, bool split,
+                           hipStream_t s) {
+    launch_fwd(p, D, dtype, causal, grid, split, s);
+    g_stub.last = StubState::kFwdDrop;
     return hipSuccess;
 }
 hipError_t launch_fwd_diag(const FwdParams& p, int D, int, bool, int64_t grid, bool split, hipStream_t) {

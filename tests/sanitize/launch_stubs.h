@@ -3,7 +3,7 @@
 #include <stdint.h>
 
 struct StubState {
-    enum Kind { kNone, kFwd, kDiag, kBwd, kExt, kNaive };
+    enum Kind { kNone, kFwd, kFwdDrop, kDiag, kBwd, kExt, kNaive };
     Kind last = kNone;
     int64_t grid = 0;
     bool split = false;

@@ -16,7 +16,7 @@ SOURCES = [os.path.join(CSRC, "fa_api.cpp"), os.path.join(CSRC, "fa_fwd_kernel.h
            os.path.join(CSRC, "fa_naive.hip"), os.path.join(CSRC, "fa_bwd.hip"),
            os.path.join(CSRC, "fa_fwd_ext.hip"), os.path.join(CSRC, "fa_bwd256.hip"),
            os.path.join(CSRC, "fa_fwd_diag.hip"), os.path.join(CSRC, "fa_clock.hip"),
-           os.path.join(CSRC, "fa_bwd_noalloc.hip")]
+           os.path.join(CSRC, "fa_bwd_noalloc.hip"), os.path.join(CSRC, "fa_fwd_drop.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Kernels whose MFMA accumulators are also worked on by vector instructions:
 # the VGPR form of the MFMA instructions keeps those accumulators in VGPRs

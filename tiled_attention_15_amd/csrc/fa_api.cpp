@@ -136,13 +136,22 @@ struct DiagArgs {
     uint32_t* tiles;
 };
 
-// The tuned kernel (D = 64 or 128) on validated arguments; mask (with its
-// byte strides) may be null; diag selects the diagnostic instance.
+// Dropout arguments of the tuned kernel: threshold t = round(p * 65536)
+// (0: no dropout), Philox key and counter offset.
+struct DropArgs {
+    uint32_t t = 0;
+    uint64_t seed = 0;
+    uint32_t offset = 0;
+};
+
+// The tuned kernel on validated arguments; mask (with its byte strides) may
+// be null; drop selects the dropout instances when drop.t > 0; diag selects
+// the diagnostic instance.
 static int launch_tuned(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Sq,
                         int Sk, int D, const int64_t* q_strides, const int64_t* k_strides,
                         const int64_t* v_strides, const int64_t* o_strides, const uint8_t* mask,
                         const int64_t* mask_strides, float scale, int causal, int dtype, void* stream,
-                        const DiagArgs* diag = nullptr) {
+                        const DiagArgs* diag = nullptr, DropArgs drop = DropArgs()) {
     fa::FwdParams p = {};
     p.q = q;
     p.k = k;
@@ -167,6 +176,11 @@ static int launch_tuned(const void* q, const void* k, const void* v, void* o, fl
     p.m_sb = mask ? mask_strides[0] : 0;
     p.m_sh = mask ? mask_strides[1] : 0;
     p.m_ss = mask ? (int)mask_strides[2] : 0;
+    p.drop_t = drop.t;
+    p.keep_scale = (float)(65536.0 / (65536.0 - (double)drop.t));
+    p.seed_lo = (uint32_t)drop.seed;
+    p.seed_hi = (uint32_t)(drop.seed >> 32);
+    p.offset = drop.offset;
     const int64_t grid = (int64_t)p.BH * p.nqb;
     if (diag != nullptr) {
         p.diag_flags = diag->flags;
@@ -175,7 +189,9 @@ static int launch_tuned(const void* q, const void* k, const void* v, void* o, fl
         const hipError_t err = fa::launch_fwd_diag(p, D, dtype, causal != 0, grid, split, (hipStream_t)stream);
         return err == hipSuccess ? FA_OK : FA_ERR_HIP;
     }
-    const hipError_t err = fa::launch_fwd(p, D, dtype, causal != 0, grid, split, (hipStream_t)stream);
+    const hipError_t err = drop.t != 0
+                               ? fa::launch_fwd_drop(p, D, dtype, causal != 0, grid, split, (hipStream_t)stream)
+                               : fa::launch_fwd(p, D, dtype, causal != 0, grid, split, (hipStream_t)stream);
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -461,13 +477,20 @@ static int ext_common(const void* q, const void* k, const void* v, void* o, floa
     }
     if (lse && overlap(out[0][0], out[0][1], out[1][0], out[1][1])) return FA_ERR_ALIAS;
 
-    // No dropout: the tuned kernel, with the mask if there is one.  Without
-    // a mask this is the plain forward exactly as fa_fwd_strided runs it (the
-    // two calls agree bit for bit).
-    if (t == 0 && head_span_ok(Sq, strides[2], D) && head_span_ok(Sk, strides[5], D) &&
-        head_span_ok(Sk, strides[8], D) && head_span_ok(Sq, strides[11], D))
+    // The tuned kernel, with the mask and the dropout if there are any,
+    // whenever its 32-bit head offsets reach (they pad a head to whole
+    // 256-row blocks); without mask or dropout this is the plain forward
+    // exactly as fa_fwd_strided runs it (the two calls agree bit for bit).
+    // Beyond that reach, the general kernel below (128-row blocks).
+    if (head_span_ok(Sq, strides[2], D) && head_span_ok(Sk, strides[5], D) && head_span_ok(Sk, strides[8], D) &&
+        head_span_ok(Sq, strides[11], D)) {
+        DropArgs drop;
+        drop.t = (uint32_t)t;
+        drop.seed = seed;
+        drop.offset = offset;
         return launch_tuned(q, k, v, o, lse, B, H, Sq, Sk, D, strides, strides + 3, strides + 6, strides + 9, mask,
-                            mask_strides, scale, causal, dtype, stream);
+                            mask_strides, scale, causal, dtype, stream, nullptr, drop);
+    }
 
     fa::ext::ExtParams p = {};
     p.q = q;

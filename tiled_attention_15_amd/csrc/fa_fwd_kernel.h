@@ -55,11 +55,21 @@
 //   does on diagonal tiles ("FlashAttention-2 on Ascend NPU: how
 //   ops-transformer reaches 3x" (2048ai.net), section 3.4: the mask acts on
 //   the score tile on chip).
+// * Optional dropout (the DROP instances): in its softmax phase each lane
+//   draws the Philox4x32-10 blocks of its own 32 keys (a lane's 16
+//   consecutive keys of a 32-key block are two whole 8-key blocks of the
+//   generator's counter, so no lane needs another's words) and clears the
+//   dropped probabilities in the packed P; O's divisor and the lse stay
+//   those of the undropped softmax and the kept weights are scaled by
+//   65536 / (65536 - t) at the end ("FlashAttention-2 on Ascend NPU: how
+//   ops-transformer reaches 3x" (2048ai.net), sections 3.4 and 6.3: dropout
+//   fused into the kernel, on chip).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "fa_launch.h"
+#include "fa_tile.h"
 
 namespace fa {
 
@@ -119,6 +129,23 @@ __device__ __forceinline__ float dot2_ones(int x, float acc) {
         const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
         return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), one, acc, false);
     }
+}
+
+// Dropout on a dword of two packed 16-bit probabilities pw: half h is kept
+// iff half h of the random word r is >= t, with t - 1 in both halves of
+// tm1x2.  The saturating difference r - (t - 1) is nonzero exactly for the
+// kept halves, its minimum with 1 is then 1 or 0, and the 16-bit product
+// keeps the probability's bits or clears them: three packed 16-bit integer
+// instructions per pair (the compiler renders the same expression as
+// compares, selects and a permute, five).  `ones` holds 1 in both halves.
+__device__ __forceinline__ int drop_pair(int pw, uint32_t r, uint32_t tm1x2, uint32_t ones) {
+    int out;
+    asm("v_pk_sub_u16 %0, %1, %2 clamp\n\t"
+        "v_pk_min_u16 %0, %0, %3\n\t"
+        "v_pk_mul_lo_u16 %0, %4, %0"
+        : "=&v"(out)
+        : "v"(r), "s"(tm1x2), "s"(ones), "v"(pw));
+    return out;
 }
 
 // Value of the partner lane (l ^ 32) combined with our own: returns both halves.
@@ -234,9 +261,9 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
 // wave runs its softmax on into p.tiles, and stores O in fp32 to p.o32
 // beside the usual store, so the kernel's own error can be measured before
 // the rounding of O to 16 bits.
-template <int D, int DT, bool CAUSAL, bool MASK, bool SPLIT, bool DIAG = false>
+template <int D, int DT, bool CAUSAL, bool MASK, bool SPLIT, bool DIAG = false, bool DROP = false>
 __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
-    static_assert(!DIAG || (!MASK && D != 256), "diagnostic instances: no mask, D <= 128");
+    static_assert(!DIAG || (!MASK && !DROP && D != 256), "diagnostic instances: no mask or dropout, D <= 128");
     constexpr int NW = 8;
     constexpr int NT = 512;
     // D = 256: the two wave groups share 128 query rows and split the head
@@ -526,6 +553,26 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) rsum = dot2_ones<DT>(pf[c][e], rsum);
         r_run += rsum;
+        if constexpr (DROP) {
+            // keys t*BC + 32*kb2 + 16*g + 8*u + 0..7 (registers 8u..8u+7 of
+            // s[kb2], i.e. pf[2*kb2 + u]) form the Philox block at counter
+            // (8t + 4kb2 + 2g + u, query, bh, offset); word e decides the
+            // keys 2e (low half) and 2e + 1 (high half) of the eight, the
+            // halves of pf[2*kb2 + u][e]
+            const uint32_t tm1 = p.drop_t - 1u;
+            const uint32_t tm1x2 = tm1 | (tm1 << 16);
+            const uint32_t c0 = (uint32_t)(8 * t + 2 * g);
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    uint32_t c[4] = {c0 + 4 * kb2 + u, (uint32_t)qrow, (uint32_t)bh, p.offset};
+                    tile::philox4x32_10(c, p.seed_lo, p.seed_hi);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        pf[2 * kb2 + u][e] = drop_pair(pf[2 * kb2 + u][e], c[e], tm1x2, 0x00010001u);
+                }
+        }
     };
 
     // Instruction order of a matrix phase (P V then K Q^T: 32 MFMAs, 2*16
@@ -883,7 +930,8 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
     if constexpr (!SPLIT) store_tiles();
     const float l_tot = xsum32(l_run);
     const float r_tot = xsum32(r_run);
-    const float inv = r_tot > 0.0f ? 1.0f / r_tot : 0.0f;
+    // with dropout the kept weights are scaled by 65536 / (65536 - t)
+    const float inv = r_tot > 0.0f ? (DROP ? p.keep_scale : 1.0f) / r_tot : 0.0f;
     const int qrow = qw0 + lq;
     if constexpr (DIAG) {
         if (p.o32 != nullptr) {

@@ -30,6 +30,13 @@ struct FwdParams {
     const uint8_t* mask;   // null = no mask
     int64_t m_sb, m_sh;
     int m_ss;
+    // Dropout (the DROP instances): score (bh, i, j) is kept iff half j%2 of
+    // word (j%8)/2 of Philox4x32-10 at counter (j/8, i, bh, offset), key
+    // (seed_lo, seed_hi), is >= drop_t (1..65535); kept probabilities are
+    // scaled by keep_scale = 65536 / (65536 - drop_t).
+    uint32_t drop_t;
+    float keep_scale;
+    uint32_t seed_lo, seed_hi, offset;
     // Diagnostic instances only (ignored by the others).
     int diag_flags;        // kDiagReverseOrder: workgroups take their blocks in reverse order
     float* o32;            // null, or fp32 O [B*H, Sq, D] contiguous
@@ -43,6 +50,10 @@ constexpr int kDiagReverseOrder = 1;
 // kBlockQSplit-row blocks); returns hipGetLastError() after the launch.
 hipError_t launch_fwd(const FwdParams& p, int D, int dtype, bool causal, int64_t grid, bool split,
                       hipStream_t stream);
+// The dropout instances (p.drop_t > 0; with the mask when p.mask is set) of
+// the same kernel (fa_fwd_drop.hip).
+hipError_t launch_fwd_drop(const FwdParams& p, int D, int dtype, bool causal, int64_t grid, bool split,
+                           hipStream_t stream);
 // The diagnostic instance (D = 64 or 128, no mask) of the same kernel.
 hipError_t launch_fwd_diag(const FwdParams& p, int D, int dtype, bool causal, int64_t grid, bool split,
                            hipStream_t stream);
