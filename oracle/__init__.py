@@ -82,11 +82,12 @@ def _bind(lib):
     lib.ora_dropout_threshold.restype = ctypes.c_int
     lib.ora_attention_fwd_ext.argtypes = [u16p, u16p, u16p] + [ctypes.c_int] * 5 + [
         ctypes.POINTER(ctypes.c_uint8), i64p, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint32,
-        ctypes.c_float, ctypes.c_int, ctypes.c_int, i64p, ctypes.c_int64, f64p, f64p, ctypes.c_int]
+        ctypes.c_float, ctypes.c_int, ctypes.c_int64, ctypes.c_int, i64p, ctypes.c_int64, f64p, f64p,
+        ctypes.c_int]
     lib.ora_attention_fwd_ext.restype = ctypes.c_int
     lib.ora_attention_bwd_ext.argtypes = [u16p, u16p, u16p, u16p] + [ctypes.c_int] * 5 + [
         ctypes.POINTER(ctypes.c_uint8), i64p, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint32,
-        ctypes.c_float, ctypes.c_int, ctypes.c_int, i64p, ctypes.c_int64, i64p, ctypes.c_int64,
+        ctypes.c_float, ctypes.c_int, ctypes.c_int64, ctypes.c_int, i64p, ctypes.c_int64, i64p, ctypes.c_int64,
         f64p, f64p, f64p, ctypes.c_int]
     lib.ora_attention_bwd_ext.restype = ctypes.c_int
     return lib
@@ -226,10 +227,12 @@ def dropout_threshold(p, lib=None):
 
 
 def attention_fwd_ext(q, k, v, *, scale, causal, dtype, mask=None, mask_strides=None,
-                      dropout_p=0.0, seed=0, offset=0, rows=None, nthreads=0, lib=None):
+                      dropout_p=0.0, seed=0, offset=0, rows=None, causal_offset=None, nthreads=0, lib=None):
     """Forward with an explicit boolean mask (uint8, nonzero = keep, element
     strides (batch, head, row) in mask_strides, columns contiguous) and
-    keep-and-rescale dropout.  rows: optional flat row ids.
+    keep-and-rescale dropout.  rows: optional flat row ids.  causal_offset:
+    the causal diagonal's offset c (key j visible to query i iff j <= i + c;
+    None: c = Sk - Sq, bottom-right).
 
     Returns (o [B,H,Sq,D] or [n, D], lse [B,H,Sq] or [n]) float64."""
     lib = lib or load()
@@ -255,19 +258,22 @@ def attention_fwd_ext(q, k, v, *, scale, causal, dtype, mask=None, mask_strides=
         o = np.empty((B, H, Sq, D), dtype=np.float64)
         lse = np.empty((B, H, Sq), dtype=np.float64)
         rp, nr = None, 0
+    c = Sk - Sq if causal_offset is None else int(causal_offset)
     rc = lib.ora_attention_fwd_ext(qp, kp, vp, B, H, Sq, Sk, D, mp, sp, ctypes.c_float(dropout_p),
                                    ctypes.c_uint64(seed), ctypes.c_uint32(offset),
-                                   ctypes.c_float(scale), int(bool(causal)), _DTYPES[dtype], rp, nr,
-                                   _f64p(o), _f64p(lse), int(nthreads))
+                                   ctypes.c_float(scale), int(bool(causal)), ctypes.c_int64(c), _DTYPES[dtype],
+                                   rp, nr, _f64p(o), _f64p(lse), int(nthreads))
     if rc != 0:
         raise RuntimeError("ora_attention_fwd_ext failed with code %d" % rc)
     return o, lse
 
 
 def attention_bwd_ext(q, k, v, dout, *, scale, causal, dtype, mask=None, mask_strides=None,
-                      dropout_p=0.0, seed=0, offset=0, qrows=None, krows=None, nthreads=0, lib=None):
+                      dropout_p=0.0, seed=0, offset=0, qrows=None, krows=None, causal_offset=None, nthreads=0,
+                      lib=None):
     """Backward of attention_fwd_ext (gradients of sum(O * dout)).  qrows /
     krows: flat query / key row ids to return (all rows when None).
+    causal_offset as for attention_fwd_ext.
 
     Returns (dq, dk, dv): [B,H,Sq,D], [B,H,Sk,D], [B,H,Sk,D] float64 when
     the rows are not given, else [nq, D], [nk, D], [nk, D]."""
@@ -293,9 +299,11 @@ def attention_bwd_ext(q, k, v, dout, *, scale, causal, dtype, mask=None, mask_st
     dk = np.empty((krows.size, D), dtype=np.float64)
     dv = np.empty((krows.size, D), dtype=np.float64)
     i64 = ctypes.POINTER(ctypes.c_int64)
+    c = Sk - Sq if causal_offset is None else int(causal_offset)
     rc = lib.ora_attention_bwd_ext(qp, kp, vp, gp, B, H, Sq, Sk, D, mp, sp, ctypes.c_float(dropout_p),
                                    ctypes.c_uint64(seed), ctypes.c_uint32(offset), ctypes.c_float(scale),
-                                   int(bool(causal)), _DTYPES[dtype], qrows.ctypes.data_as(i64), qrows.size,
+                                   int(bool(causal)), ctypes.c_int64(c), _DTYPES[dtype],
+                                   qrows.ctypes.data_as(i64), qrows.size,
                                    krows.ctypes.data_as(i64), krows.size, _f64p(dq), _f64p(dk), _f64p(dv),
                                    int(nthreads))
     if rc != 0:

@@ -30,7 +30,13 @@
  *     "Causal Mask implementation": each position sees only earlier tokens.
  *     Reading used here: key j is visible to query i iff j <= i + (Sk - Sq)
  *     (bottom-right alignment; for Sq == Sk this is j <= i, the diagonal
- *     included).
+ *     included).  The masked/dropout functions also take the diagonal's
+ *     offset c explicitly (j visible iff j <= i + c): a block of a sequence
+ *     split into chunks, queries from global position qs and keys from ks,
+ *     sees key j iff ks + j <= qs + i, i.e. c = qs - ks ("FlashAttention-2
+ *     on Ascend NPU" (2048ai.net), section 6.4, sequence parallelism: each
+ *     device works on its own chunk of the sequence); c = Sk - Sq is the
+ *     rule above.
  *   - The log-sum-exp output is not named by the pages; it is the row
  *     normaliser L that their block pseudo-code divides by (lanjinlin.com.cn,
  *     "math principle"), written in natural-log form: lse_i = m_i + ln l_i.
@@ -93,9 +99,11 @@ void ora_decode(const uint16_t* src, double* dst, int64_t n, int dtype) {
         dst[i] = dtype == ORA_BF16 ? ora_bf16_to_f64(src[i]) : ora_f16_to_f64(src[i]);
 }
 
-static int visible(int64_t i, int64_t j, int64_t Sq, int64_t Sk, int causal) {
+/* Causal rule with the diagonal at offset c: key j visible to query i iff
+ * j <= i + c (everything visible without the causal flag). */
+static int visible(int64_t i, int64_t j, int64_t c, int causal) {
     if (!causal) return 1;
-    return j <= i + (Sk - Sq);
+    return j <= i + c;
 }
 
 /* Probabilities of one query row against all keys of its head: materialise
@@ -106,7 +114,7 @@ static double row_probs(const double* qrow, const double* K, int64_t i, int64_t 
                         int D, double scale, int causal, double* srow) {
     /* scores */
     for (int64_t j = 0; j < Sk; ++j) {
-        if (!visible(i, j, Sq, Sk, causal)) { srow[j] = -INFINITY; continue; }
+        if (!visible(i, j, Sk - Sq, causal)) { srow[j] = -INFINITY; continue; }
         const double* kr = K + j * D;
         double acc = 0.0;
         for (int d = 0; d < D; ++d) acc += qrow[d] * kr[d];
@@ -535,8 +543,9 @@ static int keep_element(uint64_t seed, uint32_t offset, int64_t bh, int64_t i, i
  * The forward with an explicit boolean mask and dropout
  * ("FlashAttention-2 on Ascend NPU" (2048ai.net), section 3.4, fused mask
  * and dropout, and section 6.3):
- *   visible(i,j) = causal rule and mask[b,h,i,j] != 0 (nonzero = keep, as the
- *                  page's kernel treats a true entry);
+ *   visible(i,j) = causal rule with the diagonal at offset c (j <= i + c)
+ *                  and mask[b,h,i,j] != 0 (nonzero = keep, as the page's
+ *                  kernel treats a true entry);
  *   P_ij         = softmax over the visible keys, lse_i as in the forward;
  *   O_i          = sum_j P_ij * keep_ij / (1 - t/65536) * v_j,
  * i.e. standard keep-and-rescale dropout applied to the probabilities (the
@@ -546,11 +555,11 @@ static int keep_element(uint64_t seed, uint32_t offset, int64_t bh, int64_t i, i
  * mstride, columns contiguous; NULL = no mask.  dropout_p = 0 keeps all.
  */
 static void row_attention_ext(const double* qrow, const double* K, const double* V, int64_t bh,
-                              int64_t i, int64_t Sq, int64_t Sk, int D, double scale, int causal,
+                              int64_t i, int64_t c, int64_t Sk, int D, double scale, int causal,
                               const uint8_t* mrow, int t, uint64_t seed, uint32_t offset,
                               double* srow, double* orow, double* lse_out) {
     for (int64_t j = 0; j < Sk; ++j) {
-        const int vis = visible(i, j, Sq, Sk, causal) && (!mrow || mrow[j] != 0);
+        const int vis = visible(i, j, c, causal) && (!mrow || mrow[j] != 0);
         if (!vis) { srow[j] = -INFINITY; continue; }
         double acc = 0.0;
         for (int d = 0; d < D; ++d) acc += qrow[d] * K[j * D + d];
@@ -579,8 +588,8 @@ static void row_attention_ext(const double* qrow, const double* K, const double*
 int ora_attention_fwd_ext(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int H,
                           int Sq, int Sk, int D, const uint8_t* mask, const int64_t* mstride,
                           float dropout_p, uint64_t seed, uint32_t offset, float scale, int causal,
-                          int dtype, const int64_t* rows, int64_t nrows, double* o, double* lse,
-                          int nthreads) {
+                          int64_t causal_diag, int dtype, const int64_t* rows, int64_t nrows, double* o,
+                          double* lse, int nthreads) {
     if (!q || !k || !v || !o || !lse || B < 0 || H < 0 || Sq < 0 || Sk < 0 || D <= 0) return 1;
     if (dtype != ORA_F16 && dtype != ORA_BF16) return 2;
     if (mask && !mstride) return 1;
@@ -619,7 +628,7 @@ int ora_attention_fwd_ext(const uint16_t* q, const uint16_t* k, const uint16_t* 
                     const int64_t b = bh / H, h = bh % H;
                     mrow = mask + b * mstride[0] + h * mstride[1] + i * mstride[2];
                 }
-                row_attention_ext(Qr, Kd, Vd, bh, i, Sq, Sk, D, sc, causal, mrow, t, seed, offset,
+                row_attention_ext(Qr, Kd, Vd, bh, i, causal_diag, Sk, D, sc, causal, mrow, t, seed, offset,
                                   Sr, o + r * D, lse + r);
             }
         }
@@ -647,8 +656,8 @@ int ora_attention_fwd_ext(const uint16_t* q, const uint16_t* k, const uint16_t* 
 int ora_attention_bwd_ext(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                           const uint16_t* dout, int B, int H, int Sq, int Sk, int D,
                           const uint8_t* mask, const int64_t* mstride, float dropout_p,
-                          uint64_t seed, uint32_t offset, float scale, int causal, int dtype,
-                          const int64_t* qrows, int64_t nq, const int64_t* krows, int64_t nk,
+                          uint64_t seed, uint32_t offset, float scale, int causal, int64_t causal_diag,
+                          int dtype, const int64_t* qrows, int64_t nq, const int64_t* krows, int64_t nk,
                           double* dq, double* dk, double* dv, int nthreads) {
     if (!q || !k || !v || !dout || B < 0 || H < 0 || Sq < 0 || Sk < 0 || D <= 0) return 1;
     if ((nq > 0 && (!qrows || !dq)) || (nk > 0 && (!krows || !dk || !dv))) return 1;
@@ -705,7 +714,7 @@ int ora_attention_bwd_ext(const uint16_t* q, const uint16_t* k, const uint16_t* 
             /* masked, undropped probabilities */
             double m = -INFINITY;
             for (int64_t j = 0; j < Sk; ++j) {
-                if (!visible(i, j, Sq, Sk, causal) || (mrow && mrow[j] == 0)) { Pr[j] = -INFINITY; continue; }
+                if (!visible(i, j, causal_diag, causal) || (mrow && mrow[j] == 0)) { Pr[j] = -INFINITY; continue; }
                 double a = 0.0;
                 for (int d = 0; d < D; ++d) a += Qr[d] * Kd[j * D + d];
                 Pr[j] = sc * a;

@@ -29,6 +29,13 @@ with the same boolean mask, by the identity-V case (O = P) against a second
 Philox written from its definition in this file, by the kept fraction, and
 by reducing to the plain forward (no mask, p = 0; all-true mask; triangular
 mask = causal flag) bit for bit.
+
+The causal diagonal at an arbitrary offset c (key j visible to query i iff
+j <= i + c) is pinned by a block decomposition: a causal sequence cut into
+query and key chunks, each block computed with c = (query chunk start) -
+(key chunk start) and the blocks merged by log-sum-exp, must give the full
+causal attention of the plain forward (which the pins above fix); and, in
+the forward and the backward, bit for bit by the equivalent explicit mask.
 """
 from decimal import Decimal, getcontext
 from fractions import Fraction
@@ -703,6 +710,57 @@ def pin_bwd_ext_rows_match_full(lib):
     assert np.max(np.abs(c - dv.reshape(-1, D)[kr])) <= 1e-13 * scl
 
 
+def pin_causal_offset_blocks(lib):
+    """A causal sequence of 90 tokens cut into chunks [0, 25), [25, 60),
+    [60, 90) for queries and keys: block (a, b) computed with the diagonal at
+    offset qs_a - ks_b (global position ks_b + j visible to qs_a + i iff
+    ks_b + j <= qs_a + i), then merged over b by log-sum-exp, equals the
+    one-shot causal forward on the whole sequence; blocks wholly in the
+    future give O = 0 and lse = -inf."""
+    S, D, dtype = 90, 16, "f16"
+    q, k, v = make_inputs(2, 2, S, D, dtype, seed=140)
+    scale = softmax_scale(D)
+    o, lse = _run(lib, q, k, v, scale, True, dtype)
+    cuts = ((0, 25), (25, 60), (60, 90))
+    for qa, qb in cuts:
+        parts = []
+        for ka, kb in cuts:
+            po, pl = _ext(lib, q[:, :, qa:qb].contiguous(), k[:, :, ka:kb].contiguous(),
+                          v[:, :, ka:kb].contiguous(), scale, True, dtype, causal_offset=qa - ka)
+            if ka > qb - 1:
+                assert np.all(po == 0.0) and np.all(np.isneginf(pl)), (qa, ka)
+            parts.append((po, pl))
+        lse_m = np.logaddexp.reduce(np.stack([p[1] for p in parts]), axis=0)
+        o_m = sum(np.where(np.isneginf(p[1]), 0.0, np.exp(p[1] - lse_m))[..., None] * p[0] for p in parts)
+        assert np.max(np.abs(lse_m - lse[:, :, qa:qb])) <= 1e-12, (qa, qb)
+        assert np.max(np.abs(o_m - o[:, :, qa:qb])) <= 1e-12, (qa, qb)
+
+
+def pin_causal_offset_as_mask(lib):
+    """The diagonal at offset c equals the explicit mask j <= i + c on a
+    non-causal call, bit for bit, in the forward (with dropout) and the
+    backward, for offsets that hide every key, some, the bottom-right and
+    top-left diagonals, and none."""
+    Sq, Sk, D, dtype = 21, 34, 16, "bf16"
+    q, k, v, g = _grad_inputs(1, 2, Sq, Sk, D, dtype, seed=150)
+    scale = softmax_scale(D)
+    kw = dict(dropout_p=0.25, seed=31, offset=4)
+    for c in (-Sq - 3, -5, 0, 4, Sk - Sq, Sk + 2):
+        tri = np.array([[1 if j <= i + c else 0 for j in range(Sk)] for i in range(Sq)], np.uint8)
+        ms = dict(mask=tri, mask_strides=(0, 0, Sk))
+        oc, lc = _ext(lib, q, k, v, scale, True, dtype, causal_offset=c, **kw)
+        om, lm = _ext(lib, q, k, v, scale, False, dtype, **ms, **kw)
+        assert np.array_equal(oc, om) and np.array_equal(lc, lm), c
+        a = _bwd_ext(lib, q, k, v, g, scale, True, dtype, causal_offset=c, **kw)
+        b = _bwd_ext(lib, q, k, v, g, scale, False, dtype, **ms, **kw)
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y), c
+    # the default is the bottom-right diagonal
+    oc, lc = _ext(lib, q, k, v, scale, True, dtype, causal_offset=Sk - Sq)
+    od, ld = _ext(lib, q, k, v, scale, True, dtype)
+    assert np.array_equal(oc, od) and np.array_equal(lc, ld)
+
+
 ALL_PINS = [pin_decode_f16, pin_decode_bf16, pin_q_zero, pin_causal_row0, pin_convexity,
             pin_bruteforce_decimal, pin_sdpa_fp64, pin_chunk_merge, pin_invariances,
             pin_rows_match_full, pin_unequal_causal_suffix, pin_bwd_autograd,
@@ -710,4 +768,5 @@ ALL_PINS = [pin_decode_f16, pin_decode_bf16, pin_q_zero, pin_causal_row0, pin_co
             pin_bwd_rows_match_full, pin_philox_kat, pin_dropout_threshold,
             pin_ext_plain_equals_forward, pin_ext_mask_sdpa, pin_ext_dropout_pattern,
             pin_ext_dropout_rate, pin_ext_rows_match_full, pin_bwd_ext_plain_equals_bwd,
-            pin_bwd_ext_autograd, pin_bwd_ext_finite_difference, pin_bwd_ext_rows_match_full]
+            pin_bwd_ext_autograd, pin_bwd_ext_finite_difference, pin_bwd_ext_rows_match_full,
+            pin_causal_offset_blocks, pin_causal_offset_as_mask]

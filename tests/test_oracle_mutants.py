@@ -17,10 +17,12 @@ MUTATIONS = [
     ("f16_subnormal_scale", "ldexp((double)frac, -24)", "ldexp((double)frac, -23)"),
     ("bf16_exponent_bias", "expo - 134);", "expo - 133);"),
     ("bf16_hidden_bit", "(double)(128 + frac)", "(double)(frac)"),
-    ("diagonal_excluded", "return j <= i + (Sk - Sq);", "return j < i + (Sk - Sq);"),
-    ("mask_polarity", "return j <= i + (Sk - Sq);", "return j >= i + (Sk - Sq);"),
-    ("causal_top_left", "return j <= i + (Sk - Sq);", "return j <= i;"),
-    ("causal_offset_sign", "return j <= i + (Sk - Sq);", "return j <= i + (Sq - Sk);"),
+    ("diagonal_excluded", "return j <= i + c;", "return j < i + c;"),
+    ("mask_polarity", "return j <= i + c;", "return j >= i + c;"),
+    ("causal_top_left", "if (!visible(i, j, Sk - Sq, causal)) { srow[j] = -INFINITY; continue; }",
+     "if (!visible(i, j, 0, causal)) { srow[j] = -INFINITY; continue; }"),
+    ("causal_offset_sign", "if (!visible(i, j, Sk - Sq, causal)) { srow[j] = -INFINITY; continue; }",
+     "if (!visible(i, j, Sq - Sk, causal)) { srow[j] = -INFINITY; continue; }"),
     ("dropped_feature", "for (int d = 0; d < D; ++d) acc += qrow[d] * kr[d];",
      "for (int d = 0; d < D - 1; ++d) acc += qrow[d] * kr[d];"),
     ("wrong_key_row", "const double* kr = K + j * D;", "const double* kr = K + ((j + 1) % Sk) * D;"),
@@ -95,16 +97,20 @@ MUTATIONS = [
     ("bwdx_dp_keep_missing", "                dPr[j] = Zr[j] * a;", "                dPr[j] = a;"),
     ("bwdx_keep_scale_missing", "const double keep_scale = 65536.0 / (double)(65536 - t);",
      "const double keep_scale = 1.0;"),
-    ("bwdx_mask_ignored", "if (!visible(i, j, Sq, Sk, causal) || (mrow && mrow[j] == 0)) { Pr[j] = -INFINITY; continue; }",
-     "if (!visible(i, j, Sq, Sk, causal)) { Pr[j] = -INFINITY; continue; }"),
+    ("bwdx_mask_ignored", "if (!visible(i, j, causal_diag, causal) || (mrow && mrow[j] == 0)) { Pr[j] = -INFINITY; continue; }",
+     "if (!visible(i, j, causal_diag, causal)) { Pr[j] = -INFINITY; continue; }"),
+    ("bwdx_offset_sign", "if (!visible(i, j, causal_diag, causal) ||", "if (!visible(i, j, -causal_diag, causal) ||"),
+    ("bwdx_offset_ignored", "if (!visible(i, j, causal_diag, causal) ||", "if (!visible(i, j, Sk - Sq, causal) ||"),
     ("bwdx_rowdot_undropped", "                rowdot += Pr[j] * dPr[j];", "                rowdot += Pr[j] * a;"),
     ("bwdx_ds_sign", "const double ds = Pr[j] * (dPr[j] - rowdot);\n                    for (int d = 0; d < D; ++d) gq[d] += ds * Kd[j * D + d];",
      "const double ds = Pr[j] * (rowdot - dPr[j]);\n                    for (int d = 0; d < D; ++d) gq[d] += ds * Kd[j * D + d];"),
     ("bwdx_dk_uses_dout", "                    ak[d] += ds * Qr[d];", "                    ak[d] += ds * Gr[d];"),
     ("bwdx_dk_scale_missing", "dk[r * D + d] = sc * dk[r * D + d];", "dk[r * D + d] = dk[r * D + d];"),
     ("bwdx_wrong_key", "const int64_t j = krows[r] - bh * Sk;", "const int64_t j = (krows[r] - bh * Sk + 1) % Sk;"),
-    ("ext_causal_ignored", "const int vis = visible(i, j, Sq, Sk, causal) && (!mrow || mrow[j] != 0);",
+    ("ext_causal_ignored", "const int vis = visible(i, j, c, causal) && (!mrow || mrow[j] != 0);",
      "const int vis = (!mrow || mrow[j] != 0);"),
+    ("ext_offset_off_by_one", "const int vis = visible(i, j, c, causal) &&", "const int vis = visible(i, j, c + 1, causal) &&"),
+    ("ext_offset_ignored", "row_attention_ext(Qr, Kd, Vd, bh, i, causal_diag, Sk,", "row_attention_ext(Qr, Kd, Vd, bh, i, Sk - Sq, Sk,"),
 ]
 
 
