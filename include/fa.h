@@ -329,6 +329,29 @@ int fa_fwd_ext_strided(const void* q, const void* k, const void* v, void* o, flo
                        float scale, int causal, int dtype, void* stream);
 
 /*
+ * fa_fwd_causal_offset -- fa_fwd_ext_strided under the causal rule with the
+ * diagonal at an explicit offset: key j is visible to query i iff
+ * j <= i + causal_offset (and the mask keeps it, when there is one).
+ * Sequence parallelism ("FlashAttention-2 on Ascend NPU" (2048ai.net),
+ * section 6.4: each device works on its own chunk of the sequence) splits a
+ * causal sequence into chunks; the block of queries from global position
+ * qs against keys from ks is this call with causal_offset = qs - ks, and the
+ * blocks' (o, lse) merge by lse = log(sum_b exp(lse_b)),
+ * o = sum_b exp(lse_b - lse) o_b.  causal_offset = Sk - Sq is fa_fwd_ext's
+ * causal rule (the calls agree bit for bit); 0 aligns the diagonal with the
+ * first query and key (top-left).  Offsets at or below -Sq hide every key
+ * (every row gets o = 0, lse = -inf) and offsets at or above Sk show every
+ * key; the offset is clamped to [-Sq, Sk].  Everything else (arguments,
+ * layouts, dropout counter, limits, errors) as for fa_fwd_ext_strided with
+ * causal = 1.
+ */
+int fa_fwd_causal_offset(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int H, int Sq, int Sk, int D, const int64_t* strides,
+                         const uint8_t* mask, const int64_t* mask_strides,
+                         float dropout_p, uint64_t seed, uint32_t offset,
+                         float scale, int64_t causal_offset, int dtype, void* stream);
+
+/*
  * fa_bwd -- gradients of the attention forward above: given dout = dL/dO,
  * writes dq = dL/dq, dk = dL/dk and dv = dL/dv.  The scores and
  * probabilities are recomputed from q, k and the forward's lse rather than
@@ -445,6 +468,21 @@ int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, c
                    const int64_t* strides, const uint8_t* mask, const int64_t* mask_strides,
                    float dropout_p, uint64_t seed, uint32_t offset, float scale, int causal, int dtype,
                    int deterministic, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * fa_bwd_causal_offset -- gradients of fa_fwd_causal_offset: fa_bwd_strided
+ * under the causal rule with the diagonal at causal_offset (key j visible
+ * to query i iff j <= i + causal_offset, clamped to [-Sq, Sk]): the
+ * gradients of sum(o * dout) for the o of fa_fwd_causal_offset on the same
+ * inputs, offset, mask and dropout arguments, whose o and lse are passed
+ * in.  Everything else as for fa_bwd_strided.
+ */
+int fa_bwd_causal_offset(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                         const float* lse, void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk,
+                         int D, const int64_t* strides, const uint8_t* mask, const int64_t* mask_strides,
+                         float dropout_p, uint64_t seed, uint32_t offset, float scale,
+                         int64_t causal_offset, int dtype, void* workspace, int64_t workspace_bytes,
+                         void* stream);
 
 /* Bytes of workspace fa_bwd, fa_bwd_ext and fa_bwd_strided need (0 for an
  * invalid shape): the row dot products D_i, B*H*Sq fp32, rounded up to 256

@@ -214,6 +214,17 @@ static void bwd_checks() {
     }
     CHECK_EQ(fa_bwd_strided(q, k, v, o, g, lse, dq, dk, dv, B, H, Sq, Sk, D, st, nullptr, nullptr, 0.0f, 0, 0, sc,
                             1, FA_BF16, 1, ws, wd, nullptr), FA_OK);
+    CHECK_EQ(g_stub.diag, Sk - Sq);
+    // the causal diagonal at an explicit offset, clamped to [-Sq, Sk]
+    const int64_t offs[4] = {-3, INT64_MIN, INT64_MAX, 0};
+    const int want[4] = {-3, -Sq, Sk, 0};
+    for (int i = 0; i < 4; ++i) {
+        g_stub.last = StubState::kNone;
+        CHECK_EQ(fa_bwd_causal_offset(q, k, v, o, g, lse, dq, dk, dv, B, H, Sq, Sk, D, st, nullptr, nullptr, 0.0f,
+                                      0, 0, sc, offs[i], FA_BF16, ws, wd, nullptr), FA_OK);
+        CHECK_EQ(g_stub.last, StubState::kBwd);
+        CHECK_EQ(g_stub.diag, want[i]);
+    }
     st[3 * 6 + 2] = 8;   // dk rows overlapping
     CHECK_EQ(fa_bwd_strided(q, k, v, o, g, lse, dq, dk, dv, B, H, Sq, Sk, D, st, nullptr, nullptr, 0.0f, 0, 0, sc,
                             1, FA_BF16, 1, ws, wd, nullptr), FA_ERR_STRIDE);
@@ -257,6 +268,24 @@ static void ext_checks() {
                                     FA_F16, nullptr), FA_OK);
         CHECK_EQ(g_stub.last, StubState::kExt);
         CHECK_EQ(g_stub.drop_t, 6554);
+    }
+    // the causal diagonal: bottom-right by default, an explicit offset clamped to [-Sq, Sk]
+    {
+        const int64_t st[12] = {4 * 256 * 128, 256 * 128, 128, 4 * 300 * 128, 300 * 128, 128,
+                                4 * 300 * 128, 300 * 128, 128, 4 * 256 * 128, 256 * 128, 128};
+        CHECK_EQ(fa_fwd_ext_strided(q, k, v, o, lse, 1, 4, 256, 300, 128, st, nullptr, nullptr, 0.0f, 1, 0, sc, 1,
+                                    FA_F16, nullptr), FA_OK);
+        CHECK_EQ(g_stub.diag, 300 - 256);
+        const int64_t offs[6] = {0, -17, 299, INT64_MIN, INT64_MAX, -256};
+        const int want[6] = {0, -17, 299, -256, 300, -256};
+        for (int i = 0; i < 6; ++i) {
+            CHECK_EQ(fa_fwd_causal_offset(q, k, v, o, lse, 1, 4, 256, 300, 128, st, nullptr, nullptr, 0.1f, 1, 0,
+                                          sc, offs[i], FA_F16, nullptr), FA_OK);
+            CHECK_EQ(g_stub.last, StubState::kFwdDrop);
+            CHECK_EQ(g_stub.diag, want[i]);
+        }
+        CHECK_EQ(fa_fwd_causal_offset(q, k, v, o, lse, 1, 4, 256, 300, 128, nullptr, nullptr, nullptr, 0.0f, 1, 0,
+                                      sc, 5, FA_F16, nullptr), FA_ERR_NULL);
     }
     // a dropout probability that rounds to 65536 is refused
     CHECK_EQ(fa_fwd_ext(q, k, v, o, lse, 1, 4, 256, 300, 128, nullptr, nullptr, 0.99999994f, 1, 0, sc, 1, FA_F16,

@@ -41,6 +41,7 @@ hipError_t launch_fwd(const FwdParams& p, int D, int dtype, bool causal, int64_t
     g_stub.causal = causal;
     g_stub.masked = p.mask != nullptr;
     g_stub.drop_t = p.drop_t;
+    g_stub.diag = p.diag;
     return hipSuccess;
 }
 hipError_t launch_fwd_drop(const FwdParams& p, int D, int dtype, bool causal, int64_t grid, bool split,
@@ -61,6 +62,7 @@ namespace bwd {
 hipError_t launch_bwd(const BwdParams& p, int D, int, int, hipStream_t) {
     g_stub.last = StubState::kBwd;
     g_stub.D = D;
+    g_stub.diag = p.diag;
     g_stub.nqb = p.nqb;
     return hipSuccess;
 }
@@ -69,6 +71,7 @@ namespace ext {
 hipError_t launch_ext(const ExtParams& p, int D, int, int, hipStream_t) {
     g_stub.last = StubState::kExt;
     g_stub.D = D;
+    g_stub.diag = p.diag;
     g_stub.nqb = p.nqb;
     g_stub.drop_t = p.drop_t;
     return hipSuccess;

@@ -13,6 +13,7 @@ struct StubState {
     bool causal = false;
     bool masked = false;
     uint32_t drop_t = 0;
+    int diag = 0;
     int device_cus = 0;          // 0: no device answers (compute units fall back to 256)
     int device_queries = 0;
     int attribute_queries = 0;

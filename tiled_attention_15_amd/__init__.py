@@ -86,6 +86,12 @@ def _load():
     lib.fa_fwd_ext_strided.argtypes = [vp] * 5 + [i] * 5 + [i64p, vp, i64p, f, ctypes.c_uint64, ctypes.c_uint32, f,
                                                              i, i, vp]
     lib.fa_fwd_ext_strided.restype = i
+    lib.fa_fwd_causal_offset.argtypes = [vp] * 5 + [i] * 5 + [i64p, vp, i64p, f, ctypes.c_uint64, ctypes.c_uint32,
+                                                               f, ctypes.c_int64, i, vp]
+    lib.fa_fwd_causal_offset.restype = i
+    lib.fa_bwd_causal_offset.argtypes = [vp] * 9 + [i] * 5 + [i64p, vp, i64p, f, ctypes.c_uint64, ctypes.c_uint32,
+                                                               f, ctypes.c_int64, i, vp, ctypes.c_int64, vp]
+    lib.fa_bwd_causal_offset.restype = i
     lib.fa_fwd_diag.argtypes = [vp] * 7 + [i] * 5 + [f, i, i, i, vp]
     lib.fa_fwd_diag.restype = i
     lib.fa_fwd_diag_tile_slots.argtypes = [i] * 5
@@ -265,6 +271,38 @@ def fa_bwd_strided(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, strides, 
                                   int(workspace_bytes), _stream(stream))
 
 
+def fa_fwd_causal_offset(q, k, v, o, lse, B, H, Sq, Sk, D, strides, mask, mask_strides, dropout_p, seed, offset,
+                         scale, causal_offset, dtype, stream):
+    """C ABI fa_fwd_causal_offset: fa_fwd_ext_strided under the causal rule
+    with key j visible to query i iff j <= i + causal_offset."""
+    st = [int(x) for x in strides]
+    if len(st) != 12:
+        raise ValueError("fa: fa_fwd_causal_offset takes 12 strides")
+    ms = None if mask_strides is None else _strides3(mask_strides)
+    return _load().fa_fwd_causal_offset(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(Sq),
+                                        int(Sk), int(D), (ctypes.c_int64 * 12)(*st), _ptr(mask), ms,
+                                        ctypes.c_float(dropout_p), ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF),
+                                        ctypes.c_uint32(int(offset) & 0xFFFFFFFF), ctypes.c_float(scale),
+                                        ctypes.c_int64(int(causal_offset)), int(dtype), _stream(stream))
+
+
+def fa_bwd_causal_offset(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, strides, mask, mask_strides,
+                         dropout_p, seed, offset, scale, causal_offset, dtype, workspace, workspace_bytes, stream):
+    """C ABI fa_bwd_causal_offset: gradients of fa_fwd_causal_offset (24
+    strides as for fa_bwd_strided)."""
+    st = [int(x) for x in strides]
+    if len(st) != 24:
+        raise ValueError("fa: fa_bwd_causal_offset takes 24 strides")
+    ms = None if mask_strides is None else _strides3(mask_strides)
+    return _load().fa_bwd_causal_offset(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                                        _ptr(dk), _ptr(dv), int(B), int(H), int(Sq), int(Sk), int(D),
+                                        (ctypes.c_int64 * 24)(*st), _ptr(mask), ms, ctypes.c_float(dropout_p),
+                                        ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF),
+                                        ctypes.c_uint32(int(offset) & 0xFFFFFFFF), ctypes.c_float(scale),
+                                        ctypes.c_int64(int(causal_offset)), int(dtype), _ptr(workspace),
+                                        int(workspace_bytes), _stream(stream))
+
+
 def fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, scale, causal, dtype, stream):
     """C ABI fa_bwd_noalloc: the backward with the library's fixed
     scratch array as its workspace (no allocation)."""
@@ -387,8 +425,10 @@ def naive_forward(q, k, v, causal=False, scale=None, workspace=None):
 
 
 def _bwd_call(q, k, v, o, lse, dout, causal, scale, mask, dropout_p, seed, offset, deterministic, workspace,
-              grads):
+              grads, causal_offset=None):
     import torch
+    if causal_offset is not None and not causal:
+        raise ValueError("fa: causal_offset places the causal diagonal; it needs causal=True")
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
         raise ValueError("fa: q/o/dout [B, H, Sq, D] and k/v [B, H, Sk, D] expected")
     if q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
@@ -423,6 +463,13 @@ def _bwd_call(q, k, v, o, lse, dout, causal, scale, mask, dropout_p, seed, offse
     strides = [s for t in ts + (dq, dk, dv) for s in t.stride()[:3]]
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream().cuda_stream
+    if causal_offset is not None:
+        st = fa_bwd_causal_offset(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, strides, mask, mstrides,
+                                  dropout_p, seed, offset, scale, causal_offset, _dtype_code(q), workspace,
+                                  workspace.numel() * workspace.element_size(), stream)
+        if st != 0:
+            raise FaError(st, "fa_bwd_causal_offset")
+        return dq, dk, dv
     st = fa_bwd_strided(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, strides, mask, mstrides, dropout_p,
                         seed, offset, scale, causal, _dtype_code(q), deterministic, workspace,
                         workspace.numel() * workspace.element_size(), stream)
@@ -475,14 +522,21 @@ def _mask_arg(mask, q, B, H, Sq, Sk):
     return m, (m.stride(0), m.stride(1), m.stride(2))
 
 
-def forward_ext(q, k, v, causal=False, scale=None, mask=None, dropout_p=0.0, seed=0, offset=0, out=None):
+def forward_ext(q, k, v, causal=False, scale=None, mask=None, dropout_p=0.0, seed=0, offset=0, out=None,
+                causal_offset=None):
     """Forward with an explicit boolean mask and/or dropout on GPU tensors
     q [B, H, Sq, D] and k, v [B, H, Sk, D] with any strides whose last
     dimension is contiguous.  mask: a uint8 or bool GPU tensor broadcastable
     to [B, H, Sq, Sk] (nonzero keeps); rows that do not start on 4-byte
-    boundaries are copied to an aligned buffer.  Returns (o, lse): o
-    contiguous (or `out`, which may be strided) and lse float32 [B, H, Sq]."""
+    boundaries are copied to an aligned buffer.  causal_offset (with
+    causal=True): key j visible to query i iff j <= i + causal_offset (None:
+    Sk - Sq, the bottom-right diagonal; 0: top-left; a block of a split
+    sequence, queries from position qs and keys from ks: qs - ks).  Returns
+    (o, lse): o contiguous (or `out`, which may be strided) and lse float32
+    [B, H, Sq]."""
     import torch
+    if causal_offset is not None and not causal:
+        raise ValueError("fa: causal_offset places the causal diagonal; it needs causal=True")
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
         raise ValueError("fa: q [B, H, Sq, D] and k, v [B, H, Sk, D] expected")
     if q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
@@ -506,6 +560,12 @@ def forward_ext(q, k, v, causal=False, scale=None, mask=None, dropout_p=0.0, see
     strides = [s for t in (q, k, v, o) for s in t.stride()[:3]]
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream().cuda_stream
+    if causal_offset is not None:
+        st = fa_fwd_causal_offset(q, k, v, o, lse, B, H, Sq, Sk, D, strides, mask, mstrides, dropout_p, seed,
+                                  offset, scale, causal_offset, _dtype_code(q), stream)
+        if st != 0:
+            raise FaError(st, "fa_fwd_causal_offset")
+        return o, lse
     st = fa_fwd_ext_strided(q, k, v, o, lse, B, H, Sq, Sk, D, strides, mask, mstrides, dropout_p, seed, offset,
                             scale, causal, _dtype_code(q), stream)
     if st != 0:
@@ -514,8 +574,9 @@ def forward_ext(q, k, v, causal=False, scale=None, mask=None, dropout_p=0.0, see
 
 
 def backward_ext(q, k, v, o, lse, dout, causal=False, scale=None, mask=None, dropout_p=0.0, seed=0, offset=0,
-                 workspace=None, grads=None):
+                 workspace=None, grads=None, causal_offset=None):
     """Gradients (dq, dk, dv) of forward_ext with the same mask, dropout_p,
-    seed and offset (o and lse from that call); strides as for backward().
-    Bitwise reproducible like backward()."""
-    return _bwd_call(q, k, v, o, lse, dout, causal, scale, mask, dropout_p, seed, offset, True, workspace, grads)
+    seed, offset and causal_offset (o and lse from that call); strides as
+    for backward().  Bitwise reproducible like backward()."""
+    return _bwd_call(q, k, v, o, lse, dout, causal, scale, mask, dropout_p, seed, offset, True, workspace, grads,
+                     causal_offset)

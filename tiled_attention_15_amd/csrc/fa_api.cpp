@@ -46,7 +46,7 @@ int compute_units() {
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 5 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 6 * 100 + 0;
 
 int validate_shape(int B, int H, int Sq, int Sk, int D, int dtype) {
     if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return FA_ERR_SHAPE;
@@ -62,6 +62,15 @@ int validate_shape(int B, int H, int Sq, int Sk, int D, int dtype) {
     const int64_t grid = (int64_t)B * H * ((Sq + fa::kBlockQ - 1) / fa::kBlockQ);
     if (grid >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
     return FA_OK;
+}
+
+// Causal diagonal of the kernels: key j visible to query i iff j <= i + diag.
+// Without an explicit offset it is bottom-right (Sk - Sq); an explicit one
+// is clamped to [-Sq, Sk], where it already hides every key from every row
+// or shows every key to every row, so that i + diag stays in int range.
+int diag_of(int Sq, int Sk, const int64_t* causal_offset) {
+    if (causal_offset == nullptr) return Sk - Sq;
+    return (int)std::min<int64_t>(std::max<int64_t>(*causal_offset, -(int64_t)Sq), (int64_t)Sk);
 }
 
 // The key-split instances of the tuned kernel (D = 64 or 128, with or
@@ -151,7 +160,8 @@ static int launch_tuned(const void* q, const void* k, const void* v, void* o, fl
                         int Sk, int D, const int64_t* q_strides, const int64_t* k_strides,
                         const int64_t* v_strides, const int64_t* o_strides, const uint8_t* mask,
                         const int64_t* mask_strides, float scale, int causal, int dtype, void* stream,
-                        const DiagArgs* diag = nullptr, DropArgs drop = DropArgs()) {
+                        const DiagArgs* diag = nullptr, DropArgs drop = DropArgs(),
+                        const int64_t* causal_offset = nullptr) {
     fa::FwdParams p = {};
     p.q = q;
     p.k = k;
@@ -167,6 +177,7 @@ static int launch_tuned(const void* q, const void* k, const void* v, void* o, fl
     // head-dimension split: both wave groups on the same rows)
     const int br = (split || D == 256) ? fa::kBlockQSplit : fa::kBlockQ;
     p.nqb = (Sq + br - 1) / br;
+    p.diag = diag_of(Sq, Sk, causal_offset);
     p.scale_log2e = (float)((double)scale * 1.4426950408889634074);
     p.q_sb = q_strides[0], p.q_sh = q_strides[1], p.q_ss = (int)q_strides[2];
     p.k_sb = k_strides[0], p.k_sh = k_strides[1], p.k_ss = (int)k_strides[2];
@@ -438,7 +449,7 @@ bool bwd_span_ok(int S, int64_t row_stride, int D) {
 static int ext_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Sq,
                       int Sk, int D, const int64_t* strides, const uint8_t* mask, const int64_t* mask_strides,
                       float dropout_p, uint64_t seed, uint32_t offset, float scale, int causal, int dtype,
-                      void* stream) {
+                      void* stream, const int64_t* causal_offset) {
     if (!q || !k || !v || !o || !strides) return FA_ERR_NULL;
     int st = validate_shape(B, H, Sq, Sk, D, dtype);
     if (st != FA_OK) return st;
@@ -489,7 +500,7 @@ static int ext_common(const void* q, const void* k, const void* v, void* o, floa
         drop.seed = seed;
         drop.offset = offset;
         return launch_tuned(q, k, v, o, lse, B, H, Sq, Sk, D, strides, strides + 3, strides + 6, strides + 9, mask,
-                            mask_strides, scale, causal, dtype, stream, nullptr, drop);
+                            mask_strides, scale, causal, dtype, stream, nullptr, drop, causal_offset);
     }
 
     fa::ext::ExtParams p = {};
@@ -511,6 +522,7 @@ static int ext_common(const void* q, const void* k, const void* v, void* o, floa
     p.H = H;
     p.BH = B * H;
     p.nqb = (Sq + fa::ext::kQueryBlock - 1) / fa::ext::kQueryBlock;
+    p.diag = diag_of(Sq, Sk, causal_offset);
     p.scale_log2e = (float)((double)scale * 1.4426950408889634074);
     p.drop_t = (uint32_t)t;
     p.keep_scale = (float)(65536.0 / (65536.0 - (double)t));
@@ -530,7 +542,7 @@ int fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
     const int64_t st[12] = {(int64_t)H * Sq * D, (int64_t)Sq * D, D, (int64_t)H * Sk * D, (int64_t)Sk * D, D,
                             (int64_t)H * Sk * D, (int64_t)Sk * D, D, (int64_t)H * Sq * D, (int64_t)Sq * D, D};
     return ext_common(q, k, v, o, lse, B, H, Sq, Sk, D, st, mask, mask_strides, dropout_p, seed, offset, scale,
-                      causal, dtype, stream);
+                      causal, dtype, stream, nullptr);
 }
 
 int fa_fwd_ext_strided(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -538,7 +550,15 @@ int fa_fwd_ext_strided(const void* q, const void* k, const void* v, void* o, flo
                        const int64_t* mask_strides, float dropout_p, uint64_t seed, uint32_t offset,
                        float scale, int causal, int dtype, void* stream) {
     return ext_common(q, k, v, o, lse, B, H, Sq, Sk, D, strides, mask, mask_strides, dropout_p, seed, offset,
-                      scale, causal, dtype, stream);
+                      scale, causal, dtype, stream, nullptr);
+}
+
+int fa_fwd_causal_offset(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                         int Sq, int Sk, int D, const int64_t* strides, const uint8_t* mask,
+                         const int64_t* mask_strides, float dropout_p, uint64_t seed, uint32_t offset,
+                         float scale, int64_t causal_offset, int dtype, void* stream) {
+    return ext_common(q, k, v, o, lse, B, H, Sq, Sk, D, strides, mask, mask_strides, dropout_p, seed, offset,
+                      scale, 1, dtype, stream, &causal_offset);
 }
 
 int64_t fa_bwd_workspace_bytes(int B, int H, int Sq, int D, int deterministic) {
@@ -553,7 +573,7 @@ static int bwd_common(const void* q, const void* k, const void* v, const void* o
                       const float* lse, void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk, int D,
                       const int64_t* strides, const uint8_t* mask, const int64_t* mask_strides,
                       float dropout_p, uint64_t seed, uint32_t offset, float scale, int causal, int dtype,
-                      void* workspace, int64_t workspace_bytes, void* stream) {
+                      void* workspace, int64_t workspace_bytes, void* stream, const int64_t* causal_offset) {
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace || !strides) return FA_ERR_NULL;
     int st = validate_shape(B, H, Sq, Sk, D, dtype);
     if (st != FA_OK) return st;
@@ -619,6 +639,7 @@ static int bwd_common(const void* q, const void* k, const void* v, const void* o
     p.Sq = Sq;
     p.Sk = Sk;
     p.BH = B * H;
+    p.diag = diag_of(Sq, Sk, causal_offset);
     p.nkb = (Sk + fa::bwd::kKeyBlock - 1) / fa::bwd::kKeyBlock;
     p.nqb = (Sq + fa::bwd::kQueryBlock - 1) / fa::bwd::kQueryBlock;
     p.scale = scale;
@@ -658,7 +679,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     int64_t st[24];
     contiguous_bwd_strides(H, Sq, Sk, D, st);
     return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, st, nullptr, nullptr, 0.0f, 0, 0,
-                      scale, causal, dtype, workspace, workspace_bytes, stream);
+                      scale, causal, dtype, workspace, workspace_bytes, stream, nullptr);
 }
 
 int fa_bwd_ext(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -671,7 +692,7 @@ int fa_bwd_ext(const void* q, const void* k, const void* v, const void* o, const
     int64_t st[24];
     contiguous_bwd_strides(H, Sq, Sk, D, st);
     return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, st, mask, mask_strides, dropout_p,
-                      seed, offset, scale, causal, dtype, workspace, workspace_bytes, stream);
+                      seed, offset, scale, causal, dtype, workspace, workspace_bytes, stream, nullptr);
 }
 
 int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -681,7 +702,16 @@ int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, c
                    int deterministic, void* workspace, int64_t workspace_bytes, void* stream) {
     (void)deterministic;   // every backward is deterministic
     return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, strides, mask, mask_strides,
-                      dropout_p, seed, offset, scale, causal, dtype, workspace, workspace_bytes, stream);
+                      dropout_p, seed, offset, scale, causal, dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
+int fa_bwd_causal_offset(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                         const float* lse, void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk, int D,
+                         const int64_t* strides, const uint8_t* mask, const int64_t* mask_strides,
+                         float dropout_p, uint64_t seed, uint32_t offset, float scale, int64_t causal_offset,
+                         int dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+    return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, Sq, Sk, D, strides, mask, mask_strides,
+                      dropout_p, seed, offset, scale, 1, dtype, workspace, workspace_bytes, stream, &causal_offset);
 }
 
 }  // extern "C"

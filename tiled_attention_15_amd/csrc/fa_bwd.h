@@ -32,6 +32,7 @@ struct BwdParams {
     uint32_t seed_lo, seed_hi, offset;
     int H;
     int Sq, Sk, BH;
+    int diag;           // causal: key j visible to query i iff j <= i + diag (in [-Sq, Sk])
     int nkb;            // key blocks of the dK/dV kernel per head
     int nqb;            // query blocks of the dQ kernel per head
     float scale;        // softmax scale

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256, (MASK || DROP || D > 128) ? 1 : 2) void bwd_dk
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     int bh, kb;
     block_order(blockIdx.x, p.nkb, p.BH, false, bh, kb);
-    const int Sq = p.Sq, Sk = p.Sk, diag = Sk - Sq;
+    const int Sq = p.Sq, Sk = p.Sk, diag = p.diag;   // causal: key j visible to query i iff j <= i + diag
     const int k0 = kb * kKeyBlock, kw0 = k0 + 32 * w;
 
     const i32x4 rq = rsrc_words(head_of(p.q, p.Lq, bh, p.H), head_bytes<D>(p.Lq, Sq));
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_dq(BwdParams p) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     int bh, qb;
     block_order(blockIdx.x, p.nqb, p.BH, CAUSAL, bh, qb);
-    const int Sq = p.Sq, Sk = p.Sk, diag = Sk - Sq;
+    const int Sq = p.Sq, Sk = p.Sk, diag = p.diag;   // causal: key j visible to query i iff j <= i + diag
     const int q0 = qb * kQueryBlock, qw0 = q0 + 32 * w;
     const int qi = qw0 + lq;
 

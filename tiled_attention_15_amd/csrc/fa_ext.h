@@ -18,6 +18,7 @@ struct ExtParams {
     const uint8_t* mask;    // nonzero = keep; null = no mask
     int64_t m_sb, m_sh, m_ss;  // mask strides in bytes (batch, head, row); multiples of 4
     int Sq, Sk, H, BH, nqb;
+    int diag;               // causal: key j visible to query i iff j <= i + diag (in [-Sq, Sk])
     float scale_log2e;
     uint32_t drop_t;        // keep iff the 16-bit draw >= drop_t (0 = no dropout)
     float keep_scale;       // 65536 / (65536 - drop_t)

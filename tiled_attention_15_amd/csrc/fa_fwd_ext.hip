@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void fwd_ext(ExtParams p) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     int bh, qb;
     block_order(blockIdx.x, p.nqb, p.BH, CAUSAL, bh, qb);
-    const int Sq = p.Sq, Sk = p.Sk, diag = Sk - Sq;
+    const int Sq = p.Sq, Sk = p.Sk, diag = p.diag;   // causal: key j visible to query i iff j <= i + diag
     const int q0 = qb * kQueryBlock, qw0 = q0 + 32 * w;
     const int qi = qw0 + lq;
 

@@ -295,9 +295,10 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
                                                                      : (int)blockIdx.x;
     schedule(wg_id, p.nqb, p.BH, CAUSAL, bh, qb);
     const int Sq = p.Sq, Sk = p.Sk;
-    // Causal diagonal: key j is visible to query i iff j <= i + diag (the
-    // last query row sees the last key).
-    const int diag = Sk - Sq;
+    // Causal diagonal: key j is visible to query i iff j <= i + diag
+    // (Sk - Sq unless the caller placed it elsewhere: the last query row then
+    // sees the last key).
+    const int diag = p.diag;
     const int q0 = qb * BR;
     const int qw0 = q0 + ((SPLIT || DSPLIT) ? (wid & 3) : wid) * 32;   // split: both groups share the rows
     const int dob = DSPLIT ? grp * DO : 0;                             // first O block of this wave

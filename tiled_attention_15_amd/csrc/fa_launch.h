@@ -20,6 +20,7 @@ struct FwdParams {
     int H;             // heads (bh = b * H + h)
     int BH;            // batch * heads
     int nqb;           // query blocks per head: ceil(Sq / kBlockQ)
+    int diag;          // causal instances: key j visible to query i iff j <= i + diag (in [-Sq, Sk])
     float scale_log2e; // scale * log2(e), fp32
     // Element strides of batch, head and row (the head dimension is contiguous).
     int64_t q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;
