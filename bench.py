@@ -93,6 +93,25 @@ def warm_up(step, launches, seconds):
     return launches + n
 
 
+def timed_steps(step, steps, stream):
+    """Mean milliseconds per call over `steps` back-to-back calls of step()
+    (after its warm-up), timed with HIP events on `stream`.  One untimed call
+    is queued first, so that the GPU is busy while the start event is
+    recorded and the timed calls are enqueued: otherwise the host's time
+    between the start event and the first launch lands in the timed region
+    (about a millisecond after the warm-up's final synchronisation)."""
+    import torch
+    step()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps
+
+
 def gpu_leg(w, steps, warmup, cold=0, warmup_s=1.0):
     """Times `steps` back-to-back launches (the headline figure) after a
     warm-up of at least `warmup` launches and `warmup_s` seconds, with the
@@ -193,14 +212,7 @@ def naive_leg(w, steps, warmup):
             raise fa.FaError(st, "fa_naive_fwd")
 
     warm_up(step, warmup, 0.2)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / steps
+    ms = timed_steps(step, steps, stream)
     del ws
     return {"ms_per_step": round(ms, 4), "value": round(w.flops() / (ms * 1e-3) / 1e12, 3),
             "unit": "TFLOP/s", "workspace_bytes": int(need), "steps": steps,
@@ -239,14 +251,7 @@ def backward_leg(w, steps, warmup):
             raise fa.FaError(st, "fa_bwd")
 
     warm_up(step, warmup, 0.2)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / steps
+    ms = timed_steps(step, steps, stream)
     if not (torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()):
         raise RuntimeError("non-finite gradient in the benchmark run")
     tf = flops / (ms * 1e-3) / 1e12
@@ -279,14 +284,7 @@ def backward_leg(w, steps, warmup):
             raise fa.FaError(st, "fa_bwd_ext")
 
     warm_up(step_x, warmup, 0.2)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(steps):
-        step_x()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms_x = ev0.elapsed_time(ev1) / steps
+    ms_x = timed_steps(step_x, steps, stream)
     tf = flops / (ms_x * 1e-3) / 1e12
     out["mask_dropout"] = {"ms_per_step": round(ms_x, 4), "value": round(tf, 3),
                            "frac_of_mfma_peak": round(tf / MFMA_PEAK_TFLOPS, 4),
@@ -328,14 +326,7 @@ def ext_leg(w, steps, warmup):
                 raise fa.FaError(st, "fa_fwd_ext")
 
         warm_up(step, warmup, 0.2)
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
-        for _ in range(steps):
-            step()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        ms_step = ev0.elapsed_time(ev1) / steps
+        ms_step = timed_steps(step, steps, stream)
         tf = w.flops() / (ms_step * 1e-3) / 1e12
         out[name] = {"ms_per_step": round(ms_step, 4), "value": round(tf, 3),
                      "frac_of_mfma_peak": round(tf / MFMA_PEAK_TFLOPS, 4)}
@@ -529,14 +520,14 @@ def main():
         "cpu_baseline": None,
     }
     if not a.no_naive:
-        nv = naive_leg(w, max(2, min(20, a.steps // 10)), 2)
+        nv = naive_leg(w, max(10, min(20, a.steps)), 2)
         if nv is not None:
             nv["fused_speedup"] = round(nv["ms_per_step"] / ms, 2)
         out["naive_unfused"] = nv
     if not a.no_backward:
-        out["backward"] = backward_leg(w, max(2, min(20, a.steps // 10)), 2)
+        out["backward"] = backward_leg(w, max(10, min(20, a.steps)), 2)
     if not a.no_ext:
-        out["mask_dropout"] = ext_leg(w, max(2, min(20, a.steps // 10)), 2)
+        out["mask_dropout"] = ext_leg(w, max(10, min(20, a.steps)), 2)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_leg(w, a.cpu_seconds)
         # the oracle timed beside the backward and the masked/dropout forward too
