@@ -266,8 +266,10 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
     static_assert(!DIAG || (!MASK && !DROP && D != 256), "diagnostic instances: no mask or dropout, D <= 128");
     constexpr int NW = 8;
     constexpr int NT = 512;
-    // D = 256: the two wave groups share 128 query rows and split the head
-    // dimension (each wave holds half of O and computes the full scores).
+    // D = 256: waves w and w ^ 1 of one group share 32 query rows; each
+    // computes the scores and probabilities of its own 32 keys of a tile and
+    // holds half of O's columns (the pair exchanges row maxima and packed
+    // probabilities through LDS).
     constexpr bool DSPLIT = D == 256;
     static_assert(!DSPLIT || !SPLIT, "D = 256 is split by head dimension, not by keys");
     constexpr int BR = (SPLIT || DSPLIT) ? 128 : 256;
@@ -281,7 +283,12 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
     constexpr int LPT = CHUNKS / NT;                // 16-byte loads per thread per tensor
     static_assert(CHUNKS % NT == 0, "tile must split evenly over threads");
 
-    __shared__ __attribute__((aligned(16))) char smem[NSLOT * SLOT_BYTES];
+    // D = 256: after the ring, each wave's row maxima (64 floats; at the end
+    // its two partial sums) and packed probabilities (2 x 64 x 16 bytes) for
+    // its pair mate
+    constexpr int XMAX_BYTES = DSPLIT ? 8 * 2 * 64 * 4 : 0;   // also the pair's final sums
+    constexpr int XP_BYTES = DSPLIT ? 8 * 2 * 64 * 16 : 0;
+    __shared__ __attribute__((aligned(16))) char smem[NSLOT * SLOT_BYTES + XMAX_BYTES + XP_BYTES];
 
     const int tid = threadIdx.x;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -300,8 +307,9 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
     // sees the last key).
     const int diag = p.diag;
     const int q0 = qb * BR;
-    const int qw0 = q0 + ((SPLIT || DSPLIT) ? (wid & 3) : wid) * 32;   // split: both groups share the rows
-    const int dob = DSPLIT ? grp * DO : 0;                             // first O block of this wave
+    // key split: both groups share the rows; D = 256: a pair per 32 rows
+    const int qw0 = q0 + (SPLIT ? (wid & 3) : DSPLIT ? (wid >> 1) : wid) * 32;
+    const int dob = DSPLIT ? (wid & 1) * DO : 0;                       // first O block of this wave
     const int b_ = bh / p.H, h_ = bh - b_ * p.H;
 
     // One buffer descriptor per tensor and head; its record count is the
@@ -814,67 +822,251 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
         m_run = m;
     }
     } else if constexpr (DSPLIT) {
-    // Head-dimension split (D = 256): waves w and w + 4 own the same 32 rows
-    // and compute the same scores and probabilities (identical instructions on
-    // identical data); wave w accumulates O's columns 0..127, wave w + 4
-    // columns 128..255.  The K/V ring has two slots of 64 KiB (a 32 KiB K tile
-    // and a 32 KiB V tile): in step t group 1 loads K of tile t + 1 (into the
-    // K half whose tile t - 1 was last read in step t - 1) and group 0, before
-    // its matrix phase, V of tile t (into the V half last read in step t - 1);
-    // every step ends with all its loads complete.
+    // Pair split (D = 256).  Waves w and w ^ 1 of one group own the same 32
+    // query rows; wave w takes the keys 32h .. 32h + 31 of every tile
+    // (h = w & 1) -- their scores S_h = K_h Q^T over the full head dimension,
+    // masking, row max and probabilities -- and O's columns 128h .. 128h + 127,
+    // for which it also needs the mate's probabilities.  The two groups own
+    // different rows and alternate phases as in the other instances.  In a
+    // matrix phase a wave reads the mate's packed probabilities of the
+    // previous tile from LDS, computes S_h of this tile, then O += P V with
+    // the full P, masks S_h and publishes its row max in LDS; in the softmax
+    // phase it takes the larger of the pair's two maxima (both waves of a
+    // pair therefore keep the same running max), forms its probabilities and
+    // publishes them packed.  Barriers between the phases carry these LDS
+    // exchanges.  A wave keeps its own probabilities in pf[0..1] and the
+    // mate's in pf[2..3] and reads the V rows of each from their key half.
+    // The K/V ring has two slots of 64 KiB (a 32 KiB K tile and a 32 KiB V
+    // tile): in step t group 1 loads K of tile t + 1 (into the K half whose
+    // tile t - 1 was last read in step t - 1) and group 0, before its matrix
+    // phase, V of tile t (into the V half last read in step t - 1); every
+    // step ends with all its loads complete.  The mask words of a tile are
+    // requested in the matrix phase before, after that phase applied its own.
+    const int h = wid & 1, mate = wid ^ 1;
+    float* const xmax = (float*)(smem + NSLOT * SLOT_BYTES);
+    i32x4* const xp = (i32x4*)(smem + NSLOT * SLOT_BYTES + XMAX_BYTES);
     auto end_step = [&]() {
         wait_vmcnt<0>();
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     };
-    // With a mask both groups apply the same words (same rows, same tile) at
-    // the start of their softmax phase, before that phase's tile loads, and
-    // request the next tile's words after them.
-    if constexpr (MASK) load_mask(0);
+    auto mid_step = [&]() {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
+    // mask bytes of this lane's query row for the keys 32h + 16g + 4j .. +3
+    // of tile t (register 4j + e of S_h: byte e of mkh[j])
+    uint32_t mkh[4];
+    auto load_mask_half = [&](int t) {
+        const int qrow = qw0 + lq;
+        const uint32_t row = qrow < Sq ? (uint32_t)qrow * (uint32_t)p.m_ss + (uint32_t)(t * BC + 32 * h + 16 * g)
+                                       : 0x80000000u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            mkh[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rm, row + 4 * j, 0, 0);
+            asm volatile("" ::: "memory");
+        }
+    };
+    auto qk_half = [&](int t) {
+        const int kb = (t & (NSLOT - 1)) * SLOT_BYTES + kbase_l;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[0][i] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+            const i32x4 a = *(const i32x4*)(smem + (kb ^ (c << 5)) + h * 32 * (2 * D));
+            s[0] = mfma32<DT>(a, qf[c], s[0]);
+        }
+    };
+    auto pv_pair = [&](int tp) {
+        const int vb = (tp & (NSLOT - 1)) * SLOT_BYTES + TILE_BYTES + vbase_l;
+        const int vown = 32 * h * (2 * D), vmate = 32 * (1 - h) * (2 * D);
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+            for (int b = 0; b < DO; ++b) {
+                const int off = (vb ^ ((b + dob) << 6)) + (kc < 2 ? vown : vmate) + 8 * (kc & 1) * (2 * D);
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4*)(smem + off));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4*)(smem + off + 4 * (2 * D)));
+                i32x4 a;
+                a[0] = __builtin_bit_cast(int, (short __attribute__((ext_vector_type(2)))){lo[0], lo[1]});
+                a[1] = __builtin_bit_cast(int, (short __attribute__((ext_vector_type(2)))){lo[2], lo[3]});
+                a[2] = __builtin_bit_cast(int, (short __attribute__((ext_vector_type(2)))){hi[0], hi[1]});
+                a[3] = __builtin_bit_cast(int, (short __attribute__((ext_vector_type(2)))){hi[2], hi[3]});
+                oacc[b] = mfma32<DT>(a, pf[kc], oacc[b]);
+            }
+        }
+    };
+    auto get_mate_p = [&]() {
+        pf[2] = xp[(2 * mate) * 64 + lane];
+        pf[3] = xp[(2 * mate + 1) * 64 + lane];
+    };
+    // hidden keys of S_h to -inf, then its row max (times scale log2 e),
+    // published for the mate
+    float mxh = -INFINITY;
+    auto mask_max = [&](int t) {
+        const int key0 = t * BC + 32 * h + 16 * g;
+        const int qrow = qw0 + lq;
+        const bool need_mask = (t * BC + 32 * h + 32 > Sk) || (CAUSAL && t * BC + 32 * h + 31 > qw0 + diag);
+        if (need_mask) {
+            const int lim = CAUSAL ? min(qrow + diag, Sk - 1) : Sk - 1;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (key0 + i > lim) s[0][i] = -INFINITY;
+        }
+        if constexpr (MASK) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (((mkh[i >> 2] >> (8 * (i & 3))) & 0xffu) == 0) s[0][i] = -INFINITY;
+        }
+        float mx = s[0][0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+        mxh = xmax32(mx) * c2;
+        xmax[wid * 64 + lane] = mxh;
+    };
+    // Instruction order of a matrix phase (S_h = K_h Q^T then O += P V: 16 + 16
+    // MFMAs after the mate's two probability words; 16 K reads, then two
+    // transposing V reads per P V MFMA): LDS reads run four MFMAs ahead.
+    auto mphase_pair_schedule = [&]() {
+        constexpr int MFMA = 0x008, DSR = 0x100;
+        constexpr int QK_N = DC, PV_N = 4 * DO, AHEAD = 4;
+        __builtin_amdgcn_sched_group_barrier(DSR, 2 + AHEAD, 0);
+#pragma unroll
+        for (int m = 0; m < QK_N - AHEAD; ++m) {
+            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(DSR, 1, 0);
+        }
+#pragma unroll
+        for (int m = 0; m < PV_N; ++m) {
+            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(DSR, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(MFMA, AHEAD, 0);
+    };
+    auto mphase_pair = [&](int tp, int t) {
+        __builtin_amdgcn_s_setprio(1);
+        get_mate_p();
+        qk_half(t);
+        pv_pair(tp);
+        mphase_pair_schedule();
+        __builtin_amdgcn_s_setprio(0);
+        mask_max(t);
+    };
+    // probabilities of this wave's keys of tile t against the pair's max
+    auto swork_half = [&](int t) {
+        if constexpr (DIAG) ++ntiles;
+        const float mx = fmaxf(mxh, xmax[mate * 64 + lane]);
+        const bool grow = mx > m_run + RESCALE_THRESHOLD;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+            r_run *= alpha;
+#pragma unroll
+            for (int b = 0; b < DO; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[b][i] *= alpha;
+        }
+        const float mb = (m_run == -INFINITY) ? 0.0f : m_run;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[0][i] = __builtin_fmaf(s[0][i], c2, -mb);
+        asm volatile("" : "+v"(s[0]));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[0][i] = fast_exp2(s[0][i]);
+        float lsum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) lsum += s[0][i];
+        l_run += lsum;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            i32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = pack2<DT>(s[0][8 * c + 2 * e], s[0][8 * c + 2 * e + 1]);
+            pf[c] = w;
+        }
+        // O's divisor: the probabilities as rounded for P V (see swork)
+        float rsum = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rsum = dot2_ones<DT>(pf[c][e], rsum);
+        r_run += rsum;
+        if constexpr (DROP) {
+            // keys t*BC + 32h + 16g + 8u + 0..7 (pf[u]) form the Philox block
+            // at counter (8t + 4h + 2g + u, query, bh, offset)
+            const uint32_t tm1 = p.drop_t - 1u;
+            const uint32_t tm1x2 = tm1 | (tm1 << 16);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                uint32_t c[4] = {(uint32_t)(8 * t + 4 * h + 2 * g + u), (uint32_t)(qw0 + lq), (uint32_t)bh, p.offset};
+                tile::philox4x32_10(c, p.seed_lo, p.seed_hi);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pf[u][e] = drop_pair(pf[u][e], c[e], tm1x2, 0x00010001u);
+            }
+        }
+        xp[(2 * wid) * 64 + lane] = pf[0];
+        xp[(2 * wid + 1) * 64 + lane] = pf[1];
+    };
+
+    if constexpr (MASK) load_mask_half(0);
     if (grp != 0) issue_tile(0);
     end_step();
     if (grp == 0) {
         issue_tile(0);
-        qk(0);
-        mid_barrier();
-        if constexpr (MASK) {
-            mask_scores();
-            if (nt > 1) load_mask(1);
-        }
-        swork(0);
+        qk_half(0);
+        mask_max(0);
+        if constexpr (MASK) if (nt > 1) load_mask_half(1);
+        mid_step();
+        swork_half(0);
         end_step();
         for (int t = 1; t < nt; ++t) {
             issue_tile(t);
-            mphase(t);
-            mid_barrier();
-            if constexpr (MASK) {
-                mask_scores();
-                if (t + 1 < nt) load_mask(t + 1);
-            }
-            swork(t);
+            mphase_pair(t - 1, t);
+            if constexpr (MASK) if (t + 1 < nt) load_mask_half(t + 1);
+            mid_step();
+            swork_half(t);
             end_step();
         }
-        pv(nt - 1);
-        mid_barrier();
+        get_mate_p();
+        pv_pair(nt - 1);
+        mid_step();
     } else {
         if (nt > 1) issue_tile(1);
-        mid_barrier();
-        qk(0);
+        mid_step();
+        qk_half(0);
+        mask_max(0);
+        if constexpr (MASK) if (nt > 1) load_mask_half(1);
         end_step();
         for (int t = 1; t < nt; ++t) {
-            if constexpr (MASK) mask_scores();
             if (t + 1 < nt) issue_tile(t + 1);
-            if constexpr (MASK) load_mask(t);
-            swork(t - 1);
-            mid_barrier();
-            mphase(t);
+            swork_half(t - 1);
+            mid_step();
+            mphase_pair(t - 1, t);
+            if constexpr (MASK) if (t + 1 < nt) load_mask_half(t + 1);
             end_step();
         }
-        if constexpr (MASK) mask_scores();
-        swork(nt - 1);
-        mid_barrier();
-        pv(nt - 1);
+        swork_half(nt - 1);
+        mid_step();
+        get_mate_p();
+        pv_pair(nt - 1);
+    }
+    // the pair's partial sums: both waves add them in the same order (h = 0
+    // first), so both hold the same totals.  The region of the row maxima is
+    // free: its last reads came before the last barrier.
+    {
+        float* const xl = (float*)(smem + NSLOT * SLOT_BYTES);
+        xl[(2 * wid) * 64 + lane] = l_run;
+        xl[(2 * wid + 1) * 64 + lane] = r_run;
+        mid_step();
+        const float l_mate = xl[(2 * mate) * 64 + lane];
+        const float r_mate = xl[(2 * mate + 1) * 64 + lane];
+        l_run = h ? l_mate + l_run : l_run + l_mate;
+        r_run = h ? r_mate + r_run : r_run + r_mate;
     }
     } else {
     // Prologue: Q, tile 0 and tile 1 requested; tile 0 (and Q) waited for.
@@ -963,7 +1155,7 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
         __builtin_amdgcn_raw_buffer_store_b128(w0, ro, off, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b128(w1, ro, off + 16, 0, 0);
     }
-    if (p.lse != nullptr && g == 0 && qrow < Sq && (!DSPLIT || grp == 0)) {
+    if (p.lse != nullptr && g == 0 && qrow < Sq && (!DSPLIT || (wid & 1) == 0)) {
         const float lse2 = (l_tot > 0.0f) ? (m_run == -INFINITY ? 0.0f : m_run) + log2f(l_tot) : -INFINITY;
         p.lse[(int64_t)bh * Sq + qrow] = lse2 * 0.69314718055994530942f;
     }
