@@ -198,6 +198,22 @@ __global__ __launch_bounds__(256, (MASK || DROP || D > 128) ? 1 : 2) void bwd_dk
 #pragma unroll
         for (int c = 0; c < DC; ++c)
             dp = mma<DT>(row_frag<D>(tdo, lq, 2 * c + g), vf[c], dp);
+        if constexpr (!MASK && !DROP && D <= 128) {
+            // LDS operands two MFMAs ahead: two reads per MFMA of S, one of dP
+            constexpr int MFMA = 0x008, DSR = 0x100, AH = 2;
+            __builtin_amdgcn_sched_group_barrier(DSR, 2 * AH, 0);
+#pragma unroll
+            for (int m = 0; m < DC - AH; ++m) {
+                __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(DSR, 2, 0);
+            }
+#pragma unroll
+            for (int m = DC - AH; m < 2 * DC - AH; ++m) {
+                __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(DSR, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(MFMA, AH, 0);
+        }
 
         // P = exp2(s * scale*log2e - lse*log2e), dS = P (Z c dP - D_i) and
         // P Z c for dV, with Z c the dropout keep factor
@@ -240,6 +256,17 @@ __global__ __launch_bounds__(256, (MASK || DROP || D > 128) ? 1 : 2) void bwd_dk
                 dva[b] = mma<DT>(tr_frag<D>(tdo, st, b, tl), pa, dva[b]);
                 dka[b] = mma<DT>(tr_frag<D>(tq, st, b, tl), da, dka[b]);
             }
+        }
+        if constexpr (!MASK && !DROP && D <= 128) {
+            // transposing reads (two per operand) four MFMAs ahead
+            constexpr int MFMA = 0x008, DSR = 0x100, N = 2 * DB * (QT / 16), AH = 4;
+            __builtin_amdgcn_sched_group_barrier(DSR, 2 * AH, 1);
+#pragma unroll
+            for (int m = 0; m < N - AH; ++m) {
+                __builtin_amdgcn_sched_group_barrier(MFMA, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(DSR, 2, 1);
+            }
+            __builtin_amdgcn_sched_group_barrier(MFMA, AH, 1);
         }
 
         wait_vmcnt<0>();
@@ -377,6 +404,17 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_dq(BwdParams p) {
                 dp[rb] = mma<DT>(row_frag<D>(tv, 32 * rb + lq, 2 * c + g), df[c], dp[rb]);
             }
         }
+        if constexpr (!MASK && !DROP && D <= 128) {
+            // LDS operands four MFMAs ahead
+            constexpr int MFMA = 0x008, DSR = 0x100, N = 4 * DC, AH = 4;
+            __builtin_amdgcn_sched_group_barrier(DSR, AH, 0);
+#pragma unroll
+            for (int m = 0; m < N - AH; ++m) {
+                __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(DSR, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(MFMA, AH, 0);
+        }
 
         const bool need_mask = MASK || (kt0 + KT > Sk) || (qw0 + 32 > Sq) || (CAUSAL && kt0 + KT - 1 > qw0 + diag);
 #pragma unroll
@@ -429,6 +467,17 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_dq(BwdParams p) {
             const i32x4 da = acc_frag<DT>(dp[st >> 1], st & 1);
 #pragma unroll
             for (int b = 0; b < DB; ++b) dqa[b] = mma<DT>(tr_frag<D>(tk, st, b, tl), da, dqa[b]);
+        }
+        if constexpr (!MASK && !DROP && D <= 128) {
+            // transposing reads (two per operand) four MFMAs ahead
+            constexpr int MFMA = 0x008, DSR = 0x100, N = 4 * DB, AH = 4;
+            __builtin_amdgcn_sched_group_barrier(DSR, 2 * AH, 1);
+#pragma unroll
+            for (int m = 0; m < N - AH; ++m) {
+                __builtin_amdgcn_sched_group_barrier(MFMA, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(DSR, 2, 1);
+            }
+            __builtin_amdgcn_sched_group_barrier(MFMA, AH, 1);
         }
 
         wait_vmcnt<0>();
