@@ -221,9 +221,10 @@ def naive_leg(w, steps, warmup):
 
 
 def backward_leg(w, steps, warmup):
-    """The backward (fa_bwd) on the same inputs, both dq modes, timed like the
-    forward.  Algorithmic flops: FlashAttention-2 convention, 2.5 x the
-    forward's (five S x S x D products), whatever a mode recomputes."""
+    """The backward (fa_bwd, bitwise reproducible) on the same inputs, then the
+    backward of the masked / dropout forward, timed like the forward.
+    Algorithmic flops: FlashAttention-2 convention, 2.5 x the forward's (five
+    S x S x D products), whatever the kernels recompute."""
     import torch
     import tiled_attention_15_amd as fa
     from workloads import make_inputs
@@ -239,7 +240,7 @@ def backward_leg(w, steps, warmup):
     flops = 2.5 * w.flops()
     out = {"unit": "TFLOP/s", "flops_per_step": flops, "steps": steps}
     if fa.fa_bwd_workspace_bytes(w.B, w.H, w.S, w.D, True) <= 0:
-        out["skipped"] = "the backward takes D in {64, 128}"
+        out["skipped"] = "the backward takes D in {64, 128, 256}"
         return out
     need = fa.fa_bwd_workspace_bytes(w.B, w.H, w.S, w.D, True)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)

@@ -114,17 +114,26 @@ __global__ __launch_bounds__(256, (MASK || DROP || D > 128) ? 1 : 2) void bwd_dk
                         (uint64_t)(((int64_t)(Sq - 1) * p.m_ss + Sk + 3) & ~(int64_t)3));
     }
     const uint32_t msk0 = (uint32_t)(uintptr_t)(lds_t*)&msk_s[0][0];
+    const TileDma<D, TN> dmq(p.Lq.ss, w, lane), dmo(p.Ldo.ss, w, lane);
+    // mask loads: instruction i of wave w covers rows 8i + 2w + lane/32 of
+    // the tile, dword lane%32 of each row's 128 key bytes
+    const uint32_t mlo = (uint32_t)((lane >> 5) * p.m_ss + 4 * (lane & 31));
     auto issue = [&](int t, int buf) {
         const uint32_t base = lds0 + (uint32_t)(KBLK + buf * 2 * TILE);
-        tile_dma<D, TN>(rq, t * QT, p.Lq.ss, base, w, lane);
-        tile_dma<D, TN>(rdo, t * QT, p.Ldo.ss, base + TILE, w, lane);
+        if constexpr (D > 128) {
+            dmq.issue(rq, t * QT, base, w);
+            dmo.issue(rdo, t * QT, base + TILE, w);
+        } else {
+            tile_dma<D, TN>(rq, t * QT, p.Lq.ss, base, w, lane);
+            tile_dma<D, TN>(rdo, t * QT, p.Ldo.ss, base + TILE, w, lane);
+        }
         if constexpr (MASK) {
-            // QT rows x 128 bytes, one dword per lane and instruction
+            static_assert(QT * kKeyBlock / 4 / 256 * 8 == QT && kKeyBlock == 128, "mask tile split");
 #pragma unroll
             for (int i = 0; i < QT * kKeyBlock / 4 / 256; ++i) {
-                const int c = (4 * i + w) * 64 + lane, r = c / (kKeyBlock / 4), dw = c % (kKeyBlock / 4);
-                lds_dma4(rm, (uint32_t)((int64_t)(t * QT + r) * p.m_ss + k0 + 4 * dw),
-                         msk0 + (uint32_t)(buf * QT * kKeyBlock + (4 * i + w) * 256));
+                int u = (int)(uint32_t)((int64_t)(t * QT + 8 * i + 2 * w) * p.m_ss + k0);
+                asm volatile("" : "+s"(u));
+                lds_dma4(rm, mlo + (uint32_t)u, msk0 + (uint32_t)(buf * QT * kKeyBlock + (4 * i + w) * 256));
             }
         }
     };
@@ -161,6 +170,7 @@ __global__ __launch_bounds__(256, (MASK || DROP || D > 128) ? 1 : 2) void bwd_dk
     };
 
     const TrLane tl = tr_lane(lane);
+    const FragOff<D> fo(lane, tl);
     const float c2 = p.scale_log2e;
     const int key = kw0 + lq;
     f32x16 dva[DB], dka[DB];
@@ -184,91 +194,168 @@ __global__ __launch_bounds__(256, (MASK || DROP || D > 128) ? 1 : 2) void bwd_dk
         if (t + 1 < nqt) {
             issue(t + 1, buf ^ 1);
             fetch_stats(t + 1);
-            if constexpr (DROP) make_keep(t + 1, buf ^ 1);
+            if constexpr (DROP && D <= 128) make_keep(t + 1, buf ^ 1);
         }
         const lds_t* tq = sm + KBLK + buf * 2 * TILE;
         const lds_t* tdo = tq + TILE;
         const int q0 = t * QT;
 
-        // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
-        f32x16 s = zero16(), dp = zero16();
+        if constexpr (D > 128) {
+            const bool need_mask = MASK || (q0 + QT > Sq) || (kw0 + 32 > Sk) || (CAUSAL && kw0 + 31 > q0 + diag);
+            const int kl = 32 * w + lq;                    // key within the block
+            // One score accumulator at a time (the dK^T, dV^T accumulators
+            // fill the AGPRs): S, then P and dV^T += dO^T (P Z c), then dP
+            // and dS = P (Z c dP - D_i), then dK^T += Q^T dS.  LDS reads use
+            // the per-lane offset tables; the tile base is kept opaque so the
+            // base + offset sums are formed here, not held for both buffers.
+            uint32_t tqa = (uint32_t)(uintptr_t)tq;
+            asm volatile("" : "+s"(tqa));
+            const lds_t* tq_ = (const lds_t*)(uintptr_t)tqa;
+            const lds_t* tdo_ = tq_ + TILE;
+            f32x16 s = zero16();
 #pragma unroll
-        for (int c = 0; c < DC; ++c)
-            s = mma<DT>(row_frag<D>(tq, lq, 2 * c + g), row_frag<D>(kblk, 32 * w + lq, 2 * c + g), s);
+            for (int c = 0; c < DC; ++c) s = mma<DT>(fo.row(tq_, 0, c), fo.row(kblk, 32 * w, c), s);
+            uint32_t zb = 0;                           // keep decision of register r at bit r
 #pragma unroll
-        for (int c = 0; c < DC; ++c)
-            dp = mma<DT>(row_frag<D>(tdo, lq, 2 * c + g), vf[c], dp);
-        if constexpr (!MASK && !DROP && D <= 128) {
-            // LDS operands two MFMAs ahead: two reads per MFMA of S, one of dP
-            constexpr int MFMA = 0x008, DSR = 0x100, AH = 2;
-            __builtin_amdgcn_sched_group_barrier(DSR, 2 * AH, 0);
+            for (int a = 0; a < 4; ++a) {
+                const int qr = 8 * a + 4 * g;
+                const f32x4 l4 = *(const f32x4*)&lse_s[buf][qr];
 #pragma unroll
-            for (int m = 0; m < DC - AH; ++m) {
-                __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(DSR, 2, 0);
-            }
-#pragma unroll
-            for (int m = DC - AH; m < 2 * DC - AH; ++m) {
-                __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(DSR, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(MFMA, AH, 0);
-        }
-
-        // P = exp2(s * scale*log2e - lse*log2e), dS = P (Z c dP - D_i) and
-        // P Z c for dV, with Z c the dropout keep factor
-        const bool need_mask = MASK || (q0 + QT > Sq) || (kw0 + 32 > Sk) || (CAUSAL && kw0 + 31 > q0 + diag);
-        const int kl = 32 * w + lq;                    // key within the block
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const int qr = 8 * a + 4 * g;
-            const f32x4 l4 = *(const f32x4*)&lse_s[buf][qr];
-            const f32x4 d4 = *(const f32x4*)&dv_s[buf][qr];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * a + e;
-                float pv = __builtin_amdgcn_exp2f(s[r] * c2 - l4[e]);
-                if (need_mask) {
-                    const int qi = q0 + qr + e;
-                    bool vis = qi < Sq && key < Sk && (!CAUSAL || key <= qi + diag);
-                    if constexpr (MASK) vis = vis && msk_s[buf][(qr + e) * kKeyBlock + kl] != 0;
-                    pv = vis ? pv : 0.0f;
-                }
-                if constexpr (DROP) {
-                    const float z = ((keep_s[buf][(qr + e) * (kKeyBlock / 8) + (kl >> 3)] >> (kl & 7)) & 1)
-                                        ? p.keep_scale : 0.0f;
-                    s[r] = pv * z;
-                    dp[r] = pv * (z * dp[r] - d4[e]);
-                } else {
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * a + e;
+                    float pv = __builtin_amdgcn_exp2f(s[r] * c2 - l4[e]);
+                    if (need_mask) {
+                        const int qi = q0 + qr + e;
+                        bool vis = qi < Sq && key < Sk && (!CAUSAL || key <= qi + diag);
+                        if constexpr (MASK) vis = vis && msk_s[buf][(qr + e) * kKeyBlock + kl] != 0;
+                        pv = vis ? pv : 0.0f;
+                    }
+                    if constexpr (DROP)
+                        zb |= ((keep_s[buf][(qr + e) * (kKeyBlock / 8) + (kl >> 3)] >> (kl & 7)) & 1u) << r;
                     s[r] = pv;
-                    dp[r] = pv * (dp[r] - d4[e]);
                 }
             }
-        }
+            auto zc = [&](int r) { return ((zb >> r) & 1u) ? p.keep_scale : 0.0f; };
+#pragma unroll
+            for (int st = 0; st < QT / 16; ++st) {
+                i32x4 pa;
+                if constexpr (DROP) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = 8 * st + 2 * i;
+                        pa[i] = pack2<DT>(s[r] * zc(r), s[r + 1] * zc(r + 1));
+                    }
+                } else {
+                    pa = acc_frag<DT>(s, st);
+                }
+#pragma unroll
+                for (int b = 0; b < DB; ++b) dva[b] = mma<DT>(fo.tr(tdo_, st, b), pa, dva[b]);
+            }
+            f32x16 dp = zero16();
+#pragma unroll
+            for (int c = 0; c < DC; ++c) dp = mma<DT>(fo.row(tdo_, 0, c), vf[c], dp);
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const int qr = 8 * a + 4 * g;
+                const f32x4 d4 = *(const f32x4*)&dv_s[buf][qr];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * a + e;
+                    if constexpr (DROP) dp[r] = s[r] * (zc(r) * dp[r] - d4[e]);
+                    else dp[r] = s[r] * (dp[r] - d4[e]);
+                }
+            }
+#pragma unroll
+            for (int st = 0; st < QT / 16; ++st) {
+                const i32x4 da = acc_frag<DT>(dp, st);
+#pragma unroll
+                for (int b = 0; b < DB; ++b) dka[b] = mma<DT>(fo.tr(tq_, st, b), da, dka[b]);
+            }
+        } else {
+            // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
+            f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+            for (int c = 0; c < DC; ++c)
+                s = mma<DT>(row_frag<D>(tq, lq, 2 * c + g), row_frag<D>(kblk, 32 * w + lq, 2 * c + g), s);
+#pragma unroll
+            for (int c = 0; c < DC; ++c)
+                dp = mma<DT>(row_frag<D>(tdo, lq, 2 * c + g), vf[c], dp);
+            if constexpr (!MASK && !DROP && D <= 128) {
+                // LDS operands two MFMAs ahead: two reads per MFMA of S, one of dP
+                constexpr int MFMA = 0x008, DSR = 0x100, AH = 2;
+                __builtin_amdgcn_sched_group_barrier(DSR, 2 * AH, 0);
+#pragma unroll
+                for (int m = 0; m < DC - AH; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(DSR, 2, 0);
+                }
+#pragma unroll
+                for (int m = DC - AH; m < 2 * DC - AH; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(DSR, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(MFMA, AH, 0);
+            }
 
-        // dV^T += dO^T P, dK^T += Q^T dS  (rows: head dimension, columns: keys)
+            // P = exp2(s * scale*log2e - lse*log2e), dS = P (Z c dP - D_i) and
+            // P Z c for dV, with Z c the dropout keep factor
+            const bool need_mask = MASK || (q0 + QT > Sq) || (kw0 + 32 > Sk) || (CAUSAL && kw0 + 31 > q0 + diag);
+            const int kl = 32 * w + lq;                    // key within the block
 #pragma unroll
-        for (int st = 0; st < QT / 16; ++st) {
-            const i32x4 pa = acc_frag<DT>(s, st);
-            const i32x4 da = acc_frag<DT>(dp, st);
+            for (int a = 0; a < 4; ++a) {
+                const int qr = 8 * a + 4 * g;
+                const f32x4 l4 = *(const f32x4*)&lse_s[buf][qr];
+                const f32x4 d4 = *(const f32x4*)&dv_s[buf][qr];
 #pragma unroll
-            for (int b = 0; b < DB; ++b) {
-                dva[b] = mma<DT>(tr_frag<D>(tdo, st, b, tl), pa, dva[b]);
-                dka[b] = mma<DT>(tr_frag<D>(tq, st, b, tl), da, dka[b]);
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * a + e;
+                    float pv = __builtin_amdgcn_exp2f(s[r] * c2 - l4[e]);
+                    if (need_mask) {
+                        const int qi = q0 + qr + e;
+                        bool vis = qi < Sq && key < Sk && (!CAUSAL || key <= qi + diag);
+                        if constexpr (MASK) vis = vis && msk_s[buf][(qr + e) * kKeyBlock + kl] != 0;
+                        pv = vis ? pv : 0.0f;
+                    }
+                    if constexpr (DROP) {
+                        const float z = ((keep_s[buf][(qr + e) * (kKeyBlock / 8) + (kl >> 3)] >> (kl & 7)) & 1)
+                                            ? p.keep_scale : 0.0f;
+                        s[r] = pv * z;
+                        dp[r] = pv * (z * dp[r] - d4[e]);
+                    } else {
+                        s[r] = pv;
+                        dp[r] = pv * (dp[r] - d4[e]);
+                    }
+                }
+            }
+
+            // dV^T += dO^T P, dK^T += Q^T dS  (rows: head dimension, columns: keys)
+#pragma unroll
+            for (int st = 0; st < QT / 16; ++st) {
+                const i32x4 pa = acc_frag<DT>(s, st);
+                const i32x4 da = acc_frag<DT>(dp, st);
+#pragma unroll
+                for (int b = 0; b < DB; ++b) {
+                    dva[b] = mma<DT>(tr_frag<D>(tdo, st, b, tl), pa, dva[b]);
+                    dka[b] = mma<DT>(tr_frag<D>(tq, st, b, tl), da, dka[b]);
+                }
+            }
+            if constexpr (!MASK && !DROP && D <= 128) {
+                // transposing reads (two per operand) four MFMAs ahead
+                constexpr int MFMA = 0x008, DSR = 0x100, N = 2 * DB * (QT / 16), AH = 4;
+                __builtin_amdgcn_sched_group_barrier(DSR, 2 * AH, 1);
+#pragma unroll
+                for (int m = 0; m < N - AH; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(MFMA, 1, 1);
+                    __builtin_amdgcn_sched_group_barrier(DSR, 2, 1);
+                }
+                __builtin_amdgcn_sched_group_barrier(MFMA, AH, 1);
             }
         }
-        if constexpr (!MASK && !DROP && D <= 128) {
-            // transposing reads (two per operand) four MFMAs ahead
-            constexpr int MFMA = 0x008, DSR = 0x100, N = 2 * DB * (QT / 16), AH = 4;
-            __builtin_amdgcn_sched_group_barrier(DSR, 2 * AH, 1);
-#pragma unroll
-            for (int m = 0; m < N - AH; ++m) {
-                __builtin_amdgcn_sched_group_barrier(MFMA, 1, 1);
-                __builtin_amdgcn_sched_group_barrier(DSR, 2, 1);
-            }
-            __builtin_amdgcn_sched_group_barrier(MFMA, AH, 1);
-        }
 
+        if constexpr (DROP && D > 128) {
+            // the next tile's keep bits once this tile's scores are dead
+            if (t + 1 < nqt) make_keep(t + 1, buf ^ 1);
+        }
         wait_vmcnt<0>();
         if (t + 1 < nqt) store_stats(buf ^ 1);
         __syncthreads();

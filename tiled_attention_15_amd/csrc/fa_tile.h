@@ -129,6 +129,51 @@ __device__ __forceinline__ i32x4 tr_frag(const lds_t* tile, int s, int b, const 
     return a;
 }
 
+// Per-lane byte offsets of the fragment reads above, computed once.  The
+// swizzle depends on a row's index mod 16 and changes only the low four bits
+// of a chunk index, so for row reads (chunk 2c + g of row r0 + lq, r0 a
+// multiple of 16) the offsets of c < 8 serve every c, the chunk of c + 8
+// lying 256 bytes further; for transposing reads (rows 16s + tl.row (+8),
+// chunks 4b + tl.ch) the offsets of b < 4 serve every b (256 bytes per four
+// blocks) and every s (16 rows).
+template <int W>
+struct FragOff {
+    static constexpr int NR = W / 16 < 8 ? W / 16 : 8;
+    static constexpr int NT = W / 32 < 4 ? W / 32 : 4;
+    uint32_t rx[NR];
+    uint32_t tx[2][NT];
+    __device__ __forceinline__ FragOff(int lane, const TrLane& tl) {
+        const int lq = lane & 31, g = lane >> 5;
+#pragma unroll
+        for (int k = 0; k < NR; ++k) rx[k] = (uint32_t)(lq * (2 * W) + (((2 * k + g) ^ swz<W>(lq)) << 4));
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int r = tl.row + 8 * h;
+#pragma unroll
+            for (int k = 0; k < NT; ++k)
+                tx[h][k] = (uint32_t)(r * (2 * W) + (((4 * k + tl.ch) ^ swz<W>(r)) << 4) + tl.byte);
+        }
+    }
+    // row_frag(tile, r0 + lq, 2c + g)
+    __device__ __forceinline__ i32x4 row(const lds_t* tile, int r0, int c) const {
+        return *(const __attribute__((address_space(3))) i32x4*)(tile + r0 * (2 * W) + rx[c % NR] + 256 * (c / NR));
+    }
+    // tr_frag(tile, s, b, tl)
+    __device__ __forceinline__ i32x4 tr(const lds_t* tile, int s, int b) const {
+        const lds_t* t = tile + 16 * s * (2 * W) + 256 * (b / NT);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(t + tx[0][b % NT]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(t + tx[1][b % NT]));
+        i32x4 a;
+        a[0] = (int)(uint16_t)lo[0] | ((int)(uint16_t)lo[1] << 16);
+        a[1] = (int)(uint16_t)lo[2] | ((int)(uint16_t)lo[3] << 16);
+        a[2] = (int)(uint16_t)hi[0] | ((int)(uint16_t)hi[1] << 16);
+        a[3] = (int)(uint16_t)hi[2] | ((int)(uint16_t)hi[3] << 16);
+        return a;
+    }
+};
+
 // B operand of k-step s from a 32-row-block pair of accumulators (rows
 // 32*(s/2) .. of the product), packed to 16 bits.
 template <int DT>
@@ -269,6 +314,39 @@ __device__ __forceinline__ void tile_dma(i32x4 rw, int row0, int ss, uint32_t ld
         lds_dma16(rw, (uint32_t)(((row0 + r) * ss + 8 * ch) * 2), lds_tile + (uint32_t)((4 * i + w) * 1024));
     }
 }
+
+// The loads of tile_dma with the per-lane part of each offset computed once.
+// Load i of a wave covers rows i*STEP + w*RPI + lane/(W/8), so its rows
+// repeat the swizzle pattern (period 16 rows) every NC loads: the lane parts
+// take NC values, kept in registers, and the rest is a wave-uniform row
+// offset added at issue time (kept opaque so the sums are not precomputed
+// into N registers).  Offsets stay whole in the vector operand, so rows
+// past the buffer's end still read as zero.
+template <int W, int N>
+struct TileDma {
+    static constexpr int RPI = 512 / W;                         // rows per load instruction
+    static constexpr int STEP = 4 * RPI;                        // rows between loads i and i+1
+    static constexpr int NC0 = (STEP % 16) ? 16 / (STEP % 16) : 1;
+    static constexpr int NC = NC0 < N ? NC0 : N;
+    static_assert(16 % ((STEP % 16) ? STEP % 16 : 16) == 0, "swizzle period");
+    uint32_t lo[NC];
+    int ss;
+    __device__ __forceinline__ TileDma(int ss_, int w, int lane) : ss(ss_) {
+#pragma unroll
+        for (int k = 0; k < NC; ++k) {
+            const int r = k * STEP + w * RPI + lane / (W / 8), pos = lane % (W / 8);
+            lo[k] = (uint32_t)((r * ss + 8 * (pos ^ swz<W>(r))) * 2);
+        }
+    }
+    __device__ __forceinline__ void issue(i32x4 rw, int row0, uint32_t lds_tile, int w) const {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            int u = (row0 + (i / NC) * NC * STEP) * ss * 2;
+            asm volatile("" : "+s"(u));
+            lds_dma16(rw, lo[i % NC] + (uint32_t)u, lds_tile + (uint32_t)((4 * i + w) * 1024));
+        }
+    }
+};
 
 }  // namespace tile
 }  // namespace fa
