@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void bwd_pre(BwdParams p) {
 // fragments and the dK^T, dV^T accumulators stay in registers; 32-query tiles
 // of Q and dO go straight from global memory into LDS.
 template <int D, int DT, bool CAUSAL, bool MASK = false, bool DROP = false>
-__global__ __launch_bounds__(256, (MASK || DROP || D > 128) ? 1 : 2) void bwd_dkdv(BwdParams p) {
+__global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_dkdv(BwdParams p) {
     constexpr int DC = D / 16;                         // k-steps over the head dimension
     constexpr int DB = D / 32;                         // 32-column blocks of the head dimension
     constexpr int QT = kQueryTile;
@@ -68,8 +68,13 @@ __global__ __launch_bounds__(256, (MASK || DROP || D > 128) ? 1 : 2) void bwd_dk
     static_assert(TN >= 1 && KN >= 1, "tile must split over the threads");
 
     __shared__ __attribute__((aligned(16))) char smem[KBLK + 4 * TILE];
-    __shared__ __attribute__((aligned(16))) float lse_s[2][QT];
-    __shared__ __attribute__((aligned(16))) float dv_s[2][QT];
+    // one score accumulator at a time: at D = 256 (accumulators fill the
+    // AGPRs) and with a mask or dropout
+    constexpr bool SEQ = D > 128 || MASK || DROP;
+    // lse and D_i of a tile (with SEQ loaded straight into LDS by one wave,
+    // 64 entries of which the first QT are the tile's)
+    __shared__ __attribute__((aligned(16))) float lse_s[2][SEQ ? 64 : QT];
+    __shared__ __attribute__((aligned(16))) float dv_s[2][SEQ ? 64 : QT];
     // mask bytes of a tile, [query][key of the block] (with a mask), and the
     // keep bits of a tile, [query][8-key group] one bit per key (with dropout)
     __shared__ __attribute__((aligned(16))) uint8_t msk_s[2][MASK ? QT * kKeyBlock : 16];
@@ -120,7 +125,7 @@ __global__ __launch_bounds__(256, (MASK || DROP || D > 128) ? 1 : 2) void bwd_dk
     const uint32_t mlo = (uint32_t)((lane >> 5) * p.m_ss + 4 * (lane & 31));
     auto issue = [&](int t, int buf) {
         const uint32_t base = lds0 + (uint32_t)(KBLK + buf * 2 * TILE);
-        if constexpr (D > 128) {
+        if constexpr (SEQ) {
             dmq.issue(rq, t * QT, base, w);
             dmo.issue(rdo, t * QT, base + TILE, w);
         } else {
@@ -140,9 +145,13 @@ __global__ __launch_bounds__(256, (MASK || DROP || D > 128) ? 1 : 2) void bwd_dk
     // keep bits of a tile: each thread draws two Philox4x32-10 blocks, one
     // per (query, 8-key group), and stores their 8 keep bits as one byte
     auto make_keep = [&](int t, int buf) {
+        // thread index kept opaque: the counters and the tile-invariant
+        // part of the rounds are recomputed, not held across the loop
+        int tid_ = tid;
+        asm volatile("" : "+v"(tid_));
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int id = 2 * tid + u, ql = id >> 4, grp = id & 15;
+            const int id = 2 * tid_ + u, ql = id >> 4, grp = id & 15;
             uint32_t c[4] = {(uint32_t)((k0 >> 3) + grp), (uint32_t)(t * QT + ql), (uint32_t)bh, p.offset};
             philox4x32_10(c, p.seed_lo, p.seed_hi);
             uint32_t bits = 0;
@@ -156,13 +165,23 @@ __global__ __launch_bounds__(256, (MASK || DROP || D > 128) ? 1 : 2) void bwd_dk
     };
     // lse (times log2 e) and D_i of a tile: threads 0..QT-1 and QT..2QT-1
     float sl = 0.0f;
-    auto fetch_stats = [&](int t) {
+    const i32x4 rl_w = rsrc_words(p.lse + (int64_t)bh * Sq, (uint64_t)Sq * 4);
+    const i32x4 rdv_w = rsrc_words(p.dvec + (int64_t)bh * Sq, (uint64_t)Sq * 4);
+    auto fetch_stats = [&](int t, int buf) {
+        if constexpr (SEQ) {
+            if (w == 0) {
+                lds_dma4(rl_w, (uint32_t)((t * QT + lane) * 4), (uint32_t)(uintptr_t)(lds_t*)&lse_s[buf][0]);
+                lds_dma4(rdv_w, (uint32_t)((t * QT + lane) * 4), (uint32_t)(uintptr_t)(lds_t*)&dv_s[buf][0]);
+            }
+            return;
+        }
         if (tid < QT)
             sl = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, (t * QT + tid) * 4, 0, 0));
         else if (tid < 2 * QT)
             sl = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdv, (t * QT + tid - QT) * 4, 0, 0));
     };
     auto store_stats = [&](int buf) {
+        if constexpr (SEQ) return;
         if (tid < QT)
             lse_s[buf][tid] = sl * LOG2E;
         else if (tid < 2 * QT)
@@ -170,7 +189,10 @@ __global__ __launch_bounds__(256, (MASK || DROP || D > 128) ? 1 : 2) void bwd_dk
     };
 
     const TrLane tl = tr_lane(lane);
-    const FragOff<D> fo(lane, tl);
+    // per-lane LDS read offsets: tables at D = 256, XOR masks (fewer
+    // registers, one VALU per read) at two waves per SIMD
+    using FO = typename std::conditional<(D > 128), FragOff<D>, FragXor<D>>::type;
+    const FO fo(lane, tl);
     const float c2 = p.scale_log2e;
     const int key = kw0 + lq;
     f32x16 dva[DB], dka[DB];
@@ -182,7 +204,7 @@ __global__ __launch_bounds__(256, (MASK || DROP || D > 128) ? 1 : 2) void bwd_dk
 
     if (t0 < nqt) {
         issue(t0, 0);
-        fetch_stats(t0);
+        fetch_stats(t0, 0);
         if constexpr (DROP) make_keep(t0, 0);
     }
     wait_vmcnt<0>();
@@ -193,14 +215,14 @@ __global__ __launch_bounds__(256, (MASK || DROP || D > 128) ? 1 : 2) void bwd_dk
         const int buf = (t - t0) & 1;
         if (t + 1 < nqt) {
             issue(t + 1, buf ^ 1);
-            fetch_stats(t + 1);
-            if constexpr (DROP && D <= 128) make_keep(t + 1, buf ^ 1);
+            fetch_stats(t + 1, buf ^ 1);
+            if constexpr (DROP && !SEQ) make_keep(t + 1, buf ^ 1);
         }
         const lds_t* tq = sm + KBLK + buf * 2 * TILE;
         const lds_t* tdo = tq + TILE;
         const int q0 = t * QT;
 
-        if constexpr (D > 128) {
+        if constexpr (SEQ) {
             const bool need_mask = MASK || (q0 + QT > Sq) || (kw0 + 32 > Sk) || (CAUSAL && kw0 + 31 > q0 + diag);
             const int kl = 32 * w + lq;                    // key within the block
             // One score accumulator at a time (the dK^T, dV^T accumulators
@@ -208,31 +230,46 @@ __global__ __launch_bounds__(256, (MASK || DROP || D > 128) ? 1 : 2) void bwd_dk
             // and dS = P (Z c dP - D_i), then dK^T += Q^T dS.  LDS reads use
             // the per-lane offset tables; the tile base is kept opaque so the
             // base + offset sums are formed here, not held for both buffers.
-            uint32_t tqa = (uint32_t)(uintptr_t)tq;
-            asm volatile("" : "+s"(tqa));
+            uint32_t tqa = (uint32_t)(uintptr_t)tq, kba = (uint32_t)(uintptr_t)(kblk + 32 * w * 2 * D);
+            asm volatile("" : "+s"(tqa), "+s"(kba));
             const lds_t* tq_ = (const lds_t*)(uintptr_t)tqa;
             const lds_t* tdo_ = tq_ + TILE;
+            const lds_t* kw_ = (const lds_t*)(uintptr_t)kba;
             f32x16 s = zero16();
 #pragma unroll
-            for (int c = 0; c < DC; ++c) s = mma<DT>(fo.row(tq_, 0, c), fo.row(kblk, 32 * w, c), s);
+            for (int c = 0; c < DC; ++c) s = mma<DT>(fo.row(tq_, 0, c), fo.row(kw_, 0, c), s);
+            // LDS operands AH MFMAs ahead (two waves per SIMD at D <= 128)
+            constexpr int MFMA = 0x008, DSR = 0x100, AH = 2;
+            if constexpr (D <= 128) {
+                __builtin_amdgcn_sched_group_barrier(DSR, 2 * AH, 0);
+#pragma unroll
+                for (int m = 0; m < DC - AH; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(DSR, 2, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(MFMA, AH, 0);
+            }
             uint32_t zb = 0;                           // keep decision of register r at bit r
+            // this lane's mask byte and keep byte of query row 4g; rows
+            // 8a + e further are constant offsets
+            const uint8_t* mrow = &msk_s[buf][4 * g * kKeyBlock + kl];
+            const uint8_t* krow = &keep_s[buf][4 * g * (kKeyBlock / 8) + (kl >> 3)];
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 const int qr = 8 * a + 4 * g;
-                const f32x4 l4 = *(const f32x4*)&lse_s[buf][qr];
+                const f32x4 l4 = *(const f32x4*)&lse_s[buf][qr] * LOG2E;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * a + e;
-                    float pv = __builtin_amdgcn_exp2f(s[r] * c2 - l4[e]);
+                    float x = s[r] * c2 - l4[e];
                     if (need_mask) {
                         const int qi = q0 + qr + e;
                         bool vis = qi < Sq && key < Sk && (!CAUSAL || key <= qi + diag);
-                        if constexpr (MASK) vis = vis && msk_s[buf][(qr + e) * kKeyBlock + kl] != 0;
-                        pv = vis ? pv : 0.0f;
+                        if constexpr (MASK) vis = vis && mrow[(8 * a + e) * kKeyBlock] != 0;
+                        x = vis ? x : -__builtin_inff();
                     }
-                    if constexpr (DROP)
-                        zb |= ((keep_s[buf][(qr + e) * (kKeyBlock / 8) + (kl >> 3)] >> (kl & 7)) & 1u) << r;
-                    s[r] = pv;
+                    if constexpr (DROP) zb |= ((krow[(8 * a + e) * (kKeyBlock / 8)] >> (kl & 7)) & 1u) << r;
+                    s[r] = __builtin_amdgcn_exp2f(x);
                 }
             }
             auto zc = [&](int r) { return ((zb >> r) & 1u) ? p.keep_scale : 0.0f; };
@@ -254,6 +291,23 @@ __global__ __launch_bounds__(256, (MASK || DROP || D > 128) ? 1 : 2) void bwd_dk
             f32x16 dp = zero16();
 #pragma unroll
             for (int c = 0; c < DC; ++c) dp = mma<DT>(fo.row(tdo_, 0, c), vf[c], dp);
+            if constexpr (D <= 128) {
+                constexpr int N = DB * (QT / 16);
+                __builtin_amdgcn_sched_group_barrier(DSR, 2 * AH, 1);
+#pragma unroll
+                for (int m = 0; m < N - AH; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(MFMA, 1, 1);
+                    __builtin_amdgcn_sched_group_barrier(DSR, 2, 1);
+                }
+                __builtin_amdgcn_sched_group_barrier(MFMA, AH, 1);
+                __builtin_amdgcn_sched_group_barrier(DSR, AH, 2);
+#pragma unroll
+                for (int m = 0; m < DC - AH; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(MFMA, 1, 2);
+                    __builtin_amdgcn_sched_group_barrier(DSR, 1, 2);
+                }
+                __builtin_amdgcn_sched_group_barrier(MFMA, AH, 2);
+            }
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 const int qr = 8 * a + 4 * g;
@@ -270,6 +324,16 @@ __global__ __launch_bounds__(256, (MASK || DROP || D > 128) ? 1 : 2) void bwd_dk
                 const i32x4 da = acc_frag<DT>(dp, st);
 #pragma unroll
                 for (int b = 0; b < DB; ++b) dka[b] = mma<DT>(fo.tr(tq_, st, b), da, dka[b]);
+            }
+            if constexpr (D <= 128) {
+                constexpr int N = DB * (QT / 16);
+                __builtin_amdgcn_sched_group_barrier(DSR, 2 * AH, 3);
+#pragma unroll
+                for (int m = 0; m < N - AH; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(MFMA, 1, 3);
+                    __builtin_amdgcn_sched_group_barrier(DSR, 2, 3);
+                }
+                __builtin_amdgcn_sched_group_barrier(MFMA, AH, 3);
             }
         } else {
             // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
@@ -352,8 +416,9 @@ __global__ __launch_bounds__(256, (MASK || DROP || D > 128) ? 1 : 2) void bwd_dk
             }
         }
 
-        if constexpr (DROP && D > 128) {
+        if constexpr (DROP && SEQ) {
             // the next tile's keep bits once this tile's scores are dead
+            __builtin_amdgcn_sched_barrier(0);
             if (t + 1 < nqt) make_keep(t + 1, buf ^ 1);
         }
         wait_vmcnt<0>();

@@ -174,6 +174,45 @@ struct FragOff {
     }
 };
 
+// The same reads with two registers per read kind: the swizzle is an XOR of
+// a chunk index with a per-lane mask, so an address is
+// (16 * chunk step) ^ (16 * mask) + per-lane base, one v_xad_u32 per read.
+template <int W>
+struct FragXor {
+    uint32_t rb, rm;                                       // row reads
+    uint32_t tb[2], tm[2];                                 // transposing reads
+    __device__ __forceinline__ FragXor(int lane, const TrLane& tl) {
+        const int lq = lane & 31, g = lane >> 5;
+        rb = (uint32_t)(lq * (2 * W));
+        rm = (uint32_t)((g ^ swz<W>(lq)) << 4);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int r = tl.row + 8 * h;
+            tb[h] = (uint32_t)(r * (2 * W) + tl.byte);
+            tm[h] = (uint32_t)((tl.ch ^ swz<W>(r)) << 4);
+        }
+    }
+    // row_frag(tile, r0 + lq, 2c + g)
+    __device__ __forceinline__ i32x4 row(const lds_t* tile, int r0, int c) const {
+        const uint32_t off = ((uint32_t)(32 * c) ^ rm) + rb;
+        return *(const __attribute__((address_space(3))) i32x4*)(tile + r0 * (2 * W) + off);
+    }
+    // tr_frag(tile, s, b, tl)
+    __device__ __forceinline__ i32x4 tr(const lds_t* tile, int s, int b) const {
+        const lds_t* t = tile + 16 * s * (2 * W);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(t + (((uint32_t)(64 * b) ^ tm[0]) + tb[0])));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(t + (((uint32_t)(64 * b) ^ tm[1]) + tb[1])));
+        i32x4 a;
+        a[0] = (int)(uint16_t)lo[0] | ((int)(uint16_t)lo[1] << 16);
+        a[1] = (int)(uint16_t)lo[2] | ((int)(uint16_t)lo[3] << 16);
+        a[2] = (int)(uint16_t)hi[0] | ((int)(uint16_t)hi[1] << 16);
+        a[3] = (int)(uint16_t)hi[2] | ((int)(uint16_t)hi[3] << 16);
+        return a;
+    }
+};
+
 // B operand of k-step s from a 32-row-block pair of accumulators (rows
 // 32*(s/2) .. of the product), packed to 16 bits.
 template <int DT>
