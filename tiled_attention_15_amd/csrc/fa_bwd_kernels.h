@@ -223,7 +223,9 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_dkdv(BwdParams p) {
         const int q0 = t * QT;
 
         if constexpr (SEQ) {
-            const bool need_mask = MASK || (q0 + QT > Sq) || (kw0 + 32 > Sk) || (CAUSAL && kw0 + 31 > q0 + diag);
+            // sequence ends and the causal diagonal only on the tiles they
+            // cross; the mask bytes on every tile
+            const bool need_bounds = (q0 + QT > Sq) || (kw0 + 32 > Sk) || (CAUSAL && kw0 + 31 > q0 + diag);
             const int kl = 32 * w + lq;                    // key within the block
             // One score accumulator at a time (the dK^T, dV^T accumulators
             // fill the AGPRs): S, then P and dV^T += dO^T (P Z c), then dP
@@ -262,12 +264,12 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_dkdv(BwdParams p) {
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * a + e;
                     float x = s[r] * c2 - l4[e];
-                    if (need_mask) {
+                    if (need_bounds) {
                         const int qi = q0 + qr + e;
-                        bool vis = qi < Sq && key < Sk && (!CAUSAL || key <= qi + diag);
-                        if constexpr (MASK) vis = vis && mrow[(8 * a + e) * kKeyBlock] != 0;
+                        const bool vis = qi < Sq && key < Sk && (!CAUSAL || key <= qi + diag);
                         x = vis ? x : -__builtin_inff();
                     }
+                    if constexpr (MASK) x = mrow[(8 * a + e) * kKeyBlock] != 0 ? x : -__builtin_inff();
                     if constexpr (DROP) zb |= ((krow[(8 * a + e) * (kKeyBlock / 8)] >> (kl & 7)) & 1u) << r;
                     s[r] = __builtin_amdgcn_exp2f(x);
                 }
@@ -568,19 +570,21 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_dq(BwdParams p) {
             __builtin_amdgcn_sched_group_barrier(MFMA, AH, 0);
         }
 
-        const bool need_mask = MASK || (kt0 + KT > Sk) || (qw0 + 32 > Sq) || (CAUSAL && kt0 + KT - 1 > qw0 + diag);
+        // sequence ends and the causal diagonal only on the tiles they
+        // cross; the mask bytes on every tile
+        const bool need_bounds = (kt0 + KT > Sk) || (qw0 + 32 > Sq) || (CAUSAL && kt0 + KT - 1 > qw0 + diag);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float pv = __builtin_amdgcn_exp2f(s[rb][r] * c2 - lse2);
-                if (need_mask) {
+                float x = s[rb][r] * c2 - lse2;
+                if (need_bounds) {
                     const int kj = kt0 + 32 * rb + 8 * (r >> 2) + 4 * g + (r & 3);
-                    bool vis = qi < Sq && kj < Sk && (!CAUSAL || kj <= qi + diag);
-                    if constexpr (MASK) vis = vis && ((mk[rb][r >> 2] >> (8 * (r & 3))) & 0xffu) != 0;
-                    pv = vis ? pv : 0.0f;
+                    const bool vis = qi < Sq && kj < Sk && (!CAUSAL || kj <= qi + diag);
+                    x = vis ? x : -__builtin_inff();
                 }
-                s[rb][r] = pv;
+                if constexpr (MASK) x = ((mk[rb][r >> 2] >> (8 * (r & 3))) & 0xffu) != 0 ? x : -__builtin_inff();
+                s[rb][r] = __builtin_amdgcn_exp2f(x);
             }
         }
         if constexpr (MASK) {
