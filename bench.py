@@ -49,7 +49,7 @@ HBM_PEAK_GBS = 8000.0
 # The fused kernel and its parameter block: the HBM counters in profiles/ stay
 # valid while these are unchanged.
 KERNEL_SOURCES = ["tiled_attention_15_amd/csrc/fa_fwd_kernel.h", "tiled_attention_15_amd/csrc/fa_fwd_kernel.hip",
-                  "tiled_attention_15_amd/csrc/fa_launch.h"]
+                  "tiled_attention_15_amd/csrc/fa_launch.h", "tiled_attention_15_amd/csrc/fa_tile.h"]
 
 
 def kernel_source_hash():
