@@ -34,10 +34,12 @@ def make_mask(kind, B, H, Sq, Sk, seed):
     if kind is None:
         return None, None
     ld = (Sk + 3) // 4 * 4
-    if kind == "per_head":
+    if kind in ("per_head", "per_head_bytes"):
         m = np.zeros((B, H, Sq, ld), np.uint8)
         m[..., :Sk] = rng.random((B, H, Sq, Sk)) < 0.7
         m[0, 0, min(2, Sq - 1), :] = 0                  # a row with no visible key
+        if kind == "per_head_bytes":                    # any nonzero byte keeps
+            m *= rng.integers(1, 256, size=m.shape, dtype=np.uint8)
         return m, (H * Sq * ld, Sq * ld, ld)
     m = np.zeros((Sq, ld + 4), np.uint8)
     m[:, :Sk] = rng.random((Sq, Sk)) < 0.85
@@ -73,6 +75,12 @@ CASES = [
     (1, 1, 100, 300, 128, True, "f16", "shared", 0.2),
     (1, 1, 300, 100, 64, True, "bf16", "per_head", 0.1),
     (2, 2, 130, 67, 128, False, "f16", None, 0.3),
+    # mask only and dropout only on shapes with interior tiles (where the
+    # bounds and causal tests are skipped) and ragged edges
+    (1, 2, 190, 333, 128, True, "bf16", "per_head_bytes", 0.0),
+    (2, 1, 129, 260, 128, False, "f16", "shared", 0.0),
+    (1, 3, 260, 260, 64, False, "f16", None, 0.2),
+    (1, 2, 333, 190, 64, True, "bf16", "shared", 0.0),
 ]
 
 

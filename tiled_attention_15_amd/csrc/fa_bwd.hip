@@ -22,18 +22,27 @@
 //   dQ_i = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i.
 //
 // Kernels:
-//   bwd_pre   D_i for every row;
-//   bwd_dkdv  one workgroup per 128-key block (32 keys per wave, K and V of
-//             those keys resident in registers); 64-query tiles of Q and dO
-//             stream through LDS (double-buffered, staged through registers);
-//             per tile S = Q K^T and dP = dO V^T on the matrix cores (queries
-//             on MFMA rows, keys on columns), P and dS in fp32 registers, then
-//             dV^T += dO^T P and dK^T += Q^T dS with P and dS taken straight
-//             from the accumulators as B operands and dO^T, Q^T read from LDS
-//             by transposing reads (ds_read_b64_tr_b16);
-//   bwd_dq    one workgroup per 128-query block (32 queries per wave, Q and
-//             dO resident); 64-key tiles of K and V stream through LDS;
-//             S^T = K Q^T, dP^T = V dO^T, then dQ^T += K^T dS^T.
+//   bwd_pre      D_i for every row;
+//   bwd_dkdv_pp  (D = 128, no mask or dropout) one workgroup of 8 waves per
+//                256-key block: two groups of four waves (128 keys each, 32
+//                per wave) alternate between a matrix phase (dV^T += dO^T P,
+//                dK^T += Q^T dS of the previous 32-query tile, then S = Q K^T
+//                and dP = dO V^T of this one) and an elementwise phase (P and
+//                dS), as the forward's two groups do; Q/dO tiles and their
+//                lse and D_i stream through a three-stage LDS ring shared by
+//                both groups;
+//   bwd_dkdv     (D = 64, D = 256, and with a mask or dropout) one workgroup of
+//                4 waves per 128-key block with the same products per tile and
+//                a double-buffered Q/dO ring;
+//   bwd_dq       one workgroup per 128-query block (32 queries per wave, Q and
+//                dO resident); 64-key tiles of K and V stream through LDS;
+//                S^T = K Q^T, dP^T = V dO^T, then dQ^T += K^T dS^T.
+// In the dK/dV kernels the key block sits in LDS and V of a wave's 32 keys in
+// registers; queries are on MFMA rows and keys on columns for S and dP; P and
+// dS go from the accumulators, packed to 16 bits, straight into the B
+// operands of dV^T and dK^T, whose A operands dO^T and Q^T come from LDS by
+// transposing reads (ds_read_b64_tr_b16).  All tiles are loaded straight into
+// LDS (buffer_load ... lds).
 //
 // The operand layouts and LDS helpers are in fa_tile.h.
 #include "fa_bwd_kernels.h"

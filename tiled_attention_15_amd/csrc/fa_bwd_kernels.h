@@ -452,6 +452,259 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_dkdv(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// dK, dV of one 256-key block at D = 128 without mask or dropout: eight
+// waves in two groups of four (group g owns keys 128g .. 128g + 127 of the
+// block, 32 per wave; waves w and w + 4 share a SIMD) that alternate, as the
+// forward does, between a matrix phase and an elementwise phase:
+//   matrix phase of tile t:  dV^T += dO_{t-1}^T P_{t-1}, dK^T += Q_{t-1}^T dS_{t-1}
+//                            (the previous tile's probabilities), then
+//                            S_t = Q_t K^T and dP_t = dO_t V^T;
+//   elementwise phase of t:  P_t = exp2(S_t scale log2 e - lse log2 e) (0 where
+//                            hidden), dS_t = P_t (dP_t - D_i), both packed.
+// While one wave of a SIMD runs its matrix phase the other runs its
+// elementwise phase; a workgroup barrier separates the phases.  Group 0 runs
+// the matrix phase of tile t in half-step 2(t - t0), group 1 one half-step
+// later, so the 32-query tiles of Q and dO (and their lse and D_i) are shared
+// by both groups through a ring of three LDS stages: tiles t - 1 and t are
+// read during half-steps 2(t - t0) and 2(t - t0) + 1, and group 1 loads tile
+// t + 1 straight into the third stage at the start of its elementwise phase
+// in half-step 2(t - t0), waiting for it before the barrier that ends
+// half-step 2(t - t0) + 1.  The key block sits in LDS (K fragments read at
+// each use), V of a wave's 32 keys in registers, as in bwd_dkdv.
+template <int D, int DT, bool CAUSAL>
+__global__ __launch_bounds__(512) void bwd_dkdv_pp(BwdParams p) {
+    constexpr int DC = D / 16;
+    constexpr int DB = D / 32;
+    constexpr int QT = kQueryTile;
+    constexpr int KBP = 256;                           // keys per workgroup
+    constexpr int TILE = QT * D * 2;                   // bytes of one Q or dO tile
+    constexpr int TN = QT * D / 8 / 256;               // direct loads per thread of a group per tile
+    constexpr int KHALF = 128 * D * 2;                 // bytes of a group's 128 keys
+    constexpr int KN = 128 * D / 8 / 256;
+    constexpr int NST = 3;
+    static_assert(TN >= 1 && KN >= 1, "tile must split over the threads");
+    static_assert(D <= 128, "two waves per SIMD");
+    __shared__ __attribute__((aligned(16))) char smem[2 * KHALF + NST * 2 * TILE];
+    __shared__ __attribute__((aligned(16))) float lse_s[NST][64];
+    __shared__ __attribute__((aligned(16))) float dv_s[NST][64];
+    lds_t* const sm = (lds_t*)smem;
+
+    const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, g = lane >> 5;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wid >> 2, w4 = wid & 3;
+    int bh, kb;
+    block_order(blockIdx.x, p.nkb, p.BH, false, bh, kb);
+    const int Sq = p.Sq, Sk = p.Sk, diag = p.diag;
+    const int k0 = kb * KBP, kw0 = k0 + 128 * grp + 32 * w4;
+
+    const i32x4 rq = rsrc_words(head_of(p.q, p.Lq, bh, p.H), head_bytes<D>(p.Lq, Sq));
+    const i32x4 rdo = rsrc_words(head_of(p.dout, p.Ldo, bh, p.H), head_bytes<D>(p.Ldo, Sq));
+    const i32x4 rk = rsrc_words(head_of(p.k, p.Lk, bh, p.H), head_bytes<D>(p.Lk, Sk));
+    const __amdgpu_buffer_rsrc_t rv = rsrc(head_of(p.v, p.Lv, bh, p.H), head_bytes<D>(p.Lv, Sk));
+    const i32x4 rl_w = rsrc_words(p.lse + (int64_t)bh * Sq, (uint64_t)Sq * 4);
+    const i32x4 rdv_w = rsrc_words(p.dvec + (int64_t)bh * Sq, (uint64_t)Sq * 4);
+
+    const uint32_t lds0 = (uint32_t)(uintptr_t)sm;
+    const lds_t* kblk = sm + KHALF * grp;              // this group's 128 keys
+    // each group loads its own 128 keys (keys past Sk read as zero)
+    tile_dma<D, KN>(rk, k0 + 128 * grp, p.Lk.ss, lds0 + (uint32_t)(KHALF * grp), w4, lane);
+    i32x4 vf[DC];
+#pragma unroll
+    for (int c = 0; c < DC; ++c)
+        vf[c] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((kw0 + lq) * p.Lv.ss + 16 * c + 8 * g) * 2, 0, 0);
+
+    const int nqt = (Sq + QT - 1) / QT;
+    int t0 = 0;
+    if (CAUSAL) t0 = min(nqt, max(0, k0 - diag) / QT);
+
+    // tile t's Q, dO, lse and D_i into stage t % 3 (group 1's waves)
+    auto issue = [&](int t) {
+        const int st = t % NST;
+        const uint32_t base = lds0 + (uint32_t)(2 * KHALF + st * 2 * TILE);
+        tile_dma<D, TN>(rq, t * QT, p.Lq.ss, base, w4, lane);
+        tile_dma<D, TN>(rdo, t * QT, p.Ldo.ss, base + TILE, w4, lane);
+        if (w4 == 0) {
+            lds_dma4(rl_w, (uint32_t)((t * QT + lane) * 4), (uint32_t)(uintptr_t)(lds_t*)&lse_s[st][0]);
+            lds_dma4(rdv_w, (uint32_t)((t * QT + lane) * 4), (uint32_t)(uintptr_t)(lds_t*)&dv_s[st][0]);
+        }
+    };
+
+    const TrLane tl = tr_lane(lane);
+    const FragXor<D> fo(lane, tl);
+    const float c2 = p.scale_log2e;
+    const int key = kw0 + lq;
+    f32x16 dva[DB], dka[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+        dva[b] = zero16();
+        dka[b] = zero16();
+    }
+    f32x16 s = zero16(), dp = zero16();
+    i32x4 pa[QT / 16], da[QT / 16];
+
+    constexpr int MFMA = 0x008, DSR = 0x100;
+    // matrix phase: products of tile tp = t - 1 (if any) with the packed
+    // P, dS, then S and dP of tile t (if any)
+    auto mphase = [&](int tp, int t) {
+        __builtin_amdgcn_s_setprio(1);
+        if (tp >= t0) {
+            // stage bases kept opaque: base + offset sums are formed per
+            // phase, not held for all three stages
+            uint32_t ta = (uint32_t)(uintptr_t)(sm + 2 * KHALF + (tp % NST) * 2 * TILE);
+            asm volatile("" : "+s"(ta));
+            const lds_t* tq = (const lds_t*)(uintptr_t)ta;
+            const lds_t* tdo = tq + TILE;
+#pragma unroll
+            for (int st = 0; st < QT / 16; ++st) {
+#pragma unroll
+                for (int b = 0; b < DB; ++b) {
+                    dva[b] = mma<DT>(fo.tr(tdo, st, b), pa[st], dva[b]);
+                    dka[b] = mma<DT>(fo.tr(tq, st, b), da[st], dka[b]);
+                }
+            }
+            constexpr int N = 2 * DB * (QT / 16), AH = 4;
+            __builtin_amdgcn_sched_group_barrier(DSR, 2 * AH, 1);
+#pragma unroll
+            for (int m = 0; m < N - AH; ++m) {
+                __builtin_amdgcn_sched_group_barrier(MFMA, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(DSR, 2, 1);
+            }
+            __builtin_amdgcn_sched_group_barrier(MFMA, AH, 1);
+        }
+        if (t < nqt) {
+            uint32_t ta = (uint32_t)(uintptr_t)(sm + 2 * KHALF + (t % NST) * 2 * TILE);
+            uint32_t ka = (uint32_t)(uintptr_t)(kblk + 32 * w4 * 2 * D);
+            asm volatile("" : "+s"(ta), "+s"(ka));
+            const lds_t* tq = (const lds_t*)(uintptr_t)ta;
+            const lds_t* tdo = tq + TILE;
+            const lds_t* kw = (const lds_t*)(uintptr_t)ka;
+            s = zero16();
+            dp = zero16();
+#pragma unroll
+            for (int c = 0; c < DC; ++c) s = mma<DT>(fo.row(tq, 0, c), fo.row(kw, 0, c), s);
+#pragma unroll
+            for (int c = 0; c < DC; ++c) dp = mma<DT>(fo.row(tdo, 0, c), vf[c], dp);
+            constexpr int AH = 2;
+            __builtin_amdgcn_sched_group_barrier(DSR, 2 * AH, 0);
+#pragma unroll
+            for (int m = 0; m < DC - AH; ++m) {
+                __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(DSR, 2, 0);
+            }
+#pragma unroll
+            for (int m = DC - AH; m < 2 * DC - AH; ++m) {
+                __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(DSR, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(MFMA, AH, 0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+    };
+    // elementwise phase of tile t
+    auto ephase = [&](int t) {
+        const int st = t % NST, q0 = t * QT;
+        const bool need_mask = (q0 + QT > Sq) || (kw0 + 32 > Sk) || (CAUSAL && kw0 + 31 > q0 + diag);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const int qr = 8 * a + 4 * g;
+            const f32x4 l4 = *(const f32x4*)&lse_s[st][qr] * LOG2E;
+            const f32x4 d4 = *(const f32x4*)&dv_s[st][qr];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * a + e;
+                float x = s[r] * c2 - l4[e];
+                if (need_mask) {
+                    const int qi = q0 + qr + e;
+                    const bool vis = qi < Sq && key < Sk && (!CAUSAL || key <= qi + diag);
+                    x = vis ? x : -__builtin_inff();
+                }
+                const float pv = __builtin_amdgcn_exp2f(x);
+                s[r] = pv;
+                dp[r] = pv * (dp[r] - d4[e]);
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < QT / 16; ++h) {
+            pa[h] = acc_frag<DT>(s, h);
+            da[h] = acc_frag<DT>(dp, h);
+        }
+    };
+    auto barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto publish = [&]() {                             // this wave's loads done, then the barrier
+        wait_vmcnt<0>();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
+
+    // Prologue: tile t0 (group 1) and the key block (both).  Then step t
+    // (t0 <= t <= nqt) is two half-steps: group 0 runs the matrix phase
+    // (tiles t - 1, t) and then the elementwise phase of tile t; group 1 first
+    // requests tile t + 1 and runs the elementwise phase of tile t - 1, then
+    // the matrix phase (tiles t - 1, t).  Each group runs its own loop with
+    // the same barriers; the first and last steps are peeled off.
+    if (grp == 1 && t0 < nqt) issue(t0);
+    publish();
+    if (t0 < nqt) {
+        if (grp == 0) {
+            mphase(t0 - 1, t0);
+            barrier();
+            ephase(t0);
+            publish();
+            for (int t = t0 + 1; t < nqt; ++t) {
+                mphase(t - 1, t);
+                barrier();
+                ephase(t);
+                publish();
+            }
+            mphase(nqt - 1, nqt);
+            barrier();
+            publish();
+        } else {
+            if (t0 + 1 < nqt) issue(t0 + 1);
+            barrier();
+            mphase(t0 - 1, t0);
+            publish();
+            for (int t = t0 + 1; t < nqt; ++t) {
+                if (t + 1 < nqt) issue(t + 1);
+                ephase(t - 1);
+                barrier();
+                mphase(t - 1, t);
+                publish();
+            }
+            ephase(nqt - 1);
+            barrier();
+            mphase(nqt - 1, nqt);
+            publish();
+        }
+    }
+
+    // dK^T (times scale) and dV^T: as in bwd_dkdv
+    const __amdgpu_buffer_rsrc_t wk = rsrc(head_of(p.dk, p.Ldk, bh, p.H), head_bytes<D>(p.Ldk, Sk));
+    const __amdgpu_buffer_rsrc_t wv = rsrc(head_of(p.dv, p.Ldv, bh, p.H), head_bytes<D>(p.Ldv, Sk));
+    const float sc = p.scale;
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const uint32_t offk = (uint32_t)((key * p.Ldk.ss + 32 * b + 8 * a + 4 * g) * 2);
+            const uint32_t offv = (uint32_t)((key * p.Ldv.ss + 32 * b + 8 * a + 4 * g) * 2);
+            i32x2 kv, vv;
+            kv[0] = pack2<DT>(dka[b][4 * a] * sc, dka[b][4 * a + 1] * sc);
+            kv[1] = pack2<DT>(dka[b][4 * a + 2] * sc, dka[b][4 * a + 3] * sc);
+            vv[0] = pack2<DT>(dva[b][4 * a], dva[b][4 * a + 1]);
+            vv[1] = pack2<DT>(dva[b][4 * a + 2], dva[b][4 * a + 3]);
+            __builtin_amdgcn_raw_buffer_store_b64(kv, wk, offk, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(vv, wv, offv, 0, 0);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // dQ of one 128-query block.
 template <int D, int DT, bool CAUSAL, bool MASK = false, bool DROP = false>
 __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_dq(BwdParams p) {
@@ -673,8 +926,15 @@ static hipError_t run(const BwdParams& p, hipStream_t st) {
         else run_masked<D, DT, CAUSAL, false, true>(p, st);
         return hipGetLastError();
     }
-    if (p.Sk > 0)
-        hipLaunchKernelGGL((bwd_dkdv<D, DT, CAUSAL>), dim3((unsigned)(p.BH * p.nkb)), dim3(256), 0, st, p);
+    if (p.Sk > 0) {
+        if constexpr (D == 128) {
+            BwdParams q = p;
+            q.nkb = (p.Sk + 255) / 256;
+            hipLaunchKernelGGL((bwd_dkdv_pp<D, DT, CAUSAL>), dim3((unsigned)(q.BH * q.nkb)), dim3(512), 0, st, q);
+        } else {
+            hipLaunchKernelGGL((bwd_dkdv<D, DT, CAUSAL>), dim3((unsigned)(p.BH * p.nkb)), dim3(256), 0, st, p);
+        }
+    }
     if (rows > 0)
         hipLaunchKernelGGL((bwd_dq<D, DT, CAUSAL>), dim3((unsigned)(p.BH * p.nqb)), dim3(256), 0, st, p);
     return hipGetLastError();
