@@ -580,23 +580,21 @@ __global__ __launch_bounds__(512) void bwd_dkdv_pp(BwdParams p) {
             const lds_t* kw = (const lds_t*)(uintptr_t)ka;
             s = zero16();
             dp = zero16();
+            // the S and dP chains interleaved (independent accumulators back
+            // to back), three LDS reads per pair two pairs ahead
 #pragma unroll
-            for (int c = 0; c < DC; ++c) s = mma<DT>(fo.row(tq, 0, c), fo.row(kw, 0, c), s);
-#pragma unroll
-            for (int c = 0; c < DC; ++c) dp = mma<DT>(fo.row(tdo, 0, c), vf[c], dp);
+            for (int c = 0; c < DC; ++c) {
+                s = mma<DT>(fo.row(tq, 0, c), fo.row(kw, 0, c), s);
+                dp = mma<DT>(fo.row(tdo, 0, c), vf[c], dp);
+            }
             constexpr int AH = 2;
-            __builtin_amdgcn_sched_group_barrier(DSR, 2 * AH, 0);
+            __builtin_amdgcn_sched_group_barrier(DSR, 3 * AH, 0);
 #pragma unroll
             for (int m = 0; m < DC - AH; ++m) {
-                __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(DSR, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(MFMA, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(DSR, 3, 0);
             }
-#pragma unroll
-            for (int m = DC - AH; m < 2 * DC - AH; ++m) {
-                __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(DSR, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(MFMA, AH, 0);
+            __builtin_amdgcn_sched_group_barrier(MFMA, 2 * AH, 0);
         }
         __builtin_amdgcn_s_setprio(0);
     };
