@@ -148,6 +148,23 @@ __device__ __forceinline__ int drop_pair(int pw, uint32_t r, uint32_t tm1x2, uin
     return out;
 }
 
+// The first two steps of drop_pair alone: 1 in each 16-bit half whose random
+// half is >= t, 0 elsewhere (a keep multiplier, applied by keep_apply).
+__device__ __forceinline__ uint32_t keep_mult(uint32_t r, uint32_t tm1x2, uint32_t ones) {
+    uint32_t out;
+    asm("v_pk_sub_u16 %0, %1, %2 clamp\n\t"
+        "v_pk_min_u16 %0, %0, %3"
+        : "=&v"(out)
+        : "v"(r), "s"(tm1x2), "s"(ones));
+    return out;
+}
+// The last step of drop_pair: the packed probabilities times their multipliers.
+__device__ __forceinline__ int keep_apply(int pw, uint32_t km) {
+    int out;
+    asm("v_pk_mul_lo_u16 %0, %1, %2" : "=v"(out) : "v"(pw), "v"(km));
+    return out;
+}
+
 // Value of the partner lane (l ^ 32) combined with our own: returns both halves.
 __device__ __forceinline__ float xmax32(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -407,6 +424,11 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
         for (int i = 0; i < 16; ++i) oacc[b][i] = 0.0f;
     f32x16 s[2];
     i32x4 pf[4];
+    // Dropout without a mask or key split: the keep multipliers of a tile are
+    // drawn in the matrix phase that computes its scores (where the vector
+    // unit has slack) instead of in its softmax phase.
+    constexpr bool KEEP_EARLY = DROP && !SPLIT && !DSPLIT && !MASK;
+    uint32_t km[4][4];
     float m_run = -INFINITY;
     float l_run = 0.0f;     // running sum of the probabilities (fp32): the lse
     float r_run = 0.0f;     // running sum of the probabilities as rounded for P V: O's divisor
@@ -562,7 +584,12 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) rsum = dot2_ones<DT>(pf[c][e], rsum);
         r_run += rsum;
-        if constexpr (DROP) {
+        if constexpr (KEEP_EARLY) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pf[j][e] = keep_apply(pf[j][e], km[j][e]);
+        } else if constexpr (DROP) {
             // keys t*BC + 32*kb2 + 16*g + 8*u + 0..7 (registers 8u..8u+7 of
             // s[kb2], i.e. pf[2*kb2 + u]) form the Philox block at counter
             // (8t + 4kb2 + 2g + u, query, bh, offset); word e decides the
@@ -609,12 +636,31 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
         }
         __builtin_amdgcn_sched_group_barrier(MFMA, AHEAD, 0);
     };
+    // keys t*BC + 32*kb2 + 16*g + 8*u + 0..7 form the Philox block at
+    // counter (8t + 4kb2 + 2g + u, query, bh, offset), as in swork
+    auto make_keep = [&](int t) {
+        if constexpr (KEEP_EARLY) {
+            const uint32_t tm1 = p.drop_t - 1u;
+            const uint32_t tm1x2 = tm1 | (tm1 << 16);
+            const uint32_t c0 = (uint32_t)(8 * t + 2 * g);
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    uint32_t c[4] = {c0 + 4 * kb2 + u, (uint32_t)(qw0 + lq), (uint32_t)bh, p.offset};
+                    tile::philox4x32_10(c, p.seed_lo, p.seed_hi);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) km[2 * kb2 + u][e] = keep_mult(c[e], tm1x2, 0x00010001u);
+                }
+        }
+    };
     // matrix phase: O += P_tp V_tp, then S = K_t Q^T
     auto mphase2 = [&](int tp, int t) {
         __builtin_amdgcn_s_setprio(1);
         pv(tp);
         qk(t);
         mphase_schedule();
+        make_keep(t);
         __builtin_amdgcn_s_setprio(0);
     };
     auto mphase = [&](int t) { mphase2(t - 1, t); };
@@ -1082,6 +1128,7 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
     // Step nt: the last O += P V.
     if (grp == 0) {
         qk(0);
+        make_keep(0);
         mid_barrier();
         if constexpr (MASK) mask_scores();
         if (nt > 2) issue_tile(2);
@@ -1103,6 +1150,7 @@ __global__ __launch_bounds__(512) void fa_fwd_kernel(FwdParams p) {
         if (nt > 2) issue_tile(2);
         mid_barrier();
         qk(0);
+        make_keep(0);
         end_barrier(0, false);
         for (int t = 1; t < nt; ++t) {
             if constexpr (MASK) mask_scores();
