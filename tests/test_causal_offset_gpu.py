@@ -133,6 +133,8 @@ BWD_CASES = [
     (1, 2, 230, 150, 64, "f16", False, 0.0, (-100, 0, 40)),
     (1, 2, 190, 300, 128, "bf16", True, 0.2, (-200, 5, 310)),
     (1, 2, 130, 130, 256, "bf16", False, 0.1, (0, -20)),
+    # plain D = 128: the 256-key dK/dV blocks, whose second half starts later
+    (1, 2, 300, 420, 128, "bf16", False, 0.0, (-150, 0, 120, 400)),
 ]
 
 
