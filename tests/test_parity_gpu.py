@@ -5,7 +5,8 @@ The workload shapes run in the launch configuration the benchmark uses,
 with NaN-filled outputs so that an unwritten element fails, and are
 compared on every row (on the 16384-long workload: every row of eight heads
 and 512 rows of each other head).  The unsplit 256-row instance is also
-checked on ragged, unequal-length and strided shapes.
+checked on ragged, unequal-length and strided shapes, and on long shapes
+whose heads the schedule groups per XCD.
 """
 import math
 
@@ -161,6 +162,56 @@ def test_unsplit_instance_ragged(case):
                                          dtype=dtype)
     st = parity.assert_parity(og.reshape(-1, D)[rows], lg.reshape(-1)[rows], o_ref, l_ref, dtype, str(case))
     say("  ", rows.size, "rows", st)
+
+
+# Long D = 128 shapes whose heads the schedule groups per XCD (B*H a multiple
+# of 8, 32 query blocks of 256 rows per head): every block of every head
+# lands exactly once, under the causal and the non-causal rule, with batch
+# > 1, a ragged last block and a [B, S, H, D] view.
+XCD_GROUPED_CASES = [
+    # (B, H, S, dtype, causal, layout)
+    (2, 16, 8000, "bf16", True, "bshd"),
+    (1, 32, 8192, "f16", False, "bhsd"),
+    (4, 8, 7990, "f16", True, "bhsd"),
+]
+
+
+@pytest.mark.parametrize("case", XCD_GROUPED_CASES, ids=["%dx%dx%d%s%s%s" % (c[0], c[1], c[2], c[3], "c" if c[4] else "n",
+                                                                         c[5]) for c in XCD_GROUPED_CASES])
+def test_xcd_grouped_every_block(case):
+    B, H, S, dtype, causal, layout = case
+    D = 128
+    assert fa.fa_fwd_plan(B, H, S, D, causal, fa.BF16 if dtype == "bf16" else fa.F16)[0] == 256
+    say("case xcd grouped", case)
+    q, k, v = make_inputs(B, H, S, D, dtype, seed=4100 + S + H, q_mult=2.0)
+    if layout == "bshd":
+        qd, kd, vd = (t.transpose(1, 2).contiguous().to(DEV).transpose(1, 2) for t in (q, k, v))
+        o = torch.full((B, S, H, D), float("nan"), dtype=q.dtype, device=DEV).transpose(1, 2)
+    else:
+        qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+        o = torch.full((B, H, S, D), float("nan"), dtype=q.dtype, device=DEV)
+    lse = torch.full((B, H, S), float("nan"), dtype=torch.float32, device=DEV)
+    fa.forward(qd, kd, vd, causal=causal, out=o, lse_out=lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all().item(), "an output element is unwritten or not finite"
+    assert torch.isfinite(lse).all().item(), "an lse element is unwritten or not finite"
+    og, lg = to64(o.contiguous()), to64(lse)
+    # every row of two heads (on different XCDs), and in every head the first
+    # and last row of each 256-row block plus 32 random rows
+    rng = np.random.default_rng(S + H)
+    BH = B * H
+    full = [0, BH - 3]
+    rows = [h * S + np.arange(S) for h in full]
+    edges = np.unique(np.clip(np.concatenate([np.arange(0, S, 256), np.arange(255, S + 255, 256)]), 0, S - 1))
+    for h in range(BH):
+        if h not in full:
+            rows.append(h * S + np.concatenate([edges, rng.choice(S, 32, replace=False)]))
+    rows = np.unique(np.concatenate(rows)).astype(np.int64)
+    o_ref, l_ref = oracle.attention_rows(bits(q), bits(k), bits(v), rows, scale=softmax_scale(D), causal=causal,
+                                         dtype=dtype)
+    st = parity.assert_parity(og.reshape(-1, D)[rows], lg.reshape(-1)[rows], o_ref, l_ref, dtype, str(case))
+    say("  ", rows.size, "rows", st)
+
 
 
 def test_pages_fp16_bound_on_llama_shape():
