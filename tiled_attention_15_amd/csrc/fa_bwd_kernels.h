@@ -764,11 +764,15 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_dq(BwdParams p) {
     // K and V tiles go straight from global memory into the LDS buffers
     // (no staging registers); a step waits for its successor's loads just
     // before the closing barrier.
+    // (one per-lane offset per swizzle class and tensor: the offsets of every
+    // load held in registers across the loop spilled in the masked and
+    // dropout variants)
     const uint32_t lds0 = (uint32_t)(uintptr_t)sm;
+    const TileDma<D, CPT> dmk(p.Lk.ss, w, lane), dmv(p.Lv.ss, w, lane);
     auto issue = [&](int t, int buf) {
         const uint32_t base = lds0 + (uint32_t)(buf * 2 * TILE);
-        tile_dma<D, CPT>(rk, t * KT, p.Lk.ss, base, w, lane);
-        tile_dma<D, CPT>(rv, t * KT, p.Lv.ss, base + TILE, w, lane);
+        dmk.issue(rk, t * KT, base, w);
+        dmv.issue(rv, t * KT, base + TILE, w);
     };
 
     const TrLane tl = tr_lane(lane);
