@@ -2,11 +2,11 @@
 
 Each case draws batch, heads, query and key lengths, head dimension, dtype,
 causality, a mask (none, per head or shared) and a dropout probability from
-a fixed generator, so the sweep reaches the tuned kernel's key-split and
-masked instances and its head-dimension split (D = 256), the general kernel
-(dropout), and strided [B, S, H, D] views, with ragged lengths throughout.
-Its small grids (B*H <= 8) always take the key-split route; the unsplit
-256-row instance is checked on ragged shapes by test_parity_gpu.py.
+a fixed generator, so the sweep reaches the tuned kernel's key-split,
+masked and dropout instances and its pair split (D = 256), and strided
+[B, S, H, D] views, with ragged lengths throughout.  Its small grids
+(B*H <= 8) always take the key-split route at D <= 128; the unsplit 256-row
+instance is checked on ragged shapes by test_parity_gpu.py.
 """
 import numpy as np
 import pytest
