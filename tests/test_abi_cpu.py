@@ -278,7 +278,7 @@ def test_ext_rejects_bad_arguments(lib):
 
 
 def test_plan_d256_uses_128_row_blocks(lib):
-    """D = 256: 128-row blocks (the head-dimension split) of 64-key tiles."""
+    """D = 256: 128-row blocks (the pair split) of 64-key tiles."""
     for causal in (0, 1):
         br, bc, grid, tiles = fa.fa_fwd_plan(2, 3, 1000, 256, causal, 1)
         assert (br, bc) == (128, 64)
@@ -416,4 +416,4 @@ def test_split_is_chosen_for_small_grids(lib):
     assert fa.fa_fwd_plan(1, 33, 1024, 128, False, 1)[0] == 256    # 132 blocks, non-causal: no split
     assert fa.fa_fwd_plan(1, 33, 1024, 128, True, 1)[0] == 128     # causal, fewer blocks than CUs
     assert fa.fa_fwd_plan(1, 64, 1024, 128, True, 1)[0] == 256     # 256 blocks
-    assert fa.fa_fwd_plan(1, 2, 2048, 256, True, 1)[0] == 128      # D = 256: the general kernel's blocks
+    assert fa.fa_fwd_plan(1, 2, 2048, 256, True, 1)[0] == 128      # D = 256: the pair split's blocks

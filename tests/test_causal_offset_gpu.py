@@ -42,7 +42,7 @@ def shared_mask(Sq, Sk, seed):
 
 
 # (B, H, Sq, Sk, D, dtype, mask, p, offsets); the 1x2 grids take the key
-# split, 2x130x300 the unsplit 256-row instance, D = 256 the head-dimension split
+# split, 2x130x300 the unsplit 256-row instance, D = 256 the pair split
 CASES = [
     (1, 2, 300, 200, 64, "f16", False, 0.0, (-305, -40, 0, 17)),
     (1, 2, 170, 420, 128, "bf16", True, 0.2, (0, 250, 425)),

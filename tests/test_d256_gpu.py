@@ -1,7 +1,7 @@
 """GPU parity of head dimension 256 against the fp64 oracle: the forward
-(the general kernel behind fa_fwd, fa_fwd_strided and fa_fwd_ext at
-D = 256) and the backward (fa_bwd / fa_bwd_strided kernels at D = 256, both
-dQ modes, with a mask and dropout, on strided views)."""
+(the tuned kernel's pair split behind fa_fwd, fa_fwd_strided and
+fa_fwd_ext at D = 256) and the backward (fa_bwd / fa_bwd_strided kernels at
+D = 256, with a mask and dropout, on strided views)."""
 import numpy as np
 import pytest
 import torch

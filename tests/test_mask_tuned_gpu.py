@@ -72,7 +72,7 @@ CASES = [
     (2, 2, 257, 131, 128, False, "bf16", True, 0),
     (1, 3, 1, 1, 128, False, "f16", False, 0),
     (1, 1, 45, 1029, 64, False, "bf16", False, 12),
-    (1, 2, 300, 400, 256, True, "bf16", False, 4),      # D = 256: the head-dimension split
+    (1, 2, 300, 400, 256, True, "bf16", False, 4),      # D = 256: the pair split
     (2, 1, 257, 257, 256, False, "f16", True, 0),
 ]
 

@@ -173,8 +173,8 @@ static int launch_tuned(const void* q, const void* k, const void* v, void* o, fl
     p.H = H;
     p.BH = B * H;
     const bool split = use_split(B, H, Sq, D, causal != 0, fa::compute_units());
-    // 128-row blocks for the key-split instances and at D = 256 (the
-    // head-dimension split: both wave groups on the same rows)
+    // 128-row blocks for the key-split instances and at D = 256 (the pair
+    // split: 64 rows per wave group, each pair of waves on 32 of them)
     const int br = (split || D == 256) ? fa::kBlockQSplit : fa::kBlockQ;
     p.nqb = (Sq + br - 1) / br;
     p.diag = diag_of(Sq, Sk, causal_offset);
@@ -232,7 +232,7 @@ int fa_fwd_plan(int B, int H, int S, int D, int causal, int dtype, int* block_q,
     int st = validate_shape(B, H, S, S, D, dtype);
     if (st == FA_OK && !head_span_ok(S, D, D)) st = FA_ERR_SHAPE;
     if (st != FA_OK) return st;
-    // 128-row blocks at D = 256 (head-dimension split) and on small grids
+    // 128-row blocks at D = 256 (pair split) and on small grids
     // (key split)
     const int br = (D == 256 || use_split(B, H, S, D, causal != 0, fa::compute_units())) ? fa::kBlockQSplit
                                                                                          : fa::kBlockQ;
