@@ -83,8 +83,9 @@ typedef enum {
  *   D        head dimension, 64, 128 or 256 (named among the head
  *            dimensions of "FlashAttention-2 on Ascend NPU" (2048ai.net),
  *            tiling parameters).  D = 256 runs the tuned kernel with
- *            128-row blocks whose two wave groups split the head dimension
- *            (each computes the full scores and accumulates half of O).
+ *            128-row blocks: each wave group owns 64 rows, and each pair
+ *            of its waves shares 32 of them, one wave per half of every
+ *            key tile's scores and per half of O's columns.
  *   scale    softmax scale applied to q.k (callers normally pass
  *            1/sqrt(D)); finite and > 0.
  *   causal   0: every key visible; nonzero: key j visible to query i iff
@@ -157,7 +158,7 @@ int fa_version(void);
  *
  * Fills (each pointer may be NULL):
  *   block_q    query rows per workgroup (B_r): 256; 128 at D = 256 (the
- *              head-dimension split), and at
+ *              pair split), and at
  *              D = 64 or 128 when n = B * H * ceil(S / 256) satisfies
  *              2n <= C, or n < C for a causal call, C the current device's
  *              compute-unit count (256 on MI355X) (the key-split
