@@ -162,3 +162,69 @@ def test_bwd_packed_gradients_are_rejected():
     with pytest.raises(fa.FaError) as e:
         fa.backward(qd, kd, vd, o, lse, gd, grads=grads)
     assert e.value.status == 7
+
+
+def test_offsets_at_the_edge_of_the_32_bit_reach():
+    """Row stride 2,790,000 elements, S = 256, D = 128: a head's rows span
+    1.42e9 bytes, and the rows its tiles address past the sequence end (read
+    as zero, never stored) reach 2.14e9 bytes, just under the 2^31-byte limit
+    of the buffer offsets in the forward and in the backward (which rounds a
+    head up to whole 128-key blocks plus one).  The forward, the backward and
+    the masked/dropout backward equal the contiguous calls bit for bit and
+    match the oracle."""
+    B, H, S, D, dtype = 1, 1, 256, 128, "bf16"
+    r = 2_790_000
+    # inside both reaches, within 8192 elements of stride of the backward's
+    assert (320 * r + D) * 2 < 2 ** 31 and (384 * r + D) * 2 < 2 ** 31 <= (384 * (r + 8192) + D) * 2
+    say("case 32-bit reach, row stride", r)
+    q, k, v, g = grad_inputs(B, H, S, S, D, dtype, seed=3600)
+    n = (S - 1) * r + D
+    bufs = []
+
+    def wide(t=None, like=q):
+        buf = torch.zeros(n, dtype=like.dtype, device=DEV)
+        bufs.append(buf)
+        view = buf.as_strided((B, H, S, D), (S * r, S * r, r, 1))
+        if t is not None:
+            view.copy_(t.to(DEV))
+        return view
+
+    qv, kv, vv, gv = (wide(t) for t in (q, k, v, g))
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
+
+    # forward and plain backward (causal)
+    ov = wide()
+    _, lse = fa.forward(qv, kv, vv, causal=True, out=ov)
+    grads = (wide(), wide(), wide())
+    fa.backward(qv, kv, vv, ov, lse, gv, causal=True, grads=grads)
+    oc, lc = fa.forward(qd, kd, vd, causal=True)
+    ref = fa.backward(qd, kd, vd, oc, lc, gd, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ov, oc) and torch.equal(lse, lc)
+    for name, a, b in zip(("dq", "dk", "dv"), grads, ref):
+        assert torch.equal(a, b), name
+    o_ref, l_ref = oracle.attention_fwd(bits(q), bits(k), bits(v), scale=softmax_scale(D), causal=True, dtype=dtype)
+    parity.assert_parity(to64(ov), to64(lse), o_ref, l_ref, dtype, "forward at the edge of the reach")
+    refs = oracle.attention_bwd(bits(q), bits(k), bits(v), bits(g), scale=softmax_scale(D), causal=True,
+                                dtype=dtype)
+    check_oracle(grads, refs, dtype, "backward at the edge of the reach", zero_scales(q, k, v, g, D, dtype))
+
+    # masked/dropout backward (the other dK/dV kernel), non-causal
+    rng = np.random.default_rng(3650)
+    mask = (rng.random((S, S)) < 0.8).astype(np.uint8)
+    md = torch.from_numpy(mask).to(DEV)
+    kw = dict(causal=False, mask=md, dropout_p=0.1, seed=7, offset=3)
+    oe, le = fa.forward_ext(qd, kd, vd, **kw)
+    ov.copy_(oe)
+    grads = (wide(), wide(), wide())
+    fa.backward_ext(qv, kv, vv, ov, le, gv, grads=grads, **kw)
+    ref = fa.backward_ext(qd, kd, vd, oe, le, gd, **kw)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), grads, ref):
+        assert torch.equal(a, b), name
+    refs = oracle.attention_bwd_ext(bits(q), bits(k), bits(v), bits(g), scale=softmax_scale(D), causal=False,
+                                    dtype=dtype, mask=mask, mask_strides=(0, 0, S), dropout_p=0.1, seed=7,
+                                    offset=3)
+    check_oracle(grads, refs, dtype, "masked/dropout backward at the edge of the reach",
+                 zero_scales(q, k, v, g, D, dtype, 0.1))
+    del bufs
