@@ -152,3 +152,67 @@ def assert_grad_parity(g_gpu, g_ref, dtype, what="", zero_tol=None):
     st = compare_grad(g_gpu, g_ref, dtype, zero_tol)
     assert grad_ok(st), "gradient parity failed %s: %s" % (what, st)
     return st
+
+
+def operand_rounding_bounds(q, k, v, dout, o, lse, scale, causal, dtype):
+    """Per-element absolute bounds on the gradients' error, for inputs whose
+    gradients cancel far below the size of their terms (where the slice-wide
+    rule above, calibrated on N(0,1) inputs, does not apply).  Same model:
+    each product takes one factor rounded to the input dtype (dS for dQ and
+    dK, P for dV; relative error u); the recomputed P carries the fp32 error
+    of its score and of the stored lse,
+        e_ij = (D + 2) 2^-24 scale sum_d |q_id k_jd| + 4 * 2^-24 max(1, |lse_i|);
+    and D_i = dO_i . O_i is formed from the stored output, rounded to the
+    dtype and carrying the forward's own rounding of P,
+        dO_id = ulp(O_id)/2 + 2 u sum_j P_ij |v_jd|,
+        dD_i  = sum_d |dO_id| dO_id + (D + 2) 2^-24 sum_d |dO_id O_id|
+    (dO_id here the error of O, beside the output gradient dO_id).  Both
+    reach dS through dS = P (dP - D_i).  With
+        w_ij = u |dS_ij| + e_ij P_ij |dP_ij - D_i| + P_ij dD_i:
+        dQ_id <= scale sum_j w_ij |k_jd|,   dK_jd <= scale sum_i w_ij |q_id|,
+        dV_jd <= sum_i (u + e_ij) P_ij |dO_id|.
+    P, dP, D_i and dS are recomputed here in fp64 from the inputs and the
+    oracle's O and lse (bottom-right causal rule).  Inputs [B, H, S, D];
+    returns {"dq", "dk", "dv"} arrays shaped like the gradients."""
+    as64 = lambda t: np.asarray(t.float().numpy() if hasattr(t, "float") else t, dtype=np.float64)
+    qa, ka, va, ga = as64(q), as64(k), as64(v), as64(dout)
+    oa = np.asarray(o, dtype=np.float64)
+    la = np.asarray(lse, dtype=np.float64)
+    Sq, Sk, D = qa.shape[-2], ka.shape[-2], qa.shape[-1]
+    kt = np.swapaxes(ka, -1, -2)
+    s = scale * np.matmul(qa, kt)
+    if causal:
+        vis = np.arange(Sk)[None, :] <= np.arange(Sq)[:, None] + (Sk - Sq)
+        s = np.where(vis, s, -np.inf)
+    with np.errstate(invalid="ignore", over="ignore"):
+        p = np.where(np.isneginf(s), 0.0, np.exp(s - la[..., None]))
+    p = np.nan_to_num(p, nan=0.0)
+    dp = np.matmul(ga, np.swapaxes(va, -1, -2))
+    di = np.sum(p * dp, axis=-1, keepdims=True)
+    ds = p * (dp - di)
+    u = GRAD_U[dtype]
+    e = (D + 2) * 2.0 ** -24 * scale * np.matmul(np.abs(qa), np.abs(kt)) + \
+        4 * 2.0 ** -24 * np.maximum(1.0, np.abs(np.nan_to_num(la, neginf=0.0)))[..., None]
+    o_err = 0.5 * ulp(oa, dtype) + 2.0 * u * np.matmul(p, np.abs(va))
+    d_err = np.sum(np.abs(ga) * o_err, axis=-1, keepdims=True) + \
+        (D + 2) * 2.0 ** -24 * np.sum(np.abs(ga * oa), axis=-1, keepdims=True)
+    w = u * np.abs(ds) + e * p * np.abs(dp - di) + p * d_err
+    return {"dq": scale * np.matmul(w, np.abs(ka)),
+            "dk": scale * np.matmul(np.swapaxes(w, -1, -2), np.abs(qa)),
+            "dv": np.matmul(np.swapaxes((u + e) * p, -1, -2), np.abs(ga))}
+
+
+def assert_grad_within_bound(g_gpu, g_ref, bound, dtype, what=""):
+    """|G_gpu - G_ref| <= 2 bound + 3 u max|G_ref| (per (batch, head) slice)
+    plus half an output ulp, elementwise, and no NaN or infinity."""
+    g = np.asarray(g_gpu, dtype=np.float64)
+    r = np.asarray(g_ref, dtype=np.float64)
+    b = np.asarray(bound, dtype=np.float64)
+    assert np.isfinite(g).all(), "non-finite gradient %s" % what
+    u = GRAD_U[dtype]
+    m = np.max(np.abs(r), axis=(-2, -1), keepdims=True)
+    excess = np.abs(g - r) - 0.5 * ulp(r, dtype) - (2.0 * b + GRAD_MAX_C * u * m)
+    worst = float(np.max(excess))
+    ratio = float(np.max(np.abs(g - r) / (2.0 * b + GRAD_MAX_C * u * m + 0.5 * ulp(r, dtype) + 1e-300)))
+    assert worst <= 0.0, "gradient beyond its rounding bound %s: worst excess %.3e, ratio %.3f" % (what, worst, ratio)
+    return {"ratio_to_bound": ratio}
