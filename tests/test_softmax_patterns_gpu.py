@@ -20,9 +20,10 @@ noise from the other channels.  Patterns of f over the key index:
 
 Each pattern runs on small grids (the key-split instance), on grids of more
 than 256 blocks (the 256-row instance) and at D = 256, causal and not, f16
-and bf16; the backward (which recomputes the probabilities from the saved
-lse) runs on the small grids, each gradient element held to the bound of
-the operand rounding (parity.operand_rounding_bounds).
+and bf16 (the masked and dropout instances on two of them); the backward
+(which recomputes the probabilities from the saved lse) runs on the small
+grids, each gradient element held to the bound of the operand rounding
+(parity.operand_rounding_bounds).
 """
 import numpy as np
 import pytest
@@ -139,3 +140,33 @@ def test_running_max_patterns_backward(shape, pattern):
     for name, got, ref in zip(("dq", "dk", "dv"), grads, refs):
         st = parity.assert_grad_within_bound(to64(got), ref, bnd[name], dtype, "%s %s %s" % (name, pattern, shape))
         say("  ", name, st)
+
+
+@pytest.mark.parametrize("pattern", PATTERNS)
+@pytest.mark.parametrize("shape", [SHAPES[0], SHAPES[2]], ids=["1x2x700x700x128bf16c", "1x130x333x333x128f16c"])
+def test_running_max_patterns_masked_dropout(shape, pattern):
+    """The masked and dropout instances on the same profiles: a shared mask
+    keeping 80% of the scores (-inf entries among the maxima) and dropout
+    0.1 applied to the probabilities after the softmax."""
+    B, H, Sq, Sk, D, dtype, causal = shape
+    say("case softmax pattern masked/dropout", pattern, shape)
+    q, k, v = shaped_inputs(B, H, Sq, Sk, D, dtype, pattern, seed=5400 + Sq + Sk + H)
+    mask = (np.random.default_rng(5450 + Sq).random((Sq, Sk)) < 0.8).astype(np.uint8)
+    kw = dict(causal=causal, mask=torch.from_numpy(mask).to(DEV), dropout_p=0.1, seed=17, offset=5)
+    o, lse = fa.forward_ext(q.to(DEV), k.to(DEV), v.to(DEV), **kw)
+    torch.cuda.synchronize()
+    og, lg = to64(o), to64(lse)
+    BH = B * H
+    if BH <= 2:
+        rows = np.arange(BH * Sq, dtype=np.int64)
+    else:
+        rng = np.random.default_rng(Sq + Sk + 1)
+        rows = [h * Sq + np.arange(Sq) for h in (0, BH - 1)]
+        rows += [h * Sq + rng.choice(Sq, 24, replace=False) for h in range(1, BH - 1)]
+        rows = np.unique(np.concatenate(rows)).astype(np.int64)
+    o_ref, l_ref = oracle.attention_fwd_ext(bits(q), bits(k), bits(v), scale=softmax_scale(D), causal=causal,
+                                            dtype=dtype, mask=mask, mask_strides=(0, 0, Sk), dropout_p=0.1,
+                                            seed=17, offset=5, rows=rows)
+    st = parity.assert_parity(og.reshape(-1, D)[rows], lg.reshape(-1)[rows], o_ref, l_ref, dtype,
+                              "masked/dropout %s %s" % (pattern, shape))
+    say("  ", rows.size, "rows", st)
