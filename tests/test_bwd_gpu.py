@@ -1,6 +1,6 @@
-"""GPU parity of the attention backward (fa_bwd, both dq modes) against the
-fp64 oracle's backward: full gradients on small and ragged shapes, sampled
-rows at workload sizes, determinism, and that every output element is
+"""GPU parity of the attention backward (fa_bwd) against the fp64 oracle's
+backward: full gradients on small and ragged shapes, rows of every head at
+the workload sizes, determinism, and that every output element is
 written."""
 import numpy as np
 import pytest
@@ -106,27 +106,41 @@ def test_bwd_overwrites_stale_outputs_and_workspace():
         parity.assert_grad_parity(to64(got), r, "f16", name)
 
 
-@pytest.mark.parametrize("name", ["gpt_causal_2x12x2048x64_f16", "llama_noncausal_1x32x2048x128_f16",
-                                  "long_causal_1x32x8192x128_bf16_q4"])
-def test_bwd_workload_sampled_rows(name):
-    """At the workload sizes, sampled dq rows (any head) and dk/dv rows (of two
-    heads: each needs a full pass over its head in the oracle)."""
+@pytest.mark.parametrize("name", [n for n in WORKLOADS if not n.startswith("tiny")])
+def test_bwd_workload_every_head(name):
+    """At the workload sizes, in the benchmark's launch configuration: the
+    three gradients pre-filled with NaN and every element written and finite;
+    12 dQ rows of every head (plus the first and last row of head 0) and 16
+    dK/dV rows (plus the first and last key) of eight heads, one from each
+    XCD's share when B*H is a multiple of 8 (each such head costs the oracle
+    a full forward over it), against the oracle."""
     w = WORKLOADS[name]
     q, k, v = workload_inputs(w)
     g, _, _ = make_inputs(w.B, w.H, w.S, w.D, w.dtype, seed=w.seed + 1000)
     say("case bwd workload", name)
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
+    o, lse = fa.forward(qd, kd, vd, causal=w.causal, scale=w.scale)
+    grads = tuple(torch.full_like(t, float("nan")) for t in (qd, kd, vd))
+    fa.backward(qd, kd, vd, o, lse, gd, causal=w.causal, scale=w.scale, grads=grads)
+    torch.cuda.synchronize()
+    for nm, t in zip(("dq", "dk", "dv"), grads):
+        assert torch.isfinite(t).all().item(), "%s: an element is unwritten or not finite" % nm
     rng = np.random.default_rng(11)
-    BH = w.B * w.H
-    qrows = np.sort(rng.choice(BH * w.S, size=96, replace=False)).astype(np.int64)
-    heads = rng.choice(BH, size=2, replace=False)
-    krows = np.sort(np.concatenate([h * w.S + rng.choice(w.S, size=24, replace=False) for h in heads]
-                                   + [np.array([heads[0] * w.S, heads[0] * w.S + w.S - 1])]))
-    krows = np.unique(krows).astype(np.int64)
+    BH, S = w.B * w.H, w.S
+    qrows = [h * S + rng.choice(S, size=12, replace=False) for h in range(BH)] + [np.array([0, S - 1])]
+    qrows = np.unique(np.concatenate(qrows)).astype(np.int64)
+    if BH % 8 == 0:
+        hpx = BH // 8
+        heads = [x * hpx + x % hpx for x in range(8)]
+    else:
+        heads = sorted(set(int(h) for h in rng.choice(BH, size=min(BH, 8), replace=False)))
+    krows = [h * S + np.concatenate([rng.choice(S, size=16, replace=False), [0, S - 1]]) for h in heads]
+    krows = np.unique(np.concatenate(krows)).astype(np.int64)
     rq, rk, rv = oracle.attention_bwd_rows(bits(q), bits(k), bits(v), bits(g), qrows, krows,
                                            scale=w.scale, causal=w.causal, dtype=w.dtype)
     # the tolerance is relative to each gradient's magnitude over the sampled rows
-    dq, dk, dv = gpu_grads(q, k, v, g, w.causal, scale=w.scale)
-    for nm, got, ref, rows in (("dq", dq, rq, qrows), ("dk", dk, rk, krows), ("dv", dv, rv, krows)):
+    for nm, got, ref, rows in (("dq", grads[0], rq, qrows), ("dk", grads[1], rk, krows),
+                               ("dv", grads[2], rv, krows)):
         sel = to64(got).reshape(-1, w.D)[rows]
         st = parity.assert_grad_parity(sel[None, None], ref[None, None], w.dtype, "%s %s" % (nm, name))
-        say("  ", nm, st)
+        say("  ", nm, rows.size, "rows", st)
