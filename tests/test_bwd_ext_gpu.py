@@ -7,7 +7,7 @@ import torch
 import oracle
 from oracle import parity
 import tiled_attention_15_amd as fa
-from workloads import bits, make_inputs, softmax_scale
+from workloads import WORKLOADS, bits, make_inputs, softmax_scale, workload_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -129,3 +129,36 @@ def test_bwd_ext_medium_sampled_rows():
     for nm, got, ref, rows in (("dq", dq, rq, qrows), ("dk", dk, rk, krows), ("dv", dv, rv, krows)):
         sel = to64(got).reshape(-1, D)[rows]
         say("  ", nm, parity.assert_grad_parity(sel[None, None], ref[None, None], "bf16", "medium " + nm))
+
+
+def test_bwd_ext_headline_size_every_head():
+    """The long causal workload (1x32x8192x128 bf16, Q x4) with one [S, S]
+    mask shared by all heads (90% kept) and dropout 0.1, as the benchmark
+    times it: gradients pre-filled with NaN and every element written and
+    finite; 8 dQ rows of every head and 12 dK/dV rows (plus the first and last
+    key) of four heads on different XCDs, against the oracle."""
+    w = WORKLOADS["long_causal_1x32x8192x128_bf16_q4"]
+    q, k, v = workload_inputs(w)
+    g, _, _ = make_inputs(w.B, w.H, w.S, w.D, w.dtype, seed=w.seed + 1000)
+    S, BH = w.S, w.B * w.H
+    mask = (np.random.default_rng(3900).random((S, S)) < 0.9).astype(np.uint8)
+    say("case bwd_ext headline size")
+    kw = dict(causal=True, scale=w.scale, mask=torch.from_numpy(mask).to(DEV), dropout_p=0.1, seed=77, offset=9)
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
+    o, lse = fa.forward_ext(qd, kd, vd, **kw)
+    grads = tuple(torch.full_like(t, float("nan")) for t in (qd, kd, vd))
+    fa.backward_ext(qd, kd, vd, o, lse, gd, grads=grads, **kw)
+    torch.cuda.synchronize()
+    for nm, t in zip(("dq", "dk", "dv"), grads):
+        assert torch.isfinite(t).all().item(), "%s: an element is unwritten or not finite" % nm
+    rng = np.random.default_rng(3901)
+    qrows = np.unique(np.concatenate([h * S + rng.choice(S, size=8, replace=False) for h in range(BH)]))
+    krows = np.unique(np.concatenate([h * S + np.concatenate([rng.choice(S, size=12, replace=False), [0, S - 1]])
+                                      for h in (0, 9, 18, 27)]))
+    rq, rk, rv = oracle.attention_bwd_ext(bits(q), bits(k), bits(v), bits(g), scale=w.scale, causal=True,
+                                          dtype=w.dtype, mask=mask, mask_strides=(0, 0, S), dropout_p=0.1, seed=77,
+                                          offset=9, qrows=qrows.astype(np.int64), krows=krows.astype(np.int64))
+    for nm, got, ref, rows in (("dq", grads[0], rq, qrows), ("dk", grads[1], rk, krows), ("dv", grads[2], rv, krows)):
+        sel = to64(got).reshape(-1, w.D)[rows]
+        say("  ", nm, rows.size, "rows", parity.assert_grad_parity(sel[None, None], ref[None, None], w.dtype,
+                                                                  "headline " + nm))
