@@ -53,8 +53,8 @@ def run_ext(q, k, v, causal, dtype, mask, ms, p, seed, offset):
     B, H, Sq, D = q.shape
     Sk = k.shape[2]
     md = None if mask is None else torch.from_numpy(mask).to(DEV)
-    o = torch.empty_like(qd)
-    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=DEV)
+    o = torch.full_like(qd, float("nan"))          # unwritten elements stay NaN
+    lse = torch.full((B, H, Sq), float("nan"), dtype=torch.float32, device=DEV)
     st = fa.fa_fwd_ext(qd, kd, vd, o, lse, B, H, Sq, Sk, D, md, ms, p, seed, offset,
                        softmax_scale(D), causal, fa.BF16 if dtype == "bf16" else fa.F16, None)
     assert st == 0, fa.fa_status_string(st)
@@ -129,9 +129,10 @@ def test_ext_plain_is_the_plain_forward(D):
             assert torch.equal(l1, l2)
 
 
-def test_ext_workload_sampled_rows():
+def test_ext_workload_every_head():
     """The long causal workload (1x32x8192x128 bf16, Q x4) with a shared random
-    mask (90% kept) and dropout 0.1: sampled rows against the oracle."""
+    mask (90% kept) and dropout 0.1: every output element written, rows of
+    every head against the oracle."""
     w = WORKLOADS["long_causal_1x32x8192x128_bf16_q4"]
     q, k, v = workload_inputs(w)
     S = w.S
@@ -140,7 +141,10 @@ def test_ext_workload_sampled_rows():
     ms = (0, 0, S)
     say("case ext workload", w.name)
     o, lse = run_ext(q, k, v, w.causal, w.dtype, mask, ms, 0.1, 77, 0)
-    rows = np.sort(rng.choice(w.B * w.H * S, size=192, replace=False)).astype(np.int64)
+    assert not torch.isnan(o).any().item() and not torch.isnan(lse).any().item(), "unwritten output"
+    # 8 random rows of every head, and the first and last row of head 0
+    rows = np.unique(np.concatenate([h * S + rng.choice(S, size=8, replace=False) for h in range(w.B * w.H)]
+                                    + [np.array([0, S - 1])])).astype(np.int64)
     o_ref, l_ref = oracle.attention_fwd_ext(bits(q), bits(k), bits(v), scale=w.scale, causal=w.causal,
                                             dtype=w.dtype, mask=mask, mask_strides=ms, dropout_p=0.1,
                                             seed=77, offset=0, rows=rows)

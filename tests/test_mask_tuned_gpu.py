@@ -53,8 +53,8 @@ def run(q, k, v, causal, dtype, mask, ms):
     B, H, Sq, D = q.shape
     Sk = k.shape[2]
     md = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask)).to(DEV)
-    o = torch.empty_like(qd)
-    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=DEV)
+    o = torch.full_like(qd, float("nan"))          # unwritten elements stay NaN
+    lse = torch.full((B, H, Sq), float("nan"), dtype=torch.float32, device=DEV)
     st = fa.fa_fwd_ext(qd, kd, vd, o, lse, B, H, Sq, Sk, D, md, ms, 0.0, 0, 0, softmax_scale(D), causal,
                        fa.BF16 if dtype == "bf16" else fa.F16, None)
     assert st == 0, fa.fa_status_string(st)
@@ -148,10 +148,10 @@ def test_masked_strided_views():
     parity.assert_parity(to64(o), to64(lse), o_ref, l_ref, dtype, "masked strided")
 
 
-def test_masked_workload_sampled_rows():
+def test_masked_workload_every_head():
     """The long causal workload (1x32x8192x128 bf16, Q x4) with one shared
-    random mask (90% kept), launched as the benchmark does: sampled rows
-    against the oracle."""
+    random mask (90% kept), launched as the benchmark does: every output
+    element written, rows of every head against the oracle."""
     w = WORKLOADS["long_causal_1x32x8192x128_bf16_q4"]
     q, k, v = workload_inputs(w)
     S = w.S
@@ -160,7 +160,10 @@ def test_masked_workload_sampled_rows():
     ms = (0, 0, S)
     say("case masked tuned workload", w.name)
     o, lse = run(q, k, v, w.causal, w.dtype, mask, ms)
-    rows = np.sort(rng.choice(w.B * w.H * S, size=192, replace=False)).astype(np.int64)
+    assert not torch.isnan(o).any().item() and not torch.isnan(lse).any().item(), "unwritten output"
+    # 8 random rows of every head, and the first and last row of head 0
+    rows = np.unique(np.concatenate([h * S + rng.choice(S, size=8, replace=False) for h in range(w.B * w.H)]
+                                    + [np.array([0, S - 1])])).astype(np.int64)
     o_ref, l_ref = oracle.attention_fwd_ext(bits(q), bits(k), bits(v), scale=w.scale, causal=w.causal,
                                             dtype=w.dtype, mask=mask, mask_strides=ms, rows=rows)
     st = parity.assert_parity(to64(o).reshape(-1, w.D)[rows], to64(lse).reshape(-1)[rows], o_ref, l_ref,
