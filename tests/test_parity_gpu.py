@@ -320,3 +320,56 @@ def test_wrong_scale_is_detected():
     o_ref, l_ref = oracle.attention_fwd(bits(q), bits(k), bits(v), scale=softmax_scale(D),
                                         causal=False, dtype="f16")
     assert not parity.ok(parity.compare(to64(o), to64(lse), o_ref, l_ref, "f16"))
+
+
+def test_cross_attention_text_context():
+    """Cross attention of image tokens over a short text context (the pages'
+    application to a diffusion model's cross attention): 2x10 heads, 4096
+    queries over 77 keys, D = 64, fp16, non-causal; one ragged key tile per
+    block.  Every output compared with the oracle."""
+    B, H, Sq, Sk, D = 2, 10, 4096, 77, 64
+    say("case cross attention", B, H, Sq, Sk, D)
+    q, k, v = make_inputs(B, H, max(Sq, Sk), D, "f16", seed=4700, Sk=Sk)
+    q = q[:, :, :Sq].contiguous()
+    o = torch.full((B, H, Sq, D), float("nan"), dtype=q.dtype, device=DEV)
+    lse = torch.full((B, H, Sq), float("nan"), dtype=torch.float32, device=DEV)
+    fa.forward(q.to(DEV), k.to(DEV), v.to(DEV), causal=False, out=o, lse_out=lse)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_fwd(bits(q), bits(k), bits(v), scale=softmax_scale(D), causal=False, dtype="f16")
+    st = parity.assert_parity(to64(o), to64(lse), o_ref, l_ref, "f16", "cross attention")
+    say("  ", st)
+
+
+def test_long_sequence_65536():
+    """One 65,536-token causal sequence (1x4 heads, D = 128, bf16): outputs
+    and the backward's three gradients pre-filled with NaN and every element
+    written; 64 rows of O and 24 rows of dQ in every head against the oracle
+    (dK and dV rows would each need a full oracle forward of a head)."""
+    B, H, S, D = 1, 4, 65536, 128
+    say("case long sequence", B, H, S, D)
+    q, k, v = make_inputs(B, H, S, D, "bf16", seed=4800)
+    g, _, _ = make_inputs(B, H, S, D, "bf16", seed=4801)
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
+    o = torch.full((B, H, S, D), float("nan"), dtype=q.dtype, device=DEV)
+    lse = torch.full((B, H, S), float("nan"), dtype=torch.float32, device=DEV)
+    fa.forward(qd, kd, vd, causal=True, out=o, lse_out=lse)
+    grads = tuple(torch.full_like(t, float("nan")) for t in (qd, kd, vd))
+    fa.backward(qd, kd, vd, o, lse, gd, causal=True, grads=grads)
+    torch.cuda.synchronize()
+    for nm, t in (("o", o), ("lse", lse), ("dq", grads[0]), ("dk", grads[1]), ("dv", grads[2])):
+        assert torch.isfinite(t).all().item(), "%s: an element is unwritten or not finite" % nm
+    rng = np.random.default_rng(4802)
+    rows = np.unique(np.concatenate([h * S + np.concatenate([rng.choice(S, size=64, replace=False), [0, S - 1]])
+                                     for h in range(B * H)])).astype(np.int64)
+    o_ref, l_ref = oracle.attention_rows(bits(q), bits(k), bits(v), rows, scale=softmax_scale(D), causal=True,
+                                         dtype="bf16")
+    st = parity.assert_parity(to64(o).reshape(-1, D)[rows], to64(lse).reshape(-1)[rows], o_ref, l_ref, "bf16",
+                              "long sequence")
+    say("  ", rows.size, "rows", st)
+    qrows = np.unique(np.concatenate([h * S + rng.choice(S, size=24, replace=False) for h in range(B * H)]))
+    rq, _, _ = oracle.attention_bwd_rows(bits(q), bits(k), bits(v), bits(g), qrows.astype(np.int64),
+                                         np.array([], dtype=np.int64), scale=softmax_scale(D), causal=True,
+                                         dtype="bf16")
+    sel = to64(grads[0]).reshape(-1, D)[qrows]
+    st = parity.assert_grad_parity(sel[None, None], rq[None, None], "bf16", "long sequence dq")
+    say("   dq", qrows.size, "rows", st)
