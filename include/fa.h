@@ -98,6 +98,12 @@ typedef enum {
  * rounded to `dtype` before the second product; O rounded to `dtype` with
  * round-to-nearest-even.  Results are bitwise reproducible run to run (no
  * atomics).  Non-finite inputs propagate to the outputs they touch.
+ * Domain: an exponent is formed as scale*log2(e)*s - m in one fused
+ * multiply-add, m the row maximum in fp32, so it carries m's rounding,
+ * up to half an fp32 ulp of m.  That stays below the probabilities'
+ * 16-bit rounding while |scale * q.k| is below about 8,000 (natural-log
+ * units; attention scores in practice are below a few hundred).  Far
+ * beyond, at about 1e9, exponentials overflow and outputs are not finite.
  *
  * Returns an fa_status.  Asynchronous: a fault inside the kernel surfaces at
  * the caller's next synchronisation, not here.

@@ -373,3 +373,48 @@ def test_long_sequence_65536():
     sel = to64(grads[0]).reshape(-1, D)[qrows]
     st = parity.assert_grad_parity(sel[None, None], rq[None, None], "bf16", "long sequence dq")
     say("   dq", qrows.size, "rows", st)
+
+
+EXTREME_CASES = [
+    # (dtype, factor on q and k, causal, shape (B, H, S, D)).  A factor of 20
+    # gives scores of up to ~4,500 (natural-log units), inside the domain the
+    # C header states for the fused exponent arguments, and one-hot rows.
+    ("f16", 20.0, False, (1, 2, 400, 128)),
+    ("f16", 20.0, True, (1, 132, 333, 64)),
+    ("f16", 1e-6, False, (1, 2, 400, 128)),     # subnormal fp16 inputs: scores ~0, uniform rows
+    ("bf16", 20.0, True, (1, 2, 400, 128)),
+    ("bf16", 1e-30, True, (1, 132, 333, 64)),   # products underflow fp32: uniform rows
+]
+
+
+@pytest.mark.parametrize("case", EXTREME_CASES, ids=["%s-%g-%s-%dx%d" % (c[0], c[1], "c" if c[2] else "n", c[3][1],
+                                                                          c[3][2]) for c in EXTREME_CASES])
+def test_extreme_input_magnitudes(case):
+    """q and k (uniform on (-1, 1)) scaled far from unit size, V uniform on
+    (-1, 1): scores of thousands whose softmax is one-hot, or so small that
+    it is uniform.  No NaN or infinity anywhere and the oracle's rows within the
+    rule."""
+    dtype, f, causal, (B, H, S, D) = case
+    say("case extreme magnitudes", case)
+    q, k, v = make_inputs(B, H, S, D, dtype, seed=4900 + S + H, dist="uniform")
+    td = q.dtype
+    q, k = (q.float() * f).to(td), (k.float() * f).to(td)
+    assert torch.isfinite(q.float()).all() and torch.isfinite(k.float()).all()
+    o = torch.full((B, H, S, D), float("nan"), dtype=td, device=DEV)
+    lse = torch.full((B, H, S), float("nan"), dtype=torch.float32, device=DEV)
+    fa.forward(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, out=o, lse_out=lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+    BH = B * H
+    if BH <= 2:
+        rows = np.arange(BH * S, dtype=np.int64)
+    else:
+        rng = np.random.default_rng(S + H)
+        rows = [h * S + np.arange(S) for h in (0, BH - 1)]
+        rows += [h * S + rng.choice(S, 16, replace=False) for h in range(1, BH - 1)]
+        rows = np.unique(np.concatenate(rows)).astype(np.int64)
+    o_ref, l_ref = oracle.attention_rows(bits(q), bits(k), bits(v), rows, scale=softmax_scale(D), causal=causal,
+                                         dtype=dtype)
+    st = parity.assert_parity(to64(o).reshape(-1, D)[rows], to64(lse).reshape(-1)[rows], o_ref, l_ref, dtype,
+                              str(case))
+    say("  ", rows.size, "rows", st)
