@@ -144,3 +144,55 @@ def test_bwd_workload_every_head(name):
         sel = to64(got).reshape(-1, w.D)[rows]
         st = parity.assert_grad_parity(sel[None, None], ref[None, None], w.dtype, "%s %s" % (nm, name))
         say("  ", nm, rows.size, "rows", st)
+
+
+def test_concurrent_streams_and_threads_match_sequential():
+    """Four host threads, each on its own stream (default priority), run the
+    forward and the backward (plain, and with a mask and dropout) on their own
+    inputs at the same time, several times over; every result equals, bit for
+    bit, the same calls made one after another on the default stream.  The
+    library keeps no state shared between calls besides read-only device
+    properties."""
+    import threading
+    shapes = [(1, 4, 700, 128, "bf16", True), (2, 3, 333, 64, "f16", False),
+              (1, 130, 300, 128, "f16", True), (1, 2, 1000, 256, "bf16", True)]
+    say("case concurrent streams", len(shapes))
+    ins = []
+    for i, (B, H, S, D, dtype, causal) in enumerate(shapes):
+        q, k, v, g = grad_inputs(B, H, S, S, D, dtype, seed=5600 + i)
+        m = torch.from_numpy((np.random.default_rng(5650 + i).random((S, S)) < 0.85).astype(np.uint8)).to(DEV)
+        ins.append(tuple(t.to(DEV) for t in (q, k, v, g)) + (m, causal))
+
+    def work(qd, kd, vd, gd, m, causal):
+        o, lse = fa.forward(qd, kd, vd, causal=causal)
+        grads = fa.backward(qd, kd, vd, o, lse, gd, causal=causal)
+        kw = dict(causal=causal, mask=m, dropout_p=0.1, seed=3, offset=1)
+        oe, le = fa.forward_ext(qd, kd, vd, **kw)
+        ge = fa.backward_ext(qd, kd, vd, oe, le, gd, **kw)
+        return (o, lse) + tuple(grads) + (oe, le) + tuple(ge)
+
+    ref = [work(*a) for a in ins]
+    torch.cuda.synchronize()
+    got = [None] * len(ins)
+    errors = []
+
+    def run(i, stream):
+        try:
+            with torch.cuda.stream(stream):
+                for _ in range(3):
+                    got[i] = work(*ins[i])
+            stream.synchronize()
+        except Exception as e:          # reported by the main thread
+            errors.append(e)
+
+    streams = [torch.cuda.Stream() for _ in ins]
+    threads = [threading.Thread(target=run, args=(i, s)) for i, s in enumerate(streams)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(ref, got)):
+        for j, (x, y) in enumerate(zip(a, b)):
+            assert torch.equal(x, y), (shapes[i], j)
