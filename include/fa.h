@@ -32,7 +32,10 @@
  *
  * Threading and ownership: every entry point is stateless and thread-safe.
  * The caller owns every buffer; the library never allocates, frees or
- * synchronises.
+ * synchronises, and it enqueues nothing but kernel launches on the given
+ * stream (no memset or copy), so calls can be captured into a HIP graph and
+ * replayed (the first call on a device reads its compute-unit count once,
+ * outside any stream).
  */
 #ifndef TILED_ATTENTION_15_FA_H
 #define TILED_ATTENTION_15_FA_H
