@@ -30,7 +30,8 @@
  *     (lanjinlin.com.cn), "kernel entry" (unlike that launcher, this one
  *     never synchronises the stream).
  *
- * Threading and ownership: every entry point is stateless and thread-safe.
+ * Threading and ownership: every entry point but fa_bwd_noalloc (whose
+ * calls on one GPU share its scratch array) is stateless and thread-safe.
  * The caller owns every buffer; the library never allocates, frees or
  * synchronises, and it enqueues nothing but kernel launches on the given
  * stream (no memset or copy), so calls can be captured into a HIP graph and
