@@ -7,6 +7,8 @@ masked and dropout instances and its pair split (D = 256), and strided
 [B, S, H, D] views, with ragged lengths throughout.  Its small grids
 (B*H <= 8) always take the key-split route at D <= 128; the unsplit 256-row
 instance is checked on ragged shapes by test_parity_gpu.py.
+24 further draws run the backward of the same routes (backward_ext) against
+the oracle's full backward.
 """
 import numpy as np
 import pytest
@@ -70,3 +72,42 @@ def test_random_shape(c):
                                             dtype=dtype, mask=m, mask_strides=ms, dropout_p=c["p"], seed=5, offset=1)
     st = parity.assert_parity(to64(o), to64(lse), o_ref, l_ref, dtype, "random %s" % (c,))
     print("  ", st, flush=True)
+
+
+BWD_CASES = [draw(100 + i) for i in range(24)]
+
+
+@pytest.mark.parametrize("c", BWD_CASES, ids=["%d:%dx%dx%dx%dx%d%s%s_%s_p%g%s" % (
+    i, c["B"], c["H"], c["Sq"], c["Sk"], c["D"], "c" if c["causal"] else "n", c["dtype"], c["mask"], c["p"],
+    "_strided" if c["strided"] else "") for i, c in enumerate(BWD_CASES)])
+def test_random_shape_backward(c):
+    """The same draws through backward_ext (after forward_ext with the same
+    mask and dropout): every gradient element against the oracle's backward."""
+    print("case backward", c, flush=True)
+    B, H, Sq, Sk, D, dtype = c["B"], c["H"], c["Sq"], c["Sk"], c["D"], c["dtype"]
+    q, k, v = make_inputs(B, H, max(Sq, Sk), D, dtype, seed=9300 + Sq + 7 * Sk + D, Sk=Sk)
+    q = q[:, :, :Sq].contiguous()
+    g, _, _ = make_inputs(B, H, Sq, D, dtype, seed=9400 + Sq + D)
+    rng = np.random.default_rng(9500 + Sq)
+    if c["mask"] == "none":
+        m, ms, mt = None, None, None
+    else:
+        mb, mh = (B, H) if c["mask"] == "per_head" else (1, 1)
+        m = (rng.random((mb, mh, Sq, Sk)) < 0.8).astype(np.uint8)
+        ms = (H * Sq * Sk if mb > 1 else 0, Sq * Sk if mh > 1 else 0, Sk)
+        mt = torch.from_numpy(m).to(DEV)
+        if c["mask"] == "shared":
+            mt = mt[0, 0]
+    args = [t.to(DEV) for t in (q, k, v, g)]
+    if c["strided"]:
+        args = [t.transpose(1, 2).contiguous().transpose(1, 2) for t in args]
+    kw = dict(causal=c["causal"], mask=mt, dropout_p=c["p"], seed=5, offset=1)
+    o, lse = fa.forward_ext(*args[:3], **kw)
+    grads = fa.backward_ext(*args[:3], o, lse, args[3], **kw)
+    torch.cuda.synchronize()
+    refs = oracle.attention_bwd_ext(bits(q), bits(k), bits(v), bits(g), scale=softmax_scale(D), causal=c["causal"],
+                                    dtype=dtype, mask=m, mask_strides=ms, dropout_p=c["p"], seed=5, offset=1)
+    zs = parity.cancellation_tolerances(q, k, v, g, softmax_scale(D), dtype, dropout_p=c["p"])
+    for name, got, ref in zip(("dq", "dk", "dv"), grads, refs):
+        st = parity.assert_grad_parity(to64(got), ref, dtype, "%s random %s" % (name, c), zero_tol=zs[name])
+        print("  ", name, st, flush=True)
