@@ -418,3 +418,35 @@ def test_extreme_input_magnitudes(case):
     st = parity.assert_parity(to64(o).reshape(-1, D)[rows], to64(lse).reshape(-1)[rows], o_ref, l_ref, dtype,
                               str(case))
     say("  ", rows.size, "rows", st)
+
+
+DECODE_CASES = [
+    # (B, H, Sq, Sk, D, dtype): a few new queries against a long key cache
+    # (bottom-right causal rule: query i of Sq sees keys 0 .. Sk - Sq + i),
+    # and a chunk of 512 new queries over an 8192-key context
+    (32, 32, 1, 8192, 128, "bf16"),
+    (8, 32, 16, 8192, 128, "f16"),
+    (4, 16, 7, 4099, 64, "bf16"),
+    (1, 32, 512, 8192, 128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=["%dx%dx%dx%dx%d%s" % c for c in DECODE_CASES])
+def test_decode_and_chunked_prefill_shapes(case):
+    """Serving shapes: every output row against the oracle, outputs
+    pre-filled with NaN."""
+    B, H, Sq, Sk, D, dtype = case
+    say("case decode", case)
+    q, k, v = make_inputs(B, H, max(Sq, Sk), D, dtype, seed=5900 + Sq + H, Sk=Sk)
+    q = q[:, :, :Sq].contiguous()
+    o = torch.full((B, H, Sq, D), float("nan"), dtype=q.dtype, device=DEV)
+    lse = torch.full((B, H, Sq), float("nan"), dtype=torch.float32, device=DEV)
+    fa.forward(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, out=o, lse_out=lse)
+    torch.cuda.synchronize()
+    og, lg = to64(o), to64(lse)
+    assert not np.isnan(og).any() and not np.isnan(lg).any()
+    rows = np.arange(B * H * Sq, dtype=np.int64)
+    o_ref, l_ref = oracle.attention_rows(bits(q), bits(k), bits(v), rows, scale=softmax_scale(D), causal=True,
+                                         dtype=dtype)
+    st = parity.assert_parity(og.reshape(-1, D), lg.reshape(-1), o_ref, l_ref, dtype, str(case))
+    say("  ", rows.size, "rows", st)
