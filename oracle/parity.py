@@ -154,26 +154,30 @@ def assert_grad_parity(g_gpu, g_ref, dtype, what="", zero_tol=None):
     return st
 
 
-def operand_rounding_bounds(q, k, v, dout, o, lse, scale, causal, dtype):
+def operand_rounding_bounds(q, k, v, dout, o, lse, scale, causal, dtype, vis=None, zc=None):
     """Per-element absolute bounds on the gradients' error, for inputs whose
     gradients cancel far below the size of their terms (where the slice-wide
-    rule above, calibrated on N(0,1) inputs, does not apply).  Same model:
-    each product takes one factor rounded to the input dtype (dS for dQ and
-    dK, P for dV; relative error u); the recomputed P carries the fp32 error
-    of its score and of the stored lse,
+    rule above, calibrated on N(0,1) inputs and many visible keys per row,
+    does not apply).  Same model: each product takes one factor rounded to
+    the input dtype (dS for dQ and dK, P for dV; relative error u); the
+    recomputed P carries the fp32 error of its score and of the stored lse,
         e_ij = (D + 2) 2^-24 scale sum_d |q_id k_jd| + 4 * 2^-24 max(1, |lse_i|);
     and D_i = dO_i . O_i is formed from the stored output, rounded to the
     dtype and carrying the forward's own rounding of P,
-        dO_id = ulp(O_id)/2 + 2 u sum_j P_ij |v_jd|,
+        dO_id = ulp(O_id)/2 + 2 u sum_j P_ij zc_ij |v_jd|,
         dD_i  = sum_d |dO_id| dO_id + (D + 2) 2^-24 sum_d |dO_id O_id|
     (dO_id here the error of O, beside the output gradient dO_id).  Both
-    reach dS through dS = P (dP - D_i).  With
-        w_ij = u |dS_ij| + e_ij P_ij |dP_ij - D_i| + P_ij dD_i:
+    reach dS = P (zc dP - D_i), zc the dropout's keep-and-rescale factor
+    (1 without dropout).  With
+        w_ij = u |dS_ij| + e_ij P_ij |zc_ij dP_ij - D_i| + P_ij dD_i:
         dQ_id <= scale sum_j w_ij |k_jd|,   dK_jd <= scale sum_i w_ij |q_id|,
-        dV_jd <= sum_i (u + e_ij) P_ij |dO_id|.
+        dV_jd <= sum_i (u + e_ij) P_ij zc_ij |dO_id|.
     P, dP, D_i and dS are recomputed here in fp64 from the inputs and the
-    oracle's O and lse (bottom-right causal rule).  Inputs [B, H, S, D];
-    returns {"dq", "dk", "dv"} arrays shaped like the gradients."""
+    oracle's O and lse.  vis: optional boolean [.., Sq, Sk] visibility (an
+    explicit mask combined with the causal rule; when None, the
+    bottom-right causal rule if `causal`); zc: optional [.., Sq, Sk] keep
+    factors.  Inputs [B, H, S, D]; returns {"dq", "dk", "dv"} arrays shaped
+    like the gradients."""
     as64 = lambda t: np.asarray(t.float().numpy() if hasattr(t, "float") else t, dtype=np.float64)
     qa, ka, va, ga = as64(q), as64(k), as64(v), as64(dout)
     oa = np.asarray(o, dtype=np.float64)
@@ -181,25 +185,27 @@ def operand_rounding_bounds(q, k, v, dout, o, lse, scale, causal, dtype):
     Sq, Sk, D = qa.shape[-2], ka.shape[-2], qa.shape[-1]
     kt = np.swapaxes(ka, -1, -2)
     s = scale * np.matmul(qa, kt)
-    if causal:
+    if vis is None and causal:
         vis = np.arange(Sk)[None, :] <= np.arange(Sq)[:, None] + (Sk - Sq)
+    if vis is not None:
         s = np.where(vis, s, -np.inf)
     with np.errstate(invalid="ignore", over="ignore"):
         p = np.where(np.isneginf(s), 0.0, np.exp(s - la[..., None]))
     p = np.nan_to_num(p, nan=0.0)
+    z = 1.0 if zc is None else np.asarray(zc, dtype=np.float64)
     dp = np.matmul(ga, np.swapaxes(va, -1, -2))
-    di = np.sum(p * dp, axis=-1, keepdims=True)
-    ds = p * (dp - di)
+    di = np.sum(p * z * dp, axis=-1, keepdims=True)
+    ds = p * (z * dp - di)
     u = GRAD_U[dtype]
     e = (D + 2) * 2.0 ** -24 * scale * np.matmul(np.abs(qa), np.abs(kt)) + \
         4 * 2.0 ** -24 * np.maximum(1.0, np.abs(np.nan_to_num(la, neginf=0.0)))[..., None]
-    o_err = 0.5 * ulp(oa, dtype) + 2.0 * u * np.matmul(p, np.abs(va))
+    o_err = 0.5 * ulp(oa, dtype) + 2.0 * u * np.matmul(p * z, np.abs(va))
     d_err = np.sum(np.abs(ga) * o_err, axis=-1, keepdims=True) + \
         (D + 2) * 2.0 ** -24 * np.sum(np.abs(ga * oa), axis=-1, keepdims=True)
-    w = u * np.abs(ds) + e * p * np.abs(dp - di) + p * d_err
+    w = u * np.abs(ds) + e * p * np.abs(z * dp - di) + p * d_err
     return {"dq": scale * np.matmul(w, np.abs(ka)),
             "dk": scale * np.matmul(np.swapaxes(w, -1, -2), np.abs(qa)),
-            "dv": np.matmul(np.swapaxes((u + e) * p, -1, -2), np.abs(ga))}
+            "dv": np.matmul(np.swapaxes((u + e) * p * z, -1, -2), np.abs(ga))}
 
 
 def assert_grad_within_bound(g_gpu, g_ref, bound, dtype, what=""):

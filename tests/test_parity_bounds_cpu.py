@@ -75,3 +75,42 @@ def test_emulated_rounding_within_bound_and_mistakes_outside(dtype, causal):
     bad = emulate(q, k, v, g, scale, causal, dtype, o, lse, mistake="row_shift")
     with pytest.raises(AssertionError):
         parity.assert_grad_within_bound(bad["dv"], refs["dv"], bnd["dv"], dtype, "row shift")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_bound_with_mask_and_dropout(dtype):
+    """The same with an explicit mask and dropout (keep factors from the
+    Philox pattern of the oracle pins): the emulation, with P Z c in the
+    products, lies within the bound; dS formed without the keep factors
+    does not."""
+    from oracle_pins import _keep_matrix
+    Sq, Sk, D, p, seed, offset = 40, 70, 32, 0.2, 21, 4
+    scale = softmax_scale(D)
+    q, k, v, g = rising_inputs(Sq, Sk, D, dtype, seed=71)
+    m = (np.random.default_rng(72).random((1, 1, Sq, Sk)) < 0.7).astype(np.uint8)
+    ms = (0, 0, Sk)
+    refs = dict(zip(("dq", "dk", "dv"), oracle.attention_bwd_ext(
+        bits(q), bits(k), bits(v), bits(g), scale=scale, causal=True, dtype=dtype, mask=m[0, 0], mask_strides=ms,
+        dropout_p=p, seed=seed, offset=offset)))
+    o, lse = oracle.attention_fwd_ext(bits(q), bits(k), bits(v), scale=scale, causal=True, dtype=dtype, mask=m[0, 0],
+                                      mask_strides=ms, dropout_p=p, seed=seed, offset=offset)
+    vis = (m != 0) & (np.arange(Sk)[None, :] <= np.arange(Sq)[:, None] + (Sk - Sq))
+    zc = _keep_matrix(1, 1, Sq, Sk, seed, offset, p)
+    bnd = parity.operand_rounding_bounds(q, k, v, g, o, lse, scale, True, dtype, vis=vis, zc=zc)
+
+    f = lambda t: t.double().numpy()
+    qa, ka, va, ga = f(q), f(k), f(v), f(g)
+    rnd = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(torch_dtype(dtype)).double().numpy()
+    s = np.where(vis, scale * qa @ np.swapaxes(ka, -1, -2), -np.inf)
+    pm = np.exp(s - lse[..., None])
+    dp = ga @ np.swapaxes(va, -1, -2)
+    di = np.sum(ga * rnd(o), axis=-1, keepdims=True)
+    for name, ds in (("emulated", pm * (zc * dp - di)), ("no keep factor in dS", pm * (dp - di))):
+        emu = {"dq": scale * rnd(ds) @ ka, "dk": scale * np.swapaxes(rnd(ds), -1, -2) @ qa,
+               "dv": np.swapaxes(rnd(pm * zc), -1, -2) @ ga}
+        if name == "emulated":
+            for gname in ("dq", "dk", "dv"):
+                parity.assert_grad_within_bound(emu[gname], refs[gname], bnd[gname], dtype, "emulated " + gname)
+        else:
+            with pytest.raises(AssertionError):
+                parity.assert_grad_within_bound(emu["dq"], refs["dq"], bnd["dq"], dtype, name)
