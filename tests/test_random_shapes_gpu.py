@@ -7,7 +7,7 @@ masked and dropout instances and its pair split (D = 256), and strided
 [B, S, H, D] views, with ragged lengths throughout.  Its small grids
 (B*H <= 8) always take the key-split route at D <= 128; the unsplit 256-row
 instance is checked on ragged shapes by test_parity_gpu.py.
-24 further draws run the backward of the same routes (backward_ext) against
+25 further draws run the backward of the same routes (backward_ext) against
 the oracle's full backward.
 """
 import numpy as np
@@ -75,7 +75,9 @@ def test_random_shape(c):
     print("  ", st, flush=True)
 
 
-BWD_CASES = [draw(100 + i) for i in range(24)]
+# draw 3040: one query over a masked 4-key range, whose gradients need the
+# per-element bound (rows see too few keys for the slice-wide rule)
+BWD_CASES = [draw(100 + i) for i in range(24)] + [draw(3040)]
 
 
 @pytest.mark.parametrize("c", BWD_CASES, ids=["%d:%dx%dx%dx%dx%d%s%s_%s_p%g%s" % (
