@@ -8,7 +8,9 @@ masked and dropout instances and its pair split (D = 256), and strided
 (B*H <= 8) always take the key-split route at D <= 128; the unsplit 256-row
 instance is checked on ragged shapes by test_parity_gpu.py.
 25 further draws run the backward of the same routes (backward_ext) against
-the oracle's full backward.
+the oracle's full backward, and 18 draws on grids large enough for the
+256-row instance (64-280 heads, 700-1536 rows; plain, masked, dropout,
+strided) compare rows of every head, forward and backward.
 """
 import numpy as np
 import pytest
@@ -134,3 +136,72 @@ def test_random_shape_backward(c):
             st = dict(st, **parity.assert_grad_within_bound(to64(got), ref, bnd[name], dtype,
                                                             "%s random %s" % (name, c)))
         print("  ", name, st, flush=True)
+
+
+def draw_big(i):
+    """Grids large enough for the 256-row instance (B*H 64-280, 700-1536 rows)."""
+    r = np.random.default_rng(7000 + i)
+    B = int(r.integers(1, 3))
+    H = int(r.integers(64, 141))
+    Sq = int(r.integers(700, 1537))
+    Sk = Sq if r.random() < 0.6 else int(r.integers(300, 1537))
+    D = int(r.choice([64, 128, 128]))
+    dtype = str(r.choice(["f16", "bf16"]))
+    causal = bool(r.random() < 0.6)
+    mask = str(r.choice(["none", "none", "shared"]))
+    p = float(r.choice([0.0, 0.0, 0.15]))
+    strided = bool(r.random() < 0.3)
+    return dict(B=B, H=H, Sq=Sq, Sk=Sk, D=D, dtype=dtype, causal=causal, mask=mask, p=p, strided=strided)
+
+
+BIG_CASES = [(i, False) for i in range(12)] + [(100 + i, True) for i in range(6)]
+
+
+@pytest.mark.parametrize("case", BIG_CASES, ids=["big%d%s" % (i, "_bwd" if b else "") for i, b in BIG_CASES])
+def test_random_big_grid(case):
+    """Random draws on grids that take the 256-row instance (plain, masked,
+    dropout, strided): six rows of every head (and the first and last rows)
+    against the oracle; with the backward, those dQ rows and eight dK/dV rows
+    of three heads."""
+    i, bwd = case
+    c = draw_big(i)
+    print("case big", i, bwd, c, flush=True)
+    B, H, Sq, Sk, D, dtype = c["B"], c["H"], c["Sq"], c["Sk"], c["D"], c["dtype"]
+    assert fa.fa_fwd_plan(B, H, Sq, D, c["causal"], fa.BF16 if dtype == "bf16" else fa.F16)[0] == 256
+    q, k, v = make_inputs(B, H, max(Sq, Sk), D, dtype, seed=7100 + i, Sk=Sk)
+    q = q[:, :, :Sq].contiguous()
+    g, _, _ = make_inputs(B, H, Sq, D, dtype, seed=7200 + i)
+    r = np.random.default_rng(7300 + i)
+    m = ms = mt = None
+    if c["mask"] == "shared":
+        m = (r.random((Sq, Sk)) < 0.85).astype(np.uint8)
+        ms = (0, 0, Sk)
+        mt = torch.from_numpy(m).to(DEV)
+    args = [t.to(DEV) for t in (q, k, v, g)]
+    if c["strided"]:
+        args = [t.transpose(1, 2).contiguous().transpose(1, 2) for t in args]
+    kw = dict(causal=c["causal"], mask=mt, dropout_p=c["p"], seed=9, offset=2)
+    o, lse = fa.forward_ext(*args[:3], **kw)
+    BH = B * H
+    rows = np.unique(np.concatenate([h * Sq + r.choice(Sq, 6, replace=False) for h in range(BH)]
+                                    + [np.array([0, Sq - 1, BH * Sq - 1])])).astype(np.int64)
+    if not bwd:
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.attention_fwd_ext(bits(q), bits(k), bits(v), scale=softmax_scale(D),
+                                                causal=c["causal"], dtype=dtype, mask=m, mask_strides=ms,
+                                                dropout_p=c["p"], seed=9, offset=2, rows=rows)
+        st = parity.assert_parity(to64(o).reshape(-1, D)[rows], to64(lse).reshape(-1)[rows], o_ref, l_ref, dtype,
+                                  str(c))
+        print("  ", rows.size, "rows", st, flush=True)
+        return
+    grads = fa.backward_ext(*args[:3], o, lse, args[3], **kw)
+    torch.cuda.synchronize()
+    heads = r.choice(BH, 3, replace=False)
+    krows = np.unique(np.concatenate([h * Sk + r.choice(Sk, 8, replace=False) for h in heads])).astype(np.int64)
+    rq, rk, rv = oracle.attention_bwd_ext(bits(q), bits(k), bits(v), bits(g), scale=softmax_scale(D),
+                                          causal=c["causal"], dtype=dtype, mask=m, mask_strides=ms,
+                                          dropout_p=c["p"], seed=9, offset=2, qrows=rows, krows=krows)
+    for nm, got, ref, rr in (("dq", grads[0], rq, rows), ("dk", grads[1], rk, krows), ("dv", grads[2], rv, krows)):
+        sel = to64(got).reshape(-1, D)[rr]
+        st = parity.assert_grad_parity(sel[None, None], ref[None, None], dtype, "%s %s" % (nm, c))
+        print("  ", nm, rr.size, "rows", st, flush=True)
